@@ -1,0 +1,437 @@
+/*
+ * qref.c -- plain, slow CPU oracle for the quantized-weight prefill linear
+ * layer  Y[M,N] = X[M,K] . dequant(W)[K,N].
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the HIP library, and it never calls it.
+ *
+ * What it computes (each step cites the passage it follows):
+ *
+ *  1. Field decode of the stored weight formats, scalar and byte by byte:
+ *     Q4_K (fp16 d and dmin, eight 6-bit sub-block scales and mins, 4-bit
+ *     codes; 144 bytes per 256 weights -- the dequant-scratch post, "The two
+ *     passes hiding inside one matmul"), Q6_K (6-bit codes split into a low
+ *     nibble and a high 2-bit pair, one int8 scale per 16 weights, fp16 d;
+ *     210 bytes per 256 weights) and W4A16 (4-bit codes, an fp16 scale and a
+ *     4-bit zero-point per group of K -- the vLLM W4A16 PR, section 1
+ *     "Packed fp16 dequant").  The byte order inside the k-quant blocks is
+ *     the GGUF convention, which the pages do not spell out.
+ *
+ *  2. The unpacked weight, in the activation type t (fp16 or bf16):
+ *        Q4_K : w = RN_t( RN_32( factor*q - bias ) ),  factor = d*sc, bias = dmin*m
+ *        Q6_K : w = RN_t( RN_32( d*s*(q - 32) ) )
+ *        W4A16: w = RN_t( RN_32( s*(q - zp) ) )
+ *     The batched-prefill post ("The fix: K-parallel batched DMMV") forms
+ *     each weight as factor*q - bias in single precision; the value is taken
+ *     here as ONE round-to-nearest-even of the exact value into binary32,
+ *     then one round-to-nearest-even into t.  For Q6_K and W4A16 the exact
+ *     value always fits binary32, so the first rounding is the identity and
+ *     w = RN_t(exact), the single rounding the W4A16 PR states ("the multiply
+ *     that follows rounds once").  Every rounding below is done on exact
+ *     integers (value = n * 2^e), so nothing depends on the host's FPU.
+ *
+ *  3. Yref[m][n] = sum_k X[m][k] * W[k][n] in fp64, a naive triple loop
+ *     (the k loop innermost, W read through a transposed copy), together with
+ *     the error scale B[m][n] = sum_k |X[m][k]| * |W[k][n]|.
+ *
+ * All 16-bit floating-point values cross this interface as raw bit patterns
+ * (uint16_t).  dtype 0 = fp16, 1 = bf16.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define QREF_F16 0
+#define QREF_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* Exact rounding of n * 2^e into a binary format                           */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int64_t n; /* signed integer significand */
+    int e;     /* value = n * 2^e */
+    int inf;   /* +-1 when the rounded value overflowed */
+    int neg;   /* sign, kept when a nonzero value rounds to zero */
+} xval;
+
+static int bitlen(uint64_t a) { return a ? 64 - __builtin_clzll(a) : 0; }
+
+/* Round n*2^e to the nearest value with p significand bits, normal exponent
+ * range [emin, emax], ties to even; values below 2^emin round on the fixed
+ * subnormal grid 2^(emin-p+1).  Requires |n| < 2^62. */
+static xval round_exact(int64_t n, int e, int p, int emin, int emax)
+{
+    xval r = {0, 0, 0, n < 0};
+    if (n == 0) return r;
+    int neg = n < 0;
+    uint64_t a = neg ? (uint64_t)(-n) : (uint64_t)n;
+    int E = bitlen(a) - 1 + e;                      /* a*2^e in [2^E, 2^(E+1)) */
+    int qexp = (E < emin ? emin : E) - (p - 1);     /* exponent of one ulp      */
+    int shift = qexp - e;
+    uint64_t q;
+    if (shift <= 0) {
+        q = a;
+        qexp = e;
+    } else if (shift >= 63) {
+        q = 0; /* a < 2^62 <= half an ulp */
+    } else {
+        q = a >> shift;
+        uint64_t rem = a & ((1ull << shift) - 1);
+        uint64_t half = 1ull << (shift - 1);
+        if (rem > half || (rem == half && (q & 1))) q++;
+    }
+    if (q == 0) return r;
+    if (bitlen(q) - 1 + qexp > emax) {
+        r.inf = neg ? -1 : 1;
+        return r;
+    }
+    r.n = neg ? -(int64_t)q : (int64_t)q;
+    r.e = qexp;
+    return r;
+}
+
+static xval rn_f32(int64_t n, int e) { return round_exact(n, e, 24, -126, 127); }
+static xval rn_f16(int64_t n, int e) { return round_exact(n, e, 11, -14, 15); }
+static xval rn_bf16(int64_t n, int e) { return round_exact(n, e, 8, -126, 127); }
+
+/* Bit pattern of an exactly representable rounded value. */
+static uint16_t enc_f16(xval v)
+{
+    if (v.inf) return v.inf < 0 ? 0xFC00 : 0x7C00;
+    if (v.n == 0) return v.neg ? 0x8000 : 0;
+    uint16_t s = v.n < 0 ? 0x8000 : 0;
+    uint64_t a = v.n < 0 ? (uint64_t)(-v.n) : (uint64_t)v.n;
+    int E = bitlen(a) - 1 + v.e;
+    if (E < -14) { /* subnormal: a*2^e = mant*2^-24 */
+        return s | (uint16_t)(a << (v.e + 24));
+    }
+    int sh = v.e - (E - 10); /* bring significand to 11 bits */
+    uint64_t sig = sh >= 0 ? a << sh : a >> (-sh);
+    return s | (uint16_t)((E + 15) << 10) | (uint16_t)(sig - 1024);
+}
+
+static uint16_t enc_bf16(xval v)
+{
+    if (v.inf) return v.inf < 0 ? 0xFF80 : 0x7F80;
+    if (v.n == 0) return v.neg ? 0x8000 : 0;
+    uint16_t s = v.n < 0 ? 0x8000 : 0;
+    uint64_t a = v.n < 0 ? (uint64_t)(-v.n) : (uint64_t)v.n;
+    int E = bitlen(a) - 1 + v.e;
+    if (E < -126) {
+        return s | (uint16_t)(a << (v.e + 133));
+    }
+    int sh = v.e - (E - 7);
+    uint64_t sig = sh >= 0 ? a << sh : a >> (-sh);
+    return s | (uint16_t)((E + 127) << 7) | (uint16_t)(sig - 128);
+}
+
+/* fp16 bits -> (integer significand, exponent); returns -1 for inf/nan. */
+static int f16_split(uint16_t h, int64_t *n, int *e)
+{
+    int ex = (h >> 10) & 31, mant = h & 1023;
+    if (ex == 31) return -1;
+    int64_t sig = ex ? (1024 + mant) : mant;
+    *e = ex ? ex - 25 : -24;
+    *n = (h & 0x8000) ? -sig : sig;
+    return 0;
+}
+
+double qref_f16_to_double(uint16_t h)
+{
+    int ex = (h >> 10) & 31, mant = h & 1023;
+    double s = (h & 0x8000) ? -1.0 : 1.0;
+    if (ex == 31) return mant ? NAN : s * INFINITY;
+    if (ex == 0) return s * ldexp((double)mant, -24);
+    return s * ldexp((double)(1024 + mant), ex - 25);
+}
+
+double qref_bf16_to_double(uint16_t b)
+{
+    int ex = (b >> 7) & 255, mant = b & 127;
+    double s = (b & 0x8000) ? -1.0 : 1.0;
+    if (ex == 255) return mant ? NAN : s * INFINITY;
+    if (ex == 0) return s * ldexp((double)mant, -133);
+    return s * ldexp((double)(128 + mant), ex - 134);
+}
+
+static double t_to_double(uint16_t v, int dtype)
+{
+    return dtype == QREF_F16 ? qref_f16_to_double(v) : qref_bf16_to_double(v);
+}
+
+/* Round-to-nearest-even of a finite double into fp16 / bf16 / binary32 bits.
+ * Exposed so the tests can pin the rounding against library conversions. */
+static int double_split(double x, int64_t *n, int *e)
+{
+    if (!isfinite(x)) return -1;
+    if (x == 0.0) { *n = 0; *e = 0; return 0; }
+    int ex;
+    double fr = frexp(x, &ex);              /* x = fr * 2^ex, 0.5 <= |fr| < 1 */
+    *n = (int64_t)ldexp(fr, 53);            /* exact: 53-bit significand      */
+    *e = ex - 53;
+    return 0;
+}
+
+uint16_t qref_rn_f16(double x)
+{
+    int64_t n; int e;
+    if (double_split(x, &n, &e)) return isnan(x) ? 0x7E00 : (x < 0 ? 0xFC00 : 0x7C00);
+    if (n == 0) return signbit(x) ? 0x8000 : 0;
+    return enc_f16(rn_f16(n, e));
+}
+
+uint16_t qref_rn_bf16(double x)
+{
+    int64_t n; int e;
+    if (double_split(x, &n, &e)) return isnan(x) ? 0x7FC0 : (x < 0 ? 0xFF80 : 0x7F80);
+    if (n == 0) return signbit(x) ? 0x8000 : 0;
+    return enc_bf16(rn_bf16(n, e));
+}
+
+/* binary32 rounding of a double, returned as a double (exact). */
+double qref_rn_f32(double x)
+{
+    int64_t n; int e;
+    if (double_split(x, &n, &e)) return x;
+    xval v = rn_f32(n, e);
+    if (v.inf) return v.inf * INFINITY;
+    return ldexp((double)v.n, v.e);
+}
+
+static uint16_t enc_t(xval v, int dtype)
+{
+    return dtype == QREF_F16 ? enc_f16(rn_f16(v.n, v.e)) : enc_bf16(rn_bf16(v.n, v.e));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Field decode                                                             */
+/* ------------------------------------------------------------------------ */
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* One Q4_K block (144 bytes): d, dmin, 8 scales, 8 mins, 256 codes. */
+void qref_q4k_fields(const uint8_t *blk, uint16_t *d, uint16_t *dmin,
+                     uint8_t sc[8], uint8_t mn[8], uint8_t q[256])
+{
+    const uint8_t *s12 = blk + 4, *qs = blk + 16;
+    *d = rd16(blk);
+    *dmin = rd16(blk + 2);
+    for (int j = 0; j < 4; j++) {
+        sc[j] = s12[j] & 63;
+        mn[j] = s12[j + 4] & 63;
+        sc[j + 4] = (uint8_t)((s12[j + 8] & 15) | ((s12[j] >> 6) << 4));
+        mn[j + 4] = (uint8_t)((s12[j + 8] >> 4) | ((s12[j + 4] >> 6) << 4));
+    }
+    for (int g = 0; g < 4; g++)
+        for (int l = 0; l < 32; l++) {
+            uint8_t b = qs[32 * g + l];
+            q[64 * g + l] = b & 15;
+            q[64 * g + 32 + l] = b >> 4;
+        }
+}
+
+/* One Q6_K block (210 bytes): 256 six-bit codes, 16 int8 scales, d. */
+void qref_q6k_fields(const uint8_t *blk, uint16_t *d, int8_t s[16], uint8_t q[256])
+{
+    const uint8_t *ql = blk, *qh = blk + 128;
+    for (int i = 0; i < 16; i++) s[i] = (int8_t)blk[192 + i];
+    *d = rd16(blk + 208);
+    for (int h = 0; h < 2; h++)
+        for (int r = 0; r < 4; r++)
+            for (int l = 0; l < 32; l++) {
+                uint8_t lob = ql[64 * h + l + 32 * (r & 1)];
+                int lo = (r < 2) ? (lob & 15) : (lob >> 4);
+                int hi = (qh[32 * h + l] >> (2 * r)) & 3;
+                q[128 * h + 32 * r + l] = (uint8_t)(lo | (hi << 4));
+            }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Unpacked weight values                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Q4_K: factor*q - bias with factor = d*sc, bias = dmin*m, all exact, then
+ * binary32, then t.  Returns -1 if d or dmin is inf/nan. */
+static int q4k_value(uint16_t d, uint16_t dmin, int sc, int mn, int q, int dtype, uint16_t *out)
+{
+    int64_t nd, nm; int ed, em;
+    if (f16_split(d, &nd, &ed) || f16_split(dmin, &nm, &em)) return -1;
+    int e0 = ed < em ? ed : em;
+    int64_t a = (nd * sc * q) * ((int64_t)1 << (ed - e0));
+    int64_t b = (nm * mn) * ((int64_t)1 << (em - e0));
+    xval v = rn_f32(a - b, e0);
+    if (v.inf) { *out = dtype == QREF_F16 ? (v.inf < 0 ? 0xFC00 : 0x7C00) : (v.inf < 0 ? 0xFF80 : 0x7F80); return 0; }
+    *out = enc_t(v, dtype);
+    return 0;
+}
+
+/* Q6_K: d*s*(q-32). */
+static int q6k_value(uint16_t d, int s, int q, int dtype, uint16_t *out)
+{
+    int64_t nd; int ed;
+    if (f16_split(d, &nd, &ed)) return -1;
+    xval v = rn_f32(nd * s * (q - 32), ed);
+    *out = enc_t(v, dtype);
+    return 0;
+}
+
+/* W4A16: s*(q-zp). */
+static int w4_value(uint16_t s, int q, int zp, int dtype, uint16_t *out)
+{
+    int64_t ns; int es;
+    if (f16_split(s, &ns, &es)) return -1;
+    xval v = rn_f32(ns * (q - zp), es);
+    *out = enc_t(v, dtype);
+    return 0;
+}
+
+/* Scalar value of one weight for the tests (no array walk). */
+int qref_q4k_weight(uint16_t d, uint16_t dmin, int sc, int mn, int q, int dtype, uint16_t *out)
+{
+    return q4k_value(d, dmin, sc, mn, q, dtype, out);
+}
+int qref_q6k_weight(uint16_t d, int s, int q, int dtype, uint16_t *out)
+{
+    return q6k_value(d, s, q, dtype, out);
+}
+int qref_w4a16_weight(uint16_t s, int q, int zp, int dtype, uint16_t *out)
+{
+    return w4_value(s, q, zp, dtype, out);
+}
+
+/* Whole-matrix dequant into logical W[K][N] (row k, column n). */
+int qref_dequant_q4k(const uint8_t *blocks, int64_t N, int64_t K, int dtype, uint16_t *W)
+{
+    if (K % 256) return -2;
+    int64_t nb = K / 256;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        uint16_t d, dmin;
+        uint8_t sc[8], mn[8], q[256];
+        for (int64_t b = 0; b < nb; b++) {
+            qref_q4k_fields(blocks + (n * nb + b) * 144, &d, &dmin, sc, mn, q);
+            for (int k = 0; k < 256; k++) {
+                int j = k / 32;
+                uint16_t w;
+                bad |= q4k_value(d, dmin, sc[j], mn[j], q[k], dtype, &w) != 0;
+                W[(b * 256 + k) * N + n] = w;
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+int qref_dequant_q6k(const uint8_t *blocks, int64_t N, int64_t K, int dtype, uint16_t *W)
+{
+    if (K % 256) return -2;
+    int64_t nb = K / 256;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        uint16_t d;
+        int8_t s[16];
+        uint8_t q[256];
+        for (int64_t b = 0; b < nb; b++) {
+            qref_q6k_fields(blocks + (n * nb + b) * 210, &d, s, q);
+            for (int k = 0; k < 256; k++) {
+                uint16_t w;
+                bad |= q6k_value(d, s[k / 16], q[k], dtype, &w) != 0;
+                W[(b * 256 + k) * N + n] = w;
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* codes [N][K] one code per byte; scales [K/g][N] fp16 bits; zeros [K/g][N]
+ * or NULL for the symmetric variant (every zero-point is 8). */
+int qref_dequant_w4a16(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                       int64_t N, int64_t K, int64_t group, int dtype, uint16_t *W)
+{
+    if (group <= 0 || K % group) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            int64_t gi = k / group;
+            int zp = zeros ? zeros[gi * N + n] : 8;
+            uint16_t w;
+            bad |= w4_value(scales[gi * N + n], codes[n * K + k], zp, dtype, &w) != 0;
+            W[k * N + n] = w;
+        }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp64 GEMM                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Y[M][N] = X[M][K] . W[K][N] in fp64 and B[M][N] = |X| . |W| (B may be NULL). */
+int qref_gemm(const uint16_t *X, const uint16_t *W, int64_t M, int64_t N, int64_t K, int dtype,
+              double *Y, double *B)
+{
+    double *wt = (double *)malloc(sizeof(double) * (size_t)(N * K));
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(M * K));
+    if (!wt || !xd) { free(wt); free(xd); return -3; }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) wt[n * K + k] = t_to_double(W[k * N + n], dtype);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M * K; i++) xd[i] = t_to_double(X[i], dtype);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; m++) {
+        const double *xr = xd + m * K;
+        for (int64_t n = 0; n < N; n++) {
+            const double *wr = wt + n * K;
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                acc += xr[k] * wr[k];
+                bnd += fabs(xr[k]) * fabs(wr[k]);
+            }
+            Y[m * N + n] = acc;
+            if (B) B[m * N + n] = bnd;
+        }
+    }
+    free(wt);
+    free(xd);
+    return 0;
+}
+
+/* The same sums for `count` chosen (row, column) pairs only. */
+int qref_gemm_at(const uint16_t *X, const uint16_t *W, int64_t M, int64_t N, int64_t K, int dtype,
+                 const int64_t *rows, const int64_t *cols, int64_t count, double *Y, double *B)
+{
+    for (int64_t i = 0; i < count; i++)
+        if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) {
+        int64_t m = rows[i], n = cols[i];
+        double acc = 0.0, bnd = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double x = t_to_double(X[m * K + k], dtype);
+            double w = t_to_double(W[k * N + n], dtype);
+            acc += x * w;
+            bnd += fabs(x) * fabs(w);
+        }
+        Y[i] = acc;
+        if (B) B[i] = bnd;
+    }
+    return 0;
+}
+
+int qref_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

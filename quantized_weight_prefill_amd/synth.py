@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for the quantized-weight prefill linear layer.
+
+This module only draws random numbers and lays the drawn fields out in the
+GGUF-style byte formats; it holds none of the dequantisation or GEMM
+arithmetic.  Both the HIP path (through the packer) and the CPU oracle read
+what it produces, so it must import nothing from either of them.
+
+Formats written here (byte layouts follow the GGUF k-quant convention):
+
+* Q4_K, 144 bytes per 256 weights: fp16 ``d``, fp16 ``dmin``, 12 bytes that
+  hold eight 6-bit sub-block scales and eight 6-bit sub-block mins, then 128
+  bytes of 4-bit codes.  Byte ``32*g + l`` of the code field holds weight
+  ``64*g + l`` in its low nibble and weight ``64*g + 32 + l`` in its high
+  nibble.  The 12 scale bytes: bytes 0..3 hold ``sc[0..3]`` in their low six
+  bits and the top two bits of ``sc[4..7]``; bytes 4..7 do the same for the
+  mins; bytes 8..11 hold the low four bits of ``sc[4..7]`` (low nibble) and of
+  ``m[4..7]`` (high nibble).
+* Q6_K, 210 bytes per 256 weights: 128 bytes of low code nibbles ``ql``, 64
+  bytes of high 2-bit pairs ``qh``, 16 signed 8-bit scales (one per 16
+  weights), then fp16 ``d``.  Each 128-weight half ``h`` uses ``ql[64h:64h+64]``
+  and ``qh[32h:32h+32]``; within it weight ``32*r + l`` (r = 0..3, l = 0..31)
+  takes its low nibble from ``ql[64h + l + 32*(r & 1)]`` (low nibble for
+  r < 2, high nibble for r >= 2) and its high two bits from bits
+  ``2r..2r+1`` of ``qh[32h + l]``.
+* W4A16 (GPTQ-style), kept logical: one 4-bit code per byte ``codes[N][K]``,
+  fp16 ``scales[K/g][N]``, zero-points ``zeros[K/g][N]`` (0..15); the symmetric
+  variant has every zero-point equal to 8.
+
+Distributions follow the workload descriptions: activations ~ N(0, 1) drawn in
+fp32 and rounded to nearest-even into fp16 or bf16; fp16 scale-like fields ~
+U[1e-3, 1e-2] drawn in fp64 and rounded to fp16; integer fields uniform over
+their stated range.  Seeds are ``1000 + workload index``; sub-streams come
+from ``SeedSequence(seed).spawn(n)`` and are consumed in a fixed order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F16 = 0
+BF16 = 1
+DTYPE_NAMES = {F16: "f16", BF16: "bf16"}
+
+Q4K_BLOCK_BYTES = 144
+Q6K_BLOCK_BYTES = 210
+QK = 256
+
+
+def streams(seed: int, n: int) -> list[np.random.Generator]:
+    """``n`` independent PCG64 generators derived from one seed."""
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def f16_bits(values) -> np.ndarray:
+    """fp64/fp32 values -> fp16 bit patterns (numpy's round-to-nearest-even)."""
+    return np.asarray(values).astype(np.float16).view(np.uint16)
+
+
+def bf16_bits_from_f32(values) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns (torch CPU round-to-nearest-even)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def activations(rng: np.random.Generator, M: int, K: int, dtype: int) -> np.ndarray:
+    """X[M][K] ~ N(0,1) drawn in fp32, stored as fp16/bf16 bits (uint16)."""
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if dtype == F16:
+        return f16_bits(x)
+    if dtype == BF16:
+        return bf16_bits_from_f32(x)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def _u_f16(rng: np.random.Generator, shape, lo=1e-3, hi=1e-2) -> np.ndarray:
+    return f16_bits(rng.uniform(lo, hi, size=shape))
+
+
+# ----------------------------------------------------------------------------
+# Q4_K
+# ----------------------------------------------------------------------------
+
+def q4k_fields(rng: np.random.Generator, N: int, K: int) -> dict:
+    """Logical Q4_K fields for W stored per output column n, blocks along K."""
+    assert K % QK == 0
+    nb = K // QK
+    return {
+        "d": _u_f16(rng, (N, nb)),
+        "dmin": _u_f16(rng, (N, nb)),
+        "sc": rng.integers(0, 64, size=(N, nb, 8), dtype=np.uint8),
+        "m": rng.integers(0, 64, size=(N, nb, 8), dtype=np.uint8),
+        "q": rng.integers(0, 16, size=(N, K), dtype=np.uint8),
+    }
+
+
+def q4k_encode(f: dict) -> np.ndarray:
+    """Logical fields -> GGUF-style Q4_K blocks, uint8 [N][K/256][144]."""
+    d, dmin, sc, m, q = f["d"], f["dmin"], f["sc"], f["m"], f["q"]
+    N, nb = d.shape
+    out = np.zeros((N, nb, Q4K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<u2").view(np.uint8).reshape(N, nb, 2)
+    out[:, :, 2:4] = dmin.astype("<u2").view(np.uint8).reshape(N, nb, 2)
+    sc = sc.astype(np.uint8)
+    m = m.astype(np.uint8)
+    s12 = np.zeros((N, nb, 12), dtype=np.uint8)
+    s12[:, :, 0:4] = (sc[:, :, 0:4] & 63) | ((sc[:, :, 4:8] >> 4) << 6)
+    s12[:, :, 4:8] = (m[:, :, 0:4] & 63) | ((m[:, :, 4:8] >> 4) << 6)
+    s12[:, :, 8:12] = (sc[:, :, 4:8] & 15) | ((m[:, :, 4:8] & 15) << 4)
+    out[:, :, 4:16] = s12
+    qb = q.reshape(N, nb, 4, 2, 32)  # [.., g, lo/hi half of 64, l]
+    out[:, :, 16:] = (qb[:, :, :, 0, :] | (qb[:, :, :, 1, :] << 4)).reshape(N, nb, 128)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Q6_K
+# ----------------------------------------------------------------------------
+
+def q6k_fields(rng: np.random.Generator, N: int, K: int) -> dict:
+    assert K % QK == 0
+    nb = K // QK
+    return {
+        "d": _u_f16(rng, (N, nb)),
+        "s": rng.integers(-128, 128, size=(N, nb, 16), dtype=np.int16).astype(np.int8),
+        "q": rng.integers(0, 64, size=(N, K), dtype=np.uint8),
+    }
+
+
+def q6k_encode(f: dict) -> np.ndarray:
+    """Logical fields -> GGUF-style Q6_K blocks, uint8 [N][K/256][210]."""
+    d, s, q = f["d"], f["s"], f["q"]
+    N, nb = d.shape
+    out = np.zeros((N, nb, Q6K_BLOCK_BYTES), dtype=np.uint8)
+    qh4 = q.reshape(N, nb, 2, 4, 32)  # [.., half, r, l]
+    lo = qh4 & 15
+    hi = qh4 >> 4
+    ql = np.zeros((N, nb, 2, 64), dtype=np.uint8)
+    ql[..., 0:32] = lo[:, :, :, 0, :] | (lo[:, :, :, 2, :] << 4)
+    ql[..., 32:64] = lo[:, :, :, 1, :] | (lo[:, :, :, 3, :] << 4)
+    qhb = hi[:, :, :, 0, :] | (hi[:, :, :, 1, :] << 2) | (hi[:, :, :, 2, :] << 4) | (hi[:, :, :, 3, :] << 6)
+    out[:, :, 0:128] = ql.reshape(N, nb, 128)
+    out[:, :, 128:192] = qhb.reshape(N, nb, 64)
+    out[:, :, 192:208] = s.view(np.uint8)
+    out[:, :, 208:210] = d.astype("<u2").view(np.uint8).reshape(N, nb, 2)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# W4A16 (group-wise scale + zero-point)
+# ----------------------------------------------------------------------------
+
+def w4a16_fields(rng: np.random.Generator, N: int, K: int, group: int, symmetric: bool) -> dict:
+    assert K % group == 0
+    ng = K // group
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    scales = _u_f16(rng, (ng, N))
+    if symmetric:
+        zeros = np.full((ng, N), 8, dtype=np.uint8)
+    else:
+        zeros = rng.integers(0, 16, size=(ng, N), dtype=np.uint8)
+    return {"codes": codes, "scales": scales, "zeros": zeros, "group": group, "symmetric": symmetric}
+
+
+# ----------------------------------------------------------------------------
+# Named workloads
+# ----------------------------------------------------------------------------
+
+#: One Qwen3-8B dense layer's seven projections at M = 658 prompt tokens:
+#: (name, K, N, format).
+QWEN3_8B_LAYER = (
+    ("q", 4096, 4096, "q4k"),
+    ("k", 4096, 1024, "q4k"),
+    ("v", 4096, 1024, "q4k"),
+    ("o", 4096, 4096, "q4k"),
+    ("gate", 4096, 12288, "q4k"),
+    ("up", 4096, 12288, "q4k"),
+    ("down", 12288, 4096, "q6k"),
+)
+QWEN3_8B_LAYERS = 36
+QWEN3_8B_PROMPT = 658
+
+
+def weight_fields(fmt: str, rng: np.random.Generator, N: int, K: int, group: int = 128,
+                  symmetric: bool = False) -> dict:
+    if fmt == "q4k":
+        return q4k_fields(rng, N, K)
+    if fmt == "q6k":
+        return q6k_fields(rng, N, K)
+    if fmt == "w4a16":
+        return w4a16_fields(rng, N, K, group, symmetric)
+    raise ValueError(fmt)
+
+
+def encode(fmt: str, fields: dict):
+    """GGUF-style bytes for the k-quants; the W4A16 fields stay logical."""
+    if fmt == "q4k":
+        return q4k_encode(fields)
+    if fmt == "q6k":
+        return q6k_encode(fields)
+    if fmt == "w4a16":
+        return fields
+    raise ValueError(fmt)

@@ -1,0 +1,475 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+Every check compares the oracle with something other than itself: library
+roundings (numpy float16/float32, torch bfloat16), exact rationals
+(``fractions.Fraction``) rounded by a brute-force nearest-neighbour search,
+closed forms the pages print, special cases whose answer is known in closed
+form, and numpy's float64 matmul.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_weight_prefill_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.txt")
+
+
+def load_golden() -> dict:
+    vals = {}
+    with open(GOLDEN) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            k, v = (s.strip() for s in line.split("="))
+            vals[k] = float(int(v, 16)) if v.startswith("0x") else float(v)
+    return vals
+
+
+# ----------------------------------------------------------------------------
+# Brute-force nearest-even rounding of an exact rational (independent of the
+# oracle's bit manipulation): look at the neighbouring grid points of the
+# target type and choose the closest, ties to the even bit pattern.
+# ----------------------------------------------------------------------------
+
+def _grid_candidates(x: Fraction, ftype, inf_at: Fraction):
+    """Grid points of ftype around x; one past the largest finite value the
+    grid continues at ``inf_at`` (2^(emax+1)), which stands for infinity."""
+    big = np.finfo(ftype).max
+    xf = float(x)
+    g = ftype(np.clip(xf, -float(big), float(big)))
+    cands = {(Fraction(float(c)), c) for c in (g, np.nextafter(g, ftype(np.inf)), np.nextafter(g, ftype(-np.inf)))
+             if np.isfinite(c)}
+    if abs(x) >= Fraction(float(big)):
+        sgn = 1 if x > 0 else -1
+        cands.add((sgn * inf_at, ftype(sgn * np.inf)))
+    return cands
+
+
+def nearest_even(x: Fraction, kind: str) -> np.generic:
+    if kind == "f16":
+        ftype, ut, inf_at = np.float16, np.uint16, Fraction(2 ** 16)
+    elif kind == "f32":
+        ftype, ut, inf_at = np.float32, np.uint32, Fraction(2 ** 128)
+    else:
+        raise ValueError(kind)
+    best = None
+    for val, c in _grid_candidates(x, ftype, inf_at):
+        key = (abs(val - x), int(np.array(c, ftype).view(ut)) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def nearest_even_bf16(x: Fraction) -> int:
+    """bf16 bits nearest to x, ties to even: candidates on the bf16 grid
+    around the float32 nearest value (2^128 stands for infinity)."""
+    f = np.float32(float(x)) if abs(x) < Fraction(2 ** 128) else np.float32(np.sign(float(x)) * 3.3e38)
+    b = int(np.array(f, np.float32).view(np.uint32))
+    lo = b & 0xFFFF0000
+    best = None
+    for c in (lo, lo + 0x10000, lo - 0x10000):
+        if c < 0 or c >= 1 << 32:
+            continue
+        v = np.array(c, np.uint32).view(np.float32)
+        if np.isnan(v):
+            continue
+        val = Fraction(float(v)) if np.isfinite(v) else (1 if v > 0 else -1) * Fraction(2 ** 128)
+        key = (abs(val - x), (c >> 16) & 1)
+        if best is None or key < best[0]:
+            best = (key, c >> 16)
+    return best[1]
+
+
+def f16_val(h: int) -> Fraction:
+    return Fraction(float(np.array(h, np.uint16).view(np.float16)))
+
+
+# ----------------------------------------------------------------------------
+# Roundings and conversions
+# ----------------------------------------------------------------------------
+
+def test_f16_decode_exhaustive():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = allbits.view(np.float16).astype(np.float64)
+    got = oracle.bits_to_double(allbits, oracle.F16)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.all(np.isnan(got[np.isnan(ref)]))
+
+
+def test_bf16_decode_exhaustive():
+    allbits = np.arange(65536, dtype=np.uint32)
+    ref = (allbits << 16).view(np.float32).astype(np.float64)
+    got = oracle.bits_to_double(allbits.astype(np.uint16), oracle.BF16)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def _rounding_probe_values(rng):
+    vals = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 1e6, -1e6, 2.0 ** -24, 2.0 ** -25,
+            3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1e-30, -1e-30]
+    # random magnitudes across the fp16 normal, subnormal and overflow ranges
+    vals += list(rng.standard_normal(2000) * np.exp2(rng.integers(-30, 20, 2000)))
+    # exact midpoints between neighbouring fp16 values (ties)
+    h = rng.integers(0, 0x7BFF, 2000).astype(np.uint16)
+    a = h.view(np.float16).astype(np.float64)
+    b = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    vals += list((a + b) / 2) + list(-(a + b) / 2)
+    # midpoints +- one double ulp
+    mids = (a + b) / 2
+    vals += list(np.nextafter(mids, np.inf)) + list(np.nextafter(mids, -np.inf))
+    return vals
+
+
+def test_rn_f16_matches_numpy():
+    rng = np.random.default_rng(11)
+    for x in _rounding_probe_values(rng):
+        want = int(np.array(np.float16(x)).view(np.uint16))
+        assert oracle.rn_f16(x) == want, x
+
+
+def test_rn_f32_matches_numpy():
+    rng = np.random.default_rng(12)
+    xs = list(rng.standard_normal(3000) * np.exp2(rng.integers(-140, 130, 3000)))
+    f = rng.standard_normal(1000).astype(np.float32)
+    nxt = np.nextafter(f, np.float32(np.inf))
+    xs += list((f.astype(np.float64) + nxt.astype(np.float64)) / 2)  # float32 ties
+    for x in xs:
+        want = float(np.float32(x))
+        got = oracle.rn_f32(x)
+        assert got == want or (math.isinf(got) and math.isinf(want)), x
+
+
+def test_rn_bf16_matches_torch():
+    rng = np.random.default_rng(13)
+    f = (rng.standard_normal(4000) * np.exp2(rng.integers(-130, 120, 4000))).astype(np.float32)
+    bits = f.view(np.uint32)
+    ties = ((bits & 0xFFFF0000) | 0x8000).view(np.float32)  # exact bf16 midpoints
+    f = np.concatenate([f, ties[np.isfinite(ties)]])
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for x, w in zip(f, want):
+        assert oracle.rn_bf16(float(x)) == int(w), x
+
+
+# ----------------------------------------------------------------------------
+# Closed forms the pages print
+# ----------------------------------------------------------------------------
+
+def test_page_closed_forms():
+    g = load_golden()
+    # Q4_K: fp16 d + fp16 dmin + 12 B of 6-bit scales/mins + 128 B of nibbles
+    assert 2 + 2 + 12 + 128 == synth.Q4K_BLOCK_BYTES
+    assert synth.Q4K_BLOCK_BYTES / 256 == g["q4k_bytes_per_weight"]
+    assert g["q4k_bytes_per_weight"] + 2.0 + 2.0 == g["staged_bytes_per_weight"]
+    assert round(g["staged_bytes_per_weight"] / g["q4k_bytes_per_weight"], 1) == g["staged_over_fused"]
+    assert round(g["rx9070xt_fp16_TFLOPs"] * 1000 / g["rx9070xt_bw_GBps"]) == g["ridge_flop_per_byte"]
+    assert round(2 * g["tile_tokens"] / g["staged_bytes_per_weight"]) == g["staged_intensity"]
+    assert round(2 * g["tile_tokens"] / g["q4k_bytes_per_weight"], -1) == g["fused_intensity"]
+    assert round(g["staged_intensity"] * g["rx9070xt_bw_GBps"] / 1000) == g["staged_cap_TFLOPs"]
+    T, tile = int(g["weight_reads_T"]), int(g["weight_reads_tile"])
+    assert T // -(-T // tile) == g["weight_reads_ratio"]
+    # Q6_K: 128 B low nibbles + 64 B high pairs + 16 int8 scales + fp16 d
+    assert 128 + 64 + 16 + 2 == synth.Q6K_BLOCK_BYTES
+    assert synth.Q6K_BLOCK_BYTES / 256 == 0.8203125
+
+
+def test_magic_fp16_exhaustive():
+    """0x6400|n read as fp16 is 1024+n for every n < 1024, and subtracting
+    1024+zp from 1024+n gives n-zp exactly for every pair of 4-bit codes."""
+    g = load_golden()
+    base = int(g["magic_f16_bits"])
+    n = np.arange(1024, dtype=np.uint16)
+    v = (base | n).astype(np.uint16).view(np.float16)
+    assert np.array_equal(v.astype(np.float64), g["magic_f16_base"] + n)
+    for nn in range(16):
+        for zp in range(16):
+            a = np.array(base | nn, np.uint16).view(np.float16)
+            b = np.array(base | zp, np.uint16).view(np.float16)
+            assert float(a - b) == nn - zp
+    # the and-or form on a whole 32-bit lane yields the nibble pair
+    mask, orv = int(g["and_or_mask"]), int(g["and_or_or"])
+    rng = np.random.default_rng(3)
+    for x in rng.integers(0, 2 ** 32, 200, dtype=np.uint64):
+        r = (int(x) & mask) | orv
+        h = np.array([r & 0xFFFF, r >> 16], np.uint16).view(np.float16)
+        assert float(h[0]) == 1024 + (int(x) & 15) and float(h[1]) == 1024 + ((int(x) >> 16) & 15)
+
+
+def test_derived_magics_exhaustive():
+    """bf16 0x4300|n = 128+n (n < 128); fp32 0x4B000000|n = 2^23+n;
+    fp16 subnormal pattern n = n * 2^-24 (n < 1024)."""
+    n = np.arange(128, dtype=np.uint32)
+    bf = ((0x4300 | n) << 16).view(np.float32)
+    assert np.array_equal(bf.astype(np.float64), 128 + n)
+    n = np.arange(1 << 16, dtype=np.uint32)
+    f = (0x4B000000 | n).view(np.float32)
+    assert np.array_equal(f.astype(np.float64), 2 ** 23 + n)
+    n = np.arange(1024, dtype=np.uint16)
+    assert np.array_equal(n.view(np.float16).astype(np.float64), n * 2.0 ** -24)
+
+
+# ----------------------------------------------------------------------------
+# Field decode: the generator's encoder and the oracle's decoder are two
+# independent readings of one layout; they must invert each other.
+# ----------------------------------------------------------------------------
+
+def test_q4k_field_roundtrip():
+    rng = np.random.default_rng(21)
+    f = synth.q4k_fields(rng, 8, 1024)
+    f["sc"][0, 0] = np.arange(56, 64)  # exercise the top two bits of every slot
+    f["m"][0, 0] = np.arange(63, 55, -1)
+    enc = synth.q4k_encode(f)
+    for n in range(8):
+        for b in range(4):
+            got = oracle.q4k_fields(enc[n, b])
+            assert got["d"] == f["d"][n, b] and got["dmin"] == f["dmin"][n, b]
+            assert np.array_equal(got["sc"], f["sc"][n, b])
+            assert np.array_equal(got["m"], f["m"][n, b])
+            assert np.array_equal(got["q"], f["q"][n, 256 * b:256 * (b + 1)])
+
+
+def test_q6k_field_roundtrip():
+    rng = np.random.default_rng(22)
+    f = synth.q6k_fields(rng, 8, 768)
+    f["s"][0, 0] = np.arange(-128, 128, 16)
+    enc = synth.q6k_encode(f)
+    for n in range(8):
+        for b in range(3):
+            got = oracle.q6k_fields(enc[n, b])
+            assert got["d"] == f["d"][n, b]
+            assert np.array_equal(got["s"], f["s"][n, b])
+            assert np.array_equal(got["q"], f["q"][n, 256 * b:256 * (b + 1)])
+
+
+# ----------------------------------------------------------------------------
+# Unpacked values against exact rationals
+# ----------------------------------------------------------------------------
+
+def _expect(exact: Fraction, dtype: int) -> int:
+    """RN_t(RN_32(exact)) by brute-force nearest search."""
+    x32 = Fraction(float(nearest_even(exact, "f32")))
+    if dtype == oracle.F16:
+        return int(np.array(nearest_even(x32, "f16"), np.float16).view(np.uint16))
+    return nearest_even_bf16(x32)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_q4k_values_exact_rationals(dtype):
+    rng = np.random.default_rng(31 + dtype)
+    f = synth.q4k_fields(rng, 64, 256)
+    n_exact32 = 0
+    for n in range(64):
+        d, dm = int(f["d"][n, 0]), int(f["dmin"][n, 0])
+        for k in range(0, 256, 7):
+            j = k // 32
+            sc, m, q = int(f["sc"][n, 0, j]), int(f["m"][n, 0, j]), int(f["q"][n, k])
+            exact = f16_val(d) * sc * q - f16_val(dm) * m
+            got = oracle.q4k_weight(d, dm, sc, m, q, dtype)
+            assert got == _expect(exact, dtype), (d, dm, sc, m, q)
+            # at these distributions the binary32 step is exact, so w = RN_t(exact)
+            n_exact32 += Fraction(float(np.float32(float(exact)))) == exact
+    assert n_exact32 == 64 * len(range(0, 256, 7))
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_q4k_values_wide_exponent_gap(dtype):
+    """d and dmin far apart in magnitude: the exact value needs more than 24
+    bits, so the binary32 rounding step matters."""
+    rng = np.random.default_rng(41 + dtype)
+    hit_inexact = 0
+    for _ in range(3000):
+        d = int(synth.f16_bits(rng.uniform(0.5, 8.0)))
+        dm = int(synth.f16_bits(rng.uniform(2.0 ** -20, 2.0 ** -12)))
+        sc, m, q = (int(v) for v in rng.integers([1, 1, 1], [64, 64, 16]))
+        exact = f16_val(d) * sc * q - f16_val(dm) * m
+        hit_inexact += Fraction(float(np.float32(float(exact)))) != exact
+        assert oracle.q4k_weight(d, dm, sc, m, q, dtype) == _expect(exact, dtype)
+    assert hit_inexact > 100
+
+
+def test_q4k_binary32_step():
+    """Inputs where forming the weight in binary32 first changes the final
+    rounding: factor*q sits exactly on a midpoint of the target grid and the
+    bias is a quarter of a binary32 ulp.  The oracle must give RN_t(RN_32(x)),
+    which differs here from RN_t(x)."""
+    cases = [  # (d, dmin, sc, m, q, dtype)
+        (0x3C01, 0x0001, 1, 1, 3, oracle.F16),   # 3075*2^-10 - 2^-24: fp16 tie at 1537.5 ulps
+        (0x400C, 0x0001, 1, 1, 1, oracle.BF16),  # 1036*2^-9 - 2^-24: bf16 tie at 129.5 ulps
+    ]
+    for d, dm, sc, m, q, dtype in cases:
+        exact = f16_val(d) * sc * q - f16_val(dm) * m
+        two_step = _expect(exact, dtype)
+        if dtype == oracle.F16:
+            direct = int(np.array(nearest_even(exact, "f16"), np.float16).view(np.uint16))
+        else:
+            direct = nearest_even_bf16(exact)
+        assert two_step != direct
+        assert oracle.q4k_weight(d, dm, sc, m, q, dtype) == two_step
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_q6k_values_exact_rationals(dtype):
+    rng = np.random.default_rng(51 + dtype)
+    ds = list(synth.f16_bits(rng.uniform(1e-3, 1e-2, 300))) + [0x0001, 0x03FF, 0x7BFF, 0x3C00]
+    for d in ds:
+        d = int(d)
+        for s, q in zip(rng.integers(-128, 128, 8), rng.integers(0, 64, 8)):
+            exact = f16_val(d) * int(s) * (int(q) - 32)
+            assert oracle.q6k_weight(d, int(s), int(q), dtype) == _expect(exact, dtype)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_w4a16_values_exact_rationals(dtype):
+    rng = np.random.default_rng(61 + dtype)
+    for s in synth.f16_bits(rng.uniform(1e-3, 1e-2, 200)):
+        for q in range(16):
+            zp = int(rng.integers(0, 16))
+            exact = f16_val(int(s)) * (q - zp)
+            want = _expect(exact, dtype)
+            assert oracle.w4a16_weight(int(s), q, zp, dtype) == want
+            if dtype == oracle.F16:
+                # the packed-fp16 route of the W4A16 PR: (1024+q)-(1024+zp) is
+                # exact, then one fp16 multiply
+                a = np.array(0x6400 | q, np.uint16).view(np.float16)
+                b = np.array(0x6400 | zp, np.uint16).view(np.float16)
+                sv = np.array(s, np.uint16).view(np.float16)
+                assert int(np.array((a - b) * sv, np.float16).view(np.uint16)) == want
+
+
+# ----------------------------------------------------------------------------
+# Special cases with closed-form answers (array walk, layout [K][N])
+# ----------------------------------------------------------------------------
+
+def test_q4k_special_cases():
+    N, K = 4, 512
+    one, half = 0x3C00, 0x3800
+    f = {"d": np.full((N, 2), one, np.uint16), "dmin": np.zeros((N, 2), np.uint16),
+         "sc": np.ones((N, 2, 8), np.uint8), "m": np.zeros((N, 2, 8), np.uint8),
+         "q": np.random.default_rng(5).integers(0, 16, (N, K), dtype=np.uint8)}
+    W = oracle.dequant_q4k(synth.q4k_encode(f), N, K, oracle.F16).view(np.float16)
+    assert np.array_equal(W.astype(np.float64), f["q"].T.astype(np.float64))  # w = q
+    # sub-block j covers k in [32j, 32j+32): scale j+1 on unit codes
+    f["q"][:] = 1
+    f["sc"][:] = np.arange(1, 9, dtype=np.uint8)
+    W = oracle.dequant_q4k(synth.q4k_encode(f), N, K, oracle.F16).view(np.float16)
+    assert np.array_equal(W[:, 0].astype(np.float64), (np.arange(K) % 256) // 32 + 1)
+    # q = 0: w = -dmin*m
+    f["q"][:] = 0
+    f["dmin"][:] = half
+    f["m"][:] = np.arange(8, dtype=np.uint8) * 3
+    W = oracle.dequant_q4k(synth.q4k_encode(f), N, K, oracle.BF16)
+    wv = oracle.bits_to_double_fast(W, oracle.BF16)
+    assert np.array_equal(wv[:, 2], -0.5 * 3 * ((np.arange(K) % 256) // 32))
+    # all codes and mins zero: exactly zero
+    f["m"][:] = 0
+    W = oracle.dequant_q4k(synth.q4k_encode(f), N, K, oracle.F16)
+    assert not np.any(W & 0x7FFF)
+
+
+def test_q6k_special_cases():
+    N, K = 3, 256
+    rng = np.random.default_rng(6)
+    f = {"d": np.full((N, 1), 0x3C00, np.uint16), "s": np.ones((N, 1, 16), np.int8),
+         "q": rng.integers(0, 64, (N, K), dtype=np.uint8)}
+    W = oracle.dequant_q6k(synth.q6k_encode(f), N, K, oracle.F16).view(np.float16)
+    assert np.array_equal(W.astype(np.float64), f["q"].T.astype(np.float64) - 32)  # w = q - 32
+    f["q"][:] = 33
+    f["s"][:] = (np.arange(16) - 8).astype(np.int8)
+    W = oracle.dequant_q6k(synth.q6k_encode(f), N, K, oracle.F16).view(np.float16)
+    assert np.array_equal(W[:, 1].astype(np.float64), np.arange(K) // 16 - 8)  # scale i covers [16i, 16i+16)
+
+
+def test_w4a16_special_cases():
+    N, K, g = 5, 256, 128
+    rng = np.random.default_rng(7)
+    f = synth.w4a16_fields(rng, N, K, g, symmetric=False)
+    f["zeros"][:] = f["codes"][:, ::g].T  # not equal to codes everywhere; set codes instead
+    codes = np.repeat(f["zeros"].T, g, axis=1)
+    W = oracle.dequant_w4a16(codes, f["scales"], f["zeros"], N, K, g, oracle.F16)
+    assert not np.any(W & 0x7FFF)  # q == zp gives zero
+    one = np.full_like(f["scales"], 0x3C00)
+    W = oracle.dequant_w4a16(f["codes"], one, None, N, K, g, oracle.BF16)
+    assert np.array_equal(oracle.bits_to_double_fast(W, oracle.BF16), f["codes"].T.astype(np.float64) - 8)
+    # group index: scale of group j applies to k in [g*j, g*j+g)
+    sc = np.zeros_like(f["scales"])
+    sc[0, :] = 0x3C00
+    sc[1, :] = 0x4000
+    W = oracle.dequant_w4a16(np.full((N, K), 9, np.uint8), sc, None, N, K, g, oracle.F16).view(np.float16)
+    assert np.array_equal(W[:, 0].astype(np.float64), np.where(np.arange(K) < g, 1.0, 2.0))
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16"])
+def test_array_walk_matches_scalar(fmt):
+    """Whole-matrix dequant places weight (k, n) at W[k][n]."""
+    rng = np.random.default_rng(8)
+    N, K = 6, 512
+    f = synth.weight_fields(fmt, rng, N, K, group=128)
+    enc = synth.encode(fmt, f)
+    W = oracle.dequant(fmt, enc, N, K, oracle.F16)
+    for n in range(N):
+        for k in rng.integers(0, K, 20):
+            b, kk = k // 256, k % 256
+            if fmt == "q4k":
+                want = oracle.q4k_weight(int(f["d"][n, b]), int(f["dmin"][n, b]), int(f["sc"][n, b, kk // 32]),
+                                         int(f["m"][n, b, kk // 32]), int(f["q"][n, k]), oracle.F16)
+            elif fmt == "q6k":
+                want = oracle.q6k_weight(int(f["d"][n, b]), int(f["s"][n, b, kk // 16]), int(f["q"][n, k]),
+                                         oracle.F16)
+            else:
+                want = oracle.w4a16_weight(int(f["scales"][k // 128, n]), int(f["codes"][n, k]),
+                                           int(f["zeros"][k // 128, n]), oracle.F16)
+            assert W[k, n] == want
+
+
+# ----------------------------------------------------------------------------
+# fp64 GEMM
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+@pytest.mark.parametrize("shape", [(1, 16, 256), (5, 48, 512), (17, 33, 384)])
+def test_gemm_matches_numpy(dtype, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(9)
+    X = synth.activations(rng, M, K, dtype)
+    W = synth.activations(rng, K, N, dtype)
+    Y, B = oracle.gemm(X, W, dtype)
+    xd = oracle.bits_to_double_fast(X, dtype)
+    wd = oracle.bits_to_double_fast(W, dtype)
+    assert np.allclose(Y, xd @ wd, rtol=1e-12, atol=1e-12)
+    assert np.allclose(B, np.abs(xd) @ np.abs(wd), rtol=1e-12, atol=1e-12)
+    r = rng.integers(0, M, 30)
+    c = rng.integers(0, N, 30)
+    Ya, Ba = oracle.gemm_at(X, W, dtype, r, c)
+    assert np.array_equal(Ya, Y[r, c]) and np.array_equal(Ba, B[r, c])
+
+
+def test_gemm_special_cases():
+    rng = np.random.default_rng(10)
+    K, N = 64, 24
+    W = synth.activations(rng, K, N, oracle.F16)
+    eye = synth.f16_bits(np.eye(K))
+    Y, _ = oracle.gemm(eye, W, oracle.F16)
+    assert np.array_equal(Y, oracle.bits_to_double_fast(W, oracle.F16))  # identity rows select W
+    ones = synth.f16_bits(np.ones((3, K)))
+    Y, _ = oracle.gemm(ones, W, oracle.F16)
+    colsum = oracle.bits_to_double_fast(W, oracle.F16).sum(axis=0)
+    assert np.allclose(Y, np.broadcast_to(colsum, Y.shape), rtol=1e-15, atol=1e-15)
+    Y, B = oracle.gemm(ones, np.zeros((K, N), np.uint16), oracle.F16)
+    assert not Y.any() and not B.any()
+
+
+def test_gemm_error_rule():
+    Yref = np.array([[1.0, 0.0], [2.0, -3.0]])
+    B = np.array([[10.0, 0.0], [4.0, 6.0]])
+    Yb = synth.f16_bits(np.array([[1.01, 0.0], [2.0, -3.0]]))
+    err, zero_ok = oracle.gemm_error(Yb, Yref, B, oracle.F16)
+    assert zero_ok and abs(err - abs(float(np.float16(1.01)) - 1.0) / 10.0) < 1e-12

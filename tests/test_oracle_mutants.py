@@ -1,0 +1,81 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies ``oracle/qref.c``, plants one mistake in the copy (a dropped
+term, a wrong sign, index or nibble, a transposed operand, a wrong tie rule),
+builds it, swaps it in for the real oracle and checks that at least one of
+the named pins in ``test_oracle.py`` now fails.  Nothing here touches a GPU.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import tests.test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "qref.c")
+
+MUTANTS = [
+    ("q4k nibble halves swapped", "q[64 * g + l] = b & 15;", "q[64 * g + l] = b >> 4;",
+     ["test_q4k_field_roundtrip", "test_q4k_special_cases"]),
+    ("q4k min term dropped", "xval v = rn_f32(a - b, e0);", "xval v = rn_f32(a, e0);",
+     ["test_q4k_special_cases"]),
+    ("q4k min sign flipped", "xval v = rn_f32(a - b, e0);", "xval v = rn_f32(a + b, e0);",
+     ["test_q4k_special_cases"]),
+    ("q4k high scale bits from the wrong byte", "((s12[j] >> 6) << 4));", "((s12[j + 4] >> 6) << 4));",
+     ["test_q4k_field_roundtrip"]),
+    ("q4k sub-block index off", "int j = k / 32;", "int j = k / 64;", ["test_q4k_special_cases"]),
+    ("q4k binary32 step skipped", "xval v = rn_f32(a - b, e0);", "xval v = {a - b, e0, 0, a < b};",
+     ["test_q4k_binary32_step"]),
+    ("q6k scale per 32 weights", "s[k / 16]", "s[k / 32]", ["test_q6k_special_cases"]),
+    ("q6k offset 31", "nd * s * (q - 32)", "nd * s * (q - 31)", ["test_q6k_special_cases"]),
+    ("q6k high pair shift", "(qh[32 * h + l] >> (2 * r)) & 3", "(qh[32 * h + l] >> r) & 3",
+     ["test_q6k_field_roundtrip"]),
+    ("w4a16 symmetric zero-point 7", "zeros[gi * N + n] : 8", "zeros[gi * N + n] : 7", ["test_w4a16_special_cases"]),
+    ("w4a16 group index by N", "int64_t gi = k / group;", "int64_t gi = (k + 1) / group;",
+     ["test_w4a16_special_cases"]),
+    ("gemm reversed K walk", "acc += xr[k] * wr[k];", "acc += xr[k] * wr[K - 1 - k];",
+     ["test_gemm_matches_numpy"]),
+    ("gemm bound signed", "bnd += fabs(xr[k]) * fabs(wr[k]);", "bnd += xr[k] * fabs(wr[k]);",
+     ["test_gemm_matches_numpy"]),
+    ("ties away from zero", "if (rem > half || (rem == half && (q & 1))) q++;", "if (rem >= half) q++;",
+     ["test_rn_f16_matches_numpy"]),
+    ("fp16 subnormal grid wrong", "static xval rn_f16(int64_t n, int e) { return round_exact(n, e, 11, -14, 15); }",
+     "static xval rn_f16(int64_t n, int e) { return round_exact(n, e, 11, -15, 15); }",
+     ["test_rn_f16_matches_numpy"]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, monkeypatch, name, old, new, catchers):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    mutant = tmp_path / "qref_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "libqref_mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w", "-o", str(lib),
+                           str(mutant), "-lm"])
+    monkeypatch.setattr(oracle, "_lib", oracle.load_library(str(lib)))
+    caught = []
+    for fn_name in catchers:
+        fn = getattr(pins, fn_name)
+        params = [oracle.F16, oracle.BF16] if "dtype" in fn.__code__.co_varnames[:fn.__code__.co_argcount] else [None]
+        for p in params:
+            try:
+                if p is None:
+                    if "shape" in fn.__code__.co_varnames[:fn.__code__.co_argcount]:
+                        fn(oracle.F16, (5, 48, 512))
+                    else:
+                        fn()
+                else:
+                    if "shape" in fn.__code__.co_varnames[:fn.__code__.co_argcount]:
+                        fn(p, (5, 48, 512))
+                    else:
+                        fn(p)
+            except (AssertionError, ValueError):
+                caught.append(fn_name)
+                break
+    assert caught, f"planted mistake '{name}' passed every pin in {catchers}"
