@@ -1,0 +1,214 @@
+"""Benchmark of the fused-dequant prefill linear layer on one MI355X.
+
+Default workload: one Qwen3-8B-shaped dense layer's seven linears at M = 658
+prompt tokens, fp16 activations (q/k/v/o/gate/up in Q4_K, down in Q6_K).  A
+step is one pass over the seven GEMMs with inputs already resident in HBM.
+
+Prints ONE JSON line: whole-step throughput in TFLOP/s (2*M*N*K summed over
+the seven linears / step time), the linear-only prefill rate, per-kernel
+times from HIP events, the roofline of the dominant kernel and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps 20] [--warmup 5] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import quantized_weight_prefill_amd as qg  # noqa: E402
+from quantized_weight_prefill_amd import synth  # noqa: E402
+
+METRIC = "fused Q4_K GEMM TFLOP/s + prefill tok/s (Qwen3-8B shapes, M=658); % roofline"
+PEAK_TFLOPS = {qg.F16: 2500.0, qg.BF16: 2500.0}  # dense MFMA, fp16 / bf16
+PEAK_HBM_GBPS = 8000.0
+BYTES_PER_WEIGHT = {"q4k": 144 / 256, "q6k": 210 / 256}
+
+
+def weight_bytes(fmt: str, N: int, K: int, group: int, sym: bool) -> float:
+    if fmt in BYTES_PER_WEIGHT:
+        return BYTES_PER_WEIGHT[fmt] * N * K
+    return N * K / 2 + (K // group) * N * 2 + (0 if sym else (K // group) * N / 2)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("qgemm.hip", "pack.cpp"):
+        with open(os.path.join(ROOT, "quantized_weight_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_layer_m658", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by N or K across GPUs, which is not built here)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    gemms = []
+    for j, (label, fmt, M, K, N, dt, group, sym) in enumerate(wl["gemms"]):
+        X, fields, enc = synth.workload_inputs(args.workload, j)
+        packed = qg.pack(fmt, enc, N, K)
+        tdt = torch.float16 if dt == qg.F16 else torch.bfloat16
+        x = torch.from_numpy(X.view(np.int16)).view(tdt).to(dev)
+        wp = torch.from_numpy(packed).to(dev)
+        y = torch.empty((M, N), dtype=tdt, device=dev)
+        info = qg.select_rung(fmt, M, N, K, dt)
+        gemms.append(dict(label=label, fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym, x=x, wp=wp, y=y,
+                          X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K,
+                          wbytes=weight_bytes(fmt, N, K, group or 128, sym)))
+        print(f"[bench] {label}: {fmt} M={M} K={K} N={N} rung={info['name']}", file=sys.stderr, flush=True)
+
+    def call(g):
+        if g["fmt"] == "q4k":
+            qg.q4k(g["x"], g["wp"], g["N"], out=g["y"])
+        elif g["fmt"] == "q6k":
+            qg.q6k(g["x"], g["wp"], g["N"], out=g["y"])
+        else:
+            qg.w4a16(g["x"], g["wp"], g["N"], g["group"], not g["sym"], out=g["y"])
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for g in gemms:
+            call(g)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events around every launch on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in gemms]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, g in enumerate(gemms):
+            ev[s][j][0].record(stream)
+            call(g)
+            ev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per = []
+    for j, g in enumerate(gemms):
+        ms = float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+        per.append(dict(label=g["label"], fmt=g["fmt"], M=g["M"], K=g["K"], N=g["N"], rung=g["rung"],
+                        ms=round(ms, 5), tflops=round(g["flops"] / ms / 1e9, 2),
+                        weight_gbps=round(g["wbytes"] / ms / 1e6, 1)))
+    flops_step = sum(g["flops"] for g in gemms)
+    kernel_ms_step = sum(p["ms"] for p in per)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel (largest share of the step) and its roofline
+    jd = int(np.argmax([p["ms"] for p in per]))
+    gd, pd = gemms[jd], per[jd]
+    intensity = gd["flops"] / (gd["wbytes"] + 2 * gd["M"] * gd["K"] + 2 * gd["M"] * gd["N"])
+    ridge = PEAK_TFLOPS[gd["dt"]] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": pd["tflops"], "peak": PEAK_TFLOPS[gd["dt"]], "unit": "TFLOP/s",
+                "frac": round(pd["tflops"] / PEAK_TFLOPS[gd["dt"]], 4)}
+    else:
+        gbps = (gd["wbytes"] + 2 * gd["M"] * gd["K"] + 2 * gd["M"] * gd["N"]) / (pd["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    roof["kernel"] = f"{gd['label']} ({gd['fmt']} M={gd['M']} K={gd['K']} N={gd['N']}, rung {gd['rung']})"
+    roof["traffic"] = measured_traffic(f"{args.workload}/{gd['label']}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if all(g["dt"] == qg.F16 for g in gemms) else "bf16" if all(g["dt"] == qg.BF16 for g in gemms) else "f16+bf16",
+        "data": "synthetic (seeded; shapes and value distributions of the workload, random weights)",
+        "config": {"workload": args.workload, "gemms": [f"{g['label']}:{g['fmt']}:{g['M']}x{g['K']}x{g['N']}"
+                                                       for g in gemms]},
+        "kernel_ms_per_step": round(kernel_ms_step, 5),
+        "per_kernel": per,
+        "roofline": roof,
+    }
+    if args.workload == "qwen3_8b_layer_m658":
+        # linear layers only: 36 layers x the seven projections of one layer
+        out["prefill_tok_s_linear_only"] = round(synth.QWEN3_8B_PROMPT / (synth.QWEN3_8B_LAYERS * ms_per_step * 1e-3), 1)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(gemms, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(gemms, target_s: float) -> dict:
+    """The oracle as it stands: full dequant of every weight of the step plus
+    the fp64 GEMM on a few rows of each linear, extrapolated linearly in M
+    (rows are independent), reported in the metric's unit."""
+    import oracle
+
+    t_deq = 0.0
+    Ws = []
+    for g in gemms:
+        t0 = time.perf_counter()
+        Ws.append(oracle.dequant(g["fmt"], g["enc"], g["N"], g["K"], g["dt"]))
+        t_deq += time.perf_counter() - t0
+    # calibrate rows so the GEMM part takes about target_s - t_deq seconds
+    t0 = time.perf_counter()
+    for g, W in zip(gemms, Ws):
+        oracle.gemm(g["X"][:1], W, g["dt"], want_bound=False)
+    t_one = time.perf_counter() - t0
+    rows = int(max(1, min(min(g["M"] for g in gemms), (target_s - t_deq) / max(t_one, 1e-6))))
+    t_gemm, full = 0.0, t_deq
+    for g, W in zip(gemms, Ws):
+        t0 = time.perf_counter()
+        oracle.gemm(g["X"][:rows], W, g["dt"], want_bound=False)
+        dt = time.perf_counter() - t0
+        t_gemm += dt
+        full += dt * g["M"] / rows
+    flops = sum(g["flops"] for g in gemms)
+    return {"value": round(flops / full / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"full dequant of all {len(gemms)} weights ({t_deq:.2f} s) + fp64 GEMM of the first {rows} "
+                      f"rows of each linear ({t_gemm:.2f} s), extrapolated linearly to all rows "
+                      f"(estimated {full:.1f} s per step)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,181 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) fused-dequant prefill linear layer
+ *
+ *     Y[M,N] = X[M,K] . dequant(W)[K,N]
+ *
+ * W is stored compressed: GGUF-style Q4_K or Q6_K super-blocks, or W4A16
+ * (4-bit codes with a group-wise fp16 scale and 4-bit zero-point).  The
+ * kernels read every packed weight byte from HBM once per output tile,
+ * unpack it in registers and feed it to fp16/bf16 MFMA with fp32
+ * accumulation; no dequantized copy of W is ever written to memory (the
+ * dequant-scratch post, "The two passes hiding inside one matmul": the fused
+ * form moves 0.5625 bytes per Q4_K weight instead of 4.5625).
+ *
+ * Conventions for every entry point
+ *   - Plain pointers and sizes only.  Device pointers must come from the HIP
+ *     allocator of the current device; host pointers are ordinary memory.
+ *     The caller owns every buffer.  The library allocates no device memory,
+ *     never synchronises the stream and keeps no mutable global state, so
+ *     calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     GEMM and dequant calls are asynchronous on that stream.
+ *   - dtype: QGEMM_F16 or QGEMM_BF16.  X and Y have that type; the weights are
+ *     unpacked into it (the MFMA operand type).
+ *   - X is row-major [M][K] contiguous, Y is row-major [M][N] contiguous.
+ *     X, Y and Wpacked must be 16-byte aligned; Y must not alias X or W.
+ *   - Return value: QGEMM_OK (0) or a negative status.  Argument errors are
+ *     found before any launch and leave Y untouched.  A failed launch returns
+ *     QGEMM_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as with any HIP launch.  An unsupported format or
+ *     dtype is an error, never a silent fallback.
+ *
+ * Unpacked weight values (bit-exact contract)
+ *   Q4_K : w = RN_t( RN_32( d*sc*q - dmin*m ) )      (sc, m: 6-bit; q: 4-bit)
+ *   Q6_K : w = RN_t( d*s*(q - 32) )                  (s: int8 per 16; q: 6-bit)
+ *   W4A16: w = RN_t( s*(q - zp) )                    (zp = 8 when has_zp == 0)
+ *   RN_32 is one round-to-nearest-even into binary32 (the batched-prefill
+ *   post forms factor*q - bias in float, "The fix: K-parallel batched DMMV");
+ *   RN_t is round-to-nearest-even into fp16/bf16.  For Q6_K and W4A16 the
+ *   exact value always fits binary32.  The products are accumulated in fp32;
+ *   the order of that accumulation is unspecified (it depends on the rung).
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define QGEMM_OK 0
+#define QGEMM_ERR_NULL (-1)   /* a required pointer is NULL                  */
+#define QGEMM_ERR_SHAPE (-2)  /* M < 0, N < 1, K not a legal multiple, ...   */
+#define QGEMM_ERR_DTYPE (-3)  /* dtype is not QGEMM_F16 / QGEMM_BF16         */
+#define QGEMM_ERR_ALIGN (-4)  /* a pointer is not 16-byte aligned            */
+#define QGEMM_ERR_FORMAT (-5) /* unknown format, group size or rung          */
+#define QGEMM_ERR_SIZE (-6)   /* an output buffer is too small               */
+#define QGEMM_ERR_HIP (-7)    /* the HIP launch failed                       */
+#define QGEMM_ERR_INPUT (-8)  /* malformed input data (e.g. code above 15)   */
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *qgemm_status_str(int status);
+
+/* ---- enumerations -------------------------------------------------------- */
+#define QGEMM_F16 0
+#define QGEMM_BF16 1
+
+#define QGEMM_FMT_Q4K 0
+#define QGEMM_FMT_Q6K 1
+#define QGEMM_FMT_W4A16 2
+
+/* ---- packed layout (what the packers write and the kernels read) --------
+ *
+ * Output columns are grouped in panels of 16; Np = ceil(N/16).  Columns past
+ * N inside the last panel are zero-filled and never stored to Y.  Inside a
+ * panel everything is arranged so that one wave's 64 lanes x 16-byte loads
+ * cover 1 KB of contiguous memory, and each lane's 16 bytes are the 32 codes
+ * of one (column, 32-wide K run): the codes of one sub-block.
+ *
+ * "Pair order" of a 16-byte code run (32 codes, k = k0 .. k0+31): 32-bit word
+ * i holds codes k0+8i .. k0+8i+7; code k0+8i+2p sits at bits [4p, 4p+4) and
+ * code k0+8i+2p+1 at bits [16+4p, 20+4p), p = 0..3 (the ExLlama shuffle of
+ * the W4A16 PR, section 1: one mask yields both halves of an fp16 pair).
+ *
+ * Q4_K: one 2304-byte record per (panel p, super-block b), record index
+ *   p*(K/256) + b.  Bytes [0,256): the 16 columns' block headers (fp16 d,
+ *   fp16 dmin, the 12 bytes of 6-bit scales/mins, exactly as in the GGUF
+ *   block), column c at 16*c.  Bytes [256,2304): codes, half h (k 128h ..
+ *   128h+127 of the block) at 256 + 1024*h, then sub-block g of that half and
+ *   column c at (16*g + c)*16, in pair order.          (144 bytes / 256 w)
+ * Q6_K: one 3360-byte record per (panel, super-block).  [0,32): the fp16 d
+ *   of columns 0..15; [32,288): their 16 int8 scales (16 bytes per column);
+ *   [288,2336): low code nibbles laid out as the Q4_K codes; [2336,3360):
+ *   high 2-bit pairs, half h at 2336 + 512*h, sub-block g and column c at
+ *   (16*g + c)*8: two 32-bit words, word e for codes k0+16e .. k0+16e+15;
+ *   code k0+8i+2p+t (i = 2e+u, t = 0/1) has its top two bits at bit
+ *   16*t + 2*(4u+p) of word e.                          (210 bytes / 256 w)
+ * W4A16: codes first: one 1024-byte run per (panel, 128-wide K chunk),
+ *   index p*(K/128) + c, group g and column c at (16*g + c)*16, pair order.
+ *   Then fp16 scales [Np][K/group][16], then (has_zp only) zero-points
+ *   [Np][K/group][8 bytes], column c in the nibble c (low nibble first).
+ */
+
+/* ---- host-side packers (host memory in, host memory out) -----------------
+ * blocks: [N][K/256] GGUF-style blocks, column n's blocks contiguous along K
+ * (Q4_K: 144 B = fp16 d, fp16 dmin, 12 B scales/mins, 128 B codes; Q6_K:
+ * 210 B = 128 B ql, 64 B qh, 16 B int8 scales, fp16 d).  K % 256 == 0.
+ * *_packed_bytes returns 0 for an illegal shape.  pack returns
+ * QGEMM_ERR_SIZE when out_bytes is smaller than *_packed_bytes.  unpack is
+ * the exact inverse (for tests and for exporting packed weights). */
+size_t qgemm_q4k_packed_bytes(int64_t N, int64_t K);
+int qgemm_q4k_pack(const void *blocks, int64_t N, int64_t K, void *out, size_t out_bytes);
+int qgemm_q4k_unpack(const void *packed, int64_t N, int64_t K, void *blocks, size_t blocks_bytes);
+
+size_t qgemm_q6k_packed_bytes(int64_t N, int64_t K);
+int qgemm_q6k_pack(const void *blocks, int64_t N, int64_t K, void *out, size_t out_bytes);
+int qgemm_q6k_unpack(const void *packed, int64_t N, int64_t K, void *blocks, size_t blocks_bytes);
+
+/* W4A16 (GPTQ-style, the W4A16 PR, section 1): codes [N][K], one 4-bit code
+ * (0..15) per byte; scales [K/group][N] fp16 bits; zeros [K/group][N]
+ * (0..15) or NULL for the symmetric variant (zero-point 8, and then no
+ * zero-point bytes are stored).  K % 128 == 0, group % 32 == 0,
+ * K % group == 0.  Codes or zeros above 15 give QGEMM_ERR_INPUT. */
+size_t qgemm_w4a16_packed_bytes(int64_t N, int64_t K, int64_t group_size, int has_zp);
+int qgemm_w4a16_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
+                     int64_t group_size, void *out, size_t out_bytes);
+int qgemm_w4a16_unpack(const void *packed, int64_t N, int64_t K, int64_t group_size, int has_zp, uint8_t *codes,
+                       uint16_t *scales, uint8_t *zeros);
+
+/* ---- fused-dequant GEMMs (device memory, asynchronous on `stream`) ------- */
+
+/* Q4_K weights (the batched-prefill post's Q4_K kpar path; the dequant-scratch
+ * post's fused GEMM).  K % 256 == 0, M >= 0 (M == 0 is a no-op), N >= 1. */
+int qgemm_q4k(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N, int64_t K, int dtype,
+              void *stream);
+
+/* Q6_K weights (the batched-prefill post, "Bug 2": ffn_down / attn_v of a
+ * Q4_K_M checkpoint).  Same preconditions as qgemm_q4k. */
+int qgemm_q6k(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N, int64_t K, int dtype,
+              void *stream);
+
+/* W4A16 weights (the W4A16 PR, sections 1 and 2).  K % 128 == 0,
+ * group_size % 32 == 0, K % group_size == 0; has_zp selects the asymmetric
+ * (stored zero-points) or symmetric (zero-point 8) variant and must match
+ * the packing. */
+int qgemm_w4a16(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                int has_zp, int dtype, void *stream);
+
+/* ---- tile selection and forced rungs (tests and benchmarks) -------------
+ * The M-ladder (the W4A16 PR, section 2: a tile per M bucket and dtype, with
+ * a K block that never straddles a quantization group) maps (format, M, N,
+ * K, dtype) to a rung.  qgemm_select_rung writes 8 integers:
+ *   [0] rung id  [1] rows per tile  [2] columns per tile  [3] K per step
+ *   [4] waves per workgroup  [5] K-split ways inside a workgroup
+ *   [6] grid x  [7] grid y
+ * and returns QGEMM_OK, or an error for an illegal shape. */
+int qgemm_num_rungs(void);
+const char *qgemm_rung_name(int rung); /* NULL for an unknown rung */
+int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
+int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
+
+/* Same as the format entry points, with the rung forced (rung = -1 selects
+ * as qgemm_q4k/q6k/w4a16 do).  group_size/has_zp are ignored for k-quants. */
+int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N,
+                    int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+
+/* ---- staged dequant (the two-pass form of the dequant-scratch post) -------
+ * Writes the unpacked weights as logical Wout[K][N] (row-major, dtype
+ * elements) with the same device unpack code the GEMMs use.  The fused
+ * GEMMs never call it; it exists to check the unpack bit for bit and to
+ * measure the staged traffic the fused form avoids. */
+int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
+                  int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,312 @@
+"""MI355X (gfx950) fused-dequant prefill linear layer: Python binding.
+
+    Y[M,N] = X[M,K] . dequant(W)[K,N]
+
+This module only marshals arguments for the C ABI of ``include/qgemm.h``
+(``libqgemm.so``, built by ``python -m quantized_weight_prefill_amd.build``):
+PyTorch supplies device memory and the current stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or the call fails, an exception is raised.
+
+Functions keep the C names without the ``qgemm_`` prefix:
+
+* packers (host, numpy): :func:`q4k_pack`, :func:`q6k_pack`,
+  :func:`w4a16_pack` and their inverses ``*_unpack``;
+* GEMMs (device, torch): :func:`q4k`, :func:`q6k`, :func:`w4a16`,
+  :func:`gemm_rung`;
+* the staged dequant :func:`dequant` and the M-ladder queries
+  :func:`select_rung`, :func:`rung_info`, :func:`rung_name`, :func:`num_rungs`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqgemm.so")
+
+F16 = 0
+BF16 = 1
+FMT_Q4K = 0
+FMT_Q6K = 1
+FMT_W4A16 = 2
+FORMATS = {"q4k": FMT_Q4K, "q6k": FMT_Q6K, "w4a16": FMT_W4A16}
+
+#: status codes of include/qgemm.h
+STATUS = {0: "QGEMM_OK", -1: "QGEMM_ERR_NULL", -2: "QGEMM_ERR_SHAPE", -3: "QGEMM_ERR_DTYPE",
+          -4: "QGEMM_ERR_ALIGN", -5: "QGEMM_ERR_FORMAT", -6: "QGEMM_ERR_SIZE", -7: "QGEMM_ERR_HIP",
+          -8: "QGEMM_ERR_INPUT"}
+
+_lib = None
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _lib.qgemm_status_str(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+
+
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+#: exported symbol -> (restype, argtypes); the tests check this against the header
+SIGNATURES = {
+    "qgemm_status_str": (ctypes.c_char_p, [_INT]),
+    "qgemm_q4k_packed_bytes": (_SZ, [_I64, _I64]),
+    "qgemm_q4k_pack": (_INT, [_VP, _I64, _I64, _VP, _SZ]),
+    "qgemm_q4k_unpack": (_INT, [_VP, _I64, _I64, _VP, _SZ]),
+    "qgemm_q6k_packed_bytes": (_SZ, [_I64, _I64]),
+    "qgemm_q6k_pack": (_INT, [_VP, _I64, _I64, _VP, _SZ]),
+    "qgemm_q6k_unpack": (_INT, [_VP, _I64, _I64, _VP, _SZ]),
+    "qgemm_w4a16_packed_bytes": (_SZ, [_I64, _I64, _I64, _INT]),
+    "qgemm_w4a16_pack": (_INT, [_VP, _VP, _VP, _I64, _I64, _I64, _VP, _SZ]),
+    "qgemm_w4a16_unpack": (_INT, [_VP, _I64, _I64, _I64, _INT, _VP, _VP, _VP]),
+    "qgemm_q4k": (_INT, [_VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
+    "qgemm_q6k": (_INT, [_VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
+    "qgemm_w4a16": (_INT, [_VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_num_rungs": (_INT, []),
+    "qgemm_rung_name": (ctypes.c_char_p, [_INT]),
+    "qgemm_select_rung": (_INT, [_INT, _I64, _I64, _I64, _INT, _VP]),
+    "qgemm_rung_info": (_INT, [_INT, _INT, _I64, _I64, _I64, _INT, _VP]),
+    "qgemm_gemm_rung": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
+}
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with `python -m quantized_weight_prefill_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise QGemmError(fn, status)
+
+
+def _np_ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# ---------------------------------------------------------------------------
+# host packers
+# ---------------------------------------------------------------------------
+
+def q4k_packed_bytes(N: int, K: int) -> int:
+    return int(lib().qgemm_q4k_packed_bytes(N, K))
+
+
+def q6k_packed_bytes(N: int, K: int) -> int:
+    return int(lib().qgemm_q6k_packed_bytes(N, K))
+
+
+def w4a16_packed_bytes(N: int, K: int, group: int, has_zp: bool) -> int:
+    return int(lib().qgemm_w4a16_packed_bytes(N, K, group, int(bool(has_zp))))
+
+
+def q4k_pack(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
+    """GGUF-style Q4_K blocks [N][K/256][144] -> packed panel layout (uint8)."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    out = np.empty(q4k_packed_bytes(N, K), np.uint8)
+    _check("qgemm_q4k_pack", lib().qgemm_q4k_pack(_np_ptr(b), N, K, _np_ptr(out), out.nbytes))
+    return out
+
+
+def q4k_unpack(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    out = np.empty((N, K // 256, 144), np.uint8)
+    _check("qgemm_q4k_unpack", lib().qgemm_q4k_unpack(_np_ptr(p), N, K, _np_ptr(out), out.nbytes))
+    return out
+
+
+def q6k_pack(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
+    """GGUF-style Q6_K blocks [N][K/256][210] -> packed panel layout (uint8)."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    out = np.empty(q6k_packed_bytes(N, K), np.uint8)
+    _check("qgemm_q6k_pack", lib().qgemm_q6k_pack(_np_ptr(b), N, K, _np_ptr(out), out.nbytes))
+    return out
+
+
+def q6k_unpack(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    out = np.empty((N, K // 256, 210), np.uint8)
+    _check("qgemm_q6k_unpack", lib().qgemm_q6k_unpack(_np_ptr(p), N, K, _np_ptr(out), out.nbytes))
+    return out
+
+
+def w4a16_pack(codes: np.ndarray, scales: np.ndarray, zeros, N: int, K: int, group: int) -> np.ndarray:
+    """codes [N][K] (0..15), fp16 scale bits [K/g][N], zeros [K/g][N] or None."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    z = None if zeros is None else np.ascontiguousarray(zeros, dtype=np.uint8)
+    out = np.empty(w4a16_packed_bytes(N, K, group, z is not None), np.uint8)
+    _check("qgemm_w4a16_pack", lib().qgemm_w4a16_pack(_np_ptr(c), _np_ptr(s), None if z is None else _np_ptr(z),
+                                                      N, K, group, _np_ptr(out), out.nbytes))
+    return out
+
+
+def w4a16_unpack(packed: np.ndarray, N: int, K: int, group: int, has_zp: bool):
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((K // group, N), np.uint16)
+    zeros = np.empty((K // group, N), np.uint8) if has_zp else None
+    _check("qgemm_w4a16_unpack", lib().qgemm_w4a16_unpack(_np_ptr(p), N, K, group, int(bool(has_zp)), _np_ptr(codes),
+                                                          _np_ptr(scales), None if zeros is None else _np_ptr(zeros)))
+    return codes, scales, zeros
+
+
+def pack(fmt: str, enc, N: int, K: int) -> np.ndarray:
+    """Pack the output of the synthetic generator's ``encode`` for ``fmt``."""
+    if fmt == "q4k":
+        return q4k_pack(enc, N, K)
+    if fmt == "q6k":
+        return q6k_pack(enc, N, K)
+    if fmt == "w4a16":
+        return w4a16_pack(enc["codes"], enc["scales"], None if enc["symmetric"] else enc["zeros"], N, K,
+                          enc["group"])
+    raise ValueError(fmt)
+
+
+# ---------------------------------------------------------------------------
+# device calls
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _out(x, N, out):
+    torch = _torch()
+    M = x.shape[0]
+    if out is None:
+        return torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if out.shape != (M, N) or out.dtype != x.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    return out
+
+
+def gemm_rung(fmt, rung: int, x, wp, N: int, group: int = 0, has_zp: bool = False, out=None, stream=None):
+    """Y = X . dequant(W) with the rung forced (rung = -1 selects as the format calls do)."""
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    y = _out(x, N, out)
+    st = lib().qgemm_gemm_rung(f, rung, _dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, group,
+                               int(bool(has_zp)), _dtype_code(x), _stream(stream))
+    _check("qgemm_gemm_rung", st)
+    return y
+
+
+def q4k(x, wp, N: int, out=None, stream=None):
+    """Y[M,N] = X[M,K] . dequant_Q4_K(W)."""
+    M, K = x.shape
+    y = _out(x, N, out)
+    st = lib().qgemm_q4k(_dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, _dtype_code(x), _stream(stream))
+    _check("qgemm_q4k", st)
+    return y
+
+
+def q6k(x, wp, N: int, out=None, stream=None):
+    """Y[M,N] = X[M,K] . dequant_Q6_K(W)."""
+    M, K = x.shape
+    y = _out(x, N, out)
+    st = lib().qgemm_q6k(_dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, _dtype_code(x), _stream(stream))
+    _check("qgemm_q6k", st)
+    return y
+
+
+def w4a16(x, wp, N: int, group: int, has_zp: bool, out=None, stream=None):
+    """Y[M,N] = X[M,K] . dequant_W4A16(W) (group-wise scale, zero-point or 8)."""
+    M, K = x.shape
+    y = _out(x, N, out)
+    st = lib().qgemm_w4a16(_dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, group, int(bool(has_zp)),
+                           _dtype_code(x), _stream(stream))
+    _check("qgemm_w4a16", st)
+    return y
+
+
+def dequant(fmt, wp, N: int, K: int, dtype, group: int = 0, has_zp: bool = False, stream=None):
+    """Staged dequant: logical W[K][N] in fp16/bf16 written by the device unpack."""
+    torch = _torch()
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    code = F16 if dtype in (F16, torch.float16) else BF16
+    tdt = torch.float16 if code == F16 else torch.bfloat16
+    w = torch.empty((K, N), dtype=tdt, device=wp.device)
+    st = lib().qgemm_dequant(f, _dev(wp, "wp"), _dev(w, "out"), N, K, group, int(bool(has_zp)), code,
+                             _stream(stream))
+    _check("qgemm_dequant", st)
+    return w
+
+
+# ---------------------------------------------------------------------------
+# M-ladder queries
+# ---------------------------------------------------------------------------
+
+_INFO_KEYS = ("rung", "rows", "cols", "k_step", "waves", "k_split", "grid_x", "grid_y")
+
+
+def num_rungs() -> int:
+    return int(lib().qgemm_num_rungs())
+
+
+def rung_name(rung: int):
+    r = lib().qgemm_rung_name(rung)
+    return None if r is None else r.decode()
+
+
+def select_rung(fmt, M: int, N: int, K: int, dtype: int = F16) -> dict:
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    info = np.zeros(8, np.int32)
+    _check("qgemm_select_rung", lib().qgemm_select_rung(f, M, N, K, dtype, _np_ptr(info)))
+    d = dict(zip(_INFO_KEYS, (int(v) for v in info)))
+    d["name"] = rung_name(d["rung"])
+    return d
+
+
+def rung_info(rung: int, fmt, M: int, N: int, K: int, dtype: int = F16) -> dict:
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    info = np.zeros(8, np.int32)
+    _check("qgemm_rung_info", lib().qgemm_rung_info(rung, f, M, N, K, dtype, _np_ptr(info)))
+    d = dict(zip(_INFO_KEYS, (int(v) for v in info)))
+    d["name"] = rung_name(d["rung"])
+    return d

@@ -1,0 +1,721 @@
+// qgemm.hip -- fused-dequant prefill GEMM for MI355X (gfx950, CDNA4) and the
+// C ABI around it (declared in include/qgemm.h).
+//
+//   Y[M,N] = X[M,K] . dequant(W)[K,N]
+//
+// The weights arrive in the panel layout written by pack.cpp: 16 output
+// columns per panel, and for every (column, 32-wide K run) 16 contiguous
+// bytes of 4-bit codes in "pair order".  One lane turns such a run into four
+// MFMA operand fragments of eight fp16/bf16 values with no shuffles:
+//
+//   * the two codes of a pair are 16 bits apart, so one AND with 0x000F000F
+//     (or 0x00F000F0 for the next pair, read as 16*code) leaves two fp16
+//     bit patterns whose value is code * 2^-24 -- the zero-exponent variant
+//     of the 0x6400|n trick of the W4A16 PR (section 1), which needs no
+//     subtraction of 1024 afterwards;
+//   * one mixed-precision FMA per weight (fp16 input, binary32 arithmetic,
+//     v_fma_mix) forms factor*q - bias exactly as the batched-prefill post's
+//     shader does ("The fix: K-parallel batched DMMV"), with factor scaled by
+//     2^24 to cancel the code's scale, and rounds it to the operand type.
+//
+// Every product d*sc, dmin*m, d*s, s*zp is exact in binary32, so each weight
+// is RN_t(RN_32(exact)), bit-identical to the CPU oracle.
+//
+// MFMA operands are used "transposed": the weight fragment is the A operand
+// and the activation fragment the B operand, so the 16x16 accumulator of one
+// v_mfma_f32_16x16x32 holds Y^T and each lane ends with four consecutive
+// output columns of one row (one 8-byte store).  The K order inside one MFMA
+// is a free permutation as long as both operands agree: lane (r, g) of
+// MFMA i carries k = 128*chunk + 32*g + 8*i + 0..7 in both operands, so the
+// lane that owns the 32 codes of sub-block g feeds all four MFMAs of a chunk.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qgemm.h"
+
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum { FMT_Q4K = QGEMM_FMT_Q4K, FMT_Q6K = QGEMM_FMT_Q6K, FMT_W4 = QGEMM_FMT_W4A16 };
+enum { DT_F16 = QGEMM_F16, DT_BF16 = QGEMM_BF16 };
+
+constexpr int kChunk = 128;  // K per step: four 32-wide runs, one per lane group
+constexpr int kQ4kRec = 2304, kQ6kRec = 3360;
+constexpr float kTwo24 = 16777216.0f;
+
+struct Args {
+    const uint16_t *X;
+    const uint8_t *W;
+    uint16_t *Y;
+    int M, N, K;
+    int np;      // panels of 16 columns
+    int group;   // W4A16 group size
+    int has_zp;  // W4A16 asymmetric
+    int kw;      // direct kernel: waves splitting K inside a workgroup
+    long long w4_sreg, w4_zreg;  // W4A16 byte offsets of the scale / zero regions
+};
+
+// ---------------------------------------------------------------------------
+// Unpack primitives
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// t holds two codes as fp16 bit patterns of value code*2^-24 each.  Returns
+// the operand pair RN_t(fma(code_lo*2^-24, fa, nb)), RN_t(fma(code_hi*2^-24,
+// fa, nb)), the FMA in binary32 (v_fma_mix on gfx950).
+template <int DT>
+__device__ __forceinline__ uint32_t dq_pair(uint32_t t, float fa, float nb);
+
+template <>
+__device__ __forceinline__ uint32_t dq_pair<DT_F16>(uint32_t t, float fa, float nb)
+{
+    f16x2 h = __builtin_bit_cast(f16x2, t);
+    float a = __builtin_fmaf((float)h.x, fa, nb);
+    float b = __builtin_fmaf((float)h.y, fa, nb);
+    f16x2 r = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <>
+__device__ __forceinline__ uint32_t dq_pair<DT_BF16>(uint32_t t, float fa, float nb)
+{
+    f16x2 h = __builtin_bit_cast(f16x2, t);
+    float a = __builtin_fmaf((float)h.x, fa, nb);
+    float b = __builtin_fmaf((float)h.y, fa, nb);
+    bf16x2 r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 32 four-bit codes in pair order -> four fragments of eight weights.
+// fa = factor * 2^24 and nb = -bias apply to all 32.
+template <int DT>
+__device__ __forceinline__ void unpack_run4(u32x4 codes, float fa, float nb, u32x4 (&out)[4])
+{
+    const float fa16 = fa * 0.0625f;  // for the pairs read as 16*code
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t x = codes[i], x8 = x >> 8;
+        out[i][0] = dq_pair<DT>(x & 0x000F000Fu, fa, nb);
+        out[i][1] = dq_pair<DT>(x & 0x00F000F0u, fa16, nb);
+        out[i][2] = dq_pair<DT>(x8 & 0x000F000Fu, fa, nb);
+        out[i][3] = dq_pair<DT>(x8 & 0x00F000F0u, fa16, nb);
+    }
+}
+
+// 32 six-bit Q6_K codes: low nibbles in pair order plus the high pairs.
+// Codes 0..15 use (fa0, nb0), codes 16..31 use (fa1, nb1).
+template <int DT>
+__device__ __forceinline__ void unpack_run6(u32x4 lo, u32x2 hi, float fa0, float nb0, float fa1, float nb1,
+                                            u32x4 (&out)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float fa = i < 2 ? fa0 : fa1, nb = i < 2 ? nb0 : nb1;
+        const float fa16 = fa * 0.0625f;
+        const uint32_t x = lo[i], x8 = x >> 8, h = hi[i >> 1];
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const uint32_t lpart = (p < 2 ? x : x8) & ((p & 1) ? 0x00F000F0u : 0x000F000Fu);
+            const int sigma = 4 * (i & 1) + p, T = (p & 1) ? 8 : 4, sh = 2 * sigma - T;
+            const uint32_t hs = sh >= 0 ? (h >> sh) : (h << (-sh));
+            const uint32_t t = lpart | (hs & (0x00030003u << T));
+            out[i][p] = dq_pair<DT>(t, (p & 1) ? fa16 : fa, nb);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-unit loads: panel p, chunk c (128 K), lane group g (32-wide run), column
+// col of the panel.
+// ---------------------------------------------------------------------------
+
+template <int FMT>
+struct Unit {
+    u32x4 codes;
+    u32x4 hd;    // Q4_K: d|dmin, 3 words of 6-bit scales; Q6_K: 16 int8 scales
+    u32x2 hi;    // Q6_K high pairs
+    uint32_t aux;  // Q6_K: d bits; W4A16: scale bits | zero-point << 16
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_unit(const Args &a, int p, int c, int g, int col, Unit<FMT> &u)
+{
+    if constexpr (FMT == FMT_Q4K) {
+        const uint8_t *rec = a.W + ((long long)p * (a.K >> 8) + (c >> 1)) * kQ4kRec;
+        u.hd = *(const u32x4 *)(rec + 16 * col);
+        u.codes = *(const u32x4 *)(rec + 256 + 1024 * (c & 1) + (16 * g + col) * 16);
+    } else if constexpr (FMT == FMT_Q6K) {
+        const uint8_t *rec = a.W + ((long long)p * (a.K >> 8) + (c >> 1)) * kQ6kRec;
+        u.aux = *(const uint16_t *)(rec + 2 * col);
+        u.hd = *(const u32x4 *)(rec + 32 + 16 * col);
+        u.codes = *(const u32x4 *)(rec + 288 + 1024 * (c & 1) + (16 * g + col) * 16);
+        u.hi = *(const u32x2 *)(rec + 2336 + 512 * (c & 1) + (16 * g + col) * 8);
+    } else {
+        u.codes = *(const u32x4 *)(a.W + ((long long)p * (a.K >> 7) + c) * 1024 + (16 * g + col) * 16);
+        const int ng = a.K / a.group;
+        const int j = (kChunk * c + 32 * g) / a.group;
+        const long long gi = (long long)p * ng + j;
+        uint32_t s = *(const uint16_t *)(a.W + a.w4_sreg + gi * 32 + 2 * col);
+        uint32_t zp = 8;
+        if (a.has_zp) zp = (a.W[a.w4_zreg + gi * 8 + (col >> 1)] >> (4 * (col & 1))) & 15u;
+        u.aux = s | (zp << 16);
+    }
+}
+
+template <int FMT, int DT>
+__device__ __forceinline__ void unpack_unit(const Unit<FMT> &u, int c, int g, u32x4 (&out)[4])
+{
+    if constexpr (FMT == FMT_Q4K) {
+        const float d = f16_to_f32(u.hd[0] & 0xFFFFu), dmin = f16_to_f32(u.hd[0] >> 16);
+        const uint32_t s0 = u.hd[1], s1 = u.hd[2], s2 = u.hd[3];
+        const int sh = 8 * g;
+        uint32_t sc, m;
+        if ((c & 1) == 0) {  // sub-blocks 0..3: low six bits of bytes 0..3 / 4..7
+            sc = (s0 >> sh) & 63u;
+            m = (s1 >> sh) & 63u;
+        } else {             // sub-blocks 4..7: nibbles of bytes 8..11 + top two bits
+            sc = ((s2 >> sh) & 15u) | (((s0 >> (sh + 6)) & 3u) << 4);
+            m = ((s2 >> (sh + 4)) & 15u) | (((s1 >> (sh + 6)) & 3u) << 4);
+        }
+        const float fa = d * (float)sc * kTwo24;  // factor = d*sc, exact in binary32
+        const float nb = -(dmin * (float)m);      // bias = dmin*m, exact
+        unpack_run4<DT>(u.codes, fa, nb, out);
+    } else if constexpr (FMT == FMT_Q6K) {
+        const float d = f16_to_f32(u.aux);
+        const uint32_t w = u.hd[2 * (c & 1) + (g >> 1)];
+        const int sh = 16 * (g & 1);
+        const float a0 = d * (float)(int)(int8_t)((w >> sh) & 0xFFu);  // exact
+        const float a1 = d * (float)(int)(int8_t)((w >> (sh + 8)) & 0xFFu);
+        unpack_run6<DT>(u.codes, u.hi, a0 * kTwo24, -32.0f * a0, a1 * kTwo24, -32.0f * a1, out);
+    } else {
+        const float s = f16_to_f32(u.aux & 0xFFFFu);
+        const float zp = (float)(u.aux >> 16);
+        unpack_run4<DT>(u.codes, s * kTwo24, -(zp * s), out);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c);
+
+template <>
+__device__ __forceinline__ f32x4 mma<DT_F16>(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4 mma<DT_BF16>(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack_out(float a, float b)
+{
+    if constexpr (DT == DT_F16) {
+        f16x2 r = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, r);
+    } else {
+        bf16x2 r = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, r);
+    }
+}
+
+// Store one 16x16 accumulator (Y^T layout): lane holds rows m, columns
+// n0 .. n0+3 with m = m_base + lane%16, n0 = n_base + 4*(lane/16).
+template <int DT>
+__device__ __forceinline__ void store_block(const Args &a, f32x4 v, int m_base, int n_base, int lane)
+{
+    const int m = m_base + (lane & 15);
+    const int n0 = n_base + 4 * (lane >> 4);
+    if (m >= a.M || n0 >= a.N) return;
+    uint16_t *y = a.Y + (long long)m * a.N + n0;
+    const uint32_t lo = pack_out<DT>(v[0], v[1]), hi = pack_out<DT>(v[2], v[3]);
+    if (n0 + 4 <= a.N && (a.N & 3) == 0) {
+        *(u32x2 *)y = u32x2{lo, hi};
+    } else {
+        const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+        for (int j = 0; j < 4 && n0 + j < a.N; j++) y[j] = e[j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Direct kernel: decode-adjacent M and skinny N.
+//
+// Each wave unpacks its weight fragments straight into VGPRs and reuses them
+// for RB row blocks of 16 tokens; the a.kw waves of a workgroup split the K
+// loop (the K-parallel shape of the batched-prefill post: many lanes share a
+// row reduction, then one reduction per output at the end) and combine their
+// partial sums through LDS.  Grid: x = panel groups of PN panels, y = row
+// groups of 16*RB rows.
+// ---------------------------------------------------------------------------
+template <int FMT, int DT, int RB, int PN>
+__global__ void __launch_bounds__(512) k_direct(Args a)
+{
+    extern __shared__ f32x4 red[];  // [kw][PN*RB][64]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int p0 = blockIdx.x * PN;
+    const int m0 = blockIdx.y * (16 * RB);
+    const int nch = a.K / kChunk;
+    const int cb = (int)((long long)nch * w / a.kw), ce = (int)((long long)nch * (w + 1) / a.kw);
+
+    f32x4 acc[PN][RB];
+#pragma unroll
+    for (int pn = 0; pn < PN; pn++)
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) acc[pn][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t *xrow[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) {
+        int r = m0 + 16 * rb + col;
+        r = r < a.M ? r : a.M - 1;  // clamped rows are computed and discarded
+        xrow[rb] = a.X + (long long)r * a.K + 32 * g;
+    }
+
+    for (int c = cb; c < ce; c++) {
+        u32x4 wf[PN][4];
+#pragma unroll
+        for (int pn = 0; pn < PN; pn++) {
+            int p = p0 + pn;
+            p = p < a.np ? p : a.np - 1;
+            Unit<FMT> u;
+            load_unit<FMT>(a, p, c, g, col, u);
+            unpack_unit<FMT, DT>(u, c, g, wf[pn]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) {
+            u32x4 xf[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) xf[i] = *(const u32x4 *)(xrow[rb] + kChunk * c + 8 * i);
+#pragma unroll
+            for (int pn = 0; pn < PN; pn++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[pn][rb] = mma<DT>(wf[pn][i], xf[i], acc[pn][rb]);
+        }
+    }
+
+    if (a.kw == 1) {
+#pragma unroll
+        for (int pn = 0; pn < PN; pn++)
+#pragma unroll
+            for (int rb = 0; rb < RB; rb++) store_block<DT>(a, acc[pn][rb], m0 + 16 * rb, 16 * (p0 + pn), lane);
+        return;
+    }
+#pragma unroll
+    for (int pn = 0; pn < PN; pn++)
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) red[(w * PN * RB + pn * RB + rb) * 64 + lane] = acc[pn][rb];
+    __syncthreads();
+    for (int blk = w; blk < PN * RB; blk += a.kw) {
+        f32x4 s = red[blk * 64 + lane];
+        for (int ww = 1; ww < a.kw; ww++) s += red[(ww * PN * RB + blk) * 64 + lane];
+        const int pn = blk / RB, rb = blk % RB;
+        store_block<DT>(a, s, m0 + 16 * rb, 16 * (p0 + pn), lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tile kernel: mid and long prefill.
+//
+// A workgroup of four waves owns a BM x BN output tile.  Per 128-wide K
+// chunk every weight of the tile is unpacked once (one or more 32-code runs
+// per lane) into LDS in MFMA-fragment order, the activation tile is staged
+// next to it, and each wave multiplies its (BM/WGM) x (BN/WGN) share from
+// LDS, so the unpack cost is shared by all BM rows of the tile.
+// ---------------------------------------------------------------------------
+template <int FMT, int DT, int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(256) k_tile(Args a)
+{
+    constexpr int RBT = BM / 16, PBT = BN / 16;
+    constexpr int RBW = RBT / WGM, PBW = PBT / WGN;
+    constexpr int UPT = PBT * 64 / 256;  // weight runs per thread per chunk
+    constexpr int XPT = BM * 16 / 256;   // 16-byte activation pieces per thread per chunk
+    static_assert(WGM * WGN == 4, "four waves");
+    static_assert(UPT >= 1 && XPT >= 1, "tile too small");
+    __shared__ u32x4 sX[RBT][4][64];
+    __shared__ u32x4 sW[PBT][4][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int m0 = blockIdx.y * BM, p0 = blockIdx.x * PBT;
+    const int nch = a.K / kChunk;
+
+    f32x4 acc[PBW][RBW];
+#pragma unroll
+    for (int pb = 0; pb < PBW; pb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = 0; c < nch; c++) {
+        u32x4 xv[XPT];
+#pragma unroll
+        for (int s = 0; s < XPT; s++) {
+            const int v = tid + 256 * s, r16 = v & 15, qq = (v >> 4) & 15, rb = v >> 8;
+            int row = m0 + 16 * rb + r16;
+            row = row < a.M ? row : a.M - 1;
+            xv[s] = *(const u32x4 *)(a.X + (long long)row * a.K + kChunk * c + 8 * qq);
+        }
+        u32x4 wf[UPT][4];
+#pragma unroll
+        for (int s = 0; s < UPT; s++) {
+            const int u = tid + 256 * s, pb = u >> 6, gg = (u >> 4) & 3, col = u & 15;
+            int p = p0 + pb;
+            p = p < a.np ? p : a.np - 1;
+            Unit<FMT> un;
+            load_unit<FMT>(a, p, c, gg, col, un);
+            unpack_unit<FMT, DT>(un, c, gg, wf[s]);
+        }
+        __syncthreads();  // the previous chunk's fragments have been read
+#pragma unroll
+        for (int s = 0; s < XPT; s++) {
+            const int v = tid + 256 * s, r16 = v & 15, qq = (v >> 4) & 15, rb = v >> 8;
+            sX[rb][qq & 3][(qq >> 2) * 16 + r16] = xv[s];
+        }
+#pragma unroll
+        for (int s = 0; s < UPT; s++) {
+            const int u = tid + 256 * s, pb = u >> 6, gg = (u >> 4) & 3, col = u & 15;
+#pragma unroll
+            for (int i = 0; i < 4; i++) sW[pb][i][gg * 16 + col] = wf[s][i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            u32x4 af[PBW], bf[RBW];
+#pragma unroll
+            for (int pb = 0; pb < PBW; pb++) af[pb] = sW[wn * PBW + pb][i][lane];
+#pragma unroll
+            for (int rb = 0; rb < RBW; rb++) bf[rb] = sX[wm * RBW + rb][i][lane];
+#pragma unroll
+            for (int pb = 0; pb < PBW; pb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = mma<DT>(af[pb], bf[rb], acc[pb][rb]);
+        }
+    }
+#pragma unroll
+    for (int pb = 0; pb < PBW; pb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+            store_block<DT>(a, acc[pb][rb], m0 + 16 * (wm * RBW + rb), 16 * (p0 + wn * PBW + pb), lane);
+}
+
+// ---------------------------------------------------------------------------
+// Staged dequant: the same unpack, written out as logical W[K][N].
+// One thread per (panel, chunk, run, column).
+// ---------------------------------------------------------------------------
+template <int FMT, int DT>
+__global__ void __launch_bounds__(256) k_dequant(Args a, uint16_t *Wout)
+{
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int nch = a.K / kChunk;
+    const long long total = (long long)a.np * nch * 64;
+    if (idx >= total) return;
+    const int lane = (int)(idx & 63), col = lane & 15, g = lane >> 4;
+    const long long pc = idx >> 6;
+    const int c = (int)(pc % nch), p = (int)(pc / nch);
+    const int n = 16 * p + col;
+    Unit<FMT> u;
+    load_unit<FMT>(a, p, c, g, col, u);
+    u32x4 f[4];
+    unpack_unit<FMT, DT>(u, c, g, f);
+    if (n >= a.N) return;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const long long k = (long long)kChunk * c + 32 * g + 8 * i + 2 * j;
+            Wout[k * a.N + n] = (uint16_t)(f[i][j] & 0xFFFFu);
+            Wout[(k + 1) * a.N + n] = (uint16_t)(f[i][j] >> 16);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation, the M-ladder, launches.
+// ---------------------------------------------------------------------------
+
+enum Rung { RUNG_SMALL_M = 0, RUNG_SKINNY_N = 1, RUNG_TILE_128 = 2, RUNG_COUNT = 3 };
+const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "tile-128x128"};
+
+struct Plan {
+    int rung;
+    int rows, cols;    // output tile
+    int waves, kw;     // waves per workgroup, K-split ways
+    int rb, pn;        // direct kernel: row blocks / panels per wave
+    dim3 grid;
+    size_t lds;        // dynamic LDS bytes
+};
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Waves splitting K inside one direct-kernel workgroup: enough waves in the
+// whole grid to keep every CU streaming (about 2048), at least two chunks
+// per wave, at most eight waves.
+int pick_kw(long long groups, int nch)
+{
+    int kw = 1;
+    while (kw < 8 && groups * kw < 2048 && nch / (2 * kw) >= 2) kw *= 2;
+    return kw;
+}
+
+bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
+{
+    const long long np = (N + 15) / 16;
+    const int nch = (int)(K / kChunk);
+    pl = Plan{};
+    pl.rung = rung;
+    switch (rung) {
+    case RUNG_SMALL_M: {
+        pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4;
+        pl.pn = 1;
+        pl.grid = dim3((unsigned)np, (unsigned)ceil_div(M, 16 * pl.rb), 1);
+        break;
+    }
+    case RUNG_SKINNY_N: {
+        pl.rb = 1;
+        pl.pn = np >= 4 ? 4 : (int)np;
+        pl.grid = dim3((unsigned)ceil_div(np, pl.pn), (unsigned)ceil_div(M, 16), 1);
+        break;
+    }
+    case RUNG_TILE_128: {
+        pl.rows = 128;
+        pl.cols = 128;
+        pl.waves = 4;
+        pl.kw = 1;
+        pl.grid = dim3((unsigned)ceil_div(np, 8), (unsigned)ceil_div(M, 128), 1);
+        pl.lds = 0;
+        return true;
+    }
+    default:
+        return false;
+    }
+    pl.rows = 16 * pl.rb;
+    pl.cols = 16 * pl.pn;
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch);
+    pl.waves = pl.kw;
+    pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
+    return true;
+}
+
+// The M-ladder.  Narrow N first: with at most four panels the grid must run
+// over M (a 128x128 tile would leave most of the part idle and most of each
+// tile padding).  Then decode-adjacent M, where each weight is used by at
+// most 64 rows and the kernel is a weight stream.  Everything else takes
+// the LDS-shared tile.
+int select_rung(long long M, long long N)
+{
+    if (N <= 64) return RUNG_SKINNY_N;
+    if (M <= 64) return RUNG_SMALL_M;
+    return RUNG_TILE_128;
+}
+
+template <int FMT, int DT, int RB, int PN>
+hipError_t launch_direct_rp(const Plan &pl, const Args &a, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_direct<FMT, DT, RB, PN>), pl.grid, dim3(64 * pl.kw), pl.lds, s, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int DT>
+hipError_t launch_direct(const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (pl.pn == 1) {
+        switch (pl.rb) {
+        case 1: return launch_direct_rp<FMT, DT, 1, 1>(pl, a, s);
+        case 2: return launch_direct_rp<FMT, DT, 2, 1>(pl, a, s);
+        case 3: return launch_direct_rp<FMT, DT, 3, 1>(pl, a, s);
+        default: return launch_direct_rp<FMT, DT, 4, 1>(pl, a, s);
+        }
+    }
+    switch (pl.pn) {
+    case 2: return launch_direct_rp<FMT, DT, 1, 2>(pl, a, s);
+    case 3: return launch_direct_rp<FMT, DT, 1, 3>(pl, a, s);
+    default: return launch_direct_rp<FMT, DT, 1, 4>(pl, a, s);
+    }
+}
+
+template <int FMT, int DT>
+hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (pl.rung == RUNG_TILE_128) {
+        hipLaunchKernelGGL((k_tile<FMT, DT, 128, 128, 2, 2>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    return launch_direct<FMT, DT>(pl, a, s);
+}
+
+hipError_t launch(int fmt, int dtype, const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (fmt == FMT_Q4K) return dtype == DT_F16 ? launch_fd<FMT_Q4K, DT_F16>(pl, a, s) : launch_fd<FMT_Q4K, DT_BF16>(pl, a, s);
+    if (fmt == FMT_Q6K) return dtype == DT_F16 ? launch_fd<FMT_Q6K, DT_F16>(pl, a, s) : launch_fd<FMT_Q6K, DT_BF16>(pl, a, s);
+    return dtype == DT_F16 ? launch_fd<FMT_W4, DT_F16>(pl, a, s) : launch_fd<FMT_W4, DT_BF16>(pl, a, s);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape rules shared by every device entry point.
+int check_shape(int fmt, long long M, long long N, long long K, long long group)
+{
+    if (fmt != FMT_Q4K && fmt != FMT_Q6K && fmt != FMT_W4) return QGEMM_ERR_FORMAT;
+    if (M < 0 || N < 1 || K < 1) return QGEMM_ERR_SHAPE;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return QGEMM_ERR_SHAPE;
+    if (fmt == FMT_W4) {  // group == 0: group size not known to the caller (rung queries)
+        if (group != 0 && (group < 32 || group % 32 != 0)) return QGEMM_ERR_FORMAT;
+        if (K % 128 != 0 || (group != 0 && K % group != 0)) return QGEMM_ERR_SHAPE;
+    } else if (K % 256 != 0) {
+        return QGEMM_ERR_SHAPE;
+    }
+    return QGEMM_OK;
+}
+
+Args make_args(int fmt, const void *X, const void *W, void *Y, long long M, long long N, long long K, long long group,
+               int has_zp)
+{
+    Args a{};
+    a.X = (const uint16_t *)X;
+    a.W = (const uint8_t *)W;
+    a.Y = (uint16_t *)Y;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.np = (int)((N + 15) / 16);
+    a.group = fmt == FMT_W4 ? (int)group : 0;
+    a.has_zp = fmt == FMT_W4 ? (has_zp ? 1 : 0) : 0;
+    a.kw = 1;
+    if (fmt == FMT_W4) {
+        a.w4_sreg = (long long)a.np * (K / 128) * 1024;
+        a.w4_zreg = a.w4_sreg + (long long)a.np * (K / group) * 32;
+    }
+    return a;
+}
+
+int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
+         long long group, int has_zp, int dtype, void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, M, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (rung < -1 || rung >= RUNG_COUNT) return QGEMM_ERR_FORMAT;
+    if (M == 0) return QGEMM_OK;
+    if (!X || !W || !Y) return QGEMM_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
+    Plan pl;
+    if (!make_plan(rung < 0 ? select_rung(M, N) : rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
+    Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
+    a.kw = pl.kw;
+    return launch(fmt, dtype, pl, a, (hipStream_t)stream) == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+}
+
+void fill_info(const Plan &pl, int32_t *info)
+{
+    info[0] = pl.rung;
+    info[1] = pl.rows;
+    info[2] = pl.cols;
+    info[3] = kChunk;
+    info[4] = pl.waves;
+    info[5] = pl.kw;
+    info[6] = (int32_t)pl.grid.x;
+    info[7] = (int32_t)pl.grid.y;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qgemm_status_str(int status)
+{
+    switch (status) {
+    case QGEMM_OK: return "ok";
+    case QGEMM_ERR_NULL: return "null pointer";
+    case QGEMM_ERR_SHAPE: return "illegal shape";
+    case QGEMM_ERR_DTYPE: return "unsupported dtype";
+    case QGEMM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QGEMM_ERR_FORMAT: return "unsupported format, group size or rung";
+    case QGEMM_ERR_SIZE: return "buffer too small";
+    case QGEMM_ERR_HIP: return "HIP launch failed";
+    case QGEMM_ERR_INPUT: return "malformed input data";
+    default: return "unknown status";
+    }
+}
+
+int qgemm_q4k(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, int dtype, void *stream)
+{
+    return gemm(FMT_Q4K, -1, X, W, Y, M, N, K, 0, 0, dtype, stream);
+}
+
+int qgemm_q6k(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, int dtype, void *stream)
+{
+    return gemm(FMT_Q6K, -1, X, W, Y, M, N, K, 0, 0, dtype, stream);
+}
+
+int qgemm_w4a16(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                int has_zp, int dtype, void *stream)
+{
+    return gemm(FMT_W4, -1, X, W, Y, M, N, K, group_size, has_zp, dtype, stream);
+}
+
+int qgemm_gemm_rung(int format, int rung, const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K,
+                    int64_t group_size, int has_zp, int dtype, void *stream)
+{
+    return gemm(format, rung, X, W, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream);
+}
+
+int qgemm_num_rungs(void) { return RUNG_COUNT; }
+
+const char *qgemm_rung_name(int rung) { return rung >= 0 && rung < RUNG_COUNT ? kRungNames[rung] : nullptr; }
+
+int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
+{
+    if (!info8) return QGEMM_ERR_NULL;
+    int st = check_shape(format, M, N, K, 0);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    Plan pl;
+    if (!make_plan(rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
+    fill_info(pl, info8);
+    return QGEMM_OK;
+}
+
+int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
+{
+    return qgemm_rung_info(select_rung(M, N), format, M, N, K, dtype, info8);
+}
+
+int qgemm_dequant(int format, const void *W, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
+                  int dtype, void *stream)
+{
+    if (format == FMT_W4 && group_size == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(format, 0, N, K, format == FMT_W4 ? group_size : 0);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (!W || !Wout) return QGEMM_ERR_NULL;
+    if (!aligned16(W) || !aligned16(Wout)) return QGEMM_ERR_ALIGN;
+    Args a = make_args(format, nullptr, W, nullptr, 0, N, K, group_size, has_zp);
+    const long long total = (long long)a.np * (K / kChunk) * 64;
+    dim3 grid((unsigned)((total + 255) / 256));
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t *o = (uint16_t *)Wout;
+#define QG_DQ(F, D) hipLaunchKernelGGL((k_dequant<F, D>), grid, dim3(256), 0, s, a, o)
+    if (format == FMT_Q4K) { if (dtype == DT_F16) QG_DQ(FMT_Q4K, DT_F16); else QG_DQ(FMT_Q4K, DT_BF16); }
+    else if (format == FMT_Q6K) { if (dtype == DT_F16) QG_DQ(FMT_Q6K, DT_F16); else QG_DQ(FMT_Q6K, DT_BF16); }
+    else { if (dtype == DT_F16) QG_DQ(FMT_W4, DT_F16); else QG_DQ(FMT_W4, DT_BF16); }
+#undef QG_DQ
+    return hipGetLastError() == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+}
+
+}  // extern "C"

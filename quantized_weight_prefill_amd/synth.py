@@ -201,3 +201,42 @@ def encode(fmt: str, fields: dict):
     if fmt == "w4a16":
         return fields
     raise ValueError(fmt)
+
+
+#: The named workloads.  Each GEMM is (label, fmt, M, K, N, dtype, group, symmetric);
+#: the seed of workload i is 1000 + i and GEMM j of it draws from sub-stream
+#: pair j of SeedSequence(seed).spawn(2 * len(gemms)) (X first, then W).
+WORKLOADS = {
+    "q4k_small": {  # single Q4_K GEMM, fp16
+        "index": 0,
+        "gemms": [("q4k_16x1024x512", "q4k", 16, 1024, 512, F16, 0, False)],
+    },
+    "q4k_ffn_up_m512": {  # Qwen3-8B FFN up-projection shape at M = 512, fp16
+        "index": 1,
+        "gemms": [("up", "q4k", 512, 4096, 12288, F16, 0, False)],
+    },
+    "qwen3_8b_layer_m658": {  # one dense layer's seven linears at 658 prompt tokens, fp16
+        "index": 2,
+        "gemms": [(name, fmt, QWEN3_8B_PROMPT, K, N, F16, 0, False) for name, K, N, fmt in QWEN3_8B_LAYER],
+    },
+    "w4a16_g128_m2048": {  # group-wise W4A16, fp16 and bf16, asymmetric and symmetric
+        "index": 3,
+        "gemms": [(f"{DTYPE_NAMES[dt]}_{'sym' if sym else 'asym'}", "w4a16", 2048, 4096, 12288, dt, 128, sym)
+                  for dt in (F16, BF16) for sym in (False, True)],
+    },
+    "long_prefill_m4096_bf16": {  # wide Q4_K projection plus a 32-wide skinny projection, bf16
+        "index": 4,
+        "gemms": [("wide", "q4k", 4096, 4096, 12288, BF16, 0, False),
+                  ("skinny", "q4k", 4096, 4096, 32, BF16, 0, False)],
+    },
+}
+
+
+def workload_inputs(name: str, j: int):
+    """(X bits, weight fields, encoded weights) of GEMM j of a named workload."""
+    w = WORKLOADS[name]
+    label, fmt, M, K, N, dt, group, sym = w["gemms"][j]
+    rs = streams(1000 + w["index"], 2 * len(w["gemms"]))
+    X = activations(rs[2 * j], M, K, dt)
+    fields = weight_fields(fmt, rs[2 * j + 1], N, K, group or 128, sym)
+    return X, fields, encode(fmt, fields)

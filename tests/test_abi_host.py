@@ -1,0 +1,226 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every function include/qgemm.h declares, the packers invert exactly and put
+each code where the header says, argument errors come back as status codes
+before any launch, and the M-ladder keeps its invariants."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_weight_prefill_amd as qg
+from quantized_weight_prefill_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+
+def header_functions() -> set[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(qgemm_[a-z0-9_]+)\s*\(", text))
+
+
+def test_library_exports_every_declared_function():
+    lib = qg.lib()
+    declared = header_functions()
+    assert len(declared) >= 18
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in qgemm.h but not exported"
+    assert declared == set(qg.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings():
+    lib = qg.lib()
+    for code in qg.STATUS:
+        s = lib.qgemm_status_str(code)
+        assert s and s.decode() != "unknown status"
+    assert lib.qgemm_status_str(12345).decode() == "unknown status"
+
+
+# ----------------------------------------------------------------------------
+# packers
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(1, 256), (16, 512), (33, 1024), (512, 1024)])
+def test_q4k_roundtrip_and_size(N, K):
+    rng = np.random.default_rng(N + K)
+    blocks = synth.q4k_encode(synth.q4k_fields(rng, N, K))
+    packed = qg.q4k_pack(blocks, N, K)
+    assert packed.nbytes == -(-N // 16) * 16 * (K // 256) * 144  # 0.5625 B per weight, panel-padded
+    assert np.array_equal(qg.q4k_unpack(packed, N, K), blocks)
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (20, 768), (64, 1024)])
+def test_q6k_roundtrip_and_size(N, K):
+    rng = np.random.default_rng(N * 3 + K)
+    blocks = synth.q6k_encode(synth.q6k_fields(rng, N, K))
+    packed = qg.q6k_pack(blocks, N, K)
+    assert packed.nbytes == -(-N // 16) * 16 * (K // 256) * 210
+    assert np.array_equal(qg.q6k_unpack(packed, N, K), blocks)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("sym", [False, True])
+def test_w4a16_roundtrip_and_size(group, sym):
+    N, K = 40, 512
+    rng = np.random.default_rng(group + sym)
+    f = synth.w4a16_fields(rng, N, K, group, sym)
+    zeros = None if sym else f["zeros"]
+    packed = qg.w4a16_pack(f["codes"], f["scales"], zeros, N, K, group)
+    npan = -(-N // 16)
+    assert packed.nbytes == npan * 16 * K // 2 + npan * 16 * (K // group) * 2 + (0 if sym else npan * 16 * (K // group) // 2)
+    codes, scales, z = qg.w4a16_unpack(packed, N, K, group, not sym)
+    assert np.array_equal(codes, f["codes"]) and np.array_equal(scales, f["scales"])
+    if not sym:
+        assert np.array_equal(z, f["zeros"])
+
+
+def _pair_order_code(run16: np.ndarray, t: int) -> int:
+    """Code t of a 16-byte run in pair order, read the way the header states."""
+    word = int(run16[4 * (t // 8):4 * (t // 8) + 4].view("<u4")[0])
+    pair, half = (t % 8) // 2, t % 2
+    return (word >> (16 * half + 4 * pair)) & 15
+
+
+def test_q4k_layout_matches_header():
+    N, K = 20, 512
+    rng = np.random.default_rng(5)
+    f = synth.q4k_fields(rng, N, K)
+    packed = qg.q4k_pack(synth.q4k_encode(f), N, K)
+    for n in (0, 7, 16, 19):
+        p, c = n // 16, n % 16
+        for b in range(K // 256):
+            rec = packed[(p * (K // 256) + b) * 2304:][:2304]
+            hdr = rec[16 * c:16 * c + 16]
+            assert int(hdr[0:2].view("<u2")[0]) == f["d"][n, b]
+            assert int(hdr[2:4].view("<u2")[0]) == f["dmin"][n, b]
+            for k in rng.integers(0, 256, 40):
+                h, g, t = k // 128, (k % 128) // 32, k % 32
+                run = rec[256 + 1024 * h + (16 * g + c) * 16:][:16]
+                assert _pair_order_code(run, int(t)) == f["q"][n, 256 * b + k]
+
+
+def test_q6k_layout_matches_header():
+    N, K = 17, 256
+    rng = np.random.default_rng(6)
+    f = synth.q6k_fields(rng, N, K)
+    packed = qg.q6k_pack(synth.q6k_encode(f), N, K)
+    for n in (0, 5, 16):
+        p, c = n // 16, n % 16
+        rec = packed[p * 3360:][:3360]
+        assert int(rec[2 * c:2 * c + 2].view("<u2")[0]) == f["d"][n, 0]
+        assert np.array_equal(rec[32 + 16 * c:48 + 16 * c].view(np.int8), f["s"][n, 0])
+        for k in range(256):
+            h, g, t = k // 128, (k % 128) // 32, k % 32
+            lo = _pair_order_code(rec[288 + 1024 * h + (16 * g + c) * 16:][:16], t)
+            hi_words = rec[2336 + 512 * h + (16 * g + c) * 8:][:8].view("<u4")
+            i, u, pr = t // 8, (t // 8) % 2, (t % 8) // 2
+            bit = 16 * (t % 2) + 2 * (4 * u + pr)
+            hi = (int(hi_words[t // 16]) >> bit) & 3
+            assert lo | (hi << 4) == f["q"][n, k]
+
+
+def test_w4a16_layout_matches_header():
+    N, K, group = 18, 256, 64
+    rng = np.random.default_rng(7)
+    f = synth.w4a16_fields(rng, N, K, group, False)
+    packed = qg.w4a16_pack(f["codes"], f["scales"], f["zeros"], N, K, group)
+    npan, nch, ng = 2, K // 128, K // group
+    sreg, zreg = npan * nch * 1024, npan * nch * 1024 + npan * ng * 32
+    for n in (0, 3, 17):
+        p, c = n // 16, n % 16
+        for k in range(0, K, 5):
+            ch, g, t = k // 128, (k % 128) // 32, k % 32
+            run = packed[(p * nch + ch) * 1024 + (16 * g + c) * 16:][:16]
+            assert _pair_order_code(run, t) == f["codes"][n, k]
+        for j in range(ng):
+            assert int(packed[sreg + (p * ng + j) * 32 + 2 * c:][:2].view("<u2")[0]) == f["scales"][j, n]
+            assert (packed[zreg + (p * ng + j) * 8 + c // 2] >> (4 * (c % 2))) & 15 == f["zeros"][j, n]
+
+
+def test_packer_errors():
+    lib = qg.lib()
+    buf = np.zeros(4096, np.uint8)
+    p = ctypes.c_void_p(buf.ctypes.data)
+    assert lib.qgemm_q4k_pack(None, 16, 256, p, buf.nbytes) == -1
+    assert lib.qgemm_q4k_pack(p, 16, 300, p, buf.nbytes) == -2
+    assert lib.qgemm_q4k_pack(p, 0, 256, p, buf.nbytes) == -2
+    assert lib.qgemm_q4k_pack(p, 16, 256, p, 100) == -6
+    assert lib.qgemm_q4k_packed_bytes(16, 100) == 0
+    assert lib.qgemm_w4a16_packed_bytes(16, 256, 48, 1) == 0
+    codes = np.full((16, 256), 16, np.uint8)  # 16 does not fit four bits
+    scales = np.zeros((2, 16), np.uint16)
+    with pytest.raises(qg.QGemmError) as e:
+        qg.w4a16_pack(codes, scales, None, 16, 256, 128)
+    assert e.value.status == -8
+
+
+# ----------------------------------------------------------------------------
+# device entry points: argument errors are detected before any launch
+# ----------------------------------------------------------------------------
+
+def test_device_entry_argument_errors():
+    lib = qg.lib()
+    A = ctypes.c_void_p(1 << 20)        # never dereferenced: each call below fails validation
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    s = None
+    assert lib.qgemm_q4k(None, A, A, 4, 16, 256, 0, s) == -1
+    assert lib.qgemm_q4k(A, A, A, 4, 16, 200, 0, s) == -2
+    assert lib.qgemm_q4k(A, A, A, -1, 16, 256, 0, s) == -2
+    assert lib.qgemm_q4k(A, A, A, 4, 0, 256, 0, s) == -2
+    assert lib.qgemm_q4k(A, A, A, 4, 16, 256, 7, s) == -3
+    assert lib.qgemm_q6k(A, mis, A, 4, 16, 256, 0, s) == -4
+    assert lib.qgemm_w4a16(A, A, A, 4, 16, 256, 48, 1, 0, s) == -5
+    assert lib.qgemm_w4a16(A, A, A, 4, 16, 192, 64, 1, 0, s) == -2
+    assert lib.qgemm_w4a16(A, A, A, 4, 16, 256, 0, 1, 0, s) == -5
+    assert lib.qgemm_gemm_rung(0, 99, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
+    assert lib.qgemm_gemm_rung(7, 0, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
+    # M == 0 is a no-op that touches nothing
+    assert lib.qgemm_q4k(None, None, None, 0, 16, 256, 0, s) == 0
+    assert lib.qgemm_dequant(0, None, A, 16, 256, 0, 0, 0, s) == -1
+    assert lib.qgemm_dequant(2, A, A, 16, 256, 0, 0, 0, s) == -5
+
+
+# ----------------------------------------------------------------------------
+# the M-ladder
+# ----------------------------------------------------------------------------
+
+SHAPES = [(4096, 12288), (4096, 4096), (4096, 1024), (12288, 4096), (4096, 32), (1024, 512), (256, 16)]
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16"])
+@pytest.mark.parametrize("dtype", [qg.F16, qg.BF16])
+def test_ladder_sweep(fmt, dtype):
+    """Sweep M over decode-adjacent to long prefill on every workload shape:
+    each rung's grid covers the whole output, the K step is whole 32-wide
+    runs (never straddling a Q4_K/Q6_K sub-block or a W4A16 group, whose
+    sizes are multiples of 32), and the K split leaves every wave work."""
+    for K, N in SHAPES:
+        if fmt != "w4a16" and K % 256:
+            continue
+        for M in list(range(1, 130)) + [255, 256, 257, 511, 512, 658, 1024, 2048, 4096, 8192]:
+            info = qg.select_rung(fmt, M, N, K, dtype)
+            assert info["rung"] in range(qg.num_rungs())
+            assert info["grid_x"] * info["cols"] >= N
+            assert info["grid_y"] * info["rows"] >= M
+            assert info["k_step"] % 32 == 0 and info["k_step"] <= K
+            assert (K // info["k_step"]) >= info["k_split"] >= 1
+            if N <= 64:
+                assert info["name"] == "direct-skinny-n"
+            elif M <= 64:
+                assert info["name"] == "direct-small-m"
+            for r in range(qg.num_rungs()):
+                ri = qg.rung_info(r, fmt, M, N, K, dtype)
+                assert ri["grid_x"] * ri["cols"] >= N and ri["grid_y"] * ri["rows"] >= M
+
+
+def test_ladder_rejects_bad_shapes():
+    with pytest.raises(qg.QGemmError):
+        qg.select_rung("q4k", 16, 512, 1000)
+    with pytest.raises(qg.QGemmError):
+        qg.select_rung("q4k", 16, 512, 1024, dtype=9)
+    assert qg.rung_name(-1) is None and qg.rung_name(qg.num_rungs()) is None

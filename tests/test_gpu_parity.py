@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Dequant is compared bit for bit (signed zeros equal); GEMM outputs must meet
+max |Y - Yref| / (|X|.|W|) <= 2e-3 element by element.  Sizes are small
+enough for the oracle to finish in seconds yet span several tiles, several
+panels and ragged M/N tails, and every rung is forced on every shape.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import quantized_weight_prefill_amd as qg
+from quantized_weight_prefill_amd import synth
+from tests.helpers import Case, assert_gemm_close, bytes_to_device, fnv1a64, from_device, same_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [("q4k", False), ("q6k", False), ("w4a16", False), ("w4a16", True)]
+FMT_IDS = ["q4k", "q6k", "w4a16-asym", "w4a16-sym"]
+DTYPES = [qg.F16, qg.BF16]
+RUNGS = list(range(3))
+
+
+def _case(fmt, sym, M, N, K, dtype, seed, group=128):
+    return Case(fmt, M, N, K, dtype, seed, group=group, symmetric=sym)
+
+
+# ----------------------------------------------------------------------------
+# dequant: bit-exact
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_dequant_bitexact(fmt, sym, dtype):
+    N, K = 72, 1024  # five panels, the last one ragged
+    c = _case(fmt, sym, 1, N, K, dtype, seed=100)
+    print(f"dequant {fmt} sym={sym} dtype={dtype} N={N} K={K}", flush=True)
+    w = qg.dequant(fmt, c.device_weights(), N, K, dtype, group=c.group, has_zp=c.has_zp)
+    got = from_device(w)
+    assert same_bits(got, c.W)
+    assert fnv1a64(got[:64]) == fnv1a64(c.W[:64])
+
+
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_dequant_w4a16_small_groups(group, dtype):
+    c = _case("w4a16", False, 1, 48, 512, dtype, seed=101, group=group)
+    w = qg.dequant("w4a16", c.device_weights(), 48, 512, dtype, group=group, has_zp=True)
+    assert same_bits(from_device(w), c.W)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_dequant_q4k_wide_exponent_gap(dtype):
+    """d and dmin far apart: the exact weight needs more than 24 bits, so the
+    binary32 formation step decides some roundings."""
+    rng = np.random.default_rng(7)
+    N, K = 64, 512
+    f = synth.q4k_fields(rng, N, K)
+    f["d"][:] = synth.f16_bits(rng.uniform(0.5, 8.0, f["d"].shape))
+    f["dmin"][:] = synth.f16_bits(rng.uniform(2.0 ** -20, 2.0 ** -12, f["dmin"].shape))
+    f["d"][0, 0], f["dmin"][0, 0] = 0x3C01, 0x0001  # a double-rounding-sensitive block
+    f["sc"][0, 0, :], f["m"][0, 0, :] = 1, 1
+    f["q"][0, :32] = 3
+    c = Case("q4k", 1, N, K, dtype, seed=102, fields=f)
+    w = from_device(qg.dequant("q4k", c.device_weights(), N, K, dtype))
+    assert same_bits(w, c.W)
+
+
+# ----------------------------------------------------------------------------
+# identity extraction: X = I makes Y equal W bit for bit through the real GEMM
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+@pytest.mark.parametrize("rung", RUNGS)
+def test_identity_extraction(fmt, sym, dtype, rung):
+    K, N = 256, 48
+    eye = synth.f16_bits(np.eye(K)) if dtype == qg.F16 else synth.bf16_bits_from_f32(np.eye(K, dtype=np.float32))
+    c = Case(fmt, K, N, K, dtype, seed=103, symmetric=sym, X=eye)
+    print(f"identity {fmt} sym={sym} dtype={dtype} rung={rung}", flush=True)
+    y = from_device(c.run(rung))
+    assert same_bits(y, c.W)
+
+
+# ----------------------------------------------------------------------------
+# GEMM parity on a grid of shapes, every rung
+# ----------------------------------------------------------------------------
+
+SHAPES = [(1, 16, 256), (5, 40, 512), (16, 96, 256), (17, 144, 512), (33, 64, 256), (64, 80, 768),
+          (65, 128, 256), (130, 160, 512), (257, 48, 256), (300, 272, 512)]
+
+
+@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+@pytest.mark.parametrize("rung", RUNGS)
+def test_gemm_parity_grid(fmt, sym, dtype, rung):
+    for i, (M, N, K) in enumerate(SHAPES):
+        c = _case(fmt, sym, M, N, K, dtype, seed=200 + i)
+        print(f"grid {fmt} sym={sym} dtype={dtype} rung={rung} M={M} N={N} K={K}", flush=True)
+        y = from_device(c.run(rung))
+        Yref, B = oracle.gemm(c.X, c.W, dtype)
+        assert_gemm_close(y, Yref, B, dtype, what=f"{fmt} M={M} N={N} K={K} rung={rung}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_w4a16_small_groups_gemm(dtype):
+    for group in (32, 64):
+        c = _case("w4a16", False, 70, 96, 512, dtype, seed=210, group=group)
+        for rung in RUNGS:
+            y = from_device(c.run(rung))
+            Yref, B = oracle.gemm(c.X, c.W, dtype)
+            assert_gemm_close(y, Yref, B, dtype, what=f"w4a16 g={group} rung={rung}")
+
+
+@pytest.mark.parametrize("rung", RUNGS)
+def test_config0_parity(rung):
+    """Single Q4_K GEMM, X fp16 [16, 1024], W [1024, 512], seed 1000."""
+    c = Case("q4k", 16, 512, 1024, qg.F16, seed=1000)
+    y = from_device(c.run(rung))
+    Yref, B = oracle.gemm(c.X, c.W, qg.F16)
+    assert_gemm_close(y, Yref, B, qg.F16, what="config0")
+
+
+# ----------------------------------------------------------------------------
+# special cases and invariants
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rung", RUNGS)
+def test_special_values(rung):
+    M, N, K = 40, 64, 512
+    rng = np.random.default_rng(9)
+    f = synth.q4k_fields(rng, N, K)
+    f["q"][:] = 0
+    f["m"][:] = 0
+    c = Case("q4k", M, N, K, qg.F16, seed=300, fields=f)
+    y = from_device(c.run(rung))
+    assert not np.any(y & 0x7FFF)  # all weights zero -> Y == 0
+    # X = ones: every row is the column sum of W (all-positive special case)
+    ones = synth.f16_bits(np.ones((M, K)))
+    c2 = Case("q4k", M, N, K, qg.F16, seed=301, X=ones)
+    y2 = from_device(c2.run(rung))
+    Yref, B = oracle.gemm(c2.X, c2.W, qg.F16)
+    assert_gemm_close(y2, Yref, B, qg.F16, allow_out_ulp=True, what="ones")
+    assert np.all(y2 == y2[0:1])
+    # W4A16 with zero-point equal to the code everywhere -> Y == 0
+    fw = synth.w4a16_fields(rng, N, K, 128, False)
+    fw["codes"][:] = np.repeat(fw["zeros"].T, 128, axis=1)
+    c3 = Case("w4a16", M, N, K, qg.BF16, seed=302, fields=fw)
+    assert not np.any(from_device(c3.run(rung)) & 0x7FFF)
+
+
+@pytest.mark.parametrize("rung", RUNGS)
+def test_guard_bands_and_ragged_n(rung):
+    """Outputs outside Y[M][N] are never written, also for N % 4 != 0."""
+    import torch
+
+    for M, N, K in [(37, 37, 256), (70, 130, 256), (3, 5, 512)]:
+        c = _case("q6k", False, M, N, K, qg.F16, seed=310)
+        pad = 4096
+        buf = torch.full((M * N + 2 * pad,), 12345.0, dtype=torch.float16, device="cuda")
+        # 16-byte aligned interior view starting at element `pad`
+        out = buf[pad:pad + M * N].view(M, N)
+        c.run(rung, out=out)
+        host = buf.cpu()
+        assert torch.all(host[:pad] == 12345.0) and torch.all(host[pad + M * N:] == 12345.0)
+        Yref, B = oracle.gemm(c.X, c.W, qg.F16)
+        assert_gemm_close(from_device(out), Yref, B, qg.F16, what=f"ragged M={M} N={N}")
+
+
+def test_m_zero_is_noop():
+    import torch
+
+    c = _case("q4k", False, 1, 32, 256, qg.F16, seed=320)
+    x = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    y = torch.full((0, 32), 1.0, dtype=torch.float16, device="cuda")
+    qg.q4k(x, c.device_weights(), 32, out=y)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("rung", RUNGS)
+def test_determinism_and_row_permutation(rung):
+    """Run-to-run bit-identical; permuting rows of X permutes rows of Y bit for
+    bit (the accumulation order of an output never depends on its row)."""
+    M, N, K = 96, 80, 512
+    c = _case("q4k", False, M, N, K, qg.BF16, seed=330)
+    y1 = from_device(c.run(rung))
+    y2 = from_device(c.run(rung))
+    assert np.array_equal(y1, y2)
+    perm = np.random.default_rng(3).permutation(M)
+    yp = from_device(c.run(rung, x_bits=c.X[perm]))
+    assert np.array_equal(yp, y1[perm])
+
+
+def test_rungs_agree_with_each_other():
+    """Rows at M = 658 equal, within the bound, the same rows computed as an
+    M = 16 problem (a different rung and K split)."""
+    M, N, K = 658, 96, 1024
+    c = _case("q4k", False, M, N, K, qg.F16, seed=340)
+    y = oracle.bits_to_double_fast(from_device(c.run(-1)), qg.F16)
+    rows = np.arange(100, 116)
+    ys = oracle.bits_to_double_fast(from_device(c.run(-1, x_bits=c.X[rows])), qg.F16)
+    _, B = oracle.gemm(c.X[rows], c.W, qg.F16)
+    assert np.all(np.abs(y[rows] - ys) <= 2 * 2e-3 * B)
