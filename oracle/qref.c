@@ -19,16 +19,14 @@
  *     the GGUF convention, which the pages do not spell out.
  *
  *  2. The unpacked weight, in the activation type t (fp16 or bf16):
- *        Q4_K : w = RN_t( RN_32( factor*q - bias ) ),  factor = d*sc, bias = dmin*m
- *        Q6_K : w = RN_t( RN_32( d*s*(q - 32) ) )
- *        W4A16: w = RN_t( RN_32( s*(q - zp) ) )
- *     The batched-prefill post ("The fix: K-parallel batched DMMV") forms
- *     each weight as factor*q - bias in single precision; the value is taken
- *     here as ONE round-to-nearest-even of the exact value into binary32,
- *     then one round-to-nearest-even into t.  For Q6_K and W4A16 the exact
- *     value always fits binary32, so the first rounding is the identity and
- *     w = RN_t(exact), the single rounding the W4A16 PR states ("the multiply
- *     that follows rounds once").  Every rounding below is done on exact
+ *        Q4_K : w = RN_t( d*sc*q - dmin*m )     (factor*q - bias, factor = d*sc, bias = dmin*m)
+ *        Q6_K : w = RN_t( d*s*(q - 32) )
+ *        W4A16: w = RN_t( s*(q - zp) )
+ *     RN_t is ONE round-to-nearest-even of the exact value into t: the W4A16
+ *     PR (section 1) subtracts exactly and lets the multiply that follows
+ *     round once; the same single rounding is read for the k-quants, whose
+ *     weight is the batched-prefill post's factor*q - bias ("The fix:
+ *     K-parallel batched DMMV").  Every rounding below is done on exact
  *     integers (value = n * 2^e), so nothing depends on the host's FPU.
  *
  *  3. Yref[m][n] = sum_k X[m][k] * W[k][n] in fp64, a naive triple loop
@@ -257,8 +255,8 @@ void qref_q6k_fields(const uint8_t *blk, uint16_t *d, int8_t s[16], uint8_t q[25
 /* Unpacked weight values                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* Q4_K: factor*q - bias with factor = d*sc, bias = dmin*m, all exact, then
- * binary32, then t.  Returns -1 if d or dmin is inf/nan. */
+/* Q4_K: factor*q - bias with factor = d*sc, bias = dmin*m, formed exactly and
+ * rounded once into t.  Returns -1 if d or dmin is inf/nan. */
 static int q4k_value(uint16_t d, uint16_t dmin, int sc, int mn, int q, int dtype, uint16_t *out)
 {
     int64_t nd, nm; int ed, em;
@@ -266,8 +264,7 @@ static int q4k_value(uint16_t d, uint16_t dmin, int sc, int mn, int q, int dtype
     int e0 = ed < em ? ed : em;
     int64_t a = (nd * sc * q) * ((int64_t)1 << (ed - e0));
     int64_t b = (nm * mn) * ((int64_t)1 << (em - e0));
-    xval v = rn_f32(a - b, e0);
-    if (v.inf) { *out = dtype == QREF_F16 ? (v.inf < 0 ? 0xFC00 : 0x7C00) : (v.inf < 0 ? 0xFF80 : 0x7F80); return 0; }
+    xval v = {a - b, e0, 0, a < b};
     *out = enc_t(v, dtype);
     return 0;
 }
@@ -277,7 +274,7 @@ static int q6k_value(uint16_t d, int s, int q, int dtype, uint16_t *out)
 {
     int64_t nd; int ed;
     if (f16_split(d, &nd, &ed)) return -1;
-    xval v = rn_f32(nd * s * (q - 32), ed);
+    xval v = {nd * s * (q - 32), ed, 0, 0};
     *out = enc_t(v, dtype);
     return 0;
 }
@@ -287,7 +284,7 @@ static int w4_value(uint16_t s, int q, int zp, int dtype, uint16_t *out)
 {
     int64_t ns; int es;
     if (f16_split(s, &ns, &es)) return -1;
-    xval v = rn_f32(ns * (q - zp), es);
+    xval v = {ns * (q - zp), es, 0, 0};
     *out = enc_t(v, dtype);
     return 0;
 }
@@ -320,7 +317,7 @@ int qref_dequant_q4k(const uint8_t *blocks, int64_t N, int64_t K, int dtype, uin
             qref_q4k_fields(blocks + (n * nb + b) * 144, &d, &dmin, sc, mn, q);
             for (int k = 0; k < 256; k++) {
                 int j = k / 32;
-                uint16_t w;
+                uint16_t w = 0;
                 bad |= q4k_value(d, dmin, sc[j], mn[j], q[k], dtype, &w) != 0;
                 W[(b * 256 + k) * N + n] = w;
             }
@@ -342,7 +339,7 @@ int qref_dequant_q6k(const uint8_t *blocks, int64_t N, int64_t K, int dtype, uin
         for (int64_t b = 0; b < nb; b++) {
             qref_q6k_fields(blocks + (n * nb + b) * 210, &d, s, q);
             for (int k = 0; k < 256; k++) {
-                uint16_t w;
+                uint16_t w = 0;
                 bad |= q6k_value(d, s[k / 16], q[k], dtype, &w) != 0;
                 W[(b * 256 + k) * N + n] = w;
             }
@@ -363,7 +360,7 @@ int qref_dequant_w4a16(const uint8_t *codes, const uint16_t *scales, const uint8
         for (int64_t k = 0; k < K; k++) {
             int64_t gi = k / group;
             int zp = zeros ? zeros[gi * N + n] : 8;
-            uint16_t w;
+            uint16_t w = 0;
             bad |= w4_value(scales[gi * N + n], codes[n * K + k], zp, dtype, &w) != 0;
             W[k * N + n] = w;
         }

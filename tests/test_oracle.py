@@ -255,11 +255,15 @@ def test_q6k_field_roundtrip():
 # ----------------------------------------------------------------------------
 
 def _expect(exact: Fraction, dtype: int) -> int:
-    """RN_t(RN_32(exact)) by brute-force nearest search."""
-    x32 = Fraction(float(nearest_even(exact, "f32")))
+    """RN_t(exact) by brute-force nearest search."""
     if dtype == oracle.F16:
-        return int(np.array(nearest_even(x32, "f16"), np.float16).view(np.uint16))
-    return nearest_even_bf16(x32)
+        return int(np.array(nearest_even(exact, "f16"), np.float16).view(np.uint16))
+    return nearest_even_bf16(exact)
+
+
+def _expect_two_step(exact: Fraction, dtype: int) -> int:
+    """RN_t(RN_32(exact)): what a binary32 intermediate would give."""
+    return _expect(Fraction(float(nearest_even(exact, "f32"))), dtype)
 
 
 @pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
@@ -275,7 +279,8 @@ def test_q4k_values_exact_rationals(dtype):
             exact = f16_val(d) * sc * q - f16_val(dm) * m
             got = oracle.q4k_weight(d, dm, sc, m, q, dtype)
             assert got == _expect(exact, dtype), (d, dm, sc, m, q)
-            # at these distributions the binary32 step is exact, so w = RN_t(exact)
+            # at these distributions the exact weight fits binary32, so a
+            # binary32 intermediate would give the same bits
             n_exact32 += Fraction(float(np.float32(float(exact)))) == exact
     assert n_exact32 == 64 * len(range(0, 256, 7))
 
@@ -283,7 +288,7 @@ def test_q4k_values_exact_rationals(dtype):
 @pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
 def test_q4k_values_wide_exponent_gap(dtype):
     """d and dmin far apart in magnitude: the exact value needs more than 24
-    bits, so the binary32 rounding step matters."""
+    bits, and the single rounding is still taken from the exact value."""
     rng = np.random.default_rng(41 + dtype)
     hit_inexact = 0
     for _ in range(3000):
@@ -296,24 +301,19 @@ def test_q4k_values_wide_exponent_gap(dtype):
     assert hit_inexact > 100
 
 
-def test_q4k_binary32_step():
-    """Inputs where forming the weight in binary32 first changes the final
-    rounding: factor*q sits exactly on a midpoint of the target grid and the
-    bias is a quarter of a binary32 ulp.  The oracle must give RN_t(RN_32(x)),
-    which differs here from RN_t(x)."""
+def test_q4k_single_rounding():
+    """Inputs where a binary32 intermediate would change the result: factor*q
+    sits exactly on a midpoint of the target grid and the bias is a quarter of
+    a binary32 ulp.  The oracle rounds the exact value once."""
     cases = [  # (d, dmin, sc, m, q, dtype)
         (0x3C01, 0x0001, 1, 1, 3, oracle.F16),   # 3075*2^-10 - 2^-24: fp16 tie at 1537.5 ulps
         (0x400C, 0x0001, 1, 1, 1, oracle.BF16),  # 1036*2^-9 - 2^-24: bf16 tie at 129.5 ulps
     ]
     for d, dm, sc, m, q, dtype in cases:
         exact = f16_val(d) * sc * q - f16_val(dm) * m
-        two_step = _expect(exact, dtype)
-        if dtype == oracle.F16:
-            direct = int(np.array(nearest_even(exact, "f16"), np.float16).view(np.uint16))
-        else:
-            direct = nearest_even_bf16(exact)
-        assert two_step != direct
-        assert oracle.q4k_weight(d, dm, sc, m, q, dtype) == two_step
+        direct = _expect(exact, dtype)
+        assert direct != _expect_two_step(exact, dtype)
+        assert oracle.q4k_weight(d, dm, sc, m, q, dtype) == direct
 
 
 @pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])

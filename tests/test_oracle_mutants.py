@@ -21,17 +21,17 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "qref.c")
 MUTANTS = [
     ("q4k nibble halves swapped", "q[64 * g + l] = b & 15;", "q[64 * g + l] = b >> 4;",
      ["test_q4k_field_roundtrip", "test_q4k_special_cases"]),
-    ("q4k min term dropped", "xval v = rn_f32(a - b, e0);", "xval v = rn_f32(a, e0);",
+    ("q4k min term dropped", "xval v = {a - b, e0, 0, a < b};", "xval v = {a, e0, 0, 0};",
      ["test_q4k_special_cases"]),
-    ("q4k min sign flipped", "xval v = rn_f32(a - b, e0);", "xval v = rn_f32(a + b, e0);",
+    ("q4k min sign flipped", "xval v = {a - b, e0, 0, a < b};", "xval v = {a + b, e0, 0, 0};",
      ["test_q4k_special_cases"]),
     ("q4k high scale bits from the wrong byte", "((s12[j] >> 6) << 4));", "((s12[j + 4] >> 6) << 4));",
      ["test_q4k_field_roundtrip"]),
     ("q4k sub-block index off", "int j = k / 32;", "int j = k / 64;", ["test_q4k_special_cases"]),
-    ("q4k binary32 step skipped", "xval v = rn_f32(a - b, e0);", "xval v = {a - b, e0, 0, a < b};",
-     ["test_q4k_binary32_step"]),
+    ("q4k extra binary32 rounding", "xval v = {a - b, e0, 0, a < b};", "xval v = rn_f32(a - b, e0);",
+     ["test_q4k_single_rounding"]),
     ("q6k scale per 32 weights", "s[k / 16]", "s[k / 32]", ["test_q6k_special_cases"]),
-    ("q6k offset 31", "nd * s * (q - 32)", "nd * s * (q - 31)", ["test_q6k_special_cases"]),
+    ("q6k offset 31", "{nd * s * (q - 32), ed, 0, 0}", "{nd * s * (q - 31), ed, 0, 0}", ["test_q6k_special_cases"]),
     ("q6k high pair shift", "(qh[32 * h + l] >> (2 * r)) & 3", "(qh[32 * h + l] >> r) & 3",
      ["test_q6k_field_roundtrip"]),
     ("w4a16 symmetric zero-point 7", "zeros[gi * N + n] : 8", "zeros[gi * N + n] : 7", ["test_w4a16_special_cases"]),
