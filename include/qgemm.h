@@ -30,14 +30,13 @@
  *     dtype is an error, never a silent fallback.
  *
  * Unpacked weight values (bit-exact contract)
- *   Q4_K : w = RN_t( RN_32( d*sc*q - dmin*m ) )      (sc, m: 6-bit; q: 4-bit)
- *   Q6_K : w = RN_t( d*s*(q - 32) )                  (s: int8 per 16; q: 6-bit)
- *   W4A16: w = RN_t( s*(q - zp) )                    (zp = 8 when has_zp == 0)
- *   RN_32 is one round-to-nearest-even into binary32 (the batched-prefill
- *   post forms factor*q - bias in float, "The fix: K-parallel batched DMMV");
- *   RN_t is round-to-nearest-even into fp16/bf16.  For Q6_K and W4A16 the
- *   exact value always fits binary32.  The products are accumulated in fp32;
- *   the order of that accumulation is unspecified (it depends on the rung).
+ *   Q4_K : w = RN_t( d*sc*q - dmin*m )      (sc, m: 6-bit; q: 4-bit)
+ *   Q6_K : w = RN_t( d*s*(q - 32) )         (s: int8 per 16; q: 6-bit)
+ *   W4A16: w = RN_t( s*(q - zp) )           (zp = 8 when has_zp == 0)
+ *   RN_t is one round-to-nearest-even of the exact value into fp16/bf16 (the
+ *   W4A16 PR, section 1: the subtraction is exact and the multiply that
+ *   follows rounds once).  The products are accumulated in fp32; the order
+ *   of that accumulation is unspecified (it depends on the rung).
  */
 #ifndef QGEMM_H
 #define QGEMM_H

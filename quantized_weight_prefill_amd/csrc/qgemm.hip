@@ -18,8 +18,12 @@
 //     shader does ("The fix: K-parallel batched DMMV"), with factor scaled by
 //     2^24 to cancel the code's scale, and rounds it to the operand type.
 //
-// Every product d*sc, dmin*m, d*s, s*zp is exact in binary32, so each weight
-// is RN_t(RN_32(exact)), bit-identical to the CPU oracle.
+// Every product d*sc, dmin*m, d*s, s*zp is exact in binary32 and v_fma_mix
+// rounds the exact a*b+c once, so an fp16 weight is RN_16(exact).  A bf16
+// weight goes through a binary32 FMA result and one conversion; that is
+// RN_bf16(exact) whenever the exact value fits binary32, which holds for Q6_K
+// and W4A16 always and for Q4_K whenever the exponents of d and dmin differ
+// by at most 3.  Other Q4_K bf16 runs take an exact two-sum path.
 //
 // MFMA operands are used "transposed": the weight fragment is the A operand
 // and the activation fragment the B operand, so the 16x16 accumulator of one
@@ -96,6 +100,38 @@ __device__ __forceinline__ uint32_t dq_pair<DT_BF16>(uint32_t t, float fa, float
     float b = __builtin_fmaf((float)h.y, fa, nb);
     bf16x2 r = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, r);
+}
+
+// bf16 weight of an exact value qs*fa + nb whose binary32 rounding may be
+// inexact (Q4_K with d and dmin far apart): qs*fa and nb are exact binary32
+// values, a two-sum gives the rounding error of their sum, and when the
+// binary32 sum sits exactly on a bf16 midpoint the error decides the side.
+__device__ __forceinline__ uint16_t exact_bf16(float qs, float fa, float nb)
+{
+#pragma clang fp contract(off)
+    const float A = qs * fa;  // exact: at most 21 significant bits
+    const float s = A + nb;
+    const float bb = s - A;
+    const float e = (A - (s - bb)) + (nb - bb);
+    uint32_t sb = __builtin_bit_cast(uint32_t, s);
+    if ((sb & 0xFFFFu) == 0x8000u && e != 0.0f) sb += ((e > 0.0f) == (s > 0.0f)) ? 1u : 0xFFFFFFFFu;
+    return __builtin_bit_cast(uint16_t, (__bf16)__builtin_bit_cast(float, sb));
+}
+
+__device__ __noinline__ void unpack_run4_exact_bf16(u32x4 codes, float fa, float nb, u32x4 (&out)[4])
+{
+    const float fa16 = fa * 0.0625f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t x = codes[i], x8 = x >> 8;
+        const uint32_t t[4] = {x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u};
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const f16x2 h = __builtin_bit_cast(f16x2, t[p]);
+            const float f = (p & 1) ? fa16 : fa;
+            out[i][p] = (uint32_t)exact_bf16((float)h.x, f, nb) | ((uint32_t)exact_bf16((float)h.y, f, nb) << 16);
+        }
+    }
 }
 
 // 32 four-bit codes in pair order -> four fragments of eight weights.
@@ -191,6 +227,14 @@ __device__ __forceinline__ void unpack_unit(const Unit<FMT> &u, int c, int g, u3
         }
         const float fa = d * (float)sc * kTwo24;  // factor = d*sc, exact in binary32
         const float nb = -(dmin * (float)m);      // bias = dmin*m, exact
+        if constexpr (DT == DT_BF16) {
+            // exponent fields of d and dmin (a subnormal counts as exponent 1)
+            const int ed = max((int)((u.hd[0] >> 10) & 31u), 1), em = max((int)((u.hd[0] >> 26) & 31u), 1);
+            if (sc != 0 && m != 0 && (ed - em > 3 || em - ed > 3)) {
+                unpack_run4_exact_bf16(u.codes, fa, nb, out);
+                return;
+            }
+        }
         unpack_run4<DT>(u.codes, fa, nb, out);
     } else if constexpr (FMT == FMT_Q6K) {
         const float d = f16_to_f32(u.aux);
