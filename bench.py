@@ -189,12 +189,18 @@ def cpu_baseline(gemms, target_s: float) -> dict:
         t0 = time.perf_counter()
         Ws.append(oracle.dequant(g["fmt"], g["enc"], g["N"], g["K"], g["dt"]))
         t_deq += time.perf_counter() - t0
-    # calibrate rows so the GEMM part takes about target_s - t_deq seconds
-    t0 = time.perf_counter()
-    for g, W in zip(gemms, Ws):
-        oracle.gemm(g["X"][:1], W, g["dt"], want_bound=False)
-    t_one = time.perf_counter() - t0
-    rows = int(max(1, min(min(g["M"] for g in gemms), (target_s - t_deq) / max(t_one, 1e-6))))
+    # grow the row sample until the GEMM part takes about target_s - t_deq
+    # seconds (or covers every row); a row costs the same in every position
+    rows, t_gemm = 1, 0.0
+    Mmin = min(g["M"] for g in gemms)
+    while True:
+        t0 = time.perf_counter()
+        for g, W in zip(gemms, Ws):
+            oracle.gemm(g["X"][:rows], W, g["dt"], want_bound=False)
+        t_gemm = time.perf_counter() - t0
+        if rows >= Mmin or t_deq + t_gemm >= 0.5 * target_s:
+            break
+        rows = min(Mmin, rows * 4)
     t_gemm, full = 0.0, t_deq
     for g, W in zip(gemms, Ws):
         t0 = time.perf_counter()

@@ -79,11 +79,18 @@ SIGNATURES = {
 
 
 def lib():
-    """The loaded C library (raises if it has not been built)."""
+    """The loaded C library (raises if it has not been built).
+
+    PyTorch ships its own HIP runtime under the same SONAME as the system one.
+    torch is imported first so that opening libqgemm.so binds it to the HIP
+    runtime already in the process: device pointers, streams and kernels then
+    all belong to one runtime."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing; build it with `python -m quantized_weight_prefill_amd.build`")
+        import torch  # noqa: F401  (binds libamdhip64.so.7 to torch's runtime)
+
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
 
 #include "qgemm.h"
 
@@ -459,6 +460,135 @@ __global__ void __launch_bounds__(256) k_tile(Args a)
 }
 
 // ---------------------------------------------------------------------------
+// Streaming tile kernel: long prefill.
+//
+// Four waves own a (4*WM) x (16*PB) output tile; wave w owns rows
+// [m0 + WM*w, m0 + WM*(w+1)) and all 16*PB columns, so no activation element
+// is loaded by two waves.  Per 128-wide K chunk:
+//   * every thread loads UPT packed weight runs of chunk c+1 and, after the
+//     chunk-c MFMAs are issued, unpacks them into the other half of a
+//     double-buffered LDS weight tile (each weight unpacked once per
+//     workgroup and shared by all 4*WM rows);
+//   * each wave loads its own activation fragments of chunk c+1 straight
+//     from global memory into VGPRs (no LDS round trip for X);
+//   * one barrier per chunk.
+// Inside one MFMA, lane (r, g) of instruction i carries k = 128c + 32i + 8g
+// + 0..7 in both operands, so an activation load of instruction i reads 64
+// contiguous bytes of each row and a weight run (32 consecutive k) fills the
+// four lane groups of one instruction.
+// Workgroups are numbered so that consecutive tiles (same row block,
+// neighbouring column panels) land on the same XCD, whose L2 then serves the
+// shared activation rows.
+// ---------------------------------------------------------------------------
+template <int FMT, int DT, int WM, int PB>
+__global__ void __launch_bounds__(256) k_stream(Args a)
+{
+    constexpr int RBW = WM / 16;          // row blocks per wave
+    constexpr int UPT = PB * 64 / 256;    // weight runs per thread per chunk
+    static_assert(UPT >= 1 && PB * 64 % 256 == 0, "PB must be a multiple of 4");
+    __shared__ u32x4 sW[2][PB][4][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tn = (a.np + PB - 1) / PB, tm = (a.M + 4 * WM - 1) / (4 * WM);
+    const int T = tn * tm;
+    // XCD-aware renumbering: WG b runs on XCD b % 8; give each XCD a contiguous
+    // range of logical tiles (a bijection on [0, T)).
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    const int L = xcd * (T >> 3) + min(xcd, T & 7) + slot;
+    const int mt = L / tn, nt = L - mt * tn;
+    const int m0 = mt * 4 * WM + w * WM, p0 = nt * PB;
+    const int nch = a.K / kChunk;
+    const int r16 = lane & 15, g4 = lane >> 4;
+
+    const uint16_t *xrow[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; rb++) {
+        int r = m0 + 16 * rb + r16;
+        r = r < a.M ? r : a.M - 1;
+        xrow[rb] = a.X + (long long)r * a.K + 8 * g4;
+    }
+
+    f32x4 acc[PB][RBW];
+#pragma unroll
+    for (int pb = 0; pb < PB; pb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // this thread's weight runs: u = tid + 256*s -> panel u/64, run (u/16)%4, column u%16
+    int upanel[UPT], urun[UPT], ucol[UPT];
+#pragma unroll
+    for (int s = 0; s < UPT; s++) {
+        const int u = tid + 256 * s;
+        int p = p0 + (u >> 6);
+        upanel[s] = p < a.np ? p : a.np - 1;
+        urun[s] = (u >> 4) & 3;
+        ucol[s] = u & 15;
+    }
+
+    Unit<FMT> un[UPT];
+    u32x4 xf[RBW][4], xn[RBW][4];
+
+    // prologue: chunk 0 into LDS buffer 0 and registers
+#pragma unroll
+    for (int s = 0; s < UPT; s++) load_unit<FMT>(a, upanel[s], 0, urun[s], ucol[s], un[s]);
+#pragma unroll
+    for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + 32 * i);
+#pragma unroll
+    for (int s = 0; s < UPT; s++) {
+        u32x4 f[4];
+        unpack_unit<FMT, DT>(un[s], 0, urun[s], f);
+        const int pb = (tid + 256 * s) >> 6;
+#pragma unroll
+        for (int j = 0; j < 4; j++) sW[0][pb][urun[s]][j * 16 + ucol[s]] = f[j];
+    }
+    __syncthreads();
+
+    for (int c = 0; c < nch; c++) {
+        const int buf = c & 1;
+        const bool more = c + 1 < nch;
+        if (more) {
+#pragma unroll
+            for (int s = 0; s < UPT; s++) load_unit<FMT>(a, upanel[s], c + 1, urun[s], ucol[s], un[s]);
+#pragma unroll
+            for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) xn[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * (c + 1) + 32 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            u32x4 wf[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; pb++) wf[pb] = sW[buf][pb][i][lane];
+#pragma unroll
+            for (int pb = 0; pb < PB; pb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = mma<DT>(wf[pb], xf[rb][i], acc[pb][rb]);
+        }
+        if (more) {
+#pragma unroll
+            for (int s = 0; s < UPT; s++) {
+                u32x4 f[4];
+                unpack_unit<FMT, DT>(un[s], c + 1, urun[s], f);
+                const int pb = (tid + 256 * s) >> 6;
+#pragma unroll
+                for (int j = 0; j < 4; j++) sW[buf ^ 1][pb][urun[s]][j * 16 + ucol[s]] = f[j];
+            }
+#pragma unroll
+            for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) xf[rb][i] = xn[rb][i];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int pb = 0; pb < PB; pb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++) store_block<DT>(a, acc[pb][rb], m0 + 16 * rb, 16 * (p0 + pb), lane);
+}
+
+// ---------------------------------------------------------------------------
 // Staged dequant: the same unpack, written out as logical W[K][N].
 // One thread per (panel, chunk, run, column).
 // ---------------------------------------------------------------------------
@@ -492,8 +622,16 @@ __global__ void __launch_bounds__(256) k_dequant(Args a, uint16_t *Wout)
 // Host side: validation, the M-ladder, launches.
 // ---------------------------------------------------------------------------
 
-enum Rung { RUNG_SMALL_M = 0, RUNG_SKINNY_N = 1, RUNG_TILE_128 = 2, RUNG_COUNT = 3 };
-const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "tile-128x128"};
+enum Rung {
+    RUNG_SMALL_M = 0,
+    RUNG_SKINNY_N = 1,
+    RUNG_TILE_128 = 2,
+    RUNG_STREAM_256 = 3,
+    RUNG_STREAM_128 = 4,
+    RUNG_COUNT = 5
+};
+const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "tile-128x128", "stream-256x128",
+                                            "stream-128x128"};
 
 struct Plan {
     int rung;
@@ -544,6 +682,17 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.lds = 0;
         return true;
     }
+    case RUNG_STREAM_256:
+    case RUNG_STREAM_128: {
+        pl.rows = rung == RUNG_STREAM_256 ? 256 : 128;
+        pl.cols = 128;
+        pl.waves = 4;
+        pl.kw = 1;
+        // one-dimensional grid: the kernel renumbers tiles per XCD
+        pl.grid = dim3((unsigned)(ceil_div(np, 8) * ceil_div(M, pl.rows)), 1, 1);
+        pl.lds = 0;
+        return true;
+    }
     default:
         return false;
     }
@@ -562,9 +711,8 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 // the LDS-shared tile.
 int select_rung(long long M, long long N)
 {
-    if (N <= 64) return RUNG_SKINNY_N;
-    if (M <= 64) return RUNG_SMALL_M;
-    return RUNG_TILE_128;
+    if (N <= 64 || M <= 64) return RUNG_SKINNY_N;
+    return RUNG_STREAM_128;
 }
 
 template <int FMT, int DT, int RB, int PN>
@@ -599,6 +747,14 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         hipLaunchKernelGGL((k_tile<FMT, DT, 128, 128, 2, 2>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
+    if (pl.rung == RUNG_STREAM_256) {
+        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    if (pl.rung == RUNG_STREAM_128) {
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     return launch_direct<FMT, DT>(pl, a, s);
 }
 
@@ -610,6 +766,15 @@ hipError_t launch(int fmt, int dtype, const Plan &pl, const Args &a, hipStream_t
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A failed launch is reported once on stderr with HIP's own text; the caller
+// gets QGEMM_ERR_HIP.
+int launch_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return QGEMM_OK;
+    fprintf(stderr, "qgemm: %s launch failed: %s (%d)\n", what, hipGetErrorString(e), (int)e);
+    return QGEMM_ERR_HIP;
+}
 
 // Shape rules shared by every device entry point.
 int check_shape(int fmt, long long M, long long N, long long K, long long group)
@@ -662,7 +827,7 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     if (!make_plan(rung < 0 ? select_rung(M, N) : rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
     Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
     a.kw = pl.kw;
-    return launch(fmt, dtype, pl, a, (hipStream_t)stream) == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+    return launch_status(launch(fmt, dtype, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
 }
 
 void fill_info(const Plan &pl, int32_t *info)
@@ -759,7 +924,7 @@ int qgemm_dequant(int format, const void *W, void *Wout, int64_t N, int64_t K, i
     else if (format == FMT_Q6K) { if (dtype == DT_F16) QG_DQ(FMT_Q6K, DT_F16); else QG_DQ(FMT_Q6K, DT_BF16); }
     else { if (dtype == DT_F16) QG_DQ(FMT_W4, DT_F16); else QG_DQ(FMT_W4, DT_BF16); }
 #undef QG_DQ
-    return hipGetLastError() == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+    return launch_status(hipGetLastError(), "dequant");
 }
 
 }  // extern "C"

@@ -209,10 +209,8 @@ def test_ladder_sweep(fmt, dtype):
             assert info["grid_y"] * info["rows"] >= M
             assert info["k_step"] % 32 == 0 and info["k_step"] <= K
             assert (K // info["k_step"]) >= info["k_split"] >= 1
-            if N <= 64:
+            if N <= 64 or M <= 64:
                 assert info["name"] == "direct-skinny-n"
-            elif M <= 64:
-                assert info["name"] == "direct-small-m"
             for r in range(qg.num_rungs()):
                 ri = qg.rung_info(r, fmt, M, N, K, dtype)
                 assert ri["grid_x"] * ri["cols"] >= N and ri["grid_y"] * ri["rows"] >= M

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 FMTS = [("q4k", False), ("q6k", False), ("w4a16", False), ("w4a16", True)]
 FMT_IDS = ["q4k", "q6k", "w4a16-asym", "w4a16-sym"]
 DTYPES = [qg.F16, qg.BF16]
-RUNGS = list(range(3))
+RUNGS = list(range(qg.num_rungs()))
 
 
 def _case(fmt, sym, M, N, K, dtype, seed, group=128):
