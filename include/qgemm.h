@@ -153,7 +153,7 @@ int qgemm_w4a16(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t 
  * K, dtype) to a rung.  qgemm_select_rung writes 8 integers:
  *   [0] rung id  [1] rows per tile  [2] columns per tile  [3] K per step
  *   [4] waves per workgroup  [5] K-split ways inside a workgroup
- *   [6] grid x  [7] grid y
+ *   [6] output tiles along N  [7] output tiles along M
  * and returns QGEMM_OK, or an error for an illegal shape. */
 int qgemm_num_rungs(void);
 const char *qgemm_rung_name(int rung); /* NULL for an unknown rung */

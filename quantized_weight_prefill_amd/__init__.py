@@ -289,7 +289,7 @@ def dequant(fmt, wp, N: int, K: int, dtype, group: int = 0, has_zp: bool = False
 # M-ladder queries
 # ---------------------------------------------------------------------------
 
-_INFO_KEYS = ("rung", "rows", "cols", "k_step", "waves", "k_split", "grid_x", "grid_y")
+_INFO_KEYS = ("rung", "rows", "cols", "k_step", "waves", "k_split", "tiles_n", "tiles_m")
 
 
 def num_rungs() -> int:

@@ -635,6 +635,7 @@ const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n",
 
 struct Plan {
     int rung;
+    int tiles_n, tiles_m;  // output tiles along N and along M
     int rows, cols;    // output tile
     int waves, kw;     // waves per workgroup, K-split ways
     int rb, pn;        // direct kernel: row blocks / panels per wave
@@ -679,6 +680,8 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.waves = 4;
         pl.kw = 1;
         pl.grid = dim3((unsigned)ceil_div(np, 8), (unsigned)ceil_div(M, 128), 1);
+        pl.tiles_n = (int)pl.grid.x;
+        pl.tiles_m = (int)pl.grid.y;
         pl.lds = 0;
         return true;
     }
@@ -689,7 +692,9 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.waves = 4;
         pl.kw = 1;
         // one-dimensional grid: the kernel renumbers tiles per XCD
-        pl.grid = dim3((unsigned)(ceil_div(np, 8) * ceil_div(M, pl.rows)), 1, 1);
+        pl.tiles_n = ceil_div(np, 8);
+        pl.tiles_m = ceil_div(M, pl.rows);
+        pl.grid = dim3((unsigned)(pl.tiles_n * pl.tiles_m), 1, 1);
         pl.lds = 0;
         return true;
     }
@@ -698,6 +703,8 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     }
     pl.rows = 16 * pl.rb;
     pl.cols = 16 * pl.pn;
+    pl.tiles_n = (int)pl.grid.x;
+    pl.tiles_m = (int)pl.grid.y;
     pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch);
     pl.waves = pl.kw;
     pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
@@ -838,8 +845,8 @@ void fill_info(const Plan &pl, int32_t *info)
     info[3] = kChunk;
     info[4] = pl.waves;
     info[5] = pl.kw;
-    info[6] = (int32_t)pl.grid.x;
-    info[7] = (int32_t)pl.grid.y;
+    info[6] = pl.tiles_n;
+    info[7] = pl.tiles_m;
 }
 
 }  // namespace

@@ -205,15 +205,15 @@ def test_ladder_sweep(fmt, dtype):
         for M in list(range(1, 130)) + [255, 256, 257, 511, 512, 658, 1024, 2048, 4096, 8192]:
             info = qg.select_rung(fmt, M, N, K, dtype)
             assert info["rung"] in range(qg.num_rungs())
-            assert info["grid_x"] * info["cols"] >= N
-            assert info["grid_y"] * info["rows"] >= M
+            assert info["tiles_n"] * info["cols"] >= N
+            assert info["tiles_m"] * info["rows"] >= M
             assert info["k_step"] % 32 == 0 and info["k_step"] <= K
             assert (K // info["k_step"]) >= info["k_split"] >= 1
             if N <= 64 or M <= 64:
                 assert info["name"] == "direct-skinny-n"
             for r in range(qg.num_rungs()):
                 ri = qg.rung_info(r, fmt, M, N, K, dtype)
-                assert ri["grid_x"] * ri["cols"] >= N and ri["grid_y"] * ri["rows"] >= M
+                assert ri["tiles_n"] * ri["cols"] >= N and ri["tiles_m"] * ri["rows"] >= M
 
 
 def test_ladder_rejects_bad_shapes():
