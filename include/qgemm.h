@@ -120,8 +120,8 @@ int qgemm_q6k_unpack(const void *packed, int64_t N, int64_t K, void *blocks, siz
 /* W4A16 (GPTQ-style, the W4A16 PR, section 1): codes [N][K], one 4-bit code
  * (0..15) per byte; scales [K/group][N] fp16 bits; zeros [K/group][N]
  * (0..15) or NULL for the symmetric variant (zero-point 8, and then no
- * zero-point bytes are stored).  K % 128 == 0, group % 32 == 0,
- * K % group == 0.  Codes or zeros above 15 give QGEMM_ERR_INPUT. */
+ * zero-point bytes are stored).  K % 128 == 0, group a power of two of at
+ * least 32, K % group == 0.  Codes or zeros above 15 give QGEMM_ERR_INPUT. */
 size_t qgemm_w4a16_packed_bytes(int64_t N, int64_t K, int64_t group_size, int has_zp);
 int qgemm_w4a16_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
                      int64_t group_size, void *out, size_t out_bytes);
@@ -141,7 +141,7 @@ int qgemm_q6k(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N,
               void *stream);
 
 /* W4A16 weights (the W4A16 PR, sections 1 and 2).  K % 128 == 0,
- * group_size % 32 == 0, K % group_size == 0; has_zp selects the asymmetric
+ * group_size a power of two >= 32, K % group_size == 0; has_zp selects the asymmetric
  * (stored zero-points) or symmetric (zero-point 8) variant and must match
  * the packing. */
 int qgemm_w4a16(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size,

@@ -6,7 +6,6 @@
 // shuffling: no value is rounded or rescaled, so unpack(pack(x)) == x.
 #include <cstdint>
 #include <cstring>
-#include <vector>
 
 #include "qgemm.h"
 
@@ -22,7 +21,7 @@ bool kquant_shape_ok(int64_t N, int64_t K) { return N >= 1 && K >= 256 && K % 25
 
 bool w4_shape_ok(int64_t N, int64_t K, int64_t g)
 {
-    return N >= 1 && K >= 128 && K % 128 == 0 && g >= 32 && g % 32 == 0 && K % g == 0;
+    return N >= 1 && K >= 128 && K % 128 == 0 && g >= 32 && (g & (g - 1)) == 0 && K % g == 0;
 }
 
 // Position of code t (0..31) of a 32-code run in "pair order": word t/8,

@@ -119,101 +119,80 @@ __device__ __forceinline__ uint16_t exact_bf16(float qs, float fa, float nb)
     return __builtin_bit_cast(uint16_t, (__bf16)__builtin_bit_cast(float, sb));
 }
 
-__device__ __noinline__ void unpack_run4_exact_bf16(u32x4 codes, float fa, float nb, u32x4 (&out)[4])
-{
-    const float fa16 = fa * 0.0625f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t x = codes[i], x8 = x >> 8;
-        const uint32_t t[4] = {x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u};
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            const f16x2 h = __builtin_bit_cast(f16x2, t[p]);
-            const float f = (p & 1) ? fa16 : fa;
-            out[i][p] = (uint32_t)exact_bf16((float)h.x, f, nb) | ((uint32_t)exact_bf16((float)h.y, f, nb) << 16);
-        }
-    }
-}
-
-// 32 four-bit codes in pair order -> four fragments of eight weights.
-// fa = factor * 2^24 and nb = -bias apply to all 32.
-template <int DT>
-__device__ __forceinline__ void unpack_run4(u32x4 codes, float fa, float nb, u32x4 (&out)[4])
-{
-    const float fa16 = fa * 0.0625f;  // for the pairs read as 16*code
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t x = codes[i], x8 = x >> 8;
-        out[i][0] = dq_pair<DT>(x & 0x000F000Fu, fa, nb);
-        out[i][1] = dq_pair<DT>(x & 0x00F000F0u, fa16, nb);
-        out[i][2] = dq_pair<DT>(x8 & 0x000F000Fu, fa, nb);
-        out[i][3] = dq_pair<DT>(x8 & 0x00F000F0u, fa16, nb);
-    }
-}
-
-// 32 six-bit Q6_K codes: low nibbles in pair order plus the high pairs.
-// Codes 0..15 use (fa0, nb0), codes 16..31 use (fa1, nb1).
-template <int DT>
-__device__ __forceinline__ void unpack_run6(u32x4 lo, u32x2 hi, float fa0, float nb0, float fa1, float nb1,
-                                            u32x4 (&out)[4])
-{
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float fa = i < 2 ? fa0 : fa1, nb = i < 2 ? nb0 : nb1;
-        const float fa16 = fa * 0.0625f;
-        const uint32_t x = lo[i], x8 = x >> 8, h = hi[i >> 1];
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            const uint32_t lpart = (p < 2 ? x : x8) & ((p & 1) ? 0x00F000F0u : 0x000F000Fu);
-            const int sigma = 4 * (i & 1) + p, T = (p & 1) ? 8 : 4, sh = 2 * sigma - T;
-            const uint32_t hs = sh >= 0 ? (h >> sh) : (h << (-sh));
-            const uint32_t t = lpart | (hs & (0x00030003u << T));
-            out[i][p] = dq_pair<DT>(t, (p & 1) ? fa16 : fa, nb);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Per-unit loads: panel p, chunk c (128 K), lane group g (32-wide run), column
-// col of the panel.
+// One lane's weight run: panel p, lane group g (the g-th 32-wide K run of a
+// 128-wide chunk) and column col of the panel.  RunSrc holds the addresses,
+// fixed for the whole K loop; load() only issues raw loads (no arithmetic on
+// loaded bytes, so nothing waits on memory until the unpack).
 // ---------------------------------------------------------------------------
 
 template <int FMT>
-struct Unit {
+struct RunRaw {
     u32x4 codes;
-    u32x4 hd;    // Q4_K: d|dmin, 3 words of 6-bit scales; Q6_K: 16 int8 scales
-    u32x2 hi;    // Q6_K high pairs
-    uint32_t aux;  // Q6_K: d bits; W4A16: scale bits | zero-point << 16
+    u32x4 hd;     // Q4_K: d|dmin and the 12 scale bytes; Q6_K: 16 int8 scales
+    u32x2 hi;     // Q6_K high pairs
+    uint32_t d;   // Q6_K: fp16 d; W4A16: fp16 scale (raw 16-bit load)
+    uint32_t z;   // W4A16: byte holding the zero-point nibble
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_unit(const Args &a, int p, int c, int g, int col, Unit<FMT> &u)
-{
-    if constexpr (FMT == FMT_Q4K) {
-        const uint8_t *rec = a.W + ((long long)p * (a.K >> 8) + (c >> 1)) * kQ4kRec;
-        u.hd = *(const u32x4 *)(rec + 16 * col);
-        u.codes = *(const u32x4 *)(rec + 256 + 1024 * (c & 1) + (16 * g + col) * 16);
-    } else if constexpr (FMT == FMT_Q6K) {
-        const uint8_t *rec = a.W + ((long long)p * (a.K >> 8) + (c >> 1)) * kQ6kRec;
-        u.aux = *(const uint16_t *)(rec + 2 * col);
-        u.hd = *(const u32x4 *)(rec + 32 + 16 * col);
-        u.codes = *(const u32x4 *)(rec + 288 + 1024 * (c & 1) + (16 * g + col) * 16);
-        u.hi = *(const u32x2 *)(rec + 2336 + 512 * (c & 1) + (16 * g + col) * 8);
-    } else {
-        u.codes = *(const u32x4 *)(a.W + ((long long)p * (a.K >> 7) + c) * 1024 + (16 * g + col) * 16);
-        const int ng = a.K / a.group;
-        const int j = (kChunk * c + 32 * g) / a.group;
-        const long long gi = (long long)p * ng + j;
-        uint32_t s = *(const uint16_t *)(a.W + a.w4_sreg + gi * 32 + 2 * col);
-        uint32_t zp = 8;
-        if (a.has_zp) zp = (a.W[a.w4_zreg + gi * 8 + (col >> 1)] >> (4 * (col & 1))) & 15u;
-        u.aux = s | (zp << 16);
+struct RunSrc {
+    const uint8_t *rec;    // Q4_K/Q6_K: record (panel, super-block 0); W4A16: codes of chunk 0
+    const uint8_t *sc;     // W4A16: scale of (panel, group 0, col)
+    const uint8_t *zp;     // W4A16: zero byte of (panel, group 0, col) (a scale byte when symmetric)
+    int g, col, gshift, has_zp;
+
+    __device__ __forceinline__ void init(const Args &a, int p, int g_, int col_)
+    {
+        g = g_;
+        col = col_;
+        has_zp = a.has_zp;
+        if constexpr (FMT == FMT_Q4K) {
+            rec = a.W + (long long)p * (a.K >> 8) * kQ4kRec;
+        } else if constexpr (FMT == FMT_Q6K) {
+            rec = a.W + (long long)p * (a.K >> 8) * kQ6kRec;
+        } else {
+            rec = a.W + (long long)p * (a.K >> 7) * 1024 + (16 * g + col) * 16;
+            gshift = 31 - __builtin_clz((unsigned)a.group);
+            const long long gi = (long long)p * (a.K >> gshift);
+            sc = a.W + a.w4_sreg + gi * 32 + 2 * col;
+            zp = a.has_zp ? a.W + a.w4_zreg + gi * 8 + (col >> 1) : sc;
+        }
     }
-}
+
+    __device__ __forceinline__ void load(int c, RunRaw<FMT> &r) const
+    {
+        if constexpr (FMT == FMT_Q4K) {
+            const uint8_t *b = rec + (long long)(c >> 1) * kQ4kRec;
+            r.hd = *(const u32x4 *)(b + 16 * col);
+            r.codes = *(const u32x4 *)(b + 256 + 1024 * (c & 1) + (16 * g + col) * 16);
+        } else if constexpr (FMT == FMT_Q6K) {
+            const uint8_t *b = rec + (long long)(c >> 1) * kQ6kRec;
+            r.d = *(const uint16_t *)(b + 2 * col);
+            r.hd = *(const u32x4 *)(b + 32 + 16 * col);
+            r.codes = *(const u32x4 *)(b + 288 + 1024 * (c & 1) + (16 * g + col) * 16);
+            r.hi = *(const u32x2 *)(b + 2336 + 512 * (c & 1) + (16 * g + col) * 8);
+        } else {
+            r.codes = *(const u32x4 *)(rec + (long long)c * 1024);
+            const int j = (kChunk * c + 32 * g) >> gshift;
+            r.d = *(const uint16_t *)(sc + (long long)j * 32);
+            r.z = *(zp + (long long)j * (has_zp ? 8 : 32));
+        }
+    }
+};
+
+// Per-run dequant constants (computed once per run, reused by its four words).
+struct RunParams {
+    float fa, nb;    // words 0..3 (Q6_K: words 0..1): factor*2^24 and -bias
+    float fa1, nb1;  // Q6_K words 2..3
+    bool exact;      // bf16 Q4_K run whose values may not fit binary32
+};
 
 template <int FMT, int DT>
-__device__ __forceinline__ void unpack_unit(const Unit<FMT> &u, int c, int g, u32x4 (&out)[4])
+__device__ __forceinline__ RunParams run_params(const RunRaw<FMT> &u, const RunSrc<FMT> &src, int c)
 {
+    RunParams pr{};
+    const int g = src.g;
     if constexpr (FMT == FMT_Q4K) {
         const float d = f16_to_f32(u.hd[0] & 0xFFFFu), dmin = f16_to_f32(u.hd[0] >> 16);
         const uint32_t s0 = u.hd[1], s1 = u.hd[2], s2 = u.hd[3];
@@ -226,29 +205,77 @@ __device__ __forceinline__ void unpack_unit(const Unit<FMT> &u, int c, int g, u3
             sc = ((s2 >> sh) & 15u) | (((s0 >> (sh + 6)) & 3u) << 4);
             m = ((s2 >> (sh + 4)) & 15u) | (((s1 >> (sh + 6)) & 3u) << 4);
         }
-        const float fa = d * (float)sc * kTwo24;  // factor = d*sc, exact in binary32
-        const float nb = -(dmin * (float)m);      // bias = dmin*m, exact
+        pr.fa = d * (float)sc * kTwo24;  // factor = d*sc, exact in binary32
+        pr.nb = -(dmin * (float)m);      // bias = dmin*m, exact
+        pr.exact = false;
         if constexpr (DT == DT_BF16) {
             // exponent fields of d and dmin (a subnormal counts as exponent 1)
             const int ed = max((int)((u.hd[0] >> 10) & 31u), 1), em = max((int)((u.hd[0] >> 26) & 31u), 1);
-            if (sc != 0 && m != 0 && (ed - em > 3 || em - ed > 3)) {
-                unpack_run4_exact_bf16(u.codes, fa, nb, out);
-                return;
-            }
+            pr.exact = sc != 0 && m != 0 && (ed - em > 3 || em - ed > 3);
         }
-        unpack_run4<DT>(u.codes, fa, nb, out);
     } else if constexpr (FMT == FMT_Q6K) {
-        const float d = f16_to_f32(u.aux);
+        const float d = f16_to_f32(u.d);
         const uint32_t w = u.hd[2 * (c & 1) + (g >> 1)];
         const int sh = 16 * (g & 1);
         const float a0 = d * (float)(int)(int8_t)((w >> sh) & 0xFFu);  // exact
         const float a1 = d * (float)(int)(int8_t)((w >> (sh + 8)) & 0xFFu);
-        unpack_run6<DT>(u.codes, u.hi, a0 * kTwo24, -32.0f * a0, a1 * kTwo24, -32.0f * a1, out);
+        pr.fa = a0 * kTwo24;
+        pr.nb = -32.0f * a0;
+        pr.fa1 = a1 * kTwo24;
+        pr.nb1 = -32.0f * a1;
     } else {
-        const float s = f16_to_f32(u.aux & 0xFFFFu);
-        const float zp = (float)(u.aux >> 16);
-        unpack_run4<DT>(u.codes, s * kTwo24, -(zp * s), out);
+        const float s = f16_to_f32(u.d);
+        const float zp = src.has_zp ? (float)((u.z >> (4 * (src.col & 1))) & 15u) : 8.0f;
+        pr.fa = s * kTwo24;
+        pr.nb = -(zp * s);
     }
+    return pr;
+}
+
+// Word i of a run: eight weights k0+8i .. k0+8i+7, one MFMA operand fragment.
+template <int FMT, int DT>
+__device__ __forceinline__ u32x4 unpack_word(const RunRaw<FMT> &u, const RunParams &pr, int i)
+{
+    u32x4 out;
+    const uint32_t x = u.codes[i], x8 = x >> 8;
+    if constexpr (FMT == FMT_Q6K) {
+        const float fa = i < 2 ? pr.fa : pr.fa1, nb = i < 2 ? pr.nb : pr.nb1;
+        const float fa16 = fa * 0.0625f;
+        const uint32_t h = u.hi[i >> 1];
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const uint32_t lpart = (p < 2 ? x : x8) & ((p & 1) ? 0x00F000F0u : 0x000F000Fu);
+            const int sigma = 4 * (i & 1) + p, T = (p & 1) ? 8 : 4, sh = 2 * sigma - T;
+            const uint32_t hs = sh >= 0 ? (h >> sh) : (h << (-sh));
+            out[p] = dq_pair<DT>(lpart | (hs & (0x00030003u << T)), (p & 1) ? fa16 : fa, nb);
+        }
+    } else {
+        const uint32_t t[4] = {x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u};
+        const float fa16 = pr.fa * 0.0625f;
+        if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
+            if (pr.exact) {
+#pragma unroll
+                for (int p = 0; p < 4; p++) {
+                    const f16x2 h = __builtin_bit_cast(f16x2, t[p]);
+                    const float f = (p & 1) ? fa16 : pr.fa;
+                    out[p] = (uint32_t)exact_bf16((float)h.x, f, pr.nb) |
+                             ((uint32_t)exact_bf16((float)h.y, f, pr.nb) << 16);
+                }
+                return out;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 4; p++) out[p] = dq_pair<DT>(t[p], (p & 1) ? fa16 : pr.fa, pr.nb);
+    }
+    return out;
+}
+
+template <int FMT, int DT>
+__device__ __forceinline__ void unpack_run(const RunRaw<FMT> &u, const RunSrc<FMT> &src, int c, u32x4 (&out)[4])
+{
+    const RunParams pr = run_params<FMT, DT>(u, src, c);
+#pragma unroll
+    for (int i = 0; i < 4; i++) out[i] = unpack_word<FMT, DT>(u, pr, i);
 }
 
 template <int DT>
@@ -305,8 +332,9 @@ __device__ __forceinline__ void store_block(const Args &a, f32x4 v, int m_base, 
 // for RB row blocks of 16 tokens; the a.kw waves of a workgroup split the K
 // loop (the K-parallel shape of the batched-prefill post: many lanes share a
 // row reduction, then one reduction per output at the end) and combine their
-// partial sums through LDS.  Grid: x = panel groups of PN panels, y = row
-// groups of 16*RB rows.
+// partial sums through LDS.  The raw weight bytes and activation fragments of
+// chunk c+1 are in flight while chunk c is unpacked and multiplied.  Grid:
+// x = panel groups of PN panels, y = row groups of 16*RB rows.
 // ---------------------------------------------------------------------------
 template <int FMT, int DT, int RB, int PN>
 __global__ void __launch_bounds__(512) k_direct(Args a)
@@ -332,27 +360,46 @@ __global__ void __launch_bounds__(512) k_direct(Args a)
         r = r < a.M ? r : a.M - 1;  // clamped rows are computed and discarded
         xrow[rb] = a.X + (long long)r * a.K + 32 * g;
     }
+    RunSrc<FMT> src[PN];
+#pragma unroll
+    for (int pn = 0; pn < PN; pn++) {
+        const int p = p0 + pn;
+        src[pn].init(a, p < a.np ? p : a.np - 1, g, col);
+    }
 
+    RunRaw<FMT> raw[PN];
+    u32x4 xf[RB][4];
+    if (cb < ce) {
+#pragma unroll
+        for (int pn = 0; pn < PN; pn++) src[pn].load(cb, raw[pn]);
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cb + 8 * i);
+    }
     for (int c = cb; c < ce; c++) {
         u32x4 wf[PN][4];
 #pragma unroll
-        for (int pn = 0; pn < PN; pn++) {
-            int p = p0 + pn;
-            p = p < a.np ? p : a.np - 1;
-            Unit<FMT> u;
-            load_unit<FMT>(a, p, c, g, col, u);
-            unpack_unit<FMT, DT>(u, c, g, wf[pn]);
+        for (int pn = 0; pn < PN; pn++) unpack_run<FMT, DT>(raw[pn], src[pn], c, wf[pn]);
+        u32x4 xc[RB][4];
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) xc[rb][i] = xf[rb][i];
+        if (c + 1 < ce) {  // prefetch chunk c+1 while this one is multiplied
+#pragma unroll
+            for (int pn = 0; pn < PN; pn++) src[pn].load(c + 1, raw[pn]);
+#pragma unroll
+            for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * (c + 1) + 8 * i);
         }
 #pragma unroll
-        for (int rb = 0; rb < RB; rb++) {
-            u32x4 xf[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) xf[i] = *(const u32x4 *)(xrow[rb] + kChunk * c + 8 * i);
+        for (int rb = 0; rb < RB; rb++)
 #pragma unroll
             for (int pn = 0; pn < PN; pn++)
 #pragma unroll
-                for (int i = 0; i < 4; i++) acc[pn][rb] = mma<DT>(wf[pn][i], xf[i], acc[pn][rb]);
-        }
+                for (int i = 0; i < 4; i++) acc[pn][rb] = mma<DT>(wf[pn][i], xc[rb][i], acc[pn][rb]);
     }
 
     if (a.kw == 1) {
@@ -376,127 +423,49 @@ __global__ void __launch_bounds__(512) k_direct(Args a)
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel: mid and long prefill.
+// Streaming tile kernel: mid and long prefill.
 //
-// A workgroup of four waves owns a BM x BN output tile.  Per 128-wide K
-// chunk every weight of the tile is unpacked once (one or more 32-code runs
-// per lane) into LDS in MFMA-fragment order, the activation tile is staged
-// next to it, and each wave multiplies its (BM/WGM) x (BN/WGN) share from
-// LDS, so the unpack cost is shared by all BM rows of the tile.
-// ---------------------------------------------------------------------------
-template <int FMT, int DT, int BM, int BN, int WGM, int WGN>
-__global__ void __launch_bounds__(256) k_tile(Args a)
-{
-    constexpr int RBT = BM / 16, PBT = BN / 16;
-    constexpr int RBW = RBT / WGM, PBW = PBT / WGN;
-    constexpr int UPT = PBT * 64 / 256;  // weight runs per thread per chunk
-    constexpr int XPT = BM * 16 / 256;   // 16-byte activation pieces per thread per chunk
-    static_assert(WGM * WGN == 4, "four waves");
-    static_assert(UPT >= 1 && XPT >= 1, "tile too small");
-    __shared__ u32x4 sX[RBT][4][64];
-    __shared__ u32x4 sW[PBT][4][64];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int m0 = blockIdx.y * BM, p0 = blockIdx.x * PBT;
-    const int nch = a.K / kChunk;
-
-    f32x4 acc[PBW][RBW];
-#pragma unroll
-    for (int pb = 0; pb < PBW; pb++)
-#pragma unroll
-        for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = 0; c < nch; c++) {
-        u32x4 xv[XPT];
-#pragma unroll
-        for (int s = 0; s < XPT; s++) {
-            const int v = tid + 256 * s, r16 = v & 15, qq = (v >> 4) & 15, rb = v >> 8;
-            int row = m0 + 16 * rb + r16;
-            row = row < a.M ? row : a.M - 1;
-            xv[s] = *(const u32x4 *)(a.X + (long long)row * a.K + kChunk * c + 8 * qq);
-        }
-        u32x4 wf[UPT][4];
-#pragma unroll
-        for (int s = 0; s < UPT; s++) {
-            const int u = tid + 256 * s, pb = u >> 6, gg = (u >> 4) & 3, col = u & 15;
-            int p = p0 + pb;
-            p = p < a.np ? p : a.np - 1;
-            Unit<FMT> un;
-            load_unit<FMT>(a, p, c, gg, col, un);
-            unpack_unit<FMT, DT>(un, c, gg, wf[s]);
-        }
-        __syncthreads();  // the previous chunk's fragments have been read
-#pragma unroll
-        for (int s = 0; s < XPT; s++) {
-            const int v = tid + 256 * s, r16 = v & 15, qq = (v >> 4) & 15, rb = v >> 8;
-            sX[rb][qq & 3][(qq >> 2) * 16 + r16] = xv[s];
-        }
-#pragma unroll
-        for (int s = 0; s < UPT; s++) {
-            const int u = tid + 256 * s, pb = u >> 6, gg = (u >> 4) & 3, col = u & 15;
-#pragma unroll
-            for (int i = 0; i < 4; i++) sW[pb][i][gg * 16 + col] = wf[s][i];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            u32x4 af[PBW], bf[RBW];
-#pragma unroll
-            for (int pb = 0; pb < PBW; pb++) af[pb] = sW[wn * PBW + pb][i][lane];
-#pragma unroll
-            for (int rb = 0; rb < RBW; rb++) bf[rb] = sX[wm * RBW + rb][i][lane];
-#pragma unroll
-            for (int pb = 0; pb < PBW; pb++)
-#pragma unroll
-                for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = mma<DT>(af[pb], bf[rb], acc[pb][rb]);
-        }
-    }
-#pragma unroll
-    for (int pb = 0; pb < PBW; pb++)
-#pragma unroll
-        for (int rb = 0; rb < RBW; rb++)
-            store_block<DT>(a, acc[pb][rb], m0 + 16 * (wm * RBW + rb), 16 * (p0 + wn * PBW + pb), lane);
-}
-
-// ---------------------------------------------------------------------------
-// Streaming tile kernel: long prefill.
-//
-// Four waves own a (4*WM) x (16*PB) output tile; wave w owns rows
-// [m0 + WM*w, m0 + WM*(w+1)) and all 16*PB columns, so no activation element
-// is loaded by two waves.  Per 128-wide K chunk:
-//   * every thread loads UPT packed weight runs of chunk c+1 and, after the
-//     chunk-c MFMAs are issued, unpacks them into the other half of a
-//     double-buffered LDS weight tile (each weight unpacked once per
-//     workgroup and shared by all 4*WM rows);
-//   * each wave loads its own activation fragments of chunk c+1 straight
-//     from global memory into VGPRs (no LDS round trip for X);
+// NWM x NWN waves own a (NWM*WM) x (16*WPB*NWN) output tile; wave (wm, wn)
+// owns rows [m0 + WM*wm, +WM) and panels [WPB*wn, +WPB).  Per 128-wide K
+// chunk:
+//   * every thread loads the raw bytes of its UPT weight runs of chunk c+1
+//     and, after the chunk-c MFMAs, unpacks them into the other half of a
+//     double-buffered LDS weight tile: each weight is unpacked once per
+//     workgroup and shared by all NWM*WM rows;
+//   * each wave loads its own activation fragments straight from global
+//     memory into VGPRs (the fragments of chunk c+1 replace those of chunk c
+//     as soon as their MFMAs are issued), so X never goes through LDS;
+//   * weight fragments are read from LDS one MFMA step ahead of their use;
 //   * one barrier per chunk.
-// Inside one MFMA, lane (r, g) of instruction i carries k = 128c + 32i + 8g
-// + 0..7 in both operands, so an activation load of instruction i reads 64
-// contiguous bytes of each row and a weight run (32 consecutive k) fills the
-// four lane groups of one instruction.
-// Workgroups are numbered so that consecutive tiles (same row block,
-// neighbouring column panels) land on the same XCD, whose L2 then serves the
-// shared activation rows.
+// Inside one MFMA, lane (r, g) of step i carries k = 128c + 32i + 8g + 0..7 in
+// both operands: an activation load of step i reads 64 contiguous bytes of
+// each row, and one weight run (32 consecutive k) fills the four lane groups
+// of one step.
+// Workgroups are renumbered so that each XCD gets a contiguous range of
+// tiles (same row block, neighbouring panels): its L2 then serves the shared
+// activation rows.
 // ---------------------------------------------------------------------------
-template <int FMT, int DT, int WM, int PB>
-__global__ void __launch_bounds__(256) k_stream(Args a)
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN>
+__global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 {
-    constexpr int RBW = WM / 16;          // row blocks per wave
-    constexpr int UPT = PB * 64 / 256;    // weight runs per thread per chunk
-    static_assert(UPT >= 1 && PB * 64 % 256 == 0, "PB must be a multiple of 4");
+    constexpr int NT = 64 * NWM * NWN;
+    constexpr int PB = WPB * NWN;          // panels per tile
+    constexpr int BM = WM * NWM;           // rows per tile
+    constexpr int RBW = WM / 16;           // row blocks per wave
+    constexpr int UPT = PB * 64 / NT;      // weight runs per thread per chunk
+    static_assert(PB * 64 % NT == 0 && UPT >= 1, "tile and workgroup do not divide");
     __shared__ u32x4 sW[2][PB][4][64];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int tn = (a.np + PB - 1) / PB, tm = (a.M + 4 * WM - 1) / (4 * WM);
+    const int wm = w % NWM, wn = w / NWM;
+    const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
     const int T = tn * tm;
     // XCD-aware renumbering: WG b runs on XCD b % 8; give each XCD a contiguous
     // range of logical tiles (a bijection on [0, T)).
     const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
     const int L = xcd * (T >> 3) + min(xcd, T & 7) + slot;
     const int mt = L / tn, nt = L - mt * tn;
-    const int m0 = mt * 4 * WM + w * WM, p0 = nt * PB;
+    const int m0 = mt * BM + wm * WM, p0 = nt * PB;
     const int nch = a.K / kChunk;
     const int r16 = lane & 15, g4 = lane >> 4;
 
@@ -508,29 +477,27 @@ __global__ void __launch_bounds__(256) k_stream(Args a)
         xrow[rb] = a.X + (long long)r * a.K + 8 * g4;
     }
 
-    f32x4 acc[PB][RBW];
+    f32x4 acc[WPB][RBW];
 #pragma unroll
-    for (int pb = 0; pb < PB; pb++)
+    for (int pb = 0; pb < WPB; pb++)
 #pragma unroll
         for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // this thread's weight runs: u = tid + 256*s -> panel u/64, run (u/16)%4, column u%16
-    int upanel[UPT], urun[UPT], ucol[UPT];
+    // this thread's weight runs: u = tid + NT*s -> panel u/64, run (u/16)%4, column u%16
+    RunSrc<FMT> src[UPT];
+    RunRaw<FMT> raw[UPT];
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
-        const int u = tid + 256 * s;
-        int p = p0 + (u >> 6);
-        upanel[s] = p < a.np ? p : a.np - 1;
-        urun[s] = (u >> 4) & 3;
-        ucol[s] = u & 15;
+        const int u = tid + NT * s;
+        const int p = p0 + (u >> 6);
+        src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, u & 15);
     }
 
-    Unit<FMT> un[UPT];
-    u32x4 xf[RBW][4], xn[RBW][4];
-
-    // prologue: chunk 0 into LDS buffer 0 and registers
+    u32x4 xf[RBW][4];
+    // prologue: chunk 0 unpacked into LDS buffer 0, chunk 1 raw in registers,
+    // chunk 0 activations in registers
 #pragma unroll
-    for (int s = 0; s < UPT; s++) load_unit<FMT>(a, upanel[s], 0, urun[s], ucol[s], un[s]);
+    for (int s = 0; s < UPT; s++) src[s].load(0, raw[s]);
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
@@ -538,54 +505,63 @@ __global__ void __launch_bounds__(256) k_stream(Args a)
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
         u32x4 f[4];
-        unpack_unit<FMT, DT>(un[s], 0, urun[s], f);
-        const int pb = (tid + 256 * s) >> 6;
+        unpack_run<FMT, DT>(raw[s], src[s], 0, f);
+        const int pb = (tid + NT * s) >> 6;
 #pragma unroll
-        for (int j = 0; j < 4; j++) sW[0][pb][urun[s]][j * 16 + ucol[s]] = f[j];
+        for (int j = 0; j < 4; j++) sW[0][pb][src[s].g][j * 16 + src[s].col] = f[j];
     }
+    const int c1 = nch > 1 ? 1 : 0;
+#pragma unroll
+    for (int s = 0; s < UPT; s++) src[s].load(c1, raw[s]);
     __syncthreads();
 
+    // Steady state, branch-free: chunk c is multiplied from LDS buffer c&1
+    // while chunk c+1 (raw bytes already in registers) is unpacked word by
+    // word into buffer (c+1)&1, the activations of chunk c+1 replace those of
+    // chunk c step by step, and the raw bytes of chunk c+2 are requested.
+    // Past the last chunk the indices are clamped: the extra work is
+    // harmless (the buffer written is never read again).
     for (int c = 0; c < nch; c++) {
         const int buf = c & 1;
-        const bool more = c + 1 < nch;
-        if (more) {
+        const int cn = c + 1 < nch ? c + 1 : nch - 1;
+        const int cnn = c + 2 < nch ? c + 2 : nch - 1;
+        RunParams pr[UPT];
 #pragma unroll
-            for (int s = 0; s < UPT; s++) load_unit<FMT>(a, upanel[s], c + 1, urun[s], ucol[s], un[s]);
+        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(raw[s], src[s], cn);
+        u32x4 wcur[WPB], wnxt[WPB];
 #pragma unroll
-            for (int rb = 0; rb < RBW; rb++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) xn[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * (c + 1) + 32 * i);
-        }
+        for (int pb = 0; pb < WPB; pb++) wcur[pb] = sW[buf][wn * WPB + pb][0][lane];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            u32x4 wf[PB];
+            if (i < 3) {
 #pragma unroll
-            for (int pb = 0; pb < PB; pb++) wf[pb] = sW[buf][pb][i][lane];
-#pragma unroll
-            for (int pb = 0; pb < PB; pb++)
-#pragma unroll
-                for (int rb = 0; rb < RBW; rb++) acc[pb][rb] = mma<DT>(wf[pb], xf[rb][i], acc[pb][rb]);
-        }
-        if (more) {
-#pragma unroll
-            for (int s = 0; s < UPT; s++) {
-                u32x4 f[4];
-                unpack_unit<FMT, DT>(un[s], c + 1, urun[s], f);
-                const int pb = (tid + 256 * s) >> 6;
-#pragma unroll
-                for (int j = 0; j < 4; j++) sW[buf ^ 1][pb][urun[s]][j * 16 + ucol[s]] = f[j];
+                for (int pb = 0; pb < WPB; pb++) wnxt[pb] = sW[buf][wn * WPB + pb][i + 1][lane];
             }
 #pragma unroll
-            for (int rb = 0; rb < RBW; rb++)
+            for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) xf[rb][i] = xn[rb][i];
+                for (int pb = 0; pb < WPB; pb++) acc[pb][rb] = mma<DT>(wcur[pb], xf[rb][i], acc[pb][rb]);
+                xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cn + 32 * i);
+            }
+#pragma unroll
+            for (int s = 0; s < UPT; s++) {
+                const int pb = (tid + NT * s) >> 6;
+                sW[buf ^ 1][pb][src[s].g][i * 16 + src[s].col] = unpack_word<FMT, DT>(raw[s], pr[s], i);
+            }
+            if (i < 3) {
+#pragma unroll
+                for (int pb = 0; pb < WPB; pb++) wcur[pb] = wnxt[pb];
+            }
         }
+#pragma unroll
+        for (int s = 0; s < UPT; s++) src[s].load(cnn, raw[s]);
         __syncthreads();
     }
 #pragma unroll
-    for (int pb = 0; pb < PB; pb++)
+    for (int pb = 0; pb < WPB; pb++)
 #pragma unroll
-        for (int rb = 0; rb < RBW; rb++) store_block<DT>(a, acc[pb][rb], m0 + 16 * rb, 16 * (p0 + pb), lane);
+        for (int rb = 0; rb < RBW; rb++)
+            store_block<DT>(a, acc[pb][rb], m0 + 16 * rb, 16 * (p0 + wn * WPB + pb), lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -603,10 +579,12 @@ __global__ void __launch_bounds__(256) k_dequant(Args a, uint16_t *Wout)
     const long long pc = idx >> 6;
     const int c = (int)(pc % nch), p = (int)(pc / nch);
     const int n = 16 * p + col;
-    Unit<FMT> u;
-    load_unit<FMT>(a, p, c, g, col, u);
+    RunSrc<FMT> src;
+    src.init(a, p, g, col);
+    RunRaw<FMT> raw;
+    src.load(c, raw);
     u32x4 f[4];
-    unpack_unit<FMT, DT>(u, c, g, f);
+    unpack_run<FMT, DT>(raw, src, c, f);
     if (n >= a.N) return;
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -623,15 +601,16 @@ __global__ void __launch_bounds__(256) k_dequant(Args a, uint16_t *Wout)
 // ---------------------------------------------------------------------------
 
 enum Rung {
-    RUNG_SMALL_M = 0,
-    RUNG_SKINNY_N = 1,
-    RUNG_TILE_128 = 2,
-    RUNG_STREAM_256 = 3,
-    RUNG_STREAM_128 = 4,
-    RUNG_COUNT = 5
+    RUNG_SMALL_M = 0,    // direct, one panel per wave, up to 64 rows per wave
+    RUNG_SKINNY_N = 1,   // direct, up to four panels per wave, 16 rows per wave
+    RUNG_S128_W4 = 2,    // stream 128x128, 4 waves of 32x128
+    RUNG_S256_W4 = 3,    // stream 256x128, 4 waves of 64x128
+    RUNG_S256_W8 = 4,    // stream 256x128, 8 waves of 64x64
+    RUNG_S128_W8 = 5,    // stream 128x128, 8 waves of 32x64
+    RUNG_COUNT = 6
 };
-const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "tile-128x128", "stream-256x128",
-                                            "stream-128x128"};
+const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "stream-128x128-w4",
+                                            "stream-256x128-w4", "stream-256x128-w8", "stream-128x128-w8"};
 
 struct Plan {
     int rung;
@@ -674,22 +653,13 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.grid = dim3((unsigned)ceil_div(np, pl.pn), (unsigned)ceil_div(M, 16), 1);
         break;
     }
-    case RUNG_TILE_128: {
-        pl.rows = 128;
+    case RUNG_S128_W4:
+    case RUNG_S256_W4:
+    case RUNG_S256_W8:
+    case RUNG_S128_W8: {
+        pl.rows = (rung == RUNG_S256_W4 || rung == RUNG_S256_W8) ? 256 : 128;
         pl.cols = 128;
-        pl.waves = 4;
-        pl.kw = 1;
-        pl.grid = dim3((unsigned)ceil_div(np, 8), (unsigned)ceil_div(M, 128), 1);
-        pl.tiles_n = (int)pl.grid.x;
-        pl.tiles_m = (int)pl.grid.y;
-        pl.lds = 0;
-        return true;
-    }
-    case RUNG_STREAM_256:
-    case RUNG_STREAM_128: {
-        pl.rows = rung == RUNG_STREAM_256 ? 256 : 128;
-        pl.cols = 128;
-        pl.waves = 4;
+        pl.waves = (rung == RUNG_S256_W8 || rung == RUNG_S128_W8) ? 8 : 4;
         pl.kw = 1;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         pl.tiles_n = ceil_div(np, 8);
@@ -719,7 +689,7 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 int select_rung(long long M, long long N)
 {
     if (N <= 64 || M <= 64) return RUNG_SKINNY_N;
-    return RUNG_STREAM_128;
+    return RUNG_S128_W4;
 }
 
 template <int FMT, int DT, int RB, int PN>
@@ -750,17 +720,21 @@ hipError_t launch_direct(const Plan &pl, const Args &a, hipStream_t s)
 template <int FMT, int DT>
 hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
-    if (pl.rung == RUNG_TILE_128) {
-        hipLaunchKernelGGL((k_tile<FMT, DT, 128, 128, 2, 2>), pl.grid, dim3(256), 0, s, a);
+    switch (pl.rung) {
+    case RUNG_S128_W4:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
-    }
-    if (pl.rung == RUNG_STREAM_256) {
-        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8>), pl.grid, dim3(256), 0, s, a);
+    case RUNG_S256_W4:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
-    }
-    if (pl.rung == RUNG_STREAM_128) {
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8>), pl.grid, dim3(256), 0, s, a);
+    case RUNG_S256_W8:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 4, 4, 2>), pl.grid, dim3(512), 0, s, a);
         return hipGetLastError();
+    case RUNG_S128_W8:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 4, 4, 2>), pl.grid, dim3(512), 0, s, a);
+        return hipGetLastError();
+    default:
+        break;
     }
     return launch_direct<FMT, DT>(pl, a, s);
 }
@@ -790,7 +764,7 @@ int check_shape(int fmt, long long M, long long N, long long K, long long group)
     if (M < 0 || N < 1 || K < 1) return QGEMM_ERR_SHAPE;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return QGEMM_ERR_SHAPE;
     if (fmt == FMT_W4) {  // group == 0: group size not known to the caller (rung queries)
-        if (group != 0 && (group < 32 || group % 32 != 0)) return QGEMM_ERR_FORMAT;
+        if (group != 0 && (group < 32 || (group & (group - 1)) != 0)) return QGEMM_ERR_FORMAT;
         if (K % 128 != 0 || (group != 0 && K % group != 0)) return QGEMM_ERR_SHAPE;
     } else if (K % 256 != 0) {
         return QGEMM_ERR_SHAPE;
