@@ -197,14 +197,13 @@ __device__ __forceinline__ RunParams run_params(const RunRaw<FMT> &u, const RunS
         const float d = f16_to_f32(u.hd[0] & 0xFFFFu), dmin = f16_to_f32(u.hd[0] >> 16);
         const uint32_t s0 = u.hd[1], s1 = u.hd[2], s2 = u.hd[3];
         const int sh = 8 * g;
-        uint32_t sc, m;
-        if ((c & 1) == 0) {  // sub-blocks 0..3: low six bits of bytes 0..3 / 4..7
-            sc = (s0 >> sh) & 63u;
-            m = (s1 >> sh) & 63u;
-        } else {             // sub-blocks 4..7: nibbles of bytes 8..11 + top two bits
-            sc = ((s2 >> sh) & 15u) | (((s0 >> (sh + 6)) & 3u) << 4);
-            m = ((s2 >> (sh + 4)) & 15u) | (((s1 >> (sh + 6)) & 3u) << 4);
-        }
+        // sub-blocks 0..3: low six bits of bytes 0..3 / 4..7; sub-blocks 4..7:
+        // nibbles of bytes 8..11 plus the top two bits of bytes 0..3 / 4..7
+        const uint32_t sc_lo = (s0 >> sh) & 63u, m_lo = (s1 >> sh) & 63u;
+        const uint32_t sc_hi = ((s2 >> sh) & 15u) | (((s0 >> (sh + 6)) & 3u) << 4);
+        const uint32_t m_hi = ((s2 >> (sh + 4)) & 15u) | (((s1 >> (sh + 6)) & 3u) << 4);
+        const bool upper = (c & 1) != 0;
+        const uint32_t sc = upper ? sc_hi : sc_lo, m = upper ? m_hi : m_lo;
         pr.fa = d * (float)sc * kTwo24;  // factor = d*sc, exact in binary32
         pr.nb = -(dmin * (float)m);      // bias = dmin*m, exact
         pr.exact = false;
@@ -252,22 +251,34 @@ __device__ __forceinline__ u32x4 unpack_word(const RunRaw<FMT> &u, const RunPara
     } else {
         const uint32_t t[4] = {x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u};
         const float fa16 = pr.fa * 0.0625f;
-        if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
-            if (pr.exact) {
-#pragma unroll
-                for (int p = 0; p < 4; p++) {
-                    const f16x2 h = __builtin_bit_cast(f16x2, t[p]);
-                    const float f = (p & 1) ? fa16 : pr.fa;
-                    out[p] = (uint32_t)exact_bf16((float)h.x, f, pr.nb) |
-                             ((uint32_t)exact_bf16((float)h.y, f, pr.nb) << 16);
-                }
-                return out;
-            }
-        }
 #pragma unroll
         for (int p = 0; p < 4; p++) out[p] = dq_pair<DT>(t[p], (p & 1) ? fa16 : pr.fa, pr.nb);
     }
     return out;
+}
+
+// Word i of a bf16 Q4_K run whose values may not fit binary32 (pr.exact).
+__device__ __noinline__ u32x4 unpack_word_exact_bf16(u32x4 codes, float fa, float nb, int i)
+{
+    u32x4 out;
+    const uint32_t x = codes[i], x8 = x >> 8;
+    const uint32_t t[4] = {x & 0x000F000Fu, x & 0x00F000F0u, x8 & 0x000F000Fu, x8 & 0x00F000F0u};
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const f16x2 h = __builtin_bit_cast(f16x2, t[p]);
+        const float f = (p & 1) ? fa * 0.0625f : fa;
+        out[p] = (uint32_t)exact_bf16((float)h.x, f, nb) | ((uint32_t)exact_bf16((float)h.y, f, nb) << 16);
+    }
+    return out;
+}
+
+template <int FMT, int DT>
+__device__ __forceinline__ u32x4 unpack_word_any(const RunRaw<FMT> &u, const RunParams &pr, int i)
+{
+    if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
+        if (pr.exact) return unpack_word_exact_bf16(u.codes, pr.fa, pr.nb, i);
+    }
+    return unpack_word<FMT, DT>(u, pr, i);
 }
 
 template <int FMT, int DT>
@@ -275,7 +286,16 @@ __device__ __forceinline__ void unpack_run(const RunRaw<FMT> &u, const RunSrc<FM
 {
     const RunParams pr = run_params<FMT, DT>(u, src, c);
 #pragma unroll
-    for (int i = 0; i < 4; i++) out[i] = unpack_word<FMT, DT>(u, pr, i);
+    for (int i = 0; i < 4; i++) out[i] = unpack_word_any<FMT, DT>(u, pr, i);
+}
+
+// VALU instructions to place after each MFMA of one step: the unpack of UPT
+// words spread evenly over the step's NMF MFMAs (rounded up).
+template <int FMT, int DT, int UPT, int NMF>
+constexpr int kValuPerMfma()
+{
+    constexpr int per_word = (FMT == FMT_Q6K ? 26 : 13) + (DT == DT_BF16 ? 4 : 0) + 2;
+    return (UPT * per_word + NMF - 1) / NMF;
 }
 
 template <int DT>
@@ -445,7 +465,7 @@ __global__ void __launch_bounds__(512) k_direct(Args a)
 // tiles (same row block, neighbouring panels): its L2 then serves the shared
 // activation rows.
 // ---------------------------------------------------------------------------
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, bool SCHED>
 __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 {
     constexpr int NT = 64 * NWM * NWN;
@@ -552,6 +572,31 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 #pragma unroll
                 for (int pb = 0; pb < WPB; pb++) wcur[pb] = wnxt[pb];
             }
+            // Interleaved variant: each MFMA is followed by a few VALU (unpack)
+            // instructions and one LDS or global access, so the matrix pipe
+            // and the VALU of one wave run side by side.
+#pragma unroll
+            for (int k = 0; k < (SCHED ? WPB * RBW : 0); k++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma<FMT, DT, UPT, WPB * RBW>(), 0);
+                if (k < WPB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                if (k >= WPB && k < WPB + UPT) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+                if (k >= WPB + UPT && k < WPB + UPT + RBW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+            }
+        }
+        if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
+            // rare: runs whose d and dmin are too far apart for binary32 are
+            // redone exactly (the fast words above are overwritten)
+#pragma unroll
+            for (int s = 0; s < UPT; s++) {
+                if (pr[s].exact) {
+                    const int pb = (tid + NT * s) >> 6;
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        sW[buf ^ 1][pb][src[s].g][i * 16 + src[s].col] =
+                            unpack_word_exact_bf16(raw[s].codes, pr[s].fa, pr[s].nb, i);
+                }
+            }
         }
 #pragma unroll
         for (int s = 0; s < UPT; s++) src[s].load(cnn, raw[s]);
@@ -603,14 +648,14 @@ __global__ void __launch_bounds__(256) k_dequant(Args a, uint16_t *Wout)
 enum Rung {
     RUNG_SMALL_M = 0,    // direct, one panel per wave, up to 64 rows per wave
     RUNG_SKINNY_N = 1,   // direct, up to four panels per wave, 16 rows per wave
-    RUNG_S128_W4 = 2,    // stream 128x128, 4 waves of 32x128
-    RUNG_S256_W4 = 3,    // stream 256x128, 4 waves of 64x128
-    RUNG_S256_W8 = 4,    // stream 256x128, 8 waves of 64x64
-    RUNG_S128_W8 = 5,    // stream 128x128, 8 waves of 32x64
+    RUNG_S128 = 2,       // stream 128x128, 4 waves of 32x128
+    RUNG_S256 = 3,       // stream 256x128, 4 waves of 64x128
+    RUNG_S128_IL = 4,    // as RUNG_S128, MFMA and unpack interleaved
+    RUNG_S256_IL = 5,    // as RUNG_S256, MFMA and unpack interleaved
     RUNG_COUNT = 6
 };
-const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "stream-128x128-w4",
-                                            "stream-256x128-w4", "stream-256x128-w8", "stream-128x128-w8"};
+const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "stream-128x128",
+                                            "stream-256x128", "stream-128x128-il", "stream-256x128-il"};
 
 struct Plan {
     int rung;
@@ -653,13 +698,13 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.grid = dim3((unsigned)ceil_div(np, pl.pn), (unsigned)ceil_div(M, 16), 1);
         break;
     }
-    case RUNG_S128_W4:
-    case RUNG_S256_W4:
-    case RUNG_S256_W8:
-    case RUNG_S128_W8: {
-        pl.rows = (rung == RUNG_S256_W4 || rung == RUNG_S256_W8) ? 256 : 128;
+    case RUNG_S128:
+    case RUNG_S256:
+    case RUNG_S128_IL:
+    case RUNG_S256_IL: {
+        pl.rows = (rung == RUNG_S256 || rung == RUNG_S256_IL) ? 256 : 128;
         pl.cols = 128;
-        pl.waves = (rung == RUNG_S256_W8 || rung == RUNG_S128_W8) ? 8 : 4;
+        pl.waves = 4;
         pl.kw = 1;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         pl.tiles_n = ceil_div(np, 8);
@@ -681,15 +726,22 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     return true;
 }
 
-// The M-ladder.  Narrow N first: with at most four panels the grid must run
-// over M (a 128x128 tile would leave most of the part idle and most of each
-// tile padding).  Then decode-adjacent M, where each weight is used by at
-// most 64 rows and the kernel is a weight stream.  Everything else takes
-// the LDS-shared tile.
+// The M-ladder (measured on MI355X; each rung is legal for every shape):
+//  * narrow N (at most four panels): the grid must run over M, so the
+//    direct kernel with all panels per wave (a 128-wide tile would leave most
+//    of the part idle and most of each tile padding);
+//  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
+//    and the kernel is a weight stream; with many panels, four panels per
+//    wave, otherwise one panel per wave and all rows per wave;
+//  * otherwise the streaming 128x128 tile, unless it would leave most CUs
+//    idle (fewer than 128 tiles), where the direct kernel keeps them busy.
 int select_rung(long long M, long long N)
 {
-    if (N <= 64 || M <= 64) return RUNG_SKINNY_N;
-    return RUNG_S128_W4;
+    const long long np = (N + 15) / 16;
+    if (np <= 4) return RUNG_SKINNY_N;
+    if (M <= 64) return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
+    if (((np + 7) / 8) * ((M + 127) / 128) < 128) return RUNG_SKINNY_N;
+    return RUNG_S128;
 }
 
 template <int FMT, int DT, int RB, int PN>
@@ -721,17 +773,17 @@ template <int FMT, int DT>
 hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
     switch (pl.rung) {
-    case RUNG_S128_W4:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1>), pl.grid, dim3(256), 0, s, a);
+    case RUNG_S128:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
-    case RUNG_S256_W4:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1>), pl.grid, dim3(256), 0, s, a);
+    case RUNG_S256:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, false>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
-    case RUNG_S256_W8:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 4, 4, 2>), pl.grid, dim3(512), 0, s, a);
+    case RUNG_S128_IL:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, true>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
-    case RUNG_S128_W8:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 4, 4, 2>), pl.grid, dim3(512), 0, s, a);
+    case RUNG_S256_IL:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, true>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     default:
         break;

@@ -209,8 +209,10 @@ def test_ladder_sweep(fmt, dtype):
             assert info["tiles_m"] * info["rows"] >= M
             assert info["k_step"] % 32 == 0 and info["k_step"] <= K
             assert (K // info["k_step"]) >= info["k_split"] >= 1
-            if N <= 64 or M <= 64:
+            if N <= 64:
                 assert info["name"] == "direct-skinny-n"
+            elif M <= 64:
+                assert info["name"].startswith("direct-")
             for r in range(qg.num_rungs()):
                 ri = qg.rung_info(r, fmt, M, N, K, dtype)
                 assert ri["tiles_n"] * ri["cols"] >= N and ri["tiles_m"] * ri["rows"] >= M
