@@ -53,6 +53,7 @@ enum { FMT_Q4K = QGEMM_FMT_Q4K, FMT_Q6K = QGEMM_FMT_Q6K, FMT_W4 = QGEMM_FMT_W4A1
 enum { DT_F16 = QGEMM_F16, DT_BF16 = QGEMM_BF16 };
 
 constexpr int kChunk = 128;  // K per step: four 32-wide runs, one per lane group
+constexpr int kGroupM = 8;   // row tiles per group in the streaming tile order
 constexpr int kQ4kRec = 2304, kQ6kRec = 3360;
 constexpr float kTwo24 = 16777216.0f;
 
@@ -461,9 +462,9 @@ __global__ void __launch_bounds__(512) k_direct(Args a)
 // both operands: an activation load of step i reads 64 contiguous bytes of
 // each row, and one weight run (32 consecutive k) fills the four lane groups
 // of one step.
-// Workgroups are renumbered so that each XCD gets a contiguous range of
-// tiles (same row block, neighbouring panels): its L2 then serves the shared
-// activation rows.
+// Workgroups are renumbered so that each XCD gets a contiguous range of a
+// grouped tile order (below): its L2 then serves both the shared weight
+// panels and the shared activation rows.
 // ---------------------------------------------------------------------------
 template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, bool SCHED>
 __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
@@ -484,7 +485,15 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
     // range of logical tiles (a bijection on [0, T)).
     const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
     const int L = xcd * (T >> 3) + min(xcd, T & 7) + slot;
-    const int mt = L / tn, nt = L - mt * tn;
+    // Logical order.  With at most kGroupM row tiles the row tile varies
+    // fastest, so the tiles that share one column panel (its weights) run
+    // together on one XCD; with more, the column tile varies fastest, so the
+    // tiles running together share one activation row block, the larger
+    // per-tile stream.
+    const int G = tm <= kGroupM ? tm : 1;
+    const int gsize = G * tn, gid = L / gsize, first_m = gid * G;
+    const int gm = min(tm - first_m, G), lin = L - gid * gsize;
+    const int mt = first_m + lin % gm, nt = lin / gm;
     const int m0 = mt * BM + wm * WM, p0 = nt * PB;
     const int nch = a.K / kChunk;
     const int r16 = lane & 15, g4 = lane >> 4;
