@@ -10,6 +10,13 @@ times from HIP events, the roofline of the dominant kernel and the CPU
 oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps 20] [--warmup 5] [--workload NAME] [--no-cpu-baseline]
+
+Profiling helpers (same JSON line, restricted work):
+    --only LABEL        run only that GEMM of the workload
+    --rung R            force rung R instead of the M-ladder's choice
+    --copy-calibration BYTES
+                        run a plain device-to-device copy of BYTES bytes three
+                        times and exit (reference for HBM byte counters)
 """
 from __future__ import annotations
 
@@ -70,7 +77,12 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_8b_layer_m658", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only", default=None, help="run only the GEMM with this label")
+    ap.add_argument("--rung", type=int, default=-1, help="force a rung (-1: M-ladder)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path would shard by N or K across GPUs, which is not built here)", file=sys.stderr)
@@ -83,20 +95,29 @@ def main() -> int:
     wl = synth.WORKLOADS[args.workload]
     gemms = []
     for j, (label, fmt, M, K, N, dt, group, sym) in enumerate(wl["gemms"]):
+        if args.only is not None and label != args.only:
+            continue
         X, fields, enc = synth.workload_inputs(args.workload, j)
         packed = qg.pack(fmt, enc, N, K)
         tdt = torch.float16 if dt == qg.F16 else torch.bfloat16
         x = torch.from_numpy(X.view(np.int16)).view(tdt).to(dev)
         wp = torch.from_numpy(packed).to(dev)
         y = torch.empty((M, N), dtype=tdt, device=dev)
-        info = qg.select_rung(fmt, M, N, K, dt)
+        info = qg.select_rung(fmt, M, N, K, dt) if args.rung < 0 else qg.rung_info(args.rung, fmt, M, N, K, dt)
         gemms.append(dict(label=label, fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym, x=x, wp=wp, y=y,
                           X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K,
                           wbytes=weight_bytes(fmt, N, K, group or 128, sym)))
         print(f"[bench] {label}: {fmt} M={M} K={K} N={N} rung={info['name']}", file=sys.stderr, flush=True)
 
+    if not gemms:
+        print(f"bench.py: no GEMM labelled {args.only!r} in {args.workload}", file=sys.stderr)
+        return 2
+
     def call(g):
-        if g["fmt"] == "q4k":
+        if args.rung >= 0:
+            qg.gemm_rung(g["fmt"], args.rung, g["x"], g["wp"], g["N"], group=g["group"], has_zp=not g["sym"],
+                         out=g["y"])
+        elif g["fmt"] == "q4k":
             qg.q4k(g["x"], g["wp"], g["N"], out=g["y"])
         elif g["fmt"] == "q6k":
             qg.q6k(g["x"], g["wp"], g["N"], out=g["y"])
@@ -167,13 +188,31 @@ def main() -> int:
         "per_kernel": per,
         "roofline": roof,
     }
-    if args.workload == "qwen3_8b_layer_m658":
+    if args.only is not None or args.rung >= 0:
+        out["config"]["only"] = args.only
+        out["config"]["rung"] = args.rung
+    if args.workload == "qwen3_8b_layer_m658" and args.only is None:
         # linear layers only: 36 layers x the seven projections of one layer
         out["prefill_tok_s_linear_only"] = round(synth.QWEN3_8B_PROMPT / (synth.QWEN3_8B_LAYERS * ms_per_step * 1e-3), 1)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(gemms, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def copy_calibration(nbytes: int) -> int:
+    """A plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read
+    for it gives the scale of those counters."""
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}), flush=True)
     return 0
 
 

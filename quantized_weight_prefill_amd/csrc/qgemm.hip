@@ -466,18 +466,22 @@ __global__ void __launch_bounds__(512) k_direct(Args a)
 // grouped tile order (below): its L2 then serves both the shared weight
 // panels and the shared activation rows.
 // ---------------------------------------------------------------------------
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, bool SCHED>
-__global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, bool SCHED, int XD, int KS>
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
 {
-    constexpr int NT = 64 * NWM * NWN;
+    constexpr int NTG = 64 * NWM * NWN;    // threads of one K group
     constexpr int PB = WPB * NWN;          // panels per tile
     constexpr int BM = WM * NWM;           // rows per tile
     constexpr int RBW = WM / 16;           // row blocks per wave
-    constexpr int UPT = PB * 64 / NT;      // weight runs per thread per chunk
-    static_assert(PB * 64 % NT == 0 && UPT >= 1, "tile and workgroup do not divide");
-    __shared__ u32x4 sW[2][PB][4][64];
+    constexpr int UPT = PB * 64 / NTG;     // weight runs per thread per chunk
+    static_assert(PB * 64 % NTG == 0 && UPT >= 1, "tile and workgroup do not divide");
+    static_assert(KS == 1 || WPB * RBW * NWM * NWN * 64 <= 2 * PB * 4 * 64, "K-split reduction must fit in LDS");
+    __shared__ u32x4 sWall[KS][2][PB][4][64];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    const int kg = wall / (NWM * NWN);                    // K group
+    const int w = wall % (NWM * NWN), tid = threadIdx.x % NTG;
+    auto &sW = sWall[kg];
     const int wm = w % NWM, wn = w / NWM;
     const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
     const int T = tn * tm;
@@ -495,7 +499,9 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
     const int gm = min(tm - first_m, G), lin = L - gid * gsize;
     const int mt = first_m + lin % gm, nt = lin / gm;
     const int m0 = mt * BM + wm * WM, p0 = nt * PB;
-    const int nch = a.K / kChunk;
+    // K group kg owns chunks [c_lo, c_hi); every group runs the same number
+    // of chunks (the host only splits K when the chunk count divides).
+    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
     const int r16 = lane & 15, g4 = lane >> 4;
 
     const uint16_t *xrow[RBW];
@@ -517,43 +523,50 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
     RunRaw<FMT> raw[UPT];
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
-        const int u = tid + NT * s;
+        const int u = tid + NTG * s;
         const int p = p0 + (u >> 6);
         src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, u & 15);
     }
 
-    u32x4 xf[RBW][4];
+    // XD register sets of activation fragments: set c % XD holds chunk c, and
+    // is refilled with chunk c + XD as soon as each fragment is consumed.
+    u32x4 xs[XD][RBW][4];
     // prologue: chunk 0 unpacked into LDS buffer 0, chunk 1 raw in registers,
-    // chunk 0 activations in registers
+    // chunks 0 .. XD-1 activations in registers
 #pragma unroll
-    for (int s = 0; s < UPT; s++) src[s].load(0, raw[s]);
+    for (int s = 0; s < UPT; s++) src[s].load(c_lo, raw[s]);
 #pragma unroll
-    for (int rb = 0; rb < RBW; rb++)
+    for (int d = 0; d < XD; d++) {
+        const int cd = c_lo + d < c_hi ? c_lo + d : c_hi - 1;
 #pragma unroll
-        for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + 32 * i);
+        for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) xs[d][rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cd + 32 * i);
+    }
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
         u32x4 f[4];
-        unpack_run<FMT, DT>(raw[s], src[s], 0, f);
-        const int pb = (tid + NT * s) >> 6;
+        unpack_run<FMT, DT>(raw[s], src[s], c_lo, f);
+        const int pb = (tid + NTG * s) >> 6;
 #pragma unroll
         for (int j = 0; j < 4; j++) sW[0][pb][src[s].g][j * 16 + src[s].col] = f[j];
     }
-    const int c1 = nch > 1 ? 1 : 0;
+    const int c1 = c_lo + 1 < c_hi ? c_lo + 1 : c_hi - 1;
 #pragma unroll
     for (int s = 0; s < UPT; s++) src[s].load(c1, raw[s]);
     __syncthreads();
 
     // Steady state, branch-free: chunk c is multiplied from LDS buffer c&1
     // while chunk c+1 (raw bytes already in registers) is unpacked word by
-    // word into buffer (c+1)&1, the activations of chunk c+1 replace those of
-    // chunk c step by step, and the raw bytes of chunk c+2 are requested.
+    // word into buffer (c+1)&1, the activations of chunk c+XD replace those
+    // of chunk c step by step, and the raw bytes of chunk c+2 are requested.
     // Past the last chunk the indices are clamped: the extra work is
     // harmless (the buffer written is never read again).
-    for (int c = 0; c < nch; c++) {
-        const int buf = c & 1;
-        const int cn = c + 1 < nch ? c + 1 : nch - 1;
-        const int cnn = c + 2 < nch ? c + 2 : nch - 1;
+    auto body = [&](int c, u32x4 (&xf)[RBW][4]) {
+        const int buf = (c - c_lo) & 1;
+        const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
+        const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
+        const int cx = c + XD < c_hi ? c + XD : c_hi - 1;
         RunParams pr[UPT];
 #pragma unroll
         for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(raw[s], src[s], cn);
@@ -570,11 +583,11 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
                 for (int pb = 0; pb < WPB; pb++) acc[pb][rb] = mma<DT>(wcur[pb], xf[rb][i], acc[pb][rb]);
-                xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cn + 32 * i);
+                xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cx + 32 * i);
             }
 #pragma unroll
             for (int s = 0; s < UPT; s++) {
-                const int pb = (tid + NT * s) >> 6;
+                const int pb = (tid + NTG * s) >> 6;
                 sW[buf ^ 1][pb][src[s].g][i * 16 + src[s].col] = unpack_word<FMT, DT>(raw[s], pr[s], i);
             }
             if (i < 3) {
@@ -599,7 +612,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 #pragma unroll
             for (int s = 0; s < UPT; s++) {
                 if (pr[s].exact) {
-                    const int pb = (tid + NT * s) >> 6;
+                    const int pb = (tid + NTG * s) >> 6;
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         sW[buf ^ 1][pb][src[s].g][i * 16 + src[s].col] =
@@ -610,6 +623,31 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 #pragma unroll
         for (int s = 0; s < UPT; s++) src[s].load(cnn, raw[s]);
         __syncthreads();
+    };
+    if constexpr (XD == 1) {
+        for (int c = c_lo; c < c_hi; c++) body(c, xs[0]);
+    } else {
+        for (int c = c_lo; c < c_hi; c += 2) {
+            body(c, xs[0]);
+            if (c + 1 < c_hi) body(c + 1, xs[1]);
+        }
+    }
+    if constexpr (KS == 2) {
+        // K group 1 hands its partial sums to group 0 through its own LDS
+        // buffers (free after the last barrier of the loop)
+        f32x4 *red = reinterpret_cast<f32x4 *>(&sWall[1][0][0][0][0]);
+        if (kg == 1) {
+#pragma unroll
+            for (int pb = 0; pb < WPB; pb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++) red[((w * WPB + pb) * RBW + rb) * 64 + lane] = acc[pb][rb];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int pb = 0; pb < WPB; pb++)
+#pragma unroll
+            for (int rb = 0; rb < RBW; rb++) acc[pb][rb] += red[((w * WPB + pb) * RBW + rb) * 64 + lane];
     }
 #pragma unroll
     for (int pb = 0; pb < WPB; pb++)
@@ -661,10 +699,14 @@ enum Rung {
     RUNG_S256 = 3,       // stream 256x128, 4 waves of 64x128
     RUNG_S128_IL = 4,    // as RUNG_S128, MFMA and unpack interleaved
     RUNG_S256_IL = 5,    // as RUNG_S256, MFMA and unpack interleaved
-    RUNG_COUNT = 6
+    RUNG_S256_W8 = 6,    // stream 256x128, 8 waves of 32x128
+    RUNG_S128_X2 = 7,    // as RUNG_S128, activations prefetched two chunks ahead
+    RUNG_S128_K2 = 8,    // as RUNG_S128, K split between two 4-wave groups of one workgroup
+    RUNG_COUNT = 9
 };
-const char *const kRungNames[RUNG_COUNT] = {"direct-small-m", "direct-skinny-n", "stream-128x128",
-                                            "stream-256x128", "stream-128x128-il", "stream-256x128-il"};
+const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "stream-128x128",
+                                            "stream-256x128",    "stream-128x128-il", "stream-256x128-il",
+                                            "stream-256x128-w8", "stream-128x128-x2", "stream-128x128-k2"};
 
 struct Plan {
     int rung;
@@ -710,11 +752,14 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_S128:
     case RUNG_S256:
     case RUNG_S128_IL:
-    case RUNG_S256_IL: {
-        pl.rows = (rung == RUNG_S256 || rung == RUNG_S256_IL) ? 256 : 128;
+    case RUNG_S256_IL:
+    case RUNG_S256_W8:
+    case RUNG_S128_X2:
+    case RUNG_S128_K2: {
+        pl.rows = (rung == RUNG_S256 || rung == RUNG_S256_IL || rung == RUNG_S256_W8) ? 256 : 128;
         pl.cols = 128;
-        pl.waves = 4;
-        pl.kw = 1;
+        pl.kw = (rung == RUNG_S128_K2 && (K / kChunk) % 2 == 0) ? 2 : 1;
+        pl.waves = rung == RUNG_S256_W8 ? 8 : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         pl.tiles_n = ceil_div(np, 8);
         pl.tiles_m = ceil_div(M, pl.rows);
@@ -742,14 +787,21 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
 //    and the kernel is a weight stream; with many panels, four panels per
 //    wave, otherwise one panel per wave and all rows per wave;
-//  * otherwise the streaming 128x128 tile, unless it would leave most CUs
-//    idle (fewer than 128 tiles), where the direct kernel keeps them busy.
+//  * fewer than 128 tiles of 128x128: the direct kernel keeps more CUs busy;
+//  * at least 256 tiles of 256x128: the 8-wave 256x128 tile, which unpacks
+//    each weight once for 256 rows;
+//  * at most 256 tiles of 128x128: the 128x128 tile with K split between two
+//    wave groups, twice the parallelism per tile;
+//  * otherwise the 128x128 tile.
 int select_rung(long long M, long long N)
 {
-    const long long np = (N + 15) / 16;
+    const long long np = (N + 15) / 16, tn = (np + 7) / 8;
     if (np <= 4) return RUNG_SKINNY_N;
     if (M <= 64) return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
-    if (((np + 7) / 8) * ((M + 127) / 128) < 128) return RUNG_SKINNY_N;
+    const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
+    if (t128 < 128) return RUNG_SKINNY_N;
+    if (t256 >= 256) return RUNG_S256_W8;
+    if (t128 <= 256) return RUNG_S128_K2;
     return RUNG_S128;
 }
 
@@ -783,16 +835,28 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
     switch (pl.rung) {
     case RUNG_S128:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_S256:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, false>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, false, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_S128_IL:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, true>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, true, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_S256_IL:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, true>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, true, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_S256_W8:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 8, 1, false, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        return hipGetLastError();
+    case RUNG_S128_X2:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 2, 1>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_S128_K2:
+        if ((a.K / kChunk) % 2 == 0)
+            hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 1, 2>), pl.grid, dim3(512), 0, s, a);
+        else  // an odd chunk count is not split
+            hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     default:
         break;
