@@ -316,6 +316,27 @@ __device__ __forceinline__ f32x4 mma<DT_BF16>(u32x4 a, u32x4 b, f32x4 c)
                                                    0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32x16 MFMA: twice the MACs of the 16x16x32 form per instruction and, on
+// gfx950, twice its sustained rate.
+template <int DT>
+__device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mma32<DT_F16>(u32x4 a, u32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mma32<DT_BF16>(u32x4 a, u32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
 template <int DT>
 __device__ __forceinline__ uint32_t pack_out(float a, float b)
 {
@@ -343,6 +364,28 @@ __device__ __forceinline__ void store_block(const Args &a, f32x4 v, int m_base, 
     } else {
         const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
         for (int j = 0; j < 4 && n0 + j < a.N; j++) y[j] = e[j];
+    }
+}
+
+// Store one 32x32 accumulator (Y^T layout): lane holds row m = m_base +
+// lane%32 and, for q = 0..3, columns n_base + 8q + 4*(lane/32) + 0..3.
+template <int DT>
+__device__ __forceinline__ void store_block32(const Args &a, const f32x16 &v, int m_base, int n_base, int lane)
+{
+    const int m = m_base + (lane & 31);
+    if (m >= a.M) return;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int n0 = n_base + 8 * q + 4 * (lane >> 5);
+        if (n0 >= a.N) continue;
+        uint16_t *y = a.Y + (long long)m * a.N + n0;
+        const uint32_t lo = pack_out<DT>(v[4 * q], v[4 * q + 1]), hi = pack_out<DT>(v[4 * q + 2], v[4 * q + 3]);
+        if (n0 + 4 <= a.N && (a.N & 3) == 0) {
+            *(u32x2 *)y = u32x2{lo, hi};
+        } else {
+            const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+            for (int j = 0; j < 4 && n0 + j < a.N; j++) y[j] = e[j];
+        }
     }
 }
 
@@ -657,6 +700,165 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
 }
 
 // ---------------------------------------------------------------------------
+// Streaming tile kernel on 32x32x16 MFMAs (the fast form on gfx950).
+//
+// Same structure as k_stream: NWM x NWN waves (times KS K groups) own a
+// (NWM*WM) x (16*WPB*NWN) tile; each weight is unpacked once per workgroup
+// into a double-buffered LDS tile, activations go straight to VGPRs, one
+// barrier per 128-wide chunk.  One MFMA covers 32 columns (two panels) and
+// 16 K; lane (r, h) of k-step s carries k = 128c + 16s + 8h + 0..7 in both
+// operands, so word i of the run g of a column lands in k-step 2g + i/2,
+// lane half i%2, and an activation fragment is 16 contiguous bytes of a row.
+// ---------------------------------------------------------------------------
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream32(Args a)
+{
+    constexpr int NTG = 64 * NWM * NWN;    // threads of one K group
+    constexpr int PB = WPB * NWN;          // panels per tile
+    constexpr int CB = PB / 2;             // 32-column blocks per tile
+    constexpr int CBW = WPB / 2;           // 32-column blocks per wave
+    constexpr int BM = WM * NWM;           // rows per tile
+    constexpr int RBW = WM / 32;           // 32-row blocks per wave
+    constexpr int UPT = PB * 64 / NTG;     // weight runs per thread per chunk
+    static_assert(WPB % 2 == 0 && WM % 32 == 0, "32x32 blocks");
+    static_assert(PB * 64 % NTG == 0 && UPT >= 1, "tile and workgroup do not divide");
+    static_assert(KS == 1 || CBW * RBW * 16 * NWM * NWN * 64 <= 2 * CB * 8 * 64 * 4, "K-split reduction must fit in LDS");
+    __shared__ u32x4 sWall[KS][2][CB][8][64];
+
+    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    const int kg = wall / (NWM * NWN);
+    const int w = wall % (NWM * NWN), tid = threadIdx.x % NTG;
+    auto &sW = sWall[kg];
+    const int wm = w % NWM, wn = w / NWM;
+    const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
+    const int T = tn * tm;
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    const int L = xcd * (T >> 3) + min(xcd, T & 7) + slot;
+    const int G = tm <= kGroupM ? tm : 1;
+    const int gsize = G * tn, gid = L / gsize, first_m = gid * G;
+    const int gm = min(tm - first_m, G), lin = L - gid * gsize;
+    const int mt = first_m + lin % gm, nt = lin / gm;
+    const int m0 = mt * BM + wm * WM, p0 = nt * PB;
+    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
+
+    const uint16_t *xrow[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; rb++) {
+        int r = m0 + 32 * rb + (lane & 31);
+        r = r < a.M ? r : a.M - 1;
+        xrow[rb] = a.X + (long long)r * a.K + 8 * (lane >> 5);
+    }
+
+    f32x16 acc[CBW][RBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0.f;
+
+    RunSrc<FMT> src[UPT];
+    RunRaw<FMT> raw[UPT];
+    int slot_cp[UPT], slot_lane[UPT];
+#pragma unroll
+    for (int s = 0; s < UPT; s++) {
+        const int u = tid + NTG * s, pl = u >> 6, col = u & 15;
+        const int p = p0 + pl;
+        src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, col);
+        slot_cp[s] = pl >> 1;
+        slot_lane[s] = 16 * (pl & 1) + col;
+    }
+    // word i of run g goes to k-step 2g + i/2, lane (i%2)*32 + slot_lane
+    auto put = [&](int buf, int s, int i, u32x4 v) {
+        sW[buf][slot_cp[s]][2 * src[s].g + (i >> 1)][(i & 1) * 32 + slot_lane[s]] = v;
+    };
+
+    u32x4 xf[RBW][8];
+#pragma unroll
+    for (int s = 0; s < UPT; s++) src[s].load(c_lo, raw[s]);
+#pragma unroll
+    for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+        for (int ks = 0; ks < 8; ks++) xf[rb][ks] = *(const u32x4 *)(xrow[rb] + kChunk * c_lo + 16 * ks);
+#pragma unroll
+    for (int s = 0; s < UPT; s++) {
+        u32x4 f[4];
+        unpack_run<FMT, DT>(raw[s], src[s], c_lo, f);
+#pragma unroll
+        for (int i = 0; i < 4; i++) put(0, s, i, f[i]);
+    }
+    const int c1 = c_lo + 1 < c_hi ? c_lo + 1 : c_hi - 1;
+#pragma unroll
+    for (int s = 0; s < UPT; s++) src[s].load(c1, raw[s]);
+    __syncthreads();
+
+    for (int c = c_lo; c < c_hi; c++) {
+        const int buf = (c - c_lo) & 1;
+        const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
+        const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
+        RunParams pr[UPT];
+#pragma unroll
+        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(raw[s], src[s], cn);
+        u32x4 wcur[CBW], wnxt[CBW];
+#pragma unroll
+        for (int cb = 0; cb < CBW; cb++) wcur[cb] = sW[buf][wn * CBW + cb][0][lane];
+#pragma unroll
+        for (int ks = 0; ks < 8; ks++) {
+            if (ks < 7) {
+#pragma unroll
+                for (int cb = 0; cb < CBW; cb++) wnxt[cb] = sW[buf][wn * CBW + cb][ks + 1][lane];
+            }
+#pragma unroll
+            for (int rb = 0; rb < RBW; rb++) {
+#pragma unroll
+                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma32<DT>(wcur[cb], xf[rb][ks], acc[cb][rb]);
+                xf[rb][ks] = *(const u32x4 *)(xrow[rb] + kChunk * cn + 16 * ks);
+            }
+            if ((ks & 1) == 0) {
+#pragma unroll
+                for (int s = 0; s < UPT; s++) put(buf ^ 1, s, ks >> 1, unpack_word<FMT, DT>(raw[s], pr[s], ks >> 1));
+            }
+            if (ks < 7) {
+#pragma unroll
+                for (int cb = 0; cb < CBW; cb++) wcur[cb] = wnxt[cb];
+            }
+        }
+        if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
+#pragma unroll
+            for (int s = 0; s < UPT; s++) {
+                if (pr[s].exact) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) put(buf ^ 1, s, i, unpack_word_exact_bf16(raw[s].codes, pr[s].fa, pr[s].nb, i));
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < UPT; s++) src[s].load(cnn, raw[s]);
+        __syncthreads();
+    }
+    if constexpr (KS == 2) {
+        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[1][0][0][0][0]);
+        if (kg == 1) {
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++) red[((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+            for (int rb = 0; rb < RBW; rb++) acc[cb][rb] += red[((w * CBW + cb) * RBW + rb) * 64 + lane];
+    }
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+            store_block32<DT>(a, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * (wn * CBW + cb), lane);
+}
+
+// ---------------------------------------------------------------------------
 // Staged dequant: the same unpack, written out as logical W[K][N].
 // One thread per (panel, chunk, run, column).
 // ---------------------------------------------------------------------------
@@ -702,11 +904,17 @@ enum Rung {
     RUNG_S256_W8 = 6,    // stream 256x128, 8 waves of 32x128
     RUNG_S128_X2 = 7,    // as RUNG_S128, activations prefetched two chunks ahead
     RUNG_S128_K2 = 8,    // as RUNG_S128, K split between two 4-wave groups of one workgroup
-    RUNG_COUNT = 9
+    RUNG_M128 = 9,       // 32x32x16 MFMA: 128x128, 4 waves of 32x128
+    RUNG_M128_K2 = 10,   // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
+    RUNG_M256_W8 = 11,   // 32x32x16 MFMA: 256x128, 8 waves of 32x128
+    RUNG_M256 = 12,      // 32x32x16 MFMA: 256x128, 4 waves of 64x128
+    RUNG_COUNT = 13
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "stream-128x128",
                                             "stream-256x128",    "stream-128x128-il", "stream-256x128-il",
-                                            "stream-256x128-w8", "stream-128x128-x2", "stream-128x128-k2"};
+                                            "stream-256x128-w8", "stream-128x128-x2", "stream-128x128-k2",
+                                            "mfma32-128x128",    "mfma32-128x128-k2", "mfma32-256x128-w8",
+                                            "mfma32-256x128"};
 
 struct Plan {
     int rung;
@@ -755,11 +963,16 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_S256_IL:
     case RUNG_S256_W8:
     case RUNG_S128_X2:
-    case RUNG_S128_K2: {
-        pl.rows = (rung == RUNG_S256 || rung == RUNG_S256_IL || rung == RUNG_S256_W8) ? 256 : 128;
+    case RUNG_S128_K2:
+    case RUNG_M128:
+    case RUNG_M128_K2:
+    case RUNG_M256_W8:
+    case RUNG_M256: {
+        pl.rows = (rung == RUNG_S256 || rung == RUNG_S256_IL || rung == RUNG_S256_W8 || rung == RUNG_M256_W8 ||
+                   rung == RUNG_M256) ? 256 : 128;
         pl.cols = 128;
-        pl.kw = (rung == RUNG_S128_K2 && (K / kChunk) % 2 == 0) ? 2 : 1;
-        pl.waves = rung == RUNG_S256_W8 ? 8 : 4 * pl.kw;
+        pl.kw = ((rung == RUNG_S128_K2 || rung == RUNG_M128_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
+        pl.waves = (rung == RUNG_S256_W8 || rung == RUNG_M256_W8) ? 8 : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         pl.tiles_n = ceil_div(np, 8);
         pl.tiles_m = ceil_div(M, pl.rows);
@@ -851,6 +1064,21 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         return hipGetLastError();
     case RUNG_S128_X2:
         hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 2, 1>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M128:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M128_K2:
+        if ((a.K / kChunk) % 2 == 0)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 2>), pl.grid, dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M256_W8:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M256:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 64, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_S128_K2:
         if ((a.K / kChunk) % 2 == 0)
