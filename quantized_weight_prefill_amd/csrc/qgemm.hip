@@ -36,6 +36,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <algorithm>
 
 #include "qgemm.h"
 
@@ -53,6 +54,7 @@ enum { FMT_Q4K = QGEMM_FMT_Q4K, FMT_Q6K = QGEMM_FMT_Q6K, FMT_W4 = QGEMM_FMT_W4A1
 enum { DT_F16 = QGEMM_F16, DT_BF16 = QGEMM_BF16 };
 
 constexpr int kChunk = 128;  // K per step: four 32-wide runs, one per lane group
+constexpr int kCUs = 256;     // compute units of one MI355X (the ladder's occupancy model)
 constexpr int kGroupM = 8;   // row tiles per group in the streaming tile order
 constexpr int kQ4kRec = 2304, kQ6kRec = 3360;
 constexpr float kTwo24 = 16777216.0f;
@@ -68,6 +70,28 @@ struct Args {
     int kw;      // direct kernel: waves splitting K inside a workgroup
     long long w4_sreg, w4_zreg;  // W4A16 byte offsets of the scale / zero regions
 };
+
+// XCD-aware renumbering: workgroup b of n runs on XCD b % 8; give each XCD a
+// contiguous range of logical indices (a bijection on [0, n)).
+__device__ __forceinline__ int xcd_order(int b, int n)
+{
+    const int xcd = b & 7, slot = b >> 3;
+    return xcd * (n >> 3) + min(xcd, n & 7) + slot;
+}
+
+// Logical tile L of a tm x tn grid.  With at most kGroupM row tiles the row
+// tile varies fastest, so the tiles that share one column panel (its weights)
+// run together on one XCD; with more, the column tile varies fastest, so the
+// tiles running together share one activation row block, the larger per-tile
+// stream.
+__device__ __forceinline__ void tile_coords(int L, int tm, int tn, int &mt, int &nt)
+{
+    const int G = tm <= kGroupM ? tm : 1;
+    const int gsize = G * tn, gid = L / gsize, first_m = gid * G;
+    const int gm = min(tm - first_m, G), lin = L - gid * gsize;
+    mt = first_m + lin % gm;
+    nt = lin / gm;
+}
 
 // ---------------------------------------------------------------------------
 // Unpack primitives
@@ -527,20 +551,8 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
     auto &sW = sWall[kg];
     const int wm = w % NWM, wn = w / NWM;
     const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
-    const int T = tn * tm;
-    // XCD-aware renumbering: WG b runs on XCD b % 8; give each XCD a contiguous
-    // range of logical tiles (a bijection on [0, T)).
-    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-    const int L = xcd * (T >> 3) + min(xcd, T & 7) + slot;
-    // Logical order.  With at most kGroupM row tiles the row tile varies
-    // fastest, so the tiles that share one column panel (its weights) run
-    // together on one XCD; with more, the column tile varies fastest, so the
-    // tiles running together share one activation row block, the larger
-    // per-tile stream.
-    const int G = tm <= kGroupM ? tm : 1;
-    const int gsize = G * tn, gid = L / gsize, first_m = gid * G;
-    const int gm = min(tm - first_m, G), lin = L - gid * gsize;
-    const int mt = first_m + lin % gm, nt = lin / gm;
+    int mt, nt;
+    tile_coords(xcd_order(blockIdx.x, gridDim.x), tm, tn, mt, nt);
     const int m0 = mt * BM + wm * WM, p0 = nt * PB;
     // K group kg owns chunks [c_lo, c_hi); every group runs the same number
     // of chunks (the host only splits K when the chunk count divides).
@@ -710,37 +722,26 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
 // operands, so word i of the run g of a column lands in k-step 2g + i/2,
 // lane half i%2, and an activation fragment is 16 contiguous bytes of a row.
 // ---------------------------------------------------------------------------
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
-__global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream32(Args a)
-{
-    constexpr int NTG = 64 * NWM * NWN;    // threads of one K group
-    constexpr int PB = WPB * NWN;          // panels per tile
-    constexpr int CB = PB / 2;             // 32-column blocks per tile
-    constexpr int CBW = WPB / 2;           // 32-column blocks per wave
-    constexpr int BM = WM * NWM;           // rows per tile
-    constexpr int RBW = WM / 32;           // 32-row blocks per wave
-    constexpr int UPT = PB * 64 / NTG;     // weight runs per thread per chunk
+// One workgroup's pass over K chunks [c_lo, c_hi) of one tile: wave (wm, wn)
+// adds its WM x (16*WPB) block of X[rows m0..][:] * W[:][panels p0..] into acc.
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN>
+struct Stream32 {
+    static constexpr int NTG = 64 * NWM * NWN;  // threads of one K group
+    static constexpr int PB = WPB * NWN;        // panels per tile
+    static constexpr int CB = PB / 2;           // 32-column blocks per tile
+    static constexpr int CBW = WPB / 2;         // 32-column blocks per wave
+    static constexpr int BM = WM * NWM;         // rows per tile
+    static constexpr int RBW = WM / 32;         // 32-row blocks per wave
+    static constexpr int RUNS = PB * 64;        // 32-code weight runs per chunk
+    static constexpr int UPT = (RUNS + NTG - 1) / NTG;  // runs per thread per chunk
+    static constexpr int UFULL = RUNS / NTG;    // slots every thread fills
     static_assert(WPB % 2 == 0 && WM % 32 == 0, "32x32 blocks");
-    static_assert(PB * 64 % NTG == 0 && UPT >= 1, "tile and workgroup do not divide");
-    static_assert(KS == 1 || CBW * RBW * 16 * NWM * NWN * 64 <= 2 * CB * 8 * 64 * 4, "K-split reduction must fit in LDS");
-    __shared__ u32x4 sWall[KS][2][CB][8][64];
+    static_assert(UPT >= 1 && (RUNS - UFULL * NTG) % 64 == 0, "a partial slot must cover whole waves");
+    typedef u32x4 Lds[2][CB][8][64];
 
-    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
-    const int kg = wall / (NWM * NWN);
-    const int w = wall % (NWM * NWN), tid = threadIdx.x % NTG;
-    auto &sW = sWall[kg];
-    const int wm = w % NWM, wn = w / NWM;
-    const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
-    const int T = tn * tm;
-    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-    const int L = xcd * (T >> 3) + min(xcd, T & 7) + slot;
-    const int G = tm <= kGroupM ? tm : 1;
-    const int gsize = G * tn, gid = L / gsize, first_m = gid * G;
-    const int gm = min(tm - first_m, G), lin = L - gid * gsize;
-    const int mt = first_m + lin % gm, nt = lin / gm;
-    const int m0 = mt * BM + wm * WM, p0 = nt * PB;
-    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
-
+    static __device__ __forceinline__ void run(const Args &a, Lds &sW, int tid, int lane, int wn, int m0, int p0,
+                                               int c_lo, int c_hi, f32x16 (&acc)[CBW][RBW])
+    {
     const uint16_t *xrow[RBW];
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++) {
@@ -749,31 +750,28 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream32(Args a)
         xrow[rb] = a.X + (long long)r * a.K + 8 * (lane >> 5);
     }
 
-    f32x16 acc[CBW][RBW];
-#pragma unroll
-    for (int cb = 0; cb < CBW; cb++)
-#pragma unroll
-        for (int rb = 0; rb < RBW; rb++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0.f;
-
+    u32x4 xf[RBW][8];
     RunSrc<FMT> src[UPT];
     RunRaw<FMT> raw[UPT];
     int slot_cp[UPT], slot_lane[UPT];
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
-        const int u = tid + NTG * s, pl = u >> 6, col = u & 15;
+        // the last slot may exist only for the first waves; the others
+        // shadow a real run (loads stay in bounds) and never store it
+        const int u0 = tid + NTG * s, u = u0 < RUNS ? u0 : u0 - NTG, pl = u >> 6, col = u & 15;
         const int p = p0 + pl;
         src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, col);
         slot_cp[s] = pl >> 1;
         slot_lane[s] = 16 * (pl & 1) + col;
     }
+    // the partial slot is live for whole waves (a wave-uniform test)
+    const bool extra = __builtin_amdgcn_readfirstlane(tid >> 6) < (RUNS - UFULL * NTG) / 64;
+    auto live = [&](int s) { return s < UFULL || extra; };
     // word i of run g goes to k-step 2g + i/2, lane (i%2)*32 + slot_lane
     auto put = [&](int buf, int s, int i, u32x4 v) {
-        sW[buf][slot_cp[s]][2 * src[s].g + (i >> 1)][(i & 1) * 32 + slot_lane[s]] = v;
+        if (live(s)) sW[buf][slot_cp[s]][2 * src[s].g + (i >> 1)][(i & 1) * 32 + slot_lane[s]] = v;
     };
 
-    u32x4 xf[RBW][8];
 #pragma unroll
     for (int s = 0; s < UPT; s++) src[s].load(c_lo, raw[s]);
 #pragma unroll
@@ -792,22 +790,33 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream32(Args a)
     for (int s = 0; s < UPT; s++) src[s].load(c1, raw[s]);
     __syncthreads();
 
-    for (int c = c_lo; c < c_hi; c++) {
-        const int buf = (c - c_lo) & 1;
+    // One chunk: MFMAs over LDS buffer `buf`, unpack of chunk c+1 (held in
+    // `ru`) into the other buffer, and the raw loads of chunk c+2 into `rf`,
+    // issued first so that a whole chunk of MFMAs covers their latency.  The
+    // activation fragment of k-step ks is reloaded for chunk c+1 as soon as
+    // its MFMAs are issued.  Scheduling barriers keep the compiler from
+    // sinking those loads to the end of the loop and put each k-step's LDS
+    // reads ahead of the previous k-step's MFMAs.
+    RunRaw<FMT> raw2[UPT];
+    auto chunk = [&](int c, int buf, RunRaw<FMT>(&ru)[UPT], RunRaw<FMT>(&rf)[UPT]) {
         const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
         const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
-        RunParams pr[UPT];
 #pragma unroll
-        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(raw[s], src[s], cn);
+        for (int s = 0; s < UPT; s++) src[s].load(cnn, rf[s]);
         u32x4 wcur[CBW], wnxt[CBW];
 #pragma unroll
         for (int cb = 0; cb < CBW; cb++) wcur[cb] = sW[buf][wn * CBW + cb][0][lane];
+        __builtin_amdgcn_sched_barrier(0);
+        RunParams pr[UPT];
+#pragma unroll
+        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(ru[s], src[s], cn);
 #pragma unroll
         for (int ks = 0; ks < 8; ks++) {
             if (ks < 7) {
 #pragma unroll
                 for (int cb = 0; cb < CBW; cb++) wnxt[cb] = sW[buf][wn * CBW + cb][ks + 1][lane];
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
@@ -816,26 +825,61 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream32(Args a)
             }
             if ((ks & 1) == 0) {
 #pragma unroll
-                for (int s = 0; s < UPT; s++) put(buf ^ 1, s, ks >> 1, unpack_word<FMT, DT>(raw[s], pr[s], ks >> 1));
+                for (int s = 0; s < UPT; s++) put(buf ^ 1, s, ks >> 1, unpack_word<FMT, DT>(ru[s], pr[s], ks >> 1));
             }
             if (ks < 7) {
 #pragma unroll
                 for (int cb = 0; cb < CBW; cb++) wcur[cb] = wnxt[cb];
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
 #pragma unroll
             for (int s = 0; s < UPT; s++) {
                 if (pr[s].exact) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) put(buf ^ 1, s, i, unpack_word_exact_bf16(raw[s].codes, pr[s].fa, pr[s].nb, i));
+                    for (int i = 0; i < 4; i++) put(buf ^ 1, s, i, unpack_word_exact_bf16(ru[s].codes, pr[s].fa, pr[s].nb, i));
                 }
             }
         }
-#pragma unroll
-        for (int s = 0; s < UPT; s++) src[s].load(cnn, raw[s]);
         __syncthreads();
+    };
+    int c = c_lo;
+    for (; c + 1 < c_hi; c += 2) {
+        chunk(c, 0, raw, raw2);
+        chunk(c + 1, 1, raw2, raw);
     }
+    if (c < c_hi) chunk(c, 0, raw, raw2);
+    }
+};
+
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(WM == 32 ? 2 : 1)))
+k_stream32(Args a)
+{
+    using S = Stream32<FMT, DT, WM, WPB, NWM, NWN>;
+    constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM, CB = S::CB;
+    static_assert(KS == 1 || CBW * RBW * 16 * NWM * NWN * 64 <= 2 * CB * 8 * 64 * 4, "K-split reduction must fit in LDS");
+    __shared__ typename S::Lds sWall[KS];
+
+    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    const int kg = wall / (NWM * NWN);
+    const int w = wall % (NWM * NWN), tid = threadIdx.x % S::NTG;
+    const int wm = w % NWM, wn = w / NWM;
+    const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
+    int mt, nt;
+    tile_coords(xcd_order(blockIdx.x, gridDim.x), tm, tn, mt, nt);
+    const int m0 = mt * BM + wm * WM, p0 = nt * PB;
+    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
+
+    f32x16 acc[CBW][RBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0.f;
+    S::run(a, sWall[kg], tid, lane, wn, m0, p0, c_lo, c_hi, acc);
     if constexpr (KS == 2) {
         f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[1][0][0][0][0]);
         if (kg == 1) {
@@ -908,13 +952,14 @@ enum Rung {
     RUNG_M128_K2 = 10,   // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
     RUNG_M256_W8 = 11,   // 32x32x16 MFMA: 256x128, 8 waves of 32x128
     RUNG_M256 = 12,      // 32x32x16 MFMA: 256x128, 4 waves of 64x128
-    RUNG_COUNT = 13
+    RUNG_M128N160 = 13,  // 32x32x16 MFMA: 128x160, 4 waves of 32x160
+    RUNG_COUNT = 14
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "stream-128x128",
                                             "stream-256x128",    "stream-128x128-il", "stream-256x128-il",
                                             "stream-256x128-w8", "stream-128x128-x2", "stream-128x128-k2",
                                             "mfma32-128x128",    "mfma32-128x128-k2", "mfma32-256x128-w8",
-                                            "mfma32-256x128"};
+                                            "mfma32-256x128",    "mfma32-128x160"};
 
 struct Plan {
     int rung;
@@ -967,14 +1012,15 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128:
     case RUNG_M128_K2:
     case RUNG_M256_W8:
-    case RUNG_M256: {
+    case RUNG_M256:
+    case RUNG_M128N160: {
         pl.rows = (rung == RUNG_S256 || rung == RUNG_S256_IL || rung == RUNG_S256_W8 || rung == RUNG_M256_W8 ||
                    rung == RUNG_M256) ? 256 : 128;
-        pl.cols = 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : 128;
         pl.kw = ((rung == RUNG_S128_K2 || rung == RUNG_M128_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
         pl.waves = (rung == RUNG_S256_W8 || rung == RUNG_M256_W8) ? 8 : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
-        pl.tiles_n = ceil_div(np, 8);
+        pl.tiles_n = ceil_div(np, pl.cols / 16);
         pl.tiles_m = ceil_div(M, pl.rows);
         pl.grid = dim3((unsigned)(pl.tiles_n * pl.tiles_m), 1, 1);
         pl.lds = 0;
@@ -1001,21 +1047,40 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    and the kernel is a weight stream; with many panels, four panels per
 //    wave, otherwise one panel per wave and all rows per wave;
 //  * fewer than 128 tiles of 128x128: the direct kernel keeps more CUs busy;
-//  * at least 256 tiles of 256x128: the 8-wave 256x128 tile, which unpacks
-//    each weight once for 256 rows;
-//  * at most 256 tiles of 128x128: the 128x128 tile with K split between two
-//    wave groups, twice the parallelism per tile;
-//  * otherwise the 128x128 tile.
-int select_rung(long long M, long long N)
+//  * at least 512 tiles of 256x128: the 8-wave 256x128 tile on 16x16x32
+//    MFMAs, which unpacks each weight once for 256 rows;
+//  * at most 256 tiles of 128x128 over K >= 8192: the 128x128 tile on
+//    32x32x16 MFMAs with K split between two wave groups;
+//  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
+//    whichever the occupancy model below finishes first.
+// Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
+// of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
+// the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
+// runs alone on a CU (one wave per SIMD) counts 1.43 (a constant fitted to
+// the measured times of both widths at M = 300, 658 and 1024).
+double stream_cost(long long M, long long np, int cols)
+{
+    const long long T = ((M + 127) / 128) * ((np + cols / 16 - 1) / (cols / 16));
+    const long long n = (T + kCUs - 1) / kCUs;
+    const double t = (n & 1) ? (double)(n - 1) + 1.43 : (double)n;
+    return t * cols / 128.0;
+}
+
+int select_rung(int fmt, long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, tn = (np + 7) / 8;
     if (np <= 4) return RUNG_SKINNY_N;
     if (M <= 64) return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     if (t128 < 128) return RUNG_SKINNY_N;
-    if (t256 >= 256) return RUNG_S256_W8;
-    if (t128 <= 256) return RUNG_S128_K2;
-    return RUNG_S128;
+    // many 256-row tiles: eight waves at two per SIMD hide the most latency
+    if (t256 >= 512) return RUNG_S256_W8;
+    // few tiles over a long K: split K inside the workgroup
+    if (t128 <= 256 && K >= 8192) return RUNG_M128_K2;
+    // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
+    // runs do not fit that variant's registers)
+    if (fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128)) return RUNG_M128N160;
+    return RUNG_M128;
 }
 
 template <int FMT, int DT, int RB, int PN>
@@ -1079,6 +1144,9 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         return hipGetLastError();
     case RUNG_M256:
         hipLaunchKernelGGL((k_stream32<FMT, DT, 64, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M128N160:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 10, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_S128_K2:
         if ((a.K / kChunk) % 2 == 0)
@@ -1158,7 +1226,7 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     if (!X || !W || !Y) return QGEMM_ERR_NULL;
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
     Plan pl;
-    if (!make_plan(rung < 0 ? select_rung(M, N) : rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
+    if (!make_plan(rung < 0 ? select_rung(fmt, M, N, K) : rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
     Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
     a.kw = pl.kw;
     return launch_status(launch(fmt, dtype, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
@@ -1236,7 +1304,7 @@ int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int d
 
 int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
 {
-    return qgemm_rung_info(select_rung(M, N), format, M, N, K, dtype, info8);
+    return qgemm_rung_info(select_rung(format, M, N, K), format, M, N, K, dtype, info8);
 }
 
 int qgemm_dequant(int format, const void *W, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,

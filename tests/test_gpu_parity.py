@@ -203,3 +203,4 @@ def test_rungs_agree_with_each_other():
     ys = oracle.bits_to_double_fast(from_device(c.run(-1, x_bits=c.X[rows])), qg.F16)
     _, B = oracle.gemm(c.X[rows], c.W, qg.F16)
     assert np.all(np.abs(y[rows] - ys) <= 2 * 2e-3 * B)
+
