@@ -17,6 +17,9 @@ Profiling helpers (same JSON line, restricted work):
     --copy-calibration BYTES
                         run a plain device-to-device copy of BYTES bytes three
                         times and exit (reference for HBM byte counters)
+    --no-ceiling        skip the MFMA rate probe (`mfma_ceiling`: what the
+                        chip sustains on random operands under its power
+                        limit, for reading `roofline.frac` against)
 """
 from __future__ import annotations
 
@@ -80,6 +83,7 @@ def main() -> int:
     ap.add_argument("--only", default=None, help="run only the GEMM with this label")
     ap.add_argument("--rung", type=int, default=-1, help="force a rung (-1: M-ladder)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
@@ -168,6 +172,9 @@ def main() -> int:
                 "frac": round(gbps / PEAK_HBM_GBPS, 4)}
     roof["kernel"] = f"{gd['label']} ({gd['fmt']} M={gd['M']} K={gd['K']} N={gd['N']}, rung {gd['rung']})"
     roof["traffic"] = measured_traffic(f"{args.workload}/{gd['label']}")
+    ceiling = None if args.no_ceiling else mfma_ceiling(gd["dt"])
+    if ceiling is not None and roof["bound"] == "mfma":
+        roof["frac_of_sustained"] = round(pd["tflops"] / ceiling["value"], 4)
 
     out = {
         "metric": METRIC,
@@ -188,6 +195,8 @@ def main() -> int:
         "per_kernel": per,
         "roofline": roof,
     }
+    if ceiling is not None:
+        out["mfma_ceiling"] = ceiling
     if args.only is not None or args.rung >= 0:
         out["config"]["only"] = args.only
         out["config"]["rung"] = args.rung
@@ -199,6 +208,39 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(gemms, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def mfma_ceiling(dt) -> dict:
+    """What the chip sustains on dense MFMA work: the rate probe (four waves
+    per SIMD, four independent 32x32x16 accumulators per wave) on seeded
+    uniform random operands, timed with HIP events on the launch stream.  The
+    clock drops under this load by an amount that depends on the operand
+    bits, so this sits below the spec peak (which assumes the full clock)."""
+    import torch
+
+    rng = np.random.default_rng(7)
+    tdt = torch.float16 if dt == qg.F16 else torch.bfloat16
+    blocks, iters, reps = 1024, 4000, 5
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = 2.0 * 32 * 32 * 16 * 4 * iters * 4 * blocks
+
+    def rate(ops):
+        for _ in range(2):
+            qg.probe_mfma(ops, out, blocks, iters, dt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            qg.probe_mfma(ops, out, blocks, iters, dt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(flops / (e0.elapsed_time(e1) / reps) / 1e9, 1)
+
+    random_ops = torch.from_numpy(rng.uniform(-1.0, 1.0, 256 * 8 * 8).astype(np.float32)).to(tdt).cuda()
+    zero_ops = torch.zeros(256 * 8 * 8, dtype=tdt, device="cuda")
+    return {"value": rate(random_ops), "unit": "TFLOP/s", "dtype": "f16" if dt == qg.F16 else "bf16",
+            "operands": "uniform random in [-1, 1], seeded", "zero_operands": rate(zero_ops),
+            "probe": "32x32x16 MFMA, 4 waves/SIMD, 4 chains/wave"}
 
 
 def copy_calibration(nbytes: int) -> int:

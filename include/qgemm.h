@@ -173,6 +173,17 @@ int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, vo
 int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
                   int dtype, void *stream);
 
+/* Measurement aid, not part of the GEMM path: runs `blocks` workgroups of
+ * 256 threads, each wave issuing `iters` rounds of four independent
+ * 32x32x16 MFMAs (fp16 or bf16 by `dtype`) on operands read once from
+ * `operands` (device, 16-byte aligned, 32 KiB: 256 threads x 8 vectors of 16
+ * bytes), and writes one float per thread to `out` (device, blocks*256
+ * floats) so the work stays live.  FLOPs = 2*32*32*16 * 4 * iters * 4 waves
+ * * blocks.  Timing it on random operands gives the MFMA rate the chip
+ * sustains under its power limit.  Errors: QGEMM_ERR_NULL, _ALIGN, _SHAPE
+ * (blocks or iters < 1), _DTYPE, _HIP. */
+int qgemm_probe_mfma(const void *operands, float *out, int blocks, int iters, int dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,6 +75,7 @@ SIGNATURES = {
     "qgemm_rung_info": (_INT, [_INT, _INT, _I64, _I64, _I64, _INT, _VP]),
     "qgemm_gemm_rung": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_probe_mfma": (_INT, [_VP, _VP, _INT, _INT, _INT, _VP]),
 }
 
 
@@ -283,6 +284,14 @@ def dequant(fmt, wp, N: int, K: int, dtype, group: int = 0, has_zp: bool = False
                              _stream(stream))
     _check("qgemm_dequant", st)
     return w
+
+
+def probe_mfma(operands, out, blocks: int, iters: int, dtype=F16, stream=None):
+    """Launch the MFMA rate probe (a measurement aid; see include/qgemm.h)."""
+    torch = _torch()
+    code = F16 if dtype in (F16, torch.float16) else BF16
+    _check("qgemm_probe_mfma", lib().qgemm_probe_mfma(_dev(operands, "operands"), _dev(out, "out"), blocks, iters, code,
+                                                      _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

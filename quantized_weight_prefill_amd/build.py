@@ -10,7 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libqgemm.so")
-SOURCES = [os.path.join(PKG, "csrc", "qgemm.hip"), os.path.join(PKG, "csrc", "pack.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("qgemm.hip", "pack.cpp", "probe.hip")]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,68 @@
+// Measurement aid, not part of the GEMM path: the sustained rate of the
+// 32x32x16 MFMA on operands the caller supplies.  MI355X lowers its clock
+// under dense MFMA load by an amount that depends on the operand bits (random
+// fp16 data draws more power than zeros or constants), so the rate a real
+// GEMM can reach sits below the 2.5 PFLOP/s dense fp16 figure, which assumes
+// the full clock.  The probe reports that ceiling for a given operand set.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qgemm.h"
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Every wave runs `iters` rounds of four independent 32x32x16 MFMAs; lane l
+// of thread t takes its A operands from ops[8t .. 8t+3] and its B operands,
+// rotating, from ops[8t+4 .. 8t+7] (one 32 KiB operand block for all waves).
+template <int DT>
+__global__ void __launch_bounds__(256) k_probe(const u32x4 *ops, float *out, int iters)
+{
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        a[j] = ops[threadIdx.x * 8 + j];
+        b[j] = ops[threadIdx.x * 8 + 4 + j];
+    }
+    f32x16 c[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) c[j][e] = 0.f;
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if constexpr (DT == QGEMM_F16)
+                c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[j]),
+                                                              __builtin_bit_cast(f16x8, b[(j + it) & 3]), c[j], 0, 0, 0);
+            else
+                c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[j]),
+                                                               __builtin_bit_cast(bf16x8, b[(j + it) & 3]), c[j], 0, 0, 0);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) s += c[j][0] + c[j][15];
+    out[blockIdx.x * 256 + threadIdx.x] = s;  // keeps the MFMAs live
+}
+
+}  // namespace
+
+extern "C" int qgemm_probe_mfma(const void *operands, float *out, int blocks, int iters, int dtype, void *stream)
+{
+    if (!operands || !out) return QGEMM_ERR_NULL;
+    if (((uintptr_t)operands & 15u) != 0) return QGEMM_ERR_ALIGN;
+    if (blocks < 1 || iters < 1) return QGEMM_ERR_SHAPE;
+    if (dtype != QGEMM_F16 && dtype != QGEMM_BF16) return QGEMM_ERR_DTYPE;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == QGEMM_F16)
+        hipLaunchKernelGGL(k_probe<QGEMM_F16>, dim3(blocks), dim3(256), 0, s, (const u32x4 *)operands, out, iters);
+    else
+        hipLaunchKernelGGL(k_probe<QGEMM_BF16>, dim3(blocks), dim3(256), 0, s, (const u32x4 *)operands, out, iters);
+    return hipGetLastError() == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+}
