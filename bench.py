@@ -13,6 +13,9 @@ oracle timed on a bounded sample of the same workload.
 
 Profiling helpers (same JSON line, restricted work):
     --only LABEL        run only that GEMM of the workload
+    --pool-mb MB        weight-bound GEMMs (below the ridge) rotate through copies of
+                        their packed weights totalling >= MB (default 640), so the
+                        256 MB Infinity Cache cannot serve them
     --rung R            force rung R instead of the M-ladder's choice
     --copy-calibration BYTES
                         run a plain device-to-device copy of BYTES bytes three
@@ -84,6 +87,9 @@ def main() -> int:
     ap.add_argument("--rung", type=int, default=-1, help="force a rung (-1: M-ladder)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
+    ap.add_argument("--pool-mb", type=float, default=640.0,
+                    help="weight-bound GEMMs rotate through copies of their weights totalling at least this many MB "
+                         "per GEMM, so the 256 MB Infinity Cache cannot hold them (0: no rotation)")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
@@ -108,9 +114,15 @@ def main() -> int:
         wp = torch.from_numpy(packed).to(dev)
         y = torch.empty((M, N), dtype=tdt, device=dev)
         info = qg.select_rung(fmt, M, N, K, dt) if args.rung < 0 else qg.rung_info(args.rung, fmt, M, N, K, dt)
+        wbytes = weight_bytes(fmt, N, K, group or 128, sym)
+        # below the ridge the kernel is a weight stream: time it on weights that come from HBM
+        intensity = 2.0 * M * N * K / (wbytes + 2 * M * K + 2 * M * N)
+        ncopy = 1
+        if args.pool_mb > 0 and intensity < PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBPS * 1e9):
+            ncopy = max(1, int(np.ceil(args.pool_mb * 1e6 / packed.nbytes)))
+        pool = [wp] + [wp.clone() for _ in range(ncopy - 1)]
         gemms.append(dict(label=label, fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym, x=x, wp=wp, y=y,
-                          X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K,
-                          wbytes=weight_bytes(fmt, N, K, group or 128, sym)))
+                          X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K, wbytes=wbytes, pool=pool, turn=0))
         print(f"[bench] {label}: {fmt} M={M} K={K} N={N} rung={info['name']}", file=sys.stderr, flush=True)
 
     if not gemms:
@@ -118,15 +130,17 @@ def main() -> int:
         return 2
 
     def call(g):
+        wp = g["pool"][g["turn"] % len(g["pool"])]
+        g["turn"] += 1
         if args.rung >= 0:
-            qg.gemm_rung(g["fmt"], args.rung, g["x"], g["wp"], g["N"], group=g["group"], has_zp=not g["sym"],
+            qg.gemm_rung(g["fmt"], args.rung, g["x"], wp, g["N"], group=g["group"], has_zp=not g["sym"],
                          out=g["y"])
         elif g["fmt"] == "q4k":
-            qg.q4k(g["x"], g["wp"], g["N"], out=g["y"])
+            qg.q4k(g["x"], wp, g["N"], out=g["y"])
         elif g["fmt"] == "q6k":
-            qg.q6k(g["x"], g["wp"], g["N"], out=g["y"])
+            qg.q6k(g["x"], wp, g["N"], out=g["y"])
         else:
-            qg.w4a16(g["x"], g["wp"], g["N"], g["group"], not g["sym"], out=g["y"])
+            qg.w4a16(g["x"], wp, g["N"], g["group"], not g["sym"], out=g["y"])
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -153,7 +167,28 @@ def main() -> int:
         ms = float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
         per.append(dict(label=g["label"], fmt=g["fmt"], M=g["M"], K=g["K"], N=g["N"], rung=g["rung"],
                         ms=round(ms, 5), tflops=round(g["flops"] / ms / 1e9, 2),
-                        weight_gbps=round(g["wbytes"] / ms / 1e6, 1)))
+                        weight_gbps=round(g["wbytes"] / ms / 1e6, 1),
+                        weight_frac_hbm=round(g["wbytes"] / ms / 1e6 / PEAK_HBM_GBPS, 4),
+                        weight_copies=len(g["pool"])))
+    # Weight-bound GEMMs are short: per-launch events add a fixed cost, so they
+    # are also timed back to back (50 launches a sample, median of 5, weights
+    # rotating) next to a plain streaming read of the same bytes.
+    for g, p in zip(gemms, per):
+        if len(g["pool"]) > 1:
+            samples = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(50):
+                    call(g)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples.append(e0.elapsed_time(e1) / 50)
+            b2b = float(np.median(samples))
+            p["ms_back_to_back"] = round(b2b, 5)
+            p["weight_gbps_back_to_back"] = round(g["wbytes"] / b2b / 1e6, 1)
+            p["read_probe_gbps"] = read_ceiling(g["pool"])
+            p["weight_frac_of_read_probe"] = round(p["weight_gbps_back_to_back"] / p["read_probe_gbps"], 4)
     flops_step = sum(g["flops"] for g in gemms)
     kernel_ms_step = sum(p["ms"] for p in per)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
@@ -175,6 +210,8 @@ def main() -> int:
     ceiling = None if args.no_ceiling else mfma_ceiling(gd["dt"])
     if ceiling is not None and roof["bound"] == "mfma":
         roof["frac_of_sustained"] = round(pd["tflops"] / ceiling["value"], 4)
+    if roof["bound"] == "hbm" and "read_probe_gbps" in pd:
+        roof["frac_of_sustained"] = round(pd["weight_gbps_back_to_back"] / pd["read_probe_gbps"], 4)
 
     out = {
         "metric": METRIC,
@@ -241,6 +278,28 @@ def mfma_ceiling(dt) -> dict:
     return {"value": rate(random_ops), "unit": "TFLOP/s", "dtype": "f16" if dt == qg.F16 else "bf16",
             "operands": "uniform random in [-1, 1], seeded", "zero_operands": rate(zero_ops),
             "probe": "32x32x16 MFMA, 4 waves/SIMD, 4 chains/wave"}
+
+
+def read_ceiling(pool, reps: int = 30) -> float:
+    """GB/s of the streaming-read probe over the same rotating weight copies
+    (best of three grid sizes), timed like the GEMMs: HIP events on the launch
+    stream around back-to-back launches."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for blocks in (1024, 2048, 4096):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        for i in range(3):
+            qg.probe_read(pool[i % len(pool)], out, blocks)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            qg.probe_read(pool[i % len(pool)], out, blocks)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, pool[0].numel() * pool[0].element_size() / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9)
+    return round(best, 1)
 
 
 def copy_calibration(nbytes: int) -> int:

@@ -184,6 +184,15 @@ int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_
  * (blocks or iters < 1), _DTYPE, _HIP. */
 int qgemm_probe_mfma(const void *operands, float *out, int blocks, int iters, int dtype, void *stream);
 
+/* Measurement aid, not part of the GEMM path: a plain streaming read of
+ * `bytes` (a positive multiple of 16) from `buf` (device, 16-byte aligned) by
+ * `blocks` workgroups of 256 threads, 16-byte loads at a grid stride, four in
+ * flight per thread; each thread writes one 32-bit word to `out` (device,
+ * blocks*256 words) so the loads stay live.  Timed on buffers that miss the
+ * Infinity Cache it is the HBM read rate a weight stream can hope for.
+ * Errors: QGEMM_ERR_NULL, _ALIGN, _SHAPE, _HIP. */
+int qgemm_probe_read(const void *buf, int64_t bytes, void *out, int blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,6 +76,7 @@ SIGNATURES = {
     "qgemm_gemm_rung": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_probe_mfma": (_INT, [_VP, _VP, _INT, _INT, _INT, _VP]),
+    "qgemm_probe_read": (_INT, [_VP, _I64, _VP, _INT, _VP]),
 }
 
 
@@ -292,6 +293,12 @@ def probe_mfma(operands, out, blocks: int, iters: int, dtype=F16, stream=None):
     code = F16 if dtype in (F16, torch.float16) else BF16
     _check("qgemm_probe_mfma", lib().qgemm_probe_mfma(_dev(operands, "operands"), _dev(out, "out"), blocks, iters, code,
                                                       _stream(stream)))
+
+
+def probe_read(buf, out, blocks: int, stream=None):
+    """Launch the streaming-read probe over all of `buf` (a measurement aid)."""
+    _check("qgemm_probe_read", lib().qgemm_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(out, "out"),
+                                                      blocks, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -1,5 +1,6 @@
-// Measurement aid, not part of the GEMM path: the sustained rate of the
-// 32x32x16 MFMA on operands the caller supplies.  MI355X lowers its clock
+// Measurement aids, not part of the GEMM path.  The MFMA probe gives the
+// sustained rate of the 32x32x16 MFMA on operands the caller supplies; the
+// read probe gives the rate of a plain streaming read.  MI355X lowers its clock
 // under dense MFMA load by an amount that depends on the operand bits (random
 // fp16 data draws more power than zeros or constants), so the rate a real
 // GEMM can reach sits below the 2.5 PFLOP/s dense fp16 figure, which assumes
@@ -51,7 +52,35 @@ __global__ void __launch_bounds__(256) k_probe(const u32x4 *ops, float *out, int
     out[blockIdx.x * 256 + threadIdx.x] = s;  // keeps the MFMAs live
 }
 
+// Streaming read: each thread loads 16-byte vectors at a grid stride, four
+// in flight per step, and folds them into one word so the loads stay live.
+__global__ void __launch_bounds__(256) k_read(const u32x4 *buf, long long nvec, uint32_t *out)
+{
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        const u32x4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+    }
+    for (; i < nvec; i += stride) {
+        const u32x4 a = buf[i];
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+    out[(long long)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+extern "C" int qgemm_probe_read(const void *buf, int64_t bytes, void *out, int blocks, void *stream)
+{
+    if (!buf || !out) return QGEMM_ERR_NULL;
+    if (((uintptr_t)buf & 15u) != 0) return QGEMM_ERR_ALIGN;
+    if (bytes < 16 || bytes % 16 != 0 || blocks < 1) return QGEMM_ERR_SHAPE;
+    hipLaunchKernelGGL(k_read, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4 *)buf, (long long)(bytes / 16),
+                       (uint32_t *)out);
+    return hipGetLastError() == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+}
 
 extern "C" int qgemm_probe_mfma(const void *operands, float *out, int blocks, int iters, int dtype, void *stream)
 {

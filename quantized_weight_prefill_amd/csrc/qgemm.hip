@@ -1044,8 +1044,9 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    direct kernel with all panels per wave (a 128-wide tile would leave most
 //    of the part idle and most of each tile padding);
 //  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
-//    and the kernel is a weight stream; with many panels, four panels per
-//    wave, otherwise one panel per wave and all rows per wave;
+//    and the kernel is a weight stream; with many panels or more than 32
+//    rows, four panels per wave, otherwise one panel per wave and all rows
+//    per wave;
 //  * fewer than 128 tiles of 128x128: the direct kernel keeps more CUs busy;
 //  * at least 512 tiles of 256x128: the 8-wave 256x128 tile on 16x16x32
 //    MFMAs, which unpacks each weight once for 256 rows;
@@ -1070,7 +1071,9 @@ int select_rung(int fmt, long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, tn = (np + 7) / 8;
     if (np <= 4) return RUNG_SKINNY_N;
-    if (M <= 64) return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
+    // above 32 rows a one-panel wave carries three or four row blocks of
+    // activations per weight run; four panels per wave and a grid over M win
+    if (M <= 64) return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     if (t128 < 128) return RUNG_SKINNY_N;
     // many 256-row tiles: eight waves at two per SIMD hide the most latency

@@ -229,6 +229,11 @@ WORKLOADS = {
         "gemms": [("wide", "q4k", 4096, 4096, 12288, BF16, 0, False),
                   ("skinny", "q4k", 4096, 4096, 32, BF16, 0, False)],
     },
+    "small_m_probes": {  # decode-adjacent M on the up (Q4_K) and down (Q6_K) shapes: weight streams
+        "index": 5,
+        "gemms": [(f"{lab}_m{M}", fmt, M, K, N, F16, 0, False) for M in (1, 16, 64)
+                  for lab, fmt, K, N in (("up", "q4k", 4096, 12288), ("down", "q6k", 12288, 4096))],
+    },
 }
 
 
