@@ -87,6 +87,7 @@ def main() -> int:
     ap.add_argument("--rung", type=int, default=-1, help="force a rung (-1: M-ladder)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
+    ap.add_argument("--no-staged", action="store_true", help="skip the staged-arm comparison")
     ap.add_argument("--pool-mb", type=float, default=640.0,
                     help="weight-bound GEMMs rotate through copies of their weights totalling at least this many MB "
                          "per GEMM, so the 256 MB Infinity Cache cannot hold them (0: no rotation)")
@@ -207,6 +208,7 @@ def main() -> int:
                 "frac": round(gbps / PEAK_HBM_GBPS, 4)}
     roof["kernel"] = f"{gd['label']} ({gd['fmt']} M={gd['M']} K={gd['K']} N={gd['N']}, rung {gd['rung']})"
     roof["traffic"] = measured_traffic(f"{args.workload}/{gd['label']}")
+    staged = None if args.no_staged else staged_arm(gd, call)
     ceiling = None if args.no_ceiling else mfma_ceiling(gd["dt"])
     if ceiling is not None and roof["bound"] == "mfma":
         roof["frac_of_sustained"] = round(pd["tflops"] / ceiling["value"], 4)
@@ -234,6 +236,8 @@ def main() -> int:
     }
     if ceiling is not None:
         out["mfma_ceiling"] = ceiling
+    if staged is not None:
+        out["staged_arm"] = staged
     if args.only is not None or args.rung >= 0:
         out["config"]["only"] = args.only
         out["config"]["rung"] = args.rung
@@ -278,6 +282,50 @@ def mfma_ceiling(dt) -> dict:
     return {"value": rate(random_ops), "unit": "TFLOP/s", "dtype": "f16" if dt == qg.F16 else "bf16",
             "operands": "uniform random in [-1, 1], seeded", "zero_operands": rate(zero_ops),
             "probe": "32x32x16 MFMA, 4 waves/SIMD, 4 chains/wave"}
+
+
+def staged_arm(g, call, reps: int = 20) -> dict:
+    """The dominant GEMM fused (M-ladder rung, and the 128x128 rung the staged
+    GEMM shares its tile with) against the staged arm: unpack into a 2-byte
+    scratch, then the same 128x128 streaming kernel on it.  Back-to-back
+    launches between HIP events on the launch stream, median of 5 samples."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    rung128 = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-128x128"][0]
+    grp = g["group"] if g["fmt"] == "w4a16" else 0
+    scratch = torch.empty(qg.staged_scratch_bytes(g["N"], g["K"]), dtype=torch.uint8, device="cuda")
+    x0 = g["x"][:0]
+    y0 = g["y"][:0]
+
+    def timed(fn):
+        fn()
+        samples = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            samples.append(e0.elapsed_time(e1) / reps)
+        return float(np.median(samples))
+
+    fused = timed(lambda: call(g))
+    same_tile = timed(lambda: qg.gemm_rung(g["fmt"], rung128, g["x"], g["wp"], g["N"], group=grp,
+                                           has_zp=not g["sym"], out=g["y"]))
+    staged = timed(lambda: qg.staged(g["fmt"], g["x"], g["wp"], g["N"], scratch=scratch, group=grp,
+                                     has_zp=not g["sym"], out=g["y"]))
+    unpack = timed(lambda: qg.staged(g["fmt"], x0, g["wp"], g["N"], scratch=scratch, group=grp,
+                                     has_zp=not g["sym"], out=y0))
+    wq = g["wbytes"]
+    w16 = 2.0 * g["K"] * (-(-g["N"] // 16) * 16)
+    return {"gemm": g["label"], "fused_ms": round(fused, 5), "fused_same_tile_ms": round(same_tile, 5),
+            "staged_ms": round(staged, 5), "unpack_ms": round(unpack, 5),
+            "staged_gemm_ms": round(staged - unpack, 5), "staged_over_fused_same_tile": round(staged / same_tile, 3),
+            "weight_bytes_fused": round(wq), "weight_bytes_staged": round(wq + 2 * w16),
+            "note": "staged = unpack pass (reads packed W, writes 2 B/weight) + the same 128x128 kernel reading "
+                    "2 B/weight; its Y equals the fused 128x128 rung's Y bit for bit"}
 
 
 def read_ceiling(pool, reps: int = 30) -> float:

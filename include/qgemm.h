@@ -173,6 +173,26 @@ int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, vo
 int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
                   int dtype, void *stream);
 
+/* The staged arm (the dequant-scratch post's "two passes": unpack to a
+ * 16-bit scratch, then a GEMM that reads it), kept beside the fused path to
+ * measure what fusing saves on this GPU.  Step one unpacks every weight of
+ * Wpacked with the fused path's unpack into `scratch` (device, 16-byte
+ * aligned, at least qgemm_staged_scratch_bytes(N, K) bytes, caller-owned;
+ * 2 bytes per weight, N padded to whole panels of 16, in the order the
+ * streaming kernel consumes: per (panel, 128-wide K chunk) 4 KB laid out
+ * [word 0..3][run 16g+col][16 bytes], word i of run g of column col holding
+ * k = 128c + 32g + 8i .. +7 of that column, two weights per 32-bit word, the
+ * lower k in the low half).  Step two is the 128x128 streaming kernel of the
+ * fused path with its unpack replaced by loads of those words, so Y equals
+ * the fused `mfma32-128x128` rung's Y bit for bit.  Both launches go on
+ * `stream`.  Arguments and errors as qgemm_gemm_rung (group_size ignored for
+ * the k-quants), plus QGEMM_ERR_SIZE when scratch_bytes is too small and
+ * QGEMM_ERR_NULL when scratch is NULL.  M = 0 still fills the scratch.
+ * qgemm_staged_scratch_bytes returns 0 for an illegal N or K. */
+size_t qgemm_staged_scratch_bytes(int64_t N, int64_t K);
+int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, size_t scratch_bytes, void *Y, int64_t M,
+                 int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+
 /* Measurement aid, not part of the GEMM path: runs `blocks` workgroups of
  * 256 threads, each wave issuing `iters` rounds of four independent
  * 32x32x16 MFMAs (fp16 or bf16 by `dtype`) on operands read once from

@@ -75,6 +75,8 @@ SIGNATURES = {
     "qgemm_rung_info": (_INT, [_INT, _INT, _I64, _I64, _I64, _INT, _VP]),
     "qgemm_gemm_rung": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_staged_scratch_bytes": (_SZ, [_I64, _I64]),
+    "qgemm_staged": (_INT, [_INT, _VP, _VP, _VP, _SZ, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_probe_mfma": (_INT, [_VP, _VP, _INT, _INT, _INT, _VP]),
     "qgemm_probe_read": (_INT, [_VP, _I64, _VP, _INT, _VP]),
 }
@@ -285,6 +287,26 @@ def dequant(fmt, wp, N: int, K: int, dtype, group: int = 0, has_zp: bool = False
                              _stream(stream))
     _check("qgemm_dequant", st)
     return w
+
+
+def staged_scratch_bytes(N: int, K: int) -> int:
+    return int(lib().qgemm_staged_scratch_bytes(N, K))
+
+
+def staged(fmt, x, wp, N: int, scratch=None, group: int = 0, has_zp: bool = True, out=None, stream=None):
+    """The staged arm: unpack into `scratch` (allocated here when None), then
+    the 128x128 streaming GEMM on it.  Returns (y, scratch)."""
+    torch = _torch()
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    M, K = x.shape
+    if scratch is None:
+        scratch = torch.empty(staged_scratch_bytes(N, K), dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    st = lib().qgemm_staged(f, _dev(x, "x"), _dev(wp, "wp"), _dev(scratch, "scratch"),
+                            scratch.numel() * scratch.element_size(), _dev(y, "out"), M, N, K, group,
+                            int(bool(has_zp)), _dtype_code(x), _stream(stream))
+    _check("qgemm_staged", st)
+    return y, scratch
 
 
 def probe_mfma(operands, out, blocks: int, iters: int, dtype=F16, stream=None):

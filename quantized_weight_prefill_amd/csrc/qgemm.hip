@@ -51,6 +51,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum { FMT_Q4K = QGEMM_FMT_Q4K, FMT_Q6K = QGEMM_FMT_Q6K, FMT_W4 = QGEMM_FMT_W4A16 };
+// internal source: weights already unpacked into the staged arm's scratch
+constexpr int FMT_DENSE = 3;
 enum { DT_F16 = QGEMM_F16, DT_BF16 = QGEMM_BF16 };
 
 constexpr int kChunk = 128;  // K per step: four 32-wide runs, one per lane group
@@ -206,6 +208,33 @@ struct RunSrc {
     }
 };
 
+// The staged arm's source: weights already unpacked into a scratch buffer,
+// 4 KB per (panel, chunk) ordered [word i][run 16g+col][16 bytes], so that a
+// wave's load (or store) of word i is one contiguous kilobyte.
+template <>
+struct RunRaw<FMT_DENSE> {
+    u32x4 w[4];
+};
+
+template <>
+struct RunSrc<FMT_DENSE> {
+    const uint8_t *rec;  // run (g, col) of chunk 0 of the panel
+    int g, col;
+
+    __device__ __forceinline__ void init(const Args &a, int p, int g_, int col_)
+    {
+        g = g_;
+        col = col_;
+        rec = a.W + (long long)p * (a.K / kChunk) * 4096 + (16 * g + col) * 16;
+    }
+
+    __device__ __forceinline__ void load(int c, RunRaw<FMT_DENSE> &r) const
+    {
+#pragma unroll
+        for (int i = 0; i < 4; i++) r.w[i] = *(const u32x4 *)(rec + (long long)c * 4096 + 1024 * i);
+    }
+};
+
 // Per-run dequant constants (computed once per run, reused by its four words).
 struct RunParams {
     float fa, nb;    // words 0..3 (Q6_K: words 0..1): factor*2^24 and -bias
@@ -218,7 +247,11 @@ __device__ __forceinline__ RunParams run_params(const RunRaw<FMT> &u, const RunS
 {
     RunParams pr{};
     const int g = src.g;
-    if constexpr (FMT == FMT_Q4K) {
+    if constexpr (FMT == FMT_DENSE) {
+        (void)u;
+        (void)g;
+        (void)c;
+    } else if constexpr (FMT == FMT_Q4K) {
         const float d = f16_to_f32(u.hd[0] & 0xFFFFu), dmin = f16_to_f32(u.hd[0] >> 16);
         const uint32_t s0 = u.hd[1], s1 = u.hd[2], s2 = u.hd[3];
         const int sh = 8 * g;
@@ -261,6 +294,10 @@ template <int FMT, int DT>
 __device__ __forceinline__ u32x4 unpack_word(const RunRaw<FMT> &u, const RunParams &pr, int i)
 {
     u32x4 out;
+    if constexpr (FMT == FMT_DENSE) {
+        (void)pr;
+        return u.w[i];
+    } else {
     const uint32_t x = u.codes[i], x8 = x >> 8;
     if constexpr (FMT == FMT_Q6K) {
         const float fa = i < 2 ? pr.fa : pr.fa1, nb = i < 2 ? pr.nb : pr.nb1;
@@ -280,6 +317,7 @@ __device__ __forceinline__ u32x4 unpack_word(const RunRaw<FMT> &u, const RunPara
         for (int p = 0; p < 4; p++) out[p] = dq_pair<DT>(t[p], (p & 1) ? fa16 : pr.fa, pr.nb);
     }
     return out;
+    }
 }
 
 // Word i of a bf16 Q4_K run whose values may not fit binary32 (pr.exact).
@@ -935,6 +973,33 @@ __global__ void __launch_bounds__(256) k_dequant(Args a, uint16_t *Wout)
 }
 
 // ---------------------------------------------------------------------------
+// Staged arm, step one: the same unpack, written to a scratch buffer in the
+// order the streaming kernel reads it (the FMT_DENSE layout): one thread per
+// (panel, chunk, run); a wave's four 16-byte stores are four contiguous
+// kilobytes.  Step two is k_stream32<FMT_DENSE, ...> on that scratch.
+// ---------------------------------------------------------------------------
+template <int FMT, int DT>
+__global__ void __launch_bounds__(256) k_stage(Args a, uint8_t *Ws)
+{
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int nch = a.K / kChunk;
+    const long long total = (long long)a.np * nch * 64;
+    if (idx >= total) return;
+    const int run = (int)(idx & 63), col = run & 15, g = run >> 4;
+    const long long pc = idx >> 6;  // = panel * nch + chunk
+    const int c = (int)(pc % nch), p = (int)(pc / nch);
+    RunSrc<FMT> src;
+    src.init(a, p, g, col);
+    RunRaw<FMT> raw;
+    src.load(c, raw);
+    u32x4 f[4];
+    unpack_run<FMT, DT>(raw, src, c, f);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(Ws + pc * 4096) + run;
+#pragma unroll
+    for (int i = 0; i < 4; i++) dst[64 * i] = f[i];
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation, the M-ladder, launches.
 // ---------------------------------------------------------------------------
 
@@ -1235,6 +1300,46 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     return launch_status(launch(fmt, dtype, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
 }
 
+size_t staged_scratch_bytes(long long N, long long K)
+{
+    if (N < 1 || K < 1 || K % kChunk != 0) return 0;
+    return (size_t)((N + 15) / 16) * 16 * (size_t)K * 2;
+}
+
+template <int DT>
+hipError_t launch_staged_dt(int fmt, const Args &a, uint8_t *scratch, const Plan &pl, hipStream_t s)
+{
+    const long long work = (long long)a.np * (a.K / kChunk) * 64;
+    const dim3 grid((unsigned)((work + 255) / 256));
+    if (fmt == FMT_Q4K) hipLaunchKernelGGL((k_stage<FMT_Q4K, DT>), grid, dim3(256), 0, s, a, scratch);
+    else if (fmt == FMT_Q6K) hipLaunchKernelGGL((k_stage<FMT_Q6K, DT>), grid, dim3(256), 0, s, a, scratch);
+    else hipLaunchKernelGGL((k_stage<FMT_W4, DT>), grid, dim3(256), 0, s, a, scratch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.M == 0) return e;
+    Args b = a;
+    b.W = scratch;
+    hipLaunchKernelGGL((k_stream32<FMT_DENSE, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
+int staged(int fmt, const void *X, const void *W, void *scratch, size_t scratch_bytes, void *Y, long long M, long long N,
+           long long K, long long group, int has_zp, int dtype, void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, M, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (!W || !scratch || (M > 0 && (!X || !Y))) return QGEMM_ERR_NULL;
+    if (!aligned16(W) || !aligned16(scratch) || (M > 0 && (!aligned16(X) || !aligned16(Y)))) return QGEMM_ERR_ALIGN;
+    if (scratch_bytes < staged_scratch_bytes(N, K)) return QGEMM_ERR_SIZE;
+    Plan pl;
+    if (!make_plan(RUNG_M128, M > 0 ? M : 1, N, K, pl)) return QGEMM_ERR_FORMAT;
+    Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
+    const hipError_t e = dtype == DT_F16 ? launch_staged_dt<DT_F16>(fmt, a, (uint8_t *)scratch, pl, (hipStream_t)stream)
+                                         : launch_staged_dt<DT_BF16>(fmt, a, (uint8_t *)scratch, pl, (hipStream_t)stream);
+    return launch_status(e, "staged");
+}
+
 void fill_info(const Plan &pl, int32_t *info)
 {
     info[0] = pl.rung;
@@ -1330,6 +1435,18 @@ int qgemm_dequant(int format, const void *W, void *Wout, int64_t N, int64_t K, i
     else { if (dtype == DT_F16) QG_DQ(FMT_W4, DT_F16); else QG_DQ(FMT_W4, DT_BF16); }
 #undef QG_DQ
     return launch_status(hipGetLastError(), "dequant");
+}
+
+size_t qgemm_staged_scratch_bytes(int64_t N, int64_t K)
+{
+    return staged_scratch_bytes(N, K);
+}
+
+int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, size_t scratch_bytes, void *Y, int64_t M,
+                 int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream)
+{
+    return staged(format, X, Wpacked, scratch, scratch_bytes, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype,
+                  stream);
 }
 
 }  // extern "C"

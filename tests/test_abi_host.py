@@ -183,6 +183,14 @@ def test_device_entry_argument_errors():
     assert lib.qgemm_q4k(None, None, None, 0, 16, 256, 0, s) == 0
     assert lib.qgemm_dequant(0, None, A, 16, 256, 0, 0, 0, s) == -1
     assert lib.qgemm_dequant(2, A, A, 16, 256, 0, 0, 0, s) == -5
+    # staged arm: scratch checks come before any launch
+    need = lib.qgemm_staged_scratch_bytes(20, 512)
+    assert need == 32 * 512 * 2 and lib.qgemm_staged_scratch_bytes(20, 200) == 0
+    assert lib.qgemm_staged(0, A, A, None, need, A, 4, 20, 512, 0, 0, 0, s) == -1
+    assert lib.qgemm_staged(0, A, A, A, need - 16, A, 4, 20, 512, 0, 0, 0, s) == -6
+    assert lib.qgemm_staged(0, A, A, mis, need, A, 4, 20, 512, 0, 0, 0, s) == -4
+    assert lib.qgemm_staged(1, A, A, A, need, A, 4, 20, 500, 0, 0, 0, s) == -2
+    assert lib.qgemm_staged(2, A, A, A, need, A, 4, 20, 512, 0, 1, 0, s) == -5
 
 
 # ----------------------------------------------------------------------------

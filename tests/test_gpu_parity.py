@@ -204,3 +204,47 @@ def test_rungs_agree_with_each_other():
     _, B = oracle.gemm(c.X[rows], c.W, qg.F16)
     assert np.all(np.abs(y[rows] - ys) <= 2 * 2e-3 * B)
 
+
+
+# ----------------------------------------------------------------------------
+# staged arm: unpack to scratch, then the same streaming GEMM on the scratch
+# ----------------------------------------------------------------------------
+
+def _scratch_to_w(scratch_bits: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Logical W[K][N] from the staged scratch, read the way include/qgemm.h
+    describes it: per (panel, chunk) [word i][run 16g+col][8 halves], halves
+    k = 128c + 32g + 8i + 0..7 in order."""
+    npan, nch = -(-N // 16), K // 128
+    s = scratch_bits[:npan * 16 * K].reshape(npan, nch, 4, 4, 16, 8)  # p, c, i, g, col, h
+    w = s.transpose(1, 3, 2, 5, 0, 4).reshape(K, npan * 16)           # (c, g, i, h) x (p, col)
+    return w[:, :N]
+
+
+@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_staged_arm(fmt, sym, dtype):
+    """The scratch holds the oracle's unpacked weights bit for bit, and the
+    staged Y equals the fused 128x128 rung's Y bit for bit (same MFMA inputs
+    in the same order), on shapes with ragged M and N."""
+    rung = [r for r in RUNGS if qg.rung_name(r) == "mfma32-128x128"][0]
+    for M, N, K in [(130, 160, 512), (37, 40, 256), (257, 272, 768)]:
+        c = _case(fmt, sym, M, N, K, dtype, seed=360)
+        print(f"staged {fmt} sym={sym} dtype={dtype} M={M} N={N} K={K}", flush=True)
+        x = to_device(c.X, dtype)
+        y, scratch = qg.staged(fmt, x, c.device_weights(), N, group=c.group if fmt == "w4a16" else 0,
+                               has_zp=c.has_zp)
+        assert scratch.numel() == qg.staged_scratch_bytes(N, K)
+        sb = scratch.cpu().numpy().view(np.uint16)
+        assert same_bits(_scratch_to_w(sb, N, K), c.W)
+        y_fused = from_device(c.run(rung))
+        assert np.array_equal(from_device(y), y_fused)
+
+
+def test_staged_arm_m_zero_fills_scratch():
+    import torch
+
+    c = _case("q6k", False, 1, 48, 512, qg.F16, seed=361)
+    x = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    y = torch.empty((0, 48), dtype=torch.float16, device="cuda")
+    _, scratch = qg.staged("q6k", x, c.device_weights(), 48, out=y)
+    assert same_bits(_scratch_to_w(scratch.cpu().numpy().view(np.uint16), 48, 512), c.W)
