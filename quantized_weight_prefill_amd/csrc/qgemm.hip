@@ -1018,13 +1018,14 @@ enum Rung {
     RUNG_M256_W8 = 11,   // 32x32x16 MFMA: 256x128, 8 waves of 32x128
     RUNG_M256 = 12,      // 32x32x16 MFMA: 256x128, 4 waves of 64x128
     RUNG_M128N160 = 13,  // 32x32x16 MFMA: 128x160, 4 waves of 32x160
-    RUNG_COUNT = 14
+    RUNG_WIDE = 14,      // direct, four panels and up to 48 rows per wave
+    RUNG_COUNT = 15
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "stream-128x128",
                                             "stream-256x128",    "stream-128x128-il", "stream-256x128-il",
                                             "stream-256x128-w8", "stream-128x128-x2", "stream-128x128-k2",
                                             "mfma32-128x128",    "mfma32-128x128-k2", "mfma32-256x128-w8",
-                                            "mfma32-256x128",    "mfma32-128x160"};
+                                            "mfma32-256x128",    "mfma32-128x160",    "direct-wide"};
 
 struct Plan {
     int rung;
@@ -1065,6 +1066,12 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.rb = 1;
         pl.pn = np >= 4 ? 4 : (int)np;
         pl.grid = dim3((unsigned)ceil_div(np, pl.pn), (unsigned)ceil_div(M, 16), 1);
+        break;
+    }
+    case RUNG_WIDE: {  // each weight run unpacked once for up to 48 rows, each activation fragment used by four panels
+        pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : 3;
+        pl.pn = 4;
+        pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)ceil_div(M, 16 * pl.rb), 1);
         break;
     }
     case RUNG_S128:
@@ -1109,9 +1116,11 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    direct kernel with all panels per wave (a 128-wide tile would leave most
 //    of the part idle and most of each tile padding);
 //  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
-//    and the kernel is a weight stream; with many panels or more than 32
-//    rows, four panels per wave, otherwise one panel per wave and all rows
-//    per wave;
+//    and the kernel is a weight stream; with many panels and 17..32 rows
+//    (17..48 for Q4_K), four panels and all rows per wave (each activation
+//    fragment feeds four panels); with many panels or more than 32 rows,
+//    four panels and 16 rows per wave; otherwise one panel per wave and all
+//    rows per wave;
 //  * fewer than 128 tiles of 128x128: the direct kernel keeps more CUs busy;
 //  * at least 512 tiles of 256x128: the 8-wave 256x128 tile on 16x16x32
 //    MFMAs, which unpacks each weight once for 256 rows;
@@ -1138,7 +1147,12 @@ int select_rung(int fmt, long long M, long long N, long long K)
     if (np <= 4) return RUNG_SKINNY_N;
     // above 32 rows a one-panel wave carries three or four row blocks of
     // activations per weight run; four panels per wave and a grid over M win
-    if (M <= 64) return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
+    if (M <= 64) {
+        // (three row blocks per wave only pay off for Q4_K: the other
+        // formats' larger raw runs spill at that size)
+        if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
+        return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
+    }
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     if (t128 < 128) return RUNG_SKINNY_N;
     // many 256-row tiles: eight waves at two per SIMD hide the most latency
@@ -1169,6 +1183,7 @@ hipError_t launch_direct(const Plan &pl, const Args &a, hipStream_t s)
         default: return launch_direct_rp<FMT, DT, 4, 1>(pl, a, s);
         }
     }
+    if (pl.rb > 1) return pl.rb == 2 ? launch_direct_rp<FMT, DT, 2, 4>(pl, a, s) : launch_direct_rp<FMT, DT, 3, 4>(pl, a, s);
     switch (pl.pn) {
     case 2: return launch_direct_rp<FMT, DT, 1, 2>(pl, a, s);
     case 3: return launch_direct_rp<FMT, DT, 1, 3>(pl, a, s);
