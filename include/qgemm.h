@@ -173,6 +173,26 @@ int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, vo
 int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
                   int dtype, void *stream);
 
+/* Grouped per-expert GEMM (the batched-prefill post, "What this did not
+ * solve": a batched per-expert matmul that amortizes each expert's weights
+ * over its routed tokens; the routing itself is not part of it).  X [T][K]
+ * holds the routed token rows grouped by expert: rows offsets[e] ..
+ * offsets[e+1]-1 use expert e, whose packed weights (the layout of the
+ * format's packer, N x K) start at Wpacked + e * (packed bytes of one
+ * expert); Y [T][N] receives their products in the same rows.  `offsets`
+ * (E+1 int32, 4-byte aligned) is DEVICE memory, read by the kernel, so the
+ * caller needs no host copy of the counts; it must be non-decreasing with
+ * offsets[0] = 0 and offsets[E] = T.  The kernel clamps every offset into
+ * [0, T] and to at least the previous one, so any contents stay inside X, Y
+ * and W (bad offsets only give wrong rows).  Rows outside [offsets[0],
+ * offsets[E]) are not written.  One launch on `stream`; results as
+ * qgemm_gemm_rung for each expert.  Errors as qgemm_w4a16 (group_size
+ * ignored for the k-quants), plus QGEMM_ERR_SHAPE for E < 1 or a grid
+ * beyond ceil(T/16) + E = 65535, QGEMM_ERR_ALIGN when one expert's packed
+ * size is not a multiple of 16 bytes; T = 0 is a no-op. */
+int qgemm_grouped(int format, const void *X, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E, int64_t T,
+                  int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+
 /* The staged arm (the dequant-scratch post's "two passes": unpack to a
  * 16-bit scratch, then a GEMM that reads it), kept beside the fused path to
  * measure what fusing saves on this GPU.  Step one unpacks every weight of

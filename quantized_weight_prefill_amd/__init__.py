@@ -75,6 +75,7 @@ SIGNATURES = {
     "qgemm_rung_info": (_INT, [_INT, _INT, _I64, _I64, _I64, _INT, _VP]),
     "qgemm_gemm_rung": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_grouped": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_staged_scratch_bytes": (_SZ, [_I64, _I64]),
     "qgemm_staged": (_INT, [_INT, _VP, _VP, _VP, _SZ, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_probe_mfma": (_INT, [_VP, _VP, _INT, _INT, _INT, _VP]),
@@ -287,6 +288,22 @@ def dequant(fmt, wp, N: int, K: int, dtype, group: int = 0, has_zp: bool = False
                              _stream(stream))
     _check("qgemm_dequant", st)
     return w
+
+
+def grouped(fmt, x, wp, N: int, offsets, E: int, group: int = 0, has_zp: bool = True, out=None, stream=None):
+    """Grouped per-expert GEMM: rows offsets[e]..offsets[e+1]-1 of x use
+    expert e's packed weights (experts concatenated in wp); offsets is an
+    int32 device tensor of E+1 entries."""
+    torch = _torch()
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    T, K = x.shape
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.numel() != E + 1:
+        raise ValueError("offsets must be an int32 device tensor of E+1 entries")
+    y = out if out is not None else torch.empty((T, N), dtype=x.dtype, device=x.device)
+    st = lib().qgemm_grouped(f, _dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), _dev(offsets, "offsets"), E, T, N, K,
+                             group, int(bool(has_zp)), _dtype_code(x), _stream(stream))
+    _check("qgemm_grouped", st)
+    return y
 
 
 def staged_scratch_bytes(N: int, K: int) -> int:

@@ -71,6 +71,9 @@ struct Args {
     int has_zp;  // W4A16 asymmetric
     int kw;      // direct kernel: waves splitting K inside a workgroup
     long long w4_sreg, w4_zreg;  // W4A16 byte offsets of the scale / zero regions
+    const int *offs;             // grouped: E+1 row offsets (device), rows offs[e]..offs[e+1] use expert e
+    int E;                       // grouped: number of experts
+    long long wstride;           // grouped: packed bytes of one expert's weights
 };
 
 // XCD-aware renumbering: workgroup b of n runs on XCD b % 8; give each XCD a
@@ -462,14 +465,14 @@ __device__ __forceinline__ void store_block32(const Args &a, const f32x16 &v, in
 // chunk c+1 are in flight while chunk c is unpacked and multiplied.  Grid:
 // x = panel groups of PN panels, y = row groups of 16*RB rows.
 // ---------------------------------------------------------------------------
+// One workgroup: rows m0 .. m0+16*RB-1 (those below a.M) of panels p0 ..
+// p0+PN-1; a.kw waves split K and reduce through LDS.
 template <int FMT, int DT, int RB, int PN>
-__global__ void __launch_bounds__(512) k_direct(Args a)
+__device__ __forceinline__ void direct_body(const Args &a, int p0, int m0)
 {
     extern __shared__ f32x4 red[];  // [kw][PN*RB][64]
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
-    const int p0 = blockIdx.x * PN;
-    const int m0 = blockIdx.y * (16 * RB);
     const int nch = a.K / kChunk;
     const int cb = (int)((long long)nch * w / a.kw), ce = (int)((long long)nch * (w + 1) / a.kw);
 
@@ -546,6 +549,38 @@ __global__ void __launch_bounds__(512) k_direct(Args a)
         const int pn = blk / RB, rb = blk % RB;
         store_block<DT>(a, s, m0 + 16 * rb, 16 * (p0 + pn), lane);
     }
+}
+
+template <int FMT, int DT, int RB, int PN>
+__global__ void __launch_bounds__(512) k_direct(Args a)
+{
+    direct_body<FMT, DT, RB, PN>(a, blockIdx.x * PN, blockIdx.y * (16 * RB));
+}
+
+// Grouped per-expert GEMM: rows offs[e] .. offs[e+1]-1 of X and Y use expert
+// e's weights (expert e's packed bytes start at W + e*wstride).  grid.y is an
+// upper bound on the row blocks of all experts (ceil(T/R) + E, T = a.M);
+// workgroup y walks the experts' block counts to find its own, and the ones
+// past the last block exit.  Offsets are clamped into [0, T] and made
+// non-decreasing, so no access leaves X, Y or W whatever they hold.
+template <int FMT, int DT, int RB, int PN>
+__global__ void __launch_bounds__(512) k_direct_grouped(Args a)
+{
+    constexpr int R = 16 * RB;
+    const int j = blockIdx.y;
+    int base = 0, lo = 0, hi = 0, e = 0;
+    for (; e < a.E; e++) {
+        lo = min(max(a.offs[e], hi), a.M);
+        hi = min(max(a.offs[e + 1], lo), a.M);
+        const int nb = (hi - lo + R - 1) / R;
+        if (j < base + nb) break;
+        base += nb;
+    }
+    if (e >= a.E) return;  // the whole workgroup leaves together, before any barrier
+    Args b = a;
+    b.W = a.W + (long long)e * a.wstride;
+    b.M = hi;
+    direct_body<FMT, DT, RB, PN>(b, blockIdx.x * PN, lo + (j - base) * R);
 }
 
 // ---------------------------------------------------------------------------
@@ -1315,6 +1350,70 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     return launch_status(launch(fmt, dtype, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
 }
 
+long long packed_bytes(int fmt, long long N, long long K, long long group, int has_zp)
+{
+    if (fmt == FMT_Q4K) return (long long)qgemm_q4k_packed_bytes(N, K);
+    if (fmt == FMT_Q6K) return (long long)qgemm_q6k_packed_bytes(N, K);
+    return (long long)qgemm_w4a16_packed_bytes(N, K, group, has_zp);
+}
+
+template <int FMT, int DT>
+hipError_t launch_grouped_fd(const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (pl.rb == 1) hipLaunchKernelGGL((k_direct_grouped<FMT, DT, 1, 4>), pl.grid, dim3(64 * pl.kw), pl.lds, s, a);
+    else if (pl.rb == 2) hipLaunchKernelGGL((k_direct_grouped<FMT, DT, 2, 4>), pl.grid, dim3(64 * pl.kw), pl.lds, s, a);
+    else hipLaunchKernelGGL((k_direct_grouped<FMT, DT, 3, 4>), pl.grid, dim3(64 * pl.kw), pl.lds, s, a);
+    return hipGetLastError();
+}
+
+// Grouped plan: four panels per wave, row blocks sized by the mean rows per
+// expert (three 16-row blocks only for Q4_K, whose runs fit that variant),
+// grid.y an upper bound on every expert's row blocks, K split as the direct
+// rungs do.
+Plan grouped_plan(int fmt, long long T, long long E, long long N, long long K)
+{
+    Plan pl{};
+    const long long np = (N + 15) / 16, avg = (T + E - 1) / E;
+    pl.rung = -1;
+    pl.pn = 4;
+    pl.rb = avg <= 16 ? 1 : (avg <= 32 || fmt != FMT_Q4K) ? 2 : 3;
+    pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)(ceil_div(T, 16 * pl.rb) + E), 1);
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, (int)(K / kChunk));
+    pl.waves = pl.kw;
+    pl.rows = 16 * pl.rb;
+    pl.cols = 64;
+    pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
+    return pl;
+}
+
+int grouped(int fmt, const void *X, const void *W, void *Y, const int32_t *offs, long long E, long long T, long long N,
+            long long K, long long group, int has_zp, int dtype, void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, T, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (E < 1 || E > INT32_MAX / 2) return QGEMM_ERR_SHAPE;
+    if (T == 0) return QGEMM_OK;
+    if (!X || !W || !Y || !offs) return QGEMM_ERR_NULL;
+    const long long wstride = packed_bytes(fmt, N, K, group, has_zp);
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || ((uintptr_t)offs & 3u) != 0 || wstride % 16 != 0)
+        return QGEMM_ERR_ALIGN;
+    if ((long long)ceil_div(T, 16) + E > 65535) return QGEMM_ERR_SHAPE;  // grid.y limit
+    Args a = make_args(fmt, X, W, Y, T, N, K, group, has_zp);
+    a.offs = offs;
+    a.E = (int)E;
+    a.wstride = wstride;
+    const Plan pl = grouped_plan(fmt, T, E, N, K);
+    a.kw = pl.kw;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (fmt == FMT_Q4K) e = dtype == DT_F16 ? launch_grouped_fd<FMT_Q4K, DT_F16>(pl, a, s) : launch_grouped_fd<FMT_Q4K, DT_BF16>(pl, a, s);
+    else if (fmt == FMT_Q6K) e = dtype == DT_F16 ? launch_grouped_fd<FMT_Q6K, DT_F16>(pl, a, s) : launch_grouped_fd<FMT_Q6K, DT_BF16>(pl, a, s);
+    else e = dtype == DT_F16 ? launch_grouped_fd<FMT_W4, DT_F16>(pl, a, s) : launch_grouped_fd<FMT_W4, DT_BF16>(pl, a, s);
+    return launch_status(e, "grouped");
+}
+
 size_t staged_scratch_bytes(long long N, long long K)
 {
     if (N < 1 || K < 1 || K % kChunk != 0) return 0;
@@ -1462,6 +1561,12 @@ int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, 
 {
     return staged(format, X, Wpacked, scratch, scratch_bytes, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype,
                   stream);
+}
+
+int qgemm_grouped(int format, const void *X, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E, int64_t T,
+                  int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream)
+{
+    return grouped(format, X, Wpacked, Y, offsets, E, T, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream);
 }
 
 }  // extern "C"

@@ -183,6 +183,13 @@ def test_device_entry_argument_errors():
     assert lib.qgemm_q4k(None, None, None, 0, 16, 256, 0, s) == 0
     assert lib.qgemm_dequant(0, None, A, 16, 256, 0, 0, 0, s) == -1
     assert lib.qgemm_dequant(2, A, A, 16, 256, 0, 0, 0, s) == -5
+    # grouped per-expert GEMM
+    assert lib.qgemm_grouped(0, A, A, A, A, 0, 8, 16, 256, 0, 0, 0, s) == -2       # E < 1
+    assert lib.qgemm_grouped(0, A, A, A, None, 2, 8, 16, 256, 0, 0, 0, s) == -1    # offsets NULL
+    assert lib.qgemm_grouped(0, A, A, A, ctypes.c_void_p((1 << 20) + 2), 2, 8, 16, 256, 0, 0, 0, s) == -4
+    assert lib.qgemm_grouped(2, A, A, A, A, 2, 8, 16, 128, 128, 1, 0, s) == -4     # 1064-byte experts
+    assert lib.qgemm_grouped(0, None, None, None, None, 3, 0, 16, 256, 0, 0, 0, s) == 0  # T = 0
+    assert lib.qgemm_grouped(1, A, A, A, A, 2, 8, 16, 300, 0, 0, 0, s) == -2
     # staged arm: scratch checks come before any launch
     need = lib.qgemm_staged_scratch_bytes(20, 512)
     assert need == 32 * 512 * 2 and lib.qgemm_staged_scratch_bytes(20, 200) == 0

@@ -248,3 +248,47 @@ def test_staged_arm_m_zero_fills_scratch():
     y = torch.empty((0, 48), dtype=torch.float16, device="cuda")
     _, scratch = qg.staged("q6k", x, c.device_weights(), 48, out=y)
     assert same_bits(_scratch_to_w(scratch.cpu().numpy().view(np.uint16), 48, 512), c.W)
+
+
+# ----------------------------------------------------------------------------
+# grouped per-expert GEMM
+# ----------------------------------------------------------------------------
+
+def _grouped_case(fmt, sym, counts, N, K, dtype, seed):
+    """Per-expert inputs: X rows grouped by expert, each expert's own weights."""
+    import torch
+
+    cases = [Case(fmt, max(m, 1), N, K, dtype, seed + e, symmetric=sym) for e, m in enumerate(counts)]
+    X = np.concatenate([c.X[:m] for c, m in zip(cases, counts)], axis=0)
+    W_all = np.concatenate([c.packed for c in cases])
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return cases, X, torch.from_numpy(W_all).cuda(), torch.from_numpy(offs).cuda(), offs
+
+
+@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_grouped_parity(fmt, sym, dtype):
+    """Each expert's rows match the oracle on that expert's weights, with empty
+    experts, one-row experts and ragged counts; mean rows per expert of 10, 27
+    and 44 select one, two and (Q4_K) three 16-row blocks per wave."""
+    import torch
+
+    N, K = 96, 512
+    for counts in ([0, 1, 17, 40, 100, 3], [5, 0, 12, 3, 30, 10], [44, 60, 28]):
+        cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=400)
+        T = int(offs[-1])
+        print(f"grouped {fmt} sym={sym} dtype={dtype} counts={counts}", flush=True)
+        pad = 4096
+        tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
+        buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
+        out = buf[pad:pad + T * N].view(T, N)
+        qg.grouped(fmt, to_device(X, dtype), W, N, offs_d, len(counts), group=128 if fmt == "w4a16" else 0,
+                   has_zp=not sym, out=out)
+        host = buf.cpu()
+        assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
+        Y = from_device(out)
+        for e, (c, m) in enumerate(zip(cases, counts)):
+            if m == 0:
+                continue
+            Yref, B = oracle.gemm(c.X[:m], c.W, dtype)
+            assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"grouped expert {e} rows {m}")
