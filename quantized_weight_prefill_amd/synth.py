@@ -245,3 +245,45 @@ def workload_inputs(name: str, j: int):
     X = activations(rs[2 * j], M, K, dt)
     fields = weight_fields(fmt, rs[2 * j + 1], N, K, group or 128, sym)
     return X, fields, encode(fmt, fields)
+
+
+# ---------------------------------------------------------------------------
+# Grouped (per-expert) workloads: the routed rows of a mixture-of-experts FFN,
+# already grouped by expert.  Routing is not part of the GEMM; its outcome is
+# drawn here: each token picks top_k distinct experts with probabilities from
+# a seeded Zipf-like popularity, so expert row counts are skewed and some may
+# be empty.
+# ---------------------------------------------------------------------------
+
+MOE_WORKLOADS = {
+    "moe_e128_top8_m658": {  # 128 experts, 8 per token, hidden 2048, expert width 768, 658 prompt tokens
+        "index": 6, "tokens": 658, "experts": 128, "top_k": 8, "zipf": 0.8,
+        "gemms": [("gate", "q4k", 2048, 768), ("up", "q4k", 2048, 768), ("down", "q6k", 768, 2048)],
+    },
+}
+
+
+def moe_counts(name: str) -> np.ndarray:
+    """Rows routed to each expert (int64 [E])."""
+    w = MOE_WORKLOADS[name]
+    rng = streams(1000 + w["index"], 1)[0]
+    E, k = w["experts"], w["top_k"]
+    pop = 1.0 / np.arange(1, E + 1) ** w["zipf"]
+    pop = pop[rng.permutation(E)]
+    pop /= pop.sum()
+    counts = np.zeros(E, np.int64)
+    for _ in range(w["tokens"]):
+        counts[rng.choice(E, size=k, replace=False, p=pop)] += 1
+    return counts
+
+
+def moe_inputs(name: str, j: int, dtype: int = F16):
+    """(X bits [T][K], weight fields of all experts as one N*E-column matrix,
+    encoded blocks) of GEMM j; expert e owns columns e*N .. (e+1)*N-1."""
+    w = MOE_WORKLOADS[name]
+    label, fmt, K, N = w["gemms"][j]
+    T = int(moe_counts(name).sum())
+    rs = streams(2000 + w["index"], 2 * len(w["gemms"]))
+    X = activations(rs[2 * j], T, K, dtype)
+    fields = weight_fields(fmt, rs[2 * j + 1], N * w["experts"], K)
+    return X, fields, encode(fmt, fields)

@@ -43,3 +43,37 @@ def test_workload_sampled(name, j):
     rel = np.abs(got - Yref) / B
     print(f"  max rel err {rel.max():.3e}", flush=True)
     assert rel.max() <= GEMM_TOL
+
+
+MOE_CASES = [("moe_e128_top8_m658", 0), ("moe_e128_top8_m658", 2)]  # gate (Q4_K), down (Q6_K)
+
+
+@pytest.mark.parametrize("name,j", MOE_CASES, ids=[f"{n}-{synth.MOE_WORKLOADS[n]['gemms'][j][0]}" for n, j in MOE_CASES])
+def test_moe_grouped_sampled(name, j):
+    """The grouped per-expert GEMM at the MoE workload's full size, as the
+    benchmark launches it, on a seeded sample of outputs (first and last rows
+    included): each sampled row is checked against its own expert's weights."""
+    import torch
+
+    w = synth.MOE_WORKLOADS[name]
+    label, fmt, K, N = w["gemms"][j]
+    E = w["experts"]
+    counts = synth.moe_counts(name)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(offs[-1])
+    print(f"moe {name}/{label} fmt={fmt} T={T} K={K} N={N} E={E}", flush=True)
+    X, fields, enc = synth.moe_inputs(name, j)
+    packed = np.concatenate([qg.pack(fmt, enc[e * N:(e + 1) * N], N, K) for e in range(E)])
+    y = qg.grouped(fmt, to_device(X, qg.F16), bytes_to_device(packed), N, torch.from_numpy(offs).cuda(), E)
+    Y = from_device(y)
+    W = oracle.dequant(fmt, enc, E * N, K, qg.F16)
+    rng = np.random.default_rng(4343 + j)
+    count = 2000
+    rows = np.concatenate([rng.integers(0, T, count), [0, T - 1]])
+    cols = np.concatenate([rng.integers(0, N, count), [N - 1, 0]])
+    expert = np.searchsorted(offs, rows, side="right") - 1
+    Yref, B = oracle.gemm_at(X, W, qg.F16, rows, expert * N + cols)
+    got = oracle.bits_to_double_fast(Y[rows, cols], qg.F16)
+    rel = np.abs(got - Yref) / B
+    print(f"  max rel err {rel.max():.3e}", flush=True)
+    assert rel.max() <= GEMM_TOL
