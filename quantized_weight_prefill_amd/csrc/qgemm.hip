@@ -1156,7 +1156,8 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    fragment feeds four panels); with many panels or more than 32 rows,
 //    four panels and 16 rows per wave; otherwise one panel per wave and all
 //    rows per wave;
-//  * fewer than 128 tiles of 128x128: the direct kernel keeps more CUs busy;
+//  * fewer than 128 tiles of 128x128: the direct kernel with four panels and
+//    up to three row blocks per wave keeps more CUs busy;
 //  * at least 512 tiles of 256x128: the 8-wave 256x128 tile on 16x16x32
 //    MFMAs, which unpacks each weight once for 256 rows;
 //  * at most 256 tiles of 128x128 over K >= 8192: the 128x128 tile on
@@ -1189,7 +1190,7 @@ int select_rung(int fmt, long long M, long long N, long long K)
         return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
     }
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
-    if (t128 < 128) return RUNG_SKINNY_N;
+    if (t128 < 128) return RUNG_WIDE;
     // many 256-row tiles: eight waves at two per SIMD hide the most latency
     if (t256 >= 512) return RUNG_S256_W8;
     // few tiles over a long K: split K inside the workgroup
