@@ -355,15 +355,6 @@ __device__ __forceinline__ void unpack_run(const RunRaw<FMT> &u, const RunSrc<FM
     for (int i = 0; i < 4; i++) out[i] = unpack_word_any<FMT, DT>(u, pr, i);
 }
 
-// VALU instructions to place after each MFMA of one step: the unpack of UPT
-// words spread evenly over the step's NMF MFMAs (rounded up).
-template <int FMT, int DT, int UPT, int NMF>
-constexpr int kValuPerMfma()
-{
-    constexpr int per_word = (FMT == FMT_Q6K ? 26 : 13) + (DT == DT_BF16 ? 4 : 0) + 2;
-    return (UPT * per_word + NMF - 1) / NMF;
-}
-
 template <int DT>
 __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c);
 
@@ -606,8 +597,8 @@ __global__ void __launch_bounds__(512) k_direct_grouped(Args a)
 // grouped tile order (below): its L2 then serves both the shared weight
 // panels and the shared activation rows.
 // ---------------------------------------------------------------------------
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, bool SCHED, int XD, int KS>
-__global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN>
+__global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 {
     constexpr int NTG = 64 * NWM * NWN;    // threads of one K group
     constexpr int PB = WPB * NWN;          // panels per tile
@@ -615,21 +606,15 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
     constexpr int RBW = WM / 16;           // row blocks per wave
     constexpr int UPT = PB * 64 / NTG;     // weight runs per thread per chunk
     static_assert(PB * 64 % NTG == 0 && UPT >= 1, "tile and workgroup do not divide");
-    static_assert(KS == 1 || WPB * RBW * NWM * NWN * 64 <= 2 * PB * 4 * 64, "K-split reduction must fit in LDS");
-    __shared__ u32x4 sWall[KS][2][PB][4][64];
+    __shared__ u32x4 sW[2][PB][4][64];
 
-    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
-    const int kg = wall / (NWM * NWN);                    // K group
-    const int w = wall % (NWM * NWN), tid = threadIdx.x % NTG;
-    auto &sW = sWall[kg];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
     const int wm = w % NWM, wn = w / NWM;
     const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
     int mt, nt;
     tile_coords(xcd_order(blockIdx.x, gridDim.x), tm, tn, mt, nt);
     const int m0 = mt * BM + wm * WM, p0 = nt * PB;
-    // K group kg owns chunks [c_lo, c_hi); every group runs the same number
-    // of chunks (the host only splits K when the chunk count divides).
-    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
+    const int c_lo = 0, c_hi = a.K / kChunk;
     const int r16 = lane & 15, g4 = lane >> 4;
 
     const uint16_t *xrow[RBW];
@@ -656,21 +641,15 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
         src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, u & 15);
     }
 
-    // XD register sets of activation fragments: set c % XD holds chunk c, and
-    // is refilled with chunk c + XD as soon as each fragment is consumed.
-    u32x4 xs[XD][RBW][4];
-    // prologue: chunk 0 unpacked into LDS buffer 0, chunk 1 raw in registers,
-    // chunks 0 .. XD-1 activations in registers
+    // prologue: chunk 0 unpacked into LDS buffer 0, chunk 1 raw in
+    // registers, chunk 0 activations in registers
+    u32x4 xf[RBW][4];
 #pragma unroll
     for (int s = 0; s < UPT; s++) src[s].load(c_lo, raw[s]);
 #pragma unroll
-    for (int d = 0; d < XD; d++) {
-        const int cd = c_lo + d < c_hi ? c_lo + d : c_hi - 1;
+    for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
-        for (int rb = 0; rb < RBW; rb++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) xs[d][rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cd + 32 * i);
-    }
+        for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * c_lo + 32 * i);
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
         u32x4 f[4];
@@ -686,15 +665,14 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
 
     // Steady state, branch-free: chunk c is multiplied from LDS buffer c&1
     // while chunk c+1 (raw bytes already in registers) is unpacked word by
-    // word into buffer (c+1)&1, the activations of chunk c+XD replace those
+    // word into buffer (c+1)&1, the activations of chunk c+1 replace those
     // of chunk c step by step, and the raw bytes of chunk c+2 are requested.
     // Past the last chunk the indices are clamped: the extra work is
     // harmless (the buffer written is never read again).
-    auto body = [&](int c, u32x4 (&xf)[RBW][4]) {
+    for (int c = c_lo; c < c_hi; c++) {
         const int buf = (c - c_lo) & 1;
         const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
         const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
-        const int cx = c + XD < c_hi ? c + XD : c_hi - 1;
         RunParams pr[UPT];
 #pragma unroll
         for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(raw[s], src[s], cn);
@@ -711,7 +689,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
                 for (int pb = 0; pb < WPB; pb++) acc[pb][rb] = mma<DT>(wcur[pb], xf[rb][i], acc[pb][rb]);
-                xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cx + 32 * i);
+                xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cn + 32 * i);
             }
 #pragma unroll
             for (int s = 0; s < UPT; s++) {
@@ -721,17 +699,6 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
             if (i < 3) {
 #pragma unroll
                 for (int pb = 0; pb < WPB; pb++) wcur[pb] = wnxt[pb];
-            }
-            // Interleaved variant: each MFMA is followed by a few VALU (unpack)
-            // instructions and one LDS or global access, so the matrix pipe
-            // and the VALU of one wave run side by side.
-#pragma unroll
-            for (int k = 0; k < (SCHED ? WPB * RBW : 0); k++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma<FMT, DT, UPT, WPB * RBW>(), 0);
-                if (k < WPB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-                if (k >= WPB && k < WPB + UPT) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-                if (k >= WPB + UPT && k < WPB + UPT + RBW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
             }
         }
         if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
@@ -751,31 +718,6 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
 #pragma unroll
         for (int s = 0; s < UPT; s++) src[s].load(cnn, raw[s]);
         __syncthreads();
-    };
-    if constexpr (XD == 1) {
-        for (int c = c_lo; c < c_hi; c++) body(c, xs[0]);
-    } else {
-        for (int c = c_lo; c < c_hi; c += 2) {
-            body(c, xs[0]);
-            if (c + 1 < c_hi) body(c + 1, xs[1]);
-        }
-    }
-    if constexpr (KS == 2) {
-        // K group 1 hands its partial sums to group 0 through its own LDS
-        // buffers (free after the last barrier of the loop)
-        f32x4 *red = reinterpret_cast<f32x4 *>(&sWall[1][0][0][0][0]);
-        if (kg == 1) {
-#pragma unroll
-            for (int pb = 0; pb < WPB; pb++)
-#pragma unroll
-                for (int rb = 0; rb < RBW; rb++) red[((w * WPB + pb) * RBW + rb) * 64 + lane] = acc[pb][rb];
-        }
-        __syncthreads();
-        if (kg == 1) return;
-#pragma unroll
-        for (int pb = 0; pb < WPB; pb++)
-#pragma unroll
-            for (int rb = 0; rb < RBW; rb++) acc[pb][rb] += red[((w * WPB + pb) * RBW + rb) * 64 + lane];
     }
 #pragma unroll
     for (int pb = 0; pb < WPB; pb++)
@@ -785,7 +727,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) k_stream(Args a)
 }
 
 // ---------------------------------------------------------------------------
-// Streaming tile kernel on 32x32x16 MFMAs (the fast form on gfx950).
+// Streaming tile kernel on 32x32x16 MFMAs.
 //
 // Same structure as k_stream: NWM x NWN waves (times KS K groups) own a
 // (NWM*WM) x (16*WPB*NWN) tile; each weight is unpacked once per workgroup
@@ -927,7 +869,7 @@ struct Stream32 {
 };
 
 template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
-__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(WM == 32 ? 2 : 1)))
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_stream32(Args a)
 {
     using S = Stream32<FMT, DT, WM, WPB, NWM, NWN>;
@@ -1039,28 +981,18 @@ __global__ void __launch_bounds__(256) k_stage(Args a, uint8_t *Ws)
 // ---------------------------------------------------------------------------
 
 enum Rung {
-    RUNG_SMALL_M = 0,    // direct, one panel per wave, up to 64 rows per wave
-    RUNG_SKINNY_N = 1,   // direct, up to four panels per wave, 16 rows per wave
-    RUNG_S128 = 2,       // stream 128x128, 4 waves of 32x128
-    RUNG_S256 = 3,       // stream 256x128, 4 waves of 64x128
-    RUNG_S128_IL = 4,    // as RUNG_S128, MFMA and unpack interleaved
-    RUNG_S256_IL = 5,    // as RUNG_S256, MFMA and unpack interleaved
-    RUNG_S256_W8 = 6,    // stream 256x128, 8 waves of 32x128
-    RUNG_S128_X2 = 7,    // as RUNG_S128, activations prefetched two chunks ahead
-    RUNG_S128_K2 = 8,    // as RUNG_S128, K split between two 4-wave groups of one workgroup
-    RUNG_M128 = 9,       // 32x32x16 MFMA: 128x128, 4 waves of 32x128
-    RUNG_M128_K2 = 10,   // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
-    RUNG_M256_W8 = 11,   // 32x32x16 MFMA: 256x128, 8 waves of 32x128
-    RUNG_M256 = 12,      // 32x32x16 MFMA: 256x128, 4 waves of 64x128
-    RUNG_M128N160 = 13,  // 32x32x16 MFMA: 128x160, 4 waves of 32x160
-    RUNG_WIDE = 14,      // direct, four panels and up to 48 rows per wave
-    RUNG_COUNT = 15
+    RUNG_SMALL_M = 0,     // direct, one panel per wave, up to 64 rows per wave
+    RUNG_SKINNY_N = 1,    // direct, up to four panels per wave, 16 rows per wave
+    RUNG_WIDE = 2,        // direct, four panels and up to 48 rows per wave
+    RUNG_M16_256 = 3,     // 16x16x32 MFMA: 256x128, 8 waves of 32x128
+    RUNG_M128 = 4,        // 32x32x16 MFMA: 128x128, 4 waves of 32x128
+    RUNG_M128_K2 = 5,     // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
+    RUNG_M128N160 = 6,    // 32x32x16 MFMA: 128x160, 4 waves of 32x160
+    RUNG_COUNT = 7
 };
-const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "stream-128x128",
-                                            "stream-256x128",    "stream-128x128-il", "stream-256x128-il",
-                                            "stream-256x128-w8", "stream-128x128-x2", "stream-128x128-k2",
-                                            "mfma32-128x128",    "mfma32-128x128-k2", "mfma32-256x128-w8",
-                                            "mfma32-256x128",    "mfma32-128x160",    "direct-wide"};
+const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
+                                            "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
+                                            "mfma32-128x160"};
 
 struct Plan {
     int rung;
@@ -1109,23 +1041,14 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)ceil_div(M, 16 * pl.rb), 1);
         break;
     }
-    case RUNG_S128:
-    case RUNG_S256:
-    case RUNG_S128_IL:
-    case RUNG_S256_IL:
-    case RUNG_S256_W8:
-    case RUNG_S128_X2:
-    case RUNG_S128_K2:
+    case RUNG_M16_256:
     case RUNG_M128:
     case RUNG_M128_K2:
-    case RUNG_M256_W8:
-    case RUNG_M256:
     case RUNG_M128N160: {
-        pl.rows = (rung == RUNG_S256 || rung == RUNG_S256_IL || rung == RUNG_S256_W8 || rung == RUNG_M256_W8 ||
-                   rung == RUNG_M256) ? 256 : 128;
+        pl.rows = rung == RUNG_M16_256 ? 256 : 128;
         pl.cols = rung == RUNG_M128N160 ? 160 : 128;
-        pl.kw = ((rung == RUNG_S128_K2 || rung == RUNG_M128_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
-        pl.waves = (rung == RUNG_S256_W8 || rung == RUNG_M256_W8) ? 8 : 4 * pl.kw;
+        pl.kw = (rung == RUNG_M128_K2 && (K / kChunk) % 2 == 0) ? 2 : 1;
+        pl.waves = rung == RUNG_M16_256 ? 8 : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         pl.tiles_n = ceil_div(np, pl.cols / 16);
         pl.tiles_m = ceil_div(M, pl.rows);
@@ -1192,7 +1115,7 @@ int select_rung(int fmt, long long M, long long N, long long K)
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     if (t128 < 128) return RUNG_WIDE;
     // many 256-row tiles: eight waves at two per SIMD hide the most latency
-    if (t256 >= 512) return RUNG_S256_W8;
+    if (t256 >= 512) return RUNG_M16_256;
     // few tiles over a long K: split K inside the workgroup
     if (t128 <= 256 && K >= 8192) return RUNG_M128_K2;
     // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
@@ -1231,23 +1154,8 @@ template <int FMT, int DT>
 hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
     switch (pl.rung) {
-    case RUNG_S128:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 1, 1>), pl.grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    case RUNG_S256:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, false, 1, 1>), pl.grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    case RUNG_S128_IL:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, true, 1, 1>), pl.grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    case RUNG_S256_IL:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 64, 8, 4, 1, true, 1, 1>), pl.grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    case RUNG_S256_W8:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 8, 1, false, 1, 1>), pl.grid, dim3(512), 0, s, a);
-        return hipGetLastError();
-    case RUNG_S128_X2:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 2, 1>), pl.grid, dim3(256), 0, s, a);
+    case RUNG_M16_256:
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 8, 1>), pl.grid, dim3(512), 0, s, a);
         return hipGetLastError();
     case RUNG_M128:
         hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
@@ -1255,23 +1163,11 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
     case RUNG_M128_K2:
         if ((a.K / kChunk) % 2 == 0)
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 2>), pl.grid, dim3(512), 0, s, a);
-        else
+        else  // an odd chunk count is not split
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    case RUNG_M256_W8:
-        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
-        return hipGetLastError();
-    case RUNG_M256:
-        hipLaunchKernelGGL((k_stream32<FMT, DT, 64, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_M128N160:
         hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 10, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    case RUNG_S128_K2:
-        if ((a.K / kChunk) % 2 == 0)
-            hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 1, 2>), pl.grid, dim3(512), 0, s, a);
-        else  // an odd chunk count is not split
-            hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 4, 1, false, 1, 1>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     default:
         break;
