@@ -165,11 +165,12 @@ int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int d
 int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N,
                     int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
 
-/* ---- staged dequant (the two-pass form of the dequant-scratch post) -------
+/* ---- logical dequant --------------------------------------------------------
  * Writes the unpacked weights as logical Wout[K][N] (row-major, dtype
- * elements) with the same device unpack code the GEMMs use.  The fused
- * GEMMs never call it; it exists to check the unpack bit for bit and to
- * measure the staged traffic the fused form avoids. */
+ * elements, device, caller-owned) with the same device unpack code the
+ * GEMMs use.  The fused GEMMs never call it; it exists to check the unpack
+ * bit for bit in the plain W[K][N] order (the staged arm, qgemm_staged
+ * below, writes its scratch in the streaming kernel's order instead). */
 int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
                   int dtype, void *stream);
 

@@ -26,12 +26,22 @@
 // by at most 3.  Other Q4_K bf16 runs take an exact two-sum path.
 //
 // MFMA operands are used "transposed": the weight fragment is the A operand
-// and the activation fragment the B operand, so the 16x16 accumulator of one
-// v_mfma_f32_16x16x32 holds Y^T and each lane ends with four consecutive
-// output columns of one row (one 8-byte store).  The K order inside one MFMA
-// is a free permutation as long as both operands agree: lane (r, g) of
-// MFMA i carries k = 128*chunk + 32*g + 8*i + 0..7 in both operands, so the
-// lane that owns the 32 codes of sub-block g feeds all four MFMAs of a chunk.
+// and the activation fragment the B operand, so the accumulator holds Y^T and
+// each lane ends with four consecutive output columns of one row (one 8-byte
+// store).  The K order inside one MFMA is a free permutation as long as both
+// operands agree; each kernel picks the one that lets a lane's 32-code run
+// fill whole fragments:
+//   * v_mfma_f32_16x16x32 (direct kernels, the 256-row streaming tile): lane
+//     (r, g) of MFMA i carries k = 128*chunk + 32*g + 8*i + 0..7 (direct) or
+//     128*chunk + 32*i + 8*g + 0..7 (streaming);
+//   * v_mfma_f32_32x32x16 (the 128-row streaming tiles): lane (r, h) of
+//     k-step s carries k = 128*chunk + 16*s + 8*h + 0..7.
+//
+// Kernels: k_direct / k_direct_grouped (small M: each wave unpacks its own
+// runs, waves split K), k_stream (16x16x32, 256x128 tiles) and k_stream32
+// (32x32x16, 128x128 and 128x160 tiles) for larger M (each weight unpacked
+// once per workgroup into double-buffered LDS), k_stage (the staged arm's
+// unpack pass) and k_dequant (logical W[K][N]).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -918,7 +928,7 @@ k_stream32(Args a)
 }
 
 // ---------------------------------------------------------------------------
-// Staged dequant: the same unpack, written out as logical W[K][N].
+// Logical dequant: the same unpack, written out as W[K][N] (row-major).
 // One thread per (panel, chunk, run, column).
 // ---------------------------------------------------------------------------
 template <int FMT, int DT>
