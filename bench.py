@@ -3,6 +3,10 @@
 Default workload: one Qwen3-8B-shaped dense layer's seven linears at M = 658
 prompt tokens, fp16 activations (q/k/v/o/gate/up in Q4_K, down in Q6_K).  A
 step is one pass over the seven GEMMs with inputs already resident in HBM.
+By default the GEMMs read fragment-major activations: the step makes that
+copy of each distinct input once (qgemm_x_to_xf: q/k/v share one input,
+gate/up another, o and down one each) and the copies are timed inside the
+step; --x-layout row runs the same GEMMs on the row-major inputs instead.
 
 Prints ONE JSON line: whole-step throughput in TFLOP/s (2*M*N*K summed over
 the seven linears / step time), the linear-only prefill rate, per-kernel
@@ -17,6 +21,7 @@ Profiling helpers (same JSON line, restricted work):
                         their packed weights totalling >= MB (default 640), so the
                         256 MB Infinity Cache cannot serve them
     --rung R            force rung R instead of the M-ladder's choice
+    --x-layout xf|row   activation layout the GEMMs read (default xf)
     --copy-calibration BYTES
                         run a plain device-to-device copy of BYTES bytes three
                         times and exit (reference for HBM byte counters)
@@ -27,6 +32,8 @@ Profiling helpers (same JSON line, restricted work):
 from __future__ import annotations
 
 import argparse
+import ctypes
+import functools
 import hashlib
 import json
 import os
@@ -45,6 +52,7 @@ METRIC = "fused Q4_K GEMM TFLOP/s + prefill tok/s (Qwen3-8B shapes, M=658); % ro
 PEAK_TFLOPS = {qg.F16: 2500.0, qg.BF16: 2500.0}  # dense MFMA, fp16 / bf16
 PEAK_HBM_GBPS = 8000.0
 BYTES_PER_WEIGHT = {"q4k": 144 / 256, "q6k": 210 / 256}
+PROFILE_STEPS = 10  # steps of the per-launch profiling pass
 
 
 def weight_bytes(fmt: str, N: int, K: int, group: int, sym: bool) -> float:
@@ -86,6 +94,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", default=None, help="run only the GEMM with this label")
     ap.add_argument("--rung", type=int, default=-1, help="force a rung (-1: M-ladder)")
+    ap.add_argument("--x-layout", choices=["xf", "row"], default="xf",
+                    help="xf: fragment-major copies made inside the step (default); row: row-major X")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-arm comparison")
@@ -107,6 +117,14 @@ def main() -> int:
         return run_grouped(args)
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
+    lib = qg.lib()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    xf_layout = args.x_layout == "xf"
+    inputs = {}  # GEMM index whose activations are read -> its device copies
     gemms = []
     for j, (label, fmt, M, K, N, dt, group, sym) in enumerate(wl["gemms"]):
         if args.only is not None and label != args.only:
@@ -114,10 +132,23 @@ def main() -> int:
         X, fields, enc = synth.workload_inputs(args.workload, j)
         packed = qg.pack(fmt, enc, N, K)
         tdt = torch.float16 if dt == qg.F16 else torch.bfloat16
-        x = torch.from_numpy(X.view(np.int16)).view(tdt).to(dev)
+        src = synth.x_source(args.workload, j)
+        prep = None
+        if src not in inputs:
+            x = torch.from_numpy(X.view(np.int16)).view(tdt).to(dev)
+            xf = torch.empty((qg.xf_bytes(M, K) // 2,), dtype=tdt, device=dev) if xf_layout else None
+            inputs[src] = (x, xf)
+            if xf_layout:  # the first GEMM reading this input makes its fragment-major copy
+                prep = dict(label=f"x_to_xf({wl['gemms'][src][0]})", M=M, K=K,
+                            call=functools.partial(lib.qgemm_x_to_xf, ptr(x), ptr(xf), M, K, sp),
+                            bytes=2.0 * M * K + qg.xf_bytes(M, K))
+        x, xf = inputs[src]
         wp = torch.from_numpy(packed).to(dev)
         y = torch.empty((M, N), dtype=tdt, device=dev)
-        info = qg.select_rung(fmt, M, N, K, dt) if args.rung < 0 else qg.rung_info(args.rung, fmt, M, N, K, dt)
+        if args.rung >= 0:
+            info = qg.rung_info(args.rung, fmt, M, N, K, dt)
+        else:
+            info = (qg.select_rung_xf if xf_layout else qg.select_rung)(fmt, M, N, K, dt)
         wbytes = weight_bytes(fmt, N, K, group or 128, sym)
         # below the ridge the kernel is a weight stream: time it on weights that come from HBM
         intensity = 2.0 * M * N * K / (wbytes + 2 * M * K + 2 * M * N)
@@ -125,50 +156,98 @@ def main() -> int:
         if args.pool_mb > 0 and intensity < PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBPS * 1e9):
             ncopy = max(1, int(np.ceil(args.pool_mb * 1e6 / packed.nbytes)))
         pool = [wp] + [wp.clone() for _ in range(ncopy - 1)]
+        # pre-marshalled C calls (one per weight copy): the GEMM entry point
+        # for the layout, rung -1 being the layout's M-ladder
+        grp, zp = (group if fmt == "w4a16" else 0), int(not sym)
+        if xf_layout:
+            calls = [functools.partial(lib.qgemm_gemm_xf, qg.FORMATS[fmt], args.rung, ptr(xf), ptr(w), ptr(y), M, N, K,
+                                       grp, zp, dt, sp) for w in pool]
+        else:
+            calls = [functools.partial(lib.qgemm_gemm_rung, qg.FORMATS[fmt], args.rung, ptr(x), ptr(w), ptr(y), M, N,
+                                       K, grp, zp, dt, sp) for w in pool]
         gemms.append(dict(label=label, fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym, x=x, wp=wp, y=y,
-                          X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K, wbytes=wbytes, pool=pool, turn=0))
-        print(f"[bench] {label}: {fmt} M={M} K={K} N={N} rung={info['name']}", file=sys.stderr, flush=True)
+                          X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K, wbytes=wbytes, pool=pool, turn=0,
+                          calls=calls, prep=prep, src=src))
+        print(f"[bench] {label}: {fmt} M={M} K={K} N={N} x={args.x_layout} rung={info['name']}", file=sys.stderr,
+              flush=True)
 
     if not gemms:
         print(f"bench.py: no GEMM labelled {args.only!r} in {args.workload}", file=sys.stderr)
         return 2
 
     def call(g):
-        wp = g["pool"][g["turn"] % len(g["pool"])]
+        st = g["calls"][g["turn"] % len(g["calls"])]()
         g["turn"] += 1
-        if args.rung >= 0:
-            qg.gemm_rung(g["fmt"], args.rung, g["x"], wp, g["N"], group=g["group"], has_zp=not g["sym"],
-                         out=g["y"])
-        elif g["fmt"] == "q4k":
-            qg.q4k(g["x"], wp, g["N"], out=g["y"])
-        elif g["fmt"] == "q6k":
-            qg.q6k(g["x"], wp, g["N"], out=g["y"])
-        else:
-            qg.w4a16(g["x"], wp, g["N"], g["group"], not g["sym"], out=g["y"])
+        if st != 0:
+            raise qg.QGemmError(f"{g['label']} GEMM", st)
+
+    def call_prep(p):
+        st = p["call"]()
+        if st != 0:
+            raise qg.QGemmError(p["label"], st)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         for g in gemms:
+            if g["prep"] is not None:
+                call_prep(g["prep"])
             call(g)
     torch.cuda.synchronize()
 
-    # timed region: K steps, HIP events around every launch on the launch stream
+    # Per-launch times: a pass of PROFILE_STEPS steps, untimed, with HIP events
+    # around every launch on the launch stream (an event between two kernels
+    # costs the queue a few microseconds, so the timed steps below carry
+    # events around the dominant GEMM only).
+    preps = [g["prep"] for g in gemms if g["prep"] is not None]
+    nprof = max(3, min(args.steps, PROFILE_STEPS))
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in gemms]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
+          for _ in range(nprof)]
+    evp = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in preps]
+           for _ in range(nprof)]
+    for s in range(nprof):
+        i = 0
         for j, g in enumerate(gemms):
+            if g["prep"] is not None:
+                evp[s][i][0].record(stream)
+                call_prep(g["prep"])
+                evp[s][i][1].record(stream)
+                i += 1
             ev[s][j][0].record(stream)
             call(g)
             ev[s][j][1].record(stream)
     torch.cuda.synchronize()
+    per = []
+    for i, p in enumerate(preps):
+        ms = float(np.mean([evp[s][i][0].elapsed_time(evp[s][i][1]) for s in range(nprof)]))
+        per.append(dict(label=p["label"], M=p["M"], K=p["K"], rung="x_to_xf", ms=round(ms, 5),
+                        gbps=round(p["bytes"] / ms / 1e6, 1)))
+    per_prep = len(per)
+    gemm_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(nprof)]))
+               for j in range(len(gemms))]
+    jd = int(np.argmax(gemm_ms))  # the dominant GEMM: largest share of the step
+
+    # timed region: K steps back to back; HIP events on the launch stream
+    # around every launch of the dominant GEMM
+    evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, g in enumerate(gemms):
+            if g["prep"] is not None:
+                call_prep(g["prep"])
+            if j == jd:
+                evd[s][0].record(stream)
+                call(g)
+                evd[s][1].record(stream)
+            else:
+                call(g)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    gemm_ms[jd] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evd]))
 
-    per = []
     for j, g in enumerate(gemms):
-        ms = float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+        ms = gemm_ms[j]
         per.append(dict(label=g["label"], fmt=g["fmt"], M=g["M"], K=g["K"], N=g["N"], rung=g["rung"],
                         ms=round(ms, 5), tflops=round(g["flops"] / ms / 1e9, 2),
                         weight_gbps=round(g["wbytes"] / ms / 1e6, 1),
@@ -177,7 +256,7 @@ def main() -> int:
     # Weight-bound GEMMs are short: per-launch events add a fixed cost, so they
     # are also timed back to back (50 launches a sample, median of 5, weights
     # rotating) next to a plain streaming read of the same bytes.
-    for g, p in zip(gemms, per):
+    for g, p in zip(gemms, per[per_prep:]):
         if len(g["pool"]) > 1:
             samples = []
             for _ in range(5):
@@ -197,9 +276,9 @@ def main() -> int:
     kernel_ms_step = sum(p["ms"] for p in per)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel (largest share of the step) and its roofline
-    jd = int(np.argmax([p["ms"] for p in per]))
-    gd, pd = gemms[jd], per[jd]
+    # dominant kernel and its roofline (its time is the timed region's mean)
+    gd, pd = gemms[jd], per[per_prep + jd]
+    pd["timed_in_step"] = True
     intensity = gd["flops"] / (gd["wbytes"] + 2 * gd["M"] * gd["K"] + 2 * gd["M"] * gd["N"])
     ridge = PEAK_TFLOPS[gd["dt"]] * 1e12 / (PEAK_HBM_GBPS * 1e9)
     if intensity >= ridge:
@@ -232,8 +311,11 @@ def main() -> int:
         "dtype": "f16" if all(g["dt"] == qg.F16 for g in gemms) else "bf16" if all(g["dt"] == qg.BF16 for g in gemms) else "f16+bf16",
         "data": "synthetic (seeded; shapes and value distributions of the workload, random weights)",
         "config": {"workload": args.workload, "gemms": [f"{g['label']}:{g['fmt']}:{g['M']}x{g['K']}x{g['N']}"
-                                                       for g in gemms]},
+                                                       for g in gemms],
+                   "x_layout": "fragment-major (copies made inside the step)" if xf_layout else "row-major"},
         "kernel_ms_per_step": round(kernel_ms_step, 5),
+        "per_kernel_timing": "HIP events around every launch in a separate profiling pass; the dominant GEMM's "
+                             "time is the mean of events around its launches inside the timed region",
         "per_kernel": per,
         "roofline": roof,
     }
@@ -249,7 +331,7 @@ def main() -> int:
         out["prefill_tok_s_linear_only"] = round(synth.QWEN3_8B_PROMPT / (synth.QWEN3_8B_LAYERS * ms_per_step * 1e-3), 1)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(gemms, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(gemms, args.cpu_seconds, xf_layout)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -391,10 +473,12 @@ def run_grouped(args) -> int:
 
 
 def staged_arm(g, call, reps: int = 20) -> dict:
-    """The dominant GEMM fused (M-ladder rung, and the 128x128 rung the staged
-    GEMM shares its tile with) against the staged arm: unpack into a 2-byte
-    scratch, then the same 128x128 streaming kernel on it.  Back-to-back
-    launches between HIP events on the launch stream, median of 5 samples."""
+    """The dominant GEMM fused (its rung in the step, on the step's activation
+    layout, and the 128x128 rung on row-major activations, the tile the staged
+    GEMM shares) against the staged arm: unpack into a 2-byte scratch, then
+    the same 128x128 streaming kernel on it, on row-major activations.
+    Back-to-back launches between HIP events on the launch stream, median of
+    5 samples."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -426,7 +510,8 @@ def staged_arm(g, call, reps: int = 20) -> dict:
                                      has_zp=not g["sym"], out=y0))
     wq = g["wbytes"]
     w16 = 2.0 * g["K"] * (-(-g["N"] // 16) * 16)
-    return {"gemm": g["label"], "fused_ms": round(fused, 5), "fused_same_tile_ms": round(same_tile, 5),
+    return {"gemm": g["label"], "fused_rung": g["rung"], "fused_ms": round(fused, 5),
+            "fused_same_tile_ms": round(same_tile, 5),
             "staged_ms": round(staged, 5), "unpack_ms": round(unpack, 5),
             "staged_gemm_ms": round(staged - unpack, 5), "staged_over_fused_same_tile": round(staged / same_tile, 3),
             "weight_bytes_fused": round(wq), "weight_bytes_staged": round(wq + 2 * w16),
@@ -471,10 +556,11 @@ def copy_calibration(nbytes: int) -> int:
     return 0
 
 
-def cpu_baseline(gemms, target_s: float) -> dict:
+def cpu_baseline(gemms, target_s: float, xf_layout: bool = False) -> dict:
     """The oracle as it stands: full dequant of every weight of the step plus
     the fp64 GEMM on a few rows of each linear, extrapolated linearly in M
-    (rows are independent), reported in the metric's unit."""
+    (rows are independent), reported in the metric's unit; with the
+    fragment-major layout also the oracle's copy of each distinct input."""
     import oracle
 
     t_deq = 0.0
@@ -482,6 +568,8 @@ def cpu_baseline(gemms, target_s: float) -> dict:
     for g in gemms:
         t0 = time.perf_counter()
         Ws.append(oracle.dequant(g["fmt"], g["enc"], g["N"], g["K"], g["dt"]))
+        if xf_layout and g["prep"] is not None:
+            oracle.fragment_major(g["X"])
         t_deq += time.perf_counter() - t0
     # grow the row sample until the GEMM part takes about target_s - t_deq
     # seconds (or covers every row); a row costs the same in every position
@@ -505,7 +593,8 @@ def cpu_baseline(gemms, target_s: float) -> dict:
     flops = sum(g["flops"] for g in gemms)
     return {"value": round(flops / full / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"full dequant of all {len(gemms)} weights ({t_deq:.2f} s) + fp64 GEMM of the first {rows} "
+            "sample": f"full dequant of all {len(gemms)} weights{' and layout copies of the inputs' if xf_layout else ''} "
+                  f"({t_deq:.2f} s) + fp64 GEMM of the first {rows} "
                       f"rows of each linear ({t_gemm:.2f} s), extrapolated linearly to all rows "
                       f"(estimated {full:.1f} s per step)"}
 

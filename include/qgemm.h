@@ -165,6 +165,40 @@ int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int d
 int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N,
                     int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
 
+/* ---- fragment-major activations ---------------------------------------------
+ * A second layout of X, made for the MFMA kernels: 32-row blocks one after
+ * the other, each a sequence of 128-wide K chunks; inside a chunk, eight
+ * 16-wide k-steps of 512 elements, each two halves (k%16 < 8, then >= 8) of
+ * 32 rows x 8 consecutive k.  Element X[m][k] sits at
+ *     ((m/32 * K/128 + k/128) * 8 + (k/16)%8) * 512 + ((k/8)%2 * 32 + m%32) * 8 + k%8
+ * and rows M .. 32*ceil(M/32)-1 of the last block hold zeros.  One
+ * activation operand of a 32x32x16 MFMA (32 rows x 16 k) is then 1 KB of
+ * contiguous memory instead of 32 separate 32-byte pieces of rows K apart;
+ * the streaming kernels spend a fifth to a third of their time refilling L1
+ * with the row-major pieces.  The layout is this library's own (the pages
+ * store activations row-major); it changes where X is read, not what is
+ * computed.
+ *
+ * qgemm_xf_bytes: bytes of the fragment-major copy of an M x K matrix
+ *   (2 * K * 32*ceil(M/32)); 0 for M < 0, K not a positive multiple of 128,
+ *   or sizes beyond int32.
+ * qgemm_x_to_xf: writes that copy of the row-major X [M][K] (fp16 or bf16
+ *   bits; the copy moves 16-bit elements and ignores the type) into Xf
+ *   (device, 16-byte aligned, qgemm_xf_bytes(M, K) bytes, caller-owned, not
+ *   overlapping X).  One launch on `stream`; M = 0 is a no-op.  Errors:
+ *   QGEMM_ERR_SHAPE, _NULL, _ALIGN, _HIP.
+ * qgemm_gemm_xf: qgemm_gemm_rung with X given in the fragment-major layout
+ *   (M and K are the logical sizes).  For the same rung, Y is bit-identical
+ *   to qgemm_gemm_rung's on the row-major X: the kernels and their
+ *   accumulation order are the same, only the activation addresses differ.
+ *   rung = -1 selects from the ladder tuned for this layout
+ *   (qgemm_select_rung_xf); errors as qgemm_gemm_rung. */
+size_t qgemm_xf_bytes(int64_t M, int64_t K);
+int qgemm_x_to_xf(const void *X, void *Xf, int64_t M, int64_t K, void *stream);
+int qgemm_gemm_xf(int format, int rung, const void *Xf, const void *Wpacked, void *Y, int64_t M, int64_t N,
+                  int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+int qgemm_select_rung_xf(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
+
 /* ---- logical dequant --------------------------------------------------------
  * Writes the unpacked weights as logical Wout[K][N] (row-major, dtype
  * elements, device, caller-owned) with the same device unpack code the

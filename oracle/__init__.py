@@ -56,6 +56,7 @@ def load_library(path: str):
         "qref_q6k_weight": (ctypes.c_int, [ctypes.c_uint16, ctypes.c_int, ctypes.c_int, ctypes.c_int, c_u16p]),
         "qref_w4a16_weight": (ctypes.c_int, [ctypes.c_uint16, ctypes.c_int, ctypes.c_int, ctypes.c_int, c_u16p]),
         "qref_dequant_q4k": (ctypes.c_int, [c_u8p, i64, i64, ctypes.c_int, c_u16p]),
+        "qref_fragment_major": (ctypes.c_int, [c_u16p, i64, i64, c_u16p]),
         "qref_dequant_q6k": (ctypes.c_int, [c_u8p, i64, i64, ctypes.c_int, c_u16p]),
         "qref_dequant_w4a16": (ctypes.c_int, [c_u8p, c_u16p, c_u8p, i64, i64, i64, ctypes.c_int, c_u16p]),
         "qref_gemm": (ctypes.c_int, [c_u16p, c_u16p, i64, i64, i64, ctypes.c_int, c_dp, c_dp]),
@@ -242,6 +243,20 @@ def gemm_at(X: np.ndarray, W: np.ndarray, dtype: int, rows, cols):
     if rc:
         raise ValueError(f"qref_gemm_at failed ({rc})")
     return Y, B
+
+
+# ---- activation layout of the library under test --------------------------
+
+def fragment_major(X: np.ndarray) -> np.ndarray:
+    """The fragment-major copy of the bit patterns X [M][K] (flat, uint16,
+    32*ceil(M/32)*K elements): an activation layout of the library under test,
+    not a step of the pages' computation; see qref.c, item 4."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    out = np.full(((M + 31) // 32) * 32 * K, 0xFFFF, np.uint16)  # every element is written below
+    if _load().qref_fragment_major(_p(X, ctypes.c_uint16), M, K, _p(out, ctypes.c_uint16)):
+        raise ValueError(f"fragment_major: K = {K} is not a positive multiple of 128")
+    return out
 
 
 def num_threads() -> int:

@@ -33,6 +33,11 @@
  *     (the k loop innermost, W read through a transposed copy), together with
  *     the error scale B[m][n] = sum_k |X[m][k]| * |W[k][n]|.
  *
+ *  4. The fragment-major copy of X, an activation layout of the library
+ *     under test (not of the pages): element (m, k) of X [M][K] moves to
+ *        ((m/32 * K/128 + k/128) * 8 + (k/16)%8) * 512 + ((k/8)%2 * 32 + m%32) * 8 + k%8
+ *     and rows M .. 32*ceil(M/32)-1 are zero.  It only moves bit patterns.
+ *
  * All 16-bit floating-point values cross this interface as raw bit patterns
  * (uint16_t).  dtype 0 = fp16, 1 = bf16.
  */
@@ -431,4 +436,18 @@ int qref_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* 4. fragment-major copy: one element at a time, straight from the formula */
+int qref_fragment_major(const uint16_t *X, int64_t M, int64_t K, uint16_t *out)
+{
+    if (M < 0 || K <= 0 || K % 128 != 0) return 1;
+    const int64_t Mp = (M + 31) / 32 * 32;
+    for (int64_t m = 0; m < Mp; m++)
+        for (int64_t k = 0; k < K; k++) {
+            const int64_t idx = ((m / 32 * (K / 128) + k / 128) * 8 + (k / 16) % 8) * 512
+                                + ((k / 8) % 2 * 32 + m % 32) * 8 + k % 8;
+            out[idx] = m < M ? X[m * K + k] : 0;
+        }
+    return 0;
 }

@@ -14,6 +14,8 @@ Functions keep the C names without the ``qgemm_`` prefix:
   :func:`w4a16_pack` and their inverses ``*_unpack``;
 * GEMMs (device, torch): :func:`q4k`, :func:`q6k`, :func:`w4a16`,
   :func:`gemm_rung`;
+* fragment-major activations: :func:`xf_bytes`, :func:`x_to_xf`,
+  :func:`gemm_xf`, :func:`select_rung_xf`;
 * the staged dequant :func:`dequant` and the M-ladder queries
   :func:`select_rung`, :func:`rung_info`, :func:`rung_name`, :func:`num_rungs`.
 """
@@ -80,6 +82,10 @@ SIGNATURES = {
     "qgemm_staged": (_INT, [_INT, _VP, _VP, _VP, _SZ, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_probe_mfma": (_INT, [_VP, _VP, _INT, _INT, _INT, _VP]),
     "qgemm_probe_read": (_INT, [_VP, _I64, _VP, _INT, _VP]),
+    "qgemm_xf_bytes": (_SZ, [_I64, _I64]),
+    "qgemm_x_to_xf": (_INT, [_VP, _VP, _I64, _I64, _VP]),
+    "qgemm_gemm_xf": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_select_rung_xf": (_INT, [_INT, _I64, _I64, _I64, _INT, _VP]),
 }
 
 
@@ -249,6 +255,46 @@ def gemm_rung(fmt, rung: int, x, wp, N: int, group: int = 0, has_zp: bool = Fals
     return y
 
 
+def xf_bytes(M: int, K: int) -> int:
+    return int(lib().qgemm_xf_bytes(M, K))
+
+
+def x_to_xf(x, out=None, stream=None):
+    """The fragment-major copy of a row-major [M, K] activation matrix: a flat
+    tensor of x's dtype with 32*ceil(M/32)*K elements."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    n = xf_bytes(M, K) // 2
+    if n == 0 and M > 0:
+        raise QGemmError("qgemm_xf_bytes", -2)
+    if out is None:
+        out = torch.empty((n,), dtype=x.dtype, device=x.device)
+    elif out.numel() < n or out.dtype != x.dtype:
+        raise ValueError("out is too small or has the wrong dtype")
+    _check("qgemm_x_to_xf", lib().qgemm_x_to_xf(_dev(x, "x"), _dev(out, "out"), M, K, _stream(stream)))
+    return out
+
+
+def gemm_xf(fmt, xf, wp, M: int, N: int, K: int, group: int = 0, has_zp: bool = False, rung: int = -1, out=None,
+            stream=None):
+    """Y = X . dequant(W) with X given as its fragment-major copy `xf`
+    (from :func:`x_to_xf`); rung -1 selects from the ladder for that layout."""
+    torch = _torch()
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if xf.numel() < xf_bytes(M, K) // 2:
+        raise ValueError("xf is smaller than the fragment-major copy of an M x K matrix")
+    if out is None:
+        out = torch.empty((M, N), dtype=xf.dtype, device=xf.device)
+    elif out.shape != (M, N) or out.dtype != xf.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    st = lib().qgemm_gemm_xf(f, rung, _dev(xf, "xf"), _dev(wp, "wp"), _dev(out, "out"), M, N, K, group,
+                             int(bool(has_zp)), _dtype_code(xf), _stream(stream))
+    _check("qgemm_gemm_xf", st)
+    return out
+
+
 def q4k(x, wp, N: int, out=None, stream=None):
     """Y[M,N] = X[M,K] . dequant_Q4_K(W)."""
     M, K = x.shape
@@ -360,6 +406,15 @@ def select_rung(fmt, M: int, N: int, K: int, dtype: int = F16) -> dict:
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
     info = np.zeros(8, np.int32)
     _check("qgemm_select_rung", lib().qgemm_select_rung(f, M, N, K, dtype, _np_ptr(info)))
+    d = dict(zip(_INFO_KEYS, (int(v) for v in info)))
+    d["name"] = rung_name(d["rung"])
+    return d
+
+
+def select_rung_xf(fmt, M: int, N: int, K: int, dtype: int = F16) -> dict:
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    info = np.zeros(8, np.int32)
+    _check("qgemm_select_rung_xf", lib().qgemm_select_rung_xf(f, M, N, K, dtype, _np_ptr(info)))
     d = dict(zip(_INFO_KEYS, (int(v) for v in info)))
     d["name"] = rung_name(d["rung"])
     return d

@@ -86,6 +86,39 @@ struct Args {
     long long wstride;           // grouped: packed bytes of one expert's weights
 };
 
+// Activation layouts.  X_ROW: X[m][k] at m*K + k.  X_FRAG (fragment-major):
+// 32-row blocks one after the other, each a sequence of 128-wide K chunks;
+// inside a chunk, eight 16-wide k-steps of 512 elements, each two halves
+// (k%16 < 8, then >= 8) of 32 rows x 8 consecutive k:
+//   X[m][k] at ((m/32 * K/128 + k/128) * 8 + (k/16)%8) * 512
+//              + ((k/8)%2 * 32 + m%32) * 8 + k%8.
+// One 32x32x16 activation fragment (32 rows x 16 k) is then 1 KB of
+// contiguous memory, and any 8 consecutive k of one row (the unit every
+// kernel loads) stay 16 contiguous bytes.  Kernels address X as row(m) +
+// chunk(c) + off(o): off takes the within-chunk offset o (a multiple of 8,
+// below 128) and is additive over offsets whose bits do not overlap.
+enum { X_ROW = 0, X_FRAG = 1 };
+
+template <int XL>
+struct XLay;
+
+template <>
+struct XLay<X_ROW> {
+    static __device__ __forceinline__ const uint16_t *row(const Args &a, int m) { return a.X + (long long)m * a.K; }
+    static __device__ __forceinline__ long long chunk(int c) { return (long long)kChunk * c; }
+    static __device__ __forceinline__ int off(int o) { return o; }
+};
+
+template <>
+struct XLay<X_FRAG> {
+    static __device__ __forceinline__ const uint16_t *row(const Args &a, int m)
+    {
+        return a.X + (long long)(m >> 5) * 32 * a.K + (m & 31) * 8;
+    }
+    static __device__ __forceinline__ long long chunk(int c) { return 32LL * kChunk * c; }
+    static __device__ __forceinline__ int off(int o) { return ((o >> 4) & 7) * 512 + ((o >> 3) & 1) * 256; }
+};
+
 // XCD-aware renumbering: workgroup b of n runs on XCD b % 8; give each XCD a
 // contiguous range of logical indices (a bijection on [0, n)).
 __device__ __forceinline__ int xcd_order(int b, int n)
@@ -468,9 +501,10 @@ __device__ __forceinline__ void store_block32(const Args &a, const f32x16 &v, in
 // ---------------------------------------------------------------------------
 // One workgroup: rows m0 .. m0+16*RB-1 (those below a.M) of panels p0 ..
 // p0+PN-1; a.kw waves split K and reduce through LDS.
-template <int FMT, int DT, int RB, int PN>
+template <int FMT, int DT, int RB, int PN, int XL>
 __device__ __forceinline__ void direct_body(const Args &a, int p0, int m0)
 {
+    using XA = XLay<XL>;
     extern __shared__ f32x4 red[];  // [kw][PN*RB][64]
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
@@ -488,7 +522,7 @@ __device__ __forceinline__ void direct_body(const Args &a, int p0, int m0)
     for (int rb = 0; rb < RB; rb++) {
         int r = m0 + 16 * rb + col;
         r = r < a.M ? r : a.M - 1;  // clamped rows are computed and discarded
-        xrow[rb] = a.X + (long long)r * a.K + 32 * g;
+        xrow[rb] = XA::row(a, r) + XA::off(32 * g);
     }
     RunSrc<FMT> src[PN];
 #pragma unroll
@@ -505,7 +539,7 @@ __device__ __forceinline__ void direct_body(const Args &a, int p0, int m0)
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cb + 8 * i);
+            for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + XA::chunk(cb) + XA::off(8 * i));
     }
     for (int c = cb; c < ce; c++) {
         u32x4 wf[PN][4];
@@ -522,7 +556,7 @@ __device__ __forceinline__ void direct_body(const Args &a, int p0, int m0)
 #pragma unroll
             for (int rb = 0; rb < RB; rb++)
 #pragma unroll
-                for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * (c + 1) + 8 * i);
+                for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + XA::chunk(c + 1) + XA::off(8 * i));
         }
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
@@ -552,10 +586,10 @@ __device__ __forceinline__ void direct_body(const Args &a, int p0, int m0)
     }
 }
 
-template <int FMT, int DT, int RB, int PN>
+template <int FMT, int DT, int RB, int PN, int XL>
 __global__ void __launch_bounds__(512) k_direct(Args a)
 {
-    direct_body<FMT, DT, RB, PN>(a, blockIdx.x * PN, blockIdx.y * (16 * RB));
+    direct_body<FMT, DT, RB, PN, XL>(a, blockIdx.x * PN, blockIdx.y * (16 * RB));
 }
 
 // Grouped per-expert GEMM: rows offs[e] .. offs[e+1]-1 of X and Y use expert
@@ -581,7 +615,7 @@ __global__ void __launch_bounds__(512) k_direct_grouped(Args a)
     Args b = a;
     b.W = a.W + (long long)e * a.wstride;
     b.M = hi;
-    direct_body<FMT, DT, RB, PN>(b, blockIdx.x * PN, lo + (j - base) * R);
+    direct_body<FMT, DT, RB, PN, X_ROW>(b, blockIdx.x * PN, lo + (j - base) * R);
 }
 
 // ---------------------------------------------------------------------------
@@ -607,9 +641,10 @@ __global__ void __launch_bounds__(512) k_direct_grouped(Args a)
 // grouped tile order (below): its L2 then serves both the shared weight
 // panels and the shared activation rows.
 // ---------------------------------------------------------------------------
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int XL>
 __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 {
+    using XA = XLay<XL>;
     constexpr int NTG = 64 * NWM * NWN;    // threads of one K group
     constexpr int PB = WPB * NWN;          // panels per tile
     constexpr int BM = WM * NWM;           // rows per tile
@@ -632,7 +667,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
     for (int rb = 0; rb < RBW; rb++) {
         int r = m0 + 16 * rb + r16;
         r = r < a.M ? r : a.M - 1;
-        xrow[rb] = a.X + (long long)r * a.K + 8 * g4;
+        xrow[rb] = XA::row(a, r) + XA::off(8 * g4);
     }
 
     f32x4 acc[WPB][RBW];
@@ -659,7 +694,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * c_lo + 32 * i);
+        for (int i = 0; i < 4; i++) xf[rb][i] = *(const u32x4 *)(xrow[rb] + XA::chunk(c_lo) + XA::off(32 * i));
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
         u32x4 f[4];
@@ -699,7 +734,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
                 for (int pb = 0; pb < WPB; pb++) acc[pb][rb] = mma<DT>(wcur[pb], xf[rb][i], acc[pb][rb]);
-                xf[rb][i] = *(const u32x4 *)(xrow[rb] + kChunk * cn + 32 * i);
+                xf[rb][i] = *(const u32x4 *)(xrow[rb] + XA::chunk(cn) + XA::off(32 * i));
             }
 #pragma unroll
             for (int s = 0; s < UPT; s++) {
@@ -749,8 +784,9 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 // ---------------------------------------------------------------------------
 // One workgroup's pass over K chunks [c_lo, c_hi) of one tile: wave (wm, wn)
 // adds its WM x (16*WPB) block of X[rows m0..][:] * W[:][panels p0..] into acc.
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int XL>
 struct Stream32 {
+    using XA = XLay<XL>;
     static constexpr int NTG = 64 * NWM * NWN;  // threads of one K group
     static constexpr int PB = WPB * NWN;        // panels per tile
     static constexpr int CB = PB / 2;           // 32-column blocks per tile
@@ -760,6 +796,9 @@ struct Stream32 {
     static constexpr int RUNS = PB * 64;        // 32-code weight runs per chunk
     static constexpr int UPT = (RUNS + NTG - 1) / NTG;  // runs per thread per chunk
     static constexpr int UFULL = RUNS / NTG;    // slots every thread fills
+    // activation k-steps held ahead: a whole chunk for one row block, half a
+    // chunk for three (a whole chunk of three row blocks is 96 VGPRs)
+    static constexpr int XD = RBW >= 3 ? 4 : 8;
     static_assert(WPB % 2 == 0 && WM % 32 == 0, "32x32 blocks");
     static_assert(UPT >= 1 && (RUNS - UFULL * NTG) % 64 == 0, "a partial slot must cover whole waves");
     typedef u32x4 Lds[2][CB][8][64];
@@ -772,10 +811,10 @@ struct Stream32 {
     for (int rb = 0; rb < RBW; rb++) {
         int r = m0 + 32 * rb + (lane & 31);
         r = r < a.M ? r : a.M - 1;
-        xrow[rb] = a.X + (long long)r * a.K + 8 * (lane >> 5);
+        xrow[rb] = XA::row(a, r) + XA::off(8 * (lane >> 5));
     }
 
-    u32x4 xf[RBW][8];
+    u32x4 xf[RBW][XD];
     RunSrc<FMT> src[UPT];
     RunRaw<FMT> raw[UPT];
     int slot_cp[UPT], slot_lane[UPT];
@@ -802,7 +841,7 @@ struct Stream32 {
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
-        for (int ks = 0; ks < 8; ks++) xf[rb][ks] = *(const u32x4 *)(xrow[rb] + kChunk * c_lo + 16 * ks);
+        for (int ks = 0; ks < XD; ks++) xf[rb][ks] = *(const u32x4 *)(xrow[rb] + XA::chunk(c_lo) + XA::off(16 * ks));
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
         u32x4 f[4];
@@ -845,8 +884,12 @@ struct Stream32 {
 #pragma unroll
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
-                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma32<DT>(wcur[cb], xf[rb][ks], acc[cb][rb]);
-                xf[rb][ks] = *(const u32x4 *)(xrow[rb] + kChunk * cn + 16 * ks);
+                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma32<DT>(wcur[cb], xf[rb][ks % XD], acc[cb][rb]);
+                // the slot just consumed takes the k-step XD ahead
+                if (ks + XD < 8)
+                    xf[rb][ks % XD] = *(const u32x4 *)(xrow[rb] + XA::chunk(c) + XA::off(16 * (ks + XD)));
+                else
+                    xf[rb][ks % XD] = *(const u32x4 *)(xrow[rb] + XA::chunk(cn) + XA::off(16 * (ks + XD - 8)));
             }
             if ((ks & 1) == 0) {
 #pragma unroll
@@ -878,11 +921,11 @@ struct Stream32 {
     }
 };
 
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int XL>
 __global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_stream32(Args a)
 {
-    using S = Stream32<FMT, DT, WM, WPB, NWM, NWN>;
+    using S = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL>;
     constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM, CB = S::CB;
     static_assert(KS == 1 || CBW * RBW * 16 * NWM * NWN * 64 <= 2 * CB * 8 * 64 * 4, "K-split reduction must fit in LDS");
     __shared__ typename S::Lds sWall[KS];
@@ -987,6 +1030,29 @@ __global__ void __launch_bounds__(256) k_stage(Args a, uint8_t *Ws)
 }
 
 // ---------------------------------------------------------------------------
+// Fragment-major copy of X (layout X_FRAG).  One workgroup per (32-row block,
+// 128-wide chunk), which is 8 KB in both layouts; each thread moves two
+// 16-byte units (8 consecutive k of one row), read row-major, 16 lanes per
+// row, and written to their fragment slot.  Rows at or past M become zeros.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_x_to_xf(const uint16_t *X, uint16_t *Xf, int M, int K)
+{
+    const int nch = K / kChunk;
+    const int tile = blockIdx.x, blk = tile / nch, c = tile % nch;
+    uint16_t *dst = Xf + (long long)tile * (32 * kChunk);
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+        const int t = threadIdx.x + 256 * half;  // unit of the tile: row r, k group kq
+        const int r = t >> 4, kq = t & 15;
+        const int m = 32 * blk + r;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (m < M) v = *(const u32x4 *)(X + (long long)m * K + kChunk * c + 8 * kq);
+        // k-step kq/2, half kq%2, row r
+        *(u32x4 *)(dst + ((kq >> 1) * 64 + (kq & 1) * 32 + r) * 8) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation, the M-ladder, launches.
 // ---------------------------------------------------------------------------
 
@@ -998,11 +1064,12 @@ enum Rung {
     RUNG_M128 = 4,        // 32x32x16 MFMA: 128x128, 4 waves of 32x128
     RUNG_M128_K2 = 5,     // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
     RUNG_M128N160 = 6,    // 32x32x16 MFMA: 128x160, 4 waves of 32x160
-    RUNG_COUNT = 7
+    RUNG_M96_K2 = 7,      // 32x32x16 MFMA: 96x128, 4 waves of 96x32, K split over two groups
+    RUNG_COUNT = 8
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
-                                            "mfma32-128x160"};
+                                            "mfma32-128x160",    "mfma32-96x128-k2"};
 
 struct Plan {
     int rung;
@@ -1054,10 +1121,11 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M16_256:
     case RUNG_M128:
     case RUNG_M128_K2:
-    case RUNG_M128N160: {
-        pl.rows = rung == RUNG_M16_256 ? 256 : 128;
+    case RUNG_M128N160:
+    case RUNG_M96_K2: {
+        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M96_K2 ? 96 : 128;
         pl.cols = rung == RUNG_M128N160 ? 160 : 128;
-        pl.kw = (rung == RUNG_M128_K2 && (K / kChunk) % 2 == 0) ? 2 : 1;
+        pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M96_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
         pl.waves = rung == RUNG_M16_256 ? 8 : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         pl.tiles_n = ceil_div(np, pl.cols / 16);
@@ -1097,6 +1165,10 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    32x32x16 MFMAs with K split between two wave groups;
 //  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
 //    whichever the occupancy model below finishes first.
+// On fragment-major activations three crossovers move (the rules are in
+// select_rung): K-split tiles take over from the direct kernel earlier over
+// a long K, 96-row K-split tiles serve shapes whose 128-row tiles leave CUs
+// idle, and the 256-row tile wins every tie of the occupancy model.
 // Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
 // of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
 // the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
@@ -1110,7 +1182,7 @@ double stream_cost(long long M, long long np, int cols)
     return t * cols / 128.0;
 }
 
-int select_rung(int fmt, long long M, long long N, long long K)
+int select_rung(int fmt, long long M, long long N, long long K, int xl)
 {
     const long long np = (N + 15) / 16, tn = (np + 7) / 8;
     if (np <= 4) return RUNG_SKINNY_N;
@@ -1122,8 +1194,26 @@ int select_rung(int fmt, long long M, long long N, long long K)
         if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
         return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
     }
-    const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
-    if (t128 < 128) return RUNG_WIDE;
+    const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256), t96 = tn * ((M + 95) / 96);
+    if (xl == X_FRAG) {
+        // fragment-major activations make every activation load one
+        // contiguous 1 KB block, which moves the crossovers:
+        //  * over a long K, K-split tiles beat the direct kernel as soon as
+        //    there are 128 tiles of 96 rows;
+        if (t128 < 128 && !(K >= 8192 && t96 >= 128)) return RUNG_WIDE;
+        //  * 96-row tiles when they fit one pass over the CUs and keep more
+        //    of them busy than 128-row tiles (each 96-row wave reads three
+        //    row blocks of activations per weight fragment);
+        if (t96 <= kCUs && t96 > t128) return RUNG_M96_K2;
+        //  * the 256-row tile whenever the occupancy model has it finish no
+        //    later than the 128-row tiles (it unpacks each weight once for
+        //    256 rows; a 256x128 tile counts as two 128x128 tiles);
+        const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
+        const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
+        if (t256 >= 512 || c256 <= c128) return RUNG_M16_256;
+    } else {
+        if (t128 < 128) return RUNG_WIDE;
+    }
     // many 256-row tiles: eight waves at two per SIMD hide the most latency
     if (t256 >= 512) return RUNG_M16_256;
     // few tiles over a long K: split K inside the workgroup
@@ -1134,62 +1224,78 @@ int select_rung(int fmt, long long M, long long N, long long K)
     return RUNG_M128;
 }
 
-template <int FMT, int DT, int RB, int PN>
+template <int FMT, int DT, int RB, int PN, int XL>
 hipError_t launch_direct_rp(const Plan &pl, const Args &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_direct<FMT, DT, RB, PN>), pl.grid, dim3(64 * pl.kw), pl.lds, s, a);
+    hipLaunchKernelGGL((k_direct<FMT, DT, RB, PN, XL>), pl.grid, dim3(64 * pl.kw), pl.lds, s, a);
     return hipGetLastError();
 }
 
-template <int FMT, int DT>
+template <int FMT, int DT, int XL>
 hipError_t launch_direct(const Plan &pl, const Args &a, hipStream_t s)
 {
     if (pl.pn == 1) {
         switch (pl.rb) {
-        case 1: return launch_direct_rp<FMT, DT, 1, 1>(pl, a, s);
-        case 2: return launch_direct_rp<FMT, DT, 2, 1>(pl, a, s);
-        case 3: return launch_direct_rp<FMT, DT, 3, 1>(pl, a, s);
-        default: return launch_direct_rp<FMT, DT, 4, 1>(pl, a, s);
+        case 1: return launch_direct_rp<FMT, DT, 1, 1, XL>(pl, a, s);
+        case 2: return launch_direct_rp<FMT, DT, 2, 1, XL>(pl, a, s);
+        case 3: return launch_direct_rp<FMT, DT, 3, 1, XL>(pl, a, s);
+        default: return launch_direct_rp<FMT, DT, 4, 1, XL>(pl, a, s);
         }
     }
-    if (pl.rb > 1) return pl.rb == 2 ? launch_direct_rp<FMT, DT, 2, 4>(pl, a, s) : launch_direct_rp<FMT, DT, 3, 4>(pl, a, s);
+    if (pl.rb > 1)
+        return pl.rb == 2 ? launch_direct_rp<FMT, DT, 2, 4, XL>(pl, a, s) : launch_direct_rp<FMT, DT, 3, 4, XL>(pl, a, s);
     switch (pl.pn) {
-    case 2: return launch_direct_rp<FMT, DT, 1, 2>(pl, a, s);
-    case 3: return launch_direct_rp<FMT, DT, 1, 3>(pl, a, s);
-    default: return launch_direct_rp<FMT, DT, 1, 4>(pl, a, s);
+    case 2: return launch_direct_rp<FMT, DT, 1, 2, XL>(pl, a, s);
+    case 3: return launch_direct_rp<FMT, DT, 1, 3, XL>(pl, a, s);
+    default: return launch_direct_rp<FMT, DT, 1, 4, XL>(pl, a, s);
     }
 }
 
-template <int FMT, int DT>
+template <int FMT, int DT, int XL>
 hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
+    const bool even = (a.K / kChunk) % 2 == 0;  // an odd chunk count is not split
     switch (pl.rung) {
     case RUNG_M16_256:
-        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 8, 1>), pl.grid, dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_stream<FMT, DT, 32, 8, 8, 1, XL>), pl.grid, dim3(512), 0, s, a);
         return hipGetLastError();
     case RUNG_M128:
-        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1, XL>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_M128_K2:
-        if ((a.K / kChunk) % 2 == 0)
-            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 2>), pl.grid, dim3(512), 0, s, a);
-        else  // an odd chunk count is not split
-            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        if (even)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 2, XL>), pl.grid, dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 8, 4, 1, 1, XL>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_M128N160:
-        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 10, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 10, 4, 1, 1, XL>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M96_K2:
+        if (even)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 96, 2, 1, 4, 2, XL>), pl.grid, dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 96, 2, 1, 4, 1, XL>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     default:
         break;
     }
-    return launch_direct<FMT, DT>(pl, a, s);
+    return launch_direct<FMT, DT, XL>(pl, a, s);
 }
 
-hipError_t launch(int fmt, int dtype, const Plan &pl, const Args &a, hipStream_t s)
+template <int XL>
+hipError_t launch_xl(int fmt, int dtype, const Plan &pl, const Args &a, hipStream_t s)
 {
-    if (fmt == FMT_Q4K) return dtype == DT_F16 ? launch_fd<FMT_Q4K, DT_F16>(pl, a, s) : launch_fd<FMT_Q4K, DT_BF16>(pl, a, s);
-    if (fmt == FMT_Q6K) return dtype == DT_F16 ? launch_fd<FMT_Q6K, DT_F16>(pl, a, s) : launch_fd<FMT_Q6K, DT_BF16>(pl, a, s);
-    return dtype == DT_F16 ? launch_fd<FMT_W4, DT_F16>(pl, a, s) : launch_fd<FMT_W4, DT_BF16>(pl, a, s);
+    if (fmt == FMT_Q4K)
+        return dtype == DT_F16 ? launch_fd<FMT_Q4K, DT_F16, XL>(pl, a, s) : launch_fd<FMT_Q4K, DT_BF16, XL>(pl, a, s);
+    if (fmt == FMT_Q6K)
+        return dtype == DT_F16 ? launch_fd<FMT_Q6K, DT_F16, XL>(pl, a, s) : launch_fd<FMT_Q6K, DT_BF16, XL>(pl, a, s);
+    return dtype == DT_F16 ? launch_fd<FMT_W4, DT_F16, XL>(pl, a, s) : launch_fd<FMT_W4, DT_BF16, XL>(pl, a, s);
+}
+
+hipError_t launch(int fmt, int dtype, int xl, const Plan &pl, const Args &a, hipStream_t s)
+{
+    return xl == X_FRAG ? launch_xl<X_FRAG>(fmt, dtype, pl, a, s) : launch_xl<X_ROW>(fmt, dtype, pl, a, s);
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -1240,7 +1346,7 @@ Args make_args(int fmt, const void *X, const void *W, void *Y, long long M, long
 }
 
 int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
-         long long group, int has_zp, int dtype, void *stream)
+         long long group, int has_zp, int dtype, void *stream, int xl = X_ROW)
 {
     if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
     int st = check_shape(fmt, M, N, K, group);
@@ -1251,10 +1357,10 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     if (!X || !W || !Y) return QGEMM_ERR_NULL;
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
     Plan pl;
-    if (!make_plan(rung < 0 ? select_rung(fmt, M, N, K) : rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
+    if (!make_plan(rung < 0 ? select_rung(fmt, M, N, K, xl) : rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
     Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
     a.kw = pl.kw;
-    return launch_status(launch(fmt, dtype, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
+    return launch_status(launch(fmt, dtype, xl, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
 }
 
 long long packed_bytes(int fmt, long long N, long long K, long long group, int has_zp)
@@ -1339,7 +1445,7 @@ hipError_t launch_staged_dt(int fmt, const Args &a, uint8_t *scratch, const Plan
     if (e != hipSuccess || a.M == 0) return e;
     Args b = a;
     b.W = scratch;
-    hipLaunchKernelGGL((k_stream32<FMT_DENSE, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, b);
+    hipLaunchKernelGGL((k_stream32<FMT_DENSE, DT, 32, 8, 4, 1, 1, X_ROW>), pl.grid, dim3(256), 0, s, b);
     return hipGetLastError();
 }
 
@@ -1433,7 +1539,37 @@ int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int d
 
 int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
 {
-    return qgemm_rung_info(select_rung(format, M, N, K), format, M, N, K, dtype, info8);
+    return qgemm_rung_info(select_rung(format, M, N, K, X_ROW), format, M, N, K, dtype, info8);
+}
+
+int qgemm_select_rung_xf(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
+{
+    return qgemm_rung_info(select_rung(format, M, N, K, X_FRAG), format, M, N, K, dtype, info8);
+}
+
+size_t qgemm_xf_bytes(int64_t M, int64_t K)
+{
+    if (M < 0 || K < kChunk || K % kChunk != 0 || M > INT32_MAX || K > INT32_MAX) return 0;
+    return (size_t)((M + 31) / 32) * 32 * (size_t)K * 2;
+}
+
+int qgemm_x_to_xf(const void *X, void *Xf, int64_t M, int64_t K, void *stream)
+{
+    if (M < 0 || K < kChunk || K % kChunk != 0 || M > INT32_MAX || K > INT32_MAX) return QGEMM_ERR_SHAPE;
+    const long long tiles = ((M + 31) / 32) * (K / kChunk);
+    if (tiles > INT32_MAX) return QGEMM_ERR_SHAPE;
+    if (M == 0) return QGEMM_OK;
+    if (!X || !Xf) return QGEMM_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Xf)) return QGEMM_ERR_ALIGN;
+    hipLaunchKernelGGL(k_x_to_xf, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, (const uint16_t *)X,
+                       (uint16_t *)Xf, (int)M, (int)K);
+    return launch_status(hipGetLastError(), "x_to_xf");
+}
+
+int qgemm_gemm_xf(int format, int rung, const void *Xf, const void *W, void *Y, int64_t M, int64_t N, int64_t K,
+                  int64_t group_size, int has_zp, int dtype, void *stream)
+{
+    return gemm(format, rung, Xf, W, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream, X_FRAG);
 }
 
 int qgemm_dequant(int format, const void *W, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,

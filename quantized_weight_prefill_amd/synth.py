@@ -206,6 +206,8 @@ def encode(fmt: str, fields: dict):
 #: The named workloads.  Each GEMM is (label, fmt, M, K, N, dtype, group, symmetric);
 #: the seed of workload i is 1000 + i and GEMM j of it draws from sub-stream
 #: pair j of SeedSequence(seed).spawn(2 * len(gemms)) (X first, then W).
+#: "shared_x" maps a GEMM label to the label whose activations it reads (the
+#: projections of one layer that take the same input).
 WORKLOADS = {
     "q4k_small": {  # single Q4_K GEMM, fp16
         "index": 0,
@@ -218,6 +220,8 @@ WORKLOADS = {
     "qwen3_8b_layer_m658": {  # one dense layer's seven linears at 658 prompt tokens, fp16
         "index": 2,
         "gemms": [(name, fmt, QWEN3_8B_PROMPT, K, N, F16, 0, False) for name, K, N, fmt in QWEN3_8B_LAYER],
+        # q, k and v read the same normalized hidden state; gate and up the same MLP input
+        "shared_x": {"k": "q", "v": "q", "up": "gate"},
     },
     "w4a16_g128_m2048": {  # group-wise W4A16, fp16 and bf16, asymmetric and symmetric
         "index": 3,
@@ -237,12 +241,19 @@ WORKLOADS = {
 }
 
 
+def x_source(name: str, j: int) -> int:
+    """Index of the GEMM whose activations GEMM j of a named workload reads."""
+    w = WORKLOADS[name]
+    src = w.get("shared_x", {}).get(w["gemms"][j][0])
+    return j if src is None else [g[0] for g in w["gemms"]].index(src)
+
+
 def workload_inputs(name: str, j: int):
     """(X bits, weight fields, encoded weights) of GEMM j of a named workload."""
     w = WORKLOADS[name]
     label, fmt, M, K, N, dt, group, sym = w["gemms"][j]
     rs = streams(1000 + w["index"], 2 * len(w["gemms"]))
-    X = activations(rs[2 * j], M, K, dt)
+    X = activations(rs[2 * x_source(name, j)], M, K, dt)
     fields = weight_fields(fmt, rs[2 * j + 1], N, K, group or 128, sym)
     return X, fields, encode(fmt, fields)
 

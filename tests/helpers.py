@@ -69,6 +69,14 @@ class Case:
                             has_zp=self.has_zp, out=out)
 
 
+    def run_xf(self, rung: int = -1, out=None):
+        """The same product through the fragment-major path: the library's
+        own copy of X (qgemm_x_to_xf), then qgemm_gemm_xf."""
+        xf = qg.x_to_xf(to_device(self.X, self.dtype))
+        return qg.gemm_xf(self.fmt, xf, self.device_weights(), self.M, self.N, self.K,
+                          group=self.group if self.fmt == "w4a16" else 0, has_zp=self.has_zp, rung=rung, out=out)
+
+
 def ulp_half(y: np.ndarray, dtype: int) -> np.ndarray:
     """Half an ulp of |y| in the output type (the output rounding alone)."""
     a = np.abs(y)

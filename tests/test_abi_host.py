@@ -198,6 +198,22 @@ def test_device_entry_argument_errors():
     assert lib.qgemm_staged(0, A, A, mis, need, A, 4, 20, 512, 0, 0, 0, s) == -4
     assert lib.qgemm_staged(1, A, A, A, need, A, 4, 20, 500, 0, 0, 0, s) == -2
     assert lib.qgemm_staged(2, A, A, A, need, A, 4, 20, 512, 0, 1, 0, s) == -5
+    # fragment-major activations
+    assert lib.qgemm_xf_bytes(1, 128) == 32 * 128 * 2 and lib.qgemm_xf_bytes(33, 256) == 64 * 256 * 2
+    assert lib.qgemm_xf_bytes(0, 128) == 0 and lib.qgemm_xf_bytes(-1, 128) == 0
+    assert lib.qgemm_xf_bytes(4, 200) == 0 and lib.qgemm_xf_bytes(4, 0) == 0
+    assert lib.qgemm_x_to_xf(A, A, 4, 200, s) == -2
+    assert lib.qgemm_x_to_xf(A, A, -1, 128, s) == -2
+    assert lib.qgemm_x_to_xf(None, A, 4, 128, s) == -1
+    assert lib.qgemm_x_to_xf(A, mis, 4, 128, s) == -4
+    assert lib.qgemm_x_to_xf(None, None, 0, 128, s) == 0     # M = 0
+    assert lib.qgemm_gemm_xf(0, -1, None, A, A, 4, 16, 256, 0, 0, 0, s) == -1
+    assert lib.qgemm_gemm_xf(0, -1, mis, A, A, 4, 16, 256, 0, 0, 0, s) == -4
+    assert lib.qgemm_gemm_xf(0, 99, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
+    assert lib.qgemm_gemm_xf(2, -1, A, A, A, 4, 16, 256, 48, 1, 0, s) == -5
+    assert lib.qgemm_gemm_xf(1, -1, A, A, A, 4, 16, 300, 0, 0, 0, s) == -2
+    assert lib.qgemm_gemm_xf(0, -1, A, A, A, 4, 16, 256, 0, 0, 5, s) == -3
+    assert lib.qgemm_gemm_xf(0, -1, None, None, None, 0, 16, 256, 0, 0, 0, s) == 0
 
 
 # ----------------------------------------------------------------------------
@@ -231,6 +247,28 @@ def test_ladder_sweep(fmt, dtype):
             for r in range(qg.num_rungs()):
                 ri = qg.rung_info(r, fmt, M, N, K, dtype)
                 assert ri["tiles_n"] * ri["cols"] >= N and ri["tiles_m"] * ri["rows"] >= M
+
+
+def test_ladder_fragment_major():
+    """The ladder for fragment-major activations: 96-row K-split tiles where
+    they fit one pass over the 256 CUs and keep more of them busy than
+    128-row tiles (the N = 4096 projections at M = 658); otherwise the same
+    rung as for row-major activations."""
+    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-96x128-k2"
+    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-96x128-k2"
+    assert qg.select_rung_xf("q6k", 300, 4096, 12288)["name"] == "mfma32-96x128-k2"   # long K: no direct kernel
+    assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
+    assert qg.select_rung_xf("q4k", 512, 12288, 4096)["name"] == "mfma16-256x128"
+    for fmt, M, K, N in [("q4k", 658, 4096, 12288), ("q4k", 658, 4096, 1024), ("q4k", 16, 4096, 12288),
+                         ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
+                         ("q6k", 1024, 12288, 4096)]:
+        assert qg.select_rung_xf(fmt, M, N, K)["name"] == qg.select_rung(fmt, M, N, K)["name"], (fmt, M, K, N)
+    for K, N in SHAPES:
+        for M in list(range(1, 70)) + [96, 200, 300, 511, 658, 1000, 1024, 4096]:
+            info = qg.select_rung_xf("w4a16", M, N, K)
+            assert info["tiles_n"] * info["cols"] >= N and info["tiles_m"] * info["rows"] >= M
+            if info["name"] == "mfma32-96x128-k2":
+                assert info["tiles_n"] * info["tiles_m"] <= 256
 
 
 def test_ladder_rejects_bad_shapes():

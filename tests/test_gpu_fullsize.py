@@ -1,5 +1,6 @@
-"""Full-size parity for every named workload, in the launch configuration the
-benchmark times (the automatic rung).  The oracle dequantizes all of W and
+"""Full-size parity for every named workload, in the launch configurations the
+benchmark times (the automatic rung, on row-major and on fragment-major
+activations).  The oracle dequantizes all of W and
 computes a seeded sample of outputs one by one; the sample always includes
 the first and last row and column so the M and N tails are covered."""
 from __future__ import annotations
@@ -17,15 +18,18 @@ pytestmark = pytest.mark.gpu
 CASES = [(name, j) for name, w in synth.WORKLOADS.items() for j in range(len(w["gemms"]))]
 
 
+@pytest.mark.parametrize("layout", ["row", "xf"])
 @pytest.mark.parametrize("name,j", CASES, ids=[f"{n}-{synth.WORKLOADS[n]['gemms'][j][0]}" for n, j in CASES])
-def test_workload_sampled(name, j):
+def test_workload_sampled(name, j, layout):
     label, fmt, M, K, N, dt, group, sym = synth.WORKLOADS[name]["gemms"][j]
-    print(f"fullsize {name}/{label} fmt={fmt} M={M} K={K} N={N} dtype={dt}", flush=True)
+    print(f"fullsize {name}/{label} layout={layout} fmt={fmt} M={M} K={K} N={N} dtype={dt}", flush=True)
     X, fields, enc = synth.workload_inputs(name, j)
     packed = qg.pack(fmt, enc, N, K)
     x = to_device(X, dt)
     wp = bytes_to_device(packed)
-    if fmt == "q4k":
+    if layout == "xf":
+        y = qg.gemm_xf(fmt, qg.x_to_xf(x), wp, M, N, K, group=group if fmt == "w4a16" else 0, has_zp=not sym)
+    elif fmt == "q4k":
         y = qg.q4k(x, wp, N)
     elif fmt == "q6k":
         y = qg.q6k(x, wp, N)

@@ -13,7 +13,8 @@ import pytest
 import oracle
 import quantized_weight_prefill_amd as qg
 from quantized_weight_prefill_amd import synth
-from tests.helpers import Case, assert_gemm_close, bytes_to_device, fnv1a64, from_device, same_bits, to_device
+from tests.helpers import (Case, assert_gemm_close, bytes_to_device, fnv1a64, from_device, same_bits, to_device,
+                           torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +113,70 @@ def test_w4a16_small_groups_gemm(dtype):
             y = from_device(c.run(rung))
             Yref, B = oracle.gemm(c.X, c.W, dtype)
             assert_gemm_close(y, Yref, B, dtype, what=f"w4a16 g={group} rung={rung}")
+
+
+# ----------------------------------------------------------------------------
+# fragment-major activations
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_x_to_xf_bitexact(dtype):
+    """The device copy equals the oracle's fragment-major copy bit for bit,
+    padding rows included, and writes nothing past its size."""
+    import torch
+
+    for i, (M, K) in enumerate([(1, 128), (31, 256), (33, 384), (70, 4096), (658, 512), (96, 12288)]):
+        print(f"x_to_xf dtype={dtype} M={M} K={K}", flush=True)
+        X = synth.activations(np.random.default_rng(500 + i), M, K, dtype)
+        n = qg.xf_bytes(M, K) // 2
+        out = torch.full((n + 64,), float("nan"), dtype=torch_dtype(dtype), device="cuda")
+        guard = from_device(out)[n:].copy()
+        qg.x_to_xf(to_device(X, dtype), out=out)
+        got = from_device(out)
+        assert np.array_equal(got[:n], oracle.fragment_major(X)), f"M={M} K={K}"
+        assert np.array_equal(got[n:], guard)
+
+
+@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+@pytest.mark.parametrize("rung", RUNGS)
+def test_gemm_xf_parity(fmt, sym, dtype, rung):
+    """Every rung on fragment-major activations: within the bound of the
+    oracle, and bit-identical to the same rung on row-major activations."""
+    for i, (M, N, K) in enumerate(SHAPES):
+        c = _case(fmt, sym, M, N, K, dtype, seed=200 + i)
+        print(f"xf grid {fmt} sym={sym} dtype={dtype} rung={rung} M={M} N={N} K={K}", flush=True)
+        y = from_device(c.run_xf(rung))
+        Yref, B = oracle.gemm(c.X, c.W, dtype)
+        assert_gemm_close(y, Yref, B, dtype, what=f"xf {fmt} M={M} N={N} K={K} rung={rung}")
+        assert np.array_equal(y, from_device(c.run(rung))), f"xf != row-major: M={M} N={N} K={K} rung={rung}"
+
+
+@pytest.mark.parametrize("rung", RUNGS)
+def test_gemm_xf_odd_chunks_and_ragged(rung):
+    """Fragment-major activations with an odd chunk count (the K-split rungs
+    run unsplit) and with ragged M and N."""
+    for i, (M, N, K) in enumerate([(70, 96, 384), (37, 37, 256), (130, 144, 640), (3, 5, 512)]):
+        fmt = "w4a16" if K % 256 else "q6k"
+        c = _case(fmt, False, M, N, K, qg.BF16, seed=230 + i)
+        print(f"xf odd/ragged {fmt} rung={rung} M={M} N={N} K={K}", flush=True)
+        y = from_device(c.run_xf(rung))
+        Yref, B = oracle.gemm(c.X, c.W, qg.BF16)
+        assert_gemm_close(y, Yref, B, qg.BF16, what=f"xf {fmt} M={M} N={N} K={K} rung={rung}")
+        assert np.array_equal(y, from_device(c.run(rung)))
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+@pytest.mark.parametrize("rung", RUNGS)
+def test_odd_chunk_count(dtype, rung):
+    """W4A16 with K an odd multiple of 128: the K-split rungs fall back to one
+    K group, every other rung walks an odd number of 128-wide chunks."""
+    for i, (M, N, K) in enumerate([(70, 96, 384), (130, 144, 640), (200, 48, 128)]):
+        c = _case("w4a16", i == 1, M, N, K, dtype, seed=215 + i)
+        print(f"odd-chunk dtype={dtype} rung={rung} M={M} N={N} K={K}", flush=True)
+        y = from_device(c.run(rung))
+        Yref, B = oracle.gemm(c.X, c.W, dtype)
+        assert_gemm_close(y, Yref, B, dtype, what=f"w4a16 M={M} N={N} K={K} rung={rung}")
 
 
 @pytest.mark.parametrize("rung", RUNGS)

@@ -473,3 +473,41 @@ def test_gemm_error_rule():
     Yb = synth.f16_bits(np.array([[1.01, 0.0], [2.0, -3.0]]))
     err, zero_ok = oracle.gemm_error(Yb, Yref, B, oracle.F16)
     assert zero_ok and abs(err - abs(float(np.float16(1.01)) - 1.0) / 10.0) < 1e-12
+
+
+# ---- fragment-major activations (a layout of the library under test) ------
+
+@pytest.mark.parametrize("M,K", [(1, 128), (32, 256), (40, 384), (65, 128)])
+def test_fragment_major_is_an_axis_permutation(M, K):
+    """The copy equals X (zero-padded to whole 32-row blocks) with its axes
+    m = 32b + r, k = 128c + 16s + 8h + j reordered to (b, c, s, h, r, j)."""
+    rng = np.random.default_rng(M * 1000 + K)
+    X = rng.integers(0, 1 << 16, (M, K), dtype=np.uint16)
+    Mp = -(-M // 32) * 32
+    Xp = np.zeros((Mp, K), np.uint16)
+    Xp[:M] = X
+    want = Xp.reshape(Mp // 32, 32, K // 128, 8, 2, 8).transpose(0, 2, 3, 4, 1, 5).ravel()
+    assert np.array_equal(oracle.fragment_major(X), want)
+
+
+def test_fragment_major_operand_blocks():
+    """Each 1 KB block is the activation operand of one 32x32x16 MFMA k-step
+    in lane order: lane (r, h) holds row 32b+r, k = 128c + 16s + 8h .. +7
+    (zeros for rows past M)."""
+    M, K = 70, 256
+    rng = np.random.default_rng(77)
+    X = rng.integers(1, 1 << 16, (M, K), dtype=np.uint16)
+    f = oracle.fragment_major(X)
+    assert f.size == 96 * K
+    nch = K // 128
+    for b in range(3):
+        for c in range(nch):
+            for s in range(8):
+                blk = f[((b * nch + c) * 8 + s) * 512:][:512].reshape(64, 8)
+                for lane in range(64):
+                    r, h = lane % 32, lane // 32
+                    m, k0 = 32 * b + r, 128 * c + 16 * s + 8 * h
+                    want = X[m, k0:k0 + 8] if m < M else np.zeros(8, np.uint16)
+                    assert np.array_equal(blk[lane], want), (b, c, s, lane)
+    with pytest.raises(ValueError):
+        oracle.fragment_major(np.zeros((4, 200), np.uint16))

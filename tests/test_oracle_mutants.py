@@ -43,6 +43,10 @@ MUTANTS = [
      ["test_gemm_matches_numpy"]),
     ("ties away from zero", "if (rem > half || (rem == half && (q & 1))) q++;", "if (rem >= half) q++;",
      ["test_rn_f16_matches_numpy"]),
+    ("fragment-major halves and rows transposed", "((k / 8) % 2 * 32 + m % 32) * 8", "((m % 32) * 2 + (k / 8) % 2) * 8",
+     ["test_fragment_major_is_an_axis_permutation", "test_fragment_major_operand_blocks"]),
+    ("fragment-major padding rows not cleared", "out[idx] = m < M ? X[m * K + k] : 0;",
+     "if (m < M) out[idx] = X[m * K + k];", ["test_fragment_major_is_an_axis_permutation"]),
     ("fp16 subnormal grid wrong", "static xval rn_f16(int64_t n, int e) { return round_exact(n, e, 11, -14, 15); }",
      "static xval rn_f16(int64_t n, int e) { return round_exact(n, e, 11, -15, 15); }",
      ["test_rn_f16_matches_numpy"]),
@@ -68,6 +72,8 @@ def test_mutant_is_caught(tmp_path, monkeypatch, name, old, new, catchers):
                 if p is None:
                     if "shape" in fn.__code__.co_varnames[:fn.__code__.co_argcount]:
                         fn(oracle.F16, (5, 48, 512))
+                    elif fn.__code__.co_varnames[:fn.__code__.co_argcount] == ("M", "K"):
+                        fn(40, 384)
                     else:
                         fn()
                 else:
