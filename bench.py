@@ -2,7 +2,10 @@
 
 Default workload: one Qwen3-8B-shaped dense layer's seven linears at M = 658
 prompt tokens, fp16 activations (q/k/v/o/gate/up in Q4_K, down in Q6_K).  A
-step is one pass over the seven GEMMs with inputs already resident in HBM.
+step is one pass over the seven linears with inputs already resident in HBM;
+projections that read the same input run as one GEMM over their weights
+concatenated along N (q/k/v as qkv, gate/up as gate_up; --no-merge runs all
+seven separately).
 By default the GEMMs read fragment-major activations: the step makes that
 copy of each distinct input once (qgemm_x_to_xf: q/k/v share one input,
 gate/up another, o and down one each) and the copies are timed inside the
@@ -22,6 +25,7 @@ Profiling helpers (same JSON line, restricted work):
                         256 MB Infinity Cache cannot serve them
     --rung R            force rung R instead of the M-ladder's choice
     --x-layout xf|row   activation layout the GEMMs read (default xf)
+    --no-merge          seven separate GEMMs instead of qkv, o, gate_up, down
     --copy-calibration BYTES
                         run a plain device-to-device copy of BYTES bytes three
                         times and exit (reference for HBM byte counters)
@@ -94,6 +98,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", default=None, help="run only the GEMM with this label")
     ap.add_argument("--rung", type=int, default=-1, help="force a rung (-1: M-ladder)")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="run the projections that share an input (q/k/v, gate/up) as separate GEMMs")
     ap.add_argument("--x-layout", choices=["xf", "row"], default="xf",
                     help="xf: fragment-major copies made inside the step (default); row: row-major X")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -126,13 +132,15 @@ def main() -> int:
     xf_layout = args.x_layout == "xf"
     inputs = {}  # GEMM index whose activations are read -> its device copies
     gemms = []
-    for j, (label, fmt, M, K, N, dt, group, sym) in enumerate(wl["gemms"]):
+    for sg in synth.step_gemms(args.workload, merge=not args.no_merge):
+        label, fmt, M, K, N = sg["label"], sg["fmt"], sg["M"], sg["K"], sg["N"]
+        dt, group, sym = sg["dt"], sg["group"], sg["sym"]
         if args.only is not None and label != args.only:
             continue
-        X, fields, enc = synth.workload_inputs(args.workload, j)
+        X, enc = synth.step_inputs(args.workload, sg["members"])
         packed = qg.pack(fmt, enc, N, K)
         tdt = torch.float16 if dt == qg.F16 else torch.bfloat16
-        src = synth.x_source(args.workload, j)
+        src = synth.x_source(args.workload, sg["members"][0])
         prep = None
         if src not in inputs:
             x = torch.from_numpy(X.view(np.int16)).view(tdt).to(dev)
@@ -167,7 +175,8 @@ def main() -> int:
                                        K, grp, zp, dt, sp) for w in pool]
         gemms.append(dict(label=label, fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym, x=x, wp=wp, y=y,
                           X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K, wbytes=wbytes, pool=pool, turn=0,
-                          calls=calls, prep=prep, src=src))
+                          calls=calls, prep=prep, src=src,
+                          members=[wl["gemms"][i][0] for i in sg["members"]]))
         print(f"[bench] {label}: {fmt} M={M} K={K} N={N} x={args.x_layout} rung={info['name']}", file=sys.stderr,
               flush=True)
 
@@ -312,7 +321,8 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and value distributions of the workload, random weights)",
         "config": {"workload": args.workload, "gemms": [f"{g['label']}:{g['fmt']}:{g['M']}x{g['K']}x{g['N']}"
                                                        for g in gemms],
-                   "x_layout": "fragment-major (copies made inside the step)" if xf_layout else "row-major"},
+                   "x_layout": "fragment-major (copies made inside the step)" if xf_layout else "row-major",
+                   "merged": {g["label"]: g["members"] for g in gemms if len(g["members"]) > 1}},
         "kernel_ms_per_step": round(kernel_ms_step, 5),
         "per_kernel_timing": "HIP events around every launch in a separate profiling pass; the dominant GEMM's "
                              "time is the mean of events around its launches inside the timed region",

@@ -222,6 +222,9 @@ WORKLOADS = {
         "gemms": [(name, fmt, QWEN3_8B_PROMPT, K, N, F16, 0, False) for name, K, N, fmt in QWEN3_8B_LAYER],
         # q, k and v read the same normalized hidden state; gate and up the same MLP input
         "shared_x": {"k": "q", "v": "q", "up": "gate"},
+        # projections that share an input, run as one GEMM over their weights
+        # concatenated along N (each member's outputs are its own columns)
+        "merged": [("qkv", ("q", "k", "v")), ("gate_up", ("gate", "up"))],
     },
     "w4a16_g128_m2048": {  # group-wise W4A16, fp16 and bf16, asymmetric and symmetric
         "index": 3,
@@ -256,6 +259,58 @@ def workload_inputs(name: str, j: int):
     X = activations(rs[2 * x_source(name, j)], M, K, dt)
     fields = weight_fields(fmt, rs[2 * j + 1], N, K, group or 128, sym)
     return X, fields, encode(fmt, fields)
+
+
+def concat_encoded(fmt: str, encs):
+    """Encoded weights of several N x K matrices (one format) as one matrix of
+    their columns side by side, in the order given."""
+    if fmt in ("q4k", "q6k"):
+        return np.concatenate(encs, axis=0)  # [N][K/256][bytes]: columns are the first axis
+    out = dict(encs[0])
+    out["codes"] = np.concatenate([e["codes"] for e in encs], axis=0)
+    out["scales"] = np.concatenate([e["scales"] for e in encs], axis=1)
+    if out.get("zeros") is not None:
+        out["zeros"] = np.concatenate([e["zeros"] for e in encs], axis=1)
+    return out
+
+
+def step_gemms(name: str, merge: bool = True) -> list[dict]:
+    """The GEMMs of one step of a named workload: with merge, each merged
+    group of the workload is one GEMM over its members' concatenated weights
+    (placed where its first member is), every other GEMM stays as it is.
+    Each entry: label, members (GEMM indices), fmt, M, K, N, dtype, group, sym."""
+    w = WORKLOADS[name]
+    labels = [g[0] for g in w["gemms"]]
+    groups = {}
+    if merge:
+        for lab, members in w.get("merged", []):
+            idx = [labels.index(m) for m in members]
+            first = w["gemms"][idx[0]]
+            for j in idx:
+                g = w["gemms"][j]
+                assert g[1:4] == first[1:4] and g[5:] == first[5:] and x_source(name, j) == x_source(name, idx[0])
+            groups[idx[0]] = (lab, idx)
+    member_of = {j for _, idx in groups.values() for j in idx}
+    out = []
+    for j, (label, fmt, M, K, N, dt, group, sym) in enumerate(w["gemms"]):
+        if j in groups:
+            lab, idx = groups[j]
+            out.append(dict(label=lab, members=idx, fmt=fmt, M=M, K=K, N=sum(w["gemms"][i][4] for i in idx), dt=dt,
+                            group=group, sym=sym))
+        elif j not in member_of:
+            out.append(dict(label=label, members=[j], fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym))
+    return out
+
+
+def step_inputs(name: str, members):
+    """(X bits, encoded weights) of a step GEMM: the members' shared
+    activations and their weights concatenated along N."""
+    encs = []
+    for j in members:
+        X, _, enc = workload_inputs(name, j)
+        encs.append(enc)
+    fmt = WORKLOADS[name]["gemms"][members[0]][1]
+    return X, (encs[0] if len(encs) == 1 else concat_encoded(fmt, encs))
 
 
 # ---------------------------------------------------------------------------

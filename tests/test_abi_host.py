@@ -277,3 +277,31 @@ def test_ladder_rejects_bad_shapes():
     with pytest.raises(qg.QGemmError):
         qg.select_rung("q4k", 16, 512, 1024, dtype=9)
     assert qg.rung_name(-1) is None and qg.rung_name(qg.num_rungs()) is None
+
+
+@pytest.mark.parametrize("fmt,sym", [("q4k", False), ("q6k", False), ("w4a16", False), ("w4a16", True)])
+def test_concat_encoded_columns(fmt, sym):
+    """Weights concatenated along N dequantize to the members' own weights
+    side by side, and pack to the same bytes as packing them jointly."""
+    import oracle
+
+    K, Ns = 512, (48, 16, 32)
+    fields = [synth.weight_fields(fmt, np.random.default_rng(60 + i), n, K, 128, sym) for i, n in enumerate(Ns)]
+    encs = [synth.encode(fmt, f) for f in fields]
+    merged = synth.concat_encoded(fmt, encs)
+    W = oracle.dequant(fmt, merged, sum(Ns), K, qg.F16)
+    edges = np.cumsum((0,) + Ns)
+    for i, e in enumerate(encs):
+        assert np.array_equal(W[:, edges[i]:edges[i + 1]], oracle.dequant(fmt, e, Ns[i], K, qg.F16))
+    packed = qg.pack(fmt, merged, sum(Ns), K)
+    if fmt != "w4a16":  # k-quant panels are whole records: joint packing is the concatenation
+        assert np.array_equal(packed, np.concatenate([qg.pack(fmt, e, n, K) for e, n in zip(encs, Ns)]))
+
+
+def test_step_gemms_merge():
+    sg = synth.step_gemms("qwen3_8b_layer_m658")
+    assert [(g["label"], g["N"]) for g in sg] == [("qkv", 6144), ("o", 4096), ("gate_up", 24576), ("down", 4096)]
+    assert [g["label"] for g in synth.step_gemms("qwen3_8b_layer_m658", merge=False)] == \
+        ["q", "k", "v", "o", "gate", "up", "down"]
+    flops = lambda gs: sum(2 * g["M"] * g["N"] * g["K"] for g in gs)
+    assert flops(sg) == flops(synth.step_gemms("qwen3_8b_layer_m658", merge=False))

@@ -81,3 +81,38 @@ def test_moe_grouped_sampled(name, j):
     rel = np.abs(got - Yref) / B
     print(f"  max rel err {rel.max():.3e}", flush=True)
     assert rel.max() <= GEMM_TOL
+
+
+MERGED = [(name, sg["label"]) for name in synth.WORKLOADS for sg in synth.step_gemms(name) if len(sg["members"]) > 1]
+
+
+@pytest.mark.parametrize("layout", ["row", "xf"])
+@pytest.mark.parametrize("name,label", MERGED, ids=[f"{n}-{lab}" for n, lab in MERGED])
+def test_merged_projection_sampled(name, label, layout):
+    """Projections that share an input run as one GEMM over their weights
+    concatenated along N, as the benchmark launches them: a seeded sample of
+    outputs (first and last rows and columns, and every member's first and
+    last column) against the oracle on the concatenated weights."""
+    sg = [g for g in synth.step_gemms(name) if g["label"] == label][0]
+    fmt, M, K, N, dt = sg["fmt"], sg["M"], sg["K"], sg["N"], sg["dt"]
+    print(f"merged {name}/{label} layout={layout} fmt={fmt} M={M} K={K} N={N}", flush=True)
+    X, enc = synth.step_inputs(name, sg["members"])
+    wp = bytes_to_device(qg.pack(fmt, enc, N, K))
+    x = to_device(X, dt)
+    grp = sg["group"] if fmt == "w4a16" else 0
+    if layout == "xf":
+        y = qg.gemm_xf(fmt, qg.x_to_xf(x), wp, M, N, K, group=grp, has_zp=not sg["sym"])
+    else:
+        y = qg.gemm_rung(fmt, -1, x, wp, N, group=grp, has_zp=not sg["sym"])
+    Y = from_device(y)
+    W = oracle.dequant(fmt, enc, N, K, dt)
+    edges = np.cumsum([0] + [synth.WORKLOADS[name]["gemms"][j][4] for j in sg["members"]])
+    member_cols = np.concatenate([edges[:-1], edges[1:] - 1])
+    rng = np.random.default_rng(4545)
+    count = 3000
+    rows = np.concatenate([rng.integers(0, M, count), [0, M - 1], np.zeros(member_cols.size, np.int64) + M // 2])
+    cols = np.concatenate([rng.integers(0, N, count), [N - 1, 0], member_cols])
+    Yref, B = oracle.gemm_at(X, W, dt, rows, cols)
+    rel = np.abs(oracle.bits_to_double_fast(Y[rows, cols], dt) - Yref) / B
+    print(f"  max rel err {rel.max():.3e}", flush=True)
+    assert rel.max() <= GEMM_TOL
