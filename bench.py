@@ -87,6 +87,50 @@ def measured_traffic(kernel_key: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+class HipTimer:
+    """HIP events for timing only, made with hipEventDisableSystemFence: when
+    such an event is recorded the runtime skips the system-scope fence (an L2
+    writeback and invalidate) that an ordinary event adds between two
+    kernels.  They come from the HIP runtime already loaded in the process
+    (the one PyTorch uses, so streams are shared)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+        rt = ctypes.CDLL(path)
+        rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt, self.events = rt, []
+
+    def pair(self):
+        evs = []
+        for _ in range(2):
+            e = ctypes.c_void_p()
+            if self.rt.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            evs.append(e)
+        self.events += evs
+        return evs
+
+    def record(self, ev, stream):
+        if self.rt.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, e0, e1) -> float:
+        v = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(v), e0, e1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(v.value)
+
+    def close(self):
+        for e in self.events:
+            self.rt.hipEventDestroy(e)
+        self.events = []
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,7 +168,12 @@ def main() -> int:
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
     lib = qg.lib()
-    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    # every launch of the step goes to one stream created here (the null
+    # stream carries the runtime's implicit synchronisation with other streams)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    timer = HipTimer()
 
     def ptr(t):
         return ctypes.c_void_p(t.data_ptr())
@@ -195,7 +244,6 @@ def main() -> int:
         if st != 0:
             raise qg.QGemmError(p["label"], st)
 
-    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         for g in gemms:
             if g["prep"] is not None:
@@ -209,35 +257,32 @@ def main() -> int:
     # events around the dominant GEMM only).
     preps = [g["prep"] for g in gemms if g["prep"] is not None]
     nprof = max(3, min(args.steps, PROFILE_STEPS))
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in gemms]
-          for _ in range(nprof)]
-    evp = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in preps]
-           for _ in range(nprof)]
+    ev = [[timer.pair() for _ in gemms] for _ in range(nprof)]
+    evp = [[timer.pair() for _ in preps] for _ in range(nprof)]
     for s in range(nprof):
         i = 0
         for j, g in enumerate(gemms):
             if g["prep"] is not None:
-                evp[s][i][0].record(stream)
+                timer.record(evp[s][i][0], sp)
                 call_prep(g["prep"])
-                evp[s][i][1].record(stream)
+                timer.record(evp[s][i][1], sp)
                 i += 1
-            ev[s][j][0].record(stream)
+            timer.record(ev[s][j][0], sp)
             call(g)
-            ev[s][j][1].record(stream)
+            timer.record(ev[s][j][1], sp)
     torch.cuda.synchronize()
     per = []
     for i, p in enumerate(preps):
-        ms = float(np.mean([evp[s][i][0].elapsed_time(evp[s][i][1]) for s in range(nprof)]))
+        ms = float(np.mean([timer.ms(*evp[s][i]) for s in range(nprof)]))
         per.append(dict(label=p["label"], M=p["M"], K=p["K"], rung="x_to_xf", ms=round(ms, 5),
                         gbps=round(p["bytes"] / ms / 1e6, 1)))
     per_prep = len(per)
-    gemm_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(nprof)]))
-               for j in range(len(gemms))]
+    gemm_ms = [float(np.mean([timer.ms(*ev[s][j]) for s in range(nprof)])) for j in range(len(gemms))]
     jd = int(np.argmax(gemm_ms))  # the dominant GEMM: largest share of the step
 
     # timed region: K steps back to back; HIP events on the launch stream
     # around every launch of the dominant GEMM
-    evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evd = [timer.pair() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -245,15 +290,15 @@ def main() -> int:
             if g["prep"] is not None:
                 call_prep(g["prep"])
             if j == jd:
-                evd[s][0].record(stream)
+                timer.record(evd[s][0], sp)
                 call(g)
-                evd[s][1].record(stream)
+                timer.record(evd[s][1], sp)
             else:
                 call(g)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    gemm_ms[jd] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evd]))
+    gemm_ms[jd] = float(np.mean([timer.ms(e0, e1) for e0, e1 in evd]))
 
     for j, g in enumerate(gemms):
         ms = gemm_ms[j]
@@ -324,8 +369,9 @@ def main() -> int:
                    "x_layout": "fragment-major (copies made inside the step)" if xf_layout else "row-major",
                    "merged": {g["label"]: g["members"] for g in gemms if len(g["members"]) > 1}},
         "kernel_ms_per_step": round(kernel_ms_step, 5),
-        "per_kernel_timing": "HIP events around every launch in a separate profiling pass; the dominant GEMM's "
-                             "time is the mean of events around its launches inside the timed region",
+        "per_kernel_timing": "HIP events (hipEventDisableSystemFence) on the launch stream around every launch in a "
+                             "separate profiling pass; the dominant GEMM's time is the mean of such events around "
+                             "its launches inside the timed region",
         "per_kernel": per,
         "roofline": roof,
     }

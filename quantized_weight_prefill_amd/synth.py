@@ -235,6 +235,7 @@ WORKLOADS = {
         "index": 4,
         "gemms": [("wide", "q4k", 4096, 4096, 12288, BF16, 0, False),
                   ("skinny", "q4k", 4096, 4096, 32, BF16, 0, False)],
+        "shared_x": {"skinny": "wide"},  # the narrow gate reads the same hidden state
     },
     "small_m_probes": {  # decode-adjacent M on the up (Q4_K) and down (Q6_K) shapes: weight streams
         "index": 5,
