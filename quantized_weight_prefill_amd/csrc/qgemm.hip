@@ -709,27 +709,35 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
     __syncthreads();
 
     // Steady state, branch-free: chunk c is multiplied from LDS buffer c&1
-    // while chunk c+1 (raw bytes already in registers) is unpacked word by
-    // word into buffer (c+1)&1, the activations of chunk c+1 replace those
-    // of chunk c step by step, and the raw bytes of chunk c+2 are requested.
-    // Past the last chunk the indices are clamped: the extra work is
-    // harmless (the buffer written is never read again).
-    for (int c = c_lo; c < c_hi; c++) {
-        const int buf = (c - c_lo) & 1;
+    // while chunk c+1 (raw bytes in registers since the start of chunk c-1)
+    // is unpacked word by word into the other buffer, and the activations
+    // of chunk c+1 replace those of chunk c step by step.  The raw bytes of
+    // chunk c+2 are requested first, into the second register set, so a
+    // whole chunk of MFMAs covers their latency.  Past the last chunk the
+    // indices are clamped: the extra work is harmless (the buffer written is
+    // never read again).
+    RunRaw<FMT> raw2[UPT];
+    auto chunk = [&](int c, int buf, RunRaw<FMT>(&ru)[UPT], RunRaw<FMT>(&rf)[UPT]) {
         const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
         const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
-        RunParams pr[UPT];
 #pragma unroll
-        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(raw[s], src[s], cn);
+        for (int s = 0; s < UPT; s++) src[s].load(cnn, rf[s]);
         u32x4 wcur[WPB], wnxt[WPB];
 #pragma unroll
         for (int pb = 0; pb < WPB; pb++) wcur[pb] = sW[buf][wn * WPB + pb][0][lane];
+        // keep the raw loads and the first LDS reads ahead of everything else
+        // (left alone, the compiler sinks the loads to the end of the chunk)
+        __builtin_amdgcn_sched_barrier(0);
+        RunParams pr[UPT];
+#pragma unroll
+        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(ru[s], src[s], cn);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             if (i < 3) {
 #pragma unroll
                 for (int pb = 0; pb < WPB; pb++) wnxt[pb] = sW[buf][wn * WPB + pb][i + 1][lane];
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
@@ -739,12 +747,13 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 #pragma unroll
             for (int s = 0; s < UPT; s++) {
                 const int pb = (tid + NTG * s) >> 6;
-                sW[buf ^ 1][pb][src[s].g][i * 16 + src[s].col] = unpack_word<FMT, DT>(raw[s], pr[s], i);
+                sW[buf ^ 1][pb][src[s].g][i * 16 + src[s].col] = unpack_word<FMT, DT>(ru[s], pr[s], i);
             }
             if (i < 3) {
 #pragma unroll
                 for (int pb = 0; pb < WPB; pb++) wcur[pb] = wnxt[pb];
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (FMT == FMT_Q4K && DT == DT_BF16) {
             // rare: runs whose d and dmin are too far apart for binary32 are
@@ -756,14 +765,18 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 #pragma unroll
                     for (int i = 0; i < 4; i++)
                         sW[buf ^ 1][pb][src[s].g][i * 16 + src[s].col] =
-                            unpack_word_exact_bf16(raw[s].codes, pr[s].fa, pr[s].nb, i);
+                            unpack_word_exact_bf16(ru[s].codes, pr[s].fa, pr[s].nb, i);
                 }
             }
         }
-#pragma unroll
-        for (int s = 0; s < UPT; s++) src[s].load(cnn, raw[s]);
         __syncthreads();
+    };
+    int c = c_lo;
+    for (; c + 1 < c_hi; c += 2) {
+        chunk(c, 0, raw, raw2);
+        chunk(c + 1, 1, raw2, raw);
     }
+    if (c < c_hi) chunk(c, 0, raw, raw2);
 #pragma unroll
     for (int pb = 0; pb < WPB; pb++)
 #pragma unroll
