@@ -1098,11 +1098,14 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // Waves splitting K inside one direct-kernel workgroup: enough waves in the
 // whole grid to keep every CU streaming (about 2048), at least two chunks
-// per wave, at most eight waves.
-int pick_kw(long long groups, int nch)
+// per wave, at most eight waves.  For decode-adjacent M (a pure weight
+// stream) a wave keeps at least eight chunks once the grid holds 512 waves:
+// with one chunk in flight ahead, shorter K ranges leave the stream idle
+// while each wave starts and drains (measured at M = 1..16).
+int pick_kw(long long groups, int nch, bool stream)
 {
     int kw = 1;
-    while (kw < 8 && groups * kw < 2048 && nch / (2 * kw) >= 2) kw *= 2;
+    while (kw < 8 && groups * kw < 2048 && nch / (2 * kw) >= ((stream && groups * kw >= 512) ? 8 : 2)) kw *= 2;
     return kw;
 }
 
@@ -1154,7 +1157,7 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     pl.cols = 16 * pl.pn;
     pl.tiles_n = (int)pl.grid.x;
     pl.tiles_m = (int)pl.grid.y;
-    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch);
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch, M <= 16);
     pl.waves = pl.kw;
     pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
     return true;
@@ -1165,7 +1168,8 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    direct kernel with all panels per wave (a 128-wide tile would leave most
 //    of the part idle and most of each tile padding);
 //  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
-//    and the kernel is a weight stream; with many panels and 17..32 rows
+//    and the kernel is a weight stream; up to 8 rows, one panel and all
+//    rows per wave (the most waves streaming); with many panels and 17..32 rows
 //    (17..48 for Q4_K), four panels and all rows per wave (each activation
 //    fragment feeds four panels); with many panels or more than 32 rows,
 //    four panels and 16 rows per wave; otherwise one panel per wave and all
@@ -1202,6 +1206,8 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // above 32 rows a one-panel wave carries three or four row blocks of
     // activations per weight run; four panels per wave and a grid over M win
     if (M <= 64) {
+        // up to 8 rows: one panel per wave, the most waves streaming weights
+        if (M <= 8) return RUNG_SMALL_M;
         // (three row blocks per wave only pay off for Q4_K: the other
         // formats' larger raw runs spill at that size)
         if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
@@ -1404,7 +1410,7 @@ Plan grouped_plan(int fmt, long long T, long long E, long long N, long long K)
     pl.pn = 4;
     pl.rb = avg <= 16 ? 1 : (avg <= 32 || fmt != FMT_Q4K) ? 2 : 3;
     pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)(ceil_div(T, 16 * pl.rb) + E), 1);
-    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, (int)(K / kChunk));
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, (int)(K / kChunk), false);
     pl.waves = pl.kw;
     pl.rows = 16 * pl.rb;
     pl.cols = 64;
