@@ -1176,8 +1176,9 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    rows per wave;
 //  * fewer than 128 tiles of 128x128: the direct kernel with four panels and
 //    up to three row blocks per wave keeps more CUs busy;
-//  * at least 512 tiles of 256x128: the 8-wave 256x128 tile on 16x16x32
-//    MFMAs, which unpacks each weight once for 256 rows;
+//  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
+//    for 256 rows) when the occupancy model below has it finish no later
+//    than the 128-row tiles;
 //  * at most 256 tiles of 128x128 over K >= 8192: the 128x128 tile on
 //    32x32x16 MFMAs with K split between two wave groups;
 //  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
@@ -1185,7 +1186,7 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 // On fragment-major activations three crossovers move (the rules are in
 // select_rung): K-split tiles take over from the direct kernel earlier over
 // a long K, 96-row K-split tiles serve shapes whose 128-row tiles leave CUs
-// idle, and the 256-row tile wins every tie of the occupancy model.
+// idle, and the 256-row tile also wins whenever it has 512 tiles.
 // Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
 // of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
 // the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
@@ -1214,6 +1215,10 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
     }
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256), t96 = tn * ((M + 95) / 96);
+    // occupancy model: a 256x128 tile counts as two 128x128 tiles; the
+    // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
+    const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
+    const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
     if (xl == X_FRAG) {
         // fragment-major activations make every activation load one
         // contiguous 1 KB block, which moves the crossovers:
@@ -1224,17 +1229,16 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         //    of them busy than 128-row tiles (each 96-row wave reads three
         //    row blocks of activations per weight fragment);
         if (t96 <= kCUs && t96 > t128) return RUNG_M96_K2;
-        //  * the 256-row tile whenever the occupancy model has it finish no
-        //    later than the 128-row tiles (it unpacks each weight once for
-        //    256 rows; a 256x128 tile counts as two 128x128 tiles);
-        const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
-        const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
+        //  * the 256-row tile at every tie of the occupancy model and
+        //    whenever there are 512 of its tiles (it unpacks each weight
+        //    once for 256 rows).
         if (t256 >= 512 || c256 <= c128) return RUNG_M16_256;
     } else {
         if (t128 < 128) return RUNG_WIDE;
+        // the 256-row tile when the occupancy model has it finish no later
+        // than the 128-row tiles
+        if (c256 <= c128) return RUNG_M16_256;
     }
-    // many 256-row tiles: eight waves at two per SIMD hide the most latency
-    if (t256 >= 512) return RUNG_M16_256;
     // few tiles over a long K: split K inside the workgroup
     if (t128 <= 256 && K >= 8192) return RUNG_M128_K2;
     // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
