@@ -24,8 +24,11 @@
  *   - X is row-major [M][K] contiguous, Y is row-major [M][N] contiguous.
  *     X, Y and Wpacked must be 16-byte aligned; Y must not alias X or W.
  *   - Return value: QGEMM_OK (0) or a negative status.  Argument errors are
- *     found before any launch and leave Y untouched.  A failed launch returns
- *     QGEMM_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     found before any launch and leave Y untouched; a forced rung whose
+ *     grid would not fit one launch (a direct rung with more than 65535 row
+ *     groups of 16 to 64 rows, or more than 2^31-1 streaming tiles) is
+ *     QGEMM_ERR_SHAPE, and the M-ladder never picks one.  A failed launch
+ *     returns QGEMM_ERR_HIP.  Faults inside a kernel surface at the caller's next
  *     synchronisation, as with any HIP launch.  An unsupported format or
  *     dtype is an error, never a silent fallback.
  *

@@ -1109,29 +1109,32 @@ int pick_kw(long long groups, int nch, bool stream)
     return kw;
 }
 
-bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
+// QGEMM_OK, QGEMM_ERR_FORMAT for an unknown rung, or QGEMM_ERR_SHAPE when
+// the grid would exceed what one launch can address (2^31-1 workgroups
+// along x, 65535 along y).
+int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 {
     const long long np = (N + 15) / 16;
     const int nch = (int)(K / kChunk);
     pl = Plan{};
     pl.rung = rung;
     switch (rung) {
-    case RUNG_SMALL_M: {
-        pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4;
-        pl.pn = 1;
-        pl.grid = dim3((unsigned)np, (unsigned)ceil_div(M, 16 * pl.rb), 1);
-        break;
-    }
-    case RUNG_SKINNY_N: {
-        pl.rb = 1;
-        pl.pn = np >= 4 ? 4 : (int)np;
-        pl.grid = dim3((unsigned)ceil_div(np, pl.pn), (unsigned)ceil_div(M, 16), 1);
-        break;
-    }
-    case RUNG_WIDE: {  // each weight run unpacked once for up to 48 rows, each activation fragment used by four panels
-        pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : 3;
-        pl.pn = 4;
-        pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)ceil_div(M, 16 * pl.rb), 1);
+    case RUNG_SMALL_M:
+    case RUNG_SKINNY_N:
+    case RUNG_WIDE: {
+        if (rung == RUNG_SMALL_M) {
+            pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4;
+            pl.pn = 1;
+        } else if (rung == RUNG_SKINNY_N) {
+            pl.rb = 1;
+            pl.pn = np >= 4 ? 4 : (int)np;
+        } else {  // each weight run unpacked once for up to 48 rows, each activation fragment used by four panels
+            pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : 3;
+            pl.pn = 4;
+        }
+        const long long gx = (np + pl.pn - 1) / pl.pn, gy = (M + 16 * pl.rb - 1) / (16 * pl.rb);
+        if (gy > 65535) return QGEMM_ERR_SHAPE;
+        pl.grid = dim3((unsigned)gx, (unsigned)gy, 1);
         break;
     }
     case RUNG_M16_256:
@@ -1144,14 +1147,16 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M96_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
         pl.waves = rung == RUNG_M16_256 ? 8 : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
-        pl.tiles_n = ceil_div(np, pl.cols / 16);
-        pl.tiles_m = ceil_div(M, pl.rows);
-        pl.grid = dim3((unsigned)(pl.tiles_n * pl.tiles_m), 1, 1);
+        const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
+        if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
+        pl.tiles_n = (int)tn;
+        pl.tiles_m = (int)tm;
+        pl.grid = dim3((unsigned)(tn * tm), 1, 1);
         pl.lds = 0;
-        return true;
+        return QGEMM_OK;
     }
     default:
-        return false;
+        return QGEMM_ERR_FORMAT;
     }
     pl.rows = 16 * pl.rb;
     pl.cols = 16 * pl.pn;
@@ -1160,7 +1165,7 @@ bool make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch, M <= 16);
     pl.waves = pl.kw;
     pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
-    return true;
+    return QGEMM_OK;
 }
 
 // The M-ladder (measured on MI355X; each rung is legal for every shape):
@@ -1203,6 +1208,9 @@ double stream_cost(long long M, long long np, int cols)
 int select_rung(int fmt, long long M, long long N, long long K, int xl)
 {
     const long long np = (N + 15) / 16, tn = (np + 7) / 8;
+    // the direct kernels put row groups of 16 on grid.y (at most 65535);
+    // beyond that only the streaming kernels' one-dimensional grid fits
+    if ((M + 15) / 16 > 65535) return fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128) ? RUNG_M128N160 : RUNG_M128;
     if (np <= 4) return RUNG_SKINNY_N;
     // above 32 rows a one-panel wave carries three or four row blocks of
     // activations per weight run; four panels per wave and a grid over M win
@@ -1380,7 +1388,8 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     if (!X || !W || !Y) return QGEMM_ERR_NULL;
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
     Plan pl;
-    if (!make_plan(rung < 0 ? select_rung(fmt, M, N, K, xl) : rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
+    st = make_plan(rung < 0 ? select_rung(fmt, M, N, K, xl) : rung, M, N, K, pl);
+    if (st != QGEMM_OK) return st;
     Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
     a.kw = pl.kw;
     return launch_status(launch(fmt, dtype, xl, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
@@ -1483,7 +1492,7 @@ int staged(int fmt, const void *X, const void *W, void *scratch, size_t scratch_
     if (!aligned16(W) || !aligned16(scratch) || (M > 0 && (!aligned16(X) || !aligned16(Y)))) return QGEMM_ERR_ALIGN;
     if (scratch_bytes < staged_scratch_bytes(N, K)) return QGEMM_ERR_SIZE;
     Plan pl;
-    if (!make_plan(RUNG_M128, M > 0 ? M : 1, N, K, pl)) return QGEMM_ERR_FORMAT;
+    if (int st = make_plan(RUNG_M128, M > 0 ? M : 1, N, K, pl); st != QGEMM_OK) return st;
     Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
     const hipError_t e = dtype == DT_F16 ? launch_staged_dt<DT_F16>(fmt, a, (uint8_t *)scratch, pl, (hipStream_t)stream)
                                          : launch_staged_dt<DT_BF16>(fmt, a, (uint8_t *)scratch, pl, (hipStream_t)stream);
@@ -1555,7 +1564,8 @@ int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int d
     if (st != QGEMM_OK) return st;
     if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
     Plan pl;
-    if (!make_plan(rung, M, N, K, pl)) return QGEMM_ERR_FORMAT;
+    st = make_plan(rung, M, N, K, pl);
+    if (st != QGEMM_OK) return st;
     fill_info(pl, info8);
     return QGEMM_OK;
 }

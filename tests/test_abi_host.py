@@ -271,6 +271,26 @@ def test_ladder_fragment_major():
                 assert info["tiles_n"] * info["tiles_m"] <= 256
 
 
+def test_grid_limits():
+    """Direct rungs put row groups of 16 on grid.y (at most 65535): forcing
+    one past that is a shape error before any launch, and the ladder moves
+    such shapes to a streaming rung (one-dimensional grid)."""
+    lib = qg.lib()
+    A = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    big = 65535 * 64 + 1  # past the limit of every direct rung (up to 64 rows per group)
+    for rung in range(3):  # the three direct rungs
+        assert lib.qgemm_gemm_rung(0, rung, A, A, A, big, 32, 256, 0, 0, 0, None) == -2
+        assert lib.qgemm_gemm_xf(0, rung, A, A, A, big, 32, 256, 0, 0, 0, None) == -2
+        with pytest.raises(qg.QGemmError) as e:
+            qg.rung_info(rung, "q4k", big, 32, 256)
+        assert e.value.status == -2
+    assert qg.rung_info(1, "q4k", 65535 * 16, 32, 256)["tiles_m"] == 65535
+    for M in (65535 * 16 + 1, big, 1 << 24):
+        info = qg.select_rung("q4k", M, 32, 256)
+        assert info["name"].startswith("mfma32-") and info["tiles_m"] * info["rows"] >= M
+        assert not qg.select_rung_xf("q4k", M, 32, 256)["name"].startswith("direct-")
+
+
 def test_ladder_rejects_bad_shapes():
     with pytest.raises(qg.QGemmError):
         qg.select_rung("q4k", 16, 512, 1000)

@@ -116,3 +116,37 @@ def test_merged_projection_sampled(name, label, layout):
     rel = np.abs(oracle.bits_to_double_fast(Y[rows, cols], dt) - Yref) / B
     print(f"  max rel err {rel.max():.3e}", flush=True)
     assert rel.max() <= GEMM_TOL
+
+
+def test_offsets_past_4gib_sampled():
+    """X of 40000 x 65536 fp16 (5.2 GB): row offsets cross 2^32 bytes in both
+    activation layouts.  The rows repeat with period 61, so a wrapped 32-bit
+    offset (2^32 bytes = 32768 rows here) would land on a different row.
+    Sampled rows against the oracle, for the ladder's rung (direct-skinny-n,
+    N = 48) and the 128x128 streaming rung."""
+    import torch
+
+    M, K, N, P = 40000, 65536, 48, 61
+    rng = np.random.default_rng(4646)
+    block = synth.activations(rng, P, K, qg.F16)
+    fields = synth.weight_fields("q4k", rng, N, K, 128, False)
+    enc = synth.encode("q4k", fields)
+    wp = bytes_to_device(qg.pack("q4k", enc, N, K))
+    x = to_device(block, qg.F16).repeat(-(-M // P), 1)[:M]
+    assert x.is_contiguous() and x.numel() * 2 > 2 ** 32
+    xf = qg.x_to_xf(x)
+    W = oracle.dequant("q4k", enc, N, K, qg.F16)
+    Yref, B = oracle.gemm(block, W, qg.F16)
+    rows = np.concatenate([[0, 1, P - 1, P, 32767, 32768, 32769, 65535 // 2, M - 1], rng.integers(0, M, 200)])
+    rung128 = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-128x128"][0]
+    for layout, rung in [("row", -1), ("row", rung128), ("xf", -1), ("xf", rung128)]:
+        print(f"offsets>4GiB layout={layout} rung={rung} M={M} K={K} N={N}", flush=True)
+        if layout == "row":
+            y = qg.gemm_rung("q4k", rung, x, wp, N)
+        else:
+            y = qg.gemm_xf("q4k", xf, wp, M, N, K, rung=rung)
+        Y = from_device(y[torch.from_numpy(rows).cuda()])
+        rel = np.abs(oracle.bits_to_double_fast(Y, qg.F16) - Yref[rows % P]) / B[rows % P]
+        print(f"  max rel err {rel.max():.3e}", flush=True)
+        assert rel.max() <= GEMM_TOL
+        del y
