@@ -940,7 +940,9 @@ k_stream32(Args a)
 {
     using S = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL>;
     constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM, CB = S::CB;
-    static_assert(KS == 1 || CBW * RBW * 16 * NWM * NWN * 64 <= 2 * CB * 8 * 64 * 4, "K-split reduction must fit in LDS");
+    // f32x16 partial sums one K group hands over: one per (wave, block, lane)
+    constexpr int NACC = NWM * NWN * CBW * RBW * 64;
+    static_assert(KS == 1 || NACC * sizeof(f32x16) <= sizeof(typename S::Lds), "K-split reduction must fit in LDS");
     __shared__ typename S::Lds sWall[KS];
 
     const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
@@ -961,20 +963,27 @@ k_stream32(Args a)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0.f;
     S::run(a, sWall[kg], tid, lane, wn, m0, p0, c_lo, c_hi, acc);
-    if constexpr (KS == 2) {
-        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[1][0][0][0][0]);
-        if (kg == 1) {
+    if constexpr (KS > 1) {
+        // K groups 1..KS-1 hand their partial sums to group 0 through the LDS
+        // of groups 1.. (free once every group has passed its last chunk's
+        // barrier); group 0 adds them in group order, independent of timing.
+        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[1]);
+        if (kg > 0) {
 #pragma unroll
             for (int cb = 0; cb < CBW; cb++)
 #pragma unroll
-                for (int rb = 0; rb < RBW; rb++) red[((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
+                for (int rb = 0; rb < RBW; rb++)
+                    red[(kg - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
         }
         __syncthreads();
-        if (kg == 1) return;
+        if (kg > 0) return;
 #pragma unroll
-        for (int cb = 0; cb < CBW; cb++)
+        for (int g = 1; g < KS; g++)
 #pragma unroll
-            for (int rb = 0; rb < RBW; rb++) acc[cb][rb] += red[((w * CBW + cb) * RBW + rb) * 64 + lane];
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    acc[cb][rb] += red[(g - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane];
     }
 #pragma unroll
     for (int cb = 0; cb < CBW; cb++)
@@ -1078,11 +1087,12 @@ enum Rung {
     RUNG_M128_K2 = 5,     // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
     RUNG_M128N160 = 6,    // 32x32x16 MFMA: 128x160, 4 waves of 32x160
     RUNG_M96_K2 = 7,      // 32x32x16 MFMA: 96x128, 4 waves of 96x32, K split over two groups
-    RUNG_COUNT = 8
+    RUNG_M64_K4 = 8,      // 32x32x16 MFMA: 64x64, 2 waves of 32x64, K split over four groups
+    RUNG_COUNT = 9
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
-                                            "mfma32-128x160",    "mfma32-96x128-k2"};
+                                            "mfma32-128x160",    "mfma32-96x128-k2",  "mfma32-64x64-k4"};
 
 struct Plan {
     int rung;
@@ -1141,11 +1151,13 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128:
     case RUNG_M128_K2:
     case RUNG_M128N160:
-    case RUNG_M96_K2: {
-        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M96_K2 ? 96 : 128;
-        pl.cols = rung == RUNG_M128N160 ? 160 : 128;
+    case RUNG_M96_K2:
+    case RUNG_M64_K4: {
+        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M96_K2 ? 96 : rung == RUNG_M64_K4 ? 64 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64_K4 ? 64 : 128;
         pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M96_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
-        pl.waves = rung == RUNG_M16_256 ? 8 : 4 * pl.kw;
+        if (rung == RUNG_M64_K4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
         if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
@@ -1177,8 +1189,9 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    rows per wave (the most waves streaming); with many panels and 17..32 rows
 //    (17..48 for Q4_K), four panels and all rows per wave (each activation
 //    fragment feeds four panels); with many panels or more than 32 rows,
-//    four panels and 16 rows per wave; otherwise one panel per wave and all
-//    rows per wave;
+//    four panels and 16 rows per wave (49..64 rows of Q4_K: 64x64 streaming
+//    tiles, K split four ways); otherwise one panel per wave and all rows per
+//    wave;
 //  * fewer than 128 tiles of 128x128: the direct kernel with four panels and
 //    up to three row blocks per wave keeps more CUs busy;
 //  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
@@ -1220,6 +1233,10 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         // (three row blocks per wave only pay off for Q4_K: the other
         // formats' larger raw runs spill at that size)
         if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
+        // 49..64 rows of Q4_K over many panels: unpack each weight once for
+        // all rows into LDS (64x64 tiles, K split four ways) instead of once
+        // per 16-row group
+        if (np >= 512 && M > 48 && fmt == FMT_Q4K) return RUNG_M64_K4;
         return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
     }
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256), t96 = tn * ((M + 95) / 96);
@@ -1307,6 +1324,14 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
             hipLaunchKernelGGL((k_stream32<FMT, DT, 96, 2, 1, 4, 2, XL>), pl.grid, dim3(512), 0, s, a);
         else
             hipLaunchKernelGGL((k_stream32<FMT, DT, 96, 2, 1, 4, 1, XL>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M64_K4:
+        if ((a.K / kChunk) % 4 == 0)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 2, 1, 4, XL>), pl.grid, dim3(512), 0, s, a);
+        else if (even)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 2, 1, 2, XL>), pl.grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 2, 1, 1, XL>), pl.grid, dim3(128), 0, s, a);
         return hipGetLastError();
     default:
         break;
