@@ -1189,9 +1189,9 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    rows per wave (the most waves streaming); with many panels and 17..32 rows
 //    (17..48 for Q4_K), four panels and all rows per wave (each activation
 //    fragment feeds four panels); with many panels or more than 32 rows,
-//    four panels and 16 rows per wave (49..64 rows of Q4_K: 64x64 streaming
-//    tiles, K split four ways); otherwise one panel per wave and all rows per
-//    wave;
+//    four panels and 16 rows per wave (49..64 rows of Q4_K and 33..64 of
+//    W4A16: 64x64 streaming tiles, K split four ways); otherwise one panel
+//    per wave and all rows per wave;
 //  * fewer than 128 tiles of 128x128: the direct kernel with four panels and
 //    up to three row blocks per wave keeps more CUs busy;
 //  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
@@ -1233,10 +1233,11 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         // (three row blocks per wave only pay off for Q4_K: the other
         // formats' larger raw runs spill at that size)
         if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
-        // 49..64 rows of Q4_K over many panels: unpack each weight once for
-        // all rows into LDS (64x64 tiles, K split four ways) instead of once
-        // per 16-row group
-        if (np >= 512 && M > 48 && fmt == FMT_Q4K) return RUNG_M64_K4;
+        // 49..64 rows of Q4_K (33..64 of W4A16) over many panels: unpack each
+        // weight once for all rows into LDS (64x64 tiles, K split four ways)
+        // instead of once per 16-row group (Q6_K's N = 4096 leaves too few
+        // such tiles)
+        if (np >= 512 && ((fmt == FMT_Q4K && M > 48) || (fmt == FMT_W4 && M > 32))) return RUNG_M64_K4;
         return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
     }
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256), t96 = tn * ((M + 95) / 96);

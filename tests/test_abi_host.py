@@ -243,7 +243,7 @@ def test_ladder_sweep(fmt, dtype):
             if N <= 64:
                 assert info["name"] == "direct-skinny-n"
             elif M <= 64:
-                assert info["name"].startswith("direct-") or (info["name"] == "mfma32-64x64-k4" and M > 48)
+                assert info["name"].startswith("direct-") or (info["name"] == "mfma32-64x64-k4" and M > 32)
             for r in range(qg.num_rungs()):
                 ri = qg.rung_info(r, fmt, M, N, K, dtype)
                 assert ri["tiles_n"] * ri["cols"] >= N and ri["tiles_m"] * ri["rows"] >= M
