@@ -1185,13 +1185,13 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    direct kernel with all panels per wave (a 128-wide tile would leave most
 //    of the part idle and most of each tile padding);
 //  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
-//    and the kernel is a weight stream; up to 8 rows, one panel and all
-//    rows per wave (the most waves streaming); with many panels and 17..32 rows
-//    (17..48 for Q4_K), four panels and all rows per wave (each activation
-//    fragment feeds four panels); with many panels or more than 32 rows,
-//    four panels and 16 rows per wave (49..64 rows of Q4_K and 33..64 of
-//    W4A16: 64x64 streaming tiles, K split four ways); otherwise one panel
-//    per wave and all rows per wave;
+//    and the kernel is a weight stream; up to 8 rows, and with fewer than
+//    512 panels up to 64 rows, one panel and all rows per wave (the most
+//    waves streaming, each weight unpacked once); with many panels: 17..32
+//    rows (17..48 for Q4_K) four panels and all rows per wave (each
+//    activation fragment feeds four panels), 49..64 rows of Q4_K and 33..64
+//    of W4A16 64x64 streaming tiles with K split four ways, otherwise four
+//    panels and 16 rows per wave;
 //  * fewer than 128 tiles of 128x128: the direct kernel with four panels and
 //    up to three row blocks per wave keeps more CUs busy;
 //  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
@@ -1238,7 +1238,9 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         // instead of once per 16-row group (Q6_K's N = 4096 leaves too few
         // such tiles)
         if (np >= 512 && ((fmt == FMT_Q4K && M > 48) || (fmt == FMT_W4 && M > 32))) return RUNG_M64_K4;
-        return (np >= 512 || M > 32) ? RUNG_SKINNY_N : RUNG_SMALL_M;
+        // fewer panels: one panel and all rows per wave (each weight
+        // unpacked once) beats four panels of 16 rows up to 64 rows
+        return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
     }
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256), t96 = tn * ((M + 95) / 96);
     // occupancy model: a 256x128 tile counts as two 128x128 tiles; the
