@@ -939,7 +939,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_wav
 k_stream32(Args a)
 {
     using S = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL>;
-    constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM, CB = S::CB;
+    constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
     // f32x16 partial sums one K group hands over: one per (wave, block, lane)
     constexpr int NACC = NWM * NWN * CBW * RBW * 64;
     static_assert(KS == 1 || NACC * sizeof(f32x16) <= sizeof(typename S::Lds), "K-split reduction must fit in LDS");
@@ -1192,8 +1192,8 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    activation fragment feeds four panels), 49..64 rows of Q4_K and 33..64
 //    of W4A16 64x64 streaming tiles with K split four ways, otherwise four
 //    panels and 16 rows per wave;
-//  * fewer than 128 tiles of 128x128: the direct kernel with four panels and
-//    up to three row blocks per wave keeps more CUs busy;
+//  * fewer than 128 tiles of 128x128: the direct kernels or 64x64 K-split
+//    streaming tiles, by the round model of mid_m_rung;
 //  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
 //    for 256 rows) when the occupancy model below has it finish no later
 //    than the 128-row tiles;
@@ -1201,10 +1201,9 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    32x32x16 MFMAs with K split between two wave groups;
 //  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
 //    whichever the occupancy model below finishes first.
-// On fragment-major activations three crossovers move (the rules are in
-// select_rung): K-split tiles take over from the direct kernel earlier over
-// a long K, 96-row K-split tiles serve shapes whose 128-row tiles leave CUs
-// idle, and the 256-row tile also wins whenever it has 512 tiles.
+// On fragment-major activations two crossovers move (the rules are in
+// select_rung): 96-row K-split tiles serve shapes whose 128-row tiles leave
+// CUs idle, and the 256-row tile also wins whenever it has 512 tiles.
 // Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
 // of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
 // the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
@@ -1216,6 +1215,23 @@ double stream_cost(long long M, long long np, int cols)
     const long long n = (T + kCUs - 1) / kCUs;
     const double t = (n & 1) ? (double)(n - 1) + 1.43 : (double)n;
     return t * cols / 128.0;
+}
+
+// Between decode-adjacent M and 128 tiles of 128x128 three rungs compete:
+// one panel and up to 64 rows per wave (direct-small-m), four panels and 48
+// rows per wave (direct-wide) and 64x64 streaming tiles with K split four
+// ways.  Their workgroups run in rounds of one per CU; a round costs a
+// constant per rung, measured on MI355X with Q4_K at K = 4096 (M = 80..300,
+// N = 1024..12288): 8, 15.5 and 17 microseconds.  The 48-row direct variant
+// spills for Q6_K and W4A16 and is left out for them.
+int mid_m_rung(int fmt, long long M, long long np)
+{
+    const long long g64 = (M + 63) / 64, g48 = (M + 47) / 48, q = (np + 3) / 4;
+    const auto rounds = [](long long wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
+    const double small = 8.0 * rounds(np * g64), k4 = 17.0 * rounds(q * g64);
+    const double wide = fmt == FMT_Q4K ? 15.5 * rounds(q * g48) : 1e30;
+    if (wide <= small && wide <= k4) return RUNG_WIDE;
+    return small <= k4 ? RUNG_SMALL_M : RUNG_M64_K4;
 }
 
 int select_rung(int fmt, long long M, long long N, long long K, int xl)
@@ -1249,10 +1265,8 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
     if (xl == X_FRAG) {
         // fragment-major activations make every activation load one
-        // contiguous 1 KB block, which moves the crossovers:
-        //  * over a long K, K-split tiles beat the direct kernel as soon as
-        //    there are 128 tiles of 96 rows;
-        if (t128 < 128 && !(K >= 8192 && t96 >= 128)) return RUNG_WIDE;
+        // contiguous 1 KB block, which moves two crossovers:
+        if (t128 < 128) return mid_m_rung(fmt, M, np);
         //  * 96-row tiles when they fit one pass over the CUs and keep more
         //    of them busy than 128-row tiles (each 96-row wave reads three
         //    row blocks of activations per weight fragment);
@@ -1262,7 +1276,7 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         //    once for 256 rows).
         if (t256 >= 512 || c256 <= c128) return RUNG_M16_256;
     } else {
-        if (t128 < 128) return RUNG_WIDE;
+        if (t128 < 128) return mid_m_rung(fmt, M, np);
         // the 256-row tile when the occupancy model has it finish no later
         // than the 128-row tiles
         if (c256 <= c128) return RUNG_M16_256;

@@ -249,6 +249,21 @@ def test_ladder_sweep(fmt, dtype):
                 assert ri["tiles_n"] * ri["cols"] >= N and ri["tiles_m"] * ri["rows"] >= M
 
 
+def test_ladder_mid_m_round_model():
+    """Below 128 tiles of 128x128 and above 64 rows the ladder picks among
+    the one-panel direct kernel, the four-panel 48-row direct kernel (Q4_K
+    only) and 64x64 K-split tiles by whole rounds of one workgroup per CU;
+    the expected names are the measured winners on MI355X."""
+    for fmt, M, N, K, want in [("q4k", 128, 1024, 4096, "direct-small-m"), ("q4k", 200, 1024, 4096, "direct-small-m"),
+                               ("q4k", 300, 1024, 4096, "direct-wide"), ("q4k", 200, 4096, 4096, "mfma32-64x64-k4"),
+                               ("q4k", 300, 4096, 4096, "direct-wide"), ("q4k", 80, 6144, 4096, "direct-wide"),
+                               ("q4k", 128, 6144, 4096, "mfma32-64x64-k4"), ("q6k", 80, 4096, 12288, "direct-small-m"),
+                               ("q6k", 128, 4096, 12288, "direct-small-m"), ("q6k", 200, 4096, 12288, "mfma32-64x64-k4"),
+                               ("q4k", 658, 1024, 4096, "direct-wide")]:
+        for sel in (qg.select_rung, qg.select_rung_xf):
+            assert sel(fmt, M, N, K)["name"] == want, (fmt, M, N, K, sel.__name__)
+
+
 def test_ladder_fragment_major():
     """The ladder for fragment-major activations: 96-row K-split tiles where
     they fit one pass over the 256 CUs and keep more of them busy than
@@ -256,7 +271,7 @@ def test_ladder_fragment_major():
     rung as for row-major activations."""
     assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-96x128-k2"
     assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-96x128-k2"
-    assert qg.select_rung_xf("q6k", 300, 4096, 12288)["name"] == "mfma32-96x128-k2"   # long K: no direct kernel
+    assert qg.select_rung_xf("q6k", 300, 4096, 12288)["name"] == "mfma32-64x64-k4"    # round model, below 128 tiles
     assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
     assert qg.select_rung_xf("q4k", 512, 12288, 4096)["name"] == "mfma16-256x128"
     for fmt, M, K, N in [("q4k", 658, 4096, 12288), ("q4k", 658, 4096, 1024), ("q4k", 16, 4096, 12288),
