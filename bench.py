@@ -20,9 +20,9 @@ oracle timed on a bounded sample of the same workload.
 
 Profiling helpers (same JSON line, restricted work):
     --only LABEL        run only that GEMM of the workload
-    --pool-mb MB        weight-bound GEMMs (below the ridge) rotate through copies of
-                        their packed weights totalling >= MB (default 640), so the
-                        256 MB Infinity Cache cannot serve them
+    --pool-mb MB        every GEMM rotates through copies of its packed weights
+                        totalling >= MB (default 640), so the 256 MB Infinity
+                        Cache cannot serve them (0: one copy)
     --rung R            force rung R instead of the M-ladder's choice
     --x-layout xf|row   activation layout the GEMMs read (default xf)
     --no-merge          seven separate GEMMs instead of qkv, o, gate_up, down
@@ -150,8 +150,8 @@ def main() -> int:
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-arm comparison")
     ap.add_argument("--pool-mb", type=float, default=640.0,
-                    help="weight-bound GEMMs rotate through copies of their weights totalling at least this many MB "
-                         "per GEMM, so the 256 MB Infinity Cache cannot hold them (0: no rotation)")
+                    help="every GEMM rotates through copies of its weights totalling at least this many MB, so the "
+                         "256 MB Infinity Cache cannot hold them (0: no rotation)")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
@@ -207,11 +207,12 @@ def main() -> int:
         else:
             info = (qg.select_rung_xf if xf_layout else qg.select_rung)(fmt, M, N, K, dt)
         wbytes = weight_bytes(fmt, N, K, group or 128, sym)
-        # below the ridge the kernel is a weight stream: time it on weights that come from HBM
         intensity = 2.0 * M * N * K / (wbytes + 2 * M * K + 2 * M * N)
-        ncopy = 1
-        if args.pool_mb > 0 and intensity < PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBPS * 1e9):
-            ncopy = max(1, int(np.ceil(args.pool_mb * 1e6 / packed.nbytes)))
+        below_ridge = intensity < PEAK_TFLOPS[dt] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+        # every GEMM rotates through copies of its packed weights (>= --pool-mb
+        # MB), so each launch reads weights the 256 MB Infinity Cache does not
+        # hold, as in a model whose layers' weights far exceed it
+        ncopy = max(1, int(np.ceil(args.pool_mb * 1e6 / packed.nbytes))) if args.pool_mb > 0 else 1
         pool = [wp] + [wp.clone() for _ in range(ncopy - 1)]
         # pre-marshalled C calls (one per weight copy): the GEMM entry point
         # for the layout, rung -1 being the layout's M-ladder
@@ -225,7 +226,7 @@ def main() -> int:
         gemms.append(dict(label=label, fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym, x=x, wp=wp, y=y,
                           X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K, wbytes=wbytes, pool=pool, turn=0,
                           calls=calls, prep=prep, src=src,
-                          members=[wl["gemms"][i][0] for i in sg["members"]]))
+                          members=[wl["gemms"][i][0] for i in sg["members"]], below_ridge=below_ridge))
         print(f"[bench] {label}: {fmt} M={M} K={K} N={N} x={args.x_layout} rung={info['name']}", file=sys.stderr,
               flush=True)
 
@@ -311,7 +312,7 @@ def main() -> int:
     # are also timed back to back (50 launches a sample, median of 5, weights
     # rotating) next to a plain streaming read of the same bytes.
     for g, p in zip(gemms, per[per_prep:]):
-        if len(g["pool"]) > 1:
+        if g["below_ridge"] and len(g["pool"]) > 1:
             samples = []
             for _ in range(5):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -557,12 +558,19 @@ def staged_arm(g, call, reps: int = 20) -> dict:
             samples.append(e0.elapsed_time(e1) / reps)
         return float(np.median(samples))
 
+    # every arm rotates through the same weight copies as the step
+    turn = [0]
+
+    def wp():
+        turn[0] += 1
+        return g["pool"][turn[0] % len(g["pool"])]
+
     fused = timed(lambda: call(g))
-    same_tile = timed(lambda: qg.gemm_rung(g["fmt"], rung128, g["x"], g["wp"], g["N"], group=grp,
+    same_tile = timed(lambda: qg.gemm_rung(g["fmt"], rung128, g["x"], wp(), g["N"], group=grp,
                                            has_zp=not g["sym"], out=g["y"]))
-    staged = timed(lambda: qg.staged(g["fmt"], g["x"], g["wp"], g["N"], scratch=scratch, group=grp,
+    staged = timed(lambda: qg.staged(g["fmt"], g["x"], wp(), g["N"], scratch=scratch, group=grp,
                                      has_zp=not g["sym"], out=g["y"]))
-    unpack = timed(lambda: qg.staged(g["fmt"], x0, g["wp"], g["N"], scratch=scratch, group=grp,
+    unpack = timed(lambda: qg.staged(g["fmt"], x0, wp(), g["N"], scratch=scratch, group=grp,
                                      has_zp=not g["sym"], out=y0))
     wq = g["wbytes"]
     w16 = 2.0 * g["K"] * (-(-g["N"] // 16) * 16)

@@ -809,9 +809,6 @@ struct Stream32 {
     static constexpr int RUNS = PB * 64;        // 32-code weight runs per chunk
     static constexpr int UPT = (RUNS + NTG - 1) / NTG;  // runs per thread per chunk
     static constexpr int UFULL = RUNS / NTG;    // slots every thread fills
-    // activation k-steps held ahead: a whole chunk for one row block, half a
-    // chunk for three (a whole chunk of three row blocks is 96 VGPRs)
-    static constexpr int XD = RBW >= 3 ? 4 : 8;
     static_assert(WPB % 2 == 0 && WM % 32 == 0, "32x32 blocks");
     static_assert(UPT >= 1 && (RUNS - UFULL * NTG) % 64 == 0, "a partial slot must cover whole waves");
     typedef u32x4 Lds[2][CB][8][64];
@@ -827,7 +824,7 @@ struct Stream32 {
         xrow[rb] = XA::row(a, r) + XA::off(8 * (lane >> 5));
     }
 
-    u32x4 xf[RBW][XD];
+    u32x4 xf[RBW][8];
     RunSrc<FMT> src[UPT];
     RunRaw<FMT> raw[UPT];
     int slot_cp[UPT], slot_lane[UPT];
@@ -854,7 +851,7 @@ struct Stream32 {
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
-        for (int ks = 0; ks < XD; ks++) xf[rb][ks] = *(const u32x4 *)(xrow[rb] + XA::chunk(c_lo) + XA::off(16 * ks));
+        for (int ks = 0; ks < 8; ks++) xf[rb][ks] = *(const u32x4 *)(xrow[rb] + XA::chunk(c_lo) + XA::off(16 * ks));
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
         u32x4 f[4];
@@ -897,12 +894,8 @@ struct Stream32 {
 #pragma unroll
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
-                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma32<DT>(wcur[cb], xf[rb][ks % XD], acc[cb][rb]);
-                // the slot just consumed takes the k-step XD ahead
-                if (ks + XD < 8)
-                    xf[rb][ks % XD] = *(const u32x4 *)(xrow[rb] + XA::chunk(c) + XA::off(16 * (ks + XD)));
-                else
-                    xf[rb][ks % XD] = *(const u32x4 *)(xrow[rb] + XA::chunk(cn) + XA::off(16 * (ks + XD - 8)));
+                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma32<DT>(wcur[cb], xf[rb][ks], acc[cb][rb]);
+                xf[rb][ks] = *(const u32x4 *)(xrow[rb] + XA::chunk(cn) + XA::off(16 * ks));
             }
             if ((ks & 1) == 0) {
 #pragma unroll
@@ -1086,13 +1079,12 @@ enum Rung {
     RUNG_M128 = 4,        // 32x32x16 MFMA: 128x128, 4 waves of 32x128
     RUNG_M128_K2 = 5,     // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
     RUNG_M128N160 = 6,    // 32x32x16 MFMA: 128x160, 4 waves of 32x160
-    RUNG_M96_K2 = 7,      // 32x32x16 MFMA: 96x128, 4 waves of 96x32, K split over two groups
-    RUNG_M64_K4 = 8,      // 32x32x16 MFMA: 64x64, 2 waves of 32x64, K split over four groups
-    RUNG_COUNT = 9
+    RUNG_M64_K4 = 7,      // 32x32x16 MFMA: 64x64, 2 waves of 32x64, K split over four groups
+    RUNG_COUNT = 8
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
-                                            "mfma32-128x160",    "mfma32-96x128-k2",  "mfma32-64x64-k4"};
+                                            "mfma32-128x160",    "mfma32-64x64-k4"};
 
 struct Plan {
     int rung;
@@ -1151,11 +1143,10 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128:
     case RUNG_M128_K2:
     case RUNG_M128N160:
-    case RUNG_M96_K2:
     case RUNG_M64_K4: {
-        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M96_K2 ? 96 : rung == RUNG_M64_K4 ? 64 : 128;
+        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : 128;
         pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64_K4 ? 64 : 128;
-        pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M96_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
+        pl.kw = (rung == RUNG_M128_K2 && (K / kChunk) % 2 == 0) ? 2 : 1;
         if (rung == RUNG_M64_K4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
         pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
@@ -1202,8 +1193,8 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
 //    whichever the occupancy model below finishes first.
 // On fragment-major activations two crossovers move (the rules are in
-// select_rung): 96-row K-split tiles serve shapes whose 128-row tiles leave
-// CUs idle, and the 256-row tile also wins whenever it has 512 tiles.
+// select_rung): the K-split 128x128 tile serves every shape with at most 256
+// of its tiles, and the 256-row tile also wins whenever it has 512 tiles.
 // Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
 // of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
 // the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
@@ -1258,31 +1249,19 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         // unpacked once) beats four panels of 16 rows up to 64 rows
         return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
     }
-    const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256), t96 = tn * ((M + 95) / 96);
+    const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     // occupancy model: a 256x128 tile counts as two 128x128 tiles; the
     // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
-    if (xl == X_FRAG) {
-        // fragment-major activations make every activation load one
-        // contiguous 1 KB block, which moves two crossovers:
-        if (t128 < 128) return mid_m_rung(fmt, M, np);
-        //  * 96-row tiles when they fit one pass over the CUs and keep more
-        //    of them busy than 128-row tiles (each 96-row wave reads three
-        //    row blocks of activations per weight fragment);
-        if (t96 <= kCUs && t96 > t128) return RUNG_M96_K2;
-        //  * the 256-row tile at every tie of the occupancy model and
-        //    whenever there are 512 of its tiles (it unpacks each weight
-        //    once for 256 rows).
-        if (t256 >= 512 || c256 <= c128) return RUNG_M16_256;
-    } else {
-        if (t128 < 128) return mid_m_rung(fmt, M, np);
-        // the 256-row tile when the occupancy model has it finish no later
-        // than the 128-row tiles
-        if (c256 <= c128) return RUNG_M16_256;
-    }
-    // few tiles over a long K: split K inside the workgroup
-    if (t128 <= 256 && K >= 8192) return RUNG_M128_K2;
+    if (t128 < 128) return mid_m_rung(fmt, M, np);
+    // the 256-row tile when the occupancy model has it finish no later than
+    // the 128-row tiles (it unpacks each weight once for 256 rows); on
+    // fragment-major activations also whenever it has 512 tiles
+    if (c256 <= c128 || (xl == X_FRAG && t256 >= 512)) return RUNG_M16_256;
+    // few tiles: split K inside the workgroup (on row-major activations only
+    // over a long K, where the halves' activation reloads stay affordable)
+    if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) return RUNG_M128_K2;
     // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
     // runs do not fit that variant's registers)
     if (fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128)) return RUNG_M128N160;
@@ -1335,12 +1314,6 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         return hipGetLastError();
     case RUNG_M128N160:
         hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 10, 4, 1, 1, XL>), pl.grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    case RUNG_M96_K2:
-        if (even)
-            hipLaunchKernelGGL((k_stream32<FMT, DT, 96, 2, 1, 4, 2, XL>), pl.grid, dim3(512), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_stream32<FMT, DT, 96, 2, 1, 4, 1, XL>), pl.grid, dim3(256), 0, s, a);
         return hipGetLastError();
     case RUNG_M64_K4:
         if ((a.K / kChunk) % 4 == 0)

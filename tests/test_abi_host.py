@@ -265,15 +265,17 @@ def test_ladder_mid_m_round_model():
 
 
 def test_ladder_fragment_major():
-    """The ladder for fragment-major activations: 96-row K-split tiles where
-    they fit one pass over the 256 CUs and keep more of them busy than
-    128-row tiles (the N = 4096 projections at M = 658); otherwise the same
-    rung as for row-major activations."""
-    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-96x128-k2"
-    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-96x128-k2"
+    """The ladder for fragment-major activations: the K-split 128x128 tile for
+    every shape with at most 256 of its tiles (row-major only over a long K),
+    the 256-row tile also whenever it has 512 tiles; otherwise the same rung
+    as for row-major activations."""
+    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-128x128-k2"
+    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128-k2"
+    assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"        # row-major: K < 8192
     assert qg.select_rung_xf("q6k", 300, 4096, 12288)["name"] == "mfma32-64x64-k4"    # round model, below 128 tiles
     assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
     assert qg.select_rung_xf("q4k", 512, 12288, 4096)["name"] == "mfma16-256x128"
+    assert qg.select_rung_xf("q4k", 1400, 12288, 4096)["name"] == "mfma16-256x128"    # 576 tiles of 256x128
     for fmt, M, K, N in [("q4k", 658, 4096, 12288), ("q4k", 658, 4096, 1024), ("q4k", 16, 4096, 12288),
                          ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
                          ("q6k", 1024, 12288, 4096)]:
@@ -282,7 +284,7 @@ def test_ladder_fragment_major():
         for M in list(range(1, 70)) + [96, 200, 300, 511, 658, 1000, 1024, 4096]:
             info = qg.select_rung_xf("w4a16", M, N, K)
             assert info["tiles_n"] * info["cols"] >= N and info["tiles_m"] * info["rows"] >= M
-            if info["name"] == "mfma32-96x128-k2":
+            if info["name"] == "mfma32-128x128-k2":
                 assert info["tiles_n"] * info["tiles_m"] <= 256
 
 
