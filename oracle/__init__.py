@@ -42,6 +42,8 @@ def load_library(path: str):
     c_u16p = ctypes.POINTER(ctypes.c_uint16)
     c_dp = ctypes.POINTER(ctypes.c_double)
     c_i64p = ctypes.POINTER(ctypes.c_int64)
+    c_fp = ctypes.POINTER(ctypes.c_float)
+    c_i8p = ctypes.POINTER(ctypes.c_int8)
     i64 = ctypes.c_int64
     sig = {
         "qref_rn_f16": (ctypes.c_uint16, [ctypes.c_double]),
@@ -63,6 +65,14 @@ def load_library(path: str):
         "qref_gemm_at": (ctypes.c_int, [c_u16p, c_u16p, i64, i64, i64, ctypes.c_int, c_i64p, c_i64p, i64,
                                         c_dp, c_dp]),
         "qref_num_threads": (ctypes.c_int, []),
+        "qref_dequant_q4k_f32": (ctypes.c_int, [c_u8p, i64, i64, c_fp]),
+        "qref_dequant_q6k_f32": (ctypes.c_int, [c_u8p, i64, i64, c_fp]),
+        "qref_dequant_w4a16_f32": (ctypes.c_int, [c_u8p, c_u16p, c_u8p, i64, i64, i64, c_fp]),
+        "qref_colscale_i8": (ctypes.c_int, [c_fp, i64, i64, c_fp, c_fp]),
+        "qref_requant_i8": (ctypes.c_int, [c_fp, c_fp, i64, i64, c_i8p]),
+        "qref_quant_rows_i8": (ctypes.c_int, [c_u16p, i64, i64, ctypes.c_int, c_i8p, c_fp]),
+        "qref_gemm_i8": (ctypes.c_int, [c_i8p, c_fp, c_i8p, c_fp, i64, i64, i64, ctypes.c_int, c_u16p]),
+        "qref_fragment_major_i8": (ctypes.c_int, [c_i8p, i64, i64, c_i8p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -256,6 +266,99 @@ def fragment_major(X: np.ndarray) -> np.ndarray:
     out = np.full(((M + 31) // 32) * 32 * K, 0xFFFF, np.uint16)  # every element is written below
     if _load().qref_fragment_major(_p(X, ctypes.c_uint16), M, K, _p(out, ctypes.c_uint16)):
         raise ValueError(f"fragment_major: K = {K} is not a positive multiple of 128")
+    return out
+
+
+# ---- int8-activation variant (qref.c, item 5) -----------------------------
+
+def dequant_f32(fmt: str, enc, N: int, K: int) -> np.ndarray:
+    """Logical W[K][N] as binary32: the exact weight rounded once (float32)."""
+    W = np.empty((K, N), np.float32)
+    lib = _load()
+    if fmt == "q4k":
+        b = _c(enc, np.uint8)
+        assert b.size == N * (K // 256) * 144
+        rc = lib.qref_dequant_q4k_f32(_p(b, ctypes.c_uint8), N, K, _p(W, ctypes.c_float))
+    elif fmt == "q6k":
+        b = _c(enc, np.uint8)
+        assert b.size == N * (K // 256) * 210
+        rc = lib.qref_dequant_q6k_f32(_p(b, ctypes.c_uint8), N, K, _p(W, ctypes.c_float))
+    elif fmt == "w4a16":
+        codes = _c(enc["codes"], np.uint8)
+        scales = _c(enc["scales"], np.uint16)
+        group = int(enc["group"])
+        assert codes.size == N * K and scales.size == (K // group) * N
+        z = None if enc["symmetric"] else _c(enc["zeros"], np.uint8)
+        zp = _p(z, ctypes.c_uint8) if z is not None else ctypes.POINTER(ctypes.c_uint8)()
+        rc = lib.qref_dequant_w4a16_f32(_p(codes, ctypes.c_uint8), _p(scales, ctypes.c_uint16), zp, N, K,
+                                        group, _p(W, ctypes.c_float))
+    else:
+        raise ValueError(f"unknown format {fmt!r}")
+    if rc:
+        raise ValueError(f"dequant_f32({fmt}) failed ({rc})")
+    return W
+
+
+def colscale_i8(W32: np.ndarray):
+    """Per-column (r, s) of binary32 weights W32 [K][N]: r = RN_f32(127/amax),
+    s = RN_f32(amax/127), both 0 for an all-zero column."""
+    W32 = _c(W32, np.float32)
+    K, N = W32.shape
+    r = np.empty(N, np.float32)
+    s = np.empty(N, np.float32)
+    if _load().qref_colscale_i8(_p(W32, ctypes.c_float), N, K, _p(r, ctypes.c_float), _p(s, ctypes.c_float)):
+        raise ValueError("colscale_i8 failed")
+    return r, s
+
+
+def requant_i8(W32: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """int8 weight codes [K][N] = RNE_int(W32 * r[n]) (exact product)."""
+    W32 = _c(W32, np.float32)
+    r = _c(r, np.float32)
+    K, N = W32.shape
+    Q = np.empty((K, N), np.int8)
+    if _load().qref_requant_i8(_p(W32, ctypes.c_float), _p(r, ctypes.c_float), N, K, _p(Q, ctypes.c_int8)):
+        raise ValueError("requant_i8 failed")
+    return Q
+
+
+def quant_rows_i8(X: np.ndarray, dtype: int):
+    """Row quantization of the bit patterns X [M][K]: codes [M][K] (int8) and
+    the per-row scale s = RN_f32(amax/127) (float32)."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    Q = np.empty((M, K), np.int8)
+    s = np.empty(M, np.float32)
+    if _load().qref_quant_rows_i8(_p(X, ctypes.c_uint16), M, K, dtype, _p(Q, ctypes.c_int8), _p(s, ctypes.c_float)):
+        raise ValueError("quant_rows_i8: input holds inf or nan")
+    return Q, s
+
+
+def gemm_i8(Qx: np.ndarray, sx: np.ndarray, Qw: np.ndarray, sw: np.ndarray, dtype: int) -> np.ndarray:
+    """Y [M][N] bit patterns of dtype: RN_t(RN_f32(RN_f32(acc) * RN_f32(sx*sw)))
+    with acc = sum_k Qx[m][k] * Qw[k][n] exactly."""
+    Qx = _c(Qx, np.int8)
+    Qw = _c(Qw, np.int8)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    M, K = Qx.shape
+    K2, N = Qw.shape
+    assert K == K2
+    Y = np.empty((M, N), np.uint16)
+    if _load().qref_gemm_i8(_p(Qx, ctypes.c_int8), _p(sx, ctypes.c_float), _p(Qw, ctypes.c_int8),
+                            _p(sw, ctypes.c_float), M, N, K, dtype, _p(Y, ctypes.c_uint16)):
+        raise ValueError("gemm_i8 failed")
+    return Y
+
+
+def fragment_major_i8(Q: np.ndarray) -> np.ndarray:
+    """The int8 activation codes [M][K] in the library's fragment-major int8
+    layout (flat, 32*ceil(M/32)*K bytes); see qref.c, item 5."""
+    Q = _c(Q, np.int8)
+    M, K = Q.shape
+    out = np.full(((M + 31) // 32) * 32 * K, 0x55, np.int8)  # every byte is written below
+    if _load().qref_fragment_major_i8(_p(Q, ctypes.c_int8), M, K, _p(out, ctypes.c_int8)):
+        raise ValueError(f"fragment_major_i8: K = {K} is not a positive multiple of 32")
     return out
 
 

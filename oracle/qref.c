@@ -38,6 +38,26 @@
  *        ((m/32 * K/128 + k/128) * 8 + (k/16)%8) * 512 + ((k/8)%2 * 32 + m%32) * 8 + k%8
  *     and rows M .. 32*ceil(M/32)-1 are zero.  It only moves bit patterns.
  *
+ *  5. The int8-activation variant (the batched-prefill PR's single-pass row
+ *     quantize feeding an int8-native GEMM, and the prefill post's closing
+ *     remark that activation quantization and weight dequant fusion are one
+ *     idea applied to the two operands).  The pages fix neither the scale
+ *     granularity nor the rounding; the reading implemented here:
+ *       - weights: w32 = RN_f32(exact step-2 value); per output column n,
+ *         amax_n = max_k |w32|, r_n = RN_f32(127/amax_n), s_n = RN_f32(amax_n/127)
+ *         (both 0 when amax_n = 0); qw = RNE_int(w32 * r_n), the product exact;
+ *       - activations: per row m the same with x (exact in binary32):
+ *         r_m = RN_f32(127/amax_m), s_m = RN_f32(amax_m/127), qx = RNE_int(x * r_m);
+ *       - Y[m][n] = RN_t( RN_f32( RN_f32(acc) * RN_f32(s_m * s_n) ) ),
+ *         acc = sum_k qx * qw exactly (an integer).
+ *     127/amax and amax/127 are formed in binary64 and rounded once more to
+ *     binary32; that second rounding is innocuous for a quotient since
+ *     53 >= 2*24 + 2 (Figueroa, "When is double rounding innocuous?", 1995),
+ *     so both equal the exact quotient rounded once.  The int8 activation
+ *     copy also has a fragment-major layout of the library under test:
+ *        Q[m][k] at (m/32)*32*K + (k/32)*1024 + (k/16)%2*512 + (m%32)*16 + k%16,
+ *     rows M .. 32*ceil(M/32)-1 zero.
+ *
  * All 16-bit floating-point values cross this interface as raw bit patterns
  * (uint16_t).  dtype 0 = fp16, 1 = bf16.
  */
@@ -260,36 +280,61 @@ void qref_q6k_fields(const uint8_t *blk, uint16_t *d, int8_t s[16], uint8_t q[25
 /* Unpacked weight values                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* Q4_K: factor*q - bias with factor = d*sc, bias = dmin*m, formed exactly and
- * rounded once into t.  Returns -1 if d or dmin is inf/nan. */
-static int q4k_value(uint16_t d, uint16_t dmin, int sc, int mn, int q, int dtype, uint16_t *out)
+/* Q4_K: factor*q - bias with factor = d*sc, bias = dmin*m, formed exactly.
+ * Returns -1 if d or dmin is inf/nan. */
+static int q4k_exact(uint16_t d, uint16_t dmin, int sc, int mn, int q, xval *v)
 {
     int64_t nd, nm; int ed, em;
     if (f16_split(d, &nd, &ed) || f16_split(dmin, &nm, &em)) return -1;
     int e0 = ed < em ? ed : em;
     int64_t a = (nd * sc * q) * ((int64_t)1 << (ed - e0));
     int64_t b = (nm * mn) * ((int64_t)1 << (em - e0));
-    xval v = {a - b, e0, 0, a < b};
-    *out = enc_t(v, dtype);
+    xval r = {a - b, e0, 0, a < b};
+    *v = r;
     return 0;
 }
 
 /* Q6_K: d*s*(q-32). */
-static int q6k_value(uint16_t d, int s, int q, int dtype, uint16_t *out)
+static int q6k_exact(uint16_t d, int s, int q, xval *v)
 {
     int64_t nd; int ed;
     if (f16_split(d, &nd, &ed)) return -1;
-    xval v = {nd * s * (q - 32), ed, 0, 0};
-    *out = enc_t(v, dtype);
+    xval r = {nd * s * (q - 32), ed, 0, 0};
+    *v = r;
     return 0;
 }
 
 /* W4A16: s*(q-zp). */
-static int w4_value(uint16_t s, int q, int zp, int dtype, uint16_t *out)
+static int w4_exact(uint16_t s, int q, int zp, xval *v)
 {
     int64_t ns; int es;
     if (f16_split(s, &ns, &es)) return -1;
-    xval v = {ns * (q - zp), es, 0, 0};
+    xval r = {ns * (q - zp), es, 0, 0};
+    *v = r;
+    return 0;
+}
+
+/* The exact values rounded once into t. */
+static int q4k_value(uint16_t d, uint16_t dmin, int sc, int mn, int q, int dtype, uint16_t *out)
+{
+    xval v;
+    if (q4k_exact(d, dmin, sc, mn, q, &v)) return -1;
+    *out = enc_t(v, dtype);
+    return 0;
+}
+
+static int q6k_value(uint16_t d, int s, int q, int dtype, uint16_t *out)
+{
+    xval v;
+    if (q6k_exact(d, s, q, &v)) return -1;
+    *out = enc_t(v, dtype);
+    return 0;
+}
+
+static int w4_value(uint16_t s, int q, int zp, int dtype, uint16_t *out)
+{
+    xval v;
+    if (w4_exact(s, q, zp, &v)) return -1;
     *out = enc_t(v, dtype);
     return 0;
 }
@@ -448,6 +493,198 @@ int qref_fragment_major(const uint16_t *X, int64_t M, int64_t K, uint16_t *out)
             const int64_t idx = ((m / 32 * (K / 128) + k / 128) * 8 + (k / 16) % 8) * 512
                                 + ((k / 8) % 2 * 32 + m % 32) * 8 + k % 8;
             out[idx] = m < M ? X[m * K + k] : 0;
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 5. int8-activation variant                                               */
+/* ------------------------------------------------------------------------ */
+
+/* An exact value rounded once into binary32 (never overflows here: every
+ * weight is below 2^27 in magnitude). */
+static float f32_of(xval v)
+{
+    xval r = rn_f32(v.n, v.e);
+    if (r.n == 0) return v.neg ? -0.0f : 0.0f;
+    return (float)ldexp((double)r.n, r.e);
+}
+
+/* Weights as binary32, logical W[K][N]: w32 = RN_f32(exact value). */
+int qref_dequant_q4k_f32(const uint8_t *blocks, int64_t N, int64_t K, float *W)
+{
+    if (K % 256) return -2;
+    int64_t nb = K / 256;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        uint16_t d, dmin;
+        uint8_t sc[8], mn[8], q[256];
+        for (int64_t b = 0; b < nb; b++) {
+            qref_q4k_fields(blocks + (n * nb + b) * 144, &d, &dmin, sc, mn, q);
+            for (int k = 0; k < 256; k++) {
+                xval v = {0, 0, 0, 0};
+                bad |= q4k_exact(d, dmin, sc[k / 32], mn[k / 32], q[k], &v) != 0;
+                W[(b * 256 + k) * N + n] = f32_of(v);
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+int qref_dequant_q6k_f32(const uint8_t *blocks, int64_t N, int64_t K, float *W)
+{
+    if (K % 256) return -2;
+    int64_t nb = K / 256;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++) {
+        uint16_t d;
+        int8_t s[16];
+        uint8_t q[256];
+        for (int64_t b = 0; b < nb; b++) {
+            qref_q6k_fields(blocks + (n * nb + b) * 210, &d, s, q);
+            for (int k = 0; k < 256; k++) {
+                xval v = {0, 0, 0, 0};
+                bad |= q6k_exact(d, s[k / 16], q[k], &v) != 0;
+                W[(b * 256 + k) * N + n] = f32_of(v);
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+int qref_dequant_w4a16_f32(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                           int64_t N, int64_t K, int64_t group, float *W)
+{
+    if (group <= 0 || K % group) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            int64_t gi = k / group;
+            int zp = zeros ? zeros[gi * N + n] : 8;
+            xval v = {0, 0, 0, 0};
+            bad |= w4_exact(scales[gi * N + n], codes[n * K + k], zp, &v) != 0;
+            W[k * N + n] = f32_of(v);
+        }
+    return bad ? -1 : 0;
+}
+
+/* Nearest integer, ties to even, of a double that is an exact product. */
+static double rne_int(double v)
+{
+    double f = floor(v), diff = v - f;  /* both exact */
+    if (diff > 0.5) return f + 1.0;
+    if (diff < 0.5) return f;
+    return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+/* r = RN_f32(127/amax), s = RN_f32(amax/127); both 0 when amax is 0. */
+static void i8_scales(double amax, float *r, float *s)
+{
+    if (amax == 0.0) {
+        *r = 0.0f;
+        *s = 0.0f;
+        return;
+    }
+    *r = (float)(127.0 / amax);
+    *s = (float)(amax / 127.0);
+}
+
+/* code = clamp(RNE_int(v * r), -127, 127); v * r is exact in binary64
+ * (two binary32 significands). */
+static int8_t i8_code(double v, float r)
+{
+    double c = rne_int(v * (double)r);
+    if (c > 127.0) c = 127.0;
+    if (c < -127.0) c = -127.0;
+    return (int8_t)c;
+}
+
+/* Per-column scales of binary32 weights W[K][N]. */
+int qref_colscale_i8(const float *W, int64_t N, int64_t K, float *r, float *s)
+{
+    if (N < 0 || K <= 0) return -2;
+    for (int64_t n = 0; n < N; n++) {
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; k++) amax = fmax(amax, fabs((double)W[k * N + n]));
+        i8_scales(amax, &r[n], &s[n]);
+    }
+    return 0;
+}
+
+/* int8 weight codes Q[K][N] = RNE_int(W[k][n] * r[n]). */
+int qref_requant_i8(const float *W, const float *r, int64_t N, int64_t K, int8_t *Q)
+{
+    if (N < 0 || K <= 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; k++)
+        for (int64_t n = 0; n < N; n++) Q[k * N + n] = i8_code((double)W[k * N + n], r[n]);
+    return 0;
+}
+
+/* Row quantization of X[M][K] (bit patterns of dtype): codes Q[M][K], scales s[M]. */
+int qref_quant_rows_i8(const uint16_t *X, int64_t M, int64_t K, int dtype, int8_t *Q, float *s)
+{
+    if (M < 0 || K <= 0) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; m++) {
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double x = t_to_double(X[m * K + k], dtype);
+            bad |= !isfinite(x);
+            amax = fmax(amax, fabs(x));
+        }
+        float r;
+        i8_scales(amax, &r, &s[m]);
+        for (int64_t k = 0; k < K; k++) Q[m * K + k] = i8_code(t_to_double(X[m * K + k], dtype), r);
+    }
+    return bad ? -1 : 0;
+}
+
+/* binary32 value -> (24-bit integer significand, exponent). */
+static xval f32_split(float f)
+{
+    xval v = {0, 0, 0, signbit(f) != 0};
+    if (f == 0.0f) return v;
+    int ex;
+    double fr = frexp((double)f, &ex);
+    v.n = (int64_t)ldexp(fr, 24);
+    v.e = ex - 24;
+    return v;
+}
+
+/* Y[M][N] (bit patterns of dtype) = RN_t(RN_f32(RN_f32(acc) * RN_f32(sx[m]*sw[n]))),
+ * acc = sum_k Qx[m][k] * Qw[k][n] exactly.  Qx [M][K], Qw [K][N]. */
+int qref_gemm_i8(const int8_t *Qx, const float *sx, const int8_t *Qw, const float *sw,
+                 int64_t M, int64_t N, int64_t K, int dtype, uint16_t *Y)
+{
+    if (M < 0 || N < 0 || K <= 0) return -2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; k++) acc += (int64_t)Qx[m * K + k] * Qw[k * N + n];
+            xval a = rn_f32(acc, 0);
+            xval x = f32_split(sx[m]), w = f32_split(sw[n]);
+            xval sc = rn_f32(x.n * w.n, x.e + w.e);
+            xval y = rn_f32(a.n * sc.n, a.e + sc.e);
+            Y[m * N + n] = enc_t(y, dtype);
+        }
+    return 0;
+}
+
+/* The int8 activation codes in the fragment-major layout (item 5). */
+int qref_fragment_major_i8(const int8_t *Q, int64_t M, int64_t K, int8_t *out)
+{
+    if (M < 0 || K <= 0 || K % 32 != 0) return 1;
+    const int64_t Mp = (M + 31) / 32 * 32;
+    for (int64_t m = 0; m < Mp; m++)
+        for (int64_t k = 0; k < K; k++) {
+            const int64_t idx = m / 32 * 32 * K + k / 32 * 1024 + (k / 16) % 2 * 512 + m % 32 * 16 + k % 16;
+            out[idx] = m < M ? Q[m * K + k] : 0;
         }
     return 0;
 }

@@ -511,3 +511,235 @@ def test_fragment_major_operand_blocks():
                     assert np.array_equal(blk[lane], want), (b, c, s, lane)
     with pytest.raises(ValueError):
         oracle.fragment_major(np.zeros((4, 200), np.uint16))
+
+
+# ----------------------------------------------------------------------------
+# int8-activation variant (qref.c item 5): binary32 weights, per-column and
+# per-row scales, int8 codes, integer GEMM with a binary32 epilogue
+# ----------------------------------------------------------------------------
+
+def _rne_int(x: Fraction) -> int:
+    """Nearest integer to an exact rational, ties to even."""
+    f = math.floor(x)
+    d = x - f
+    if d > Fraction(1, 2):
+        return f + 1
+    if d < Fraction(1, 2):
+        return f
+    return f if f % 2 == 0 else f + 1
+
+
+def _f32(x: Fraction) -> Fraction:
+    return Fraction(float(nearest_even(x, "f32")))
+
+
+def _amax_samples(rng):
+    vals = [1.0, 127.0, 254.0, 0.5, 3.0, 2.0 ** -14, 2.0 ** -20, 65504.0, 1e-3, 7.25]
+    vals += list(np.float32(rng.uniform(1e-3, 40.0, 200)))
+    vals += list(np.float32(np.exp2(rng.uniform(-30, 30, 200))))
+    return [float(np.float32(v)) for v in vals]
+
+
+def test_i8_scales_exact_rationals():
+    """r = RN_f32(127/amax) and s = RN_f32(amax/127), checked against the exact
+    quotient rounded by brute-force nearest search; a zero column gives 0, 0."""
+    rng = np.random.default_rng(501)
+    for amax in _amax_samples(rng):
+        W = np.array([[amax], [-amax / 2], [0.0]], np.float32)
+        r, s = oracle.colscale_i8(W)
+        assert Fraction(float(r[0])) == _f32(Fraction(127) / Fraction(amax)), amax
+        assert Fraction(float(s[0])) == _f32(Fraction(amax) / 127), amax
+        Wn = -W  # the column's extreme is negative now
+        r2, s2 = oracle.colscale_i8(Wn)
+        assert r2[0] == r[0] and s2[0] == s[0]
+    r, s = oracle.colscale_i8(np.zeros((5, 3), np.float32))
+    assert not r.any() and not s.any()
+
+
+def test_i8_codes_ties_and_range():
+    """Row amax 127 makes r = s = 1 exactly, so the codes are the values
+    rounded to the nearest integer, ties to even (the pages' RNE reading)."""
+    vals = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, 126.5, -127.0, 0.0, -1.25, 64.75]
+    want = [127, 2, 4, -2, -4, 0, 0, 2, 126, -127, 0, -1, 65]
+    X = synth.f16_bits(np.array([vals]))
+    Q, s = oracle.quant_rows_i8(X, oracle.F16)
+    assert Q.tolist() == [want] and s[0] == np.float32(1.0)
+    # amax 254: r = 1/2, so x = 5 -> 2.5 -> 2 and x = 7 -> 3.5 -> 4
+    X = synth.f16_bits(np.array([[254.0, 5.0, 7.0, -5.0, 1.0]]))
+    Q, s = oracle.quant_rows_i8(X, oracle.F16)
+    assert Q.tolist() == [[127, 2, 4, -2, 0]] and s[0] == np.float32(2.0)
+    # an all-zero row: codes 0, scale 0
+    Q, s = oracle.quant_rows_i8(np.zeros((2, 64), np.uint16), oracle.BF16)
+    assert not Q.any() and not s.any()
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_i8_codes_exact_rationals(dtype):
+    """Every code is RNE(x * r) of the exact product, within [-127, 127], and
+    the element of largest magnitude gets +-127."""
+    rng = np.random.default_rng(502 + dtype)
+    X = synth.activations(rng, 6, 256, dtype)
+    X[3, 17] = X[3, 17] ^ 0x8000  # flip one sign: extremes of both signs
+    Q, s = oracle.quant_rows_i8(X, dtype)
+    xd = oracle.bits_to_double_fast(X, dtype)
+    for m in range(X.shape[0]):
+        amax = Fraction(float(np.abs(xd[m]).max()))
+        r = _f32(Fraction(127) / amax)
+        assert Fraction(float(s[m])) == _f32(amax / 127)
+        for k in range(0, 256, 3):
+            assert int(Q[m, k]) == _rne_int(Fraction(float(xd[m, k])) * r), (m, k)
+        assert abs(int(Q[m, int(np.abs(xd[m]).argmax())])) == 127
+        assert np.abs(Q[m].astype(int)).max() == 127
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16"])
+def test_dequant_f32_matches_exact(fmt):
+    """Binary32 weights are the exact weight rounded once to binary32; at the
+    pages' distributions that rounding is exact, and the fp16 dequant of the
+    same weight is the binary32 value rounded once more."""
+    rng = np.random.default_rng(503)
+    N, K = 24, 512
+    f = synth.weight_fields(fmt, rng, N, K, 128, False)
+    enc = synth.encode(fmt, f)
+    W32 = oracle.dequant_f32(fmt, enc, N, K)
+    W16 = oracle.dequant(fmt, enc, N, K, oracle.F16)
+    assert np.array_equal(W32.astype(np.float16).view(np.uint16), W16)
+    for k in range(0, K, 5):
+        for n in range(0, N, 3):
+            if fmt == "q4k":
+                b, kk = divmod(k, 256)
+                j = kk // 32
+                exact = (f16_val(int(f["d"][n, b])) * int(f["sc"][n, b, j]) * int(f["q"][n, k])
+                         - f16_val(int(f["dmin"][n, b])) * int(f["m"][n, b, j]))
+            elif fmt == "q6k":
+                b, kk = divmod(k, 256)
+                exact = f16_val(int(f["d"][n, b])) * int(f["s"][n, b, kk // 16]) * (int(f["q"][n, k]) - 32)
+            else:
+                gi = k // 128
+                exact = f16_val(int(f["scales"][gi, n])) * (int(f["codes"][n, k]) - int(f["zeros"][gi, n]))
+            assert Fraction(float(W32[k, n])) == exact, (k, n)
+
+
+def test_dequant_f32_rounds_once():
+    """With d and dmin far apart the exact Q4_K weight needs more than 24 bits:
+    the binary32 weight is then its nearest binary32 value."""
+    rng = np.random.default_rng(504)
+    N, K = 8, 256
+    f = synth.q4k_fields(rng, N, K)
+    f["d"][:] = synth.f16_bits(rng.uniform(0.5, 8.0, f["d"].shape))
+    f["dmin"][:] = synth.f16_bits(rng.uniform(2.0 ** -20, 2.0 ** -12, f["dmin"].shape))
+    W32 = oracle.dequant_f32("q4k", synth.q4k_encode(f), N, K)
+    inexact = 0
+    for n in range(N):
+        for k in range(K):
+            j = k // 32
+            exact = (f16_val(int(f["d"][n, 0])) * int(f["sc"][n, 0, j]) * int(f["q"][n, k])
+                     - f16_val(int(f["dmin"][n, 0])) * int(f["m"][n, 0, j]))
+            got = Fraction(float(W32[k, n]))
+            inexact += got != exact
+            assert got == _f32(exact), (n, k)
+    assert inexact > 0
+
+
+def test_requant_i8_exact_rationals():
+    """Weight codes are RNE(w * r_n) of the exact product; each column's
+    largest-magnitude weight gets +-127; a constant column is all 127."""
+    rng = np.random.default_rng(505)
+    N, K = 12, 512
+    f = synth.q4k_fields(rng, N, K)
+    W32 = oracle.dequant_f32("q4k", synth.q4k_encode(f), N, K)
+    W32[:, 5] = np.float32(0.3)
+    r, s = oracle.colscale_i8(W32)
+    Q = oracle.requant_i8(W32, r)
+    assert (Q[:, 5] == 127).all()
+    for n in range(N):
+        assert abs(int(Q[int(np.abs(W32[:, n]).argmax()), n])) == 127
+        for k in range(0, K, 7):
+            assert int(Q[k, n]) == _rne_int(Fraction(float(W32[k, n])) * Fraction(float(r[n]))), (k, n)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_gemm_i8_unit_scales_is_integer_dot(dtype):
+    """With unit scales the output is the integer dot product (numpy int64
+    matmul) rounded to binary32 and then to the output type."""
+    rng = np.random.default_rng(506 + dtype)
+    M, N, K = 7, 9, 1024
+    Qx = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    Qw = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    Qx[:, :40] = 127  # push some sums past 2^24 / 2^11 so both roundings act
+    Qw[:40, :] = 127
+    one = np.ones(M, np.float32), np.ones(N, np.float32)
+    Y = oracle.gemm_i8(Qx, one[0], Qw, one[1], dtype)
+    acc = Qx.astype(np.int64) @ Qw.astype(np.int64)
+    y32 = acc.astype(np.float32)
+    if dtype == oracle.F16:
+        with np.errstate(over="ignore"):  # sums past 65504 become inf in both
+            want = y32.astype(np.float16).view(np.uint16)
+    else:
+        want = torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(Y, want)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_gemm_i8_scaled_matches_numpy_binary32(dtype):
+    """Scaled epilogue against numpy's own binary32 arithmetic: RN_f32(acc),
+    RN_f32(sx*sw), their RN_f32 product, then RN_t."""
+    rng = np.random.default_rng(508 + dtype)
+    M, N, K = 11, 13, 768
+    Qx = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    Qw = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    sx = np.float32(rng.uniform(1e-3, 0.1, M))
+    sw = np.float32(np.exp2(rng.uniform(-14, -4, N)))
+    Y = oracle.gemm_i8(Qx, sx, Qw, sw, dtype)
+    acc = (Qx.astype(np.int64) @ Qw.astype(np.int64)).astype(np.float32)
+    y32 = acc * (sx[:, None] * sw[None, :])
+    assert y32.dtype == np.float32
+    if dtype == oracle.F16:
+        want = y32.astype(np.float16).view(np.uint16)
+    else:
+        want = torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(Y, want)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16"])
+def test_gemm_i8_chain_close_to_fp64_product(fmt):
+    """The whole int8 chain stays within its quantization error of the exact
+    product X . W: |Y - XW| <= sum_k (|x| sw/2 + sx/2 |w| + sx sw/4) plus the
+    binary32 and output roundings (a bound from the definitions alone)."""
+    rng = np.random.default_rng(510)
+    M, N, K = 9, 20, 512
+    X = synth.activations(rng, M, K, oracle.F16)
+    f = synth.weight_fields(fmt, rng, N, K, 128, False)
+    enc = synth.encode(fmt, f)
+    W32 = oracle.dequant_f32(fmt, enc, N, K)
+    r, sw = oracle.colscale_i8(W32)
+    Qw = oracle.requant_i8(W32, r)
+    Qx, sx = oracle.quant_rows_i8(X, oracle.F16)
+    Y = oracle.bits_to_double_fast(oracle.gemm_i8(Qx, sx, Qw, sw, oracle.F16), oracle.F16)
+    xd = oracle.bits_to_double_fast(X, oracle.F16)
+    wd = W32.astype(np.float64)
+    exact = xd @ wd
+    sxd, swd = sx.astype(np.float64), sw.astype(np.float64)
+    # 1/r and s differ by at most a few binary32 ulps: allow 1e-6 relative slack
+    q_err = (np.abs(xd) @ np.ones((K, N)) * swd[None, :] / 2 + sxd[:, None] / 2 * (np.ones((M, K)) @ np.abs(wd))
+             + K * sxd[:, None] * swd[None, :] / 4) * (1 + 1e-6)
+    bound = q_err + np.abs(exact) * 3e-7 + np.abs(Y) * 2.0 ** -11
+    assert (np.abs(Y - exact) <= bound).all()
+    # and the bound is not vacuous: the error is a small fraction of |X||W|
+    assert (np.abs(Y - exact) <= 0.05 * (np.abs(xd) @ np.abs(wd))).all()
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (32, 256), (40, 384), (65, 128)])
+def test_fragment_major_i8_is_an_axis_permutation(M, K):
+    """The int8 copy equals the codes (zero-padded to whole 32-row blocks) with
+    their axes m = 32b + r, k = 32s + 16h + j reordered to (b, s, h, r, j):
+    each 1 KB is one 32x32x32 int8 MFMA operand in lane order."""
+    rng = np.random.default_rng(M * 100 + K)
+    Q = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    Mp = -(-M // 32) * 32
+    Qp = np.zeros((Mp, K), np.int8)
+    Qp[:M] = Q
+    want = Qp.reshape(Mp // 32, 32, K // 32, 2, 16).transpose(0, 2, 3, 1, 4).ravel()
+    assert np.array_equal(oracle.fragment_major_i8(Q), want)
+    with pytest.raises(ValueError):
+        oracle.fragment_major_i8(np.zeros((4, 48), np.int8))

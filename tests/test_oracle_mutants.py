@@ -47,6 +47,20 @@ MUTANTS = [
      ["test_fragment_major_is_an_axis_permutation", "test_fragment_major_operand_blocks"]),
     ("fragment-major padding rows not cleared", "out[idx] = m < M ? X[m * K + k] : 0;",
      "if (m < M) out[idx] = X[m * K + k];", ["test_fragment_major_is_an_axis_permutation"]),
+    ("i8 ties away from zero", "return fmod(f, 2.0) == 0.0 ? f : f + 1.0;", "return f + 1.0;",
+     ["test_i8_codes_ties_and_range"]),
+    ("i8 scale over 255 levels", "*r = (float)(127.0 / amax);", "*r = (float)(255.0 / amax);",
+     ["test_i8_scales_exact_rationals", "test_i8_codes_ties_and_range"]),
+    ("i8 output scale inverted", "*s = (float)(amax / 127.0);", "*s = (float)(127.0 / amax);",
+     ["test_i8_scales_exact_rationals", "test_gemm_i8_chain_close_to_fp64_product"]),
+    ("i8 gemm drops the weight scale", "xval sc = rn_f32(x.n * w.n, x.e + w.e);", "xval sc = x;",
+     ["test_gemm_i8_scaled_matches_numpy_binary32"]),
+    ("i8 gemm weight codes transposed", "acc += (int64_t)Qx[m * K + k] * Qw[k * N + n];",
+     "acc += (int64_t)Qx[m * K + k] * Qw[n * K + k];", ["test_gemm_i8_unit_scales_is_integer_dot"]),
+    ("i8 binary32 weights rounded to bf16", "xval r = rn_f32(v.n, v.e);", "xval r = rn_bf16(v.n, v.e);",
+     ["test_dequant_f32_matches_exact"]),
+    ("i8 fragment-major halves and rows transposed", "(k / 16) % 2 * 512 + m % 32 * 16",
+     "m % 32 * 32 + (k / 16) % 2 * 16", ["test_fragment_major_i8_is_an_axis_permutation"]),
     ("fp16 subnormal grid wrong", "static xval rn_f16(int64_t n, int e) { return round_exact(n, e, 11, -14, 15); }",
      "static xval rn_f16(int64_t n, int e) { return round_exact(n, e, 11, -15, 15); }",
      ["test_rn_f16_matches_numpy"]),
@@ -74,6 +88,8 @@ def test_mutant_is_caught(tmp_path, monkeypatch, name, old, new, catchers):
                         fn(oracle.F16, (5, 48, 512))
                     elif fn.__code__.co_varnames[:fn.__code__.co_argcount] == ("M", "K"):
                         fn(40, 384)
+                    elif fn.__code__.co_varnames[:fn.__code__.co_argcount] == ("fmt",):
+                        fn("q4k")
                     else:
                         fn()
                 else:
