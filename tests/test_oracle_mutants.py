@@ -21,14 +21,14 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "qref.c")
 MUTANTS = [
     ("q4k nibble halves swapped", "q[64 * g + l] = b & 15;", "q[64 * g + l] = b >> 4;",
      ["test_q4k_field_roundtrip", "test_q4k_special_cases"]),
-    ("q4k min term dropped", "xval v = {a - b, e0, 0, a < b};", "xval v = {a, e0, 0, 0};",
+    ("q4k min term dropped", "xval r = {a - b, e0, 0, a < b};", "xval r = {a, e0, 0, 0};",
      ["test_q4k_special_cases"]),
-    ("q4k min sign flipped", "xval v = {a - b, e0, 0, a < b};", "xval v = {a + b, e0, 0, 0};",
+    ("q4k min sign flipped", "xval r = {a - b, e0, 0, a < b};", "xval r = {a + b, e0, 0, 0};",
      ["test_q4k_special_cases"]),
     ("q4k high scale bits from the wrong byte", "((s12[j] >> 6) << 4));", "((s12[j + 4] >> 6) << 4));",
      ["test_q4k_field_roundtrip"]),
     ("q4k sub-block index off", "int j = k / 32;", "int j = k / 64;", ["test_q4k_special_cases"]),
-    ("q4k extra binary32 rounding", "xval v = {a - b, e0, 0, a < b};", "xval v = rn_f32(a - b, e0);",
+    ("q4k extra binary32 rounding", "xval r = {a - b, e0, 0, a < b};", "xval r = rn_f32(a - b, e0);",
      ["test_q4k_single_rounding"]),
     ("q6k scale per 32 weights", "s[k / 16]", "s[k / 32]", ["test_q6k_special_cases"]),
     ("q6k offset 31", "{nd * s * (q - 32), ed, 0, 0}", "{nd * s * (q - 31), ed, 0, 0}", ["test_q6k_special_cases"]),
