@@ -251,6 +251,64 @@ size_t qgemm_staged_scratch_bytes(int64_t N, int64_t K);
 int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, size_t scratch_bytes, void *Y, int64_t M,
                  int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
 
+/* ---- int8-activation variant ----------------------------------------------
+ * The other operand of the same idea (the prefill post, closing section:
+ * activation quantization and weight-dequant fusion keep each operand
+ * compressed until the multiply; the batched-prefill PR: a single-pass row
+ * quantize feeding an int8-native prefill GEMM, weights dequantized to int8
+ * rows).  The pages fix neither the scale granularity nor the rounding; this
+ * library's reading, every step defined to the bit:
+ *   weights     w32 = RN_f32(exact weight of the unpack contract above);
+ *               per output column n: amax_n = max_k |w32[k][n]|,
+ *               r_n = RN_f32(127/amax_n), s_n = RN_f32(amax_n/127);
+ *               code qw = RNE(w32 * r_n) (the product exact, |qw| <= 127)
+ *   activations per row m the same on X (exact in binary32): r_m, s_m, qx
+ *   output      Y[m][n] = RN_t( RN_f32( RN_f32(acc) * RN_f32(s_m * s_n) ) ),
+ *               acc = sum_k qx*qw exactly (int32)
+ * with r = s = 0 when amax < 2^-96 (only a bf16 row gets there).  The
+ * weight codes are never stored: the GEMM unpacks the packed bytes and
+ * requantizes them on the way into the int8 MFMA operand, so W stays at its
+ * packed size in HBM.  This path is an approximation of X . dequant(W) by
+ * construction (int8 codes); its contract is bit-exactness against the
+ * definition above, not the fp16 path's error bound.
+ *
+ * qgemm_i8_colscale: the per-column factors of one packed weight (the same
+ *   Wpacked, N, K, group_size, has_zp as the GEMMs), once at load: r_n into
+ *   rw[N] and s_n into sw[N] (device floats, 4-byte aligned, caller-owned).
+ *   One launch on `stream`.  Errors as qgemm_dequant, without a dtype.
+ * qgemm_i8_xq_bytes: bytes of the int8 activation copy, 32*ceil(M/32)*K; 0
+ *   for M < 0, K not a positive multiple of 32, or sizes beyond int32.
+ * qgemm_i8_quantize: X [M][K] row-major (dtype bits, device, 16-byte
+ *   aligned) -> codes Xq (device, 16-byte aligned, qgemm_i8_xq_bytes bytes)
+ *   and s_m into sx[M] (device floats).  Xq is fragment-major: 32-row
+ *   blocks, each a sequence of 32-wide k-steps of 1 KB in which lane
+ *   (r, h) holds row r, k = 32s + 16h .. +15, i.e. code (m, k) at
+ *       (m/32)*32*K + (k/32)*1024 + ((k/16)%2)*512 + (m%32)*16 + k%16,
+ *   rows M .. 32*ceil(M/32)-1 zero: one 1 KB piece is one int8 MFMA
+ *   operand.  X must be finite.  One launch (one workgroup per row, the row
+ *   read once); M = 0 is a no-op.  Errors: QGEMM_ERR_SHAPE, _DTYPE, _NULL,
+ *   _ALIGN, _HIP.
+ * qgemm_i8_gemm: Y [M][N] (dtype, row-major, 16-byte aligned) from Xq and sx
+ *   of qgemm_i8_quantize and Wpacked with rw and sw of qgemm_i8_colscale.
+ *   rung -1 picks from this path's own ladder (qgemm_i8_select_rung), else
+ *   0 .. qgemm_i8_num_rungs()-1; every rung gives the same bits.  K at most
+ *   131072 (int32 sums stay exact).  One launch on `stream`; M = 0 is a
+ *   no-op.  Errors as qgemm_gemm_rung. */
+size_t qgemm_i8_xq_bytes(int64_t M, int64_t K);
+int qgemm_i8_quantize(const void *X, void *Xq, float *sx, int64_t M, int64_t K, int dtype, void *stream);
+int qgemm_i8_colscale(int format, const void *Wpacked, float *rw, float *sw, int64_t N, int64_t K, int64_t group_size,
+                      int has_zp, void *stream);
+int qgemm_i8_gemm(int format, int rung, const void *Xq, const float *sx, const void *Wpacked, const float *rw,
+                  const float *sw, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype,
+                  void *stream);
+/* The int8 ladder: rung count and names (as qgemm_num_rungs /
+ * qgemm_rung_name); rung_info / select_rung fill info8 as qgemm_rung_info
+ * (dtype does not enter: every rung computes the same bits). */
+int qgemm_i8_num_rungs(void);
+const char *qgemm_i8_rung_name(int rung);
+int qgemm_i8_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int32_t *info8);
+int qgemm_i8_select_rung(int format, int64_t M, int64_t N, int64_t K, int32_t *info8);
+
 /* Measurement aid, not part of the GEMM path: runs `blocks` workgroups of
  * 256 threads, each wave issuing `iters` rounds of four independent
  * 32x32x16 MFMAs (fp16 or bf16 by `dtype`) on operands read once from

@@ -45,7 +45,9 @@
  *     granularity nor the rounding; the reading implemented here:
  *       - weights: w32 = RN_f32(exact step-2 value); per output column n,
  *         amax_n = max_k |w32|, r_n = RN_f32(127/amax_n), s_n = RN_f32(amax_n/127)
- *         (both 0 when amax_n = 0); qw = RNE_int(w32 * r_n), the product exact;
+ *         (both 0 when amax_n < 2^-96, a bound that only a bf16 row can go
+ *         below, where 127/amax would leave binary32); qw = RNE_int(w32 * r_n),
+ *         the product exact;
  *       - activations: per row m the same with x (exact in binary32):
  *         r_m = RN_f32(127/amax_m), s_m = RN_f32(amax_m/127), qx = RNE_int(x * r_m);
  *       - Y[m][n] = RN_t( RN_f32( RN_f32(acc) * RN_f32(s_m * s_n) ) ),
@@ -580,10 +582,10 @@ static double rne_int(double v)
     return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
 }
 
-/* r = RN_f32(127/amax), s = RN_f32(amax/127); both 0 when amax is 0. */
+/* r = RN_f32(127/amax), s = RN_f32(amax/127); both 0 when amax < 2^-96. */
 static void i8_scales(double amax, float *r, float *s)
 {
-    if (amax == 0.0) {
+    if (amax < ldexp(1.0, -96)) {
         *r = 0.0f;
         *s = 0.0f;
         return;

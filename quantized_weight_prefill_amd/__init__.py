@@ -86,6 +86,14 @@ SIGNATURES = {
     "qgemm_x_to_xf": (_INT, [_VP, _VP, _I64, _I64, _VP]),
     "qgemm_gemm_xf": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_select_rung_xf": (_INT, [_INT, _I64, _I64, _I64, _INT, _VP]),
+    "qgemm_i8_xq_bytes": (_SZ, [_I64, _I64]),
+    "qgemm_i8_quantize": (_INT, [_VP, _VP, _VP, _I64, _I64, _INT, _VP]),
+    "qgemm_i8_colscale": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
+    "qgemm_i8_gemm": (_INT, [_INT, _INT, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_i8_num_rungs": (_INT, []),
+    "qgemm_i8_rung_name": (ctypes.c_char_p, [_INT]),
+    "qgemm_i8_rung_info": (_INT, [_INT, _INT, _I64, _I64, _I64, _VP]),
+    "qgemm_i8_select_rung": (_INT, [_INT, _I64, _I64, _I64, _VP]),
 }
 
 
@@ -293,6 +301,96 @@ def gemm_xf(fmt, xf, wp, M: int, N: int, K: int, group: int = 0, has_zp: bool = 
                              int(bool(has_zp)), _dtype_code(xf), _stream(stream))
     _check("qgemm_gemm_xf", st)
     return out
+
+
+# ---- int8-activation variant ----------------------------------------------
+
+def i8_xq_bytes(M: int, K: int) -> int:
+    return int(lib().qgemm_i8_xq_bytes(M, K))
+
+
+def i8_colscale(fmt, wp, N: int, K: int, group: int = 0, has_zp: bool = False, out=None, stream=None):
+    """Per-column int8 requantization factors (r, s) of one packed weight, as
+    two float32 device tensors of N elements (computed once at load)."""
+    torch = _torch()
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if out is None:
+        out = (torch.empty(N, dtype=torch.float32, device=wp.device),
+               torch.empty(N, dtype=torch.float32, device=wp.device))
+    rw, sw = out
+    if rw.numel() < N or sw.numel() < N or rw.dtype != torch.float32 or sw.dtype != torch.float32:
+        raise ValueError("colscale outputs must be float32 with N elements")
+    st = lib().qgemm_i8_colscale(f, _dev(wp, "wp"), _dev(rw, "rw"), _dev(sw, "sw"), N, K, group, int(bool(has_zp)),
+                                 _stream(stream))
+    _check("qgemm_i8_colscale", st)
+    return rw, sw
+
+
+def i8_quantize(x, out=None, stream=None):
+    """Row quantization of a row-major [M, K] fp16/bf16 matrix: the int8
+    codes in the fragment-major int8 layout (flat int8 tensor of
+    32*ceil(M/32)*K bytes) and the per-row scales (float32, M)."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    n = i8_xq_bytes(M, K)
+    if n == 0 and M > 0:
+        raise QGemmError("qgemm_i8_xq_bytes", -2)
+    if out is None:
+        out = (torch.empty((n,), dtype=torch.int8, device=x.device), torch.empty((M,), dtype=torch.float32, device=x.device))
+    xq, sx = out
+    if xq.numel() < n or xq.dtype != torch.int8 or sx.numel() < M or sx.dtype != torch.float32:
+        raise ValueError("quantize outputs too small or of the wrong dtype")
+    st = lib().qgemm_i8_quantize(_dev(x, "x"), _dev(xq, "xq"), _dev(sx, "sx"), M, K, _dtype_code(x), _stream(stream))
+    _check("qgemm_i8_quantize", st)
+    return xq, sx
+
+
+def gemm_i8(fmt, xq, sx, wp, rw, sw, M: int, N: int, K: int, dtype, group: int = 0, has_zp: bool = False,
+            rung: int = -1, out=None, stream=None):
+    """Y [M, N] (dtype) of the int8 path from i8_quantize's (xq, sx) and
+    i8_colscale's (rw, sw) of the packed weight wp."""
+    torch = _torch()
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    tdt = dtype if isinstance(dtype, torch.dtype) else (torch.float16 if dtype == F16 else torch.bfloat16)
+    if xq.numel() < i8_xq_bytes(M, K) or sx.numel() < M or rw.numel() < N or sw.numel() < N:
+        raise ValueError("int8 inputs are smaller than an M x K / N problem needs")
+    if out is None:
+        out = torch.empty((M, N), dtype=tdt, device=xq.device)
+    elif out.shape != (M, N) or out.dtype != tdt:
+        raise ValueError("out has the wrong shape or dtype")
+    st = lib().qgemm_i8_gemm(f, rung, _dev(xq, "xq"), _dev(sx, "sx"), _dev(wp, "wp"), _dev(rw, "rw"), _dev(sw, "sw"),
+                             _dev(out, "out"), M, N, K, group, int(bool(has_zp)), _dtype_code(out), _stream(stream))
+    _check("qgemm_i8_gemm", st)
+    return out
+
+
+def i8_num_rungs() -> int:
+    return int(lib().qgemm_i8_num_rungs())
+
+
+def i8_rung_name(rung: int):
+    r = lib().qgemm_i8_rung_name(rung)
+    return None if r is None else r.decode()
+
+
+def i8_rung_info(rung: int, fmt, M: int, N: int, K: int) -> dict:
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    info = np.zeros(8, np.int32)
+    _check("qgemm_i8_rung_info", lib().qgemm_i8_rung_info(rung, f, M, N, K, _np_ptr(info)))
+    d = dict(zip(_INFO_KEYS, (int(v) for v in info)))
+    d["name"] = i8_rung_name(d["rung"])
+    return d
+
+
+def i8_select_rung(fmt, M: int, N: int, K: int) -> dict:
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    info = np.zeros(8, np.int32)
+    _check("qgemm_i8_select_rung", lib().qgemm_i8_select_rung(f, M, N, K, _np_ptr(info)))
+    d = dict(zip(_INFO_KEYS, (int(v) for v in info)))
+    d["name"] = i8_rung_name(d["rung"])
+    return d
 
 
 def q4k(x, wp, N: int, out=None, stream=None):

@@ -84,6 +84,8 @@ struct Args {
     const int *offs;             // grouped: E+1 row offsets (device), rows offs[e]..offs[e+1] use expert e
     int E;                       // grouped: number of experts
     long long wstride;           // grouped: packed bytes of one expert's weights
+    const float *sx;             // int8 path: per-row activation scales
+    const float *rw, *sw;        // int8 path: per-column weight requantization factors and scales
 };
 
 // Activation layouts.  X_ROW: X[m][k] at m*K + k.  X_FRAG (fragment-major):
@@ -1067,6 +1069,443 @@ __global__ void __launch_bounds__(256) k_x_to_xf(const uint16_t *X, uint16_t *Xf
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// int8-activation variant.
+//
+// Activations are quantized per row to int8 in one pass (the row held in
+// registers, as in the batched-prefill PR's row quantizer); weights go from
+// their packed bytes straight to int8 inside the GEMM, requantized per output
+// column with factors computed once at load; the contraction runs on
+// 32x32x32 int8 MFMAs with exact int32 sums and one binary32 rescale per
+// output.  Every step is defined to the bit:
+//   w32 = RN_f32(exact weight)        (the same FMA as the fp16 unpack)
+//   qw  = RNE(w32 * r_n), qx = RNE(x * r_m)   (one FMA with 1.5*2^23 each)
+//   Y   = RN_t(RN_f32(acc) * RN_f32(s_m * s_n))
+// with r = RN_f32(127/amax) and s = RN_f32(amax/127) of the column's binary32
+// weights or the row's activations (both 0 when amax < 2^-96, which only a
+// bf16 row can reach).  The int8 activations are stored fragment-major:
+// 32-row blocks, each a run of 32-wide k-steps of 1 KB in which lane (r, h)
+// holds row r, k = 32s + 16h .. +15:
+//   Xq[m][k] at (m/32)*32*K + (k/32)*1024 + ((k/16)%2)*512 + (m%32)*16 + k%16.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+constexpr float kRneMagic = 12582912.0f;  // 1.5 * 2^23: binary32 values in [2^23, 2^24) are the integers
+
+// The quotients are formed in binary64 (correctly rounded) and rounded again
+// to binary32: for a quotient that equals one rounding of the exact value,
+// since 53 >= 2*24 + 2 (Figueroa, "When is double rounding innocuous?").
+__device__ __forceinline__ void i8_scales(float amax, float &r, float &s)
+{
+    if (!(amax >= 0x1p-96f)) {
+        r = 0.0f;
+        s = 0.0f;
+        return;
+    }
+    r = (float)(127.0 / (double)amax);
+    s = (float)((double)amax / 127.0);
+}
+
+// RN(v*r + 1.5*2^23) is 1.5*2^23 + RNE(v*r) for |v*r| < 2^22 (one rounding of
+// the exact product plus an integer); its low byte is RNE(v*r) in two's
+// complement.  |v*r| <= 127*(1 + 2^-24) for every v of the row or column
+// that gave r, so the code is never above 127.
+__device__ __forceinline__ uint32_t i8_code_bits(float v, float r)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_fmaf(v, r, kRneMagic));
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return (a & 0xFFu) | ((b & 0xFFu) << 8) | ((c & 0xFFu) << 16) | (d << 24);
+}
+
+// Element e (0 or 1) of a pair of activations, exactly widened to binary32.
+template <int DT>
+__device__ __forceinline__ float x_elem(uint32_t w, int e)
+{
+    if constexpr (DT == DT_F16) {
+        const f16x2 h = __builtin_bit_cast(f16x2, w);
+        return (float)(e ? h.y : h.x);
+    } else {
+        return __builtin_bit_cast(float, e ? (w & 0xFFFF0000u) : (w << 16));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float vec_amax(u32x4 v)
+{
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) a = fmaxf(a, fabsf(x_elem<DT>(v[j >> 1], j & 1)));
+    return a;
+}
+
+template <int DT>
+__device__ __forceinline__ u32x2 vec_codes(u32x4 v, float r)
+{
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) c[j] = i8_code_bits(x_elem<DT>(v[j >> 1], j & 1), r);
+    return u32x2{pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])};
+}
+
+// Row quantizer: one 256-thread workgroup per row of the padded 32-row
+// blocks; each thread keeps up to kQv 8-element vectors of its row in
+// registers between the max and the code pass (longer rows reread the rest,
+// from L2).  Rows at or past M are written as zeros.
+constexpr int kQv = 8;
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_i8_quant(const uint16_t *X, uint8_t *Xq, float *sx, int M, int K)
+{
+    __shared__ float red[4];
+    const int m = blockIdx.x, tid = threadIdx.x, nv = K >> 3;
+    uint8_t *qrow = Xq + (long long)(m >> 5) * 32 * K + (m & 31) * 16;
+    // the 8 codes of vector v (k = 8v .. 8v+7): one half of a lane's 16 bytes
+    auto dst = [&](int v) -> u32x2 * {
+        const int k = 8 * v;
+        return reinterpret_cast<u32x2 *>(qrow + (long long)(k >> 5) * 1024 + ((k >> 4) & 1) * 512 + (k & 15));
+    };
+    if (m >= M) {
+        for (int v = tid; v < nv; v += 256) *dst(v) = u32x2{0u, 0u};
+        return;
+    }
+    const uint16_t *xr = X + (long long)m * K;
+    u32x4 held[kQv];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kQv; j++) {
+        const int v = tid + 256 * j;
+        held[j] = u32x4{0u, 0u, 0u, 0u};
+        if (v < nv) held[j] = *reinterpret_cast<const u32x4 *>(xr + 8 * v);
+        amax = fmaxf(amax, vec_amax<DT>(held[j]));
+    }
+    for (int v = tid + 256 * kQv; v < nv; v += 256)
+        amax = fmaxf(amax, vec_amax<DT>(*reinterpret_cast<const u32x4 *>(xr + 8 * v)));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float r, s;
+    i8_scales(amax, r, s);
+    if (tid == 0) sx[m] = s;
+#pragma unroll
+    for (int j = 0; j < kQv; j++) {
+        const int v = tid + 256 * j;
+        if (v < nv) *dst(v) = vec_codes<DT>(held[j], r);
+    }
+    for (int v = tid + 256 * kQv; v < nv; v += 256) *dst(v) = vec_codes<DT>(*reinterpret_cast<const u32x4 *>(xr + 8 * v), r);
+}
+
+// The eight binary32 weights of word i of a run, in k order: the fp16
+// unpack's FMA (code * factor - bias, one rounding) without the final
+// rounding to 16 bits.
+template <int FMT>
+__device__ __forceinline__ void unpack_word_f32(const RunRaw<FMT> &u, const RunParams &pr, int i, float (&w)[8])
+{
+    const uint32_t x = u.codes[i], x8 = x >> 8;
+    uint32_t t[4];
+    float fa = pr.fa, nb = pr.nb;
+    if constexpr (FMT == FMT_Q6K) {
+        fa = i < 2 ? pr.fa : pr.fa1;
+        nb = i < 2 ? pr.nb : pr.nb1;
+        const uint32_t h = u.hi[i >> 1];
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const uint32_t lpart = (p < 2 ? x : x8) & ((p & 1) ? 0x00F000F0u : 0x000F000Fu);
+            const int sigma = 4 * (i & 1) + p, T = (p & 1) ? 8 : 4, sh = 2 * sigma - T;
+            const uint32_t hs = sh >= 0 ? (h >> sh) : (h << (-sh));
+            t[p] = lpart | (hs & (0x00030003u << T));
+        }
+    } else {
+        t[0] = x & 0x000F000Fu;
+        t[1] = x & 0x00F000F0u;
+        t[2] = x8 & 0x000F000Fu;
+        t[3] = x8 & 0x00F000F0u;
+    }
+    const float fa16 = fa * 0.0625f;
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const f16x2 h = __builtin_bit_cast(f16x2, t[p]);
+        const float f = (p & 1) ? fa16 : fa;
+        w[2 * p] = __builtin_fmaf((float)h.x, f, nb);
+        w[2 * p + 1] = __builtin_fmaf((float)h.y, f, nb);
+    }
+}
+
+// Word i of a run as eight int8 codes RNE(w32 * r).
+template <int FMT>
+__device__ __forceinline__ u32x2 unpack_word_i8(const RunRaw<FMT> &u, const RunParams &pr, int i, float r)
+{
+    float w[8];
+    unpack_word_f32<FMT>(u, pr, i, w);
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) c[j] = i8_code_bits(w[j], r);
+    return u32x2{pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])};
+}
+
+// Per-column requantization factors, once per weight at load: one wave per
+// panel, lane (g, col) walks run g of its column through every chunk, and
+// the four lane groups combine their maxima.
+template <int FMT>
+__global__ void __launch_bounds__(64) k_i8_colscale(Args a, float *rw, float *sw)
+{
+    const int p = blockIdx.x, lane = threadIdx.x, g = lane >> 4, col = lane & 15;
+    RunSrc<FMT> src;
+    src.init(a, p, g, col);
+    RunRaw<FMT> raw;
+    float amax = 0.0f;
+    const int nch = a.K / kChunk;
+    for (int c = 0; c < nch; c++) {
+        src.load(c, raw);
+        const RunParams pr = run_params<FMT, DT_F16>(raw, src, c);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float w[8];
+            unpack_word_f32<FMT>(raw, pr, i, w);
+#pragma unroll
+            for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(w[j]));
+        }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int n = 16 * p + col;
+    if (g == 0 && n < a.N) {
+        float r, s;
+        i8_scales(amax, r, s);
+        rw[n] = r;
+        sw[n] = s;
+    }
+}
+
+__device__ __forceinline__ i32x16 mma_i8(u32x4 a, u32x4 b, i32x16 c)
+{
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0,
+                                                 0);
+}
+
+// One 32x32 int32 accumulator (Y^T layout, as store_block32) rescaled and
+// stored: y = RN_t(RN_f32(acc) * RN_f32(s_m * s_n)).
+template <int DT>
+__device__ __forceinline__ void store_block_i8(const Args &a, const i32x16 &v, int m_base, int n_base, int lane)
+{
+    const int m = m_base + (lane & 31);
+    if (m >= a.M) return;
+    const float sm = a.sx[m];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int n0 = n_base + 8 * q + 4 * (lane >> 5);
+        if (n0 >= a.N) continue;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float sn = n0 + j < a.N ? a.sw[n0 + j] : 0.0f;
+            y[j] = (float)v[4 * q + j] * (sm * sn);
+        }
+        uint16_t *yp = a.Y + (long long)m * a.N + n0;
+        const uint32_t lo = pack_out<DT>(y[0], y[1]), hi = pack_out<DT>(y[2], y[3]);
+        if (n0 + 4 <= a.N && (a.N & 3) == 0) {
+            *(u32x2 *)yp = u32x2{lo, hi};
+        } else {
+            const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+            for (int j = 0; j < 4 && n0 + j < a.N; j++) yp[j] = e[j];
+        }
+    }
+}
+
+// Streaming int8 tile: the structure of Stream32 (W unpacked once per
+// workgroup into double-buffered LDS, activations straight to VGPRs, raw
+// weight bytes two chunks ahead, one barrier per 128-wide chunk) on 32x32x32
+// int8 MFMAs.  A chunk is four k-steps of 32; run g of a column (32 codes)
+// is k-step g, lane halves 0 (words 0, 1) and 1 (words 2, 3), so both
+// operands carry k = 128c + 32s + 16h + 0..15 in lane (r, h) of k-step s.
+template <int FMT, int WM, int WPB, int NWM, int NWN>
+struct StreamI8 {
+    static constexpr int NTG = 64 * NWM * NWN;
+    static constexpr int PB = WPB * NWN;
+    static constexpr int CB = PB / 2;
+    static constexpr int CBW = WPB / 2;
+    static constexpr int BM = WM * NWM;
+    static constexpr int RBW = WM / 32;
+    static constexpr int RUNS = PB * 64;
+    static constexpr int UPT = (RUNS + NTG - 1) / NTG;
+    static constexpr int UFULL = RUNS / NTG;
+    static_assert(WPB % 2 == 0 && WM % 32 == 0, "32x32 blocks");
+    static_assert(UPT >= 1 && (RUNS - UFULL * NTG) % 64 == 0, "a partial slot must cover whole waves");
+    typedef u32x4 Lds[2][CB][4][64];
+
+    static __device__ __forceinline__ void run(const Args &a, Lds &sW, int tid, int lane, int wn, int m0, int p0,
+                                               int c_lo, int c_hi, i32x16 (&acc)[CBW][RBW])
+    {
+    const uint8_t *Xq = reinterpret_cast<const uint8_t *>(a.X);
+    const int nblk = (a.M + 31) >> 5;
+    const uint8_t *xrow[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; rb++) {
+        // blocks past the last one hold no rows below M: read the last (in
+        // bounds), store nothing
+        const int blk = min((m0 >> 5) + rb, nblk - 1);
+        xrow[rb] = Xq + (long long)blk * 32 * a.K + (lane & 31) * 16 + (lane >> 5) * 512;
+    }
+
+    u32x4 xf[RBW][4];
+    RunSrc<FMT> src[UPT];
+    RunRaw<FMT> raw[UPT];
+    int slot_cp[UPT], slot_lane[UPT];
+    float rs[UPT];
+#pragma unroll
+    for (int s = 0; s < UPT; s++) {
+        const int u0 = tid + NTG * s, u = u0 < RUNS ? u0 : u0 - NTG, pl = u >> 6, col = u & 15;
+        const int p = p0 + pl, n = 16 * p + col;
+        src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, col);
+        slot_cp[s] = pl >> 1;
+        slot_lane[s] = 16 * (pl & 1) + col;
+        rs[s] = (p < a.np && n < a.N) ? a.rw[n] : 0.0f;
+    }
+    const bool extra = __builtin_amdgcn_readfirstlane(tid >> 6) < (RUNS - UFULL * NTG) / 64;
+    auto live = [&](int s) { return s < UFULL || extra; };
+    auto put = [&](int buf, int s, int h, u32x4 v) {
+        if (live(s)) sW[buf][slot_cp[s]][src[s].g][h * 32 + slot_lane[s]] = v;
+    };
+    auto xload = [&](int rb, int c, int ks) {
+        return *reinterpret_cast<const u32x4 *>(xrow[rb] + (long long)c * 4096 + ks * 1024);
+    };
+
+#pragma unroll
+    for (int s = 0; s < UPT; s++) src[s].load(c_lo, raw[s]);
+#pragma unroll
+    for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) xf[rb][ks] = xload(rb, c_lo, ks);
+#pragma unroll
+    for (int s = 0; s < UPT; s++) {
+        const RunParams pr = run_params<FMT, DT_F16>(raw[s], src[s], c_lo);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const u32x2 w0 = unpack_word_i8<FMT>(raw[s], pr, 2 * h, rs[s]);
+            const u32x2 w1 = unpack_word_i8<FMT>(raw[s], pr, 2 * h + 1, rs[s]);
+            put(0, s, h, u32x4{w0.x, w0.y, w1.x, w1.y});
+        }
+    }
+    const int c1 = c_lo + 1 < c_hi ? c_lo + 1 : c_hi - 1;
+#pragma unroll
+    for (int s = 0; s < UPT; s++) src[s].load(c1, raw[s]);
+    __syncthreads();
+
+    RunRaw<FMT> raw2[UPT];
+    auto chunk = [&](int c, int buf, RunRaw<FMT>(&ru)[UPT], RunRaw<FMT>(&rf)[UPT]) {
+        const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
+        const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
+#pragma unroll
+        for (int s = 0; s < UPT; s++) src[s].load(cnn, rf[s]);
+        u32x4 wcur[CBW], wnxt[CBW];
+#pragma unroll
+        for (int cb = 0; cb < CBW; cb++) wcur[cb] = sW[buf][wn * CBW + cb][0][lane];
+        __builtin_amdgcn_sched_barrier(0);
+        RunParams pr[UPT];
+#pragma unroll
+        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT_F16>(ru[s], src[s], cn);
+        u32x2 pend[UPT];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            if (ks < 3) {
+#pragma unroll
+                for (int cb = 0; cb < CBW; cb++) wnxt[cb] = sW[buf][wn * CBW + cb][ks + 1][lane];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rb = 0; rb < RBW; rb++) {
+#pragma unroll
+                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma_i8(wcur[cb], xf[rb][ks], acc[cb][rb]);
+                xf[rb][ks] = xload(rb, cn, ks);
+            }
+#pragma unroll
+            for (int s = 0; s < UPT; s++) {
+                const u32x2 wv = unpack_word_i8<FMT>(ru[s], pr[s], ks, rs[s]);
+                if (ks & 1) put(buf ^ 1, s, ks >> 1, u32x4{pend[s].x, pend[s].y, wv.x, wv.y});
+                else pend[s] = wv;
+            }
+            if (ks < 3) {
+#pragma unroll
+                for (int cb = 0; cb < CBW; cb++) wcur[cb] = wnxt[cb];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+    };
+    int c = c_lo;
+    for (; c + 1 < c_hi; c += 2) {
+        chunk(c, 0, raw, raw2);
+        chunk(c + 1, 1, raw2, raw);
+    }
+    if (c < c_hi) chunk(c, 0, raw, raw2);
+    }
+};
+
+// WPE: minimum waves per SIMD the register budget must allow (1 lets a
+// 4-wave tile of 64-row waves hold its 128 accumulators without spilling).
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int WPE = 2>
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(WPE)))
+k_i8_stream(Args a)
+{
+    using S = StreamI8<FMT, WM, WPB, NWM, NWN>;
+    constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
+    constexpr int NACC = NWM * NWN * CBW * RBW * 64;
+    // the partial sums of groups 1.. overlay the LDS of every group (free
+    // once all groups have passed their last chunk's barrier)
+    static_assert(KS == 1 || (KS - 1) * NACC * sizeof(i32x16) <= KS * sizeof(typename S::Lds),
+                  "K-split reduction must fit in LDS");
+    __shared__ typename S::Lds sWall[KS];
+
+    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    const int kg = wall / (NWM * NWN);
+    const int w = wall % (NWM * NWN), tid = threadIdx.x % S::NTG;
+    const int wm = w % NWM, wn = w / NWM;
+    const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM;
+    int mt, nt;
+    tile_coords(xcd_order(blockIdx.x, gridDim.x), tm, tn, mt, nt);
+    const int m0 = mt * BM + wm * WM, p0 = nt * PB;
+    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
+
+    i32x16 acc[CBW][RBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0;
+    S::run(a, sWall[kg], tid, lane, wn, m0, p0, c_lo, c_hi, acc);
+    if constexpr (KS > 1) {
+        // integer partial sums: the order of the additions does not matter
+        i32x16 *red = reinterpret_cast<i32x16 *>(&sWall[0]);
+        if (kg > 0) {
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    red[(kg - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; g++)
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    acc[cb][rb] += red[(g - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane];
+    }
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+            store_block_i8<DT>(a, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * (wn * CBW + cb), lane);
+}
+
 // ---------------------------------------------------------------------------
 // Host side: validation, the M-ladder, launches.
 // ---------------------------------------------------------------------------
@@ -1514,6 +1953,149 @@ int staged(int fmt, const void *X, const void *W, void *scratch, size_t scratch_
     return launch_status(e, "staged");
 }
 
+
+// ---------------------------------------------------------------------------
+// int8-activation path: rungs, validation, launches.
+// ---------------------------------------------------------------------------
+
+enum I8Rung {
+    I8_M128 = 0,      // 128x128, 4 waves of 32x128
+    I8_M256 = 1,      // 256x128, 8 waves of 32x128: each weight unpacked once for 256 rows
+    I8_M128_K2 = 2,   // 128x128, K split over two 4-wave groups
+    I8_M256W64 = 3,   // 256x128, 4 waves of 64x128
+    I8_RUNG_COUNT = 4
+};
+const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x128-w64"};
+// int32 sums stay exact while K * 127 * 127 < 2^31
+constexpr long long kI8MaxK = 131072;
+
+int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
+{
+    pl = Plan{};
+    pl.rung = rung;
+    pl.kw = 1;
+    switch (rung) {
+    case I8_M128: pl.rows = 128; pl.cols = 128; pl.waves = 4; break;
+    case I8_M256: pl.rows = 256; pl.cols = 128; pl.waves = 8; break;
+    case I8_M128_K2:
+        pl.rows = 128;
+        pl.cols = 128;
+        pl.kw = (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = 4 * pl.kw;
+        break;
+    case I8_M256W64: pl.rows = 256; pl.cols = 128; pl.waves = 4; break;
+    default: return QGEMM_ERR_FORMAT;
+    }
+    const long long np = (N + 15) / 16;
+    const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
+    if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
+    pl.tiles_n = (int)tn;
+    pl.tiles_m = (int)tm;
+    pl.grid = dim3((unsigned)(tn * tm), 1, 1);
+    return QGEMM_OK;
+}
+
+int i8_select(long long M, long long N, long long K)
+{
+    const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8);
+    if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
+    return M >= 512 ? I8_M256 : I8_M128;
+}
+
+template <int FMT, int DT>
+hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
+{
+    switch (pl.rung) {
+    case I8_M128:
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        break;
+    case I8_M256:
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        break;
+    case I8_M128_K2:
+        if (pl.kw == 2)
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 2>), pl.grid, dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 8, 4, 1, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        break;
+    }
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_i8_dt(int fmt, const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (fmt == FMT_Q4K) return launch_i8_fd<FMT_Q4K, DT>(pl, a, s);
+    if (fmt == FMT_Q6K) return launch_i8_fd<FMT_Q6K, DT>(pl, a, s);
+    return launch_i8_fd<FMT_W4, DT>(pl, a, s);
+}
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+int i8_gemm(int fmt, int rung, const void *Xq, const float *sx, const void *W, const float *rw, const float *sw,
+            void *Y, long long M, long long N, long long K, long long group, int has_zp, int dtype, void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, M, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (K > kI8MaxK) return QGEMM_ERR_SHAPE;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (rung < -1 || rung >= I8_RUNG_COUNT) return QGEMM_ERR_FORMAT;
+    if (M == 0) return QGEMM_OK;
+    if (!Xq || !sx || !W || !rw || !sw || !Y) return QGEMM_ERR_NULL;
+    if (!aligned16(Xq) || !aligned16(W) || !aligned16(Y) || !aligned4(sx) || !aligned4(rw) || !aligned4(sw))
+        return QGEMM_ERR_ALIGN;
+    Plan pl;
+    st = i8_plan(rung < 0 ? i8_select(M, N, K) : rung, M, N, K, pl);
+    if (st != QGEMM_OK) return st;
+    Args a = make_args(fmt, Xq, W, Y, M, N, K, group, has_zp);
+    a.sx = sx;
+    a.rw = rw;
+    a.sw = sw;
+    const hipError_t e = dtype == DT_F16 ? launch_i8_dt<DT_F16>(fmt, pl, a, (hipStream_t)stream)
+                                         : launch_i8_dt<DT_BF16>(fmt, pl, a, (hipStream_t)stream);
+    return launch_status(e, kI8RungNames[pl.rung]);
+}
+
+int i8_quantize(const void *X, void *Xq, float *sx, long long M, long long K, int dtype, void *stream)
+{
+    if (M < 0 || K < 32 || K % 32 != 0 || M > INT32_MAX - 31 || K > INT32_MAX) return QGEMM_ERR_SHAPE;
+    if ((M + 31) / 32 * 32 * K / 32 > INT32_MAX) return QGEMM_ERR_SHAPE;  // byte offsets of one block row fit
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (M == 0) return QGEMM_OK;
+    if (!X || !Xq || !sx) return QGEMM_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return QGEMM_ERR_ALIGN;
+    const unsigned rows = (unsigned)((M + 31) / 32 * 32);
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == DT_F16)
+        hipLaunchKernelGGL((k_i8_quant<DT_F16>), dim3(rows), dim3(256), 0, s, (const uint16_t *)X, (uint8_t *)Xq, sx,
+                           (int)M, (int)K);
+    else
+        hipLaunchKernelGGL((k_i8_quant<DT_BF16>), dim3(rows), dim3(256), 0, s, (const uint16_t *)X, (uint8_t *)Xq, sx,
+                           (int)M, (int)K);
+    return launch_status(hipGetLastError(), "i8 quantize");
+}
+
+int i8_colscale(int fmt, const void *W, float *rw, float *sw, long long N, long long K, long long group, int has_zp,
+                void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, 0, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (!W || !rw || !sw) return QGEMM_ERR_NULL;
+    if (!aligned16(W) || !aligned4(rw) || !aligned4(sw)) return QGEMM_ERR_ALIGN;
+    Args a = make_args(fmt, nullptr, W, nullptr, 0, N, K, group, has_zp);
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((unsigned)a.np);
+    if (fmt == FMT_Q4K) hipLaunchKernelGGL((k_i8_colscale<FMT_Q4K>), grid, dim3(64), 0, s, a, rw, sw);
+    else if (fmt == FMT_Q6K) hipLaunchKernelGGL((k_i8_colscale<FMT_Q6K>), grid, dim3(64), 0, s, a, rw, sw);
+    else hipLaunchKernelGGL((k_i8_colscale<FMT_W4>), grid, dim3(64), 0, s, a, rw, sw);
+    return launch_status(hipGetLastError(), "i8 colscale");
+}
+
 void fill_info(const Plan &pl, int32_t *info)
 {
     info[0] = pl.rung;
@@ -1658,6 +2240,53 @@ int qgemm_grouped(int format, const void *X, const void *Wpacked, void *Y, const
                   int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream)
 {
     return grouped(format, X, Wpacked, Y, offsets, E, T, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream);
+}
+
+size_t qgemm_i8_xq_bytes(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 32 || K % 32 != 0 || M > INT32_MAX - 31 || K > INT32_MAX) return 0;
+    return (size_t)((M + 31) / 32) * 32 * (size_t)K;
+}
+
+int qgemm_i8_quantize(const void *X, void *Xq, float *sx, int64_t M, int64_t K, int dtype, void *stream)
+{
+    return i8_quantize(X, Xq, sx, M, K, dtype, stream);
+}
+
+int qgemm_i8_colscale(int format, const void *Wpacked, float *rw, float *sw, int64_t N, int64_t K, int64_t group_size,
+                      int has_zp, void *stream)
+{
+    return i8_colscale(format, Wpacked, rw, sw, N, K, format == FMT_W4 ? group_size : 0, has_zp, stream);
+}
+
+int qgemm_i8_gemm(int format, int rung, const void *Xq, const float *sx, const void *Wpacked, const float *rw,
+                  const float *sw, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype,
+                  void *stream)
+{
+    return i8_gemm(format, rung, Xq, sx, Wpacked, rw, sw, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype,
+                   stream);
+}
+
+int qgemm_i8_num_rungs(void) { return I8_RUNG_COUNT; }
+
+const char *qgemm_i8_rung_name(int rung) { return rung >= 0 && rung < I8_RUNG_COUNT ? kI8RungNames[rung] : nullptr; }
+
+int qgemm_i8_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int32_t *info8)
+{
+    if (!info8) return QGEMM_ERR_NULL;
+    int st = check_shape(format, M, N, K, 0);
+    if (st != QGEMM_OK) return st;
+    if (K > kI8MaxK) return QGEMM_ERR_SHAPE;
+    Plan pl;
+    st = i8_plan(rung, M, N, K, pl);
+    if (st != QGEMM_OK) return st;
+    fill_info(pl, info8);
+    return QGEMM_OK;
+}
+
+int qgemm_i8_select_rung(int format, int64_t M, int64_t N, int64_t K, int32_t *info8)
+{
+    return qgemm_i8_rung_info(i8_select(M, N, K), format, M, N, K, info8);
 }
 
 }  // extern "C"

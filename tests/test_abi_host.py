@@ -216,6 +216,61 @@ def test_device_entry_argument_errors():
     assert lib.qgemm_gemm_xf(0, -1, None, None, None, 0, 16, 256, 0, 0, 0, s) == 0
 
 
+def test_i8_entry_argument_errors():
+    """The int8 path's entry points reject bad arguments before any launch."""
+    lib = qg.lib()
+    A = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    odd4 = ctypes.c_void_p((1 << 20) + 2)
+    s = None
+    assert lib.qgemm_i8_xq_bytes(1, 32) == 32 * 32 and lib.qgemm_i8_xq_bytes(33, 256) == 64 * 256
+    assert lib.qgemm_i8_xq_bytes(4, 48) == 0 and lib.qgemm_i8_xq_bytes(-1, 64) == 0 and lib.qgemm_i8_xq_bytes(4, 0) == 0
+    # quantize
+    assert lib.qgemm_i8_quantize(A, A, A, 4, 48, 0, s) == -2
+    assert lib.qgemm_i8_quantize(A, A, A, -1, 64, 0, s) == -2
+    assert lib.qgemm_i8_quantize(A, A, A, 4, 64, 5, s) == -3
+    assert lib.qgemm_i8_quantize(None, A, A, 4, 64, 0, s) == -1
+    assert lib.qgemm_i8_quantize(A, A, None, 4, 64, 0, s) == -1
+    assert lib.qgemm_i8_quantize(A, mis, A, 4, 64, 0, s) == -4
+    assert lib.qgemm_i8_quantize(A, A, odd4, 4, 64, 0, s) == -4
+    assert lib.qgemm_i8_quantize(None, None, None, 0, 64, 0, s) == 0   # M = 0
+    # colscale
+    assert lib.qgemm_i8_colscale(0, A, A, A, 16, 200, 0, 0, s) == -2
+    assert lib.qgemm_i8_colscale(3, A, A, A, 16, 256, 0, 0, s) == -5
+    assert lib.qgemm_i8_colscale(2, A, A, A, 16, 256, 0, 1, s) == -5   # W4A16 without a group size
+    assert lib.qgemm_i8_colscale(0, None, A, A, 16, 256, 0, 0, s) == -1
+    assert lib.qgemm_i8_colscale(0, A, odd4, A, 16, 256, 0, 0, s) == -4
+    assert lib.qgemm_i8_colscale(0, mis, A, A, 16, 256, 0, 0, s) == -4
+    # gemm
+    g = lib.qgemm_i8_gemm
+    assert g(0, -1, A, A, A, A, A, A, 4, 16, 200, 0, 0, 0, s) == -2
+    assert g(0, -1, A, A, A, A, A, A, 4, 16, 262144, 0, 0, 0, s) == -2  # int32 sums would overflow
+    assert g(0, -1, A, A, A, A, A, A, 4, 16, 256, 0, 0, 9, s) == -3
+    assert g(0, 4, A, A, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
+    assert g(2, -1, A, A, A, A, A, A, 4, 16, 256, 48, 1, 0, s) == -5
+    assert g(0, -1, A, None, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -1
+    assert g(0, -1, A, A, A, A, None, A, 4, 16, 256, 0, 0, 0, s) == -1
+    assert g(0, -1, mis, A, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -4
+    assert g(0, -1, A, odd4, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -4
+    assert g(0, -1, None, None, None, None, None, None, 0, 16, 256, 0, 0, 0, s) == 0   # M = 0
+
+
+def test_i8_ladder():
+    """The int8 ladder: every rung plans every legal shape; the automatic
+    choice is one of them; grids stay within one launch."""
+    names = [qg.i8_rung_name(r) for r in range(qg.i8_num_rungs())]
+    assert len(set(names)) == len(names) and qg.i8_rung_name(qg.i8_num_rungs()) is None
+    for fmt in ("q4k", "q6k", "w4a16"):
+        for M in (1, 31, 64, 130, 658, 2048, 4096):
+            for K, N in ((4096, 24576), (12288, 4096), (4096, 1024), (256, 16)):
+                sel = qg.i8_select_rung(fmt, M, N, K)
+                assert 0 <= sel["rung"] < qg.i8_num_rungs()
+                for r in range(qg.i8_num_rungs()):
+                    info = qg.i8_rung_info(r, fmt, M, N, K)
+                    assert info["tiles_m"] * info["rows"] >= M and info["tiles_n"] * info["cols"] >= N
+                    assert info["tiles_m"] * info["tiles_n"] < 2 ** 31
+
+
 # ----------------------------------------------------------------------------
 # the M-ladder
 # ----------------------------------------------------------------------------

@@ -571,6 +571,11 @@ def test_i8_codes_ties_and_range():
     # an all-zero row: codes 0, scale 0
     Q, s = oracle.quant_rows_i8(np.zeros((2, 64), np.uint16), oracle.BF16)
     assert not Q.any() and not s.any()
+    # bf16 rows below and at the 2^-96 floor: scale 0 below it, full codes at it
+    tiny = synth.bf16_bits_from_f32(np.array([[2.0 ** -100, -2.0 ** -101, 0.0], [2.0 ** -96, -2.0 ** -97, 0.0]]))
+    Q, s = oracle.quant_rows_i8(tiny, oracle.BF16)
+    assert Q.tolist() == [[0, 0, 0], [127, -64, 0]] and s[0] == 0.0
+    assert Fraction(float(s[1])) == _f32(Fraction(2) ** -96 / 127)
 
 
 @pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])

@@ -53,6 +53,8 @@ MUTANTS = [
      ["test_i8_scales_exact_rationals", "test_i8_codes_ties_and_range"]),
     ("i8 output scale inverted", "*s = (float)(amax / 127.0);", "*s = (float)(127.0 / amax);",
      ["test_i8_scales_exact_rationals", "test_gemm_i8_chain_close_to_fp64_product"]),
+    ("i8 scale floor moved", "if (amax < ldexp(1.0, -96)) {", "if (amax < ldexp(1.0, -95)) {",
+     ["test_i8_codes_ties_and_range"]),
     ("i8 gemm drops the weight scale", "xval sc = rn_f32(x.n * w.n, x.e + w.e);", "xval sc = x;",
      ["test_gemm_i8_scaled_matches_numpy_binary32"]),
     ("i8 gemm weight codes transposed", "acc += (int64_t)Qx[m * K + k] * Qw[k * N + n];",
