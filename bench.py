@@ -32,6 +32,10 @@ Profiling helpers (same JSON line, restricted work):
     --no-ceiling        skip the MFMA rate probe (`mfma_ceiling`: what the
                         chip sustains on random operands under its power
                         limit, for reading `roofline.frac` against)
+    --no-int8           skip the int8-activation arm (`int8_arm`: the same
+                        step with per-row int8 activations quantized inside the
+                        step and the weights requantized to int8 inside the
+                        GEMM, on the same rotating weight copies)
 """
 from __future__ import annotations
 
@@ -55,6 +59,7 @@ from quantized_weight_prefill_amd import synth  # noqa: E402
 METRIC = "fused Q4_K GEMM TFLOP/s + prefill tok/s (Qwen3-8B shapes, M=658); % roofline"
 PEAK_TFLOPS = {qg.F16: 2500.0, qg.BF16: 2500.0}  # dense MFMA, fp16 / bf16
 PEAK_HBM_GBPS = 8000.0
+PEAK_INT8_TOPS = 5000.0  # dense int8 MFMA
 BYTES_PER_WEIGHT = {"q4k": 144 / 256, "q6k": 210 / 256}
 PROFILE_STEPS = 10  # steps of the per-launch profiling pass
 
@@ -149,6 +154,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-arm comparison")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8-activation arm")
     ap.add_argument("--pool-mb", type=float, default=640.0,
                     help="every GEMM rotates through copies of its weights totalling at least this many MB, so the "
                          "256 MB Infinity Cache cannot hold them (0: no rotation)")
@@ -346,6 +352,7 @@ def main() -> int:
     roof["kernel"] = f"{gd['label']} ({gd['fmt']} M={gd['M']} K={gd['K']} N={gd['N']}, rung {gd['rung']})"
     roof["traffic"] = measured_traffic(f"{args.workload}/{gd['label']}")
     staged = None if args.no_staged else staged_arm(gd, call)
+    int8 = None if args.no_int8 else int8_arm(gemms, wl, lib, sp, timer, args)
     ceiling = None if args.no_ceiling else mfma_ceiling(gd["dt"])
     if ceiling is not None and roof["bound"] == "mfma":
         roof["frac_of_sustained"] = round(pd["tflops"] / ceiling["value"], 4)
@@ -380,6 +387,8 @@ def main() -> int:
         out["mfma_ceiling"] = ceiling
     if staged is not None:
         out["staged_arm"] = staged
+    if int8 is not None:
+        out["int8_arm"] = int8
     if args.only is not None or args.rung >= 0:
         out["config"]["only"] = args.only
         out["config"]["rung"] = args.rung
@@ -581,6 +590,120 @@ def staged_arm(g, call, reps: int = 20) -> dict:
             "weight_bytes_fused": round(wq), "weight_bytes_staged": round(wq + 2 * w16),
             "note": "staged = unpack pass (reads packed W, writes 2 B/weight) + the same 128x128 kernel reading "
                     "2 B/weight; its Y equals the fused 128x128 rung's Y bit for bit"}
+
+
+def int8_arm(gemms, wl, lib, sp, timer, args) -> dict:
+    """The same step on the int8-activation path: each distinct input is
+    quantized per row (qgemm_i8_quantize, inside the step, replacing the
+    fragment-major copy), each GEMM unpacks its packed weights straight to
+    int8 (per-column factors from qgemm_i8_colscale, computed once here as at
+    load) on the same rotating weight copies.  Per-launch times from HIP
+    events in a profiling pass, the step time from the wall clock over
+    --steps steps between synchronisations, the dominant GEMM's time from
+    events around it inside that region (as for the main line)."""
+    import torch
+
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    dev = gemms[0]["y"].device
+    quant, arm = {}, []
+    for g in gemms:
+        M, N, K, dt = g["M"], g["N"], g["K"], g["dt"]
+        grp, zp, f = (g["group"] if g["fmt"] == "w4a16" else 0), int(not g["sym"]), qg.FORMATS[g["fmt"]]
+        rw = torch.empty(N, dtype=torch.float32, device=dev)
+        sw = torch.empty(N, dtype=torch.float32, device=dev)
+        st = lib.qgemm_i8_colscale(f, ptr(g["wp"]), ptr(rw), ptr(sw), N, K, grp, zp, sp)
+        if st != 0:
+            raise qg.QGemmError("qgemm_i8_colscale", st)
+        prep = None
+        if g["src"] not in quant:
+            xq = torch.empty(qg.i8_xq_bytes(M, K), dtype=torch.int8, device=dev)
+            sx = torch.empty(M, dtype=torch.float32, device=dev)
+            quant[g["src"]] = (xq, sx)
+            prep = dict(label=f"i8_quantize({wl['gemms'][g['src']][0]})", M=M, K=K,
+                        call=functools.partial(lib.qgemm_i8_quantize, ptr(g["x"]), ptr(xq), ptr(sx), M, K, dt, sp),
+                        bytes=2.0 * M * K + qg.i8_xq_bytes(M, K) + 4.0 * M)
+        xq, sx = quant[g["src"]]
+        # rw and sw are the same for every copy of the weights
+        calls = [functools.partial(lib.qgemm_i8_gemm, f, -1, ptr(xq), ptr(sx), ptr(w), ptr(rw), ptr(sw), ptr(g["y"]),
+                                   M, N, K, grp, zp, dt, sp) for w in g["pool"]]
+        arm.append(dict(g=g, prep=prep, calls=calls, turn=0, rw=rw, sw=sw,
+                        rung=qg.i8_select_rung(g["fmt"], M, N, K)["name"]))
+
+    def run(a, which):
+        if which == "prep":
+            st = a["prep"]["call"]()
+        else:
+            st = a["calls"][a["turn"] % len(a["calls"])]()
+            a["turn"] += 1
+        if st != 0:
+            raise qg.QGemmError(f"int8 {a['g']['label']} {which}", st)
+
+    for _ in range(max(1, args.warmup)):
+        for a in arm:
+            if a["prep"] is not None:
+                run(a, "prep")
+            run(a, "gemm")
+    torch.cuda.synchronize()
+    nprof = max(3, min(args.steps, PROFILE_STEPS))
+    evg = [[timer.pair() for _ in arm] for _ in range(nprof)]
+    evp = [[timer.pair() for _ in arm] for _ in range(nprof)]
+    for s in range(nprof):
+        for j, a in enumerate(arm):
+            if a["prep"] is not None:
+                timer.record(evp[s][j][0], sp)
+                run(a, "prep")
+                timer.record(evp[s][j][1], sp)
+            timer.record(evg[s][j][0], sp)
+            run(a, "gemm")
+            timer.record(evg[s][j][1], sp)
+    torch.cuda.synchronize()
+    gemm_ms = [float(np.mean([timer.ms(*evg[s][j]) for s in range(nprof)])) for j in range(len(arm))]
+    jd = int(np.argmax(gemm_ms))
+    evd = [timer.pair() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, a in enumerate(arm):
+            if a["prep"] is not None:
+                run(a, "prep")
+            if j == jd:
+                timer.record(evd[s][0], sp)
+                run(a, "gemm")
+                timer.record(evd[s][1], sp)
+            else:
+                run(a, "gemm")
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gemm_ms[jd] = float(np.mean([timer.ms(e0, e1) for e0, e1 in evd]))
+    per = []
+    for j, a in enumerate(arm):
+        if a["prep"] is not None:
+            p = a["prep"]
+            ms = float(np.mean([timer.ms(*evp[s][j]) for s in range(nprof)]))
+            per.append(dict(label=p["label"], M=p["M"], K=p["K"], rung="i8_quantize", ms=round(ms, 5),
+                            gbps=round(p["bytes"] / ms / 1e6, 1)))
+        g = a["g"]
+        per.append(dict(label=g["label"], fmt=g["fmt"], M=g["M"], K=g["K"], N=g["N"], rung=a["rung"],
+                        ms=round(gemm_ms[j], 5), tops=round(g["flops"] / gemm_ms[j] / 1e9, 2),
+                        weight_copies=len(g["pool"])))
+    ops = sum(a["g"]["flops"] for a in arm)
+    gd = arm[jd]["g"]
+    dom = next(p for p in per if p.get("fmt") and p["label"] == gd["label"])
+    dom["timed_in_step"] = True
+    out = {"what": "the same step with per-row int8 activations (quantized inside the step) and weights unpacked to "
+                   "int8 inside the GEMM (per-column scales computed once at load): bit-exact to its own definition, "
+                   "an approximation of the fp16 path's result",
+           "ms_per_step": round(ms_step, 5), "tops": round(ops / (ms_step * 1e-3) / 1e12, 3), "unit": "TOP/s",
+           "per_kernel": per,
+           "roofline": {"bound": "mfma", "achieved": dom["tops"], "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                        "frac": round(dom["tops"] / PEAK_INT8_TOPS, 4),
+                        "kernel": f"{gd['label']} ({gd['fmt']} M={gd['M']} K={gd['K']} N={gd['N']}, rung "
+                                  f"{arm[jd]['rung']})"}}
+    if args.workload == "qwen3_8b_layer_m658" and args.only is None:
+        out["prefill_tok_s_linear_only"] = round(synth.QWEN3_8B_PROMPT / (synth.QWEN3_8B_LAYERS * ms_step * 1e-3), 1)
+    return out
 
 
 def read_ceiling(pool, reps: int = 30) -> float:

@@ -1116,9 +1116,14 @@ __device__ __forceinline__ uint32_t i8_code_bits(float v, float r)
     return __builtin_bit_cast(uint32_t, __builtin_fmaf(v, r, kRneMagic));
 }
 
+// The low bytes of a, b, c, d as one word (byte 0 = a): three byte permutes.
+// v_perm_b32 picks each result byte from the eight bytes {src1 (0..3),
+// src0 (4..7)}; selector 0x0c gives a zero byte.
 __device__ __forceinline__ uint32_t pack4_i8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
-    return (a & 0xFFu) | ((b & 0xFFu) << 8) | ((c & 0xFFu) << 16) | (d << 24);
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a.0, b.0, 0, 0
+    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);  // c.0, d.0, 0, 0
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);             // a.0, b.0, c.0, d.0
 }
 
 // Element e (0 or 1) of a pair of activations, exactly widened to binary32.
@@ -1359,7 +1364,10 @@ struct StreamI8 {
     float rs[UPT];
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
-        const int u0 = tid + NTG * s, u = u0 < RUNS ? u0 : u0 - NTG, pl = u >> 6, col = u & 15;
+        // a slot past the tile's runs (the last slot of the later waves, or
+        // every slot when a tile has fewer runs than threads) shadows a real
+        // run, so its loads stay in bounds; it never stores
+        const int u0 = tid + NTG * s, u = u0 < RUNS ? u0 : u0 % RUNS, pl = u >> 6, col = u & 15;
         const int p = p0 + pl, n = 16 * p + col;
         src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, col);
         slot_cp[s] = pl >> 1;
@@ -1446,10 +1454,8 @@ struct StreamI8 {
     }
 };
 
-// WPE: minimum waves per SIMD the register budget must allow (1 lets a
-// 4-wave tile of 64-row waves hold its 128 accumulators without spilling).
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int WPE = 2>
-__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(WPE)))
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_i8_stream(Args a)
 {
     using S = StreamI8<FMT, WM, WPB, NWM, NWN>;
@@ -1962,10 +1968,10 @@ enum I8Rung {
     I8_M128 = 0,      // 128x128, 4 waves of 32x128
     I8_M256 = 1,      // 256x128, 8 waves of 32x128: each weight unpacked once for 256 rows
     I8_M128_K2 = 2,   // 128x128, K split over two 4-wave groups
-    I8_M256W64 = 3,   // 256x128, 4 waves of 64x128
+    I8_M256N96 = 3,   // 256x96, 8 waves of 32x96
     I8_RUNG_COUNT = 4
 };
-const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x128-w64"};
+const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x96"};
 // int32 sums stay exact while K * 127 * 127 < 2^31
 constexpr long long kI8MaxK = 131072;
 
@@ -1983,7 +1989,7 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.kw = (K / kChunk) % 2 == 0 ? 2 : 1;
         pl.waves = 4 * pl.kw;
         break;
-    case I8_M256W64: pl.rows = 256; pl.cols = 128; pl.waves = 4; break;
+    case I8_M256N96: pl.rows = 256; pl.cols = 96; pl.waves = 8; break;
     default: return QGEMM_ERR_FORMAT;
     }
     const long long np = (N + 15) / 16;
@@ -1995,11 +2001,24 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
     return QGEMM_OK;
 }
 
+// The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 512..4096):
+//  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
+//    tile with K split over two wave groups (o and down at M = 658);
+//  * up to 128 rows: the 128x128 tile;
+//  * otherwise a 256-row tile, 128 or 96 columns wide, whichever finishes
+//    in fewer rounds of one workgroup per CU, a round of 96-wide tiles
+//    counting 0.85 of a 128-wide one (measured: 114 against 119 us for the
+//    merged gate_up at M = 658, 768 against 576 tiles; 154 against 137 us
+//    at M = 2048, 1024 against 768 tiles).
 int i8_select(long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8);
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
-    return M >= 512 ? I8_M256 : I8_M128;
+    if (M <= 128) return I8_M128;
+    const long long tm = (M + 255) / 256;
+    const auto rounds = [](long long tiles) { return (double)((tiles + kCUs - 1) / kCUs); };
+    const double c128 = rounds(tm * ((np + 7) / 8)), c96 = 0.85 * rounds(tm * ((np + 5) / 6));
+    return c96 < c128 ? I8_M256N96 : I8_M256;
 }
 
 template <int FMT, int DT>
@@ -2019,7 +2038,7 @@ hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
             hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
         break;
     default:
-        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 8, 4, 1, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
         break;
     }
     return hipGetLastError();

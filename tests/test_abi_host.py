@@ -246,7 +246,7 @@ def test_i8_entry_argument_errors():
     assert g(0, -1, A, A, A, A, A, A, 4, 16, 200, 0, 0, 0, s) == -2
     assert g(0, -1, A, A, A, A, A, A, 4, 16, 262144, 0, 0, 0, s) == -2  # int32 sums would overflow
     assert g(0, -1, A, A, A, A, A, A, 4, 16, 256, 0, 0, 9, s) == -3
-    assert g(0, 4, A, A, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
+    assert g(0, 99, A, A, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
     assert g(2, -1, A, A, A, A, A, A, 4, 16, 256, 48, 1, 0, s) == -5
     assert g(0, -1, A, None, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -1
     assert g(0, -1, A, A, A, A, None, A, 4, 16, 256, 0, 0, 0, s) == -1

@@ -88,13 +88,15 @@ def _run_i8(c: Case, rung: int = -1):
 GEMM_SHAPES = [(1, 48, 512), (37, 200, 768), (130, 72, 256), (300, 264, 1024)]
 
 
-@pytest.mark.parametrize("rung", list(range(4)))
+@pytest.mark.parametrize("rung", list(range(8)))
 @pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16"])
 @pytest.mark.parametrize("dtype", [qg.F16, qg.BF16])
 def test_i8_gemm_bitexact(rung, fmt, dtype):
     """Every rung gives the oracle's bits on shapes with ragged M and N tails,
     several tiles, and an odd chunk count (K = 768: the K-split rung runs
     unsplit)."""
+    if rung >= qg.i8_num_rungs():
+        pytest.skip(f"the int8 ladder has {qg.i8_num_rungs()} rungs")
     for i, (M, N, K) in enumerate(GEMM_SHAPES):
         print(f"i8 gemm rung={rung} {fmt} dtype={dtype} M={M} N={N} K={K}", flush=True)
         c = Case(fmt, M, N, K, dtype, seed=900 + 10 * i + rung, group=128)
