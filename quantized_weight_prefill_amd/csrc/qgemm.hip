@@ -1969,9 +1969,11 @@ enum I8Rung {
     I8_M256 = 1,      // 256x128, 8 waves of 32x128: each weight unpacked once for 256 rows
     I8_M128_K2 = 2,   // 128x128, K split over two 4-wave groups
     I8_M256N96 = 3,   // 256x96, 8 waves of 32x96
-    I8_RUNG_COUNT = 4
+    I8_M512N96 = 4,   // 512x96, 8 waves of 64x96: each weight unpacked once for 512 rows
+    I8_RUNG_COUNT = 5
 };
-const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x96"};
+const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x96",
+                                                   "i8-512x96"};
 // int32 sums stay exact while K * 127 * 127 < 2^31
 constexpr long long kI8MaxK = 131072;
 
@@ -1990,6 +1992,7 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.waves = 4 * pl.kw;
         break;
     case I8_M256N96: pl.rows = 256; pl.cols = 96; pl.waves = 8; break;
+    case I8_M512N96: pl.rows = 512; pl.cols = 96; pl.waves = 8; break;
     default: return QGEMM_ERR_FORMAT;
     }
     const long long np = (N + 15) / 16;
@@ -2001,23 +2004,26 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
     return QGEMM_OK;
 }
 
-// The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 512..4096):
+// The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 512..4096).
+// The unpack costs about four VALU instructions per weight, so a tile is
+// VALU-bound unless many rows share each unpacked weight:
 //  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
 //    tile with K split over two wave groups (o and down at M = 658);
 //  * up to 128 rows: the 128x128 tile;
-//  * otherwise a 256-row tile, 128 or 96 columns wide, whichever finishes
-//    in fewer rounds of one workgroup per CU, a round of 96-wide tiles
-//    counting 0.85 of a 128-wide one (measured: 114 against 119 us for the
-//    merged gate_up at M = 658, 768 against 576 tiles; 154 against 137 us
-//    at M = 2048, 1024 against 768 tiles).
+//  * otherwise the 256x128, 256x96 or 512x96 tile, whichever finishes in the
+//    fewest rounds of one workgroup per CU, a round costing 1, 0.85 and 1.35
+//    (fitted to the measured times: gate_up at M = 658 117.6 us on 256x96
+//    against 123 on 256x128 and 120 on 512x96; M = 2048 125.6 us on 512x96
+//    against 140 on 256x128; M = 4096 249 against 277).
 int i8_select(long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8);
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
     if (M <= 128) return I8_M128;
-    const long long tm = (M + 255) / 256;
+    const long long tm256 = (M + 255) / 256, tm512 = (M + 511) / 512, tn128 = (np + 7) / 8, tn96 = (np + 5) / 6;
     const auto rounds = [](long long tiles) { return (double)((tiles + kCUs - 1) / kCUs); };
-    const double c128 = rounds(tm * ((np + 7) / 8)), c96 = 0.85 * rounds(tm * ((np + 5) / 6));
+    const double c128 = rounds(tm256 * tn128), c96 = 0.85 * rounds(tm256 * tn96), c512 = 1.35 * rounds(tm512 * tn96);
+    if (c512 < c96 && c512 < c128) return I8_M512N96;
     return c96 < c128 ? I8_M256N96 : I8_M256;
 }
 
@@ -2037,8 +2043,11 @@ hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
         else
             hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
         break;
-    default:
+    case I8_M256N96:
         hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 6, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
         break;
     }
     return hipGetLastError();
