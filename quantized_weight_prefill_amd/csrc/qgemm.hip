@@ -1328,7 +1328,12 @@ __device__ __forceinline__ void store_block_i8(const Args &a, const i32x16 &v, i
 // int8 MFMAs.  A chunk is four k-steps of 32; run g of a column (32 codes)
 // is k-step g, lane halves 0 (words 0, 1) and 1 (words 2, 3), so both
 // operands carry k = 128c + 32s + 16h + 0..15 in lane (r, h) of k-step s.
-template <int FMT, int WM, int WPB, int NWM, int NWN>
+// CPB chunks share one LDS stage and one barrier (a stage of 4*CPB k-steps;
+// chunk j of a stage is k-steps 4j .. 4j+3): an int8 chunk is only four
+// k-steps of MFMAs, so with CPB = 2 the barrier and the LDS round trip after
+// it are paid half as often.  Each thread then unpacks one run of each chunk
+// of the stage (same column and lane group).
+template <int FMT, int WM, int WPB, int NWM, int NWN, int CPB>
 struct StreamI8 {
     static constexpr int NTG = 64 * NWM * NWN;
     static constexpr int PB = WPB * NWN;
@@ -1339,10 +1344,13 @@ struct StreamI8 {
     static constexpr int RUNS = PB * 64;
     static constexpr int UPT = (RUNS + NTG - 1) / NTG;
     static constexpr int UFULL = RUNS / NTG;
+    static constexpr int KSTEPS = 4 * CPB;  // k-steps per stage
     static_assert(WPB % 2 == 0 && WM % 32 == 0, "32x32 blocks");
     static_assert(UPT >= 1 && (RUNS - UFULL * NTG) % 64 == 0, "a partial slot must cover whole waves");
-    typedef u32x4 Lds[2][CB][4][64];
+    static_assert(CPB == 1 || CPB == 2, "one or two chunks per stage");
+    typedef u32x4 Lds[2][CB][KSTEPS][64];
 
+    // Stages [c_lo, c_hi) (stage t = chunks CPB*t .. CPB*t+CPB-1).
     static __device__ __forceinline__ void run(const Args &a, Lds &sW, int tid, int lane, int wn, int m0, int p0,
                                                int c_lo, int c_hi, i32x16 (&acc)[CBW][RBW])
     {
@@ -1357,9 +1365,9 @@ struct StreamI8 {
         xrow[rb] = Xq + (long long)blk * 32 * a.K + (lane & 31) * 16 + (lane >> 5) * 512;
     }
 
-    u32x4 xf[RBW][4];
+    u32x4 xf[RBW][KSTEPS];
     RunSrc<FMT> src[UPT];
-    RunRaw<FMT> raw[UPT];
+    RunRaw<FMT> raw[UPT][CPB];
     int slot_cp[UPT], slot_lane[UPT];
     float rs[UPT];
 #pragma unroll
@@ -1376,51 +1384,62 @@ struct StreamI8 {
     }
     const bool extra = __builtin_amdgcn_readfirstlane(tid >> 6) < (RUNS - UFULL * NTG) / 64;
     auto live = [&](int s) { return s < UFULL || extra; };
-    auto put = [&](int buf, int s, int h, u32x4 v) {
-        if (live(s)) sW[buf][slot_cp[s]][src[s].g][h * 32 + slot_lane[s]] = v;
+    // run g of chunk j of the stage is k-step 4j + g
+    auto put = [&](int buf, int s, int j, int h, u32x4 v) {
+        if (live(s)) sW[buf][slot_cp[s]][4 * j + src[s].g][h * 32 + slot_lane[s]] = v;
     };
-    auto xload = [&](int rb, int c, int ks) {
-        return *reinterpret_cast<const u32x4 *>(xrow[rb] + (long long)c * 4096 + ks * 1024);
+    auto xload = [&](int rb, int t, int ks) {
+        return *reinterpret_cast<const u32x4 *>(xrow[rb] + (long long)t * (CPB * 4096) + ks * 1024);
+    };
+    auto load_stage = [&](int t, RunRaw<FMT>(&r)[UPT][CPB]) {
+#pragma unroll
+        for (int s = 0; s < UPT; s++)
+#pragma unroll
+            for (int j = 0; j < CPB; j++) src[s].load(CPB * t + j, r[s][j]);
     };
 
-#pragma unroll
-    for (int s = 0; s < UPT; s++) src[s].load(c_lo, raw[s]);
+    load_stage(c_lo, raw);
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) xf[rb][ks] = xload(rb, c_lo, ks);
+        for (int ks = 0; ks < KSTEPS; ks++) xf[rb][ks] = xload(rb, c_lo, ks);
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
-        const RunParams pr = run_params<FMT, DT_F16>(raw[s], src[s], c_lo);
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const u32x2 w0 = unpack_word_i8<FMT>(raw[s], pr, 2 * h, rs[s]);
-            const u32x2 w1 = unpack_word_i8<FMT>(raw[s], pr, 2 * h + 1, rs[s]);
-            put(0, s, h, u32x4{w0.x, w0.y, w1.x, w1.y});
+        for (int j = 0; j < CPB; j++) {
+            const RunParams pr = run_params<FMT, DT_F16>(raw[s][j], src[s], CPB * c_lo + j);
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const u32x2 w0 = unpack_word_i8<FMT>(raw[s][j], pr, 2 * h, rs[s]);
+                const u32x2 w1 = unpack_word_i8<FMT>(raw[s][j], pr, 2 * h + 1, rs[s]);
+                put(0, s, j, h, u32x4{w0.x, w0.y, w1.x, w1.y});
+            }
         }
     }
-    const int c1 = c_lo + 1 < c_hi ? c_lo + 1 : c_hi - 1;
-#pragma unroll
-    for (int s = 0; s < UPT; s++) src[s].load(c1, raw[s]);
+    load_stage(c_lo + 1 < c_hi ? c_lo + 1 : c_hi - 1, raw);
     __syncthreads();
 
-    RunRaw<FMT> raw2[UPT];
-    auto chunk = [&](int c, int buf, RunRaw<FMT>(&ru)[UPT], RunRaw<FMT>(&rf)[UPT]) {
-        const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
-        const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
-#pragma unroll
-        for (int s = 0; s < UPT; s++) src[s].load(cnn, rf[s]);
+    // One stage: MFMAs over LDS buffer `buf`, the unpack of stage t+1 (held
+    // in `ru`, one word of each of its runs per k-step) into the other
+    // buffer, and the raw loads of stage t+2 into `rf`, issued first.
+    RunRaw<FMT> raw2[UPT][CPB];
+    auto stage = [&](int t, int buf, RunRaw<FMT>(&ru)[UPT][CPB], RunRaw<FMT>(&rf)[UPT][CPB]) {
+        const int tn = t + 1 < c_hi ? t + 1 : c_hi - 1;
+        const int tnn = t + 2 < c_hi ? t + 2 : c_hi - 1;
+        load_stage(tnn, rf);
         u32x4 wcur[CBW], wnxt[CBW];
 #pragma unroll
         for (int cb = 0; cb < CBW; cb++) wcur[cb] = sW[buf][wn * CBW + cb][0][lane];
         __builtin_amdgcn_sched_barrier(0);
-        RunParams pr[UPT];
+        RunParams pr[UPT][CPB];
 #pragma unroll
-        for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT_F16>(ru[s], src[s], cn);
+        for (int s = 0; s < UPT; s++)
+#pragma unroll
+            for (int j = 0; j < CPB; j++) pr[s][j] = run_params<FMT, DT_F16>(ru[s][j], src[s], CPB * tn + j);
         u32x2 pend[UPT];
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) {
-            if (ks < 3) {
+        for (int ks = 0; ks < KSTEPS; ks++) {
+            if (ks < KSTEPS - 1) {
 #pragma unroll
                 for (int cb = 0; cb < CBW; cb++) wnxt[cb] = sW[buf][wn * CBW + cb][ks + 1][lane];
             }
@@ -1429,15 +1448,17 @@ struct StreamI8 {
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
                 for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma_i8(wcur[cb], xf[rb][ks], acc[cb][rb]);
-                xf[rb][ks] = xload(rb, cn, ks);
+                xf[rb][ks] = xload(rb, tn, ks);
             }
+            // word ks%4 of the runs of chunk ks/4
+            const int j = ks >> 2, i = ks & 3;
 #pragma unroll
             for (int s = 0; s < UPT; s++) {
-                const u32x2 wv = unpack_word_i8<FMT>(ru[s], pr[s], ks, rs[s]);
-                if (ks & 1) put(buf ^ 1, s, ks >> 1, u32x4{pend[s].x, pend[s].y, wv.x, wv.y});
+                const u32x2 wv = unpack_word_i8<FMT>(ru[s][j], pr[s][j], i, rs[s]);
+                if (i & 1) put(buf ^ 1, s, j, i >> 1, u32x4{pend[s].x, pend[s].y, wv.x, wv.y});
                 else pend[s] = wv;
             }
-            if (ks < 3) {
+            if (ks < KSTEPS - 1) {
 #pragma unroll
                 for (int cb = 0; cb < CBW; cb++) wcur[cb] = wnxt[cb];
             }
@@ -1445,20 +1466,20 @@ struct StreamI8 {
         }
         __syncthreads();
     };
-    int c = c_lo;
-    for (; c + 1 < c_hi; c += 2) {
-        chunk(c, 0, raw, raw2);
-        chunk(c + 1, 1, raw2, raw);
+    int t = c_lo;
+    for (; t + 1 < c_hi; t += 2) {
+        stage(t, 0, raw, raw2);
+        stage(t + 1, 1, raw2, raw);
     }
-    if (c < c_hi) chunk(c, 0, raw, raw2);
+    if (t < c_hi) stage(t, 0, raw, raw2);
     }
 };
 
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int CPB = 1>
 __global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_i8_stream(Args a)
 {
-    using S = StreamI8<FMT, WM, WPB, NWM, NWN>;
+    using S = StreamI8<FMT, WM, WPB, NWM, NWN, CPB>;
     constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
     constexpr int NACC = NWM * NWN * CBW * RBW * 64;
     // the partial sums of groups 1.. overlay the LDS of every group (free
@@ -1475,7 +1496,7 @@ k_i8_stream(Args a)
     int mt, nt;
     tile_coords(xcd_order(blockIdx.x, gridDim.x), tm, tn, mt, nt);
     const int m0 = mt * BM + wm * WM, p0 = nt * PB;
-    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
+    const int nstg = a.K / (kChunk * CPB) / KS, c_lo = kg * nstg, c_hi = c_lo + nstg;
 
     i32x16 acc[CBW][RBW];
 #pragma unroll
@@ -2027,30 +2048,44 @@ int i8_select(long long M, long long N, long long K)
     return c96 < c128 ? I8_M256N96 : I8_M256;
 }
 
-template <int FMT, int DT>
-hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
+template <int FMT, int DT, int CPB>
+hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
 {
-    switch (pl.rung) {
+    switch (base) {
     case I8_M128:
-        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1, CPB>), pl.grid, dim3(256), 0, s, a);
         break;
     case I8_M256:
-        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 8, 1, 1, CPB>), pl.grid, dim3(512), 0, s, a);
         break;
     case I8_M128_K2:
         if (pl.kw == 2)
-            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 2>), pl.grid, dim3(512), 0, s, a);
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 2, CPB>), pl.grid, dim3(512), 0, s, a);
         else
-            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1>), pl.grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 8, 4, 1, 1, CPB>), pl.grid, dim3(256), 0, s, a);
         break;
     case I8_M256N96:
-        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 8, 1, 1, CPB>), pl.grid, dim3(512), 0, s, a);
         break;
     default:
-        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 6, 8, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 6, 8, 1, 1, CPB>), pl.grid, dim3(512), 0, s, a);
         break;
     }
     return hipGetLastError();
+}
+
+// Two chunks per LDS stage (half the barriers; measured 3-7% faster on the
+// M = 658 layer GEMMs and 2% at M >= 2048) wherever the stages of each K
+// group cover its chunks exactly, i.e. the chunk count divides by 2 * (K
+// groups); one otherwise, and for the two combinations that measured slower
+// with two (W4A16 on 256x96: 155 against 137 us at M = 2048; Q6_K on
+// 512x96, which spills).
+template <int FMT, int DT>
+hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
+{
+    const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) || (FMT == FMT_Q6K && pl.rung == I8_M512N96);
+    if (!slower2 && (a.K / kChunk) % (2 * pl.kw) == 0) return launch_i8_cpb<FMT, DT, 2>(pl.rung, pl, a, s);
+    return launch_i8_cpb<FMT, DT, 1>(pl.rung, pl, a, s);
 }
 
 template <int DT>
@@ -2090,8 +2125,8 @@ int i8_gemm(int fmt, int rung, const void *Xq, const float *sx, const void *W, c
 
 int i8_quantize(const void *X, void *Xq, float *sx, long long M, long long K, int dtype, void *stream)
 {
+    // one workgroup per padded row: the grid fits while M + 31 does
     if (M < 0 || K < 32 || K % 32 != 0 || M > INT32_MAX - 31 || K > INT32_MAX) return QGEMM_ERR_SHAPE;
-    if ((M + 31) / 32 * 32 * K / 32 > INT32_MAX) return QGEMM_ERR_SHAPE;  // byte offsets of one block row fit
     if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
     if (M == 0) return QGEMM_OK;
     if (!X || !Xq || !sx) return QGEMM_ERR_NULL;

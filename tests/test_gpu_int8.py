@@ -144,3 +144,51 @@ def test_i8_fullsize_sampled(label):
     assert np.array_equal(_f32(sx).view(np.uint32), sxo.view(np.uint32))
     want = oracle.gemm_i8(Qx[rows], sxo[rows], oracle.requant_i8(W32[:, cols], r[cols]), s[cols], dt)
     assert same_bits(Y[np.ix_(rows, cols)], want)
+
+
+def test_i8_k_at_the_int32_limit():
+    """K = 131072 (the largest K the path accepts) with every code at +-127:
+    each int32 sum reaches 131072 * 127 * 127 = 2114060288, just below 2^31,
+    and must still be exact."""
+    M, N, K = 3, 32, 131072
+    print(f"i8 K limit M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(8)
+    X = np.where(rng.random((M, K)) < 0.5, 1.0, -1.0)
+    X[1] = 1.0  # an all-positive row: its sums against a positive column are the maximum
+    Xb = synth.f16_bits(X)
+    f = synth.q6k_fields(rng, N, K)
+    # every weight d * s * (q - 32) with s = 1, q = 63 or 1 and one d per column: +-31 d, so every
+    # code is +-127
+    f["s"][:] = 1
+    f["d"][:] = f["d"][:, :1]
+    f["q"][:] = np.where(rng.random(f["q"].shape) < 0.5, 63, 1).astype(f["q"].dtype)
+    f["q"][0] = 63  # column 0 all positive
+    c = Case("q6k", M, N, K, qg.F16, seed=1, fields=f, X=Xb)
+    Y = _run_i8(c)
+    want = _oracle_y(c)
+    assert same_bits(Y, want)
+    W32 = _weights_f32(c)
+    r, _ = oracle.colscale_i8(W32)
+    Qx, _ = oracle.quant_rows_i8(Xb, qg.F16)
+    acc = Qx.astype(np.int64) @ oracle.requant_i8(W32, r).astype(np.int64)
+    assert acc.max() == 131072 * 127 * 127 < 2 ** 31
+
+
+def test_i8_bf16_rows_at_the_scale_floor():
+    """bf16 rows whose largest magnitude is just below 2^-96 quantize to zero
+    codes and a zero scale; a row at 2^-96 keeps full codes."""
+    M, N, K = 4, 48, 256
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[1] *= np.float32(2.0 ** -100)
+    X[2] = X[2] / np.abs(X[2]).max() * np.float32(2.0 ** -96)
+    Xb = synth.bf16_bits_from_f32(X)
+    c = Case("q4k", M, N, K, qg.BF16, seed=3, X=Xb)
+    wp = c.device_weights()
+    xq, sx = qg.i8_quantize(to_device(Xb, qg.BF16))
+    Q, s = oracle.quant_rows_i8(Xb, qg.BF16)
+    assert np.array_equal(_f32(sx).view(np.uint32), s.view(np.uint32)) and s[1] == 0 and s[2] > 0
+    assert np.array_equal(_i8(xq), oracle.fragment_major_i8(Q))
+    rw, sw = qg.i8_colscale("q4k", wp, N, K)
+    Y = from_device(qg.gemm_i8("q4k", xq, sx, wp, rw, sw, M, N, K, qg.BF16))
+    assert same_bits(Y, _oracle_y(c)) and not (Y[1] & 0x7FFF).any()
