@@ -1156,17 +1156,17 @@ __device__ __forceinline__ u32x2 vec_codes(u32x4 v, float r)
     return u32x2{pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])};
 }
 
-// Row quantizer: one 256-thread workgroup per row of the padded 32-row
-// blocks; each thread keeps up to kQv 8-element vectors of its row in
-// registers between the max and the code pass (longer rows reread the rest,
-// from L2).  Rows at or past M are written as zeros.
-constexpr int kQv = 8;
+// Row quantizer: one wave per row of the padded 32-row blocks, four rows per
+// workgroup.  Each lane keeps up to kQv 8-element vectors of its row in
+// registers between the max (a wave reduction, no LDS and no barrier) and
+// the code pass; rows longer than 64*8*kQv elements reread the rest (from
+// L2).  Rows at or past M are written as zeros.
+constexpr int kQv = 24;
 
 template <int DT>
 __global__ void __launch_bounds__(256) k_i8_quant(const uint16_t *X, uint8_t *Xq, float *sx, int M, int K)
 {
-    __shared__ float red[4];
-    const int m = blockIdx.x, tid = threadIdx.x, nv = K >> 3;
+    const int lane = threadIdx.x & 63, m = 4 * blockIdx.x + (threadIdx.x >> 6), nv = K >> 3;
     uint8_t *qrow = Xq + (long long)(m >> 5) * 32 * K + (m & 31) * 16;
     // the 8 codes of vector v (k = 8v .. 8v+7): one half of a lane's 16 bytes
     auto dst = [&](int v) -> u32x2 * {
@@ -1174,7 +1174,7 @@ __global__ void __launch_bounds__(256) k_i8_quant(const uint16_t *X, uint8_t *Xq
         return reinterpret_cast<u32x2 *>(qrow + (long long)(k >> 5) * 1024 + ((k >> 4) & 1) * 512 + (k & 15));
     };
     if (m >= M) {
-        for (int v = tid; v < nv; v += 256) *dst(v) = u32x2{0u, 0u};
+        for (int v = lane; v < nv; v += 64) *dst(v) = u32x2{0u, 0u};
         return;
     }
     const uint16_t *xr = X + (long long)m * K;
@@ -1182,27 +1182,24 @@ __global__ void __launch_bounds__(256) k_i8_quant(const uint16_t *X, uint8_t *Xq
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < kQv; j++) {
-        const int v = tid + 256 * j;
+        const int v = lane + 64 * j;
         held[j] = u32x4{0u, 0u, 0u, 0u};
         if (v < nv) held[j] = *reinterpret_cast<const u32x4 *>(xr + 8 * v);
         amax = fmaxf(amax, vec_amax<DT>(held[j]));
     }
-    for (int v = tid + 256 * kQv; v < nv; v += 256)
+    for (int v = lane + 64 * kQv; v < nv; v += 64)
         amax = fmaxf(amax, vec_amax<DT>(*reinterpret_cast<const u32x4 *>(xr + 8 * v)));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if ((tid & 63) == 0) red[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     float r, s;
     i8_scales(amax, r, s);
-    if (tid == 0) sx[m] = s;
+    if (lane == 0) sx[m] = s;
 #pragma unroll
     for (int j = 0; j < kQv; j++) {
-        const int v = tid + 256 * j;
+        const int v = lane + 64 * j;
         if (v < nv) *dst(v) = vec_codes<DT>(held[j], r);
     }
-    for (int v = tid + 256 * kQv; v < nv; v += 256) *dst(v) = vec_codes<DT>(*reinterpret_cast<const u32x4 *>(xr + 8 * v), r);
+    for (int v = lane + 64 * kQv; v < nv; v += 64) *dst(v) = vec_codes<DT>(*reinterpret_cast<const u32x4 *>(xr + 8 * v), r);
 }
 
 // The eight binary32 weights of word i of a run, in k order: the fp16
@@ -1991,10 +1988,11 @@ enum I8Rung {
     I8_M128_K2 = 2,   // 128x128, K split over two 4-wave groups
     I8_M256N96 = 3,   // 256x96, 8 waves of 32x96
     I8_M512N96 = 4,   // 512x96, 8 waves of 64x96: each weight unpacked once for 512 rows
-    I8_RUNG_COUNT = 5
+    I8_M352N96 = 5,   // 352x96, 11 waves of 32x96 (three per SIMD)
+    I8_RUNG_COUNT = 6
 };
 const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x96",
-                                                   "i8-512x96"};
+                                                   "i8-512x96", "i8-352x96"};
 // int32 sums stay exact while K * 127 * 127 < 2^31
 constexpr long long kI8MaxK = 131072;
 
@@ -2014,6 +2012,7 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
         break;
     case I8_M256N96: pl.rows = 256; pl.cols = 96; pl.waves = 8; break;
     case I8_M512N96: pl.rows = 512; pl.cols = 96; pl.waves = 8; break;
+    case I8_M352N96: pl.rows = 352; pl.cols = 96; pl.waves = 11; break;
     default: return QGEMM_ERR_FORMAT;
     }
     const long long np = (N + 15) / 16;
@@ -2031,21 +2030,29 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
 //    tile with K split over two wave groups (o and down at M = 658);
 //  * up to 128 rows: the 128x128 tile;
-//  * otherwise the 256x128, 256x96 or 512x96 tile, whichever finishes in the
-//    fewest rounds of one workgroup per CU, a round costing 1, 0.85 and 1.35
-//    (fitted to the measured times: gate_up at M = 658 117.6 us on 256x96
-//    against 123 on 256x128 and 120 on 512x96; M = 2048 125.6 us on 512x96
-//    against 140 on 256x128; M = 4096 249 against 277).
+//  * otherwise the 256x128, 256x96, 352x96 or 512x96 tile, whichever
+//    finishes in the fewest rounds of one workgroup per CU, a round costing
+//    1, 0.85, 1.17 and 1.35 (fitted to the measured times: the merged
+//    gate_up at M = 658 91 us on 352x96 against 107 on 256x96 and 117 on
+//    256x128; M = 2048 121 us on 512x96 against 133 on 256x128 and 138 on
+//    352x96; M = 4096 238 against 260 and 268).  The 352-row tile runs three
+//    waves per SIMD and unpacks each weight for 352 rows: two of its row
+//    tiles cover M = 658 where 256-row tiles need three.
 int i8_select(long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8);
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
     if (M <= 128) return I8_M128;
-    const long long tm256 = (M + 255) / 256, tm512 = (M + 511) / 512, tn128 = (np + 7) / 8, tn96 = (np + 5) / 6;
+    const long long tm256 = (M + 255) / 256, tm352 = (M + 351) / 352, tm512 = (M + 511) / 512;
+    const long long tn128 = (np + 7) / 8, tn96 = (np + 5) / 6;
     const auto rounds = [](long long tiles) { return (double)((tiles + kCUs - 1) / kCUs); };
-    const double c128 = rounds(tm256 * tn128), c96 = 0.85 * rounds(tm256 * tn96), c512 = 1.35 * rounds(tm512 * tn96);
-    if (c512 < c96 && c512 < c128) return I8_M512N96;
-    return c96 < c128 ? I8_M256N96 : I8_M256;
+    const double c[4] = {rounds(tm256 * tn128), 0.85 * rounds(tm256 * tn96), 1.17 * rounds(tm352 * tn96),
+                         1.35 * rounds(tm512 * tn96)};
+    const int rung[4] = {I8_M256, I8_M256N96, I8_M352N96, I8_M512N96};
+    int best = 0;
+    for (int i = 1; i < 4; i++)
+        if (c[i] < c[best]) best = i;
+    return rung[best];
 }
 
 template <int FMT, int DT, int CPB>
@@ -2067,6 +2074,9 @@ hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
     case I8_M256N96:
         hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 8, 1, 1, CPB>), pl.grid, dim3(512), 0, s, a);
         break;
+    case I8_M352N96:
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 11, 1, 1, CPB>), pl.grid, dim3(704), 0, s, a);
+        break;
     default:
         hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 6, 8, 1, 1, CPB>), pl.grid, dim3(512), 0, s, a);
         break;
@@ -2077,13 +2087,14 @@ hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
 // Two chunks per LDS stage (half the barriers; measured 3-7% faster on the
 // M = 658 layer GEMMs and 2% at M >= 2048) wherever the stages of each K
 // group cover its chunks exactly, i.e. the chunk count divides by 2 * (K
-// groups); one otherwise, and for the two combinations that measured slower
-// with two (W4A16 on 256x96: 155 against 137 us at M = 2048; Q6_K on
-// 512x96, which spills).
+// groups); one otherwise, and for the combinations that measured slower
+// with two (W4A16 on 256x96: 155 against 137 us at M = 2048) or spill with
+// two (Q6_K on 512x96 and on 352x96).
 template <int FMT, int DT>
 hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
-    const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) || (FMT == FMT_Q6K && pl.rung == I8_M512N96);
+    const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) ||
+                         (FMT == FMT_Q6K && (pl.rung == I8_M512N96 || pl.rung == I8_M352N96));
     if (!slower2 && (a.K / kChunk) % (2 * pl.kw) == 0) return launch_i8_cpb<FMT, DT, 2>(pl.rung, pl, a, s);
     return launch_i8_cpb<FMT, DT, 1>(pl.rung, pl, a, s);
 }
@@ -2125,19 +2136,19 @@ int i8_gemm(int fmt, int rung, const void *Xq, const float *sx, const void *W, c
 
 int i8_quantize(const void *X, void *Xq, float *sx, long long M, long long K, int dtype, void *stream)
 {
-    // one workgroup per padded row: the grid fits while M + 31 does
+    // one wave per padded row: the grid fits while M + 31 does
     if (M < 0 || K < 32 || K % 32 != 0 || M > INT32_MAX - 31 || K > INT32_MAX) return QGEMM_ERR_SHAPE;
     if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
     if (M == 0) return QGEMM_OK;
     if (!X || !Xq || !sx) return QGEMM_ERR_NULL;
     if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return QGEMM_ERR_ALIGN;
-    const unsigned rows = (unsigned)((M + 31) / 32 * 32);
+    const unsigned groups = (unsigned)((M + 31) / 32 * 8);  // four padded rows per workgroup
     hipStream_t s = (hipStream_t)stream;
     if (dtype == DT_F16)
-        hipLaunchKernelGGL((k_i8_quant<DT_F16>), dim3(rows), dim3(256), 0, s, (const uint16_t *)X, (uint8_t *)Xq, sx,
+        hipLaunchKernelGGL((k_i8_quant<DT_F16>), dim3(groups), dim3(256), 0, s, (const uint16_t *)X, (uint8_t *)Xq, sx,
                            (int)M, (int)K);
     else
-        hipLaunchKernelGGL((k_i8_quant<DT_BF16>), dim3(rows), dim3(256), 0, s, (const uint16_t *)X, (uint8_t *)Xq, sx,
+        hipLaunchKernelGGL((k_i8_quant<DT_BF16>), dim3(groups), dim3(256), 0, s, (const uint16_t *)X, (uint8_t *)Xq, sx,
                            (int)M, (int)K);
     return launch_status(hipGetLastError(), "i8 quantize");
 }
