@@ -832,9 +832,10 @@ struct Stream32 {
     int slot_cp[UPT], slot_lane[UPT];
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
-        // the last slot may exist only for the first waves; the others
-        // shadow a real run (loads stay in bounds) and never store it
-        const int u0 = tid + NTG * s, u = u0 < RUNS ? u0 : u0 - NTG, pl = u >> 6, col = u & 15;
+        // the last slot may exist only for the first waves (every slot, when
+        // a tile has fewer runs than threads); the others shadow a real run
+        // (loads stay in bounds) and never store it
+        const int u0 = tid + NTG * s, u = u0 < RUNS ? u0 : u0 % RUNS, pl = u >> 6, col = u & 15;
         const int p = p0 + pl;
         src[s].init(a, p < a.np ? p : a.np - 1, (u >> 4) & 3, col);
         slot_cp[s] = pl >> 1;
@@ -1543,11 +1544,12 @@ enum Rung {
     RUNG_M128_K2 = 5,     // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
     RUNG_M128N160 = 6,    // 32x32x16 MFMA: 128x160, 4 waves of 32x160
     RUNG_M64_K4 = 7,      // 32x32x16 MFMA: 64x64, 2 waves of 32x64, K split over four groups
-    RUNG_COUNT = 8
+    RUNG_M352N96 = 8,     // 32x32x16 MFMA: 352x96, 11 waves of 32x96
+    RUNG_COUNT = 9
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
-                                            "mfma32-128x160",    "mfma32-64x64-k4"};
+                                            "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96"};
 
 struct Plan {
     int rung;
@@ -1606,12 +1608,13 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128:
     case RUNG_M128_K2:
     case RUNG_M128N160:
-    case RUNG_M64_K4: {
-        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : 128;
-        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64_K4 ? 64 : 128;
+    case RUNG_M64_K4:
+    case RUNG_M352N96: {
+        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 352 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 96 : 128;
         pl.kw = (rung == RUNG_M128_K2 && (K / kChunk) % 2 == 0) ? 2 : 1;
         if (rung == RUNG_M64_K4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
-        pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : 4 * pl.kw;
+        pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11 : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
         if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
@@ -1718,6 +1721,17 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
     if (t128 < 128) return mid_m_rung(fmt, M, np);
+    // on fragment-major activations, the 352x96 tile (11 waves, three per
+    // SIMD) when its rounds, each costing 1.22 rounds of the 256-row tile,
+    // come out cheapest: two of its row tiles cover M = 641..704 where
+    // 256-row tiles need three (merged gate_up at M = 658: 147 against 173 us;
+    // M = 700, N = 12288: 76 against 95 us for 128x160).  Q6_K's larger raw
+    // runs spill in it.
+    if (xl == X_FRAG && fmt != FMT_Q6K) {
+        const long long t352 = ((np + 5) / 6) * ((M + 351) / 352);
+        const double c352 = 2.44 * (double)((t352 + kCUs - 1) / kCUs);
+        if (c352 < c256 && c352 < c128) return RUNG_M352N96;
+    }
     // the 256-row tile when the occupancy model has it finish no later than
     // the 128-row tiles (it unpacks each weight once for 256 rows); on
     // fragment-major activations also whenever it has 512 tiles
@@ -1777,6 +1791,9 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         return hipGetLastError();
     case RUNG_M128N160:
         hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 10, 4, 1, 1, XL>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M352N96:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 6, 11, 1, 1, XL>), pl.grid, dim3(704), 0, s, a);
         return hipGetLastError();
     case RUNG_M64_K4:
         if ((a.K / kChunk) % 4 == 0)

@@ -322,16 +322,22 @@ def test_ladder_mid_m_round_model():
 def test_ladder_fragment_major():
     """The ladder for fragment-major activations: the K-split 128x128 tile for
     every shape with at most 256 of its tiles (row-major only over a long K),
-    the 256-row tile also whenever it has 512 tiles; otherwise the same rung
-    as for row-major activations."""
+    the 352x96 tile where its rounds cost least (two of its row tiles cover
+    M = 641..704), the 256-row tile also whenever it has 512 tiles; otherwise
+    the same rung as for row-major activations."""
     assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-128x128-k2"
     assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128-k2"
     assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"        # row-major: K < 8192
     assert qg.select_rung_xf("q6k", 300, 4096, 12288)["name"] == "mfma32-64x64-k4"    # round model, below 128 tiles
     assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
     assert qg.select_rung_xf("q4k", 512, 12288, 4096)["name"] == "mfma16-256x128"
-    assert qg.select_rung_xf("q4k", 1400, 12288, 4096)["name"] == "mfma16-256x128"    # 576 tiles of 256x128
-    for fmt, M, K, N in [("q4k", 658, 4096, 12288), ("q4k", 658, 4096, 1024), ("q4k", 16, 4096, 12288),
+    # 512 tiles of 352x96 in two rounds against 576 of 256x128 in three
+    assert qg.select_rung_xf("q4k", 1400, 12288, 4096)["name"] == "mfma32-352x96"
+    assert qg.select_rung_xf("q4k", 658, 24576, 4096)["name"] == "mfma32-352x96"       # merged gate_up
+    assert qg.select_rung("q4k", 658, 24576, 4096)["name"] == "mfma32-128x160"         # row-major: not measured
+    assert qg.select_rung_xf("q6k", 658, 24576, 4096)["name"] != "mfma32-352x96"       # spills for Q6_K
+    assert qg.select_rung_xf("q4k", 2048, 12288, 4096)["name"] == "mfma16-256x128"    # 768 tiles: three rounds either way
+    for fmt, M, K, N in [("q4k", 658, 4096, 1024), ("q4k", 16, 4096, 12288),
                          ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
                          ("q6k", 1024, 12288, 4096)]:
         assert qg.select_rung_xf(fmt, M, N, K)["name"] == qg.select_rung(fmt, M, N, K)["name"], (fmt, M, K, N)
