@@ -938,7 +938,10 @@ k_stream32(Args a)
     constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
     // f32x16 partial sums one K group hands over: one per (wave, block, lane)
     constexpr int NACC = NWM * NWN * CBW * RBW * 64;
-    static_assert(KS == 1 || NACC * sizeof(f32x16) <= sizeof(typename S::Lds), "K-split reduction must fit in LDS");
+    // the partial sums of groups 1.. overlay the LDS of every group (free
+    // once all groups have passed their last chunk's barrier)
+    static_assert(KS == 1 || (KS - 1) * NACC * sizeof(f32x16) <= KS * sizeof(typename S::Lds),
+                  "K-split reduction must fit in LDS");
     __shared__ typename S::Lds sWall[KS];
 
     const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
@@ -960,10 +963,10 @@ k_stream32(Args a)
             for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0.f;
     S::run(a, sWall[kg], tid, lane, wn, m0, p0, c_lo, c_hi, acc);
     if constexpr (KS > 1) {
-        // K groups 1..KS-1 hand their partial sums to group 0 through the LDS
-        // of groups 1.. (free once every group has passed its last chunk's
+        // K groups 1..KS-1 hand their partial sums to group 0 through LDS
+        // (all of it is free once every group has passed its last chunk's
         // barrier); group 0 adds them in group order, independent of timing.
-        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[1]);
+        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[0]);
         if (kg > 0) {
 #pragma unroll
             for (int cb = 0; cb < CBW; cb++)
@@ -1545,11 +1548,13 @@ enum Rung {
     RUNG_M128N160 = 6,    // 32x32x16 MFMA: 128x160, 4 waves of 32x160
     RUNG_M64_K4 = 7,      // 32x32x16 MFMA: 64x64, 2 waves of 32x64, K split over four groups
     RUNG_M352N96 = 8,     // 32x32x16 MFMA: 352x96, 11 waves of 32x96
-    RUNG_COUNT = 9
+    RUNG_M192N96_K2 = 9,  // 32x32x16 MFMA: 192x96, K split over two 6-wave groups (three waves per SIMD)
+    RUNG_COUNT = 10
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
-                                            "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96"};
+                                            "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
+                                            "mfma32-192x96-k2"};
 
 struct Plan {
     int rung;
@@ -1609,12 +1614,16 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128_K2:
     case RUNG_M128N160:
     case RUNG_M64_K4:
-    case RUNG_M352N96: {
-        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 352 : 128;
-        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 96 : 128;
-        pl.kw = (rung == RUNG_M128_K2 && (K / kChunk) % 2 == 0) ? 2 : 1;
+    case RUNG_M352N96:
+    case RUNG_M192N96_K2: {
+        const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2;
+        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 352
+                  : rung == RUNG_M192N96_K2 ? 192 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64_K4 ? 64 : n96 ? 96 : 128;
+        pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M192N96_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
         if (rung == RUNG_M64_K4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
-        pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11 : 4 * pl.kw;
+        pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11
+                   : rung == RUNG_M192N96_K2 ? 6 * pl.kw : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
         if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
@@ -1737,8 +1746,17 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // fragment-major activations also whenever it has 512 tiles
     if (c256 <= c128 || (xl == X_FRAG && t256 >= 512)) return RUNG_M16_256;
     // few tiles: split K inside the workgroup (on row-major activations only
-    // over a long K, where the halves' activation reloads stay affordable)
-    if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) return RUNG_M128_K2;
+    // over a long K, where the halves' activation reloads stay affordable).
+    // On fragment-major activations the 192x96 tile (two 6-wave groups,
+    // three waves per SIMD) where its tiles fit one round and cover M with no
+    // more rows than 128-row tiles (o and down at M = 658: 40 and 120 us
+    // against 43 and 132 us for 128x128).
+    if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) {
+        const long long r192 = (M + 191) / 192;
+        if (xl == X_FRAG && r192 * ((np + 5) / 6) <= kCUs && r192 * 192 <= (M + 127) / 128 * 128)
+            return RUNG_M192N96_K2;
+        return RUNG_M128_K2;
+    }
     // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
     // runs do not fit that variant's registers)
     if (fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128)) return RUNG_M128N160;
@@ -1794,6 +1812,12 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         return hipGetLastError();
     case RUNG_M352N96:
         hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 6, 11, 1, 1, XL>), pl.grid, dim3(704), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M192N96_K2:
+        if (even)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 6, 6, 1, 2, XL>), pl.grid, dim3(768), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 6, 6, 1, 1, XL>), pl.grid, dim3(384), 0, s, a);
         return hipGetLastError();
     case RUNG_M64_K4:
         if ((a.K / kChunk) % 4 == 0)

@@ -320,13 +320,18 @@ def test_ladder_mid_m_round_model():
 
 
 def test_ladder_fragment_major():
-    """The ladder for fragment-major activations: the K-split 128x128 tile for
-    every shape with at most 256 of its tiles (row-major only over a long K),
+    """The ladder for fragment-major activations: a K-split tile for every
+    shape with at most 256 tiles of 128x128 (row-major only over a long K;
+    192x96 where it fits one round without more padding, else 128x128),
     the 352x96 tile where its rounds cost least (two of its row tiles cover
     M = 641..704), the 256-row tile also whenever it has 512 tiles; otherwise
     the same rung as for row-major activations."""
-    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-128x128-k2"
-    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128-k2"
+    # few tiles on fragment-major X: the 192x96 K-split tile where its 172 tiles fit one round and its
+    # 768 rows are no more than the 128-row tiles' (down and o); 128x128 when 192-row tiles pad more
+    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-192x96-k2"
+    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-192x96-k2"
+    assert qg.select_rung_xf("q4k", 200, 12288, 4096)["name"] == "mfma32-128x128-k2"
+    assert qg.select_rung_xf("q4k", 1000, 4096, 4096)["name"] == "mfma32-128x128-k2"
     assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"        # row-major: K < 8192
     assert qg.select_rung_xf("q6k", 300, 4096, 12288)["name"] == "mfma32-64x64-k4"    # round model, below 128 tiles
     assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
@@ -345,7 +350,7 @@ def test_ladder_fragment_major():
         for M in list(range(1, 70)) + [96, 200, 300, 511, 658, 1000, 1024, 4096]:
             info = qg.select_rung_xf("w4a16", M, N, K)
             assert info["tiles_n"] * info["cols"] >= N and info["tiles_m"] * info["rows"] >= M
-            if info["name"] == "mfma32-128x128-k2":
+            if info["name"] in ("mfma32-128x128-k2", "mfma32-192x96-k2"):
                 assert info["tiles_n"] * info["tiles_m"] <= 256
 
 
