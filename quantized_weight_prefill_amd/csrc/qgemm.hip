@@ -1484,10 +1484,12 @@ k_i8_stream(Args a)
     constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
     constexpr int NACC = NWM * NWN * CBW * RBW * 64;
     // the partial sums of groups 1.. overlay the LDS of every group (free
-    // once all groups have passed their last chunk's barrier)
-    static_assert(KS == 1 || (KS - 1) * NACC * sizeof(i32x16) <= KS * sizeof(typename S::Lds),
-                  "K-split reduction must fit in LDS");
-    __shared__ typename S::Lds sWall[KS];
+    // once all groups have passed their last stage's barrier); the array is
+    // sized for whichever of the two needs more
+    constexpr size_t kStageBytes = KS * sizeof(typename S::Lds);
+    constexpr size_t kRedBytes = KS > 1 ? (KS - 1) * NACC * sizeof(i32x16) : 0;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
+    auto &sWall = *reinterpret_cast<typename S::Lds(*)[KS]>(smem);
 
     const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
     const int kg = wall / (NWM * NWN);
@@ -1509,7 +1511,7 @@ k_i8_stream(Args a)
     S::run(a, sWall[kg], tid, lane, wn, m0, p0, c_lo, c_hi, acc);
     if constexpr (KS > 1) {
         // integer partial sums: the order of the additions does not matter
-        i32x16 *red = reinterpret_cast<i32x16 *>(&sWall[0]);
+        i32x16 *red = reinterpret_cast<i32x16 *>(smem);
         if (kg > 0) {
 #pragma unroll
             for (int cb = 0; cb < CBW; cb++)
@@ -1730,6 +1732,15 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
     if (t128 < 128) return mid_m_rung(fmt, M, np);
+    // on fragment-major activations, the 192x96 tile with K split over two
+    // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
+    // and cover M with no more rows than 128-row tiles (qkv, o and down at
+    // M = 658: 49, 40 and 120 us against 62 for 128x160, 43 and 132 for the
+    // 128x128 K-split tile)
+    const long long r192 = (M + 191) / 192;
+    if (xl == X_FRAG && (K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs &&
+        r192 * 192 <= (M + 127) / 128 * 128)
+        return RUNG_M192N96_K2;
     // on fragment-major activations, the 352x96 tile (11 waves, three per
     // SIMD) when its rounds, each costing 1.22 rounds of the 256-row tile,
     // come out cheapest: two of its row tiles cover M = 641..704 where
@@ -1746,17 +1757,8 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // fragment-major activations also whenever it has 512 tiles
     if (c256 <= c128 || (xl == X_FRAG && t256 >= 512)) return RUNG_M16_256;
     // few tiles: split K inside the workgroup (on row-major activations only
-    // over a long K, where the halves' activation reloads stay affordable).
-    // On fragment-major activations the 192x96 tile (two 6-wave groups,
-    // three waves per SIMD) where its tiles fit one round and cover M with no
-    // more rows than 128-row tiles (o and down at M = 658: 40 and 120 us
-    // against 43 and 132 us for 128x128).
-    if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) {
-        const long long r192 = (M + 191) / 192;
-        if (xl == X_FRAG && r192 * ((np + 5) / 6) <= kCUs && r192 * 192 <= (M + 127) / 128 * 128)
-            return RUNG_M192N96_K2;
-        return RUNG_M128_K2;
-    }
+    // over a long K, where the halves' activation reloads stay affordable)
+    if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) return RUNG_M128_K2;
     // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
     // runs do not fit that variant's registers)
     if (fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128)) return RUNG_M128N160;
@@ -2030,10 +2032,11 @@ enum I8Rung {
     I8_M256N96 = 3,   // 256x96, 8 waves of 32x96
     I8_M512N96 = 4,   // 512x96, 8 waves of 64x96: each weight unpacked once for 512 rows
     I8_M352N96 = 5,   // 352x96, 11 waves of 32x96 (three per SIMD)
-    I8_RUNG_COUNT = 6
+    I8_M192N96_K2 = 6,  // 192x96, K split over two 6-wave groups (three waves per SIMD)
+    I8_RUNG_COUNT = 7
 };
 const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x96",
-                                                   "i8-512x96", "i8-352x96"};
+                                                   "i8-512x96", "i8-352x96", "i8-192x96-k2"};
 // int32 sums stay exact while K * 127 * 127 < 2^31
 constexpr long long kI8MaxK = 131072;
 
@@ -2054,6 +2057,12 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case I8_M256N96: pl.rows = 256; pl.cols = 96; pl.waves = 8; break;
     case I8_M512N96: pl.rows = 512; pl.cols = 96; pl.waves = 8; break;
     case I8_M352N96: pl.rows = 352; pl.cols = 96; pl.waves = 11; break;
+    case I8_M192N96_K2:
+        pl.rows = 192;
+        pl.cols = 96;
+        pl.kw = (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = 6 * pl.kw;
+        break;
     default: return QGEMM_ERR_FORMAT;
     }
     const long long np = (N + 15) / 16;
@@ -2068,6 +2077,10 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 // The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 512..4096).
 // The unpack costs about four VALU instructions per weight, so a tile is
 // VALU-bound unless many rows share each unpacked weight:
+//  * with an even chunk count, the 192x96 tile with K split over two 6-wave
+//    groups (three waves per SIMD) when its tiles fit one round and cover M
+//    with no more rows than 128-row tiles (qkv, o and down at M = 658: 32.7,
+//    28.5 and 75 us against 34, 32 and 84 us);
 //  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
 //    tile with K split over two wave groups (o and down at M = 658);
 //  * up to 128 rows: the 128x128 tile;
@@ -2081,7 +2094,9 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    tiles cover M = 658 where 256-row tiles need three.
 int i8_select(long long M, long long N, long long K)
 {
-    const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8);
+    const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8), r192 = (M + 191) / 192;
+    if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs && r192 * 192 <= (M + 127) / 128 * 128)
+        return I8_M192N96_K2;
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
     if (M <= 128) return I8_M128;
     const long long tm256 = (M + 255) / 256, tm352 = (M + 351) / 352, tm512 = (M + 511) / 512;
@@ -2118,6 +2133,12 @@ hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
     case I8_M352N96:
         hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 11, 1, 1, CPB>), pl.grid, dim3(704), 0, s, a);
         break;
+    case I8_M192N96_K2:
+        if (pl.kw == 2)
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 6, 1, 2, CPB>), pl.grid, dim3(768), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 6, 1, 1, CPB>), pl.grid, dim3(384), 0, s, a);
+        break;
     default:
         hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 6, 8, 1, 1, CPB>), pl.grid, dim3(512), 0, s, a);
         break;
@@ -2130,11 +2151,11 @@ hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
 // group cover its chunks exactly, i.e. the chunk count divides by 2 * (K
 // groups); one otherwise, and for the combinations that measured slower
 // with two (W4A16 on 256x96: 155 against 137 us at M = 2048) or spill with
-// two (Q6_K on 512x96 and on 352x96).
+// two (Q6_K on 512x96 and on 352x96, every format on 192x96 split in two).
 template <int FMT, int DT>
 hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
-    const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) ||
+    const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) || pl.rung == I8_M192N96_K2 ||
                          (FMT == FMT_Q6K && (pl.rung == I8_M512N96 || pl.rung == I8_M352N96));
     if (!slower2 && (a.K / kChunk) % (2 * pl.kw) == 0) return launch_i8_cpb<FMT, DT, 2>(pl.rung, pl, a, s);
     return launch_i8_cpb<FMT, DT, 1>(pl.rung, pl, a, s);
