@@ -1736,22 +1736,26 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
     // and cover M with no more rows than 128-row tiles (qkv, o and down at
     // M = 658: 49, 40 and 120 us against 62 for 128x160, 43 and 132 for the
-    // 128x128 K-split tile)
-    const long long r192 = (M + 191) / 192;
-    if (xl == X_FRAG && (K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs &&
-        r192 * 192 <= (M + 127) / 128 * 128)
-        return RUNG_M192N96_K2;
+    // 128x128 K-split tile); after the 352x96 check below, also over two
+    // rounds at least 90% full (M = 768, N = 12288: Q4_K 90 against 101, Q6_K
+    // 254 against 331 us; with 1.5 or three rounds it loses to the 256-row
+    // tile)
+    const long long r192 = (M + 191) / 192, t192 = r192 * ((np + 5) / 6);
+    const bool k2_192 = xl == X_FRAG && (K / kChunk) % 2 == 0 && r192 * 192 <= (M + 127) / 128 * 128;
+    if (k2_192 && t192 <= kCUs) return RUNG_M192N96_K2;
     // on fragment-major activations, the 352x96 tile (11 waves, three per
     // SIMD) when its rounds, each costing 1.22 rounds of the 256-row tile,
     // come out cheapest: two of its row tiles cover M = 641..704 where
     // 256-row tiles need three (merged gate_up at M = 658: 147 against 173 us;
-    // M = 700, N = 12288: 76 against 95 us for 128x160).  Q6_K's larger raw
-    // runs spill in it.
-    if (xl == X_FRAG && fmt != FMT_Q6K) {
+    // M = 700, N = 12288: 76 against 95 us for 128x160; Q6_K, whose larger raw
+    // runs spill four registers in it, at M = 658, N = 12288: 218 against
+    // 333 us for 128x128).
+    if (xl == X_FRAG) {
         const long long t352 = ((np + 5) / 6) * ((M + 351) / 352);
         const double c352 = 2.44 * (double)((t352 + kCUs - 1) / kCUs);
         if (c352 < c256 && c352 < c128) return RUNG_M352N96;
     }
+    if (k2_192 && t192 <= 2 * kCUs && 10 * t192 >= 18 * kCUs) return RUNG_M192N96_K2;
     // the 256-row tile when the occupancy model has it finish no later than
     // the 128-row tiles (it unpacks each weight once for 256 rows); on
     // fragment-major activations also whenever it has 512 tiles
@@ -2078,9 +2082,10 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 // The unpack costs about four VALU instructions per weight, so a tile is
 // VALU-bound unless many rows share each unpacked weight:
 //  * with an even chunk count, the 192x96 tile with K split over two 6-wave
-//    groups (three waves per SIMD) when its tiles fit one round and cover M
-//    with no more rows than 128-row tiles (qkv, o and down at M = 658: 32.7,
-//    28.5 and 75 us against 34, 32 and 84 us);
+//    groups (three waves per SIMD) when its tiles fit one round, even where
+//    it computes more padding rows (qkv, o and down at M = 658: 32.7, 28.5
+//    and 75 us against 34, 32 and 84 us; Q6_K M = 512, N = 4096: 72 against
+//    84 us for the 128x128 K-split tile);
 //  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
 //    tile with K split over two wave groups (o and down at M = 658);
 //  * up to 128 rows: the 128x128 tile;
@@ -2095,8 +2100,7 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 int i8_select(long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8), r192 = (M + 191) / 192;
-    if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs && r192 * 192 <= (M + 127) / 128 * 128)
-        return I8_M192N96_K2;
+    if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs) return I8_M192N96_K2;
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
     if (M <= 128) return I8_M128;
     const long long tm256 = (M + 255) / 256, tm352 = (M + 351) / 352, tm512 = (M + 511) / 512;

@@ -340,7 +340,9 @@ def test_ladder_fragment_major():
     assert qg.select_rung_xf("q4k", 1400, 12288, 4096)["name"] == "mfma32-352x96"
     assert qg.select_rung_xf("q4k", 658, 24576, 4096)["name"] == "mfma32-352x96"       # merged gate_up
     assert qg.select_rung("q4k", 658, 24576, 4096)["name"] == "mfma32-128x160"         # row-major: not measured
-    assert qg.select_rung_xf("q6k", 658, 24576, 4096)["name"] != "mfma32-352x96"       # spills for Q6_K
+    assert qg.select_rung_xf("q6k", 658, 24576, 4096)["name"] == "mfma32-352x96"       # Q6_K too (4 VGPRs spill)
+    assert qg.select_rung_xf("q4k", 658, 12288, 4096)["name"] == "mfma32-352x96"       # 352x96 before two 192x96 rounds
+    assert qg.select_rung_xf("q6k", 768, 12288, 4096)["name"] == "mfma32-192x96-k2"    # two full rounds of 192x96
     assert qg.select_rung_xf("q4k", 2048, 12288, 4096)["name"] == "mfma16-256x128"    # 768 tiles: three rounds either way
     for fmt, M, K, N in [("q4k", 658, 4096, 1024), ("q4k", 16, 4096, 12288),
                          ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
