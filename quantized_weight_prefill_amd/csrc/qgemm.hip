@@ -1551,12 +1551,13 @@ enum Rung {
     RUNG_M64_K4 = 7,      // 32x32x16 MFMA: 64x64, 2 waves of 32x64, K split over four groups
     RUNG_M352N96 = 8,     // 32x32x16 MFMA: 352x96, 11 waves of 32x96
     RUNG_M192N96_K2 = 9,  // 32x32x16 MFMA: 192x96, K split over two 6-wave groups (three waves per SIMD)
-    RUNG_COUNT = 10
+    RUNG_M192N64_K2 = 10, // 32x32x16 MFMA: 192x64, K split over two 6-wave groups
+    RUNG_COUNT = 11
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
                                             "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
-                                            "mfma32-192x96-k2"};
+                                            "mfma32-192x96-k2",  "mfma32-192x64-k2"};
 
 struct Plan {
     int rung;
@@ -1617,15 +1618,16 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128N160:
     case RUNG_M64_K4:
     case RUNG_M352N96:
-    case RUNG_M192N96_K2: {
+    case RUNG_M192N96_K2:
+    case RUNG_M192N64_K2: {
         const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2;
-        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 352
-                  : rung == RUNG_M192N96_K2 ? 192 : 128;
-        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64_K4 ? 64 : n96 ? 96 : 128;
-        pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M192N96_K2) && (K / kChunk) % 2 == 0) ? 2 : 1;
+        const bool r192 = rung == RUNG_M192N96_K2 || rung == RUNG_M192N64_K2;
+        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : (rung == RUNG_M64_K4 || rung == RUNG_M192N64_K2) ? 64 : n96 ? 96 : 128;
+        pl.kw = ((rung == RUNG_M128_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
         if (rung == RUNG_M64_K4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
         pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11
-                   : rung == RUNG_M192N96_K2 ? 6 * pl.kw : 4 * pl.kw;
+                   : r192 ? 6 * pl.kw : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
         if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
@@ -1688,16 +1690,21 @@ double stream_cost(long long M, long long np, int cols)
 // Between decode-adjacent M and 128 tiles of 128x128 three rungs compete:
 // one panel and up to 64 rows per wave (direct-small-m), four panels and 48
 // rows per wave (direct-wide) and 64x64 streaming tiles with K split four
-// ways.  Their workgroups run in rounds of one per CU; a round costs a
-// constant per rung, measured on MI355X with Q4_K at K = 4096 (M = 80..300,
-// N = 1024..12288): 8, 15.5 and 17 microseconds.  The 48-row direct variant
-// spills for Q6_K and W4A16 and is left out for them.
-int mid_m_rung(int fmt, long long M, long long np)
+// ways, and on fragment-major activations with an even chunk count a fourth,
+// the 192x64 tile with K split over two 6-wave groups.  Their workgroups run
+// in rounds of one per CU; a round costs a constant per rung, measured on
+// MI355X with Q4_K at K = 4096 (M = 80..384, N = 1024..12288): 8, 15.5, 17
+// and 27 microseconds.  The 48-row direct variant spills for Q6_K and W4A16
+// and is left out for them.  (Q6_K at M = 300..384, N = 4096: 192x64 72-73
+// against 91 us for the 64x64 tiles.)
+int mid_m_rung(int fmt, long long M, long long np, bool k2_192)
 {
     const long long g64 = (M + 63) / 64, g48 = (M + 47) / 48, q = (np + 3) / 4;
     const auto rounds = [](long long wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
     const double small = 8.0 * rounds(np * g64), k4 = 17.0 * rounds(q * g64);
     const double wide = fmt == FMT_Q4K ? 15.5 * rounds(q * g48) : 1e30;
+    const double t192 = k2_192 ? 27.0 * rounds(((M + 191) / 192) * q) : 1e30;
+    if (t192 < wide && t192 < small && t192 < k4) return RUNG_M192N64_K2;
     if (wide <= small && wide <= k4) return RUNG_WIDE;
     return small <= k4 ? RUNG_SMALL_M : RUNG_M64_K4;
 }
@@ -1731,17 +1738,22 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
-    if (t128 < 128) return mid_m_rung(fmt, M, np);
-    // on fragment-major activations, the 192x96 tile with K split over two
+    if (t128 < 128) return mid_m_rung(fmt, M, np, xl == X_FRAG && (K / kChunk) % 2 == 0);
+    // on fragment-major activations, a 192-row tile with K split over two
     // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
-    // and cover M with no more rows than 128-row tiles (qkv, o and down at
-    // M = 658: 49, 40 and 120 us against 62 for 128x160, 43 and 132 for the
-    // 128x128 K-split tile); after the 352x96 check below, also over two
-    // rounds at least 90% full (M = 768, N = 12288: Q4_K 90 against 101, Q6_K
-    // 254 against 331 us; with 1.5 or three rounds it loses to the 256-row
-    // tile)
+    // and cover M with no more rows than 128-row tiles: 64 columns wide when
+    // those tiles fit (o and down at M = 658: 36.5 and 113-119 us), else 96
+    // (qkv: 47-50 us against 62 for 128x160; 192x64 would take 1.5 rounds, 64
+    // us); after the 352x96 check below, the 96-wide one also over two rounds
+    // at least 90% full (M = 768, N = 12288: Q4_K 90 against 101, Q6_K 254
+    // against 331 us; with 1.5 or three rounds it loses to the 256-row tile)
     const long long r192 = (M + 191) / 192, t192 = r192 * ((np + 5) / 6);
-    const bool k2_192 = xl == X_FRAG && (K / kChunk) % 2 == 0 && r192 * 192 <= (M + 127) / 128 * 128;
+    const bool even2 = xl == X_FRAG && (K / kChunk) % 2 == 0;
+    const bool k2_192 = even2 && r192 * 192 <= (M + 127) / 128 * 128;
+    // (the 64-wide tile pays even where it computes more padding rows: Q4_K
+    // and Q6_K at M = 512, N = 4096: 29 and 85 us against 35 and 106 us for
+    // the 128x128 K-split tile)
+    if (even2 && r192 * ((np + 3) / 4) <= kCUs) return RUNG_M192N64_K2;
     if (k2_192 && t192 <= kCUs) return RUNG_M192N96_K2;
     // on fragment-major activations, the 352x96 tile (11 waves, three per
     // SIMD) when its rounds, each costing 1.22 rounds of the 256-row tile,
@@ -1824,6 +1836,12 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 6, 6, 1, 2, XL>), pl.grid, dim3(768), 0, s, a);
         else
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 6, 6, 1, 1, XL>), pl.grid, dim3(384), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M192N64_K2:
+        if (even)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 6, 1, 2, XL>), pl.grid, dim3(768), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 6, 1, 1, XL>), pl.grid, dim3(384), 0, s, a);
         return hipGetLastError();
     case RUNG_M64_K4:
         if ((a.K / kChunk) % 4 == 0)
@@ -2037,10 +2055,11 @@ enum I8Rung {
     I8_M512N96 = 4,   // 512x96, 8 waves of 64x96: each weight unpacked once for 512 rows
     I8_M352N96 = 5,   // 352x96, 11 waves of 32x96 (three per SIMD)
     I8_M192N96_K2 = 6,  // 192x96, K split over two 6-wave groups (three waves per SIMD)
-    I8_RUNG_COUNT = 7
+    I8_M192N64_K2 = 7,  // 192x64, K split over two 6-wave groups
+    I8_RUNG_COUNT = 8
 };
 const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x96",
-                                                   "i8-512x96", "i8-352x96", "i8-192x96-k2"};
+                                                   "i8-512x96", "i8-352x96", "i8-192x96-k2", "i8-192x64-k2"};
 // int32 sums stay exact while K * 127 * 127 < 2^31
 constexpr long long kI8MaxK = 131072;
 
@@ -2062,8 +2081,9 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case I8_M512N96: pl.rows = 512; pl.cols = 96; pl.waves = 8; break;
     case I8_M352N96: pl.rows = 352; pl.cols = 96; pl.waves = 11; break;
     case I8_M192N96_K2:
+    case I8_M192N64_K2:
         pl.rows = 192;
-        pl.cols = 96;
+        pl.cols = rung == I8_M192N64_K2 ? 64 : 96;
         pl.kw = (K / kChunk) % 2 == 0 ? 2 : 1;
         pl.waves = 6 * pl.kw;
         break;
@@ -2081,11 +2101,13 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 // The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 512..4096).
 // The unpack costs about four VALU instructions per weight, so a tile is
 // VALU-bound unless many rows share each unpacked weight:
-//  * with an even chunk count, the 192x96 tile with K split over two 6-wave
+//  * with an even chunk count, a 192-row tile with K split over two 6-wave
 //    groups (three waves per SIMD) when its tiles fit one round, even where
-//    it computes more padding rows (qkv, o and down at M = 658: 32.7, 28.5
-//    and 75 us against 34, 32 and 84 us; Q6_K M = 512, N = 4096: 72 against
-//    84 us for the 128x128 K-split tile);
+//    it computes more padding rows: 64 columns wide when those tiles fit (o
+//    and down at M = 658: 25.0 and 64.0 us against 28.7 and 75.5 us for
+//    192x96), else 96 (qkv: 32.1 us against 34.5 on 256x96 and 43 on
+//    192x64; Q6_K M = 512, N = 4096: 72 against 84 us for the 128x128
+//    K-split tile);
 //  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
 //    tile with K split over two wave groups (o and down at M = 658);
 //  * up to 128 rows: the 128x128 tile;
@@ -2100,6 +2122,7 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 int i8_select(long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8), r192 = (M + 191) / 192;
+    if ((K / kChunk) % 2 == 0 && r192 * ((np + 3) / 4) <= kCUs) return I8_M192N64_K2;
     if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs) return I8_M192N96_K2;
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
     if (M <= 128) return I8_M128;
@@ -2142,6 +2165,12 @@ hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
             hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 6, 1, 2, CPB>), pl.grid, dim3(768), 0, s, a);
         else
             hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 6, 1, 1, CPB>), pl.grid, dim3(384), 0, s, a);
+        break;
+    case I8_M192N64_K2:
+        if (pl.kw == 2)
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 4, 6, 1, 2, CPB>), pl.grid, dim3(768), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 4, 6, 1, 1, CPB>), pl.grid, dim3(384), 0, s, a);
         break;
     default:
         hipLaunchKernelGGL((k_i8_stream<FMT, DT, 64, 6, 8, 1, 1, CPB>), pl.grid, dim3(512), 0, s, a);

@@ -307,16 +307,26 @@ def test_ladder_sweep(fmt, dtype):
 def test_ladder_mid_m_round_model():
     """Below 128 tiles of 128x128 and above 64 rows the ladder picks among
     the one-panel direct kernel, the four-panel 48-row direct kernel (Q4_K
-    only) and 64x64 K-split tiles by whole rounds of one workgroup per CU;
+    only), 64x64 K-split tiles and, on fragment-major activations, 192x64
+    tiles split over two groups, by whole rounds of one workgroup per CU;
     the expected names are the measured winners on MI355X."""
     for fmt, M, N, K, want in [("q4k", 128, 1024, 4096, "direct-small-m"), ("q4k", 200, 1024, 4096, "direct-small-m"),
                                ("q4k", 300, 1024, 4096, "direct-wide"), ("q4k", 200, 4096, 4096, "mfma32-64x64-k4"),
-                               ("q4k", 300, 4096, 4096, "direct-wide"), ("q4k", 80, 6144, 4096, "direct-wide"),
+                               ("q4k", 80, 6144, 4096, "direct-wide"),
                                ("q4k", 128, 6144, 4096, "mfma32-64x64-k4"), ("q6k", 80, 4096, 12288, "direct-small-m"),
                                ("q6k", 128, 4096, 12288, "direct-small-m"), ("q6k", 200, 4096, 12288, "mfma32-64x64-k4"),
                                ("q4k", 658, 1024, 4096, "direct-wide")]:
         for sel in (qg.select_rung, qg.select_rung_xf):
             assert sel(fmt, M, N, K)["name"] == want, (fmt, M, N, K, sel.__name__)
+    # one round of 192x64 tiles (27 us) against two of 48-row direct or 64x64 tiles (Q6_K at
+    # M = 300, N = 4096: 72 against 91 us); row-major activations keep the three direct/64x64 rungs
+    for fmt, M, K, xf, row in [("q4k", 300, 4096, "mfma32-192x64-k2", "direct-wide"),
+                               ("q6k", 300, 12288, "mfma32-192x64-k2", "mfma32-64x64-k4"),
+                               ("q6k", 384, 12288, "mfma32-192x64-k2", "mfma32-64x64-k4")]:
+        assert qg.select_rung_xf(fmt, M, 4096, K)["name"] == xf, (fmt, M)
+        assert qg.select_rung(fmt, M, 4096, K)["name"] == row, (fmt, M)
+    # the 64x64 K-split tile stays where one round of it beats one of 192x64
+    assert qg.select_rung_xf("q6k", 256, 4096, 12288)["name"] == "mfma32-64x64-k4"
 
 
 def test_ladder_fragment_major():
@@ -326,14 +336,16 @@ def test_ladder_fragment_major():
     the 352x96 tile where its rounds cost least (two of its row tiles cover
     M = 641..704), the 256-row tile also whenever it has 512 tiles; otherwise
     the same rung as for row-major activations."""
-    # few tiles on fragment-major X: the 192x96 K-split tile where its 172 tiles fit one round and its
-    # 768 rows are no more than the 128-row tiles' (down and o); 128x128 when 192-row tiles pad more
-    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-192x96-k2"
-    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-192x96-k2"
+    # few tiles on fragment-major X: a 192-row K-split tile where its tiles fit one round and its
+    # 768 rows are no more than the 128-row tiles' (down and o: 256 tiles of 192x64; qkv: 256 of
+    # 192x96, where 192x64 would need 384); 128x128 when 192-row tiles pad more
+    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-192x64-k2"
+    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-192x64-k2"
+    assert qg.select_rung_xf("q4k", 658, 6144, 4096)["name"] == "mfma32-192x96-k2"
     assert qg.select_rung_xf("q4k", 200, 12288, 4096)["name"] == "mfma32-128x128-k2"
     assert qg.select_rung_xf("q4k", 1000, 4096, 4096)["name"] == "mfma32-128x128-k2"
     assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"        # row-major: K < 8192
-    assert qg.select_rung_xf("q6k", 300, 4096, 12288)["name"] == "mfma32-64x64-k4"    # round model, below 128 tiles
+    assert qg.select_rung_xf("q4k", 512, 4096, 4096)["name"] == "mfma32-192x64-k2"    # one round, despite 64 padding rows
     assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
     assert qg.select_rung_xf("q4k", 512, 12288, 4096)["name"] == "mfma16-256x128"
     # 512 tiles of 352x96 in two rounds against 576 of 256x128 in three
@@ -352,7 +364,7 @@ def test_ladder_fragment_major():
         for M in list(range(1, 70)) + [96, 200, 300, 511, 658, 1000, 1024, 4096]:
             info = qg.select_rung_xf("w4a16", M, N, K)
             assert info["tiles_n"] * info["cols"] >= N and info["tiles_m"] * info["rows"] >= M
-            if info["name"] in ("mfma32-128x128-k2", "mfma32-192x96-k2"):
+            if info["name"] in ("mfma32-128x128-k2", "mfma32-192x96-k2", "mfma32-192x64-k2"):
                 assert info["tiles_n"] * info["tiles_m"] <= 256
 
 
