@@ -14,9 +14,16 @@
  * Conventions for every entry point
  *   - Plain pointers and sizes only.  Device pointers must come from the HIP
  *     allocator of the current device; host pointers are ordinary memory.
- *     The caller owns every buffer.  The library allocates no device memory,
- *     never synchronises the stream and keeps no mutable global state, so
- *     calls are re-entrant.
+ *     The caller owns every buffer.  The library never synchronises the
+ *     stream and allocates no device memory, with one exception: the rung
+ *     that splits K across workgroups (mfma32-64x64-sk) keeps a workspace
+ *     for its fp32 partial sums per (device, stream), taken in stream order
+ *     from the device's default memory pool (hipMallocAsync) on first use,
+ *     replaced in stream order by a larger one when a call needs more
+ *     (S*M*N*4 bytes rounded up to whole MiB, S <= 8 slices) and held until
+ *     the process ends; a lock serialises its bookkeeping and the two
+ *     launches of such a call.  Calls are re-entrant; calls on different
+ *     streams never share a workspace.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     GEMM and dequant calls are asynchronous on that stream.
  *   - dtype: QGEMM_F16 or QGEMM_BF16.  X and Y have that type; the weights are
@@ -155,7 +162,8 @@ int qgemm_w4a16(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t 
  * a K block that never straddles a quantization group) maps (format, M, N,
  * K, dtype) to a rung.  qgemm_select_rung writes 8 integers:
  *   [0] rung id  [1] rows per tile  [2] columns per tile  [3] K per step
- *   [4] waves per workgroup  [5] K-split ways inside a workgroup
+ *   [4] waves per workgroup  [5] K-split ways (inside a workgroup, times the
+ *       K slices across workgroups for mfma32-64x64-sk)
  *   [6] output tiles along N  [7] output tiles along M
  * and returns QGEMM_OK, or an error for an illegal shape. */
 int qgemm_num_rungs(void);
@@ -164,7 +172,14 @@ int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, in
 int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
 
 /* Same as the format entry points, with the rung forced (rung = -1 selects
- * as qgemm_q4k/q6k/w4a16 do).  group_size/has_zp are ignored for k-quants. */
+ * as qgemm_q4k/q6k/w4a16 do).  group_size/has_zp are ignored for k-quants.
+ * mfma32-64x64-sk splits K into S slices across workgroups (S = 1..8, as
+ * many as keep the grid within two workgroups per CU and each of a slice's
+ * four K groups at least four whole 128-wide chunks), each writing fp32
+ * partial sums of its 64x64 tiles; a second launch adds the S slices in
+ * slice order and rounds once into Y, so Y is deterministic and independent
+ * of the layout of X, but its fp32 summation order differs from the other
+ * rungs'.  Its workspace failing to allocate returns QGEMM_ERR_HIP. */
 int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N,
                     int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
 

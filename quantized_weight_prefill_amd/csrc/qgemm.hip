@@ -47,6 +47,8 @@
 #include <cstdint>
 #include <cstdio>
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "qgemm.h"
 
@@ -86,6 +88,9 @@ struct Args {
     long long wstride;           // grouped: packed bytes of one expert's weights
     const float *sx;             // int8 path: per-row activation scales
     const float *rw, *sw;        // int8 path: per-column weight requantization factors and scales
+    float *part;                 // K split across workgroups: fp32 partial sums, one slice after another
+    long long pstride;           // elements from one slice to the next
+    int split;                   // number of slices
 };
 
 // Activation layouts.  X_ROW: X[m][k] at m*K + k.  X_FRAG (fragment-major):
@@ -486,6 +491,26 @@ __device__ __forceinline__ void store_block32(const Args &a, const f32x16 &v, in
         } else {
             const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
             for (int j = 0; j < 4 && n0 + j < a.N; j++) y[j] = e[j];
+        }
+    }
+}
+
+// The same block as fp32 partial sums into P[m][n] (row stride N), rows
+// below M only: a K slice's share of Y before the slices are added.
+__device__ __forceinline__ void store_block32_f32(float *P, int M, int N, const f32x16 &v, int m_base, int n_base,
+                                                  int lane)
+{
+    const int m = m_base + (lane & 31);
+    if (m >= M) return;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int n0 = n_base + 8 * q + 4 * (lane >> 5);
+        if (n0 >= N) continue;
+        float *p = P + (long long)m * N + n0;
+        if (n0 + 4 <= N && (N & 3) == 0) {
+            *(f32x4 *)p = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        } else {
+            for (int j = 0; j < 4 && n0 + j < N; j++) p[j] = v[4 * q + j];
         }
     }
 }
@@ -989,6 +1014,99 @@ k_stream32(Args a)
 #pragma unroll
         for (int rb = 0; rb < RBW; rb++)
             store_block32<DT>(a, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * (wn * CBW + cb), lane);
+}
+
+// ---------------------------------------------------------------------------
+// K split across workgroups, for the weight-stream regime (M of one or two
+// 32-row blocks).  There every workgroup of k_stream32 reads the activations
+// of its rows over all of K, so each CU pulls M*K*2 bytes of X through its
+// L1 while its share of the weights is small; slice s of S instead covers
+// chunks [s*C/S, (s+1)*C/S) of its tile (C = K/128), split again over the
+// KS K groups inside the workgroup and reduced through LDS as in k_stream32,
+// and writes its fp32 partial sums to a.part + s*a.pstride (row-major
+// [M][N], rows below M).  k_splitk_reduce then adds the S slices in slice
+// order and rounds once, so the result does not depend on timing.  Grid: S
+// times the tiles; consecutive logical indices share a slice, so the tiles
+// running together on one XCD read the same activation slice.
+// ---------------------------------------------------------------------------
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int XL>
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
+k_stream32_sk(Args a)
+{
+    const int S = a.split;
+    using St = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL>;
+    constexpr int CBW = St::CBW, RBW = St::RBW, PB = St::PB, BM = St::BM;
+    constexpr int NACC = NWM * NWN * CBW * RBW * 64;
+    static_assert(KS == 1 || (KS - 1) * NACC * sizeof(f32x16) <= KS * sizeof(typename St::Lds),
+                  "K-split reduction must fit in LDS");
+    __shared__ typename St::Lds sWall[KS];
+
+    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    const int kg = wall / (NWM * NWN);
+    const int w = wall % (NWM * NWN), tid = threadIdx.x % St::NTG;
+    const int wm = w % NWM, wn = w / NWM;
+    const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM, tiles = tm * tn;
+    const int L = xcd_order(blockIdx.x, gridDim.x), slice = L / tiles;
+    int mt, nt;
+    tile_coords(L - slice * tiles, tm, tn, mt, nt);
+    const int m0 = mt * BM + wm * WM, p0 = nt * PB;
+    const int nall = a.K / kChunk, s_lo = (int)((long long)slice * nall / S);
+    const int nchk = ((int)((long long)(slice + 1) * nall / S) - s_lo) / KS;
+    const int c_lo = s_lo + kg * nchk, c_hi = c_lo + nchk;
+
+    f32x16 acc[CBW][RBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0.f;
+    St::run(a, sWall[kg], tid, lane, wn, m0, p0, c_lo, c_hi, acc);
+    if constexpr (KS > 1) {
+        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[0]);
+        if (kg > 0) {
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    red[(kg - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; g++)
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    acc[cb][rb] += red[(g - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane];
+    }
+    float *P = a.part + (long long)slice * a.pstride;
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+            store_block32_f32(P, a.M, a.N, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * (wn * CBW + cb), lane);
+}
+
+// Y[i] = RN_t(sum over s = 0..S-1, in that order, of part[s*slice_stride + i])
+// for the MN outputs of Y (row-major [M][N]); four outputs per thread
+// (slice_stride is a multiple of 4, so every slice stays 16-byte aligned).
+template <int DT>
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float *part, uint16_t *Y, long long MN,
+                                                       long long slice_stride, int S)
+{
+    const long long i = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
+    if (i >= MN) return;
+    f32x4 v = *(const f32x4 *)(part + i);
+    for (int s = 1; s < S; s++) v += *(const f32x4 *)(part + (long long)s * slice_stride + i);
+    const uint32_t lo = pack_out<DT>(v[0], v[1]), hi = pack_out<DT>(v[2], v[3]);
+    if (i + 4 <= MN) {
+        *(u32x2 *)(Y + i) = u32x2{lo, hi};
+    } else {
+        const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+        for (int j = 0; i + j < MN; j++) Y[i + j] = e[j];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1552,18 +1670,20 @@ enum Rung {
     RUNG_M352N96 = 8,     // 32x32x16 MFMA: 352x96, 11 waves of 32x96
     RUNG_M192N96_K2 = 9,  // 32x32x16 MFMA: 192x96, K split over two 6-wave groups (three waves per SIMD)
     RUNG_M192N64_K2 = 10, // 32x32x16 MFMA: 192x64, K split over two 6-wave groups
-    RUNG_COUNT = 11
+    RUNG_M64_SK = 11,     // 32x32x16 MFMA: 64x64, K split over four groups and across workgroups
+    RUNG_COUNT = 12
 };
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
                                             "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
-                                            "mfma32-192x96-k2",  "mfma32-192x64-k2"};
+                                            "mfma32-192x96-k2",  "mfma32-192x64-k2",  "mfma32-64x64-sk"};
 
 struct Plan {
     int rung;
     int tiles_n, tiles_m;  // output tiles along N and along M
     int rows, cols;    // output tile
-    int waves, kw;     // waves per workgroup, K-split ways
+    int waves, kw;     // waves per workgroup, K-split ways inside one workgroup
+    int split;         // K slices across workgroups (1: none)
     int rb, pn;        // direct kernel: row blocks / panels per wave
     dim3 grid;
     size_t lds;        // dynamic LDS bytes
@@ -1617,23 +1737,35 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128_K2:
     case RUNG_M128N160:
     case RUNG_M64_K4:
+    case RUNG_M64_SK:
     case RUNG_M352N96:
     case RUNG_M192N96_K2:
     case RUNG_M192N64_K2: {
         const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2;
         const bool r192 = rung == RUNG_M192N96_K2 || rung == RUNG_M192N64_K2;
-        pl.rows = rung == RUNG_M16_256 ? 256 : rung == RUNG_M64_K4 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192 : 128;
-        pl.cols = rung == RUNG_M128N160 ? 160 : (rung == RUNG_M64_K4 || rung == RUNG_M192N64_K2) ? 64 : n96 ? 96 : 128;
+        const bool r64 = rung == RUNG_M64_K4 || rung == RUNG_M64_SK;
+        pl.rows = rung == RUNG_M16_256 ? 256 : r64 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : (r64 || rung == RUNG_M192N64_K2) ? 64 : n96 ? 96 : 128;
         pl.kw = ((rung == RUNG_M128_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
-        if (rung == RUNG_M64_K4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
-        pl.waves = rung == RUNG_M16_256 ? 8 : rung == RUNG_M64_K4 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11
+        if (r64) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = rung == RUNG_M16_256 ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11
                    : r192 ? 6 * pl.kw : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
         if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
         pl.tiles_n = (int)tn;
         pl.tiles_m = (int)tm;
-        pl.grid = dim3((unsigned)(tn * tm), 1, 1);
+        pl.split = 1;
+        if (rung == RUNG_M64_SK) {
+            // slices across workgroups: double while the grid stays within
+            // two workgroups per CU, the slices divide the chunks evenly
+            // among the in-group K groups and each group keeps four chunks
+            while (pl.split < 8 && tn * tm * 2 * pl.split <= 2 * kCUs && nch % (2 * pl.split * pl.kw) == 0 &&
+                   nch / (2 * pl.split * pl.kw) >= 4)
+                pl.split *= 2;
+        }
+        if (tn * tm * pl.split > INT32_MAX) return QGEMM_ERR_SHAPE;
+        pl.grid = dim3((unsigned)(tn * tm * pl.split), 1, 1);
         pl.lds = 0;
         return QGEMM_OK;
     }
@@ -1642,6 +1774,7 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     }
     pl.rows = 16 * pl.rb;
     pl.cols = 16 * pl.pn;
+    pl.split = 1;
     pl.tiles_n = (int)pl.grid.x;
     pl.tiles_m = (int)pl.grid.y;
     pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch, M <= 16);
@@ -1697,6 +1830,17 @@ double stream_cost(long long M, long long np, int cols)
 // and 27 microseconds.  The 48-row direct variant spills for Q6_K and W4A16
 // and is left out for them.  (Q6_K at M = 300..384, N = 4096: 192x64 72-73
 // against 91 us for the 64x64 tiles.)
+// The split rung over few panels of Q6_K, 33..128 rows, on fragment-major
+// activations: one panel and all rows per wave reads the activations once
+// per panel; 64x64 tiles split four ways across workgroups (K = 12288, N =
+// 4096) tie it up to 48 rows and win from 64 (24.2 against 28.1 us; M =
+// 80..128: 39.4-42.3 against 43.0-46.0 us).
+bool split_pays(int fmt, long long M, long long np, long long K, int xl)
+{
+    return xl == X_FRAG && fmt == FMT_Q6K && np < 512 && M > 32 && M <= 128 && (K / kChunk) % 16 == 0 &&
+           K / kChunk >= 64;
+}
+
 int mid_m_rung(int fmt, long long M, long long np, bool k2_192)
 {
     const long long g64 = (M + 63) / 64, g48 = (M + 47) / 48, q = (np + 3) / 4;
@@ -1724,11 +1868,15 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         // (three row blocks per wave only pay off for Q4_K: the other
         // formats' larger raw runs spill at that size)
         if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
-        // 49..64 rows of Q4_K (33..64 of W4A16) over many panels: unpack each
-        // weight once for all rows into LDS (64x64 tiles, K split four ways)
-        // instead of once per 16-row group (Q6_K's N = 4096 leaves too few
-        // such tiles)
-        if (np >= 512 && ((fmt == FMT_Q4K && M > 48) || (fmt == FMT_W4 && M > 32))) return RUNG_M64_K4;
+        // 49..64 rows of Q4_K (33..64 of W4A16 and Q6_K) over many panels:
+        // unpack each weight once for all rows into LDS (64x64 tiles, K split
+        // four ways) instead of once per 16-row group (Q6_K 12288->12288 at
+        // M = 64: 50.5 against 90.1 us for direct-skinny-n)
+        if (np >= 512 && ((fmt == FMT_Q4K && M > 48) || (fmt != FMT_Q4K && M > 32))) return RUNG_M64_K4;
+        // Q6_K over few panels (N = 4096): 64x64 tiles with K also split
+        // across workgroups, so that each CU reads a quarter of the
+        // activations
+        if (split_pays(fmt, M, np, K, xl)) return RUNG_M64_SK;
         // fewer panels: one panel and all rows per wave (each weight
         // unpacked once) beats four panels of 16 rows up to 64 rows
         return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
@@ -1738,6 +1886,7 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
+    if (split_pays(fmt, M, np, K, xl)) return RUNG_M64_SK;
     if (t128 < 128) return mid_m_rung(fmt, M, np, xl == X_FRAG && (K / kChunk) % 2 == 0);
     // on fragment-major activations, a 192-row tile with K split over two
     // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
@@ -1843,6 +1992,14 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         else
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 6, 1, 1, XL>), pl.grid, dim3(384), 0, s, a);
         return hipGetLastError();
+    case RUNG_M64_SK:
+        if (pl.kw == 4)
+            hipLaunchKernelGGL((k_stream32_sk<FMT, DT, 32, 4, 2, 1, 4, XL>), pl.grid, dim3(512), 0, s, a);
+        else if (pl.kw == 2)
+            hipLaunchKernelGGL((k_stream32_sk<FMT, DT, 32, 4, 2, 1, 2, XL>), pl.grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32_sk<FMT, DT, 32, 4, 2, 1, 1, XL>), pl.grid, dim3(128), 0, s, a);
+        return hipGetLastError();
     case RUNG_M64_K4:
         if ((a.K / kChunk) % 4 == 0)
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 2, 1, 4, XL>), pl.grid, dim3(512), 0, s, a);
@@ -1919,6 +2076,73 @@ Args make_args(int fmt, const void *X, const void *W, void *Y, long long M, long
     return a;
 }
 
+// The split rung's partial sums live in a workspace kept per (device,
+// stream): taken from the device's default pool in stream order the first
+// time, and replaced by a larger one (the old one freed in stream order, after
+// the work already queued) when a call needs more.  Workspaces are held until
+// the process ends.  The lock is held across both launches of a call, so
+// calls from several host threads on one stream cannot interleave them, and
+// calls on different streams never share a workspace.
+struct SplitWs {
+    int dev;
+    hipStream_t stream;
+    void *p;
+    size_t bytes;
+};
+std::mutex g_ws_mu;
+std::vector<SplitWs> g_ws;
+
+// With g_ws_mu held: a workspace of at least `bytes` for (current device, s).
+hipError_t split_workspace(hipStream_t s, size_t bytes, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    bytes = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);  // whole MiB: fewer regrowths
+    for (SplitWs &w : g_ws) {
+        if (w.dev != dev || w.stream != s) continue;
+        if (w.bytes < bytes) {
+            void *np = nullptr;
+            if ((e = hipMallocAsync(&np, bytes, s)) != hipSuccess) return e;
+            if ((e = hipFreeAsync(w.p, s)) != hipSuccess) return e;
+            w.p = np;
+            w.bytes = bytes;
+        }
+        *out = w.p;
+        return hipSuccess;
+    }
+    void *np = nullptr;
+    if ((e = hipMallocAsync(&np, bytes, s)) != hipSuccess) return e;
+    g_ws.push_back(SplitWs{dev, s, np, bytes});
+    *out = np;
+    return hipSuccess;
+}
+
+int gemm_split(int fmt, int dtype, int xl, const Plan &pl, Args a, hipStream_t s)
+{
+    const long long MN = (long long)a.M * a.N, stride = (MN + 3) & ~3LL, rblocks = ((MN + 3) / 4 + 255) / 256;
+    if (rblocks > INT32_MAX) return QGEMM_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    void *ws = nullptr;
+    hipError_t e = split_workspace(s, (size_t)(stride * pl.split) * sizeof(float), &ws);
+    if (e != hipSuccess) return launch_status(e, "split-K workspace");
+    a.part = (float *)ws;
+    a.pstride = stride;
+    a.split = pl.split;
+    e = launch(fmt, dtype, xl, pl, a, s);
+    if (e == hipSuccess) {
+        const dim3 grid((unsigned)rblocks);
+        if (dtype == DT_F16)
+            hipLaunchKernelGGL((k_splitk_reduce<DT_F16>), grid, dim3(256), 0, s, (const float *)ws, a.Y, MN, stride,
+                               pl.split);
+        else
+            hipLaunchKernelGGL((k_splitk_reduce<DT_BF16>), grid, dim3(256), 0, s, (const float *)ws, a.Y, MN, stride,
+                               pl.split);
+        e = hipGetLastError();
+    }
+    return launch_status(e, kRungNames[pl.rung]);
+}
+
 int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
          long long group, int has_zp, int dtype, void *stream, int xl = X_ROW)
 {
@@ -1935,6 +2159,7 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     if (st != QGEMM_OK) return st;
     Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
     a.kw = pl.kw;
+    if (pl.rung == RUNG_M64_SK) return gemm_split(fmt, dtype, xl, pl, a, (hipStream_t)stream);
     return launch_status(launch(fmt, dtype, xl, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
 }
 
@@ -2272,7 +2497,7 @@ void fill_info(const Plan &pl, int32_t *info)
     info[2] = pl.cols;
     info[3] = kChunk;
     info[4] = pl.waves;
-    info[5] = pl.kw;
+    info[5] = pl.kw * pl.split;
     info[6] = pl.tiles_n;
     info[7] = pl.tiles_m;
 }

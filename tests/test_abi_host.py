@@ -298,7 +298,11 @@ def test_ladder_sweep(fmt, dtype):
             if N <= 64:
                 assert info["name"] == "direct-skinny-n"
             elif M <= 64:
-                assert info["name"].startswith("direct-") or (info["name"] == "mfma32-64x64-k4" and M > 32)
+                assert info["name"].startswith("direct-") or (
+                    info["name"] in ("mfma32-64x64-k4", "mfma32-64x64-sk") and M > 32)
+            if info["name"] == "mfma32-64x64-sk":
+                # slices across workgroups: whole chunks for every K group of every slice
+                assert (K // info["k_step"]) % info["k_split"] == 0 and info["k_split"] % info["waves"] == 0
             for r in range(qg.num_rungs()):
                 ri = qg.rung_info(r, fmt, M, N, K, dtype)
                 assert ri["tiles_n"] * ri["cols"] >= N and ri["tiles_m"] * ri["rows"] >= M
@@ -313,8 +317,7 @@ def test_ladder_mid_m_round_model():
     for fmt, M, N, K, want in [("q4k", 128, 1024, 4096, "direct-small-m"), ("q4k", 200, 1024, 4096, "direct-small-m"),
                                ("q4k", 300, 1024, 4096, "direct-wide"), ("q4k", 200, 4096, 4096, "mfma32-64x64-k4"),
                                ("q4k", 80, 6144, 4096, "direct-wide"),
-                               ("q4k", 128, 6144, 4096, "mfma32-64x64-k4"), ("q6k", 80, 4096, 12288, "direct-small-m"),
-                               ("q6k", 128, 4096, 12288, "direct-small-m"), ("q6k", 200, 4096, 12288, "mfma32-64x64-k4"),
+                               ("q4k", 128, 6144, 4096, "mfma32-64x64-k4"),                                ("q6k", 200, 4096, 12288, "mfma32-64x64-k4"),
                                ("q4k", 658, 1024, 4096, "direct-wide")]:
         for sel in (qg.select_rung, qg.select_rung_xf):
             assert sel(fmt, M, N, K)["name"] == want, (fmt, M, N, K, sel.__name__)
@@ -327,6 +330,19 @@ def test_ladder_mid_m_round_model():
         assert qg.select_rung(fmt, M, 4096, K)["name"] == row, (fmt, M)
     # the 64x64 K-split tile stays where one round of it beats one of 192x64
     assert qg.select_rung_xf("q6k", 256, 4096, 12288)["name"] == "mfma32-64x64-k4"
+    # Q6_K over few panels, 33..128 rows: row-major keeps one panel and all rows per wave,
+    # fragment-major splits 64x64 tiles four ways across workgroups (M = 64: 24.2 against 28.1 us)
+    for M in (33, 64, 80, 128):
+        assert qg.select_rung("q6k", M, 4096, 12288)["name"] == "direct-small-m", M
+        sk = qg.select_rung_xf("q6k", M, 4096, 12288)
+        assert sk["name"] == "mfma32-64x64-sk" and sk["k_split"] == 16, (M, sk)
+    assert qg.select_rung_xf("q6k", 150, 4096, 12288)["name"] == "mfma32-64x64-k4"
+    # Q6_K over many panels, 33..64 rows: 64x64 tiles unpack each weight once for all rows
+    # (M = 64, N = K = 12288: 52 against 93 us for direct-skinny-n)
+    for M in (33, 48, 64):
+        for sel in (qg.select_rung, qg.select_rung_xf):
+            assert sel("q6k", M, 12288, 12288)["name"] == "mfma32-64x64-k4", (M, sel.__name__)
+            assert sel("q6k", M, 12288, 4096)["name"] == "mfma32-64x64-k4", (M, sel.__name__)
 
 
 def test_ladder_fragment_major():

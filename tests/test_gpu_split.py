@@ -1,0 +1,64 @@
+"""GPU parity of the rung that splits K across workgroups (64x64 tiles, fp32
+partial sums per K slice, then one ordered reduction): against the oracle at
+K long enough for two, four and eight slices, with ragged M and N, on both
+activation layouts and through the automatic ladder at the down projection's
+shape, and bit-identical from call to call and between layouts.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import quantized_weight_prefill_amd as qg
+from tests.helpers import Case, assert_gemm_close, from_device
+
+pytestmark = pytest.mark.gpu
+
+SK = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-64x64-sk"][0]
+
+
+@pytest.mark.parametrize("fmt,M,N,K,dtype,slices", [
+    ("q4k", 37, 200, 4096, qg.F16, 2),      # 13 panels (the last ragged), 37 rows of a 64-row tile
+    ("w4a16", 64, 256, 4096, qg.BF16, 2),
+    ("q6k", 96, 130, 12288, qg.F16, 4),     # two row tiles, 9 panels
+    ("q6k", 5, 64, 16384, qg.BF16, 8),
+])
+def test_split_rung_forced(fmt, M, N, K, dtype, slices):
+    c = Case(fmt, M, N, K, dtype, seed=700 + M, group=128)
+    info = qg.rung_info(SK, fmt, M, N, K, dtype)
+    print(f"split forced {fmt} M={M} N={N} K={K} dtype={dtype} info={info}", flush=True)
+    assert info["k_split"] == 4 * slices, info
+    Yref, B = oracle.gemm(c.X, c.W, dtype)
+    y = from_device(c.run(SK))
+    assert_gemm_close(y, Yref, B, dtype, what=f"split {fmt} M={M} N={N} K={K}")
+    yx = from_device(c.run_xf(SK))
+    assert np.array_equal(y, yx), "row-major and fragment-major activations differ"
+    assert np.array_equal(y, from_device(c.run(SK))), "not reproducible from call to call"
+
+
+@pytest.mark.parametrize("M", [40, 64, 96, 128])
+def test_split_rung_auto_down_projection(M):
+    """Q6_K 12288 -> 4096 at 33..128 rows on fragment-major activations: the
+    ladder picks the split rung (four slices of 24 chunks, each split over
+    four K groups)."""
+    N, K = 4096, 12288
+    sel = qg.select_rung_xf("q6k", M, N, K, qg.F16)
+    assert sel["name"] == "mfma32-64x64-sk" and sel["k_split"] == 16, sel
+    c = Case("q6k", M, N, K, qg.F16, seed=720 + M)
+    print(f"split auto q6k M={M} N={N} K={K}", flush=True)
+    y = from_device(c.run_xf(-1))
+    Yref, B = oracle.gemm(c.X, c.W, qg.F16)
+    assert_gemm_close(y, Yref, B, qg.F16, what=f"split auto M={M}")
+    assert np.array_equal(y, from_device(c.run_xf(-1)))
+
+
+def test_split_workspace_grows_between_calls():
+    """A call that needs a larger workspace than the previous one on the same
+    stream (the old one is replaced in stream order), then a smaller one."""
+    for i, (M, N, K) in enumerate([(8, 64, 4096), (64, 512, 8192), (16, 80, 4096)]):
+        c = Case("q4k", M, N, K, qg.F16, seed=740 + i)
+        print(f"split workspace M={M} N={N} K={K}", flush=True)
+        y = from_device(c.run(SK))
+        Yref, B = oracle.gemm(c.X, c.W, qg.F16)
+        assert_gemm_close(y, Yref, B, qg.F16, what=f"split workspace M={M} N={N} K={K}")
