@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import quantized_weight_prefill_amd as qg
-from tests.helpers import Case, assert_gemm_close, from_device
+from tests.helpers import Case, assert_gemm_close, from_device, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -62,3 +62,27 @@ def test_split_workspace_grows_between_calls():
         y = from_device(c.run(SK))
         Yref, B = oracle.gemm(c.X, c.W, qg.F16)
         assert_gemm_close(y, Yref, B, qg.F16, what=f"split workspace M={M} N={N} K={K}")
+
+
+def test_split_rung_concurrent_streams():
+    """Two streams (default priority) running split-rung GEMMs at once, each
+    several times back to back: every result equals the same problem run
+    alone, so calls on different streams never share partial sums."""
+    import torch
+
+    cases = [Case("q6k", 64, 256, 12288, qg.F16, seed=760), Case("q4k", 40, 320, 8192, qg.F16, seed=761)]
+    alone = [from_device(c.run(SK)) for c in cases]
+    torch.cuda.synchronize()
+    xs = [to_device(c.X, c.dtype) for c in cases]
+    wps = [c.device_weights() for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[None] * 4 for _ in cases]
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for i, c in enumerate(cases):
+            with torch.cuda.stream(streams[i]):
+                outs[i][rep] = qg.gemm_rung(c.fmt, SK, xs[i], wps[i], c.N, stream=streams[i].cuda_stream)
+    torch.cuda.synchronize()
+    for i in range(len(cases)):
+        for rep in range(4):
+            assert np.array_equal(from_device(outs[i][rep]), alone[i]), (i, rep)
