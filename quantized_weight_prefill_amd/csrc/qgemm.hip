@@ -1654,6 +1654,115 @@ k_i8_stream(Args a)
             store_block_i8<DT>(a, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * (wn * CBW + cb), lane);
 }
 
+// K split across workgroups on the int8 path, for few tiles (M of a few
+// 32-row blocks over few panels): slice s of a.split covers stages
+// [s*T/S, (s+1)*T/S) of its tile (T = K/128 one-chunk stages), split again
+// over the KS K groups inside the workgroup, and writes its int32 partial
+// sums to (int *)a.part + s*a.pstride (row-major [M][N], rows below M).
+// The sums are exact, so k_i8_splitk_reduce's total, and with it Y, equals
+// the unsplit rungs' bit for bit.  Grid: a.split times the tiles, the tiles
+// of one slice consecutive in the XCD order.
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS>
+__global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
+k_i8_stream_sk(Args a)
+{
+    using S = StreamI8<FMT, WM, WPB, NWM, NWN, 1>;
+    constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
+    constexpr int NACC = NWM * NWN * CBW * RBW * 64;
+    constexpr size_t kStageBytes = KS * sizeof(typename S::Lds);
+    constexpr size_t kRedBytes = KS > 1 ? (KS - 1) * NACC * sizeof(i32x16) : 0;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
+    auto &sWall = *reinterpret_cast<typename S::Lds(*)[KS]>(smem);
+
+    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    const int kg = wall / (NWM * NWN);
+    const int w = wall % (NWM * NWN), tid = threadIdx.x % S::NTG;
+    const int wm = w % NWM, wn = w / NWM;
+    const int tn = (a.np + PB - 1) / PB, tm = (a.M + BM - 1) / BM, tiles = tm * tn;
+    const int L = xcd_order(blockIdx.x, gridDim.x), slice = L / tiles;
+    int mt, nt;
+    tile_coords(L - slice * tiles, tm, tn, mt, nt);
+    const int m0 = mt * BM + wm * WM, p0 = nt * PB;
+    const int nall = a.K / kChunk, s_lo = (int)((long long)slice * nall / a.split);
+    const int nstg = ((int)((long long)(slice + 1) * nall / a.split) - s_lo) / KS;
+    const int c_lo = s_lo + kg * nstg, c_hi = c_lo + nstg;
+
+    i32x16 acc[CBW][RBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[cb][rb][e] = 0;
+    S::run(a, sWall[kg], tid, lane, wn, m0, p0, c_lo, c_hi, acc);
+    if constexpr (KS > 1) {
+        i32x16 *red = reinterpret_cast<i32x16 *>(smem);
+        if (kg > 0) {
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    red[(kg - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; g++)
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    acc[cb][rb] += red[(g - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane];
+    }
+    int *P = reinterpret_cast<int *>(a.part) + (long long)slice * a.pstride;
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++) {
+            const int m = m0 + 32 * rb + (lane & 31);
+            if (m >= a.M) continue;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int n0 = 16 * p0 + 32 * (wn * CBW + cb) + 8 * q + 4 * (lane >> 5);
+                if (n0 >= a.N) continue;
+                int *pp = P + (long long)m * a.N + n0;
+                const i32x16 &v = acc[cb][rb];
+                if (n0 + 4 <= a.N && (a.N & 3) == 0) {
+                    *(i32x4 *)pp = i32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+                } else {
+                    for (int j = 0; j < 4 && n0 + j < a.N; j++) pp[j] = v[4 * q + j];
+                }
+            }
+        }
+}
+
+// Y[m][n] = RN_t(RN_f32(acc) * RN_f32(sx[m] * sw[n])) with acc the int32 sum
+// of the a.split slices' partial sums (exact in any order), as the unsplit
+// epilogue computes it; four consecutive outputs per thread.
+template <int DT>
+__global__ void __launch_bounds__(256) k_i8_splitk_reduce(const int *part, const float *sx, const float *sw,
+                                                          uint16_t *Y, int M, int N, long long stride, int S)
+{
+    const long long MN = (long long)M * N, i = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
+    if (i >= MN) return;
+    i32x4 v = *(const i32x4 *)(part + i);
+    for (int s = 1; s < S; s++) v += *(const i32x4 *)(part + (long long)s * stride + i);
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const long long e = i + j < MN ? i + j : MN - 1;
+        const int m = (int)(e / N), n = (int)(e - (long long)m * N);
+        y[j] = (float)v[j] * (sx[m] * sw[n]);
+    }
+    const uint32_t lo = pack_out<DT>(y[0], y[1]), hi = pack_out<DT>(y[2], y[3]);
+    if (i + 4 <= MN) {
+        *(u32x2 *)(Y + i) = u32x2{lo, hi};
+    } else {
+        const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+        for (int j = 0; i + j < MN; j++) Y[i + j] = e[j];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: validation, the M-ladder, launches.
 // ---------------------------------------------------------------------------
@@ -2104,9 +2213,10 @@ hipError_t split_workspace(hipStream_t s, size_t bytes, void **out)
         if (w.bytes < bytes) {
             void *np = nullptr;
             if ((e = hipMallocAsync(&np, bytes, s)) != hipSuccess) return e;
-            if ((e = hipFreeAsync(w.p, s)) != hipSuccess) return e;
-            w.p = np;
+            void *old = w.p;
+            w.p = np;  // recorded before the old one is released, so nothing leaks if that fails
             w.bytes = bytes;
+            if ((e = hipFreeAsync(old, s)) != hipSuccess) return e;
         }
         *out = w.p;
         return hipSuccess;
@@ -2281,10 +2391,12 @@ enum I8Rung {
     I8_M352N96 = 5,   // 352x96, 11 waves of 32x96 (three per SIMD)
     I8_M192N96_K2 = 6,  // 192x96, K split over two 6-wave groups (three waves per SIMD)
     I8_M192N64_K2 = 7,  // 192x64, K split over two 6-wave groups
-    I8_RUNG_COUNT = 8
+    I8_M64_SK = 8,      // 64x64, K split over four groups and across workgroups
+    I8_RUNG_COUNT = 9
 };
-const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128", "i8-256x128", "i8-128x128-k2", "i8-256x96",
-                                                   "i8-512x96", "i8-352x96", "i8-192x96-k2", "i8-192x64-k2"};
+const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128",   "i8-256x128",   "i8-128x128-k2",
+                                                   "i8-256x96",    "i8-512x96",    "i8-352x96",
+                                                   "i8-192x96-k2", "i8-192x64-k2", "i8-64x64-sk"};
 // int32 sums stay exact while K * 127 * 127 < 2^31
 constexpr long long kI8MaxK = 131072;
 
@@ -2293,6 +2405,8 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
     pl = Plan{};
     pl.rung = rung;
     pl.kw = 1;
+    pl.split = 1;
+    const int nch = (int)(K / kChunk);
     switch (rung) {
     case I8_M128: pl.rows = 128; pl.cols = 128; pl.waves = 4; break;
     case I8_M256: pl.rows = 256; pl.cols = 128; pl.waves = 8; break;
@@ -2312,6 +2426,12 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
         pl.kw = (K / kChunk) % 2 == 0 ? 2 : 1;
         pl.waves = 6 * pl.kw;
         break;
+    case I8_M64_SK:
+        pl.rows = 64;
+        pl.cols = 64;
+        pl.kw = nch % 4 == 0 ? 4 : nch % 2 == 0 ? 2 : 1;
+        pl.waves = 2 * pl.kw;
+        break;
     default: return QGEMM_ERR_FORMAT;
     }
     const long long np = (N + 15) / 16;
@@ -2319,11 +2439,20 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
     if (tn * tm > INT32_MAX) return QGEMM_ERR_SHAPE;
     pl.tiles_n = (int)tn;
     pl.tiles_m = (int)tm;
-    pl.grid = dim3((unsigned)(tn * tm), 1, 1);
+    if (rung == I8_M64_SK) {
+        // slices across workgroups: double while the grid stays within two
+        // workgroups per CU, the slices divide the chunks evenly among the
+        // in-group K groups and each group keeps two chunks
+        while (pl.split < 8 && tn * tm * 2 * pl.split <= 2 * kCUs && nch % (2 * pl.split * pl.kw) == 0 &&
+               nch / (2 * pl.split * pl.kw) >= 2)
+            pl.split *= 2;
+    }
+    if (tn * tm * pl.split > INT32_MAX) return QGEMM_ERR_SHAPE;
+    pl.grid = dim3((unsigned)(tn * tm * pl.split), 1, 1);
     return QGEMM_OK;
 }
 
-// The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 512..4096).
+// The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 16..4096).
 // The unpack costs about four VALU instructions per weight, so a tile is
 // VALU-bound unless many rows share each unpacked weight:
 //  * with an even chunk count, a 192-row tile with K split over two 6-wave
@@ -2344,9 +2473,18 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    352x96; M = 4096 238 against 260 and 268).  The 352-row tile runs three
 //    waves per SIMD and unpacks each weight for 352 rows: two of its row
 //    tiles cover M = 658 where 256-row tiles need three.
-int i8_select(long long M, long long N, long long K)
+int i8_select(int fmt, long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8), r192 = (M + 191) / 192;
+    const long long nch = K / kChunk;
+    // few tiles of 192x64 (at most half the CUs): 64x64 tiles with K split
+    // across workgroups as well, up to 64 rows (Q6_K, whose unpack weighs
+    // most, up to 256): Q6_K 12288->4096 at M = 16..256 28.6-56.1 against
+    // 59.4-64.3 us, Q4_K 4096->4096 at M = 16..64 15.2-17.0 against
+    // 23.5-24.1 us (row quantizer included); over more tiles, or Q4_K from
+    // 96 rows, the 192x64 tile wins (4096->12288: 23.7-25.7 against 24.2-26.3)
+    if (nch % 8 == 0 && nch >= 16 && r192 * ((np + 3) / 4) <= kCUs / 2 && (M <= 64 || (fmt == FMT_Q6K && M <= 256)))
+        return I8_M64_SK;
     if ((K / kChunk) % 2 == 0 && r192 * ((np + 3) / 4) <= kCUs) return I8_M192N64_K2;
     if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs) return I8_M192N96_K2;
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
@@ -2411,8 +2549,21 @@ hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
 // with two (W4A16 on 256x96: 155 against 137 us at M = 2048) or spill with
 // two (Q6_K on 512x96 and on 352x96, every format on 192x96 split in two).
 template <int FMT, int DT>
+hipError_t launch_i8_sk(const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (pl.kw == 4)
+        hipLaunchKernelGGL((k_i8_stream_sk<FMT, DT, 32, 4, 2, 1, 4>), pl.grid, dim3(512), 0, s, a);
+    else if (pl.kw == 2)
+        hipLaunchKernelGGL((k_i8_stream_sk<FMT, DT, 32, 4, 2, 1, 2>), pl.grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_i8_stream_sk<FMT, DT, 32, 4, 2, 1, 1>), pl.grid, dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int DT>
 hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
+    if (pl.rung == I8_M64_SK) return launch_i8_sk<FMT, DT>(pl, a, s);
     const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) || pl.rung == I8_M192N96_K2 ||
                          (FMT == FMT_Q6K && (pl.rung == I8_M512N96 || pl.rung == I8_M352N96));
     if (!slower2 && (a.K / kChunk) % (2 * pl.kw) == 0) return launch_i8_cpb<FMT, DT, 2>(pl.rung, pl, a, s);
@@ -2443,12 +2594,37 @@ int i8_gemm(int fmt, int rung, const void *Xq, const float *sx, const void *W, c
     if (!aligned16(Xq) || !aligned16(W) || !aligned16(Y) || !aligned4(sx) || !aligned4(rw) || !aligned4(sw))
         return QGEMM_ERR_ALIGN;
     Plan pl;
-    st = i8_plan(rung < 0 ? i8_select(M, N, K) : rung, M, N, K, pl);
+    st = i8_plan(rung < 0 ? i8_select(fmt, M, N, K) : rung, M, N, K, pl);
     if (st != QGEMM_OK) return st;
     Args a = make_args(fmt, Xq, W, Y, M, N, K, group, has_zp);
     a.sx = sx;
     a.rw = rw;
     a.sw = sw;
+    if (pl.rung == I8_M64_SK) {
+        // int32 partial sums per K slice in the per-stream workspace, then
+        // their exact total through the unsplit epilogue
+        const hipStream_t s = (hipStream_t)stream;
+        const long long MN = M * N, stride = (MN + 3) & ~3LL, rblocks = ((MN + 3) / 4 + 255) / 256;
+        if (rblocks > INT32_MAX) return QGEMM_ERR_SHAPE;
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        void *ws = nullptr;
+        hipError_t e = split_workspace(s, (size_t)(stride * pl.split) * sizeof(int), &ws);
+        if (e != hipSuccess) return launch_status(e, "split-K workspace");
+        a.part = (float *)ws;
+        a.pstride = stride;
+        a.split = pl.split;
+        e = dtype == DT_F16 ? launch_i8_dt<DT_F16>(fmt, pl, a, s) : launch_i8_dt<DT_BF16>(fmt, pl, a, s);
+        if (e == hipSuccess) {
+            if (dtype == DT_F16)
+                hipLaunchKernelGGL((k_i8_splitk_reduce<DT_F16>), dim3((unsigned)rblocks), dim3(256), 0, s,
+                                   (const int *)ws, sx, sw, (uint16_t *)Y, (int)M, (int)N, stride, pl.split);
+            else
+                hipLaunchKernelGGL((k_i8_splitk_reduce<DT_BF16>), dim3((unsigned)rblocks), dim3(256), 0, s,
+                                   (const int *)ws, sx, sw, (uint16_t *)Y, (int)M, (int)N, stride, pl.split);
+            e = hipGetLastError();
+        }
+        return launch_status(e, kI8RungNames[pl.rung]);
+    }
     const hipError_t e = dtype == DT_F16 ? launch_i8_dt<DT_F16>(fmt, pl, a, (hipStream_t)stream)
                                          : launch_i8_dt<DT_BF16>(fmt, pl, a, (hipStream_t)stream);
     return launch_status(e, kI8RungNames[pl.rung]);
@@ -2497,7 +2673,7 @@ void fill_info(const Plan &pl, int32_t *info)
     info[2] = pl.cols;
     info[3] = kChunk;
     info[4] = pl.waves;
-    info[5] = pl.kw * pl.split;
+    info[5] = pl.kw * std::max(pl.split, 1);
     info[6] = pl.tiles_n;
     info[7] = pl.tiles_m;
 }
@@ -2680,7 +2856,7 @@ int qgemm_i8_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, in
 
 int qgemm_i8_select_rung(int format, int64_t M, int64_t N, int64_t K, int32_t *info8)
 {
-    return qgemm_i8_rung_info(i8_select(M, N, K), format, M, N, K, info8);
+    return qgemm_i8_rung_info(i8_select(format, M, N, K), format, M, N, K, info8);
 }
 
 }  // extern "C"

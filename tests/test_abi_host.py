@@ -269,6 +269,18 @@ def test_i8_ladder():
                     info = qg.i8_rung_info(r, fmt, M, N, K)
                     assert info["tiles_m"] * info["rows"] >= M and info["tiles_n"] * info["cols"] >= N
                     assert info["tiles_m"] * info["tiles_n"] < 2 ** 31
+                    assert K // info["k_step"] >= info["k_split"] >= 1, info
+    # few 192x64 tiles: 64x64 tiles with K also split across workgroups, up to 64 rows (Q6_K up
+    # to 256); measured winners on MI355X, the row quantizer included
+    for fmt, M, N, K, want in [("q6k", 16, 4096, 12288, "i8-64x64-sk"), ("q6k", 256, 4096, 12288, "i8-64x64-sk"),
+                               ("q6k", 300, 4096, 12288, "i8-192x64-k2"), ("q4k", 64, 4096, 4096, "i8-64x64-sk"),
+                               ("q4k", 96, 4096, 4096, "i8-192x64-k2"), ("q4k", 64, 6144, 4096, "i8-64x64-sk"),
+                               ("q4k", 64, 12288, 4096, "i8-192x64-k2"), ("q6k", 658, 4096, 12288, "i8-192x64-k2")]:
+        sel = qg.i8_select_rung(fmt, M, N, K)
+        assert sel["name"] == want, (fmt, M, N, K, sel)
+        if want == "i8-64x64-sk":
+            # at least two slices, each a whole number of chunks for each of four K groups
+            assert sel["k_split"] >= 8 and (K // 128) % sel["k_split"] == 0, sel
 
 
 # ----------------------------------------------------------------------------

@@ -88,7 +88,7 @@ def _run_i8(c: Case, rung: int = -1):
 GEMM_SHAPES = [(1, 48, 512), (37, 200, 768), (130, 72, 256), (300, 264, 1024)]
 
 
-@pytest.mark.parametrize("rung", list(range(8)))
+@pytest.mark.parametrize("rung", list(range(qg.i8_num_rungs())))
 @pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16"])
 @pytest.mark.parametrize("dtype", [qg.F16, qg.BF16])
 def test_i8_gemm_bitexact(rung, fmt, dtype):
@@ -103,6 +103,43 @@ def test_i8_gemm_bitexact(rung, fmt, dtype):
         Y = _run_i8(c, rung)
         want = _oracle_y(c)
         assert same_bits(Y, want), f"{fmt} rung {rung} M={M} N={N} K={K}: {(Y != want).sum()} outputs differ"
+
+
+I8_SK = [r for r in range(qg.i8_num_rungs()) if qg.i8_rung_name(r) == "i8-64x64-sk"][0]
+
+
+@pytest.mark.parametrize("fmt,M,N,K,dtype,ways", [
+    ("q4k", 37, 200, 4096, qg.F16, 16),      # four slices of four K groups; ragged M and N
+    ("w4a16", 64, 256, 4096, qg.BF16, 16),
+    ("q6k", 96, 130, 12288, qg.F16, 32),     # eight slices, two row tiles
+    ("q4k", 5, 64, 16384, qg.BF16, 32),
+])
+def test_i8_split_rung_bitexact(fmt, M, N, K, dtype, ways):
+    """K split across workgroups on the int8 path: the int32 partial sums of
+    the slices add up exactly, so Y has the oracle's bits, and the same bits
+    as the unsplit 128x128 rung."""
+    info = qg.i8_rung_info(I8_SK, fmt, M, N, K)
+    assert info["k_split"] == ways, info
+    c = Case(fmt, M, N, K, dtype, seed=950 + M, group=128)
+    print(f"i8 split {fmt} M={M} N={N} K={K} dtype={dtype} info={info}", flush=True)
+    Y = _run_i8(c, I8_SK)
+    want = _oracle_y(c)
+    assert same_bits(Y, want), f"{(Y != want).sum()} outputs differ"
+    assert same_bits(_run_i8(c, 0), Y)
+
+
+@pytest.mark.parametrize("M", [40, 200])
+def test_i8_split_rung_auto_down_projection(M):
+    """Q6_K 12288 -> 4096 at 40 and 200 rows: the int8 ladder picks the split
+    rung, and its Y has the oracle's bits."""
+    N, K = 4096, 12288
+    sel = qg.i8_select_rung("q6k", M, N, K)
+    assert sel["name"] == "i8-64x64-sk", sel
+    c = Case("q6k", M, N, K, qg.F16, seed=970 + M)
+    print(f"i8 split auto q6k M={M} N={N} K={K} info={sel}", flush=True)
+    Y = _run_i8(c, -1)
+    want = _oracle_y(c)
+    assert same_bits(Y, want), f"{(Y != want).sum()} outputs differ"
 
 
 def test_i8_gemm_zero_rows_and_columns():
