@@ -15,9 +15,10 @@
  *   - Plain pointers and sizes only.  Device pointers must come from the HIP
  *     allocator of the current device; host pointers are ordinary memory.
  *     The caller owns every buffer.  The library never synchronises the
- *     stream and allocates no device memory, with one exception: the rung
- *     that splits K across workgroups (mfma32-64x64-sk) keeps a workspace
- *     for its fp32 partial sums per (device, stream), taken in stream order
+ *     stream and allocates no device memory, with one exception: the rungs
+ *     that split K across workgroups (mfma32-64x64-sk, i8-64x64-sk) keep a
+ *     workspace for their partial sums (fp32, int32) per (device, stream),
+ *     shared by both rungs, taken in stream order
  *     from the device's default memory pool (hipMallocAsync) on first use,
  *     replaced in stream order by a larger one when a call needs more
  *     (S*M*N*4 bytes rounded up to whole MiB, S <= 8 slices) and held until
@@ -307,8 +308,11 @@ int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, 
  *   of qgemm_i8_quantize and Wpacked with rw and sw of qgemm_i8_colscale.
  *   rung -1 picks from this path's own ladder (qgemm_i8_select_rung), else
  *   0 .. qgemm_i8_num_rungs()-1; every rung gives the same bits.  K at most
- *   131072 (int32 sums stay exact).  One launch on `stream`; M = 0 is a
- *   no-op.  Errors as qgemm_gemm_rung. */
+ *   131072 (int32 sums stay exact).  One launch on `stream` (two for
+ *   i8-64x64-sk, which splits K into up to 8 slices across workgroups,
+ *   writes each slice's int32 partial sums to the workspace described at
+ *   the top of this file and adds them, exactly, in the epilogue launch);
+ *   M = 0 is a no-op.  Errors as qgemm_gemm_rung. */
 size_t qgemm_i8_xq_bytes(int64_t M, int64_t K);
 int qgemm_i8_quantize(const void *X, void *Xq, float *sx, int64_t M, int64_t K, int dtype, void *stream);
 int qgemm_i8_colscale(int format, const void *Wpacked, float *rw, float *sw, int64_t N, int64_t K, int64_t group_size,
