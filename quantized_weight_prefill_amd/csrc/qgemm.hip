@@ -1939,15 +1939,17 @@ double stream_cost(long long M, long long np, int cols)
 // and 27 microseconds.  The 48-row direct variant spills for Q6_K and W4A16
 // and is left out for them.  (Q6_K at M = 300..384, N = 4096: 192x64 72-73
 // against 91 us for the 64x64 tiles.)
-// The split rung over few panels of Q6_K, 33..128 rows, on fragment-major
-// activations: one panel and all rows per wave reads the activations once
-// per panel; 64x64 tiles split four ways across workgroups (K = 12288, N =
-// 4096) tie it up to 48 rows and win from 64 (24.2 against 28.1 us; M =
-// 80..128: 39.4-42.3 against 43.0-46.0 us).
+// The split rung over few panels on fragment-major activations (the down
+// projection's K = 12288, N = 4096): one panel and all rows per wave reads
+// the activations once per panel; 64x64 tiles split four ways across
+// workgroups tie it at 33..48 rows and win from 64 (Q6_K M = 64 24.2 against
+// 28.1 us, M = 80..128 39.4-42.3 against 43.0-46.0; W4A16 M = 64..128
+// 20.8-33.8 against 24.9-38.7; Q4_K M = 64 20.6 against 25.2, but from 96
+// rows direct-wide takes Q4_K: 33.0 against 34.6 us).
 bool split_pays(int fmt, long long M, long long np, long long K, int xl)
 {
-    return xl == X_FRAG && fmt == FMT_Q6K && np < 512 && M > 32 && M <= 128 && (K / kChunk) % 16 == 0 &&
-           K / kChunk >= 64;
+    const bool rows = fmt == FMT_Q6K ? (M > 32 && M <= 128) : fmt == FMT_W4 ? (M > 48 && M <= 128) : (M > 48 && M <= 64);
+    return xl == X_FRAG && rows && np < 512 && (K / kChunk) % 16 == 0 && K / kChunk >= 64;
 }
 
 int mid_m_rung(int fmt, long long M, long long np, bool k2_192)
@@ -1972,8 +1974,13 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // above 32 rows a one-panel wave carries three or four row blocks of
     // activations per weight run; four panels per wave and a grid over M win
     if (M <= 64) {
-        // up to 8 rows: one panel per wave, the most waves streaming weights
-        if (M <= 8) return RUNG_SMALL_M;
+        // up to 16 rows: one panel per wave, the most waves streaming
+        // weights, except over 1536 panels and more (gate and up merged),
+        // where four panels per wave keep fewer, longer streams (M = 8, N =
+        // 24576: Q4_K 20.7 against 23.8 us, W4A16 18.2 against 22.7; at N =
+        // 12288 one panel per wave ties at M = 8 and wins at M = 16: Q4_K
+        // 10.6 against 11.7 us)
+        if (M <= 16) return np >= 1536 ? RUNG_SKINNY_N : RUNG_SMALL_M;
         // (three row blocks per wave only pay off for Q4_K: the other
         // formats' larger raw runs spill at that size)
         if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
@@ -1988,7 +1995,7 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         if (split_pays(fmt, M, np, K, xl)) return RUNG_M64_SK;
         // fewer panels: one panel and all rows per wave (each weight
         // unpacked once) beats four panels of 16 rows up to 64 rows
-        return np >= 512 ? RUNG_SKINNY_N : RUNG_SMALL_M;
+        return RUNG_SMALL_M;
     }
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     // occupancy model: a 256x128 tile counts as two 128x128 tiles; the

@@ -349,6 +349,19 @@ def test_ladder_mid_m_round_model():
         sk = qg.select_rung_xf("q6k", M, 4096, 12288)
         assert sk["name"] == "mfma32-64x64-sk" and sk["k_split"] == 16, (M, sk)
     assert qg.select_rung_xf("q6k", 150, 4096, 12288)["name"] == "mfma32-64x64-k4"
+    # up to 16 rows: one panel per wave, except over >= 1536 panels (merged gate/up), where four
+    # panels per wave win (M = 8, N = 24576: Q4_K 20.7 against 23.8 us); both layouts
+    for fmt in ("q4k", "q6k", "w4a16"):
+        for sel in (qg.select_rung, qg.select_rung_xf):
+            for M in (1, 8, 16):
+                assert sel(fmt, M, 24576, 4096)["name"] == "direct-skinny-n", (fmt, M, sel.__name__)
+                assert sel(fmt, M, 12288, 4096)["name"] == "direct-small-m", (fmt, M, sel.__name__)
+    # the split rung at the down projection's shape (fragment-major X): Q6_K 33..128 rows, W4A16
+    # 49..128, Q4_K 49..64 (from 96 rows direct-wide)
+    for fmt, M, want in [("q6k", 40, "mfma32-64x64-sk"), ("w4a16", 40, "direct-small-m"),
+                         ("w4a16", 64, "mfma32-64x64-sk"), ("w4a16", 128, "mfma32-64x64-sk"),
+                         ("q4k", 64, "mfma32-64x64-sk"), ("q4k", 96, "direct-wide"), ("q4k", 32, "direct-small-m")]:
+        assert qg.select_rung_xf(fmt, M, 4096, 12288)["name"] == want, (fmt, M)
     # Q6_K over many panels, 33..64 rows: 64x64 tiles unpack each weight once for all rows
     # (M = 64, N = K = 12288: 52 against 93 us for direct-skinny-n)
     for M in (33, 48, 64):
