@@ -1977,10 +1977,15 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         // up to 16 rows: one panel per wave, the most waves streaming
         // weights, except over 1536 panels and more (gate and up merged),
         // where four panels per wave keep fewer, longer streams (M = 8, N =
-        // 24576: Q4_K 20.7 against 23.8 us, W4A16 18.2 against 22.7; at N =
-        // 12288 one panel per wave ties at M = 8 and wins at M = 16: Q4_K
-        // 10.6 against 11.7 us)
-        if (M <= 16) return np >= 1536 ? RUNG_SKINNY_N : RUNG_SMALL_M;
+        // 24576: Q4_K 20.2 against 23.4 us, W4A16 18.6 against 20.6), and
+        // for 9..16 rows of row-major activations over 512 panels and more,
+        // where each 16-row piece of X then serves four panels (M = 16, N =
+        // 12288: Q4_K 12.2 against 15.7 us; on fragment-major X one panel
+        // per wave wins there, 10.6 against 11.7 us)
+        if (M <= 16) {
+            if (np >= 1536 || (xl == X_ROW && M > 8 && np >= 512)) return RUNG_SKINNY_N;
+            return RUNG_SMALL_M;
+        }
         // (three row blocks per wave only pay off for Q4_K: the other
         // formats' larger raw runs spill at that size)
         if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
