@@ -44,6 +44,7 @@
 // unpack pass) and k_dequant (logical W[K][N]).
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 #include <cstdio>
 #include <algorithm>
@@ -1014,6 +1015,123 @@ k_stream32(Args a)
 #pragma unroll
         for (int rb = 0; rb < RBW; rb++)
             store_block32<DT>(a, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * (wn * CBW + cb), lane);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped streaming tiles (per-expert GEMM, rows pre-grouped by expert):
+// each workgroup owns one 64x64 tile of one expert (two 32-row waves per K
+// group, KS K groups reduced through LDS as in k_stream32), so an expert's
+// activation rows are read once per 64 columns instead of once per 16 as in
+// k_direct_grouped.  Grid: (ceil(T/64) + E) row-tile slots (an upper bound of
+// the experts' row tiles) times the column tiles; a workgroup finds its
+// expert by scanning the device offsets (clamped to be non-decreasing and at
+// most T, as k_direct_grouped does) and leaves at once, before any barrier,
+// when its slot is past the last tile.  Activations row-major.
+// ---------------------------------------------------------------------------
+// Row tile j of the grouped problem: expert e, rows [lo, hi) of the expert
+// (offsets clamped as k_direct_grouped clamps them), tile t of it; false
+// when j is past the last tile.  The clamped bounds are prefix maxima,
+// lo_e = min(M, max(0, offs[0..e])) and hi_e = lo_{e+1}, so one wave settles
+// 64 experts per step with a max scan and a sum scan over its lanes; the
+// result is the same in every lane.
+__device__ __forceinline__ bool find_group_tile(const Args &a, int j, int BMt, int lane, int &e_out, int &lo_out,
+                                                int &hi_out, int &t_out)
+{
+    int qc = max(0, a.offs[0]);  // max(0, offs[0..e0])
+    int base = 0;
+    for (int e0 = 0; e0 < a.E; e0 += 64) {
+        const int e = e0 + lane;
+        const bool live = e < a.E;
+        int q = live ? a.offs[e + 1] : INT_MIN;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(q, d, 64);
+            if (lane >= d) q = max(q, u);
+        }
+        q = max(q, qc);                                  // max(0, offs[0..e+1])
+        int qprev = __shfl_up(q, 1, 64);
+        if (lane == 0) qprev = qc;                       // max(0, offs[0..e])
+        const int lo = min(qprev, a.M), hi = min(q, a.M);
+        const int nb = live ? (hi - lo + BMt - 1) / BMt : 0;
+        int incl = nb;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += u;
+        }
+        const unsigned long long hit = __ballot(live && j < base + incl);
+        if (hit) {
+            const int l = __ffsll((long long)hit) - 1;
+            e_out = e0 + l;
+            lo_out = __shfl(lo, l, 64);
+            hi_out = __shfl(hi, l, 64);
+            t_out = j - (base + __shfl(incl, l, 64) - __shfl(nb, l, 64));
+            return true;
+        }
+        base += __shfl(incl, 63, 64);
+        qc = __shfl(q, 63, 64);
+    }
+    return false;
+}
+
+template <int FMT, int DT, int KS>
+__global__ void __launch_bounds__(128 * KS) __attribute__((amdgpu_waves_per_eu(2)))
+k_stream32_grouped(Args a)
+{
+    using St = Stream32<FMT, DT, 32, 4, 2, 1, X_ROW>;
+    constexpr int CBW = St::CBW, RBW = St::RBW, PB = St::PB, BM = St::BM;
+    constexpr int NACC = 2 * CBW * RBW * 64;
+    static_assert(KS == 1 || (KS - 1) * NACC * sizeof(f32x16) <= KS * sizeof(typename St::Lds),
+                  "K-split reduction must fit in LDS");
+    __shared__ typename St::Lds sWall[KS];
+
+    const int tn = (a.np + PB - 1) / PB;
+    const int nt = blockIdx.x % tn, j = blockIdx.x / tn;
+    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    int e, lo, hi, t;
+    // every wave computes the same answer: the whole workgroup leaves
+    // together, before any barrier
+    if (!find_group_tile(a, j, BM, lane, e, lo, hi, t)) return;
+    Args b = a;
+    b.W = a.W + (long long)e * a.wstride;
+    b.M = hi;
+
+    const int kg = wall / 2, w = wall % 2, tid = threadIdx.x % St::NTG;
+    const int m0 = lo + t * BM + w * 32, p0 = nt * PB;
+    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
+
+    f32x16 acc[CBW][RBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+#pragma unroll
+            for (int q = 0; q < 16; q++) acc[cb][rb][q] = 0.f;
+    St::run(b, sWall[kg], tid, lane, 0, m0, p0, c_lo, c_hi, acc);
+    if constexpr (KS > 1) {
+        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[0]);
+        if (kg > 0) {
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    red[(kg - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; g++)
+#pragma unroll
+            for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+                for (int rb = 0; rb < RBW; rb++)
+                    acc[cb][rb] += red[(g - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane];
+    }
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++)
+#pragma unroll
+        for (int rb = 0; rb < RBW; rb++)
+            store_block32<DT>(b, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * cb, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -2305,6 +2423,18 @@ hipError_t launch_grouped_fd(const Plan &pl, const Args &a, hipStream_t s)
 // expert (three 16-row blocks only for Q4_K, whose runs fit that variant),
 // grid.y an upper bound on every expert's row blocks, K split as the direct
 // rungs do.
+// Grouped 64x64 streaming tiles (k_stream32_grouped), two waves per
+// workgroup over all of K (splitting K inside the workgroup measured slower:
+// too few chunks per group at an expert's K, 98-103 against 80-81 us).
+template <int FMT, int DT>
+hipError_t launch_grouped_stream(const Args &a, long long T, long long E, hipStream_t s)
+{
+    const long long tn = (a.np + 3) / 4, slots = (T + 63) / 64 + E;
+    const dim3 grid((unsigned)(tn * slots));
+    hipLaunchKernelGGL((k_stream32_grouped<FMT, DT, 1>), grid, dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
 Plan grouped_plan(int fmt, long long T, long long E, long long N, long long K)
 {
     Plan pl{};
@@ -2339,10 +2469,22 @@ int grouped(int fmt, const void *X, const void *W, void *Y, const int32_t *offs,
     a.offs = offs;
     a.E = (int)E;
     a.wstride = wstride;
-    const Plan pl = grouped_plan(fmt, T, E, N, K);
-    a.kw = pl.kw;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    // more than 32 rows per expert on average and at least 16 chunks: 64x64
+    // streaming tiles, which read an expert's activation rows once per 64
+    // columns (the direct kernel reads them once per 16): 128 experts, 41
+    // rows each on average, Q4_K 2048 -> 768: 80-81 against 101 us; over 6
+    // chunks (Q6_K 768 -> 2048) the direct kernel stays ahead, 91 against 94
+    if ((T + E - 1) / E > 32 && K / kChunk >= 16) {
+        if (((N + 63) / 64) * ((T + 63) / 64 + E) > INT32_MAX) return QGEMM_ERR_SHAPE;
+        if (fmt == FMT_Q4K) e = dtype == DT_F16 ? launch_grouped_stream<FMT_Q4K, DT_F16>(a, T, E, s) : launch_grouped_stream<FMT_Q4K, DT_BF16>(a, T, E, s);
+        else if (fmt == FMT_Q6K) e = dtype == DT_F16 ? launch_grouped_stream<FMT_Q6K, DT_F16>(a, T, E, s) : launch_grouped_stream<FMT_Q6K, DT_BF16>(a, T, E, s);
+        else e = dtype == DT_F16 ? launch_grouped_stream<FMT_W4, DT_F16>(a, T, E, s) : launch_grouped_stream<FMT_W4, DT_BF16>(a, T, E, s);
+        return launch_status(e, "grouped");
+    }
+    const Plan pl = grouped_plan(fmt, T, E, N, K);
+    a.kw = pl.kw;
     if (fmt == FMT_Q4K) e = dtype == DT_F16 ? launch_grouped_fd<FMT_Q4K, DT_F16>(pl, a, s) : launch_grouped_fd<FMT_Q4K, DT_BF16>(pl, a, s);
     else if (fmt == FMT_Q6K) e = dtype == DT_F16 ? launch_grouped_fd<FMT_Q6K, DT_F16>(pl, a, s) : launch_grouped_fd<FMT_Q6K, DT_BF16>(pl, a, s);
     else e = dtype == DT_F16 ? launch_grouped_fd<FMT_W4, DT_F16>(pl, a, s) : launch_grouped_fd<FMT_W4, DT_BF16>(pl, a, s);
