@@ -239,8 +239,11 @@ int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_
  * offsets[0] = 0 and offsets[E] = T.  The kernel clamps every offset into
  * [0, T] and to at least the previous one, so any contents stay inside X, Y
  * and W (bad offsets only give wrong rows).  Rows outside [offsets[0],
- * offsets[E]) are not written.  One launch on `stream`; results as
- * qgemm_gemm_rung for each expert.  Errors as qgemm_w4a16 (group_size
+ * offsets[E]) are not written.  One launch on `stream`: with more than 32
+ * rows per expert on average (ceil(T/E)) and K of at least 16 chunks of 128,
+ * 64x64 streaming tiles of one expert per workgroup, else the direct kernel
+ * with 16-row groups; results as qgemm_gemm_rung for each expert.  Errors
+ * as qgemm_w4a16 (group_size
  * ignored for the k-quants), plus QGEMM_ERR_SHAPE for E < 1 or a grid
  * beyond ceil(T/16) + E = 65535, QGEMM_ERR_ALIGN when one expert's packed
  * size is not a multiple of 16 bytes; T = 0 is a no-op. */
