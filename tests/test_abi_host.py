@@ -468,3 +468,25 @@ def test_step_gemms_merge():
         ["q", "k", "v", "o", "gate", "up", "down"]
     flops = lambda gs: sum(2 * g["M"] * g["N"] * g["K"] for g in gs)
     assert flops(sg) == flops(synth.step_gemms("qwen3_8b_layer_m658", merge=False))
+
+
+def test_grouped_offset_clamping_prefix_max_form():
+    """The grouped streaming tiles find an expert's rows from prefix maxima,
+    lo_e = min(T, max(0, offs[0..e])) and hi_e = min(T, max(0, offs[0..e+1])),
+    instead of clamping the offsets one after another (each into [0, T] and to
+    at least the previous end).  The two forms agree on arbitrary offsets,
+    negative, decreasing and past T included."""
+    def serial(offs, T):
+        out, hi = [], 0
+        for e in range(len(offs) - 1):
+            lo = min(max(int(offs[e]), hi), T)
+            hi = min(max(int(offs[e + 1]), lo), T)
+            out.append((lo, hi))
+        return out
+
+    rng = np.random.default_rng(17)
+    for _ in range(5000):
+        E, T = int(rng.integers(1, 12)), int(rng.integers(0, 300))
+        offs = rng.integers(-50, 400, E + 1)
+        q = np.maximum.accumulate(np.concatenate([[0], offs]))[1:]
+        assert [(min(int(q[e]), T), min(int(q[e + 1]), T)) for e in range(E)] == serial(offs, T), (offs, T)

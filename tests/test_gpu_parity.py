@@ -330,6 +330,49 @@ def _grouped_case(fmt, sym, counts, N, K, dtype, seed):
     return cases, X, torch.from_numpy(W_all).cuda(), torch.from_numpy(offs).cuda(), offs
 
 
+def _clamped_ranges(offs, T):
+    """The row range each expert gets from arbitrary offsets, by the header's
+    rule: every offset clamped into [0, T] and to at least the previous
+    expert's end (written out serially)."""
+    out, hi = [], 0
+    for e in range(len(offs) - 1):
+        lo = min(max(int(offs[e]), hi), T)
+        hi = min(max(int(offs[e + 1]), lo), T)
+        out.append((lo, hi))
+    return out
+
+
+@pytest.mark.parametrize("K", [512, 2048], ids=["direct", "stream"])
+def test_grouped_malformed_offsets(K):
+    """Offsets that are negative, decreasing or past T: both grouped kernels
+    (K = 512 takes the direct kernel, K = 2048 the 64x64 streaming tiles at
+    these 50 rows per expert) compute exactly the clamped ranges, and write
+    nothing outside Y."""
+    import torch
+
+    T, N, fmt = 200, 80, "q4k"
+    offs = np.array([-5, 90, 40, 170, 500], np.int32)
+    cases = [Case(fmt, T, N, K, qg.F16, seed=450 + e) for e in range(len(offs) - 1)]
+    X = cases[0].X
+    W = torch.from_numpy(np.concatenate([c.packed for c in cases])).cuda()
+    pad = 4096
+    buf = torch.full((T * N + 2 * pad,), 7.0, dtype=torch.float16, device="cuda")
+    out = buf[pad:pad + T * N].view(T, N)
+    print(f"grouped malformed offsets K={K} offs={offs.tolist()}", flush=True)
+    qg.grouped(fmt, to_device(X, qg.F16), W, N, torch.from_numpy(offs).cuda(), len(cases), out=out)
+    host = buf.cpu()
+    assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
+    Y = from_device(out)
+    covered = np.zeros(T, bool)
+    for e, (lo, hi) in enumerate(_clamped_ranges(offs, T)):
+        if hi <= lo:
+            continue
+        covered[lo:hi] = True
+        Yref, B = oracle.gemm(X[lo:hi], cases[e].W, qg.F16)
+        assert_gemm_close(Y[lo:hi], Yref, B, qg.F16, what=f"malformed offsets expert {e} rows {lo}..{hi}")
+    assert covered.all()  # [0, T) is covered by the clamped ranges here
+
+
 @pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
 def test_grouped_stream_parity(fmt, sym, dtype):
