@@ -2057,17 +2057,30 @@ double stream_cost(long long M, long long np, int cols)
 // and 27 microseconds.  The 48-row direct variant spills for Q6_K and W4A16
 // and is left out for them.  (Q6_K at M = 300..384, N = 4096: 192x64 72-73
 // against 91 us for the 64x64 tiles.)
-// The split rung over few panels on fragment-major activations (the down
-// projection's K = 12288, N = 4096): one panel and all rows per wave reads
-// the activations once per panel; 64x64 tiles split four ways across
-// workgroups tie it at 33..48 rows and win from 64 (Q6_K M = 64 24.2 against
-// 28.1 us, M = 80..128 39.4-42.3 against 43.0-46.0; W4A16 M = 64..128
-// 20.8-33.8 against 24.9-38.7; Q4_K M = 64 20.6 against 25.2, but from 96
-// rows direct-wide takes Q4_K: 33.0 against 34.6 us).
-bool split_pays(int fmt, long long M, long long np, long long K, int xl)
+// The split rung over few panels (N = 4096) on fragment-major activations:
+// one panel and all rows per wave reads the activations once per panel, the
+// 64x64 tiles split across workgroups read a slice of them.  Measured on
+// MI355X (weights rotating):
+//  * K = 12288 (four slices): Q6_K and W4A16, and every format in bf16,
+//    from 33 rows (Q6_K M = 64 24.2 against 28.1 us; W4A16 M = 48..128
+//    18.5-33.8 against 20.4-38.7; bf16 Q4_K M = 96 33.3 against 42.2 on
+//    direct-wide); fp16 Q4_K at 49..64 only (from 96 rows direct-wide leads,
+//    33.0 against 34.6 us);
+//  * K = 4096 (two slices): 65..128 rows in both dtypes (W4A16 M = 96: 14.2
+//    against 15.2 us fp16, 13.7 against 15.5 bf16), while the two slices'
+//    tiles fit one workgroup per CU (at N = 6144 they lose, 28.3 against
+//    15.8 us).
+// Over at most 128 panels the split grid fills a quarter of the CUs or less
+// and one panel per wave stays ahead (N = 1024, M = 96..128: 8.3-9.4
+// against 12.5-14.7 us).
+bool split_pays(int fmt, int dtype, long long M, long long np, long long K, int xl)
 {
-    const bool rows = fmt == FMT_Q6K ? (M > 32 && M <= 128) : fmt == FMT_W4 ? (M > 48 && M <= 128) : (M > 48 && M <= 64);
-    return xl == X_FRAG && rows && np < 512 && (K / kChunk) % 16 == 0 && K / kChunk >= 64;
+    const long long nch = K / kChunk, tn = (np + 3) / 4, tm = (M + 63) / 64;
+    if (xl != X_FRAG || np > 256 || np <= 128 || M > 128) return false;
+    if (nch >= 32 && nch < 64 && nch % 8 == 0) return M > 64 && tn * tm * 2 <= kCUs;
+    if (nch < 64 || nch % 16 != 0) return false;
+    if (dtype == DT_BF16 || fmt != FMT_Q4K) return M > 32;
+    return M > 48 && M <= 64;
 }
 
 int mid_m_rung(int fmt, long long M, long long np, bool k2_192)
@@ -2082,7 +2095,7 @@ int mid_m_rung(int fmt, long long M, long long np, bool k2_192)
     return small <= k4 ? RUNG_SMALL_M : RUNG_M64_K4;
 }
 
-int select_rung(int fmt, long long M, long long N, long long K, int xl)
+int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtype = DT_F16)
 {
     const long long np = (N + 15) / 16, tn = (np + 7) / 8;
     // the direct kernels put row groups of 16 on grid.y (at most 65535);
@@ -2115,7 +2128,7 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
         // Q6_K over few panels (N = 4096): 64x64 tiles with K also split
         // across workgroups, so that each CU reads a quarter of the
         // activations
-        if (split_pays(fmt, M, np, K, xl)) return RUNG_M64_SK;
+        if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
         // fewer panels: one panel and all rows per wave (each weight
         // unpacked once) beats four panels of 16 rows up to 64 rows
         return RUNG_SMALL_M;
@@ -2125,7 +2138,7 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl)
     // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
-    if (split_pays(fmt, M, np, K, xl)) return RUNG_M64_SK;
+    if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
     if (t128 < 128) return mid_m_rung(fmt, M, np, xl == X_FRAG && (K / kChunk) % 2 == 0);
     // on fragment-major activations, a 192-row tile with K split over two
     // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
@@ -2395,7 +2408,7 @@ int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, 
     if (!X || !W || !Y) return QGEMM_ERR_NULL;
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
     Plan pl;
-    st = make_plan(rung < 0 ? select_rung(fmt, M, N, K, xl) : rung, M, N, K, pl);
+    st = make_plan(rung < 0 ? select_rung(fmt, M, N, K, xl, dtype) : rung, M, N, K, pl);
     if (st != QGEMM_OK) return st;
     Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
     a.kw = pl.kw;
@@ -2893,12 +2906,12 @@ int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int d
 
 int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
 {
-    return qgemm_rung_info(select_rung(format, M, N, K, X_ROW), format, M, N, K, dtype, info8);
+    return qgemm_rung_info(select_rung(format, M, N, K, X_ROW, dtype), format, M, N, K, dtype, info8);
 }
 
 int qgemm_select_rung_xf(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
 {
-    return qgemm_rung_info(select_rung(format, M, N, K, X_FRAG), format, M, N, K, dtype, info8);
+    return qgemm_rung_info(select_rung(format, M, N, K, X_FRAG, dtype), format, M, N, K, dtype, info8);
 }
 
 size_t qgemm_xf_bytes(int64_t M, int64_t K)

@@ -360,12 +360,23 @@ def test_ladder_mid_m_round_model():
             assert qg.select_rung_xf(fmt, M, 12288, 4096)["name"] == "direct-small-m", (fmt, M)
         assert qg.select_rung(fmt, 8, 12288, 4096)["name"] == "direct-small-m", fmt
         assert qg.select_rung(fmt, 16, 12288, 4096)["name"] == "direct-skinny-n", fmt
-    # the split rung at the down projection's shape (fragment-major X): Q6_K 33..128 rows, W4A16
-    # 49..128, Q4_K 49..64 (from 96 rows direct-wide)
-    for fmt, M, want in [("q6k", 40, "mfma32-64x64-sk"), ("w4a16", 40, "direct-small-m"),
+    # the split rung at the down projection's shape (fragment-major X): fp16 Q6_K and W4A16 33..128
+    # rows, Q4_K 49..64 (from 96 rows direct-wide); bf16 every format from 33 rows
+    for fmt, M, want in [("q6k", 40, "mfma32-64x64-sk"), ("w4a16", 40, "mfma32-64x64-sk"),
                          ("w4a16", 64, "mfma32-64x64-sk"), ("w4a16", 128, "mfma32-64x64-sk"),
                          ("q4k", 64, "mfma32-64x64-sk"), ("q4k", 96, "direct-wide"), ("q4k", 32, "direct-small-m")]:
         assert qg.select_rung_xf(fmt, M, 4096, 12288)["name"] == want, (fmt, M)
+    for fmt, M, want in [("q4k", 96, "mfma32-64x64-sk"), ("q4k", 48, "mfma32-64x64-sk"),
+                         ("w4a16", 40, "mfma32-64x64-sk"), ("q4k", 32, "direct-small-m")]:
+        assert qg.select_rung_xf(fmt, M, 4096, 12288, qg.BF16)["name"] == want, (fmt, M)
+    # K = 4096 over 4096 columns: two slices from 65 rows in both dtypes; not over 1024 or 6144 columns
+    for dt in (qg.F16, qg.BF16):
+        for fmt in ("q4k", "q6k", "w4a16"):
+            sk = qg.select_rung_xf(fmt, 96, 4096, 4096, dt)
+            assert sk["name"] == "mfma32-64x64-sk" and sk["k_split"] == 8, (fmt, dt, sk)
+            assert qg.select_rung_xf(fmt, 64, 4096, 4096, dt)["name"] == "direct-small-m", (fmt, dt)
+            assert qg.select_rung_xf(fmt, 128, 1024, 4096, dt)["name"] != "mfma32-64x64-sk", (fmt, dt)
+            assert qg.select_rung_xf(fmt, 96, 6144, 4096, dt)["name"] != "mfma32-64x64-sk", (fmt, dt)
     # Q6_K over many panels, 33..64 rows: 64x64 tiles unpack each weight once for all rows
     # (M = 64, N = K = 12288: 52 against 93 us for direct-skinny-n)
     for M in (33, 48, 64):
