@@ -34,14 +34,19 @@
 //   * v_mfma_f32_16x16x32 (direct kernels, the 256-row streaming tile): lane
 //     (r, g) of MFMA i carries k = 128*chunk + 32*g + 8*i + 0..7 (direct) or
 //     128*chunk + 32*i + 8*g + 0..7 (streaming);
-//   * v_mfma_f32_32x32x16 (the 128-row streaming tiles): lane (r, h) of
-//     k-step s carries k = 128*chunk + 16*s + 8*h + 0..7.
+//   * v_mfma_f32_32x32x16 (the k_stream32 family): lane (r, h) of k-step s
+//     carries k = 128*chunk + 16*s + 8*h + 0..7.
 //
 // Kernels: k_direct / k_direct_grouped (small M: each wave unpacks its own
 // runs, waves split K), k_stream (16x16x32, 256x128 tiles) and k_stream32
-// (32x32x16, 128x128 and 128x160 tiles) for larger M (each weight unpacked
-// once per workgroup into double-buffered LDS), k_stage (the staged arm's
-// unpack pass) and k_dequant (logical W[K][N]).
+// (32x32x16: 128x128, 128x160, 352x96, 192x96, 192x64 and 64x64 tiles, K
+// split over wave groups where it pays) for larger M (each weight unpacked
+// once per workgroup into double-buffered LDS), k_stream32_sk +
+// k_splitk_reduce (64x64 tiles with K also split across workgroups, for few
+// tiles), k_stream32_grouped (per-expert 64x64 tiles), k_stage (the staged
+// arm's unpack pass), k_dequant (logical W[K][N]); the int8-activation path's
+// k_i8_quant, k_i8_colscale, k_i8_stream and k_i8_stream_sk +
+// k_i8_splitk_reduce.
 #include <hip/hip_runtime.h>
 
 #include <climits>
