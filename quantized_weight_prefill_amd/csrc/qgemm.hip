@@ -2020,15 +2020,19 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    direct kernel with all panels per wave (a 128-wide tile would leave most
 //    of the part idle and most of each tile padding);
 //  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
-//    and the kernel is a weight stream; up to 8 rows, and with fewer than
-//    512 panels up to 64 rows, one panel and all rows per wave (the most
-//    waves streaming, each weight unpacked once); with many panels: 17..32
-//    rows (17..48 for Q4_K) four panels and all rows per wave (each
-//    activation fragment feeds four panels), 49..64 rows of Q4_K and 33..64
-//    of W4A16 64x64 streaming tiles with K split four ways, otherwise four
-//    panels and 16 rows per wave;
-//  * fewer than 128 tiles of 128x128: the direct kernels or 64x64 K-split
-//    streaming tiles, by the round model of mid_m_rung;
+//    and the kernel is a weight stream; up to 16 rows one panel and all rows
+//    per wave (the most waves streaming, each weight unpacked once), except
+//    over 1536 panels and more and, on row-major activations, at 9..16 rows
+//    over 512 panels and more: four panels and 16 rows per wave; with fewer
+//    than 512 panels up to 64 rows one panel per wave, or on fragment-major
+//    activations over 129..256 panels 64x64 tiles with K split across
+//    workgroups too (split_pays); with many panels: 17..32 rows (17..48 for
+//    Q4_K) four panels and all rows per wave (each activation fragment feeds
+//    four panels), 49..64 rows of Q4_K and 33..64 of W4A16 and Q6_K 64x64
+//    streaming tiles with K split four ways;
+//  * fewer than 128 tiles of 128x128: the split rung where split_pays, else
+//    the direct kernels, 64x64 K-split tiles or (fragment-major) 192x64
+//    K-split tiles, by the round model of mid_m_rung;
 //  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
 //    for 256 rows) when the occupancy model below has it finish no later
 //    than the 128-row tiles;
@@ -2036,9 +2040,11 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    32x32x16 MFMAs with K split between two wave groups;
 //  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
 //    whichever the occupancy model below finishes first.
-// On fragment-major activations two crossovers move (the rules are in
-// select_rung): the K-split 128x128 tile serves every shape with at most 256
-// of its tiles, and the 256-row tile also wins whenever it has 512 tiles.
+// On fragment-major activations the three-waves-per-SIMD tiles come first
+// where they fit (192x64 and 192x96 with K split over two 6-wave groups,
+// 352x96; the rules are in select_rung), the K-split 128x128 tile serves the
+// other shapes with at most 256 of its tiles, and the 256-row tile also wins
+// whenever it has 512 tiles.
 // Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
 // of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
 // the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
