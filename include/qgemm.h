@@ -23,7 +23,11 @@
  *     replaced in stream order by a larger one when a call needs more
  *     (S*M*N*4 bytes rounded up to whole MiB, S <= 8 slices) and held until
  *     the process ends; a lock serialises its bookkeeping and the two
- *     launches of such a call.  Calls are re-entrant; calls on different
+ *     launches of such a call.  While the stream is being captured into a
+ *     HIP graph nothing is taken or returned: a call that would need a
+ *     larger workspace then fails with QGEMM_ERR_HIP before launching, so
+ *     make one call of the same or larger size on that stream before the
+ *     capture.  Calls are re-entrant; calls on different
  *     streams never share a workspace.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     GEMM and dequant calls are asynchronous on that stream.

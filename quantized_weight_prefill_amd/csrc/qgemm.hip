@@ -2356,15 +2356,22 @@ std::mutex g_ws_mu;
 std::vector<SplitWs> g_ws;
 
 // With g_ws_mu held: a workspace of at least `bytes` for (current device, s).
+// While `s` is being captured into a graph nothing is taken or returned (the
+// graph would own that memory): a workspace too small then is an error, and
+// one eager call on the stream beforehand provides it.
 hipError_t split_workspace(hipStream_t s, size_t bytes, void **out)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(s, &cap)) != hipSuccess) return e;
+    const bool capturing = cap != hipStreamCaptureStatusNone;
     bytes = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);  // whole MiB: fewer regrowths
     for (SplitWs &w : g_ws) {
         if (w.dev != dev || w.stream != s) continue;
         if (w.bytes < bytes) {
+            if (capturing) return hipErrorStreamCaptureUnsupported;
             void *np = nullptr;
             if ((e = hipMallocAsync(&np, bytes, s)) != hipSuccess) return e;
             void *old = w.p;
@@ -2375,6 +2382,7 @@ hipError_t split_workspace(hipStream_t s, size_t bytes, void **out)
         *out = w.p;
         return hipSuccess;
     }
+    if (capturing) return hipErrorStreamCaptureUnsupported;
     void *np = nullptr;
     if ((e = hipMallocAsync(&np, bytes, s)) != hipSuccess) return e;
     g_ws.push_back(SplitWs{dev, s, np, bytes});

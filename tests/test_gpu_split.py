@@ -86,3 +86,37 @@ def test_split_rung_concurrent_streams():
     for i in range(len(cases)):
         for rep in range(4):
             assert np.array_equal(from_device(outs[i][rep]), alone[i]), (i, rep)
+
+
+def test_split_rung_graph_capture_after_warmup():
+    """A split-rung call captured into a HIP graph after one eager call on the
+    capture stream (which takes that stream's workspace, so the capture takes
+    or returns no memory): every replay, with eager work and synchronisations
+    in between, equals the eager result."""
+    import torch
+
+    c = Case("q6k", 64, 256, 12288, qg.F16, seed=780)
+    x = to_device(c.X, c.dtype)
+    wp = c.device_weights()
+    ref = from_device(c.run(SK))
+    s = torch.cuda.Stream()
+    y = torch.empty((64, 256), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    print("split graph capture: warm-up on the capture stream", flush=True)
+    with torch.cuda.stream(s):
+        qg.gemm_rung("q6k", SK, x, wp, 256, out=y, stream=s.cuda_stream)
+    s.synchronize()
+    assert np.array_equal(from_device(y), ref)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    print("split graph capture: capture", flush=True)
+    with torch.cuda.graph(g, stream=s):
+        qg.gemm_rung("q6k", SK, x, wp, 256, out=y, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(0)
+        torch.cuda.synchronize()
+        print(f"split graph capture: replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_device(y), ref), rep
