@@ -488,6 +488,9 @@ def probe_read(buf, out, blocks: int, stream=None):
 # M-ladder queries
 # ---------------------------------------------------------------------------
 
+# The eight integers of qgemm_select_rung / qgemm_rung_info: k_split counts the
+# K-split ways inside a workgroup times the K slices across workgroups (the
+# split rungs mfma32-64x64-sk and i8-64x64-sk).
 _INFO_KEYS = ("rung", "rows", "cols", "k_step", "waves", "k_split", "tiles_n", "tiles_m")
 
 
