@@ -2182,8 +2182,10 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
     if (k2_192 && t192 <= 2 * kCUs && 10 * t192 >= 18 * kCUs) return RUNG_M192N96_K2;
     // the 256-row tile when the occupancy model has it finish no later than
     // the 128-row tiles (it unpacks each weight once for 256 rows); on
-    // fragment-major activations also whenever it has 512 tiles
-    if (c256 <= c128 || (xl == X_FRAG && t256 >= 512)) return RUNG_M16_256;
+    // fragment-major activations also whenever it has 512 tiles, and for
+    // Q6_K, whose unpack costs most, from one full round of them (M = 1024,
+    // N = K = 12288: 363.9 against 400.4 us for 128x128)
+    if (c256 <= c128 || (xl == X_FRAG && (t256 >= 512 || (fmt == FMT_Q6K && t256 >= kCUs)))) return RUNG_M16_256;
     // few tiles: split K inside the workgroup (on row-major activations only
     // over a long K, where the halves' activation reloads stay affordable)
     if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) return RUNG_M128_K2;

@@ -412,6 +412,8 @@ def test_ladder_fragment_major():
     assert qg.select_rung_xf("q4k", 658, 12288, 4096)["name"] == "mfma32-352x96"       # 352x96 before two 192x96 rounds
     assert qg.select_rung_xf("q6k", 768, 12288, 4096)["name"] == "mfma32-192x96-k2"    # two full rounds of 192x96
     assert qg.select_rung_xf("q4k", 2048, 12288, 4096)["name"] == "mfma16-256x128"    # 768 tiles: three rounds either way
+    assert qg.select_rung_xf("q6k", 1024, 12288, 12288)["name"] == "mfma16-256x128"   # Q6_K from one round of 256-row tiles
+    assert qg.select_rung_xf("q6k", 1024, 4096, 12288)["name"] == "mfma32-128x128-k2"  # half a round: not
     # (at 9..16 rows over 512..1535 panels the layouts differ on purpose: see the small-M test)
     for fmt, M, K, N in [("q4k", 658, 4096, 1024), ("q4k", 8, 4096, 12288),
                          ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
