@@ -54,7 +54,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import quantized_weight_prefill_amd as qg  # noqa: E402
-from quantized_weight_prefill_amd import synth  # noqa: E402
+from quantized_weight_prefill_amd import probe, synth  # noqa: E402
 
 METRIC = "fused Q4_K GEMM TFLOP/s + prefill tok/s (Qwen3-8B shapes, M=658); % roofline"
 PEAK_TFLOPS = {qg.F16: 2500.0, qg.BF16: 2500.0}  # dense MFMA, fp16 / bf16
@@ -71,10 +71,17 @@ def weight_bytes(fmt: str, N: int, K: int, group: int, sym: bool) -> float:
 
 
 def source_hash() -> str:
+    """Digest of the library's sources (every file under csrc/ but the probe
+    library's), the key that ties a committed counter summary to the
+    kernels it was taken on."""
     h = hashlib.sha256()
-    for f in ("qgemm.hip", "pack.cpp"):
-        with open(os.path.join(ROOT, "quantized_weight_prefill_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    base = os.path.join(ROOT, "quantized_weight_prefill_amd", "csrc")
+    for f in sorted(os.listdir(base)):
+        path = os.path.join(base, f)
+        if os.path.isfile(path):
+            h.update(f.encode())
+            with open(path, "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -139,7 +146,7 @@ class HipTimer:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=70)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_layer_m658",
                     choices=sorted(synth.WORKLOADS) + sorted(synth.MOE_WORKLOADS))
@@ -223,15 +230,18 @@ def main() -> int:
         # pre-marshalled C calls (one per weight copy): the GEMM entry point
         # for the layout, rung -1 being the layout's M-ladder
         grp, zp = (group if fmt == "w4a16" else 0), int(not sym)
+        # the split rungs' partial sums live in a workspace the caller owns
+        nws = qg.workspace_bytes(fmt, args.rung, M, N, K, dt, qg.X_FRAG if xf_layout else qg.X_ROW)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
         if xf_layout:
             calls = [functools.partial(lib.qgemm_gemm_xf, qg.FORMATS[fmt], args.rung, ptr(xf), ptr(w), ptr(y), M, N, K,
-                                       grp, zp, dt, sp) for w in pool]
+                                       grp, zp, dt, ptr(ws), nws, sp) for w in pool]
         else:
             calls = [functools.partial(lib.qgemm_gemm_rung, qg.FORMATS[fmt], args.rung, ptr(x), ptr(w), ptr(y), M, N,
-                                       K, grp, zp, dt, sp) for w in pool]
+                                       K, grp, zp, dt, ptr(ws), nws, sp) for w in pool]
         gemms.append(dict(label=label, fmt=fmt, M=M, K=K, N=N, dt=dt, group=group, sym=sym, x=x, wp=wp, y=y,
                           X=X, enc=enc, rung=info["name"], flops=2.0 * M * N * K, wbytes=wbytes, pool=pool, turn=0,
-                          calls=calls, prep=prep, src=src,
+                          calls=calls, prep=prep, src=src, ws=ws,
                           members=[wl["gemms"][i][0] for i in sg["members"]], below_ridge=below_ridge))
         print(f"[bench] {label}: {fmt} M={M} K={K} N={N} x={args.x_layout} rung={info['name']}", file=sys.stderr,
               flush=True)
@@ -287,25 +297,41 @@ def main() -> int:
     gemm_ms = [float(np.mean([timer.ms(*ev[s][j]) for s in range(nprof)])) for j in range(len(gemms))]
     jd = int(np.argmax(gemm_ms))  # the dominant GEMM: largest share of the step
 
-    # timed region: K steps back to back; HIP events on the launch stream
-    # around every launch of the dominant GEMM
+    # timed region: K steps back to back, in (up to) ten samples of
+    # consecutive steps; fence-less HIP events on the launch stream mark the
+    # samples' ends and bracket every launch of the dominant GEMM
+    nsamp = min(10, args.steps)
+    bounds = [round(i * args.steps / nsamp) for i in range(nsamp + 1)]
+    evs = [timer.pair() for _ in range(nsamp)]
     evd = [timer.pair() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        for j, g in enumerate(gemms):
-            if g["prep"] is not None:
-                call_prep(g["prep"])
-            if j == jd:
-                timer.record(evd[s][0], sp)
-                call(g)
-                timer.record(evd[s][1], sp)
-            else:
-                call(g)
+    for i in range(nsamp):
+        timer.record(evs[i][0], sp)
+        for s in range(bounds[i], bounds[i + 1]):
+            for j, g in enumerate(gemms):
+                if g["prep"] is not None:
+                    call_prep(g["prep"])
+                if j == jd:
+                    timer.record(evd[s][0], sp)
+                    call(g)
+                    timer.record(evd[s][1], sp)
+                else:
+                    call(g)
+        timer.record(evs[i][1], sp)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     gemm_ms[jd] = float(np.mean([timer.ms(e0, e1) for e0, e1 in evd]))
+    sample_ms = [timer.ms(*evs[i]) / (bounds[i + 1] - bounds[i]) for i in range(nsamp)]
+    launches_per_step = len(gemms) + len(preps)
+
+    def run_step():
+        for g in gemms:
+            if g["prep"] is not None:
+                call_prep(g["prep"])
+            call(g)
+    state = gpu_state(run_step)
 
     for j, g in enumerate(gemms):
         ms = gemm_ms[j]
@@ -367,6 +393,13 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(float(np.median(sample_ms)), 5),
+        "ms_per_step_samples": [round(v, 5) for v in sample_ms],
+        "timing": f"{args.steps} steps in {nsamp} samples of consecutive steps ({launches_per_step} launches a step, "
+                  f"{min(b - a for a, b in zip(bounds, bounds[1:])) * launches_per_step}+ a sample); ms_per_step is "
+                  "the wall clock over all of them between synchronisations, ms_per_step_median the median of the "
+                  "samples' HIP-event times",
+        "gpu_state": state,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -402,6 +435,70 @@ def main() -> int:
     return 0
 
 
+def gpu_state(run_step, steps: int = 300, every: int = 10) -> dict:
+    """Shader clock, memory clock and temperatures while the step runs: the
+    step is queued `every` steps at a time and the GPU's metrics table is read
+    between the batches (the GPU is busy with the queued work meanwhile), over
+    `steps` steps after the timed region.  Read through amdsmi; on a host
+    without it the reason is recorded instead."""
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        h = handles[0]
+        try:  # the GPU torch runs on, by PCI address, when several are listed
+            props = torch.cuda.get_device_properties(0)
+            want = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}"
+            for cand in handles:
+                if amdsmi.amdsmi_get_gpu_device_bdf(cand).lower().startswith(want):
+                    h = cand
+                    break
+        except Exception:
+            pass
+    except Exception as e:  # pragma: no cover - depends on the host
+        return {"error": f"amdsmi unavailable: {e}"}
+
+    def valid(v):
+        vals = v if isinstance(v, (list, tuple)) else [v]
+        return [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 0xFFFF]
+
+    keys = {"sclk_mhz": ("current_gfxclk", "current_gfxclks"), "mclk_mhz": ("current_uclk",),
+            "temp_hotspot_c": ("temperature_hotspot",), "temp_mem_c": ("temperature_mem",),
+            "power_w": ("current_socket_power",), "gfx_activity_pct": ("average_gfx_activity",)}
+    got = {k: [] for k in keys}
+    err = None
+    for i in range(steps // every):
+        for _ in range(every):
+            run_step()
+        if i < 2:
+            continue  # let the queue fill first
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        except Exception as e:  # pragma: no cover
+            err = str(e)
+            break
+        for k, names in keys.items():
+            for n in names:
+                if n in m and valid(m[n]):
+                    got[k].append(float(np.mean(valid(m[n]))))
+                    break
+    torch.cuda.synchronize()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    out = {k: ([round(min(v), 1), round(float(np.mean(v)), 1), round(max(v), 1)] if v else None)
+           for k, v in got.items()}
+    out["format"] = "[min, mean, max] over the samples read while the step ran (amdsmi gpu_metrics; sclk averaged over XCDs)"
+    out["samples"] = max((len(v) for v in got.values()), default=0)
+    if err:
+        out["error"] = err
+    return out
+
+
 def mfma_ceiling(dt) -> dict:
     """What the chip sustains on dense MFMA work: the rate probe (four waves
     per SIMD, four independent 32x32x16 accumulators per wave) on seeded
@@ -419,11 +516,11 @@ def mfma_ceiling(dt) -> dict:
 
     def rate(ops):
         for _ in range(2):
-            qg.probe_mfma(ops, out, blocks, iters, dt)
+            probe.mfma(ops, out, blocks, iters, dt)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
-            qg.probe_mfma(ops, out, blocks, iters, dt)
+            probe.mfma(ops, out, blocks, iters, dt)
         e1.record(stream)
         torch.cuda.synchronize()
         return round(flops / (e0.elapsed_time(e1) / reps) / 1e9, 1)
@@ -538,35 +635,43 @@ def run_grouped(args) -> int:
     return 0
 
 
-def staged_arm(g, call, reps: int = 20) -> dict:
-    """The dominant GEMM fused (its rung in the step, on the step's activation
-    layout, and the 128x128 rung on row-major activations, the tile the staged
-    GEMM shares) against the staged arm: unpack into a 2-byte scratch, then
-    the same 128x128 streaming kernel on it, on row-major activations.
-    Back-to-back launches between HIP events on the launch stream, median of
-    5 samples."""
+def interleaved(arms: dict, reps: int = 20, rounds: int = 5) -> dict:
+    """Median ms per launch of each arm, the arms interleaved (one sample of
+    `reps` back-to-back launches of each arm in turn, `rounds` times), so
+    that clock and thermal drift hit every arm alike.  HIP events on the
+    launch stream around each sample."""
     import torch
 
     stream = torch.cuda.current_stream()
-    rung128 = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-128x128"][0]
-    grp = g["group"] if g["fmt"] == "w4a16" else 0
-    scratch = torch.empty(qg.staged_scratch_bytes(g["N"], g["K"]), dtype=torch.uint8, device="cuda")
-    x0 = g["x"][:0]
-    y0 = g["y"][:0]
-
-    def timed(fn):
+    for fn in arms.values():
         fn()
-        samples = []
-        for _ in range(5):
+    samples = {k: [] for k in arms}
+    for _ in range(rounds):
+        for k, fn in arms.items():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(reps):
                 fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            samples.append(e0.elapsed_time(e1) / reps)
-        return float(np.median(samples))
+            samples[k].append(e0.elapsed_time(e1) / reps)
+    return {k: float(np.median(v)) for k, v in samples.items()}
 
+
+def staged_arm(g, call, reps: int = 20) -> dict:
+    """The dominant GEMM fused (its rung in the step, on the step's activation
+    layout, and the 128x128 rung on row-major activations, the tile the staged
+    GEMM shares) against the staged arm: unpack into a 2-byte scratch, then
+    the same 128x128 streaming kernel on it, on row-major activations.  The
+    arms are interleaved: five rounds of 20 back-to-back launches each, the
+    median sample per arm."""
+    import torch
+
+    rung128 = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-128x128"][0]
+    grp = g["group"] if g["fmt"] == "w4a16" else 0
+    scratch = torch.empty(qg.staged_scratch_bytes(g["N"], g["K"]), dtype=torch.uint8, device="cuda")
+    x0 = g["x"][:0]
+    y0 = g["y"][:0]
     # every arm rotates through the same weight copies as the step
     turn = [0]
 
@@ -574,13 +679,15 @@ def staged_arm(g, call, reps: int = 20) -> dict:
         turn[0] += 1
         return g["pool"][turn[0] % len(g["pool"])]
 
-    fused = timed(lambda: call(g))
-    same_tile = timed(lambda: qg.gemm_rung(g["fmt"], rung128, g["x"], wp(), g["N"], group=grp,
-                                           has_zp=not g["sym"], out=g["y"]))
-    staged = timed(lambda: qg.staged(g["fmt"], g["x"], wp(), g["N"], scratch=scratch, group=grp,
-                                     has_zp=not g["sym"], out=g["y"]))
-    unpack = timed(lambda: qg.staged(g["fmt"], x0, wp(), g["N"], scratch=scratch, group=grp,
-                                     has_zp=not g["sym"], out=y0))
+    t = interleaved({
+        "fused": lambda: call(g),
+        "same_tile": lambda: qg.gemm_rung(g["fmt"], rung128, g["x"], wp(), g["N"], group=grp, has_zp=not g["sym"],
+                                          out=g["y"]),
+        "staged": lambda: qg.staged(g["fmt"], g["x"], wp(), g["N"], scratch=scratch, group=grp, has_zp=not g["sym"],
+                                    out=g["y"]),
+        "unpack": lambda: qg.staged(g["fmt"], x0, wp(), g["N"], scratch=scratch, group=grp, has_zp=not g["sym"],
+                                    out=y0)}, reps)
+    fused, same_tile, staged, unpack = t["fused"], t["same_tile"], t["staged"], t["unpack"]
     wq = g["wbytes"]
     w16 = 2.0 * g["K"] * (-(-g["N"] // 16) * 16)
     return {"gemm": g["label"], "fused_rung": g["rung"], "fused_ms": round(fused, 5),
@@ -588,6 +695,7 @@ def staged_arm(g, call, reps: int = 20) -> dict:
             "staged_ms": round(staged, 5), "unpack_ms": round(unpack, 5),
             "staged_gemm_ms": round(staged - unpack, 5), "staged_over_fused_same_tile": round(staged / same_tile, 3),
             "weight_bytes_fused": round(wq), "weight_bytes_staged": round(wq + 2 * w16),
+            "timing": "arms interleaved, 5 rounds of 20 launches each, median",
             "note": "staged = unpack pass (reads packed W, writes 2 B/weight) + the same 128x128 kernel reading "
                     "2 B/weight; its Y equals the fused 128x128 rung's Y bit for bit"}
 
@@ -625,10 +733,12 @@ def int8_arm(gemms, wl, lib, sp, timer, args) -> dict:
                         call=functools.partial(lib.qgemm_i8_quantize, ptr(g["x"]), ptr(xq), ptr(sx), M, K, dt, sp),
                         bytes=2.0 * M * K + qg.i8_xq_bytes(M, K) + 4.0 * M)
         xq, sx = quant[g["src"]]
+        nws = qg.i8_workspace_bytes(g["fmt"], -1, M, N, K)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
         # rw and sw are the same for every copy of the weights
         calls = [functools.partial(lib.qgemm_i8_gemm, f, -1, ptr(xq), ptr(sx), ptr(w), ptr(rw), ptr(sw), ptr(g["y"]),
-                                   M, N, K, grp, zp, dt, sp) for w in g["pool"]]
-        arm.append(dict(g=g, prep=prep, calls=calls, turn=0, rw=rw, sw=sw,
+                                   M, N, K, grp, zp, dt, ptr(ws), nws, sp) for w in g["pool"]]
+        arm.append(dict(g=g, prep=prep, calls=calls, turn=0, rw=rw, sw=sw, ws=ws,
                         rung=qg.i8_select_rung(g["fmt"], M, N, K)["name"]))
 
     def run(a, which):
@@ -717,11 +827,11 @@ def read_ceiling(pool, reps: int = 30) -> float:
     for blocks in (1024, 2048, 4096):
         out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
         for i in range(3):
-            qg.probe_read(pool[i % len(pool)], out, blocks)
+            probe.read(pool[i % len(pool)], out, blocks)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(reps):
-            qg.probe_read(pool[i % len(pool)], out, blocks)
+            probe.read(pool[i % len(pool)], out, blocks)
         e1.record(stream)
         torch.cuda.synchronize()
         best = max(best, pool[0].numel() * pool[0].element_size() / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9)
@@ -743,47 +853,86 @@ def copy_calibration(nbytes: int) -> int:
     return 0
 
 
-def cpu_baseline(gemms, target_s: float, xf_layout: bool = False) -> dict:
-    """The oracle as it stands: full dequant of every weight of the step plus
-    the fp64 GEMM on a few rows of each linear, extrapolated linearly in M
-    (rows are independent), reported in the metric's unit; with the
-    fragment-major layout also the oracle's copy of each distinct input."""
+def _oracle_leg(items, rows_cap, target_s):
+    """Time the oracle on `items` (dicts with fmt, enc, N, K, M, dt, X): the
+    full dequant of every weight, then the fp64 GEMM of the first r and 2r
+    rows of each (r grown by 4x until r >= 8 and the 2r run takes about
+    target_s / 4, or 2r reaches all rows).  Rows are independent and cost the same, so the
+    GEMM time is linear in the rows plus a fixed part (the oracle's
+    transposed copy of W): the two runs give both, and the GEMM time of all
+    rows follows.  Returns (unpack seconds, GEMM seconds for all rows, r)."""
     import oracle
 
-    t_deq = 0.0
-    Ws = []
-    for g in gemms:
+    t0 = time.perf_counter()
+    Ws = [oracle.dequant(g["fmt"], g["enc"], g["N"], g["K"], g["dt"]) for g in items]
+    t_unpack = time.perf_counter() - t0
+
+    def run(rows):
         t0 = time.perf_counter()
-        Ws.append(oracle.dequant(g["fmt"], g["enc"], g["N"], g["K"], g["dt"]))
-        if xf_layout and g["prep"] is not None:
-            oracle.fragment_major(g["X"])
-        t_deq += time.perf_counter() - t0
-    # grow the row sample until the GEMM part takes about target_s - t_deq
-    # seconds (or covers every row); a row costs the same in every position
-    rows, t_gemm = 1, 0.0
-    Mmin = min(g["M"] for g in gemms)
+        for g, W in zip(items, Ws):
+            oracle.gemm(g["X"][:min(rows, g["M"])], W, g["dt"], want_bound=False)
+        return time.perf_counter() - t0
+
+    Mmin = min(g["M"] for g in items)
+    r = 1
     while True:
-        t0 = time.perf_counter()
-        for g, W in zip(gemms, Ws):
-            oracle.gemm(g["X"][:rows], W, g["dt"], want_bound=False)
-        t_gemm = time.perf_counter() - t0
-        if rows >= Mmin or t_deq + t_gemm >= 0.5 * target_s:
+        t2 = run(min(2 * r, Mmin))
+        if 2 * r >= min(Mmin, rows_cap) or (t2 >= target_s / 4 and r >= 8):
             break
-        rows = min(Mmin, rows * 4)
-    t_gemm, full = 0.0, t_deq
-    for g, W in zip(gemms, Ws):
-        t0 = time.perf_counter()
-        oracle.gemm(g["X"][:rows], W, g["dt"], want_bound=False)
-        dt = time.perf_counter() - t0
-        t_gemm += dt
-        full += dt * g["M"] / rows
+        r *= 4
+    if 2 * r >= Mmin and all(g["M"] == Mmin for g in items):
+        return t_unpack, run(Mmin), Mmin  # every row timed
+    t1 = run(r)
+    per_row = max(t2 - t1, 0.0) / r
+    fixed = max(t1 - per_row * r, 0.0)
+    # (items share a row count or the smallest bounds it; each item's rows beyond it cost per_row / len(items) on average)
+    total = fixed + sum(per_row / len(items) * g["M"] for g in items)
+    return t_unpack, total, r
+
+
+def cpu_baseline(gemms, target_s: float, xf_layout: bool = False) -> dict:
+    """The oracle as it stands, on the host's cores: the step's weights
+    unpacked in full and the fp64 GEMM of a row sample extrapolated to all
+    rows (reported in the metric's unit, unpack and GEMM also apart), and the
+    single Q4_K GEMM workloads (16x1024x512 and the FFN up projection at
+    M = 512) on all cores and on one."""
+    import oracle
+
+    cores = oracle.num_threads()
     flops = sum(g["flops"] for g in gemms)
-    return {"value": round(flops / full / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"full dequant of all {len(gemms)} weights{' and layout copies of the inputs' if xf_layout else ''} "
-                  f"({t_deq:.2f} s) + fp64 GEMM of the first {rows} "
-                      f"rows of each linear ({t_gemm:.2f} s), extrapolated linearly to all rows "
-                      f"(estimated {full:.1f} s per step)"}
+    t_copy = 0.0
+    if xf_layout:
+        t0 = time.perf_counter()
+        for g in gemms:
+            if g["prep"] is not None:
+                oracle.fragment_major(g["X"])
+        t_copy = time.perf_counter() - t0
+    unpack, gemm_s, rows = _oracle_leg(gemms, 10 ** 9, target_s)
+    full = unpack + gemm_s + t_copy
+    out = {"value": round(flops / full / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "nproc": os.cpu_count(),
+           "unpack_s": round(unpack, 3), "gemm_s_extrapolated": round(gemm_s, 3), "layout_copy_s": round(t_copy, 3),
+           "sample": f"full dequant of all {len(gemms)} weights ({unpack:.2f} s) + fp64 GEMM of the first {rows} rows "
+                     f"of each linear, extrapolated linearly to all rows ({gemm_s:.1f} s)"
+                     f"{' + the oracle layout copies of the inputs' if xf_layout else ''}; {cores} OpenMP threads"}
+    try:
+        configs = {}
+        for name in ("q4k_small", "q4k_ffn_up_m512"):
+            X, _fields, enc = synth.workload_inputs(name, 0)
+            _, fmt, M, K, N, dt, _, _ = synth.WORKLOADS[name]["gemms"][0]
+            item = dict(fmt=fmt, enc=enc, N=N, K=K, M=M, dt=dt, X=X)
+            leg = {}
+            for threads in (cores, 1):
+                oracle.set_num_threads(threads)
+                u, gs, r = _oracle_leg([item], M, target_s / 6)
+                leg["all_cores" if threads == cores else "one_core"] = {
+                    "unpack_s": round(u, 4), "gemm_s_extrapolated": round(gs, 4), "rows_timed": r,
+                    "gemm_gflops": round(2.0 * M * N * K / gs / 1e9, 3)}
+            configs[name] = dict(shape=f"{fmt} M={M} K={K} N={N}", **leg)
+        out["configs"] = configs
+    finally:
+        oracle.set_num_threads(cores)
+    return out
 
 
 if __name__ == "__main__":

@@ -7,28 +7,29 @@
  * (4-bit codes with a group-wise fp16 scale and 4-bit zero-point).  The
  * kernels read every packed weight byte from HBM once per output tile,
  * unpack it in registers and feed it to fp16/bf16 MFMA with fp32
- * accumulation; no dequantized copy of W is ever written to memory (the
- * dequant-scratch post, "The two passes hiding inside one matmul": the fused
- * form moves 0.5625 bytes per Q4_K weight instead of 4.5625).
+ * accumulation; no dequantized copy of W is ever written to memory.
+ *
+ * The pages cited below, by the short names used in this file:
+ *   the batched-prefill post  "How ZINC's RDNA4 batched prefill went from 42
+ *                             to 208 tok/s" (ZINC blog)
+ *   the W4A16 PR              "[ROCm][Perf] W4A16: packed fp16 prefill
+ *                             dequant" (vLLM pull request 55711)
+ *   the delta-net page        "Delta-Net: llama.cpp vs ZINC Analysis" (ZINC docs)
+ *   the dequant-scratch post  "The dequant scratch round-trip is ZINC's last
+ *                             RDNA4 prefill tax" (ZINC blog)
+ *   the sparkinfer PR         sparkinfer pull request 511 (chunk-parallel GDN
+ *                             scan, int8 prefill GEMM, skinny GEMM)
+ * The dequant-scratch post, "The two passes hiding inside one matmul", is the
+ * method: the fused form moves 0.5625 bytes per Q4_K weight instead of 4.5625.
  *
  * Conventions for every entry point
  *   - Plain pointers and sizes only.  Device pointers must come from the HIP
  *     allocator of the current device; host pointers are ordinary memory.
- *     The caller owns every buffer.  The library never synchronises the
- *     stream and allocates no device memory, with one exception: the rungs
- *     that split K across workgroups (mfma32-64x64-sk, i8-64x64-sk) keep a
- *     workspace for their partial sums (fp32, int32) per (device, stream),
- *     shared by both rungs, taken in stream order
- *     from the device's default memory pool (hipMallocAsync) on first use,
- *     replaced in stream order by a larger one when a call needs more
- *     (S*M*N*4 bytes rounded up to whole MiB, S <= 8 slices) and held until
- *     the process ends; a lock serialises its bookkeeping and the two
- *     launches of such a call.  While the stream is being captured into a
- *     HIP graph nothing is taken or returned: a call that would need a
- *     larger workspace then fails with QGEMM_ERR_HIP before launching, so
- *     make one call of the same or larger size on that stream before the
- *     capture.  Calls are re-entrant; calls on different
- *     streams never share a workspace.
+ *     The caller owns every buffer, including the workspace of the rungs that
+ *     split K across workgroups.  The library never synchronises the stream,
+ *     never allocates device memory and keeps no mutable global state, so
+ *     every call is re-entrant; calls that share a workspace buffer must be
+ *     ordered (one stream), as for any buffer both write.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     GEMM and dequant calls are asynchronous on that stream.
  *   - dtype: QGEMM_F16 or QGEMM_BF16.  X and Y have that type; the weights are
@@ -36,22 +37,25 @@
  *   - X is row-major [M][K] contiguous, Y is row-major [M][N] contiguous.
  *     X, Y and Wpacked must be 16-byte aligned; Y must not alias X or W.
  *   - Return value: QGEMM_OK (0) or a negative status.  Argument errors are
- *     found before any launch and leave Y untouched; a forced rung whose
- *     grid would not fit one launch (a direct rung with more than 65535 row
- *     groups of 16 to 64 rows, or more than 2^31-1 streaming tiles) is
- *     QGEMM_ERR_SHAPE, and the M-ladder never picks one.  A failed launch
- *     returns QGEMM_ERR_HIP.  Faults inside a kernel surface at the caller's next
- *     synchronisation, as with any HIP launch.  An unsupported format or
- *     dtype is an error, never a silent fallback.
+ *     found before any launch and leave Y untouched; a shape whose grid would
+ *     not fit one launch (more than 2^31-1 workgroups or 2^32-1 threads along
+ *     x, or 65535 row groups of a direct rung along y) is QGEMM_ERR_SHAPE,
+ *     and the M-ladder never picks a rung it cannot launch.  A failed launch
+ *     returns QGEMM_ERR_HIP.  Faults inside a kernel surface at the caller's
+ *     next synchronisation, as with any HIP launch.  An unsupported format or
+ *     dtype is an error, never a silent fallback (the batched-prefill post,
+ *     "Bug 2: Q6_K had a gate but no dispatcher").
  *
  * Unpacked weight values (bit-exact contract)
  *   Q4_K : w = RN_t( d*sc*q - dmin*m )      (sc, m: 6-bit; q: 4-bit)
  *   Q6_K : w = RN_t( d*s*(q - 32) )         (s: int8 per 16; q: 6-bit)
  *   W4A16: w = RN_t( s*(q - zp) )           (zp = 8 when has_zp == 0)
  *   RN_t is one round-to-nearest-even of the exact value into fp16/bf16 (the
- *   W4A16 PR, section 1: the subtraction is exact and the multiply that
- *   follows rounds once).  The products are accumulated in fp32; the order
- *   of that accumulation is unspecified (it depends on the rung).
+ *   W4A16 PR, "1. Packed fp16 dequant": the subtraction is exact and the
+ *   multiply that follows rounds once; the k-quants' factor*q - bias is the
+ *   batched-prefill post's, "The fix: K-parallel batched DMMV").  The
+ *   products are accumulated in fp32; the order of that accumulation is
+ *   unspecified (it depends on the rung; the W4A16 PR, "Model evaluation").
  */
 #ifndef QGEMM_H
 #define QGEMM_H
@@ -74,7 +78,10 @@ extern "C" {
 #define QGEMM_ERR_HIP (-7)    /* the HIP launch failed                       */
 #define QGEMM_ERR_INPUT (-8)  /* malformed input data (e.g. code above 15)   */
 
-/* Human-readable text for a status code (static storage, never NULL). */
+/* Human-readable text for a status code (static storage, never NULL).  Every
+ * failure names itself instead of degrading to another path (the
+ * batched-prefill post, "Bug 2: Q6_K had a gate but no dispatcher": an
+ * unsupported quant type surfaced as an error, not as a wrong answer). */
 const char *qgemm_status_str(int status);
 
 /* ---- enumerations -------------------------------------------------------- */
@@ -84,6 +91,11 @@ const char *qgemm_status_str(int status);
 #define QGEMM_FMT_Q4K 0
 #define QGEMM_FMT_Q6K 1
 #define QGEMM_FMT_W4A16 2
+
+/* activation layouts (qgemm_workspace_bytes): row-major X, or the
+ * fragment-major copy of qgemm_x_to_xf */
+#define QGEMM_X_ROW 0
+#define QGEMM_X_FRAG 1
 
 /* ---- packed layout (what the packers write and the kernels read) --------
  *
@@ -96,7 +108,8 @@ const char *qgemm_status_str(int status);
  * "Pair order" of a 16-byte code run (32 codes, k = k0 .. k0+31): 32-bit word
  * i holds codes k0+8i .. k0+8i+7; code k0+8i+2p sits at bits [4p, 4p+4) and
  * code k0+8i+2p+1 at bits [16+4p, 20+4p), p = 0..3 (the ExLlama shuffle of
- * the W4A16 PR, section 1: one mask yields both halves of an fp16 pair).
+ * the W4A16 PR, "1. Packed fp16 dequant": one mask yields both halves of an
+ * fp16 pair).
  *
  * Q4_K: one 2304-byte record per (panel p, super-block b), record index
  *   p*(K/256) + b.  Bytes [0,256): the 16 columns' block headers (fp16 d,
@@ -118,25 +131,36 @@ const char *qgemm_status_str(int status);
  */
 
 /* ---- host-side packers (host memory in, host memory out) -----------------
+ * Run once per weight at load time, off the GEMM path (the W4A16 PR repacks
+ * at load, "Duplicate-work check"; the bytes per weight are the
+ * dequant-scratch post's 0.5625 for Q4_K, "The two passes hiding inside one
+ * matmul").
  * blocks: [N][K/256] GGUF-style blocks, column n's blocks contiguous along K
  * (Q4_K: 144 B = fp16 d, fp16 dmin, 12 B scales/mins, 128 B codes; Q6_K:
  * 210 B = 128 B ql, 64 B qh, 16 B int8 scales, fp16 d).  K % 256 == 0.
  * *_packed_bytes returns 0 for an illegal shape.  pack returns
- * QGEMM_ERR_SIZE when out_bytes is smaller than *_packed_bytes.  unpack is
- * the exact inverse (for tests and for exporting packed weights). */
+ * QGEMM_ERR_SIZE when out_bytes is smaller than *_packed_bytes and
+ * QGEMM_ERR_NULL for a NULL buffer.  unpack is the exact inverse (for tests
+ * and for exporting packed weights); pack and unpack are pure byte shuffles
+ * and never touch a value. */
 size_t qgemm_q4k_packed_bytes(int64_t N, int64_t K);
 int qgemm_q4k_pack(const void *blocks, int64_t N, int64_t K, void *out, size_t out_bytes);
 int qgemm_q4k_unpack(const void *packed, int64_t N, int64_t K, void *blocks, size_t blocks_bytes);
 
+/* Q6_K: the format of ffn_down and attn_v in a Q4_K_M checkpoint (the
+ * batched-prefill post, "Bug 2: Q6_K had a gate but no dispatcher"); same
+ * conventions as the Q4_K packer above. */
 size_t qgemm_q6k_packed_bytes(int64_t N, int64_t K);
 int qgemm_q6k_pack(const void *blocks, int64_t N, int64_t K, void *out, size_t out_bytes);
 int qgemm_q6k_unpack(const void *packed, int64_t N, int64_t K, void *blocks, size_t blocks_bytes);
 
-/* W4A16 (GPTQ-style, the W4A16 PR, section 1): codes [N][K], one 4-bit code
- * (0..15) per byte; scales [K/group][N] fp16 bits; zeros [K/group][N]
- * (0..15) or NULL for the symmetric variant (zero-point 8, and then no
- * zero-point bytes are stored).  K % 128 == 0, group a power of two of at
- * least 32, K % group == 0.  Codes or zeros above 15 give QGEMM_ERR_INPUT. */
+/* W4A16 (GPTQ-style, the W4A16 PR, "1. Packed fp16 dequant"): codes [N][K],
+ * one 4-bit code (0..15) per byte; scales [K/group][N] fp16 bits; zeros
+ * [K/group][N] (0..15) or NULL for the symmetric variant (zero-point 8, and
+ * then no zero-point bytes are stored).  K % 128 == 0, group a power of two
+ * of at least 32, K % group == 0 (a 32-wide run never straddles a group: the
+ * W4A16 PR, "2. dtype-aware gfx1151 tile selection").  Codes or zeros above
+ * 15 give QGEMM_ERR_INPUT. */
 size_t qgemm_w4a16_packed_bytes(int64_t N, int64_t K, int64_t group_size, int has_zp);
 int qgemm_w4a16_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, int64_t N, int64_t K,
                      int64_t group_size, void *out, size_t out_bytes);
@@ -145,48 +169,71 @@ int qgemm_w4a16_unpack(const void *packed, int64_t N, int64_t K, int64_t group_s
 
 /* ---- fused-dequant GEMMs (device memory, asynchronous on `stream`) ------- */
 
-/* Q4_K weights (the batched-prefill post's Q4_K kpar path; the dequant-scratch
- * post's fused GEMM).  K % 256 == 0, M >= 0 (M == 0 is a no-op), N >= 1. */
+/* Q4_K weights (the dequant-scratch post, "What removing it was worth": the
+ * Q4_K dequant fused into the matrix-core GEMM; the batched-prefill post,
+ * "The fix: K-parallel batched DMMV").  K % 256 == 0, M >= 0 (M == 0 is a
+ * no-op), N >= 1.  Row-major X; the rung comes from the row-major M-ladder,
+ * which never picks a rung that needs a workspace. */
 int qgemm_q4k(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N, int64_t K, int dtype,
               void *stream);
 
-/* Q6_K weights (the batched-prefill post, "Bug 2": ffn_down / attn_v of a
- * Q4_K_M checkpoint).  Same preconditions as qgemm_q4k. */
+/* Q6_K weights (the batched-prefill post, "Bug 2: Q6_K had a gate but no
+ * dispatcher": ffn_down / attn_v of a Q4_K_M checkpoint).  Same
+ * preconditions as qgemm_q4k. */
 int qgemm_q6k(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N, int64_t K, int dtype,
               void *stream);
 
-/* W4A16 weights (the W4A16 PR, sections 1 and 2).  K % 128 == 0,
- * group_size a power of two >= 32, K % group_size == 0; has_zp selects the asymmetric
- * (stored zero-points) or symmetric (zero-point 8) variant and must match
- * the packing. */
+/* W4A16 weights (the W4A16 PR, sections "1. Packed fp16 dequant" and "2.
+ * dtype-aware gfx1151 tile selection").  K % 128 == 0, group_size a power of
+ * two >= 32, K % group_size == 0; has_zp selects the asymmetric (stored
+ * zero-points) or symmetric (zero-point 8) variant and must match the
+ * packing. */
 int qgemm_w4a16(const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size,
                 int has_zp, int dtype, void *stream);
 
 /* ---- tile selection and forced rungs (tests and benchmarks) -------------
- * The M-ladder (the W4A16 PR, section 2: a tile per M bucket and dtype, with
- * a K block that never straddles a quantization group) maps (format, M, N,
- * K, dtype) to a rung.  qgemm_select_rung writes 8 integers:
+ * The M-ladder (the W4A16 PR, "2. dtype-aware gfx1151 tile selection": a
+ * tile per M bucket and dtype, with a K block that never straddles a
+ * quantization group) maps (format, M, N, K, dtype) to a rung.
+ * qgemm_select_rung writes 8 integers:
  *   [0] rung id  [1] rows per tile  [2] columns per tile  [3] K per step
  *   [4] waves per workgroup  [5] K-split ways (inside a workgroup, times the
  *       K slices across workgroups for mfma32-64x64-sk)
  *   [6] output tiles along N  [7] output tiles along M
- * and returns QGEMM_OK, or an error for an illegal shape. */
+ * and returns QGEMM_OK, or an error for an illegal shape.  num_rungs and
+ * rung_name (NULL for an unknown rung) name the rungs; rung_info fills the
+ * same integers for a given rung. */
 int qgemm_num_rungs(void);
-const char *qgemm_rung_name(int rung); /* NULL for an unknown rung */
+const char *qgemm_rung_name(int rung);
 int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
 int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
 
-/* Same as the format entry points, with the rung forced (rung = -1 selects
- * as qgemm_q4k/q6k/w4a16 do).  group_size/has_zp are ignored for k-quants.
+/* Workspace of the rung that splits K across workgroups (mfma32-64x64-sk:
+ * the batched-prefill post's K-parallel row reduction, "The fix: K-parallel
+ * batched DMMV", carried across workgroups with one reduction at the end):
+ * the bytes a qgemm_gemm_rung (layout QGEMM_X_ROW) or qgemm_gemm_xf
+ * (QGEMM_X_FRAG) call with these arguments needs, S*M*N*4 rounded so that
+ * each of the S <= 8 slices of fp32 partial sums starts 16-byte aligned; 0
+ * when the rung (rung = -1: the ladder's choice for that layout) needs none,
+ * for M = 0, or for illegal arguments.  For W4A16 the group size does not
+ * change the answer. */
+size_t qgemm_workspace_bytes(int format, int rung, int layout, int64_t M, int64_t N, int64_t K, int dtype);
+
+/* The format entry points with the rung forced (rung = -1 selects as
+ * qgemm_q4k/q6k/w4a16 do; the W4A16 PR, "2. dtype-aware gfx1151 tile
+ * selection").  group_size/has_zp are ignored for k-quants.
  * mfma32-64x64-sk splits K into S slices across workgroups (S = 1..8, as
  * many as keep the grid within two workgroups per CU and each of a slice's
  * four K groups at least four whole 128-wide chunks), each writing fp32
- * partial sums of its 64x64 tiles; a second launch adds the S slices in
- * slice order and rounds once into Y, so Y is deterministic and independent
- * of the layout of X, but its fp32 summation order differs from the other
- * rungs'.  Its workspace failing to allocate returns QGEMM_ERR_HIP. */
+ * partial sums of its 64x64 tiles to `workspace` (device, 16-byte aligned,
+ * caller-owned, at least qgemm_workspace_bytes); a second launch adds the S
+ * slices in slice order and rounds once into Y, so Y is deterministic, but
+ * its fp32 summation order differs from the other rungs'.  Such a call with
+ * workspace_bytes below that size (NULL included) returns QGEMM_ERR_SIZE
+ * before any launch; the other rungs ignore both workspace arguments. */
 int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N,
-                    int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+                    int64_t K, int64_t group_size, int has_zp, int dtype, void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /* ---- fragment-major activations ---------------------------------------------
  * A second layout of X, made for the MFMA kernels: 32-row blocks one after
@@ -196,11 +243,10 @@ int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, vo
  *     ((m/32 * K/128 + k/128) * 8 + (k/16)%8) * 512 + ((k/8)%2 * 32 + m%32) * 8 + k%8
  * and rows M .. 32*ceil(M/32)-1 of the last block hold zeros.  One
  * activation operand of a 32x32x16 MFMA (32 rows x 16 k) is then 1 KB of
- * contiguous memory instead of 32 separate 32-byte pieces of rows K apart;
- * the streaming kernels spend a fifth to a third of their time refilling L1
- * with the row-major pieces.  The layout is this library's own (the pages
- * store activations row-major); it changes where X is read, not what is
- * computed.
+ * contiguous memory instead of 32 separate 32-byte pieces of rows K apart:
+ * the layout lesson of the delta-net page ("Gap #2: State Layout": one cache
+ * line per read instead of 32).  The layout is this library's own; it
+ * changes where X is read, not what is computed.
  *
  * qgemm_xf_bytes: bytes of the fragment-major copy of an M x K matrix
  *   (2 * K * 32*ceil(M/32)); 0 for M < 0, K not a positive multiple of 128,
@@ -211,23 +257,27 @@ int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, vo
  *   overlapping X).  One launch on `stream`; M = 0 is a no-op.  Errors:
  *   QGEMM_ERR_SHAPE, _NULL, _ALIGN, _HIP.
  * qgemm_gemm_xf: qgemm_gemm_rung with X given in the fragment-major layout
- *   (M and K are the logical sizes).  For the same rung, Y is bit-identical
- *   to qgemm_gemm_rung's on the row-major X: the kernels and their
- *   accumulation order are the same, only the activation addresses differ.
- *   rung = -1 selects from the ladder tuned for this layout
- *   (qgemm_select_rung_xf); errors as qgemm_gemm_rung. */
+ *   (M and K are the logical sizes), workspace as there.  For the same rung,
+ *   Y is bit-identical to qgemm_gemm_rung's on the row-major X: the kernels
+ *   and their accumulation order are the same, only the activation addresses
+ *   differ.  rung = -1 selects from the ladder tuned for this layout
+ *   (qgemm_select_rung_xf), which may pick mfma32-64x64-sk: size the
+ *   workspace with qgemm_workspace_bytes(..., QGEMM_X_FRAG, ...). */
 size_t qgemm_xf_bytes(int64_t M, int64_t K);
 int qgemm_x_to_xf(const void *X, void *Xf, int64_t M, int64_t K, void *stream);
 int qgemm_gemm_xf(int format, int rung, const void *Xf, const void *Wpacked, void *Y, int64_t M, int64_t N,
-                  int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+                  int64_t K, int64_t group_size, int has_zp, int dtype, void *workspace, size_t workspace_bytes,
+                  void *stream);
 int qgemm_select_rung_xf(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
 
 /* ---- logical dequant --------------------------------------------------------
  * Writes the unpacked weights as logical Wout[K][N] (row-major, dtype
  * elements, device, caller-owned) with the same device unpack code the
- * GEMMs use.  The fused GEMMs never call it; it exists to check the unpack
- * bit for bit in the plain W[K][N] order (the staged arm, qgemm_staged
- * below, writes its scratch in the streaming kernel's order instead). */
+ * GEMMs use (the sparkinfer PR, "Proof of speedup": the dequant is checked
+ * bit for bit, with an FNV-1a digest, against the reference values).  The
+ * fused GEMMs never call it; it exists to check the unpack bit for bit in
+ * the plain W[K][N] order.  Errors as qgemm_w4a16 (group_size ignored for
+ * the k-quants). */
 int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
                   int dtype, void *stream);
 
@@ -237,50 +287,51 @@ int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_
  * holds the routed token rows grouped by expert: rows offsets[e] ..
  * offsets[e+1]-1 use expert e, whose packed weights (the layout of the
  * format's packer, N x K) start at Wpacked + e * (packed bytes of one
- * expert); Y [T][N] receives their products in the same rows.  `offsets`
- * (E+1 int32, 4-byte aligned) is DEVICE memory, read by the kernel, so the
- * caller needs no host copy of the counts; it must be non-decreasing with
- * offsets[0] = 0 and offsets[E] = T.  The kernel clamps every offset into
- * [0, T] and to at least the previous one, so any contents stay inside X, Y
- * and W (bad offsets only give wrong rows).  Rows outside [offsets[0],
- * offsets[E]) are not written.  One launch on `stream`: with more than 32
- * rows per expert on average (ceil(T/E)) and K of at least 16 chunks of 128,
- * 64x64 streaming tiles of one expert per workgroup, else the direct kernel
- * with 16-row groups; results as qgemm_gemm_rung for each expert.  Errors
- * as qgemm_w4a16 (group_size
- * ignored for the k-quants), plus QGEMM_ERR_SHAPE for E < 1 or a grid
- * beyond ceil(T/16) + E = 65535, QGEMM_ERR_ALIGN when one expert's packed
- * size is not a multiple of 16 bytes; T = 0 is a no-op. */
+ * expert), so Wpacked holds E times the packed bytes; Y [T][N] receives
+ * their products in the same rows.  `offsets` (E+1 int32, 4-byte aligned)
+ * is DEVICE memory, read by the kernel, so the caller needs no host copy of
+ * the counts; it must be non-decreasing with offsets[0] = 0 and offsets[E] =
+ * T.  The kernel clamps every offset into [0, T] and to at least the
+ * previous one, so any contents stay inside X, Y and W (bad offsets only
+ * give wrong rows).  Rows outside [offsets[0], offsets[E]) are not written.
+ * One launch on `stream`: with more than 32 rows per expert on average
+ * (ceil(T/E)) and K of at least 16 chunks of 128, 64x64 streaming tiles of
+ * one expert per workgroup, else the direct kernel with 16-row groups;
+ * results as qgemm_gemm_rung for each expert.  Errors as qgemm_w4a16
+ * (group_size ignored for the k-quants), plus QGEMM_ERR_SHAPE for E < 1 or a
+ * grid beyond ceil(T/16) + E = 65535, QGEMM_ERR_ALIGN when one expert's
+ * packed size is not a multiple of 16 bytes; T = 0 is a no-op. */
 int qgemm_grouped(int format, const void *X, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E, int64_t T,
                   int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
 
-/* The staged arm (the dequant-scratch post's "two passes": unpack to a
- * 16-bit scratch, then a GEMM that reads it), kept beside the fused path to
- * measure what fusing saves on this GPU.  Step one unpacks every weight of
- * Wpacked with the fused path's unpack into `scratch` (device, 16-byte
- * aligned, at least qgemm_staged_scratch_bytes(N, K) bytes, caller-owned;
- * 2 bytes per weight, N padded to whole panels of 16, in the order the
- * streaming kernel consumes: per (panel, 128-wide K chunk) 4 KB laid out
- * [word 0..3][run 16g+col][16 bytes], word i of run g of column col holding
- * k = 128c + 32g + 8i .. +7 of that column, two weights per 32-bit word, the
- * lower k in the low half).  Step two is the 128x128 streaming kernel of the
- * fused path with its unpack replaced by loads of those words, so Y equals
- * the fused `mfma32-128x128` rung's Y bit for bit.  Both launches go on
- * `stream`.  Arguments and errors as qgemm_gemm_rung (group_size ignored for
- * the k-quants), plus QGEMM_ERR_SIZE when scratch_bytes is too small and
- * QGEMM_ERR_NULL when scratch is NULL.  M = 0 still fills the scratch.
+/* The staged arm (the dequant-scratch post, "The two passes hiding inside
+ * one matmul": unpack to a 16-bit scratch, then a GEMM that reads it), kept
+ * beside the fused path to measure what fusing saves on this GPU.  Step one
+ * unpacks every weight of Wpacked with the fused path's unpack into
+ * `scratch` (device, 16-byte aligned, at least qgemm_staged_scratch_bytes(N,
+ * K) bytes, caller-owned; 2 bytes per weight, N padded to whole panels of
+ * 16, in the order the streaming kernel consumes: per (panel, 128-wide K
+ * chunk) 4 KB laid out [word 0..3][run 16g+col][16 bytes], word i of run g
+ * of column col holding k = 128c + 32g + 8i .. +7 of that column, two
+ * weights per 32-bit word, the lower k in the low half).  Step two is the
+ * 128x128 streaming kernel of the fused path with its unpack replaced by
+ * loads of those words, so Y equals the fused `mfma32-128x128` rung's Y bit
+ * for bit.  Both launches go on `stream`.  Arguments and errors as
+ * qgemm_gemm_rung (group_size ignored for the k-quants), plus
+ * QGEMM_ERR_SIZE when scratch_bytes is too small and QGEMM_ERR_NULL when
+ * scratch is NULL.  M = 0 still fills the scratch.
  * qgemm_staged_scratch_bytes returns 0 for an illegal N or K. */
 size_t qgemm_staged_scratch_bytes(int64_t N, int64_t K);
 int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, size_t scratch_bytes, void *Y, int64_t M,
                  int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
 
 /* ---- int8-activation variant ----------------------------------------------
- * The other operand of the same idea (the prefill post, closing section:
- * activation quantization and weight-dequant fusion keep each operand
- * compressed until the multiply; the batched-prefill PR: a single-pass row
- * quantize feeding an int8-native prefill GEMM, weights dequantized to int8
- * rows).  The pages fix neither the scale granularity nor the rounding; this
- * library's reading, every step defined to the bit:
+ * The other operand of the same idea (the dequant-scratch post, "Where the
+ * gap stands now": activation quantization and weight-dequant fusion keep
+ * each operand compressed until the multiply; the sparkinfer PR, "Summary":
+ * a single-pass row quantize feeding an int8-native prefill GEMM, weights
+ * dequantized to int8 rows).  The pages fix neither the scale granularity
+ * nor the rounding; this library's reading, every step defined to the bit:
  *   weights     w32 = RN_f32(exact weight of the unpack contract above);
  *               per output column n: amax_n = max_k |w32[k][n]|,
  *               r_n = RN_f32(127/amax_n), s_n = RN_f32(amax_n/127);
@@ -308,52 +359,41 @@ int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, 
  *   (r, h) holds row r, k = 32s + 16h .. +15, i.e. code (m, k) at
  *       (m/32)*32*K + (k/32)*1024 + ((k/16)%2)*512 + (m%32)*16 + k%16,
  *   rows M .. 32*ceil(M/32)-1 zero: one 1 KB piece is one int8 MFMA
- *   operand.  X must be finite.  One launch (one workgroup per row, the row
- *   read once); M = 0 is a no-op.  Errors: QGEMM_ERR_SHAPE, _DTYPE, _NULL,
- *   _ALIGN, _HIP.
+ *   operand.  X must be finite.  One launch (one wave per row, four rows per
+ *   workgroup, each row read once); M = 0 is a no-op.  Errors:
+ *   QGEMM_ERR_SHAPE, _DTYPE, _NULL, _ALIGN, _HIP.
  * qgemm_i8_gemm: Y [M][N] (dtype, row-major, 16-byte aligned) from Xq and sx
  *   of qgemm_i8_quantize and Wpacked with rw and sw of qgemm_i8_colscale.
  *   rung -1 picks from this path's own ladder (qgemm_i8_select_rung), else
  *   0 .. qgemm_i8_num_rungs()-1; every rung gives the same bits.  K at most
  *   131072 (int32 sums stay exact).  One launch on `stream` (two for
  *   i8-64x64-sk, which splits K into up to 8 slices across workgroups,
- *   writes each slice's int32 partial sums to the workspace described at
- *   the top of this file and adds them, exactly, in the epilogue launch);
- *   M = 0 is a no-op.  Errors as qgemm_gemm_rung. */
+ *   writes each slice's int32 partial sums to `workspace` (device, 16-byte
+ *   aligned, caller-owned, at least qgemm_i8_workspace_bytes) and adds them,
+ *   exactly, in the epilogue launch; with a smaller workspace, NULL
+ *   included, it returns QGEMM_ERR_SIZE before any launch); M = 0 is a
+ *   no-op.  Errors as qgemm_gemm_rung.
+ * qgemm_i8_workspace_bytes: the workspace such a call needs (rung -1: the
+ *   int8 ladder's choice), 0 when it needs none or the arguments are
+ *   illegal. */
 size_t qgemm_i8_xq_bytes(int64_t M, int64_t K);
 int qgemm_i8_quantize(const void *X, void *Xq, float *sx, int64_t M, int64_t K, int dtype, void *stream);
 int qgemm_i8_colscale(int format, const void *Wpacked, float *rw, float *sw, int64_t N, int64_t K, int64_t group_size,
                       int has_zp, void *stream);
 int qgemm_i8_gemm(int format, int rung, const void *Xq, const float *sx, const void *Wpacked, const float *rw,
                   const float *sw, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype,
-                  void *stream);
-/* The int8 ladder: rung count and names (as qgemm_num_rungs /
- * qgemm_rung_name); rung_info / select_rung fill info8 as qgemm_rung_info
- * (dtype does not enter: every rung computes the same bits). */
+                  void *workspace, size_t workspace_bytes, void *stream);
+size_t qgemm_i8_workspace_bytes(int format, int rung, int64_t M, int64_t N, int64_t K);
+
+/* The int8 ladder (the W4A16 PR, "2. dtype-aware gfx1151 tile selection",
+ * applied to this path's own tiles): rung count and names (as
+ * qgemm_num_rungs / qgemm_rung_name); rung_info / select_rung fill info8 as
+ * qgemm_rung_info (dtype does not enter: every rung computes the same
+ * bits). */
 int qgemm_i8_num_rungs(void);
 const char *qgemm_i8_rung_name(int rung);
 int qgemm_i8_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int32_t *info8);
 int qgemm_i8_select_rung(int format, int64_t M, int64_t N, int64_t K, int32_t *info8);
-
-/* Measurement aid, not part of the GEMM path: runs `blocks` workgroups of
- * 256 threads, each wave issuing `iters` rounds of four independent
- * 32x32x16 MFMAs (fp16 or bf16 by `dtype`) on operands read once from
- * `operands` (device, 16-byte aligned, 32 KiB: 256 threads x 8 vectors of 16
- * bytes), and writes one float per thread to `out` (device, blocks*256
- * floats) so the work stays live.  FLOPs = 2*32*32*16 * 4 * iters * 4 waves
- * * blocks.  Timing it on random operands gives the MFMA rate the chip
- * sustains under its power limit.  Errors: QGEMM_ERR_NULL, _ALIGN, _SHAPE
- * (blocks or iters < 1), _DTYPE, _HIP. */
-int qgemm_probe_mfma(const void *operands, float *out, int blocks, int iters, int dtype, void *stream);
-
-/* Measurement aid, not part of the GEMM path: a plain streaming read of
- * `bytes` (a positive multiple of 16) from `buf` (device, 16-byte aligned) by
- * `blocks` workgroups of 256 threads, 16-byte loads at a grid stride, four in
- * flight per thread; each thread writes one 32-bit word to `out` (device,
- * blocks*256 words) so the loads stay live.  Timed on buffers that miss the
- * Infinity Cache it is the HBM read rate a weight stream can hope for.
- * Errors: QGEMM_ERR_NULL, _ALIGN, _SHAPE, _HIP. */
-int qgemm_probe_read(const void *buf, int64_t bytes, void *out, int blocks, void *stream);
 
 #ifdef __cplusplus
 }

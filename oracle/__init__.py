@@ -65,6 +65,7 @@ def load_library(path: str):
         "qref_gemm_at": (ctypes.c_int, [c_u16p, c_u16p, i64, i64, i64, ctypes.c_int, c_i64p, c_i64p, i64,
                                         c_dp, c_dp]),
         "qref_num_threads": (ctypes.c_int, []),
+        "qref_set_num_threads": (None, [ctypes.c_int]),
         "qref_dequant_q4k_f32": (ctypes.c_int, [c_u8p, i64, i64, c_fp]),
         "qref_dequant_q6k_f32": (ctypes.c_int, [c_u8p, i64, i64, c_fp]),
         "qref_dequant_w4a16_f32": (ctypes.c_int, [c_u8p, c_u16p, c_u8p, i64, i64, i64, c_fp]),
@@ -364,6 +365,11 @@ def fragment_major_i8(Q: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().qref_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on (timing only)."""
+    _load().qref_set_num_threads(int(n))
 
 
 # ---- acceptance rule -------------------------------------------------------

@@ -485,6 +485,17 @@ int qref_num_threads(void)
 #endif
 }
 
+/* The number of OpenMP threads the loops above use from now on (timing only:
+   no result depends on it). */
+void qref_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* 4. fragment-major copy: one element at a time, straight from the formula */
 int qref_fragment_major(const uint16_t *X, int64_t M, int64_t K, uint16_t *out)
 {

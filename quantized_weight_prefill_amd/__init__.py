@@ -17,7 +17,10 @@ Functions keep the C names without the ``qgemm_`` prefix:
 * fragment-major activations: :func:`xf_bytes`, :func:`x_to_xf`,
   :func:`gemm_xf`, :func:`select_rung_xf`;
 * the staged dequant :func:`dequant` and the M-ladder queries
-  :func:`select_rung`, :func:`rung_info`, :func:`rung_name`, :func:`num_rungs`.
+  :func:`select_rung`, :func:`rung_info`, :func:`rung_name`, :func:`num_rungs`;
+* the split rungs' workspace size :func:`workspace_bytes` (the C library
+  never allocates: when a call needs a workspace and none is passed, the
+  binding takes one from torch's allocator for that call).
 """
 from __future__ import annotations
 
@@ -35,6 +38,8 @@ FMT_Q4K = 0
 FMT_Q6K = 1
 FMT_W4A16 = 2
 FORMATS = {"q4k": FMT_Q4K, "q6k": FMT_Q6K, "w4a16": FMT_W4A16}
+X_ROW = 0
+X_FRAG = 1
 
 #: status codes of include/qgemm.h
 STATUS = {0: "QGEMM_OK", -1: "QGEMM_ERR_NULL", -2: "QGEMM_ERR_SHAPE", -3: "QGEMM_ERR_DTYPE",
@@ -75,21 +80,22 @@ SIGNATURES = {
     "qgemm_rung_name": (ctypes.c_char_p, [_INT]),
     "qgemm_select_rung": (_INT, [_INT, _I64, _I64, _I64, _INT, _VP]),
     "qgemm_rung_info": (_INT, [_INT, _INT, _I64, _I64, _I64, _INT, _VP]),
-    "qgemm_gemm_rung": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_gemm_rung": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP, _SZ, _VP]),
+    "qgemm_workspace_bytes": (_SZ, [_INT, _INT, _INT, _I64, _I64, _I64, _INT]),
     "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_grouped": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_staged_scratch_bytes": (_SZ, [_I64, _I64]),
     "qgemm_staged": (_INT, [_INT, _VP, _VP, _VP, _SZ, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
-    "qgemm_probe_mfma": (_INT, [_VP, _VP, _INT, _INT, _INT, _VP]),
-    "qgemm_probe_read": (_INT, [_VP, _I64, _VP, _INT, _VP]),
     "qgemm_xf_bytes": (_SZ, [_I64, _I64]),
     "qgemm_x_to_xf": (_INT, [_VP, _VP, _I64, _I64, _VP]),
-    "qgemm_gemm_xf": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_gemm_xf": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP, _SZ, _VP]),
     "qgemm_select_rung_xf": (_INT, [_INT, _I64, _I64, _I64, _INT, _VP]),
     "qgemm_i8_xq_bytes": (_SZ, [_I64, _I64]),
     "qgemm_i8_quantize": (_INT, [_VP, _VP, _VP, _I64, _I64, _INT, _VP]),
     "qgemm_i8_colscale": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
-    "qgemm_i8_gemm": (_INT, [_INT, _INT, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_i8_gemm": (_INT, [_INT, _INT, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP, _SZ,
+                             _VP]),
+    "qgemm_i8_workspace_bytes": (_SZ, [_INT, _INT, _I64, _I64, _I64]),
     "qgemm_i8_num_rungs": (_INT, []),
     "qgemm_i8_rung_name": (ctypes.c_char_p, [_INT]),
     "qgemm_i8_rung_info": (_INT, [_INT, _INT, _I64, _I64, _I64, _VP]),
@@ -250,15 +256,52 @@ def _out(x, N, out):
     return out
 
 
-def gemm_rung(fmt, rung: int, x, wp, N: int, group: int = 0, has_zp: bool = False, out=None, stream=None):
+def packed_bytes(fmt, N: int, K: int, group: int = 128, has_zp: bool = False) -> int:
+    """Packed bytes of one N x K weight of format ``fmt``."""
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if f == FMT_Q4K:
+        return q4k_packed_bytes(N, K)
+    if f == FMT_Q6K:
+        return q6k_packed_bytes(N, K)
+    return w4a16_packed_bytes(N, K, group, has_zp)
+
+
+def _check_wp(fmt, wp, N: int, K: int, group: int, has_zp: bool, experts: int = 1):
+    need = packed_bytes(fmt, N, K, group if group else 128, has_zp) * experts
+    if need == 0:
+        raise QGemmError("packed_bytes", -2)
+    if wp.numel() * wp.element_size() < need:
+        raise ValueError(f"wp holds {wp.numel() * wp.element_size()} bytes, the packed weight needs {need}")
+
+
+def workspace_bytes(fmt, rung: int, M: int, N: int, K: int, dtype: int = F16, layout: int = X_ROW) -> int:
+    """Bytes of the workspace a GEMM call with these arguments needs (0: none)."""
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    return int(lib().qgemm_workspace_bytes(f, rung, layout, M, N, K, dtype))
+
+
+def _workspace(need: int, workspace, device):
+    """(pointer, bytes) of the caller's workspace, or of one taken from
+    torch's allocator when the call needs one and none was given."""
+    if workspace is None:
+        if need == 0:
+            return None, 0, None
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=device)
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), workspace
+
+
+def gemm_rung(fmt, rung: int, x, wp, N: int, group: int = 0, has_zp: bool = False, out=None, stream=None,
+              workspace=None):
     """Y = X . dequant(W) with the rung forced (rung = -1 selects as the format calls do)."""
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
     if x.dim() != 2:
         raise ValueError("x must be [M, K]")
     M, K = x.shape
+    _check_wp(f, wp, N, K, group, has_zp)
     y = _out(x, N, out)
+    ws, wsb, _keep = _workspace(workspace_bytes(f, rung, M, N, K, _dtype_code(x), X_ROW), workspace, x.device)
     st = lib().qgemm_gemm_rung(f, rung, _dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, group,
-                               int(bool(has_zp)), _dtype_code(x), _stream(stream))
+                               int(bool(has_zp)), _dtype_code(x), ws, wsb, _stream(stream))
     _check("qgemm_gemm_rung", st)
     return y
 
@@ -286,19 +329,21 @@ def x_to_xf(x, out=None, stream=None):
 
 
 def gemm_xf(fmt, xf, wp, M: int, N: int, K: int, group: int = 0, has_zp: bool = False, rung: int = -1, out=None,
-            stream=None):
+            stream=None, workspace=None):
     """Y = X . dequant(W) with X given as its fragment-major copy `xf`
     (from :func:`x_to_xf`); rung -1 selects from the ladder for that layout."""
     torch = _torch()
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
     if xf.numel() < xf_bytes(M, K) // 2:
         raise ValueError("xf is smaller than the fragment-major copy of an M x K matrix")
+    _check_wp(f, wp, N, K, group, has_zp)
     if out is None:
         out = torch.empty((M, N), dtype=xf.dtype, device=xf.device)
     elif out.shape != (M, N) or out.dtype != xf.dtype:
         raise ValueError("out has the wrong shape or dtype")
+    ws, wsb, _keep = _workspace(workspace_bytes(f, rung, M, N, K, _dtype_code(xf), X_FRAG), workspace, xf.device)
     st = lib().qgemm_gemm_xf(f, rung, _dev(xf, "xf"), _dev(wp, "wp"), _dev(out, "out"), M, N, K, group,
-                             int(bool(has_zp)), _dtype_code(xf), _stream(stream))
+                             int(bool(has_zp)), _dtype_code(xf), ws, wsb, _stream(stream))
     _check("qgemm_gemm_xf", st)
     return out
 
@@ -320,6 +365,7 @@ def i8_colscale(fmt, wp, N: int, K: int, group: int = 0, has_zp: bool = False, o
     rw, sw = out
     if rw.numel() < N or sw.numel() < N or rw.dtype != torch.float32 or sw.dtype != torch.float32:
         raise ValueError("colscale outputs must be float32 with N elements")
+    _check_wp(f, wp, N, K, group, has_zp)
     st = lib().qgemm_i8_colscale(f, _dev(wp, "wp"), _dev(rw, "rw"), _dev(sw, "sw"), N, K, group, int(bool(has_zp)),
                                  _stream(stream))
     _check("qgemm_i8_colscale", st)
@@ -347,8 +393,13 @@ def i8_quantize(x, out=None, stream=None):
     return xq, sx
 
 
+def i8_workspace_bytes(fmt, rung: int, M: int, N: int, K: int) -> int:
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    return int(lib().qgemm_i8_workspace_bytes(f, rung, M, N, K))
+
+
 def gemm_i8(fmt, xq, sx, wp, rw, sw, M: int, N: int, K: int, dtype, group: int = 0, has_zp: bool = False,
-            rung: int = -1, out=None, stream=None):
+            rung: int = -1, out=None, stream=None, workspace=None):
     """Y [M, N] (dtype) of the int8 path from i8_quantize's (xq, sx) and
     i8_colscale's (rw, sw) of the packed weight wp."""
     torch = _torch()
@@ -356,12 +407,15 @@ def gemm_i8(fmt, xq, sx, wp, rw, sw, M: int, N: int, K: int, dtype, group: int =
     tdt = dtype if isinstance(dtype, torch.dtype) else (torch.float16 if dtype == F16 else torch.bfloat16)
     if xq.numel() < i8_xq_bytes(M, K) or sx.numel() < M or rw.numel() < N or sw.numel() < N:
         raise ValueError("int8 inputs are smaller than an M x K / N problem needs")
+    _check_wp(f, wp, N, K, group, has_zp)
     if out is None:
         out = torch.empty((M, N), dtype=tdt, device=xq.device)
     elif out.shape != (M, N) or out.dtype != tdt:
         raise ValueError("out has the wrong shape or dtype")
+    ws, wsb, _keep = _workspace(i8_workspace_bytes(f, rung, M, N, K), workspace, xq.device)
     st = lib().qgemm_i8_gemm(f, rung, _dev(xq, "xq"), _dev(sx, "sx"), _dev(wp, "wp"), _dev(rw, "rw"), _dev(sw, "sw"),
-                             _dev(out, "out"), M, N, K, group, int(bool(has_zp)), _dtype_code(out), _stream(stream))
+                             _dev(out, "out"), M, N, K, group, int(bool(has_zp)), _dtype_code(out), ws, wsb,
+                             _stream(stream))
     _check("qgemm_i8_gemm", st)
     return out
 
@@ -396,6 +450,7 @@ def i8_select_rung(fmt, M: int, N: int, K: int) -> dict:
 def q4k(x, wp, N: int, out=None, stream=None):
     """Y[M,N] = X[M,K] . dequant_Q4_K(W)."""
     M, K = x.shape
+    _check_wp(FMT_Q4K, wp, N, K, 0, False)
     y = _out(x, N, out)
     st = lib().qgemm_q4k(_dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, _dtype_code(x), _stream(stream))
     _check("qgemm_q4k", st)
@@ -405,6 +460,7 @@ def q4k(x, wp, N: int, out=None, stream=None):
 def q6k(x, wp, N: int, out=None, stream=None):
     """Y[M,N] = X[M,K] . dequant_Q6_K(W)."""
     M, K = x.shape
+    _check_wp(FMT_Q6K, wp, N, K, 0, False)
     y = _out(x, N, out)
     st = lib().qgemm_q6k(_dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, _dtype_code(x), _stream(stream))
     _check("qgemm_q6k", st)
@@ -414,6 +470,7 @@ def q6k(x, wp, N: int, out=None, stream=None):
 def w4a16(x, wp, N: int, group: int, has_zp: bool, out=None, stream=None):
     """Y[M,N] = X[M,K] . dequant_W4A16(W) (group-wise scale, zero-point or 8)."""
     M, K = x.shape
+    _check_wp(FMT_W4A16, wp, N, K, group, has_zp)
     y = _out(x, N, out)
     st = lib().qgemm_w4a16(_dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), M, N, K, group, int(bool(has_zp)),
                            _dtype_code(x), _stream(stream))
@@ -427,6 +484,7 @@ def dequant(fmt, wp, N: int, K: int, dtype, group: int = 0, has_zp: bool = False
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
     code = F16 if dtype in (F16, torch.float16) else BF16
     tdt = torch.float16 if code == F16 else torch.bfloat16
+    _check_wp(f, wp, N, K, group, has_zp)
     w = torch.empty((K, N), dtype=tdt, device=wp.device)
     st = lib().qgemm_dequant(f, _dev(wp, "wp"), _dev(w, "out"), N, K, group, int(bool(has_zp)), code,
                              _stream(stream))
@@ -434,16 +492,19 @@ def dequant(fmt, wp, N: int, K: int, dtype, group: int = 0, has_zp: bool = False
     return w
 
 
-def grouped(fmt, x, wp, N: int, offsets, E: int, group: int = 0, has_zp: bool = True, out=None, stream=None):
+def grouped(fmt, x, wp, N: int, offsets, E: int, group: int = 0, has_zp: bool = False, out=None, stream=None):
     """Grouped per-expert GEMM: rows offsets[e]..offsets[e+1]-1 of x use
-    expert e's packed weights (experts concatenated in wp); offsets is an
+    expert e's packed weights (E experts concatenated in wp); offsets is an
     int32 device tensor of E+1 entries."""
     torch = _torch()
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if x.dim() != 2:
+        raise ValueError("x must be [T, K]")
     T, K = x.shape
+    _check_wp(f, wp, N, K, group, has_zp, experts=E)
+    y = _out(x, N, out)
     if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.numel() != E + 1:
         raise ValueError("offsets must be an int32 device tensor of E+1 entries")
-    y = out if out is not None else torch.empty((T, N), dtype=x.dtype, device=x.device)
     st = lib().qgemm_grouped(f, _dev(x, "x"), _dev(wp, "wp"), _dev(y, "out"), _dev(offsets, "offsets"), E, T, N, K,
                              group, int(bool(has_zp)), _dtype_code(x), _stream(stream))
     _check("qgemm_grouped", st)
@@ -454,34 +515,23 @@ def staged_scratch_bytes(N: int, K: int) -> int:
     return int(lib().qgemm_staged_scratch_bytes(N, K))
 
 
-def staged(fmt, x, wp, N: int, scratch=None, group: int = 0, has_zp: bool = True, out=None, stream=None):
+def staged(fmt, x, wp, N: int, scratch=None, group: int = 0, has_zp: bool = False, out=None, stream=None):
     """The staged arm: unpack into `scratch` (allocated here when None), then
     the 128x128 streaming GEMM on it.  Returns (y, scratch)."""
     torch = _torch()
     f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
     M, K = x.shape
+    _check_wp(f, wp, N, K, group, has_zp)
     if scratch is None:
         scratch = torch.empty(staged_scratch_bytes(N, K), dtype=torch.uint8, device=x.device)
-    y = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    y = _out(x, N, out)
     st = lib().qgemm_staged(f, _dev(x, "x"), _dev(wp, "wp"), _dev(scratch, "scratch"),
                             scratch.numel() * scratch.element_size(), _dev(y, "out"), M, N, K, group,
                             int(bool(has_zp)), _dtype_code(x), _stream(stream))
     _check("qgemm_staged", st)
     return y, scratch
-
-
-def probe_mfma(operands, out, blocks: int, iters: int, dtype=F16, stream=None):
-    """Launch the MFMA rate probe (a measurement aid; see include/qgemm.h)."""
-    torch = _torch()
-    code = F16 if dtype in (F16, torch.float16) else BF16
-    _check("qgemm_probe_mfma", lib().qgemm_probe_mfma(_dev(operands, "operands"), _dev(out, "out"), blocks, iters, code,
-                                                      _stream(stream)))
-
-
-def probe_read(buf, out, blocks: int, stream=None):
-    """Launch the streaming-read probe over all of `buf` (a measurement aid)."""
-    _check("qgemm_probe_read", lib().qgemm_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(out, "out"),
-                                                      blocks, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,901 @@
+// api.hip -- host side of the fused-dequant prefill GEMM: argument checks,
+// the M-ladder (which rung serves a shape), launch plans, and the C ABI of
+// include/qgemm.h.  No kernels live here; the launch functions of plan.h do.
+// The library holds no device memory and no mutable state: every buffer,
+// the split rungs' workspace included, belongs to the caller.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <cstdio>
+
+#include "plan.h"
+#include "qgemm.h"
+
+namespace qg {
+namespace {
+
+const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
+                                            "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
+                                            "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
+                                            "mfma32-192x96-k2",  "mfma32-192x64-k2",  "mfma32-64x64-sk"};
+
+// A one-dimensional launch of gx workgroups of `threads` threads fits when
+// gx is at most 2^31-1 and the work-items along x at most 2^32-1.
+bool launch_fits(long long gx, long long threads) { return gx >= 0 && gx <= INT32_MAX && gx * threads <= (long long)UINT32_MAX; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Waves splitting K inside one direct-kernel workgroup: enough waves in the
+// whole grid to keep every CU streaming (about 2048), at least two chunks
+// per wave, at most eight waves.  For decode-adjacent M (a pure weight
+// stream) a wave keeps at least eight chunks once the grid holds 512 waves:
+// with one chunk in flight ahead, shorter K ranges leave the stream idle
+// while each wave starts and drains (measured at M = 1..16).
+int pick_kw(long long groups, int nch, bool stream)
+{
+    int kw = 1;
+    while (kw < 8 && groups * kw < 2048 && nch / (2 * kw) >= ((stream && groups * kw >= 512) ? 8 : 2)) kw *= 2;
+    return kw;
+}
+
+// QGEMM_OK, QGEMM_ERR_FORMAT for an unknown rung, or QGEMM_ERR_SHAPE when
+// the grid would exceed what one launch can address (2^31-1 workgroups and
+// 2^32-1 work-items along x, 65535 workgroups along y).
+int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
+{
+    const long long np = (N + 15) / 16;
+    const int nch = (int)(K / kChunk);
+    pl = Plan{};
+    pl.rung = rung;
+    switch (rung) {
+    case RUNG_SMALL_M:
+    case RUNG_SKINNY_N:
+    case RUNG_WIDE: {
+        if (rung == RUNG_SMALL_M) {
+            pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4;
+            pl.pn = 1;
+        } else if (rung == RUNG_SKINNY_N) {
+            pl.rb = 1;
+            pl.pn = np >= 4 ? 4 : (int)np;
+        } else {  // each weight run unpacked once for up to 48 rows, each activation fragment used by four panels
+            pl.rb = M <= 16 ? 1 : M <= 32 ? 2 : 3;
+            pl.pn = 4;
+        }
+        const long long gx = (np + pl.pn - 1) / pl.pn, gy = (M + 16 * pl.rb - 1) / (16 * pl.rb);
+        if (gy > 65535 || gx > INT32_MAX) return QGEMM_ERR_SHAPE;
+        pl.grid = dim3((unsigned)gx, (unsigned)gy, 1);
+        break;
+    }
+    case RUNG_M16_256:
+    case RUNG_M128:
+    case RUNG_M128_K2:
+    case RUNG_M128N160:
+    case RUNG_M64_K4:
+    case RUNG_M64_SK:
+    case RUNG_M352N96:
+    case RUNG_M192N96_K2:
+    case RUNG_M192N64_K2: {
+        const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2;
+        const bool r192 = rung == RUNG_M192N96_K2 || rung == RUNG_M192N64_K2;
+        const bool r64 = rung == RUNG_M64_K4 || rung == RUNG_M64_SK;
+        pl.rows = rung == RUNG_M16_256 ? 256 : r64 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : (r64 || rung == RUNG_M192N64_K2) ? 64 : n96 ? 96 : 128;
+        pl.kw = ((rung == RUNG_M128_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
+        if (r64) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = rung == RUNG_M16_256 ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11
+                   : r192 ? 6 * pl.kw : 4 * pl.kw;
+        // one-dimensional grid: the kernel renumbers tiles per XCD
+        const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
+        if (!launch_fits(tn * tm, 64 * pl.waves)) return QGEMM_ERR_SHAPE;
+        pl.tiles_n = (int)tn;
+        pl.tiles_m = (int)tm;
+        pl.split = 1;
+        if (rung == RUNG_M64_SK) {
+            // slices across workgroups: double while the grid stays within
+            // two workgroups per CU, the slices divide the chunks evenly
+            // among the in-group K groups and each group keeps four chunks
+            while (pl.split < 8 && tn * tm * 2 * pl.split <= 2 * kCUs && nch % (2 * pl.split * pl.kw) == 0 &&
+                   nch / (2 * pl.split * pl.kw) >= 4)
+                pl.split *= 2;
+        }
+        if (!launch_fits(tn * tm * pl.split, 64 * pl.waves)) return QGEMM_ERR_SHAPE;
+        pl.grid = dim3((unsigned)(tn * tm * pl.split), 1, 1);
+        pl.lds = 0;
+        return QGEMM_OK;
+    }
+    default:
+        return QGEMM_ERR_FORMAT;
+    }
+    pl.rows = 16 * pl.rb;
+    pl.cols = 16 * pl.pn;
+    pl.split = 1;
+    pl.tiles_n = (int)pl.grid.x;
+    pl.tiles_m = (int)pl.grid.y;
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch, M <= 16);
+    pl.waves = pl.kw;
+    pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
+    return launch_fits(pl.grid.x, 64 * pl.kw) ? QGEMM_OK : QGEMM_ERR_SHAPE;
+}
+
+// The M-ladder (measured on MI355X; each rung is legal for every shape):
+//  * narrow N (at most four panels): the grid must run over M, so the
+//    direct kernel with all panels per wave (a 128-wide tile would leave most
+//    of the part idle and most of each tile padding);
+//  * decode-adjacent M (at most 64 rows): each weight feeds at most 64 rows
+//    and the kernel is a weight stream; up to 16 rows one panel and all rows
+//    per wave (the most waves streaming, each weight unpacked once), except
+//    over 1536 panels and more and, on row-major activations, at 9..16 rows
+//    over 512 panels and more: four panels and 16 rows per wave; with fewer
+//    than 512 panels up to 64 rows one panel per wave, or on fragment-major
+//    activations over 129..256 panels 64x64 tiles with K split across
+//    workgroups too (split_pays); with many panels: 17..32 rows (17..48 for
+//    Q4_K) four panels and all rows per wave (each activation fragment feeds
+//    four panels), 49..64 rows of Q4_K and 33..64 of W4A16 and Q6_K 64x64
+//    streaming tiles with K split four ways;
+//  * fewer than 128 tiles of 128x128: the split rung where split_pays, else
+//    the direct kernels, 64x64 K-split tiles or (fragment-major) 192x64
+//    K-split tiles, by the round model of mid_m_rung;
+//  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
+//    for 256 rows) when the occupancy model below has it finish no later
+//    than the 128-row tiles;
+//  * at most 256 tiles of 128x128 over K >= 8192: the 128x128 tile on
+//    32x32x16 MFMAs with K split between two wave groups;
+//  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
+//    whichever the occupancy model below finishes first.
+// On fragment-major activations the three-waves-per-SIMD tiles come first
+// where they fit (192x64 and 192x96 with K split over two 6-wave groups,
+// 352x96; the rules are in select_rung), the K-split 128x128 tile serves the
+// other shapes with at most 256 of its tiles, and the 256-row tile also wins
+// whenever it has 512 tiles.
+// Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
+// of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
+// the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
+// runs alone on a CU (one wave per SIMD) counts 1.43 (a constant fitted to
+// the measured times of both widths at M = 300, 658 and 1024).
+double stream_cost(long long M, long long np, int cols)
+{
+    const long long T = ((M + 127) / 128) * ((np + cols / 16 - 1) / (cols / 16));
+    const long long n = (T + kCUs - 1) / kCUs;
+    const double t = (n & 1) ? (double)(n - 1) + 1.43 : (double)n;
+    return t * cols / 128.0;
+}
+
+// Between decode-adjacent M and 128 tiles of 128x128 three rungs compete:
+// one panel and up to 64 rows per wave (direct-small-m), four panels and 48
+// rows per wave (direct-wide) and 64x64 streaming tiles with K split four
+// ways, and on fragment-major activations with an even chunk count a fourth,
+// the 192x64 tile with K split over two 6-wave groups.  Their workgroups run
+// in rounds of one per CU; a round costs a constant per rung, measured on
+// MI355X with Q4_K at K = 4096 (M = 80..384, N = 1024..12288): 8, 15.5, 17
+// and 27 microseconds.  The 48-row direct variant spills for Q6_K and W4A16
+// and is left out for them.  (Q6_K at M = 300..384, N = 4096: 192x64 72-73
+// against 91 us for the 64x64 tiles.)
+// The split rung over few panels (N = 4096) on fragment-major activations:
+// one panel and all rows per wave reads the activations once per panel, the
+// 64x64 tiles split across workgroups read a slice of them.  Measured on
+// MI355X (weights rotating):
+//  * K = 12288 (four slices): Q6_K and W4A16, and every format in bf16,
+//    from 33 rows (Q6_K M = 64 24.2 against 28.1 us; W4A16 M = 48..128
+//    18.5-33.8 against 20.4-38.7; bf16 Q4_K M = 96 33.3 against 42.2 on
+//    direct-wide); fp16 Q4_K at 49..64 only (from 96 rows direct-wide leads,
+//    33.0 against 34.6 us);
+//  * K = 4096 (two slices): 65..128 rows in both dtypes (W4A16 M = 96: 14.2
+//    against 15.2 us fp16, 13.7 against 15.5 bf16), while the two slices'
+//    tiles fit one workgroup per CU (at N = 6144 they lose, 28.3 against
+//    15.8 us).
+// Over at most 128 panels the split grid fills a quarter of the CUs or less
+// and one panel per wave stays ahead (N = 1024, M = 96..128: 8.3-9.4
+// against 12.5-14.7 us).
+bool split_pays(int fmt, int dtype, long long M, long long np, long long K, int xl)
+{
+    const long long nch = K / kChunk, tn = (np + 3) / 4, tm = (M + 63) / 64;
+    if (xl != X_FRAG || np > 256 || np <= 128 || M > 128) return false;
+    if (nch >= 32 && nch < 64 && nch % 8 == 0) return M > 64 && tn * tm * 2 <= kCUs;
+    if (nch < 64 || nch % 16 != 0) return false;
+    if (dtype == DT_BF16 || fmt != FMT_Q4K) return M > 32;
+    return M > 48 && M <= 64;
+}
+
+int mid_m_rung(int fmt, long long M, long long np, bool k2_192)
+{
+    const long long g64 = (M + 63) / 64, g48 = (M + 47) / 48, q = (np + 3) / 4;
+    const auto rounds = [](long long wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
+    const double small = 8.0 * rounds(np * g64), k4 = 17.0 * rounds(q * g64);
+    const double wide = fmt == FMT_Q4K ? 15.5 * rounds(q * g48) : 1e30;
+    const double t192 = k2_192 ? 27.0 * rounds(((M + 191) / 192) * q) : 1e30;
+    if (t192 < wide && t192 < small && t192 < k4) return RUNG_M192N64_K2;
+    if (wide <= small && wide <= k4) return RUNG_WIDE;
+    return small <= k4 ? RUNG_SMALL_M : RUNG_M64_K4;
+}
+
+int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtype = DT_F16)
+{
+    const long long np = (N + 15) / 16, tn = (np + 7) / 8;
+    // the direct kernels put row groups of 16 on grid.y (at most 65535);
+    // beyond that only the streaming kernels' one-dimensional grid fits
+    if ((M + 15) / 16 > 65535) return fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128) ? RUNG_M128N160 : RUNG_M128;
+    if (np <= 4) return RUNG_SKINNY_N;
+    // above 32 rows a one-panel wave carries three or four row blocks of
+    // activations per weight run; four panels per wave and a grid over M win
+    if (M <= 64) {
+        // up to 16 rows: one panel per wave, the most waves streaming
+        // weights, except over 1536 panels and more (gate and up merged),
+        // where four panels per wave keep fewer, longer streams (M = 8, N =
+        // 24576: Q4_K 20.2 against 23.4 us, W4A16 18.6 against 20.6), and
+        // for 9..16 rows of row-major activations over 512 panels and more,
+        // where each 16-row piece of X then serves four panels (M = 16, N =
+        // 12288: Q4_K 12.2 against 15.7 us; on fragment-major X one panel
+        // per wave wins there, 10.6 against 11.7 us)
+        if (M <= 16) {
+            if (np >= 1536 || (xl == X_ROW && M > 8 && np >= 512)) return RUNG_SKINNY_N;
+            return RUNG_SMALL_M;
+        }
+        // (three row blocks per wave only pay off for Q4_K: the other
+        // formats' larger raw runs spill at that size)
+        if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
+        // 49..64 rows of Q4_K (33..64 of W4A16 and Q6_K) over many panels:
+        // unpack each weight once for all rows into LDS (64x64 tiles, K split
+        // four ways) instead of once per 16-row group (Q6_K 12288->12288 at
+        // M = 64: 50.5 against 90.1 us for direct-skinny-n)
+        if (np >= 512 && ((fmt == FMT_Q4K && M > 48) || (fmt != FMT_Q4K && M > 32))) return RUNG_M64_K4;
+        // Q6_K over few panels (N = 4096): 64x64 tiles with K also split
+        // across workgroups, so that each CU reads a quarter of the
+        // activations
+        if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
+        // fewer panels: one panel and all rows per wave (each weight
+        // unpacked once) beats four panels of 16 rows up to 64 rows
+        return RUNG_SMALL_M;
+    }
+    const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
+    // occupancy model: a 256x128 tile counts as two 128x128 tiles; the
+    // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
+    const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
+    const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
+    if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
+    if (t128 < 128) return mid_m_rung(fmt, M, np, xl == X_FRAG && (K / kChunk) % 2 == 0);
+    // on fragment-major activations, a 192-row tile with K split over two
+    // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
+    // and cover M with no more rows than 128-row tiles: 64 columns wide when
+    // those tiles fit (o and down at M = 658: 36.5 and 113-119 us), else 96
+    // (qkv: 47-50 us against 62 for 128x160; 192x64 would take 1.5 rounds, 64
+    // us); after the 352x96 check below, the 96-wide one also over two rounds
+    // at least 90% full (M = 768, N = 12288: Q4_K 90 against 101, Q6_K 254
+    // against 331 us; with 1.5 or three rounds it loses to the 256-row tile)
+    const long long r192 = (M + 191) / 192, t192 = r192 * ((np + 5) / 6);
+    const bool even2 = xl == X_FRAG && (K / kChunk) % 2 == 0;
+    const bool k2_192 = even2 && r192 * 192 <= (M + 127) / 128 * 128;
+    // (the 64-wide tile pays even where it computes more padding rows: Q4_K
+    // and Q6_K at M = 512, N = 4096: 29 and 85 us against 35 and 106 us for
+    // the 128x128 K-split tile)
+    if (even2 && r192 * ((np + 3) / 4) <= kCUs) return RUNG_M192N64_K2;
+    if (k2_192 && t192 <= kCUs) return RUNG_M192N96_K2;
+    // on fragment-major activations, the 352x96 tile (11 waves, three per
+    // SIMD) when its rounds, each costing 1.22 rounds of the 256-row tile,
+    // come out cheapest: two of its row tiles cover M = 641..704 where
+    // 256-row tiles need three (merged gate_up at M = 658: 147 against 173 us;
+    // M = 700, N = 12288: 76 against 95 us for 128x160; Q6_K, whose larger raw
+    // runs spill four registers in it, at M = 658, N = 12288: 218 against
+    // 333 us for 128x128).
+    if (xl == X_FRAG) {
+        const long long t352 = ((np + 5) / 6) * ((M + 351) / 352);
+        const double c352 = 2.44 * (double)((t352 + kCUs - 1) / kCUs);
+        if (c352 < c256 && c352 < c128) return RUNG_M352N96;
+    }
+    if (k2_192 && t192 <= 2 * kCUs && 10 * t192 >= 18 * kCUs) return RUNG_M192N96_K2;
+    // the 256-row tile when the occupancy model has it finish no later than
+    // the 128-row tiles (it unpacks each weight once for 256 rows); on
+    // fragment-major activations also whenever it has 512 tiles, and for
+    // Q6_K, whose unpack costs most, from one full round of them (M = 1024,
+    // N = K = 12288: 363.9 against 400.4 us for 128x128)
+    if (c256 <= c128 || (xl == X_FRAG && (t256 >= 512 || (fmt == FMT_Q6K && t256 >= kCUs)))) return RUNG_M16_256;
+    // few tiles: split K inside the workgroup (on row-major activations only
+    // over a long K, where the halves' activation reloads stay affordable)
+    if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) return RUNG_M128_K2;
+    // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
+    // runs do not fit that variant's registers)
+    if (fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128)) return RUNG_M128N160;
+    return RUNG_M128;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A failed launch is reported once on stderr with HIP's own text; the caller
+// gets QGEMM_ERR_HIP.
+int launch_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return QGEMM_OK;
+    fprintf(stderr, "qgemm: %s launch failed: %s (%d)\n", what, hipGetErrorString(e), (int)e);
+    return QGEMM_ERR_HIP;
+}
+
+// Shape rules shared by every device entry point.
+int check_shape(int fmt, long long M, long long N, long long K, long long group)
+{
+    if (fmt != FMT_Q4K && fmt != FMT_Q6K && fmt != FMT_W4) return QGEMM_ERR_FORMAT;
+    if (M < 0 || N < 1 || K < 1) return QGEMM_ERR_SHAPE;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return QGEMM_ERR_SHAPE;
+    if (fmt == FMT_W4) {  // group == 0: group size not known to the caller (rung queries)
+        if (group != 0 && (group < 32 || (group & (group - 1)) != 0)) return QGEMM_ERR_FORMAT;
+        if (K % 128 != 0 || (group != 0 && K % group != 0)) return QGEMM_ERR_SHAPE;
+    } else if (K % 256 != 0) {
+        return QGEMM_ERR_SHAPE;
+    }
+    return QGEMM_OK;
+}
+
+Args make_args(int fmt, const void *X, const void *W, void *Y, long long M, long long N, long long K, long long group,
+               int has_zp)
+{
+    Args a{};
+    a.X = (const uint16_t *)X;
+    a.W = (const uint8_t *)W;
+    a.Y = (uint16_t *)Y;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.np = (int)((N + 15) / 16);
+    a.group = fmt == FMT_W4 ? (int)group : 0;
+    a.has_zp = fmt == FMT_W4 ? (has_zp ? 1 : 0) : 0;
+    a.kw = 1;
+    if (fmt == FMT_W4) {
+        a.w4_sreg = (long long)a.np * (K / 128) * 1024;
+        a.w4_zreg = a.w4_sreg + (long long)a.np * (K / group) * 32;
+    }
+    return a;
+}
+template <int XL>
+hipError_t launch_xl(int fmt, int dtype, const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (fmt == FMT_Q4K)
+        return dtype == DT_F16 ? launch_fd<FMT_Q4K, DT_F16, XL>(pl, a, s) : launch_fd<FMT_Q4K, DT_BF16, XL>(pl, a, s);
+    if (fmt == FMT_Q6K)
+        return dtype == DT_F16 ? launch_fd<FMT_Q6K, DT_F16, XL>(pl, a, s) : launch_fd<FMT_Q6K, DT_BF16, XL>(pl, a, s);
+    return dtype == DT_F16 ? launch_fd<FMT_W4, DT_F16, XL>(pl, a, s) : launch_fd<FMT_W4, DT_BF16, XL>(pl, a, s);
+}
+
+hipError_t launch(int fmt, int dtype, int xl, const Plan &pl, const Args &a, hipStream_t s)
+{
+    return xl == X_FRAG ? launch_xl<X_FRAG>(fmt, dtype, pl, a, s) : launch_xl<X_ROW>(fmt, dtype, pl, a, s);
+}
+
+// Bytes of the split rungs' partial sums: S slices of 4-byte sums (fp32 or
+// int32), each row-major [M][N], the slice stride rounded up to 4 elements
+// so that every slice starts 16-byte aligned.  0 for the other rungs.
+size_t split_ws_bytes(const Plan &pl, long long M, long long N)
+{
+    if (pl.split <= 1 && pl.rung != RUNG_M64_SK) return 0;
+    const long long stride = (M * N + 3) & ~3LL;
+    return (size_t)(stride * pl.split) * 4;
+}
+
+// K split across workgroups: the slices' partial sums go to the caller's
+// workspace, then one launch adds them in slice order and rounds once.
+int gemm_split(int fmt, int dtype, int xl, const Plan &pl, Args a, void *ws, hipStream_t s)
+{
+    const long long MN = (long long)a.M * a.N, stride = (MN + 3) & ~3LL;
+    a.part = (float *)ws;
+    a.pstride = stride;
+    a.split = pl.split;
+    hipError_t e = launch(fmt, dtype, xl, pl, a, s);
+    if (e == hipSuccess) e = launch_splitk_reduce(dtype, (const float *)ws, a.Y, MN, stride, pl.split, s);
+    return launch_status(e, kRungNames[pl.rung]);
+}
+
+// Checks shared by the GEMM entry points; on success fills the plan.
+int gemm_plan(int fmt, int rung, long long M, long long N, long long K, long long group, int dtype, int xl, Plan &pl)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, M, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (rung < -1 || rung >= RUNG_COUNT) return QGEMM_ERR_FORMAT;
+    return make_plan(rung < 0 ? select_rung(fmt, M > 0 ? M : 1, N, K, xl, dtype) : rung, M > 0 ? M : 1, N, K, pl);
+}
+
+int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
+         long long group, int has_zp, int dtype, void *ws, size_t ws_bytes, void *stream, int xl = X_ROW)
+{
+    Plan pl;
+    int st = gemm_plan(fmt, rung, M, N, K, group, dtype, xl, pl);
+    if (st != QGEMM_OK) return st;
+    if (M == 0) return QGEMM_OK;
+    if (!X || !W || !Y) return QGEMM_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
+    const size_t need = split_ws_bytes(pl, M, N);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return QGEMM_ERR_SIZE;
+        if (!aligned16(ws)) return QGEMM_ERR_ALIGN;
+        if (!launch_fits(((M * N + 3) / 4 + 255) / 256, 256)) return QGEMM_ERR_SHAPE;
+    }
+    Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
+    a.kw = pl.kw;
+    if (need > 0) return gemm_split(fmt, dtype, xl, pl, a, ws, (hipStream_t)stream);
+    return launch_status(launch(fmt, dtype, xl, pl, a, (hipStream_t)stream), kRungNames[pl.rung]);
+}
+
+long long packed_bytes(int fmt, long long N, long long K, long long group, int has_zp)
+{
+    if (fmt == FMT_Q4K) return (long long)qgemm_q4k_packed_bytes(N, K);
+    if (fmt == FMT_Q6K) return (long long)qgemm_q6k_packed_bytes(N, K);
+    return (long long)qgemm_w4a16_packed_bytes(N, K, group, has_zp);
+}
+
+// Grouped plan: four panels per wave, row blocks sized by the mean rows per
+// expert (three 16-row blocks only for Q4_K, whose runs fit that variant),
+// grid.y an upper bound on every expert's row blocks, K split as the direct
+// rungs do.
+Plan grouped_plan(int fmt, long long T, long long E, long long N, long long K)
+{
+    Plan pl{};
+    const long long np = (N + 15) / 16, avg = (T + E - 1) / E;
+    pl.rung = -1;
+    pl.pn = 4;
+    pl.rb = avg <= 16 ? 1 : (avg <= 32 || fmt != FMT_Q4K) ? 2 : 3;
+    pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)(ceil_div(T, 16 * pl.rb) + E), 1);
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, (int)(K / kChunk), false);
+    pl.waves = pl.kw;
+    pl.rows = 16 * pl.rb;
+    pl.cols = 64;
+    pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
+    return pl;
+}
+
+int grouped(int fmt, const void *X, const void *W, void *Y, const int32_t *offs, long long E, long long T, long long N,
+            long long K, long long group, int has_zp, int dtype, void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, T, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (E < 1 || E > INT32_MAX / 2) return QGEMM_ERR_SHAPE;
+    if (T == 0) return QGEMM_OK;
+    if (!X || !W || !Y || !offs) return QGEMM_ERR_NULL;
+    const long long wstride = packed_bytes(fmt, N, K, group, has_zp);
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || ((uintptr_t)offs & 3u) != 0 || wstride % 16 != 0)
+        return QGEMM_ERR_ALIGN;
+    if ((long long)ceil_div(T, 16) + E > 65535) return QGEMM_ERR_SHAPE;  // grid.y limit
+    Args a = make_args(fmt, X, W, Y, T, N, K, group, has_zp);
+    a.offs = offs;
+    a.E = (int)E;
+    a.wstride = wstride;
+    // more than 32 rows per expert on average and at least 16 chunks: 64x64
+    // streaming tiles, which read an expert's activation rows once per 64
+    // columns (the direct kernel reads them once per 16): 128 experts, 41
+    // rows each on average, Q4_K 2048 -> 768: 80-81 against 101 us; over 6
+    // chunks (Q6_K 768 -> 2048) the direct kernel stays ahead, 91 against 94
+    const bool tiles = (T + E - 1) / E > 32 && K / kChunk >= 16;
+    const Plan pl = grouped_plan(fmt, T, E, N, K);
+    if (tiles ? !launch_fits(((N + 63) / 64) * ((T + 63) / 64 + E), 128) : !launch_fits(pl.grid.x, 64 * pl.kw))
+        return QGEMM_ERR_SHAPE;
+    a.kw = pl.kw;
+    return launch_status(launch_grouped(fmt, dtype, tiles, pl, a, T, E, (hipStream_t)stream), "grouped");
+}
+
+size_t staged_scratch_bytes(long long N, long long K)
+{
+    if (N < 1 || K < 1 || K % kChunk != 0 || N > INT32_MAX || K > INT32_MAX) return 0;
+    return (size_t)((N + 15) / 16) * 16 * (size_t)K * 2;
+}
+
+int staged(int fmt, const void *X, const void *W, void *scratch, size_t scratch_bytes, void *Y, long long M, long long N,
+           long long K, long long group, int has_zp, int dtype, void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, M, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (!W || !scratch || (M > 0 && (!X || !Y))) return QGEMM_ERR_NULL;
+    if (!aligned16(W) || !aligned16(scratch) || (M > 0 && (!aligned16(X) || !aligned16(Y)))) return QGEMM_ERR_ALIGN;
+    if (scratch_bytes < staged_scratch_bytes(N, K)) return QGEMM_ERR_SIZE;
+    Plan pl;
+    if (int st = make_plan(RUNG_M128, M > 0 ? M : 1, N, K, pl); st != QGEMM_OK) return st;
+    if (!launch_fits((((N + 15) / 16) * (K / kChunk) * 64 + 255) / 256, 256)) return QGEMM_ERR_SHAPE;
+    Args a = make_args(fmt, X, W, Y, M, N, K, group, has_zp);
+    return launch_status(launch_staged(fmt, dtype, a, (uint8_t *)scratch, pl, (hipStream_t)stream), "staged");
+}
+
+// ---------------------------------------------------------------------------
+// int8-activation path: rungs, validation, launches.
+// ---------------------------------------------------------------------------
+
+const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128",   "i8-256x128",   "i8-128x128-k2",
+                                                   "i8-256x96",    "i8-512x96",    "i8-352x96",
+                                                   "i8-192x96-k2", "i8-192x64-k2", "i8-64x64-sk"};
+// int32 sums stay exact while K * 127 * 127 < 2^31
+constexpr long long kI8MaxK = 131072;
+
+int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
+{
+    pl = Plan{};
+    pl.rung = rung;
+    pl.kw = 1;
+    pl.split = 1;
+    const int nch = (int)(K / kChunk);
+    switch (rung) {
+    case I8_M128: pl.rows = 128; pl.cols = 128; pl.waves = 4; break;
+    case I8_M256: pl.rows = 256; pl.cols = 128; pl.waves = 8; break;
+    case I8_M128_K2:
+        pl.rows = 128;
+        pl.cols = 128;
+        pl.kw = (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = 4 * pl.kw;
+        break;
+    case I8_M256N96: pl.rows = 256; pl.cols = 96; pl.waves = 8; break;
+    case I8_M512N96: pl.rows = 512; pl.cols = 96; pl.waves = 8; break;
+    case I8_M352N96: pl.rows = 352; pl.cols = 96; pl.waves = 11; break;
+    case I8_M192N96_K2:
+    case I8_M192N64_K2:
+        pl.rows = 192;
+        pl.cols = rung == I8_M192N64_K2 ? 64 : 96;
+        pl.kw = (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = 6 * pl.kw;
+        break;
+    case I8_M64_SK:
+        pl.rows = 64;
+        pl.cols = 64;
+        pl.kw = nch % 4 == 0 ? 4 : nch % 2 == 0 ? 2 : 1;
+        pl.waves = 2 * pl.kw;
+        break;
+    default: return QGEMM_ERR_FORMAT;
+    }
+    const long long np = (N + 15) / 16;
+    const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
+    if (!launch_fits(tn * tm, 64 * pl.waves)) return QGEMM_ERR_SHAPE;
+    pl.tiles_n = (int)tn;
+    pl.tiles_m = (int)tm;
+    if (rung == I8_M64_SK) {
+        // slices across workgroups: double while the grid stays within two
+        // workgroups per CU, the slices divide the chunks evenly among the
+        // in-group K groups and each group keeps two chunks
+        while (pl.split < 8 && tn * tm * 2 * pl.split <= 2 * kCUs && nch % (2 * pl.split * pl.kw) == 0 &&
+               nch / (2 * pl.split * pl.kw) >= 2)
+            pl.split *= 2;
+    }
+    if (!launch_fits(tn * tm * pl.split, 64 * pl.waves)) return QGEMM_ERR_SHAPE;
+    pl.grid = dim3((unsigned)(tn * tm * pl.split), 1, 1);
+    return QGEMM_OK;
+}
+
+// The int8 ladder (measured on MI355X, Q4_K/Q6_K/W4A16, M = 16..4096).
+// The unpack costs about four VALU instructions per weight, so a tile is
+// VALU-bound unless many rows share each unpacked weight:
+//  * with an even chunk count, a 192-row tile with K split over two 6-wave
+//    groups (three waves per SIMD) when its tiles fit one round, even where
+//    it computes more padding rows: 64 columns wide when those tiles fit (o
+//    and down at M = 658: 25.0 and 64.0 us against 28.7 and 75.5 us for
+//    192x96), else 96 (qkv: 32.1 us against 34.5 on 256x96 and 43 on
+//    192x64; Q6_K M = 512, N = 4096: 72 against 84 us for the 128x128
+//    K-split tile);
+//  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
+//    tile with K split over two wave groups (o and down at M = 658);
+//  * up to 128 rows: the 128x128 tile;
+//  * otherwise the 256x128, 256x96, 352x96 or 512x96 tile, whichever
+//    finishes in the fewest rounds of one workgroup per CU, a round costing
+//    1, 0.85, 1.17 and 1.35 (fitted to the measured times: the merged
+//    gate_up at M = 658 91 us on 352x96 against 107 on 256x96 and 117 on
+//    256x128; M = 2048 121 us on 512x96 against 133 on 256x128 and 138 on
+//    352x96; M = 4096 238 against 260 and 268).  The 352-row tile runs three
+//    waves per SIMD and unpacks each weight for 352 rows: two of its row
+//    tiles cover M = 658 where 256-row tiles need three.
+int i8_select(int fmt, long long M, long long N, long long K)
+{
+    const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8), r192 = (M + 191) / 192;
+    const long long nch = K / kChunk;
+    // few tiles of 192x64 (at most half the CUs): 64x64 tiles with K split
+    // across workgroups as well, up to 64 rows (Q6_K, whose unpack weighs
+    // most, up to 256): Q6_K 12288->4096 at M = 16..256 28.6-56.1 against
+    // 59.4-64.3 us, Q4_K 4096->4096 at M = 16..64 15.2-17.0 against
+    // 23.5-24.1 us (row quantizer included); over more tiles, or Q4_K from
+    // 96 rows, the 192x64 tile wins (4096->12288: 23.7-25.7 against 24.2-26.3)
+    if (nch % 8 == 0 && nch >= 16 && r192 * ((np + 3) / 4) <= kCUs / 2 && (M <= 64 || (fmt == FMT_Q6K && M <= 256)))
+        return I8_M64_SK;
+    if ((K / kChunk) % 2 == 0 && r192 * ((np + 3) / 4) <= kCUs) return I8_M192N64_K2;
+    if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs) return I8_M192N96_K2;
+    if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
+    if (M <= 128) return I8_M128;
+    const long long tm256 = (M + 255) / 256, tm352 = (M + 351) / 352, tm512 = (M + 511) / 512;
+    const long long tn128 = (np + 7) / 8, tn96 = (np + 5) / 6;
+    const auto rounds = [](long long tiles) { return (double)((tiles + kCUs - 1) / kCUs); };
+    const double c[4] = {rounds(tm256 * tn128), 0.85 * rounds(tm256 * tn96), 1.17 * rounds(tm352 * tn96),
+                         1.35 * rounds(tm512 * tn96)};
+    const int rung[4] = {I8_M256, I8_M256N96, I8_M352N96, I8_M512N96};
+    int best = 0;
+    for (int i = 1; i < 4; i++)
+        if (c[i] < c[best]) best = i;
+    return rung[best];
+}
+
+template <int DT>
+hipError_t launch_i8_dt(int fmt, const Plan &pl, const Args &a, hipStream_t s)
+{
+    if (fmt == FMT_Q4K) return launch_i8_fd<FMT_Q4K, DT>(pl, a, s);
+    if (fmt == FMT_Q6K) return launch_i8_fd<FMT_Q6K, DT>(pl, a, s);
+    return launch_i8_fd<FMT_W4, DT>(pl, a, s);
+}
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+int i8_gemm_plan(int fmt, int rung, long long M, long long N, long long K, long long group, int dtype, Plan &pl)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, M, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (K > kI8MaxK) return QGEMM_ERR_SHAPE;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (rung < -1 || rung >= I8_RUNG_COUNT) return QGEMM_ERR_FORMAT;
+    const long long m = M > 0 ? M : 1;
+    return i8_plan(rung < 0 ? i8_select(fmt, m, N, K) : rung, m, N, K, pl);
+}
+
+size_t i8_ws_bytes(const Plan &pl, long long M, long long N)
+{
+    if (pl.rung != I8_M64_SK) return 0;
+    return (size_t)(((M * N + 3) & ~3LL) * pl.split) * 4;
+}
+
+int i8_gemm(int fmt, int rung, const void *Xq, const float *sx, const void *W, const float *rw, const float *sw,
+            void *Y, long long M, long long N, long long K, long long group, int has_zp, int dtype, void *ws,
+            size_t ws_bytes, void *stream)
+{
+    Plan pl;
+    int st = i8_gemm_plan(fmt, rung, M, N, K, group, dtype, pl);
+    if (st != QGEMM_OK) return st;
+    if (M == 0) return QGEMM_OK;
+    if (!Xq || !sx || !W || !rw || !sw || !Y) return QGEMM_ERR_NULL;
+    if (!aligned16(Xq) || !aligned16(W) || !aligned16(Y) || !aligned4(sx) || !aligned4(rw) || !aligned4(sw))
+        return QGEMM_ERR_ALIGN;
+    Args a = make_args(fmt, Xq, W, Y, M, N, K, group, has_zp);
+    a.sx = sx;
+    a.rw = rw;
+    a.sw = sw;
+    const hipStream_t s = (hipStream_t)stream;
+    const size_t need = i8_ws_bytes(pl, M, N);
+    if (need > 0) {
+        // int32 partial sums per K slice in the caller's workspace, then
+        // their exact total through the unsplit epilogue
+        if (!ws || ws_bytes < need) return QGEMM_ERR_SIZE;
+        if (!aligned16(ws)) return QGEMM_ERR_ALIGN;
+        const long long MN = M * N, stride = (MN + 3) & ~3LL;
+        if (!launch_fits(((MN + 3) / 4 + 255) / 256, 256)) return QGEMM_ERR_SHAPE;
+        a.part = (float *)ws;
+        a.pstride = stride;
+        a.split = pl.split;
+        hipError_t e = dtype == DT_F16 ? launch_i8_dt<DT_F16>(fmt, pl, a, s) : launch_i8_dt<DT_BF16>(fmt, pl, a, s);
+        if (e == hipSuccess) e = launch_i8_reduce(dtype, (const int *)ws, sx, sw, (uint16_t *)Y, (int)M, (int)N, stride, pl.split, s);
+        return launch_status(e, kI8RungNames[pl.rung]);
+    }
+    const hipError_t e = dtype == DT_F16 ? launch_i8_dt<DT_F16>(fmt, pl, a, s) : launch_i8_dt<DT_BF16>(fmt, pl, a, s);
+    return launch_status(e, kI8RungNames[pl.rung]);
+}
+
+int i8_quantize(const void *X, void *Xq, float *sx, long long M, long long K, int dtype, void *stream)
+{
+    // one wave per padded row, four per workgroup of 256 threads
+    if (M < 0 || K < 32 || K % 32 != 0 || M > INT32_MAX - 31 || K > INT32_MAX) return QGEMM_ERR_SHAPE;
+    if (!launch_fits((M + 31) / 32 * 8, 256)) return QGEMM_ERR_SHAPE;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (M == 0) return QGEMM_OK;
+    if (!X || !Xq || !sx) return QGEMM_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return QGEMM_ERR_ALIGN;
+    return launch_status(launch_i8_quant(dtype, (const uint16_t *)X, (uint8_t *)Xq, sx, (int)M, (int)K, (hipStream_t)stream),
+                         "i8 quantize");
+}
+
+int i8_colscale(int fmt, const void *W, float *rw, float *sw, long long N, long long K, long long group, int has_zp,
+                void *stream)
+{
+    if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(fmt, 0, N, K, group);
+    if (st != QGEMM_OK) return st;
+    if (!W || !rw || !sw) return QGEMM_ERR_NULL;
+    if (!aligned16(W) || !aligned4(rw) || !aligned4(sw)) return QGEMM_ERR_ALIGN;
+    Args a = make_args(fmt, nullptr, W, nullptr, 0, N, K, group, has_zp);
+    return launch_status(launch_i8_colscale(fmt, a, rw, sw, (hipStream_t)stream), "i8 colscale");
+}
+
+void fill_info(const Plan &pl, int32_t *info)
+{
+    info[0] = pl.rung;
+    info[1] = pl.rows;
+    info[2] = pl.cols;
+    info[3] = kChunk;
+    info[4] = pl.waves;
+    info[5] = pl.kw * std::max(pl.split, 1);
+    info[6] = pl.tiles_n;
+    info[7] = pl.tiles_m;
+}
+
+}  // namespace
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" {
+
+const char *qgemm_status_str(int status)
+{
+    switch (status) {
+    case QGEMM_OK: return "ok";
+    case QGEMM_ERR_NULL: return "null pointer";
+    case QGEMM_ERR_SHAPE: return "illegal shape";
+    case QGEMM_ERR_DTYPE: return "unsupported dtype";
+    case QGEMM_ERR_ALIGN: return "pointer not aligned";
+    case QGEMM_ERR_FORMAT: return "unsupported format, group size or rung";
+    case QGEMM_ERR_SIZE: return "buffer too small";
+    case QGEMM_ERR_HIP: return "HIP launch failed";
+    case QGEMM_ERR_INPUT: return "malformed input data";
+    default: return "unknown status";
+    }
+}
+
+// The format entry points use the row-major ladder, which never picks a rung
+// that needs a workspace (a CPU test sweeps it); were it to, the call would
+// fail with QGEMM_ERR_SIZE rather than allocate.
+int qgemm_q4k(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, int dtype, void *stream)
+{
+    return gemm(FMT_Q4K, -1, X, W, Y, M, N, K, 0, 0, dtype, nullptr, 0, stream);
+}
+
+int qgemm_q6k(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, int dtype, void *stream)
+{
+    return gemm(FMT_Q6K, -1, X, W, Y, M, N, K, 0, 0, dtype, nullptr, 0, stream);
+}
+
+int qgemm_w4a16(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                int has_zp, int dtype, void *stream)
+{
+    return gemm(FMT_W4, -1, X, W, Y, M, N, K, group_size, has_zp, dtype, nullptr, 0, stream);
+}
+
+int qgemm_gemm_rung(int format, int rung, const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K,
+                    int64_t group_size, int has_zp, int dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm(format, rung, X, W, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, workspace,
+                workspace_bytes, stream);
+}
+
+size_t qgemm_workspace_bytes(int format, int rung, int layout, int64_t M, int64_t N, int64_t K, int dtype)
+{
+    if (layout != QGEMM_X_ROW && layout != QGEMM_X_FRAG) return 0;
+    Plan pl;
+    if (gemm_plan(format, rung, M, N, K, format == FMT_W4 ? 128 : 0, dtype, layout, pl) != QGEMM_OK) return 0;
+    return M > 0 ? split_ws_bytes(pl, M, N) : 0;
+}
+
+int qgemm_num_rungs(void) { return RUNG_COUNT; }
+
+const char *qgemm_rung_name(int rung) { return rung >= 0 && rung < RUNG_COUNT ? kRungNames[rung] : nullptr; }
+
+int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
+{
+    if (!info8) return QGEMM_ERR_NULL;
+    int st = check_shape(format, M, N, K, 0);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    Plan pl;
+    st = make_plan(rung, M, N, K, pl);
+    if (st != QGEMM_OK) return st;
+    fill_info(pl, info8);
+    return QGEMM_OK;
+}
+
+int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
+{
+    return qgemm_rung_info(select_rung(format, M, N, K, X_ROW, dtype), format, M, N, K, dtype, info8);
+}
+
+int qgemm_select_rung_xf(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8)
+{
+    return qgemm_rung_info(select_rung(format, M, N, K, X_FRAG, dtype), format, M, N, K, dtype, info8);
+}
+
+size_t qgemm_xf_bytes(int64_t M, int64_t K)
+{
+    if (M < 0 || K < kChunk || K % kChunk != 0 || M > INT32_MAX || K > INT32_MAX) return 0;
+    return (size_t)((M + 31) / 32) * 32 * (size_t)K * 2;
+}
+
+int qgemm_x_to_xf(const void *X, void *Xf, int64_t M, int64_t K, void *stream)
+{
+    if (M < 0 || K < kChunk || K % kChunk != 0 || M > INT32_MAX || K > INT32_MAX) return QGEMM_ERR_SHAPE;
+    if (!launch_fits(((M + 31) / 32) * (K / kChunk), 256)) return QGEMM_ERR_SHAPE;
+    if (M == 0) return QGEMM_OK;
+    if (!X || !Xf) return QGEMM_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Xf)) return QGEMM_ERR_ALIGN;
+    return launch_status(launch_x_to_xf((const uint16_t *)X, (uint16_t *)Xf, (int)M, (int)K, (hipStream_t)stream),
+                         "x_to_xf");
+}
+
+int qgemm_gemm_xf(int format, int rung, const void *Xf, const void *W, void *Y, int64_t M, int64_t N, int64_t K,
+                  int64_t group_size, int has_zp, int dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm(format, rung, Xf, W, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, workspace,
+                workspace_bytes, stream, X_FRAG);
+}
+
+int qgemm_dequant(int format, const void *W, void *Wout, int64_t N, int64_t K, int64_t group_size, int has_zp,
+                  int dtype, void *stream)
+{
+    if (format == FMT_W4 && group_size == 0) return QGEMM_ERR_FORMAT;
+    int st = check_shape(format, 0, N, K, format == FMT_W4 ? group_size : 0);
+    if (st != QGEMM_OK) return st;
+    if (dtype != DT_F16 && dtype != DT_BF16) return QGEMM_ERR_DTYPE;
+    if (!W || !Wout) return QGEMM_ERR_NULL;
+    if (!aligned16(W) || !aligned16(Wout)) return QGEMM_ERR_ALIGN;
+    Args a = make_args(format, nullptr, W, nullptr, 0, N, K, group_size, has_zp);
+    if (!launch_fits(((long long)a.np * (K / kChunk) * 64 + 255) / 256, 256)) return QGEMM_ERR_SHAPE;
+    return launch_status(launch_dequant(format, dtype, a, (uint16_t *)Wout, (hipStream_t)stream), "dequant");
+}
+
+size_t qgemm_staged_scratch_bytes(int64_t N, int64_t K) { return staged_scratch_bytes(N, K); }
+
+int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, size_t scratch_bytes, void *Y, int64_t M,
+                 int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream)
+{
+    return staged(format, X, Wpacked, scratch, scratch_bytes, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype,
+                  stream);
+}
+
+int qgemm_grouped(int format, const void *X, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E, int64_t T,
+                  int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream)
+{
+    return grouped(format, X, Wpacked, Y, offsets, E, T, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream);
+}
+
+size_t qgemm_i8_xq_bytes(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 32 || K % 32 != 0 || M > INT32_MAX - 31 || K > INT32_MAX) return 0;
+    return (size_t)((M + 31) / 32) * 32 * (size_t)K;
+}
+
+int qgemm_i8_quantize(const void *X, void *Xq, float *sx, int64_t M, int64_t K, int dtype, void *stream)
+{
+    return i8_quantize(X, Xq, sx, M, K, dtype, stream);
+}
+
+int qgemm_i8_colscale(int format, const void *Wpacked, float *rw, float *sw, int64_t N, int64_t K, int64_t group_size,
+                      int has_zp, void *stream)
+{
+    return i8_colscale(format, Wpacked, rw, sw, N, K, format == FMT_W4 ? group_size : 0, has_zp, stream);
+}
+
+int qgemm_i8_gemm(int format, int rung, const void *Xq, const float *sx, const void *Wpacked, const float *rw,
+                  const float *sw, void *Y, int64_t M, int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    return i8_gemm(format, rung, Xq, sx, Wpacked, rw, sw, Y, M, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype,
+                   workspace, workspace_bytes, stream);
+}
+
+size_t qgemm_i8_workspace_bytes(int format, int rung, int64_t M, int64_t N, int64_t K)
+{
+    Plan pl;
+    if (i8_gemm_plan(format, rung, M, N, K, format == FMT_W4 ? 128 : 0, DT_F16, pl) != QGEMM_OK) return 0;
+    return M > 0 ? i8_ws_bytes(pl, M, N) : 0;
+}
+
+int qgemm_i8_num_rungs(void) { return I8_RUNG_COUNT; }
+
+const char *qgemm_i8_rung_name(int rung) { return rung >= 0 && rung < I8_RUNG_COUNT ? kI8RungNames[rung] : nullptr; }
+
+int qgemm_i8_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int32_t *info8)
+{
+    if (!info8) return QGEMM_ERR_NULL;
+    int st = check_shape(format, M, N, K, 0);
+    if (st != QGEMM_OK) return st;
+    if (K > kI8MaxK) return QGEMM_ERR_SHAPE;
+    Plan pl;
+    st = i8_plan(rung, M, N, K, pl);
+    if (st != QGEMM_OK) return st;
+    fill_info(pl, info8);
+    return QGEMM_OK;
+}
+
+int qgemm_i8_select_rung(int format, int64_t M, int64_t N, int64_t K, int32_t *info8)
+{
+    return qgemm_i8_rung_info(i8_select(format, M, N, K), format, M, N, K, info8);
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// plan.h -- host-side launch plans of the fused-dequant GEMM and the launch
+// functions each kernel translation unit provides.  The M-ladder and the C
+// ABI (api.hip) fill a Plan and call these; the kernels and their template
+// instantiations live in the inst_*.hip and misc*.hip units, compiled apart
+// so that the library builds in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "common.h"
+
+namespace qg {
+
+enum Rung {
+    RUNG_SMALL_M = 0,     // direct, one panel per wave, up to 64 rows per wave
+    RUNG_SKINNY_N = 1,    // direct, up to four panels per wave, 16 rows per wave
+    RUNG_WIDE = 2,        // direct, four panels and up to 48 rows per wave
+    RUNG_M16_256 = 3,     // 16x16x32 MFMA: 256x128, 8 waves of 32x128
+    RUNG_M128 = 4,        // 32x32x16 MFMA: 128x128, 4 waves of 32x128
+    RUNG_M128_K2 = 5,     // 32x32x16 MFMA: 128x128, K split over two 4-wave groups
+    RUNG_M128N160 = 6,    // 32x32x16 MFMA: 128x160, 4 waves of 32x160
+    RUNG_M64_K4 = 7,      // 32x32x16 MFMA: 64x64, 2 waves of 32x64, K split over four groups
+    RUNG_M352N96 = 8,     // 32x32x16 MFMA: 352x96, 11 waves of 32x96
+    RUNG_M192N96_K2 = 9,  // 32x32x16 MFMA: 192x96, K split over two 6-wave groups (three waves per SIMD)
+    RUNG_M192N64_K2 = 10, // 32x32x16 MFMA: 192x64, K split over two 6-wave groups
+    RUNG_M64_SK = 11,     // 32x32x16 MFMA: 64x64, K split over four groups and across workgroups
+    RUNG_COUNT = 12
+};
+
+enum I8Rung {
+    I8_M128 = 0,        // 128x128, 4 waves of 32x128
+    I8_M256 = 1,        // 256x128, 8 waves of 32x128: each weight unpacked once for 256 rows
+    I8_M128_K2 = 2,     // 128x128, K split over two 4-wave groups
+    I8_M256N96 = 3,     // 256x96, 8 waves of 32x96
+    I8_M512N96 = 4,     // 512x96, 8 waves of 64x96: each weight unpacked once for 512 rows
+    I8_M352N96 = 5,     // 352x96, 11 waves of 32x96 (three per SIMD)
+    I8_M192N96_K2 = 6,  // 192x96, K split over two 6-wave groups (three waves per SIMD)
+    I8_M192N64_K2 = 7,  // 192x64, K split over two 6-wave groups
+    I8_M64_SK = 8,      // 64x64, K split over four groups and across workgroups
+    I8_RUNG_COUNT = 9
+};
+
+struct Plan {
+    int rung;
+    int tiles_n, tiles_m;  // output tiles along N and along M
+    int rows, cols;        // output tile
+    int waves, kw;         // waves per workgroup, K-split ways inside one workgroup
+    int split;             // K slices across workgroups (1: none)
+    int rb, pn;            // direct kernel: row blocks / panels per wave
+    dim3 grid;
+    size_t lds;            // dynamic LDS bytes
+};
+
+// fp16/bf16 path, one instantiation per (format, dtype, activation layout)
+// in inst_fp.hip: the direct and streaming rungs of a Plan.
+template <int FMT, int DT, int XL>
+hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s);
+
+// misc.hip
+hipError_t launch_splitk_reduce(int dtype, const float *part, uint16_t *Y, long long MN, long long stride, int S,
+                                hipStream_t s);
+hipError_t launch_dequant(int fmt, int dtype, const Args &a, uint16_t *out, hipStream_t s);
+hipError_t launch_x_to_xf(const uint16_t *X, uint16_t *Xf, int M, int K, hipStream_t s);
+hipError_t launch_staged(int fmt, int dtype, const Args &a, uint8_t *scratch, const Plan &pl, hipStream_t s);
+// misc_grouped.hip: the direct grouped kernel with the Plan's row blocks, or
+// (stream_tiles) the 64x64 streaming tiles over T rows and E experts
+hipError_t launch_grouped(int fmt, int dtype, bool stream_tiles, const Plan &pl, const Args &a, long long T,
+                          long long E, hipStream_t s);
+
+// int8 path: one instantiation per (format, dtype) in inst_i8.hip, the rest in
+// misc_i8.hip
+template <int FMT, int DT>
+hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s);
+hipError_t launch_i8_reduce(int dtype, const int *part, const float *sx, const float *sw, uint16_t *Y, int M, int N,
+                            long long stride, int S, hipStream_t s);
+hipError_t launch_i8_quant(int dtype, const uint16_t *X, uint8_t *Xq, float *sx, int M, int K, hipStream_t s);
+hipError_t launch_i8_colscale(int fmt, const Args &a, float *rw, float *sw, hipStream_t s);
+
+}  // namespace qg

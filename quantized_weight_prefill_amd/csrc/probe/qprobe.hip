@@ -1,4 +1,4 @@
-// Measurement aids, not part of the GEMM path.  The MFMA probe gives the
+// Measurement aids (libqprobe.so), not part of the GEMM library.  The MFMA probe gives the
 // sustained rate of the 32x32x16 MFMA on operands the caller supplies; the
 // read probe gives the rate of a plain streaming read.  MI355X lowers its clock
 // under dense MFMA load by an amount that depends on the operand bits (random
@@ -9,7 +9,7 @@
 
 #include <cstdint>
 
-#include "qgemm.h"
+#include "qprobe.h"
 
 namespace {
 
@@ -38,7 +38,7 @@ __global__ void __launch_bounds__(256) k_probe(const u32x4 *ops, float *out, int
     for (int it = 0; it < iters; it++) {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            if constexpr (DT == QGEMM_F16)
+            if constexpr (DT == QPROBE_F16)
                 c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[j]),
                                                               __builtin_bit_cast(f16x8, b[(j + it) & 3]), c[j], 0, 0, 0);
             else
@@ -72,26 +72,26 @@ __global__ void __launch_bounds__(256) k_read(const u32x4 *buf, long long nvec, 
 
 }  // namespace
 
-extern "C" int qgemm_probe_read(const void *buf, int64_t bytes, void *out, int blocks, void *stream)
+extern "C" int qprobe_read(const void *buf, int64_t bytes, void *out, int blocks, void *stream)
 {
-    if (!buf || !out) return QGEMM_ERR_NULL;
-    if (((uintptr_t)buf & 15u) != 0) return QGEMM_ERR_ALIGN;
-    if (bytes < 16 || bytes % 16 != 0 || blocks < 1) return QGEMM_ERR_SHAPE;
+    if (!buf || !out) return QPROBE_ERR_NULL;
+    if (((uintptr_t)buf & 15u) != 0) return QPROBE_ERR_ALIGN;
+    if (bytes < 16 || bytes % 16 != 0 || blocks < 1) return QPROBE_ERR_SHAPE;
     hipLaunchKernelGGL(k_read, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4 *)buf, (long long)(bytes / 16),
                        (uint32_t *)out);
-    return hipGetLastError() == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? QPROBE_OK : QPROBE_ERR_HIP;
 }
 
-extern "C" int qgemm_probe_mfma(const void *operands, float *out, int blocks, int iters, int dtype, void *stream)
+extern "C" int qprobe_mfma(const void *operands, float *out, int blocks, int iters, int dtype, void *stream)
 {
-    if (!operands || !out) return QGEMM_ERR_NULL;
-    if (((uintptr_t)operands & 15u) != 0) return QGEMM_ERR_ALIGN;
-    if (blocks < 1 || iters < 1) return QGEMM_ERR_SHAPE;
-    if (dtype != QGEMM_F16 && dtype != QGEMM_BF16) return QGEMM_ERR_DTYPE;
+    if (!operands || !out) return QPROBE_ERR_NULL;
+    if (((uintptr_t)operands & 15u) != 0) return QPROBE_ERR_ALIGN;
+    if (blocks < 1 || iters < 1) return QPROBE_ERR_SHAPE;
+    if (dtype != QPROBE_F16 && dtype != QPROBE_BF16) return QPROBE_ERR_DTYPE;
     hipStream_t s = (hipStream_t)stream;
-    if (dtype == QGEMM_F16)
-        hipLaunchKernelGGL(k_probe<QGEMM_F16>, dim3(blocks), dim3(256), 0, s, (const u32x4 *)operands, out, iters);
+    if (dtype == QPROBE_F16)
+        hipLaunchKernelGGL(k_probe<QPROBE_F16>, dim3(blocks), dim3(256), 0, s, (const u32x4 *)operands, out, iters);
     else
-        hipLaunchKernelGGL(k_probe<QGEMM_BF16>, dim3(blocks), dim3(256), 0, s, (const u32x4 *)operands, out, iters);
-    return hipGetLastError() == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+        hipLaunchKernelGGL(k_probe<QPROBE_BF16>, dim3(blocks), dim3(256), 0, s, (const u32x4 *)operands, out, iters);
+    return hipGetLastError() == hipSuccess ? QPROBE_OK : QPROBE_ERR_HIP;
 }

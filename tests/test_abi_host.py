@@ -177,8 +177,8 @@ def test_device_entry_argument_errors():
     assert lib.qgemm_w4a16(A, A, A, 4, 16, 256, 48, 1, 0, s) == -5
     assert lib.qgemm_w4a16(A, A, A, 4, 16, 192, 64, 1, 0, s) == -2
     assert lib.qgemm_w4a16(A, A, A, 4, 16, 256, 0, 1, 0, s) == -5
-    assert lib.qgemm_gemm_rung(0, 99, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
-    assert lib.qgemm_gemm_rung(7, 0, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
+    assert lib.qgemm_gemm_rung(0, 99, A, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -5
+    assert lib.qgemm_gemm_rung(7, 0, A, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -5
     # M == 0 is a no-op that touches nothing
     assert lib.qgemm_q4k(None, None, None, 0, 16, 256, 0, s) == 0
     assert lib.qgemm_dequant(0, None, A, 16, 256, 0, 0, 0, s) == -1
@@ -207,13 +207,13 @@ def test_device_entry_argument_errors():
     assert lib.qgemm_x_to_xf(None, A, 4, 128, s) == -1
     assert lib.qgemm_x_to_xf(A, mis, 4, 128, s) == -4
     assert lib.qgemm_x_to_xf(None, None, 0, 128, s) == 0     # M = 0
-    assert lib.qgemm_gemm_xf(0, -1, None, A, A, 4, 16, 256, 0, 0, 0, s) == -1
-    assert lib.qgemm_gemm_xf(0, -1, mis, A, A, 4, 16, 256, 0, 0, 0, s) == -4
-    assert lib.qgemm_gemm_xf(0, 99, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
-    assert lib.qgemm_gemm_xf(2, -1, A, A, A, 4, 16, 256, 48, 1, 0, s) == -5
-    assert lib.qgemm_gemm_xf(1, -1, A, A, A, 4, 16, 300, 0, 0, 0, s) == -2
-    assert lib.qgemm_gemm_xf(0, -1, A, A, A, 4, 16, 256, 0, 0, 5, s) == -3
-    assert lib.qgemm_gemm_xf(0, -1, None, None, None, 0, 16, 256, 0, 0, 0, s) == 0
+    assert lib.qgemm_gemm_xf(0, -1, None, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -1
+    assert lib.qgemm_gemm_xf(0, -1, mis, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -4
+    assert lib.qgemm_gemm_xf(0, 99, A, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -5
+    assert lib.qgemm_gemm_xf(2, -1, A, A, A, 4, 16, 256, 48, 1, 0, None, 0, s) == -5
+    assert lib.qgemm_gemm_xf(1, -1, A, A, A, 4, 16, 300, 0, 0, 0, None, 0, s) == -2
+    assert lib.qgemm_gemm_xf(0, -1, A, A, A, 4, 16, 256, 0, 0, 5, None, 0, s) == -3
+    assert lib.qgemm_gemm_xf(0, -1, None, None, None, 0, 16, 256, 0, 0, 0, None, 0, s) == 0
 
 
 def test_i8_entry_argument_errors():
@@ -243,16 +243,16 @@ def test_i8_entry_argument_errors():
     assert lib.qgemm_i8_colscale(0, mis, A, A, 16, 256, 0, 0, s) == -4
     # gemm
     g = lib.qgemm_i8_gemm
-    assert g(0, -1, A, A, A, A, A, A, 4, 16, 200, 0, 0, 0, s) == -2
-    assert g(0, -1, A, A, A, A, A, A, 4, 16, 262144, 0, 0, 0, s) == -2  # int32 sums would overflow
-    assert g(0, -1, A, A, A, A, A, A, 4, 16, 256, 0, 0, 9, s) == -3
-    assert g(0, 99, A, A, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -5
-    assert g(2, -1, A, A, A, A, A, A, 4, 16, 256, 48, 1, 0, s) == -5
-    assert g(0, -1, A, None, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -1
-    assert g(0, -1, A, A, A, A, None, A, 4, 16, 256, 0, 0, 0, s) == -1
-    assert g(0, -1, mis, A, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -4
-    assert g(0, -1, A, odd4, A, A, A, A, 4, 16, 256, 0, 0, 0, s) == -4
-    assert g(0, -1, None, None, None, None, None, None, 0, 16, 256, 0, 0, 0, s) == 0   # M = 0
+    assert g(0, -1, A, A, A, A, A, A, 4, 16, 200, 0, 0, 0, None, 0, s) == -2
+    assert g(0, -1, A, A, A, A, A, A, 4, 16, 262144, 0, 0, 0, None, 0, s) == -2  # int32 sums would overflow
+    assert g(0, -1, A, A, A, A, A, A, 4, 16, 256, 0, 0, 9, None, 0, s) == -3
+    assert g(0, 99, A, A, A, A, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -5
+    assert g(2, -1, A, A, A, A, A, A, 4, 16, 256, 48, 1, 0, None, 0, s) == -5
+    assert g(0, -1, A, None, A, A, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -1
+    assert g(0, -1, A, A, A, A, None, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -1
+    assert g(0, -1, mis, A, A, A, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -4
+    assert g(0, -1, A, odd4, A, A, A, A, 4, 16, 256, 0, 0, 0, None, 0, s) == -4
+    assert g(0, -1, None, None, None, None, None, None, 0, 16, 256, 0, 0, 0, None, 0, s) == 0   # M = 0
 
 
 def test_i8_ladder():
@@ -435,8 +435,8 @@ def test_grid_limits():
     A = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
     big = 65535 * 64 + 1  # past the limit of every direct rung (up to 64 rows per group)
     for rung in range(3):  # the three direct rungs
-        assert lib.qgemm_gemm_rung(0, rung, A, A, A, big, 32, 256, 0, 0, 0, None) == -2
-        assert lib.qgemm_gemm_xf(0, rung, A, A, A, big, 32, 256, 0, 0, 0, None) == -2
+        assert lib.qgemm_gemm_rung(0, rung, A, A, A, big, 32, 256, 0, 0, 0, None, 0, None) == -2
+        assert lib.qgemm_gemm_xf(0, rung, A, A, A, big, 32, 256, 0, 0, 0, None, 0, None) == -2
         with pytest.raises(qg.QGemmError) as e:
             qg.rung_info(rung, "q4k", big, 32, 256)
         assert e.value.status == -2
@@ -503,3 +503,137 @@ def test_grouped_offset_clamping_prefix_max_form():
         offs = rng.integers(-50, 400, E + 1)
         q = np.maximum.accumulate(np.concatenate([[0], offs]))[1:]
         assert [(min(int(q[e]), T), min(int(q[e + 1]), T)) for e in range(E)] == serial(offs, T), (offs, T)
+
+
+def test_grid_work_item_limit():
+    """A launch holds at most 2^31-1 workgroups and 2^32-1 work-items along x:
+    shapes whose grid would exceed that are shape errors before any launch,
+    not failed launches."""
+    lib = qg.lib()
+    A = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    # 128x128 tiles of 256 threads: 2^24 tiles is 2^32 work-items, one too many
+    n_tiles = 1 << 24
+    N = 128 * n_tiles
+    with pytest.raises(qg.QGemmError) as e:
+        qg.rung_info(4, "q4k", 128, N, 256)  # mfma32-128x128
+    assert e.value.status == -2
+    assert lib.qgemm_gemm_rung(0, 4, A, A, A, 128, N, 256, 0, 0, 0, None, 0, None) == -2
+    info = qg.rung_info(4, "q4k", 128, N - 128, 256)  # 2^24 - 1 tiles fit
+    assert info["tiles_n"] == n_tiles - 1
+    # the direct rungs: 64 threads per wave, the waves splitting K (one wave
+    # at K = 256); 2^26 panels of 16 columns is 2^32 work-items
+    with pytest.raises(qg.QGemmError):
+        qg.rung_info(0, "q4k", 16, 16 * (1 << 26), 256)
+    assert qg.rung_info(0, "q4k", 16, 16 * ((1 << 26) - 1), 256)["tiles_n"] == (1 << 26) - 1
+    # the fragment-major copy: one 256-thread workgroup per (32 rows, 128 k)
+    assert lib.qgemm_x_to_xf(A, A, 32 * (1 << 13), 128 * (1 << 11), None) == -2
+    # the dequant: one thread per (panel, chunk, run)
+    assert lib.qgemm_dequant(0, A, A, 16 * (1 << 21), 256 * (1 << 10), 0, 0, 0, None) == -2
+
+
+def test_workspace_contract():
+    """The library allocates nothing: the split rungs take the caller's
+    workspace and report its size; a call without enough of it fails before
+    any launch; the other rungs need none.  The row-major ladder (the format
+    entry points) never picks a rung that needs one."""
+    lib = qg.lib()
+    A = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    sk = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-64x64-sk"][0]
+    M, N, K = 64, 4096, 12288
+    info = qg.rung_info(sk, "q6k", M, N, K)
+    S = info["k_split"] // 4  # four K groups inside each workgroup
+    need = qg.workspace_bytes("q6k", sk, M, N, K)
+    assert S >= 2 and need == S * M * N * 4
+    assert qg.workspace_bytes("q6k", sk, M, N, K, layout=qg.X_FRAG) == need
+    assert qg.workspace_bytes("q6k", sk, 0, N, K) == 0
+    assert qg.workspace_bytes("q6k", 4, M, N, K) == 0                 # a rung with no split
+    assert lib.qgemm_workspace_bytes(1, sk, 7, M, N, K, 0) == 0       # unknown layout
+    # the fragment-major ladder picks the split rung for the down projection at M = 64
+    assert qg.select_rung_xf("q6k", M, N, K)["name"] == "mfma32-64x64-sk"
+    assert qg.workspace_bytes("q6k", -1, M, N, K, layout=qg.X_FRAG) == need
+    for call in (lib.qgemm_gemm_rung, lib.qgemm_gemm_xf):
+        assert call(1, sk, A, A, A, M, N, K, 0, 0, 0, None, 0, None) == -6
+        assert call(1, sk, A, A, A, M, N, K, 0, 0, 0, A, need - 16, None) == -6
+        assert call(1, sk, A, A, A, M, N, K, 0, 0, 0, mis, need, None) == -4
+    assert lib.qgemm_gemm_xf(1, -1, A, A, A, M, N, K, 0, 0, 0, None, 0, None) == -6
+    # odd M*N: each slice starts 16-byte aligned
+    assert qg.workspace_bytes("q6k", sk, 33, 4094, K) == S * ((33 * 4094 + 3) // 4 * 4) * 4
+    # the int8 path's split rung
+    i8sk = [r for r in range(qg.i8_num_rungs()) if qg.i8_rung_name(r) == "i8-64x64-sk"][0]
+    need8 = qg.i8_workspace_bytes("q6k", i8sk, M, N, K)
+    assert need8 > 0 and need8 % (M * N * 4) == 0
+    assert qg.i8_workspace_bytes("q6k", -1, 16, N, K) > 0             # the int8 ladder's pick
+    assert lib.qgemm_i8_gemm(1, i8sk, A, A, A, A, A, A, M, N, K, 0, 0, 0, None, 0, None) == -6
+    assert lib.qgemm_i8_gemm(1, i8sk, A, A, A, A, A, A, M, N, K, 0, 0, 0, A, need8 - 4, None) == -6
+    # the row-major ladder never needs a workspace
+    for fmt in ("q4k", "q6k", "w4a16"):
+        for dt in (qg.F16, qg.BF16):
+            for M in (1, 8, 16, 24, 33, 48, 49, 64, 80, 96, 128, 130, 200, 256, 658, 2048):
+                for K, N in ((4096, 4096), (12288, 4096), (4096, 2048), (4096, 3072), (4096, 12288), (8192, 4096)):
+                    assert qg.workspace_bytes(fmt, -1, M, N, K, dt, qg.X_ROW) == 0, (fmt, dt, M, N, K)
+
+
+# every declaration in include/qgemm.h carries a citation of the pages (a
+# page's short name from the header's preamble and the section it follows)
+PAGE_NAMES = ("batched-prefill post", "W4A16 PR", "delta-net page", "dequant-scratch post", "sparkinfer PR")
+
+
+def _declaration_comments(path):
+    """(function name, the comment block that precedes its declaration group)."""
+    text = open(path).read()
+    out = []
+    last_comment = ""
+    pos = 0
+    for m in re.finditer(r"/\*.*?\*/|^[a-z_ ]+\**\s*\b(q[a-z0-9_]+)\s*\(", text, flags=re.S | re.M):
+        if m.group(0).startswith("/*"):
+            last_comment = m.group(0)
+        else:
+            out.append((m.group(1), last_comment))
+    return out
+
+
+def test_header_declarations_cite_the_pages():
+    decls = _declaration_comments(HEADER)
+    assert len(decls) == len(header_functions())
+    for name, comment in decls:
+        flat = " ".join(comment.split())
+        assert any(p in flat for p in PAGE_NAMES), f"{name}: its comment cites no page"
+        assert re.search(r'"[^"]{3,}"', flat), f"{name}: its comment names no section of the page it cites"
+
+
+def test_binding_checks_buffers_before_any_call():
+    """The Python binding refuses a packed weight smaller than the format's
+    packed size (times the experts for the grouped GEMM) and an output of the
+    wrong shape or dtype before it calls the library, on every device entry
+    point; the W4A16 zero-point flag defaults to symmetric everywhere."""
+    import inspect
+
+    import torch
+
+    M, N, K = 8, 48, 512
+    x = torch.zeros((M, K), dtype=torch.float16)
+    full = qg.packed_bytes("q4k", N, K)
+    short = torch.zeros(full - 16, dtype=torch.uint8)
+    ok = torch.zeros(full, dtype=torch.uint8)
+    offs = torch.zeros(3, dtype=torch.int32)
+    for call in (lambda: qg.q4k(x, short, N), lambda: qg.gemm_rung("q4k", -1, x, short, N),
+                 lambda: qg.staged("q4k", x, short, N), lambda: qg.grouped("q4k", x, ok, N, offs, 2),
+                 lambda: qg.dequant("q4k", short, N, K, qg.F16)):
+        with pytest.raises(ValueError, match="packed weight"):
+            call()
+    w4_sym = qg.packed_bytes("w4a16", N, K, 128, False)
+    assert w4_sym < qg.packed_bytes("w4a16", N, K, 128, True)
+    with pytest.raises(ValueError, match="packed weight"):  # an asymmetric call on a symmetric packing
+        qg.w4a16(x, torch.zeros(w4_sym, dtype=torch.uint8), N, 128, True)
+    bad_out = torch.zeros((M, N + 1), dtype=torch.float16)
+    bad_dt = torch.zeros((M, N), dtype=torch.bfloat16)
+    two = torch.zeros(2 * full, dtype=torch.uint8)
+    for out in (bad_out, bad_dt):
+        for call in (lambda: qg.grouped("q4k", x, two, N, offs, 2, out=out), lambda: qg.staged("q4k", x, ok, N, out=out),
+                     lambda: qg.gemm_rung("q4k", -1, x, ok, N, out=out), lambda: qg.q6k(x, torch.zeros(
+                         qg.packed_bytes("q6k", N, K), dtype=torch.uint8), N, out=out)):
+            with pytest.raises(ValueError, match="out"):
+                call()
+    for fn in (qg.grouped, qg.staged, qg.gemm_rung, qg.gemm_xf, qg.gemm_i8, qg.dequant, qg.i8_colscale):
+        assert inspect.signature(fn).parameters["has_zp"].default is False, fn.__name__

@@ -53,21 +53,41 @@ def test_split_rung_auto_down_projection(M):
     assert np.array_equal(y, from_device(c.run_xf(-1)))
 
 
-def test_split_workspace_grows_between_calls():
-    """A call that needs a larger workspace than the previous one on the same
-    stream (the old one is replaced in stream order), then a smaller one."""
+def _ws(nbytes: int, guard: int = 0):
+    import torch
+
+    return torch.full((nbytes + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+
+
+def test_split_workspace_caller_owned_sizes():
+    """The caller's workspace, sized by qgemm_workspace_bytes, for calls that
+    need more, then less, than the previous one: every result meets the
+    bound, and nothing past the stated size is written (a guard band of 4 KB
+    after it keeps its pattern).  A workspace one slice short is refused."""
+    import torch
+
     for i, (M, N, K) in enumerate([(8, 64, 4096), (64, 512, 8192), (16, 80, 4096)]):
         c = Case("q4k", M, N, K, qg.F16, seed=740 + i)
-        print(f"split workspace M={M} N={N} K={K}", flush=True)
-        y = from_device(c.run(SK))
+        need = qg.workspace_bytes("q4k", SK, M, N, K)
+        print(f"split workspace M={M} N={N} K={K} bytes={need}", flush=True)
+        assert need > 0
+        ws = _ws(need, 4096)
+        x = to_device(c.X, c.dtype)
+        wp = c.device_weights()
+        y = qg.gemm_rung("q4k", SK, x, wp, N, workspace=ws)
+        torch.cuda.synchronize()
         Yref, B = oracle.gemm(c.X, c.W, qg.F16)
-        assert_gemm_close(y, Yref, B, qg.F16, what=f"split workspace M={M} N={N} K={K}")
+        assert_gemm_close(from_device(y), Yref, B, qg.F16, what=f"split workspace M={M} N={N} K={K}")
+        assert bool((ws[need:] == 0xA5).all()), "the library wrote past the workspace size it reported"
+        with pytest.raises(qg.QGemmError) as e:
+            qg.gemm_rung("q4k", SK, x, wp, N, workspace=ws[:need - 16])
+        assert e.value.status == -6
 
 
 def test_split_rung_concurrent_streams():
     """Two streams (default priority) running split-rung GEMMs at once, each
-    several times back to back: every result equals the same problem run
-    alone, so calls on different streams never share partial sums."""
+    several times back to back, each with its own workspace: every result
+    equals the same problem run alone."""
     import torch
 
     cases = [Case("q6k", 64, 256, 12288, qg.F16, seed=760), Case("q4k", 40, 320, 8192, qg.F16, seed=761)]
@@ -75,48 +95,54 @@ def test_split_rung_concurrent_streams():
     torch.cuda.synchronize()
     xs = [to_device(c.X, c.dtype) for c in cases]
     wps = [c.device_weights() for c in cases]
+    wss = [_ws(qg.workspace_bytes(c.fmt, SK, c.M, c.N, c.K)) for c in cases]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [[None] * 4 for _ in cases]
     torch.cuda.synchronize()
     for rep in range(4):
         for i, c in enumerate(cases):
             with torch.cuda.stream(streams[i]):
-                outs[i][rep] = qg.gemm_rung(c.fmt, SK, xs[i], wps[i], c.N, stream=streams[i].cuda_stream)
+                outs[i][rep] = qg.gemm_rung(c.fmt, SK, xs[i], wps[i], c.N, stream=streams[i].cuda_stream,
+                                            workspace=wss[i])
     torch.cuda.synchronize()
     for i in range(len(cases)):
         for rep in range(4):
             assert np.array_equal(from_device(outs[i][rep]), alone[i]), (i, rep)
 
 
-def test_split_rung_graph_capture_after_warmup():
-    """A split-rung call captured into a HIP graph after one eager call on the
-    capture stream (which takes that stream's workspace, so the capture takes
-    or returns no memory): every replay, with eager work and synchronisations
-    in between, equals the eager result."""
+def test_split_rung_graph_capture_then_larger_eager_call():
+    """A split-rung call captured into a HIP graph with its own workspace;
+    then, between replays, eager split calls of a larger size with another
+    workspace on the same stream (a library-held workspace would have been
+    regrown and freed under the graph here).  Every replay equals the eager
+    result, and so does every eager call."""
     import torch
 
     c = Case("q6k", 64, 256, 12288, qg.F16, seed=780)
-    x = to_device(c.X, c.dtype)
-    wp = c.device_weights()
+    big = Case("q6k", 128, 512, 12288, qg.F16, seed=781)
+    x, wp = to_device(c.X, c.dtype), c.device_weights()
+    xb, wpb = to_device(big.X, big.dtype), big.device_weights()
     ref = from_device(c.run(SK))
+    ref_big = from_device(big.run(SK))
+    ws = _ws(qg.workspace_bytes("q6k", SK, 64, 256, 12288))
+    ws_big = _ws(qg.workspace_bytes("q6k", SK, 128, 512, 12288))
+    assert ws_big.numel() > ws.numel()
     s = torch.cuda.Stream()
     y = torch.empty((64, 256), dtype=torch.float16, device="cuda")
-    torch.cuda.synchronize()
-    print("split graph capture: warm-up on the capture stream", flush=True)
-    with torch.cuda.stream(s):
-        qg.gemm_rung("q6k", SK, x, wp, 256, out=y, stream=s.cuda_stream)
-    s.synchronize()
-    assert np.array_equal(from_device(y), ref)
+    yb = torch.empty((128, 512), dtype=torch.float16, device="cuda")
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     print("split graph capture: capture", flush=True)
     with torch.cuda.graph(g, stream=s):
-        qg.gemm_rung("q6k", SK, x, wp, 256, out=y, stream=s.cuda_stream)
+        qg.gemm_rung("q6k", SK, x, wp, 256, out=y, stream=s.cuda_stream, workspace=ws)
     torch.cuda.synchronize()
     for rep in range(3):
         y.fill_(0)
         torch.cuda.synchronize()
-        print(f"split graph capture: replay {rep}", flush=True)
+        with torch.cuda.stream(s):
+            qg.gemm_rung("q6k", SK, xb, wpb, 512, out=yb, stream=s.cuda_stream, workspace=ws_big)
+        print(f"split graph capture: replay {rep} after a larger eager call", flush=True)
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(from_device(y), ref), rep
+        assert np.array_equal(from_device(yb), ref_big), rep
