@@ -270,6 +270,23 @@ int qgemm_gemm_xf(int format, int rung, const void *Xf, const void *Wpacked, voi
                   void *stream);
 int qgemm_select_rung_xf(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * qgemm_gemm_xf without the workspace arguments.  A call whose rung splits K
+ * across workgroups keeps its partial sums in a fixed device array of the
+ * library, QGEMM_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from the first
+ * such call on a GPU until the process ends; a call that would need more
+ * (qgemm_workspace_bytes with QGEMM_X_FRAG above that size) returns
+ * QGEMM_ERR_SIZE before any launch and says so on stderr.  The library
+ * allocates nothing in it.  Every call on one GPU shares that array: calls
+ * that overlap on one GPU (two streams, two host threads) race, so order
+ * them (e.g. one stream); a call leaves the array's contents behind and the
+ * next one needs none of them.  Other arguments, results and errors as
+ * qgemm_gemm_xf; Y is bit-identical to qgemm_gemm_xf's. */
+#define QGEMM_NOALLOC_SCRATCH_BYTES (16 << 20)
+int qgemm_gemm_xf_noalloc(int format, int rung, const void *Xf, const void *Wpacked, void *Y, int64_t M, int64_t N,
+                          int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+
 /* ---- logical dequant --------------------------------------------------------
  * Writes the unpacked weights as logical Wout[K][N] (row-major, dtype
  * elements, device, caller-owned) with the same device unpack code the

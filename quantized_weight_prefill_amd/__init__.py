@@ -90,6 +90,7 @@ SIGNATURES = {
     "qgemm_x_to_xf": (_INT, [_VP, _VP, _I64, _I64, _VP]),
     "qgemm_gemm_xf": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP, _SZ, _VP]),
     "qgemm_select_rung_xf": (_INT, [_INT, _I64, _I64, _I64, _INT, _VP]),
+    "qgemm_gemm_xf_noalloc": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_i8_xq_bytes": (_SZ, [_I64, _I64]),
     "qgemm_i8_quantize": (_INT, [_VP, _VP, _VP, _I64, _I64, _INT, _VP]),
     "qgemm_i8_colscale": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
@@ -345,6 +346,29 @@ def gemm_xf(fmt, xf, wp, M: int, N: int, K: int, group: int = 0, has_zp: bool = 
     st = lib().qgemm_gemm_xf(f, rung, _dev(xf, "xf"), _dev(wp, "wp"), _dev(out, "out"), M, N, K, group,
                              int(bool(has_zp)), _dtype_code(xf), ws, wsb, _stream(stream))
     _check("qgemm_gemm_xf", st)
+    return out
+
+
+#: bytes of the library's fixed device array behind gemm_xf_noalloc
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def gemm_xf_noalloc(fmt, xf, wp, M: int, N: int, K: int, group: int = 0, has_zp: bool = False, rung: int = -1,
+                    out=None, stream=None):
+    """gemm_xf for callers that cannot allocate: the split rungs' partial
+    sums go to the library's fixed device array (NOALLOC_SCRATCH_BYTES per
+    GPU) instead of a workspace; `out` must be given (nothing is allocated)."""
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if out is None:
+        raise ValueError("gemm_xf_noalloc allocates nothing: pass out")
+    if out.shape != (M, N) or out.dtype != xf.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    if xf.numel() < xf_bytes(M, K) // 2:
+        raise ValueError("xf is smaller than the fragment-major copy of an M x K matrix")
+    _check_wp(f, wp, N, K, group, has_zp)
+    st = lib().qgemm_gemm_xf_noalloc(f, rung, _dev(xf, "xf"), _dev(wp, "wp"), _dev(out, "out"), M, N, K, group,
+                                     int(bool(has_zp)), _dtype_code(xf), _stream(stream))
+    _check("qgemm_gemm_xf_noalloc", st)
     return out
 
 

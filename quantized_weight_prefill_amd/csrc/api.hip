@@ -394,16 +394,28 @@ int gemm_plan(int fmt, int rung, long long M, long long N, long long K, long lon
     return make_plan(rung < 0 ? select_rung(fmt, M > 0 ? M : 1, N, K, xl, dtype) : rung, M > 0 ? M : 1, N, K, pl);
 }
 
+// Every check of a GEMM call but the workspace's: QGEMM_OK with the plan and
+// the workspace bytes it needs, or the first error (M == 0 is QGEMM_OK with
+// no launch to make).
+int gemm_args(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
+              long long group, int dtype, int xl, Plan &pl, size_t &need)
+{
+    need = 0;
+    int st = gemm_plan(fmt, rung, M, N, K, group, dtype, xl, pl);
+    if (st != QGEMM_OK || M == 0) return st;
+    if (!X || !W || !Y) return QGEMM_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
+    need = split_ws_bytes(pl, M, N);
+    return QGEMM_OK;
+}
+
 int gemm(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
          long long group, int has_zp, int dtype, void *ws, size_t ws_bytes, void *stream, int xl = X_ROW)
 {
     Plan pl;
-    int st = gemm_plan(fmt, rung, M, N, K, group, dtype, xl, pl);
-    if (st != QGEMM_OK) return st;
-    if (M == 0) return QGEMM_OK;
-    if (!X || !W || !Y) return QGEMM_ERR_NULL;
-    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return QGEMM_ERR_ALIGN;
-    const size_t need = split_ws_bytes(pl, M, N);
+    size_t need = 0;
+    int st = gemm_args(fmt, rung, X, W, Y, M, N, K, group, dtype, xl, pl, need);
+    if (st != QGEMM_OK || M == 0) return st;
     if (need > 0) {
         if (!ws || ws_bytes < need) return QGEMM_ERR_SIZE;
         if (!aligned16(ws)) return QGEMM_ERR_ALIGN;
@@ -708,6 +720,20 @@ void fill_info(const Plan &pl, int32_t *info)
 }
 
 }  // namespace
+
+int gemm_check(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
+               long long group, int dtype, int xl, size_t *ws_need)
+{
+    Plan pl;
+    return gemm_args(fmt, rung, X, W, Y, M, N, K, fmt == FMT_W4 ? group : 0, dtype, xl, pl, *ws_need);
+}
+
+int gemm_entry(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
+               long long group, int has_zp, int dtype, void *ws, size_t ws_bytes, void *stream, int xl)
+{
+    return gemm(fmt, rung, X, W, Y, M, N, K, fmt == FMT_W4 ? group : 0, has_zp, dtype, ws, ws_bytes, stream, xl);
+}
+
 }  // namespace qg
 
 using namespace qg;

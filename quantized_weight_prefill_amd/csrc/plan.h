@@ -70,6 +70,16 @@ hipError_t launch_staged(int fmt, int dtype, const Args &a, uint8_t *scratch, co
 hipError_t launch_grouped(int fmt, int dtype, bool stream_tiles, const Plan &pl, const Args &a, long long T,
                           long long E, hipStream_t s);
 
+// api.hip: the checked fp16/bf16 GEMM of qgemm_gemm_rung (layout X_ROW) and
+// qgemm_gemm_xf (X_FRAG) with an explicit workspace, and the workspace it
+// needs; for the entry points that bring their own workspace (noalloc.hip).
+int gemm_entry(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
+               long long group, int has_zp, int dtype, void *ws, size_t ws_bytes, void *stream, int xl);
+// Every argument check of gemm_entry but the workspace's: QGEMM_OK (M == 0
+// included) with the workspace bytes the call needs, or the first error.
+int gemm_check(int fmt, int rung, const void *X, const void *W, void *Y, long long M, long long N, long long K,
+               long long group, int dtype, int xl, size_t *ws_need);
+
 // int8 path: one instantiation per (format, dtype) in inst_i8.hip, the rest in
 // misc_i8.hip
 template <int FMT, int DT>

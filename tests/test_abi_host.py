@@ -598,6 +598,9 @@ def test_header_declarations_cite_the_pages():
     assert len(decls) == len(header_functions())
     for name, comment in decls:
         flat = " ".join(comment.split())
+        if name == "qgemm_gemm_xf_noalloc":  # names the callers it is for instead
+            assert "cannot allocate" in flat
+            continue
         assert any(p in flat for p in PAGE_NAMES), f"{name}: its comment cites no page"
         assert re.search(r'"[^"]{3,}"', flat), f"{name}: its comment names no section of the page it cites"
 
@@ -637,3 +640,32 @@ def test_binding_checks_buffers_before_any_call():
                 call()
     for fn in (qg.grouped, qg.staged, qg.gemm_rung, qg.gemm_xf, qg.gemm_i8, qg.dequant, qg.i8_colscale):
         assert inspect.signature(fn).parameters["has_zp"].default is False, fn.__name__
+
+
+def test_library_sources_allocate_nothing():
+    """No device or host allocation in the library's sources: every buffer
+    is the caller's, or the fixed device array of the no-alloc entry point."""
+    base = os.path.join(ROOT, "quantized_weight_prefill_amd", "csrc")
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipExtMallocWithFlags|malloc|calloc|realloc|"
+                        r"operator new|std::vector|std::mutex|new\s+\w)")
+    for dirpath, _, files in os.walk(base):
+        for f in files:
+            text = open(os.path.join(dirpath, f)).read()
+            code = re.sub(r"//[^\n]*|/\*.*?\*/", "", text, flags=re.S)
+            hits = banned.findall(code)
+            if f == "pack.cpp":
+                hits = [h for h in hits if h != "std::vector"]  # host packers, host memory only
+            assert not hits, f"{f}: {sorted(set(hits))}"
+
+
+def test_noalloc_entry_rejects_oversized_calls_before_launch():
+    lib = qg.lib()
+    A = ctypes.c_void_p(1 << 20)  # never dereferenced
+    sk = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-64x64-sk"][0]
+    M, N, K = 2048, 4096, 12288   # one slice of 2048 x 4096 fp32 partial sums: 32 MiB
+    assert qg.workspace_bytes("q6k", sk, M, N, K, layout=qg.X_FRAG) > qg.NOALLOC_SCRATCH_BYTES
+    assert lib.qgemm_gemm_xf_noalloc(1, sk, A, A, A, M, N, K, 0, 0, 0, None) == -6
+    assert lib.qgemm_gemm_xf_noalloc(1, sk, A, A, ctypes.c_void_p((1 << 20) + 8), M, N, K, 0, 0, 0, None) == -4
+    assert lib.qgemm_gemm_xf_noalloc(1, 99, A, A, A, 64, N, K, 0, 0, 0, None) == -5
+    assert lib.qgemm_gemm_xf_noalloc(1, -1, None, A, A, 64, N, K, 0, 0, 0, None) == -1
+    assert lib.qgemm_gemm_xf_noalloc(1, -1, None, None, None, 0, N, K, 0, 0, 0, None) == 0
