@@ -167,6 +167,51 @@ int qgemm_w4a16_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t
 int qgemm_w4a16_unpack(const void *packed, int64_t N, int64_t K, int64_t group_size, int has_zp, uint8_t *codes,
                        uint16_t *scales, uint8_t *zeros);
 
+/* ---- GGUF checkpoints (host memory) ----------------------------------------
+ * The k-quant weights the pages run come in GGUF files: the batched-prefill
+ * post's Qwen3-8B Q4_K_M ("The measured result"), whose ffn_down and attn_v
+ * tensors are Q6_K and the rest Q4_K ("Bug 2: Q6_K had a gate but no
+ * dispatcher").  These calls read such a file -- version 2 or 3 of the
+ * container: header, metadata, tensor infos, the data section at
+ * `general.alignment` (default 32) -- from one caller-owned host buffer
+ * holding the whole file (read or memory-mapped), allocate nothing, and
+ * check every length, count and offset against `size`: a truncated or
+ * malformed file returns QGEMM_ERR_INPUT, never a read outside the buffer.
+ * A tensor's dims[0] is its row length (contiguous in the file): for a
+ * linear layer's weight, dims = {K, N}, which is the packers' [N][K/256]
+ * block order, so a Q4_K or Q6_K tensor packs with no reordering.
+ *
+ * qgemm_gguf_header: the container version, tensor and metadata counts, the
+ *   alignment and the byte offset of the data section.
+ * qgemm_gguf_tensor_info: tensor `index` (0 .. n_tensors-1; else
+ *   QGEMM_ERR_SHAPE): its name (NUL-terminated into name[name_cap];
+ *   QGEMM_ERR_SIZE, with the name cut, when it does not fit), ggml type
+ *   (QGEMM_GGML_Q4_K, QGEMM_GGML_Q6_K, ...), dimension count and dims (dims4[4],
+ *   1 past n_dims), the byte offset of its data in the buffer and its byte
+ *   size (0 for a type this library does not size).  Any output may be NULL.
+ * qgemm_gguf_find_kv: the metadata entry `key` (NUL-terminated): its value
+ *   type (the container's codes: 4 u32, 6 f32, 8 string, 9 array, ...), and
+ *   the byte offset and size of its encoded value in the buffer (a string:
+ *   u64 length then bytes; an array: u32 element type, u64 count, elements);
+ *   QGEMM_ERR_FORMAT when no entry has that key.
+ * qgemm_gguf_packed_bytes / qgemm_gguf_pack: a two-dimensional Q4_K or Q6_K
+ *   tensor packed with qgemm_q4k_pack / qgemm_q6k_pack into `out` (host,
+ *   caller-owned, at least qgemm_gguf_packed_bytes bytes); *format (QGEMM_FMT_*),
+ *   *N = dims[1] and *K = dims[0] say how to call the GEMMs on it.  Any other
+ *   tensor type is QGEMM_ERR_FORMAT (packed_bytes returns 0), never a
+ *   conversion. */
+#define QGEMM_GGML_Q4_K 12
+#define QGEMM_GGML_Q6_K 14
+int qgemm_gguf_header(const void *buf, size_t size, uint32_t *version, int64_t *n_tensors, int64_t *n_kv,
+                      int64_t *alignment, int64_t *data_offset);
+int qgemm_gguf_tensor_info(const void *buf, size_t size, int64_t index, char *name, size_t name_cap, int32_t *type,
+                           int32_t *n_dims, int64_t *dims4, int64_t *data_offset, int64_t *data_bytes);
+int qgemm_gguf_find_kv(const void *buf, size_t size, const char *key, int32_t *value_type, int64_t *value_offset,
+                       int64_t *value_bytes);
+size_t qgemm_gguf_packed_bytes(const void *buf, size_t size, int64_t index);
+int qgemm_gguf_pack(const void *buf, size_t size, int64_t index, void *out, size_t out_bytes, int32_t *format,
+                    int64_t *N, int64_t *K);
+
 /* ---- fused-dequant GEMMs (device memory, asynchronous on `stream`) ------- */
 
 /* Q4_K weights (the dequant-scratch post, "What removing it was worth": the

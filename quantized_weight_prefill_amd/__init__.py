@@ -91,6 +91,11 @@ SIGNATURES = {
     "qgemm_gemm_xf": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP, _SZ, _VP]),
     "qgemm_select_rung_xf": (_INT, [_INT, _I64, _I64, _I64, _INT, _VP]),
     "qgemm_gemm_xf_noalloc": (_INT, [_INT, _INT, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_gguf_header": (_INT, [_VP, _SZ, _VP, _VP, _VP, _VP, _VP]),
+    "qgemm_gguf_tensor_info": (_INT, [_VP, _SZ, _I64, _VP, _SZ, _VP, _VP, _VP, _VP, _VP]),
+    "qgemm_gguf_find_kv": (_INT, [_VP, _SZ, ctypes.c_char_p, _VP, _VP, _VP]),
+    "qgemm_gguf_packed_bytes": (_SZ, [_VP, _SZ, _I64]),
+    "qgemm_gguf_pack": (_INT, [_VP, _SZ, _I64, _VP, _SZ, _VP, _VP, _VP]),
     "qgemm_i8_xq_bytes": (_SZ, [_I64, _I64]),
     "qgemm_i8_quantize": (_INT, [_VP, _VP, _VP, _I64, _I64, _INT, _VP]),
     "qgemm_i8_colscale": (_INT, [_INT, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _VP]),
@@ -212,6 +217,97 @@ def pack(fmt: str, enc, N: int, K: int) -> np.ndarray:
         return w4a16_pack(enc["codes"], enc["scales"], None if enc["symmetric"] else enc["zeros"], N, K,
                           enc["group"])
     raise ValueError(fmt)
+
+
+# ---------------------------------------------------------------------------
+# GGUF checkpoints (host)
+# ---------------------------------------------------------------------------
+
+GGML_Q4_K = 12
+GGML_Q6_K = 14
+_GGUF_SCALAR = {0: "<u1", 1: "<i1", 2: "<u2", 3: "<i2", 4: "<u4", 5: "<i4", 6: "<f4", 7: "<u1", 10: "<u8", 11: "<i8",
+                12: "<f8"}
+
+
+def gguf_map(path: str) -> np.ndarray:
+    """The whole file as a read-only uint8 array (memory-mapped)."""
+    return np.memmap(path, dtype=np.uint8, mode="r")
+
+
+def _buf(buf: np.ndarray):
+    b = np.asarray(buf, dtype=np.uint8)
+    if not b.flags.c_contiguous:
+        b = np.ascontiguousarray(b)
+    return b, ctypes.c_void_p(b.ctypes.data), b.nbytes
+
+
+def gguf_header(buf: np.ndarray) -> dict:
+    b, p, n = _buf(buf)
+    v = ctypes.c_uint32()
+    nt, nk, al, do = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("qgemm_gguf_header", lib().qgemm_gguf_header(p, n, ctypes.byref(v), ctypes.byref(nt), ctypes.byref(nk),
+                                                        ctypes.byref(al), ctypes.byref(do)))
+    return dict(version=v.value, n_tensors=nt.value, n_kv=nk.value, alignment=al.value, data_offset=do.value)
+
+
+def gguf_tensors(buf: np.ndarray) -> list:
+    """Every tensor's name, ggml type, dims (row length first), byte offset and size."""
+    b, p, n = _buf(buf)
+    out = []
+    for i in range(gguf_header(b)["n_tensors"]):
+        name = ctypes.create_string_buffer(1024)
+        t, nd = ctypes.c_int32(), ctypes.c_int32()
+        dims = (ctypes.c_int64 * 4)()
+        off, nb = ctypes.c_int64(), ctypes.c_int64()
+        _check("qgemm_gguf_tensor_info", lib().qgemm_gguf_tensor_info(p, n, i, name, 1024, ctypes.byref(t), ctypes.byref(nd),
+                                                                      dims, ctypes.byref(off), ctypes.byref(nb)))
+        out.append(dict(index=i, name=name.value.decode(), type=t.value, dims=tuple(dims[:nd.value]), offset=off.value,
+                        nbytes=nb.value))
+    return out
+
+
+def gguf_kv(buf: np.ndarray, key: str):
+    """The metadata value of `key`: a number, a string, or a list (arrays of
+    numbers or strings); None when the file has no such key."""
+    b, p, n = _buf(buf)
+    t, off, nb = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    st = lib().qgemm_gguf_find_kv(p, n, key.encode(), ctypes.byref(t), ctypes.byref(off), ctypes.byref(nb))
+    if st == -5:
+        return None
+    _check("qgemm_gguf_find_kv", st)
+    raw = bytes(b[off.value:off.value + nb.value])
+
+    def string(r, i):
+        ln = int.from_bytes(r[i:i + 8], "little")
+        return r[i + 8:i + 8 + ln].decode("utf-8", "replace"), i + 8 + ln
+
+    if t.value == 8:
+        return string(raw, 0)[0]
+    if t.value == 9:
+        et = int.from_bytes(raw[0:4], "little")
+        cnt = int.from_bytes(raw[4:12], "little")
+        if et == 8:
+            vals, i = [], 12
+            for _ in range(cnt):
+                s, i = string(raw, i)
+                vals.append(s)
+            return vals
+        return np.frombuffer(raw[12:], dtype=_GGUF_SCALAR[et], count=cnt).tolist()
+    v = np.frombuffer(raw, dtype=_GGUF_SCALAR[t.value], count=1)[0]
+    return bool(v) if t.value == 7 else v.item()
+
+
+def gguf_pack(buf: np.ndarray, index: int):
+    """Tensor `index` (Q4_K or Q6_K, two-dimensional) packed for the GEMMs:
+    (format name, N, K, packed uint8 array)."""
+    b, p, n = _buf(buf)
+    need = int(lib().qgemm_gguf_packed_bytes(p, n, index))
+    out = np.empty(max(need, 16), np.uint8)
+    f, N, K = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check("qgemm_gguf_pack", lib().qgemm_gguf_pack(p, n, index, _np_ptr(out), need, ctypes.byref(f), ctypes.byref(N),
+                                                    ctypes.byref(K)))
+    name = {FMT_Q4K: "q4k", FMT_Q6K: "q6k"}[f.value]
+    return name, N.value, K.value, out[:need]
 
 
 # ---------------------------------------------------------------------------

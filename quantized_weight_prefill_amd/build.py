@@ -44,7 +44,7 @@ def units():
     """(object name, source, extra flags) of every translation unit."""
     out = [("api", "api.hip", []), ("misc", "misc.hip", []), ("misc_grouped", "misc_grouped.hip", []),
            ("misc_i8", "misc_i8.hip", []), ("pack", "pack.cpp", []),
-           ("noalloc", "noalloc.hip", [])]
+           ("noalloc", "noalloc.hip", []), ("gguf", "gguf.cpp", [])]
     for f in FORMATS:
         for d in DTYPES:
             for x in LAYOUTS:

@@ -597,7 +597,7 @@ def test_header_declarations_cite_the_pages():
     decls = _declaration_comments(HEADER)
     assert len(decls) == len(header_functions())
     for name, comment in decls:
-        flat = " ".join(comment.split())
+        flat = " ".join(re.sub(r"\n\s*\*(?!/)", " ", comment).split())  # comment lines joined, their '*' dropped
         if name == "qgemm_gemm_xf_noalloc":  # names the callers it is for instead
             assert "cannot allocate" in flat
             continue
