@@ -452,6 +452,56 @@ def test_gemm_matches_numpy(dtype, shape):
     assert np.array_equal(Ya, Y[r, c]) and np.array_equal(Ba, B[r, c])
 
 
+def _frac_bits(bits: int, dtype: int) -> Fraction:
+    if dtype == oracle.F16:
+        return f16_val(bits)
+    return Fraction(float(np.array(bits << 16, np.uint32).view(np.float32)))
+
+
+def _exact_weight(fmt: str, f: dict, n: int, k: int) -> Fraction:
+    """W[k][n] from the logical fields by the formats' formulas, as an exact rational."""
+    b = k // 256
+    if fmt == "q4k":
+        j = (k % 256) // 32
+        return (f16_val(int(f["d"][n, b])) * int(f["sc"][n, b, j]) * int(f["q"][n, k])
+                - f16_val(int(f["dmin"][n, b])) * int(f["m"][n, b, j]))
+    if fmt == "q6k":
+        j = (k % 256) // 16
+        return f16_val(int(f["d"][n, b])) * int(f["s"][n, b, j]) * (int(f["q"][n, k]) - 32)
+    g = k // f["group"]
+    return f16_val(int(f["scales"][g, n])) * (int(f["codes"][n, k]) - int(f["zeros"][g, n]))
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+@pytest.mark.parametrize("fmt,sym", [("q4k", False), ("q6k", False), ("w4a16", False), ("w4a16", True)])
+def test_gemm_smallest_shapes_exact_rationals(fmt, sym, dtype):
+    """The smallest shapes of the brute-force grid end to end in exact
+    arithmetic: every weight from its fields by the format's formula, rounded
+    once by the brute-force nearest search, must equal the oracle's unpack bit
+    for bit, and every output of the oracle's fp64 product must lie within
+    fp64 summation error of the exact rational sum of X.W."""
+    rng = np.random.default_rng(71 + dtype)
+    N, K = 16, 256 if fmt != "w4a16" else 128
+    f = synth.weight_fields(fmt, rng, N, K, 64 if fmt == "w4a16" else 128, sym)
+    W = oracle.dequant(fmt, synth.encode(fmt, f), N, K, dtype)
+    Wq = [[None] * N for _ in range(K)]
+    for k in range(K):
+        for n in range(N):
+            want = _expect(_exact_weight(fmt, f, n, k), dtype)
+            assert int(W[k, n]) == want, (fmt, k, n)
+            Wq[k][n] = _frac_bits(want, dtype)
+    for M in (1, 2, 3):
+        X = synth.activations(rng, M, K, dtype)
+        Y, B = oracle.gemm(X, W, dtype)
+        for m in range(M):
+            xs = [_frac_bits(int(X[m, k]), dtype) for k in range(K)]
+            for n in range(N):
+                exact = sum(xs[k] * Wq[k][n] for k in range(K))
+                bound = sum(abs(xs[k] * Wq[k][n]) for k in range(K))
+                assert abs(Fraction(float(Y[m, n])) - exact) <= Fraction(K + 2, 2 ** 53) * bound, (fmt, m, n)
+                assert abs(Fraction(float(B[m, n])) - bound) <= Fraction(K + 2, 2 ** 53) * bound
+
+
 def test_gemm_special_cases():
     rng = np.random.default_rng(10)
     K, N = 64, 24

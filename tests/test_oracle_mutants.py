@@ -40,7 +40,12 @@ MUTANTS = [
     ("gemm reversed K walk", "acc += xr[k] * wr[k];", "acc += xr[k] * wr[K - 1 - k];",
      ["test_gemm_matches_numpy"]),
     ("gemm bound signed", "bnd += fabs(xr[k]) * fabs(wr[k]);", "bnd += xr[k] * fabs(wr[k]);",
-     ["test_gemm_matches_numpy"]),
+     ["test_gemm_matches_numpy", "test_gemm_smallest_shapes_exact_rationals"]),
+    ("gemm accumulates in binary32", "acc += xr[k] * wr[k];", "acc = (float)(acc + xr[k] * wr[k]);",
+     ["test_gemm_smallest_shapes_exact_rationals"]),
+    ("gemm drops the last k", "for (int64_t k = 0; k < K; k++) {\n                acc += xr[k] * wr[k];",
+     "for (int64_t k = 0; k < K - 1; k++) {\n                acc += xr[k] * wr[k];",
+     ["test_gemm_smallest_shapes_exact_rationals", "test_gemm_matches_numpy"]),
     ("ties away from zero", "if (rem > half || (rem == half && (q & 1))) q++;", "if (rem >= half) q++;",
      ["test_rn_f16_matches_numpy"]),
     ("fragment-major halves and rows transposed", "((k / 8) % 2 * 32 + m % 32) * 8", "((m % 32) * 2 + (k / 8) % 2) * 8",
@@ -97,6 +102,8 @@ def test_mutant_is_caught(tmp_path, monkeypatch, name, old, new, catchers):
                 else:
                     if "shape" in fn.__code__.co_varnames[:fn.__code__.co_argcount]:
                         fn(p, (5, 48, 512))
+                    elif fn.__code__.co_varnames[:fn.__code__.co_argcount] == ("fmt", "sym", "dtype"):
+                        fn("q4k", False, p)
                     else:
                         fn(p)
             except (AssertionError, ValueError):
