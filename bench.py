@@ -161,6 +161,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-arm comparison")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the comparison with the vendor dense GEMM on the unpacked weights")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8-activation arm")
     ap.add_argument("--pool-mb", type=float, default=640.0,
                     help="every GEMM rotates through copies of its weights totalling at least this many MB, so the "
@@ -378,6 +380,7 @@ def main() -> int:
     roof["kernel"] = f"{gd['label']} ({gd['fmt']} M={gd['M']} K={gd['K']} N={gd['N']}, rung {gd['rung']})"
     roof["traffic"] = measured_traffic(f"{args.workload}/{gd['label']}")
     staged = None if args.no_staged else staged_arm(gd, call)
+    dense = None if args.no_dense else dense_reference(gemms, call)
     int8 = None if args.no_int8 else int8_arm(gemms, wl, lib, sp, timer, args)
     ceiling = None if args.no_ceiling else mfma_ceiling(gd["dt"])
     if ceiling is not None and roof["bound"] == "mfma":
@@ -420,6 +423,8 @@ def main() -> int:
         out["mfma_ceiling"] = ceiling
     if staged is not None:
         out["staged_arm"] = staged
+    if dense is not None:
+        out["dense_reference"] = dense
     if int8 is not None:
         out["int8_arm"] = int8
     if args.only is not None or args.rung >= 0:
@@ -435,11 +440,13 @@ def main() -> int:
     return 0
 
 
-def gpu_state(run_step, steps: int = 300, every: int = 10) -> dict:
+def gpu_state(run_step, steps: int = 2400, every: int = 80) -> dict:
     """Shader clock, memory clock and temperatures while the step runs: the
     step is queued `every` steps at a time and the GPU's metrics table is read
     between the batches (the GPU is busy with the queued work meanwhile), over
-    `steps` steps after the timed region.  Read through amdsmi; on a host
+    `steps` steps after the timed region (about a second of the layer step:
+    the metrics table refreshes on its own period, so a window of a few
+    milliseconds would repeat one reading).  Read through amdsmi; on a host
     without it the reason is recorded instead."""
     import torch
 
@@ -470,6 +477,7 @@ def gpu_state(run_step, steps: int = 300, every: int = 10) -> dict:
             "power_w": ("current_socket_power",), "gfx_activity_pct": ("average_gfx_activity",)}
     got = {k: [] for k in keys}
     err = None
+    t0 = time.perf_counter()
     for i in range(steps // every):
         for _ in range(every):
             run_step()
@@ -486,6 +494,7 @@ def gpu_state(run_step, steps: int = 300, every: int = 10) -> dict:
                     got[k].append(float(np.mean(valid(m[n]))))
                     break
     torch.cuda.synchronize()
+    window_ms = (time.perf_counter() - t0) * 1e3
     try:
         amdsmi.amdsmi_shut_down()
     except Exception:
@@ -494,6 +503,7 @@ def gpu_state(run_step, steps: int = 300, every: int = 10) -> dict:
            for k, v in got.items()}
     out["format"] = "[min, mean, max] over the samples read while the step ran (amdsmi gpu_metrics; sclk averaged over XCDs)"
     out["samples"] = max((len(v) for v in got.values()), default=0)
+    out["window_ms"] = round(window_ms, 1)
     if err:
         out["error"] = err
     return out
@@ -698,6 +708,42 @@ def staged_arm(g, call, reps: int = 20) -> dict:
             "timing": "arms interleaved, 5 rounds of 20 launches each, median",
             "note": "staged = unpack pass (reads packed W, writes 2 B/weight) + the same 128x128 kernel reading "
                     "2 B/weight; its Y equals the fused 128x128 rung's Y bit for bit"}
+
+
+def dense_reference(gemms, call, reps: int = 20) -> dict:
+    """Each GEMM of the step fused (its rung and activation layout as in the
+    step) against the vendor library's dense GEMM on the same shape: W
+    unpacked once by the library's own dequant to fp16/bf16, then
+    torch.matmul (hipBLASLt) of row-major X by it, its dense copies rotating
+    through >= 640 MB as the packed ones do.  Arms interleaved, five rounds
+    of 20 launches, medians.  A calibration of what the chip reaches on these
+    shapes without any unpacking, not a path of the library."""
+    import torch
+
+    rows = []
+    for g in gemms:
+        grp = g["group"] if g["fmt"] == "w4a16" else 0
+        w = qg.dequant(g["fmt"], g["pool"][0], g["N"], g["K"], g["dt"], group=grp, has_zp=not g["sym"])
+        copies = max(1, -(-int(640e6) // (w.numel() * w.element_size())))
+        pool = [w] + [w.clone() for _ in range(copies - 1)]
+        y = torch.empty((g["M"], g["N"]), dtype=w.dtype, device="cuda")
+        turn = [0]
+
+        def dense(g=g, pool=pool, y=y):
+            turn[0] += 1
+            torch.matmul(g["x"], pool[turn[0] % len(pool)], out=y)
+
+        t = interleaved({"fused": lambda g=g: call(g), "dense": dense}, reps)
+        flops = 2.0 * g["M"] * g["N"] * g["K"]
+        rows.append({"gemm": g["label"], "shape": f"{g['fmt']} M={g['M']} K={g['K']} N={g['N']}",
+                     "fused_rung": g["rung"], "fused_ms": round(t["fused"], 5), "dense_ms": round(t["dense"], 5),
+                     "fused_tflops": round(flops / t["fused"] / 1e9, 1), "dense_tflops": round(flops / t["dense"] / 1e9, 1),
+                     "dense_over_fused_time": round(t["dense"] / t["fused"], 3)})
+        del pool, w, y
+        torch.cuda.empty_cache()
+    return {"what": "vendor dense GEMM (torch.matmul / hipBLASLt) on the unpacked weights, same shapes, "
+                    "weights rotating, interleaved with the fused launches: a calibration, not a library path",
+            "per_gemm": rows}
 
 
 def int8_arm(gemms, wl, lib, sp, timer, args) -> dict:
