@@ -161,6 +161,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-arm comparison")
+    ap.add_argument("--no-gpu-state", action="store_true",
+                    help="skip the clock/temperature window (~2400 extra steps; for profiler runs)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the comparison with the vendor dense GEMM on the unpacked weights")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8-activation arm")
@@ -333,7 +335,7 @@ def main() -> int:
             if g["prep"] is not None:
                 call_prep(g["prep"])
             call(g)
-    state = gpu_state(run_step)
+    state = None if args.no_gpu_state else gpu_state(run_step)
 
     for j, g in enumerate(gemms):
         ms = gemm_ms[j]
