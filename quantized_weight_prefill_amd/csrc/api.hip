@@ -19,7 +19,8 @@ namespace {
 const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-n",   "direct-wide",
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
                                             "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
-                                            "mfma32-192x96-k2",  "mfma32-192x64-k2",  "mfma32-64x64-sk"};
+                                            "mfma32-192x96-k2",  "mfma32-192x64-k2",  "mfma32-64x64-sk",
+                                            "mfma32-64x32-k4"};
 
 // A one-dimensional launch of gx workgroups of `threads` threads fits when
 // gx is at most 2^31-1 and the work-items along x at most 2^32-1.
@@ -74,14 +75,16 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M128N160:
     case RUNG_M64_K4:
     case RUNG_M64_SK:
+    case RUNG_M64N32_K4:
     case RUNG_M352N96:
     case RUNG_M192N96_K2:
     case RUNG_M192N64_K2: {
         const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2;
         const bool r192 = rung == RUNG_M192N96_K2 || rung == RUNG_M192N64_K2;
-        const bool r64 = rung == RUNG_M64_K4 || rung == RUNG_M64_SK;
+        const bool r64 = rung == RUNG_M64_K4 || rung == RUNG_M64_SK || rung == RUNG_M64N32_K4;
         pl.rows = rung == RUNG_M16_256 ? 256 : r64 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192 : 128;
-        pl.cols = rung == RUNG_M128N160 ? 160 : (r64 || rung == RUNG_M192N64_K2) ? 64 : n96 ? 96 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64N32_K4 ? 32
+                  : (r64 || rung == RUNG_M192N64_K2) ? 64 : n96 ? 96 : 128;
         pl.kw = ((rung == RUNG_M128_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
         if (r64) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
         pl.waves = rung == RUNG_M16_256 ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11
@@ -134,6 +137,8 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    Q4_K) four panels and all rows per wave (each activation fragment feeds
 //    four panels), 49..64 rows of Q4_K and 33..64 of W4A16 and Q6_K 64x64
 //    streaming tiles with K split four ways;
+//  * 65..128 rows over 129..256 panels: 64x32 tiles with K split four ways
+//    (not fp16 Q4_K on row-major activations, where direct-wide leads);
 //  * fewer than 128 tiles of 128x128: the split rung where split_pays, else
 //    the direct kernels, 64x64 K-split tiles or (fragment-major) 192x64
 //    K-split tiles, by the round model of mid_m_rung;
@@ -253,6 +258,19 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
     // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
+    // 65..128 rows over 129..256 panels (N = 2049..4096): 64x32 tiles, two
+    // 32x32 waves per K group, K split over four groups (two row tiles by
+    // N/32 column tiles: one workgroup per CU at N = 4096).  Measured on
+    // MI355X against the rungs this range had before, weights rotating, both
+    // dtypes and activation layouts: N = 4096, K = 4096 at M = 65..128 Q4_K
+    // 11.0-11.4 against 14.8-15.7 us (64x64 split across workgroups), Q6_K
+    // 13.2-14.0 against 17.3-18.4, W4A16 10.7-11.4 against 14.3-15.3; K = 12288
+    // Q6_K 35-37 against 44-47 us; N = 3072 every format 0.6-0.75 of the former
+    // time.  It loses over 2048 columns and from 6144 (the direct kernels and
+    // the 192x64 tiles stay ahead there), and to direct-wide for fp16 Q4_K on
+    // row-major activations (20.8 against 19.1 us at N = 4096).
+    if (M <= 128 && np > 128 && np <= 256 && !(xl == X_ROW && fmt == FMT_Q4K && dtype == DT_F16))
+        return RUNG_M64N32_K4;
     if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
     if (t128 < 128) return mid_m_rung(fmt, M, np, xl == X_FRAG && (K / kChunk) % 2 == 0);
     // on fragment-major activations, a 192-row tile with K split over two

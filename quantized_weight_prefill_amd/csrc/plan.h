@@ -27,7 +27,8 @@ enum Rung {
     RUNG_M192N96_K2 = 9,  // 32x32x16 MFMA: 192x96, K split over two 6-wave groups (three waves per SIMD)
     RUNG_M192N64_K2 = 10, // 32x32x16 MFMA: 192x64, K split over two 6-wave groups
     RUNG_M64_SK = 11,     // 32x32x16 MFMA: 64x64, K split over four groups and across workgroups
-    RUNG_COUNT = 12
+    RUNG_M64N32_K4 = 12,  // 32x32x16 MFMA: 64x32, 2 waves of 32x32, K split over four groups
+    RUNG_COUNT = 13
 };
 
 enum I8Rung {

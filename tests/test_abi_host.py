@@ -312,6 +312,8 @@ def test_ladder_sweep(fmt, dtype):
             elif M <= 64:
                 assert info["name"].startswith("direct-") or (
                     info["name"] in ("mfma32-64x64-k4", "mfma32-64x64-sk") and M > 32)
+            if info["name"] == "mfma32-64x32-k4":
+                assert 64 < M <= 128 and 2048 < N <= 4096
             if info["name"] == "mfma32-64x64-sk":
                 # slices across workgroups: whole chunks for every K group of every slice
                 assert (K // info["k_step"]) % info["k_split"] == 0 and info["k_split"] % info["waves"] == 0
@@ -342,12 +344,17 @@ def test_ladder_mid_m_round_model():
         assert qg.select_rung(fmt, M, 4096, K)["name"] == row, (fmt, M)
     # the 64x64 K-split tile stays where one round of it beats one of 192x64
     assert qg.select_rung_xf("q6k", 256, 4096, 12288)["name"] == "mfma32-64x64-k4"
-    # Q6_K over few panels, 33..128 rows: row-major keeps one panel and all rows per wave,
-    # fragment-major splits 64x64 tiles four ways across workgroups (M = 64: 24.2 against 28.1 us)
-    for M in (33, 64, 80, 128):
+    # Q6_K over few panels, 33..64 rows: row-major keeps one panel and all rows per wave,
+    # fragment-major splits 64x64 tiles four ways across workgroups (M = 64: 24.2 against 28.1 us);
+    # from 65 rows both take 64x32 tiles with K split four ways (M = 96: 36 against 45 us, 56
+    # against 81 us on row-major X)
+    for M in (33, 64):
         assert qg.select_rung("q6k", M, 4096, 12288)["name"] == "direct-small-m", M
         sk = qg.select_rung_xf("q6k", M, 4096, 12288)
         assert sk["name"] == "mfma32-64x64-sk" and sk["k_split"] == 16, (M, sk)
+    for M in (65, 80, 128):
+        for sel in (qg.select_rung, qg.select_rung_xf):
+            assert sel("q6k", M, 4096, 12288)["name"] == "mfma32-64x32-k4", (M, sel.__name__)
     assert qg.select_rung_xf("q6k", 150, 4096, 12288)["name"] == "mfma32-64x64-k4"
     # up to 16 rows: one panel per wave, except over >= 1536 panels (merged gate/up), where four
     # panels per wave win (M = 8, N = 24576: Q4_K 20.7 against 23.8 us); both layouts
@@ -363,18 +370,25 @@ def test_ladder_mid_m_round_model():
     # the split rung at the down projection's shape (fragment-major X): fp16 Q6_K and W4A16 33..128
     # rows, Q4_K 49..64 (from 96 rows direct-wide); bf16 every format from 33 rows
     for fmt, M, want in [("q6k", 40, "mfma32-64x64-sk"), ("w4a16", 40, "mfma32-64x64-sk"),
-                         ("w4a16", 64, "mfma32-64x64-sk"), ("w4a16", 128, "mfma32-64x64-sk"),
-                         ("q4k", 64, "mfma32-64x64-sk"), ("q4k", 96, "direct-wide"), ("q4k", 32, "direct-small-m")]:
+                         ("w4a16", 64, "mfma32-64x64-sk"), ("w4a16", 128, "mfma32-64x32-k4"),
+                         ("q4k", 64, "mfma32-64x64-sk"), ("q4k", 96, "mfma32-64x32-k4"), ("q4k", 32, "direct-small-m")]:
         assert qg.select_rung_xf(fmt, M, 4096, 12288)["name"] == want, (fmt, M)
-    for fmt, M, want in [("q4k", 96, "mfma32-64x64-sk"), ("q4k", 48, "mfma32-64x64-sk"),
+    for fmt, M, want in [("q4k", 96, "mfma32-64x32-k4"), ("q4k", 48, "mfma32-64x64-sk"),
                          ("w4a16", 40, "mfma32-64x64-sk"), ("q4k", 32, "direct-small-m")]:
         assert qg.select_rung_xf(fmt, M, 4096, 12288, qg.BF16)["name"] == want, (fmt, M)
-    # K = 4096 over 4096 columns: two slices from 65 rows in both dtypes; not over 1024 or 6144 columns
+    # K = 4096 over 4096 columns: 64x32 tiles with K split four ways at 65..128 rows in both
+    # dtypes (Q4_K M = 96: 11.1 against 15.0 us for two slices of 64x64 tiles); not over 2048,
+    # 1024 or 6144 columns, nor above 128 rows; fp16 Q4_K on row-major X keeps direct-wide
     for dt in (qg.F16, qg.BF16):
         for fmt in ("q4k", "q6k", "w4a16"):
-            sk = qg.select_rung_xf(fmt, 96, 4096, 4096, dt)
-            assert sk["name"] == "mfma32-64x64-sk" and sk["k_split"] == 8, (fmt, dt, sk)
+            for M in (65, 96, 128):
+                assert qg.select_rung_xf(fmt, M, 4096, 4096, dt)["name"] == "mfma32-64x32-k4", (fmt, dt, M)
+                assert qg.select_rung_xf(fmt, M, 3072, 4096, dt)["name"] == "mfma32-64x32-k4", (fmt, dt, M)
+                row = qg.select_rung(fmt, M, 4096, 4096, dt)["name"]
+                assert (row == "mfma32-64x32-k4") == (fmt != "q4k" or dt == qg.BF16), (fmt, dt, M, row)
             assert qg.select_rung_xf(fmt, 64, 4096, 4096, dt)["name"] == "direct-small-m", (fmt, dt)
+            for M, N in ((160, 4096), (96, 2048), (128, 1024), (96, 6144)):
+                assert qg.select_rung_xf(fmt, M, N, 4096, dt)["name"] != "mfma32-64x32-k4", (fmt, dt, M, N)
             assert qg.select_rung_xf(fmt, 128, 1024, 4096, dt)["name"] != "mfma32-64x64-sk", (fmt, dt)
             assert qg.select_rung_xf(fmt, 96, 6144, 4096, dt)["name"] != "mfma32-64x64-sk", (fmt, dt)
     # Q6_K over many panels, 33..64 rows: 64x64 tiles unpack each weight once for all rows

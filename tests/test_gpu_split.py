@@ -39,12 +39,16 @@ def test_split_rung_forced(fmt, M, N, K, dtype, slices):
 
 @pytest.mark.parametrize("M", [40, 64, 96, 128])
 def test_split_rung_auto_down_projection(M):
-    """Q6_K 12288 -> 4096 at 33..128 rows on fragment-major activations: the
-    ladder picks the split rung (four slices of 24 chunks, each split over
-    four K groups)."""
+    """Q6_K 12288 -> 4096 on fragment-major activations through the ladder:
+    at 33..64 rows the split rung (four slices of 24 chunks, each split over
+    four K groups), at 65..128 rows the 64x32 tiles with K split four ways
+    inside the workgroup."""
     N, K = 4096, 12288
     sel = qg.select_rung_xf("q6k", M, N, K, qg.F16)
-    assert sel["name"] == "mfma32-64x64-sk" and sel["k_split"] == 16, sel
+    if M <= 64:
+        assert sel["name"] == "mfma32-64x64-sk" and sel["k_split"] == 16, sel
+    else:
+        assert sel["name"] == "mfma32-64x32-k4" and sel["k_split"] == 4, sel
     c = Case("q6k", M, N, K, qg.F16, seed=720 + M)
     print(f"split auto q6k M={M} N={N} K={K}", flush=True)
     y = from_device(c.run_xf(-1))
