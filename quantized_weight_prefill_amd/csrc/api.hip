@@ -20,7 +20,7 @@ const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
                                             "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
                                             "mfma32-192x96-k2",  "mfma32-192x64-k2",  "mfma32-64x64-sk",
-                                            "mfma32-64x32-k4"};
+                                            "mfma32-64x32-k4",   "mfma32-128x64-k2",  "mfma32-96x32-k4"};
 
 // A one-dimensional launch of gx workgroups of `threads` threads fits when
 // gx is at most 2^31-1 and the work-items along x at most 2^32-1.
@@ -76,19 +76,23 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M64_K4:
     case RUNG_M64_SK:
     case RUNG_M64N32_K4:
+    case RUNG_M128N64_K2:
+    case RUNG_M96N32_K4:
     case RUNG_M352N96:
     case RUNG_M192N96_K2:
     case RUNG_M192N64_K2: {
         const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2;
         const bool r192 = rung == RUNG_M192N96_K2 || rung == RUNG_M192N64_K2;
         const bool r64 = rung == RUNG_M64_K4 || rung == RUNG_M64_SK || rung == RUNG_M64N32_K4;
-        pl.rows = rung == RUNG_M16_256 ? 256 : r64 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192 : 128;
-        pl.cols = rung == RUNG_M128N160 ? 160 : rung == RUNG_M64N32_K4 ? 32
-                  : (r64 || rung == RUNG_M192N64_K2) ? 64 : n96 ? 96 : 128;
-        pl.kw = ((rung == RUNG_M128_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
-        if (r64) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
-        pl.waves = rung == RUNG_M16_256 ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M352N96 ? 11
-                   : r192 ? 6 * pl.kw : 4 * pl.kw;
+        const bool k4 = r64 || rung == RUNG_M96N32_K4;  // K split over up to four groups
+        pl.rows = rung == RUNG_M16_256 ? 256 : r64 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192
+                  : rung == RUNG_M96N32_K4 ? 96 : 128;
+        pl.cols = rung == RUNG_M128N160 ? 160 : (rung == RUNG_M64N32_K4 || rung == RUNG_M96N32_K4) ? 32
+                  : (r64 || rung == RUNG_M192N64_K2 || rung == RUNG_M128N64_K2) ? 64 : n96 ? 96 : 128;
+        pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M128N64_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
+        if (k4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
+        pl.waves = rung == RUNG_M16_256 ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M96N32_K4 ? 3 * pl.kw
+                   : rung == RUNG_M352N96 ? 11 : r192 ? 6 * pl.kw : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
         if (!launch_fits(tn * tm, 64 * pl.waves)) return QGEMM_ERR_SHAPE;
@@ -137,11 +141,11 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    Q4_K) four panels and all rows per wave (each activation fragment feeds
 //    four panels), 49..64 rows of Q4_K and 33..64 of W4A16 and Q6_K 64x64
 //    streaming tiles with K split four ways;
-//  * 65..128 rows over 129..256 panels: 64x32 tiles with K split four ways
-//    (not fp16 Q4_K on row-major activations, where direct-wide leads);
-//  * fewer than 128 tiles of 128x128: the split rung where split_pays, else
-//    the direct kernels, 64x64 K-split tiles or (fragment-major) 192x64
-//    K-split tiles, by the round model of mid_m_rung;
+//  * above 64 rows, the round model of round_model_rung over the direct
+//    kernels and the streaming tiles that run one workgroup per CU (64x32,
+//    96x32 and 64x64 with K split four ways, 128x64 and 192x64 with K split
+//    two ways), whenever its cheapest rung is one of those and not one of the
+//    large tiles below;
 //  * the 8-wave 256x128 tile on 16x16x32 MFMAs (each weight unpacked once
 //    for 256 rows) when the occupancy model below has it finish no later
 //    than the 128-row tiles;
@@ -167,52 +171,96 @@ double stream_cost(long long M, long long np, int cols)
     return t * cols / 128.0;
 }
 
-// Between decode-adjacent M and 128 tiles of 128x128 three rungs compete:
-// one panel and up to 64 rows per wave (direct-small-m), four panels and 48
-// rows per wave (direct-wide) and 64x64 streaming tiles with K split four
-// ways, and on fragment-major activations with an even chunk count a fourth,
-// the 192x64 tile with K split over two 6-wave groups.  Their workgroups run
-// in rounds of one per CU; a round costs a constant per rung, measured on
-// MI355X with Q4_K at K = 4096 (M = 80..384, N = 1024..12288): 8, 15.5, 17
-// and 27 microseconds.  The 48-row direct variant spills for Q6_K and W4A16
-// and is left out for them.  (Q6_K at M = 300..384, N = 4096: 192x64 72-73
-// against 91 us for the 64x64 tiles.)
-// The split rung over few panels (N = 4096) on fragment-major activations:
-// one panel and all rows per wave reads the activations once per panel, the
-// 64x64 tiles split across workgroups read a slice of them.  Measured on
-// MI355X (weights rotating):
-//  * K = 12288 (four slices): Q6_K and W4A16, and every format in bf16,
-//    from 33 rows (Q6_K M = 64 24.2 against 28.1 us; W4A16 M = 48..128
-//    18.5-33.8 against 20.4-38.7; bf16 Q4_K M = 96 33.3 against 42.2 on
-//    direct-wide); fp16 Q4_K at 49..64 only (from 96 rows direct-wide leads,
-//    33.0 against 34.6 us);
-//  * K = 4096 (two slices): 65..128 rows in both dtypes (W4A16 M = 96: 14.2
-//    against 15.2 us fp16, 13.7 against 15.5 bf16), while the two slices'
-//    tiles fit one workgroup per CU (at N = 6144 they lose, 28.3 against
-//    15.8 us).
-// Over at most 128 panels the split grid fills a quarter of the CUs or less
-// and one panel per wave stays ahead (N = 1024, M = 96..128: 8.3-9.4
-// against 12.5-14.7 us).
+// The split rung at 33..64 rows over 129..256 panels (N = 2049..4096) on
+// fragment-major activations: one panel and all rows per wave reads the
+// activations once per panel, the 64x64 tiles split across workgroups read a
+// slice of them.  Measured on MI355X (weights rotating), K = 12288 (four
+// slices): Q6_K and W4A16, and every format in bf16, from 33 rows (Q6_K M =
+// 64 24.2 against 28.1 us; W4A16 M = 48 18.5 against 20.4), fp16 Q4_K at
+// 49..64 only.  Shorter K leaves too few chunks per slice.  (Above 64 rows
+// the round model's tiles beat it on fragment-major activations; on
+// row-major ones it would win at 65..128 rows over N <= 4096, by 3-25%, but
+// the row-major ladder serves the format entry points, which take no
+// workspace.)
 bool split_pays(int fmt, int dtype, long long M, long long np, long long K, int xl)
 {
-    const long long nch = K / kChunk, tn = (np + 3) / 4, tm = (M + 63) / 64;
-    if (xl != X_FRAG || np > 256 || np <= 128 || M > 128) return false;
-    if (nch >= 32 && nch < 64 && nch % 8 == 0) return M > 64 && tn * tm * 2 <= kCUs;
+    const long long nch = K / kChunk;
+    if (xl != X_FRAG || np > 256 || np <= 128 || M > 64) return false;
     if (nch < 64 || nch % 16 != 0) return false;
     if (dtype == DT_BF16 || fmt != FMT_Q4K) return M > 32;
-    return M > 48 && M <= 64;
+    return M > 48;
 }
 
-int mid_m_rung(int fmt, long long M, long long np, bool k2_192)
+// Cost of one full round of a rung's workgroups (256 CUs, `per_cu`
+// workgroups on each at once), in microseconds at K = 4096, by activation
+// layout (row-major, fragment-major) and format (Q4_K, Q6_K, W4A16).
+// Measured on MI355X with every rung forced, weights rotating through 320 MB:
+// medians of time / rounds over M = 65..512 and N = 1024..12288, both dtypes
+// (the four-panel direct kernel runs about 15% faster in fp16 on Q4_K and
+// has a row per dtype; its 48-row variant spills for Q6_K and W4A16, and
+// the zero entries leave it out for them: 64x64 tiles beat it there by
+// 6-10% where the medians tie).  Every rung's time grows with K alike, so
+// the comparison holds at other K.  `large` marks the tiles whose rules
+// follow in select_rung: when one of them is cheapest, the model defers to
+// those.
+struct RoundCost {
+    int rung, per_cu, dtype, large;  // dtype -1: both
+    float us[2][3];
+};
+constexpr RoundCost kRoundCost[] = {
+    {RUNG_M64N32_K4, 1, -1, 0, {{18.8f, 20.5f, 18.5f}, {9.9f, 11.3f, 8.7f}}},
+    {RUNG_M96N32_K4, 1, -1, 0, {{27.8f, 29.6f, 27.3f}, {13.6f, 15.6f, 12.9f}}},
+    {RUNG_M64_K4, 1, -1, 0, {{22.4f, 25.1f, 21.7f}, {16.9f, 19.4f, 15.7f}}},
+    {RUNG_M128N64_K2, 1, -1, 0, {{35.2f, 37.2f, 34.8f}, {20.4f, 22.1f, 19.1f}}},
+    {RUNG_M192N64_K2, 1, -1, 0, {{45.5f, 48.0f, 44.9f}, {26.2f, 29.1f, 25.0f}}},
+    {RUNG_SMALL_M, 1, -1, 0, {{15.8f, 16.2f, 15.6f}, {7.3f, 7.9f, 6.8f}}},
+    {RUNG_WIDE, 1, DT_F16, 0, {{18.3f, 0.0f, 0.0f}, {14.3f, 0.0f, 0.0f}}},
+    {RUNG_WIDE, 1, DT_BF16, 0, {{20.8f, 0.0f, 0.0f}, {16.9f, 0.0f, 0.0f}}},
+    {RUNG_M128, 2, -1, 1, {{38.9f, 43.0f, 36.9f}, {39.2f, 42.3f, 35.7f}}},
+    {RUNG_M128_K2, 1, -1, 1, {{38.9f, 43.8f, 37.8f}, {33.6f, 37.8f, 32.0f}}},
+    {RUNG_M128N160, 2, -1, 1, {{52.0f, 92.2f, 47.0f}, {53.2f, 92.2f, 48.1f}}},
+    {RUNG_M16_256, 1, -1, 1, {{52.5f, 56.7f, 50.2f}, {49.1f, 52.5f, 48.4f}}},
+    {RUNG_M192N96_K2, 1, -1, 1, {{49.9f, 51.0f, 46.1f}, {32.4f, 34.5f, 30.5f}}},
+};
+
+// The rung the round model finishes first, or -1 when that is one of the
+// large tiles; on a tie the earlier entry of the table, a streaming tile
+// before a direct kernel (Q4_K at M = 100, N = 5120, K = 13824, bf16: 64x64
+// tiles 46.0 against 54.5 us for direct-wide, whose costs tie).  A K-split
+// rung takes part only with an even chunk count: with an odd one it runs a
+// single K group.  With two chunks over (K = 11008: 86 chunks) the four-way
+// tiles run two K groups and measured no slower per round than with four
+// (64x32 tiles at M = 100, N = 4096: 44-50 us, the K = 12288 times scaled
+// to that K).  Measured against the fastest forced rung over the sweep
+// above: 1.002-1.005 of it on average, where the earlier rules (fixed
+// thresholds and a Q4_K-only round model) came to 1.06-1.13; e.g. M = 320,
+// N = 1024 on fragment-major Q4_K: 64x32 tiles 10.5 against 17.1 us for
+// direct-wide; M = 129..192, N = 4096: 96x32 tiles 13.8-14.9 against
+// 17.2-18.8; M = 320..512, N = 4096: 128x64 tiles 22.7-26.0 against
+// 28.0-32.5 for 192x64; M = 65..128, N = 12288: 128x64 tiles 0.58-0.86 of
+// the former time.
+int round_model_rung(int fmt, long long M, long long N, long long K, int xl, int dtype)
 {
-    const long long g64 = (M + 63) / 64, g48 = (M + 47) / 48, q = (np + 3) / 4;
-    const auto rounds = [](long long wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
-    const double small = 8.0 * rounds(np * g64), k4 = 17.0 * rounds(q * g64);
-    const double wide = fmt == FMT_Q4K ? 15.5 * rounds(q * g48) : 1e30;
-    const double t192 = k2_192 ? 27.0 * rounds(((M + 191) / 192) * q) : 1e30;
-    if (t192 < wide && t192 < small && t192 < k4) return RUNG_M192N64_K2;
-    if (wide <= small && wide <= k4) return RUNG_WIDE;
-    return small <= k4 ? RUNG_SMALL_M : RUNG_M64_K4;
+    double best = 1e30;
+    int pick = -1, large = 1;
+    for (const RoundCost &rc : kRoundCost) {
+        const float us = rc.us[xl == X_FRAG][fmt];
+        if ((rc.dtype >= 0 && rc.dtype != dtype) || us <= 0.0f) continue;
+        Plan pl;
+        if (make_plan(rc.rung, M, N, K, pl) != QGEMM_OK) continue;
+        if (pl.kw == 1 && rc.rung != RUNG_SMALL_M && rc.rung != RUNG_WIDE && rc.rung != RUNG_M128 &&
+            rc.rung != RUNG_M128N160 && rc.rung != RUNG_M16_256)
+            continue;  // a K-split tile left with one K group
+        const long long wgs = (long long)pl.grid.x * pl.grid.y * pl.grid.z;
+        const long long per_round = (long long)kCUs * rc.per_cu;
+        const double cost = us * (double)((wgs + per_round - 1) / per_round);
+        if (cost < best) {
+            best = cost;
+            pick = rc.rung;
+            large = rc.large;
+        }
+    }
+    return large ? -1 : pick;
 }
 
 int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtype = DT_F16)
@@ -253,26 +301,12 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
         // unpacked once) beats four panels of 16 rows up to 64 rows
         return RUNG_SMALL_M;
     }
+    if (const int r = round_model_rung(fmt, M, N, K, xl, dtype); r >= 0) return r;
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     // occupancy model: a 256x128 tile counts as two 128x128 tiles; the
     // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
-    // 65..128 rows over 129..256 panels (N = 2049..4096): 64x32 tiles, two
-    // 32x32 waves per K group, K split over four groups (two row tiles by
-    // N/32 column tiles: one workgroup per CU at N = 4096).  Measured on
-    // MI355X against the rungs this range had before, weights rotating, both
-    // dtypes and activation layouts: N = 4096, K = 4096 at M = 65..128 Q4_K
-    // 11.0-11.4 against 14.8-15.7 us (64x64 split across workgroups), Q6_K
-    // 13.2-14.0 against 17.3-18.4, W4A16 10.7-11.4 against 14.3-15.3; K = 12288
-    // Q6_K 35-37 against 44-47 us; N = 3072 every format 0.6-0.75 of the former
-    // time.  It loses over 2048 columns and from 6144 (the direct kernels and
-    // the 192x64 tiles stay ahead there), and to direct-wide for fp16 Q4_K on
-    // row-major activations (20.8 against 19.1 us at N = 4096).
-    if (M <= 128 && np > 128 && np <= 256 && !(xl == X_ROW && fmt == FMT_Q4K && dtype == DT_F16))
-        return RUNG_M64N32_K4;
-    if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
-    if (t128 < 128) return mid_m_rung(fmt, M, np, xl == X_FRAG && (K / kChunk) % 2 == 0);
     // on fragment-major activations, a 192-row tile with K split over two
     // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
     // and cover M with no more rows than 128-row tiles: 64 columns wide when
@@ -307,6 +341,12 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
     // fragment-major activations also whenever it has 512 tiles, and for
     // Q6_K, whose unpack costs most, from one full round of them (M = 1024,
     // N = K = 12288: 363.9 against 400.4 us for 128x128)
+    // (on row-major activations Q6_K takes one round of 192x96 K-split tiles
+    // instead where they fit: M = 300..384, N = 11008..12288: 61-66 against
+    // 73-76 us; for the other formats, and elsewhere, they lose by 5-50%)
+    if (c256 <= c128 && xl == X_ROW && fmt == FMT_Q6K && (K / kChunk) % 2 == 0 &&
+        r192 * 192 <= (M + 127) / 128 * 128 && t192 <= kCUs)
+        return RUNG_M192N96_K2;
     if (c256 <= c128 || (xl == X_FRAG && (t256 >= 512 || (fmt == FMT_Q6K && t256 >= kCUs)))) return RUNG_M16_256;
     // few tiles: split K inside the workgroup (on row-major activations only
     // over a long K, where the halves' activation reloads stay affordable)

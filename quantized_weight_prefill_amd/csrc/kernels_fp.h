@@ -807,6 +807,20 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         else
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 2, 2, 1, 1, XL>), pl.grid, dim3(128), 0, s, a);
         return hipGetLastError();
+    case RUNG_M128N64_K2:
+        if (even)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 4, 1, 2, XL>), pl.grid, dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 4, 1, 1, XL>), pl.grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M96N32_K4:
+        if ((a.K / kChunk) % 4 == 0)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 2, 3, 1, 4, XL>), pl.grid, dim3(768), 0, s, a);
+        else if (even)
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 2, 3, 1, 2, XL>), pl.grid, dim3(384), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 2, 3, 1, 1, XL>), pl.grid, dim3(192), 0, s, a);
+        return hipGetLastError();
     default:
         break;
     }

@@ -28,7 +28,9 @@ enum Rung {
     RUNG_M192N64_K2 = 10, // 32x32x16 MFMA: 192x64, K split over two 6-wave groups
     RUNG_M64_SK = 11,     // 32x32x16 MFMA: 64x64, K split over four groups and across workgroups
     RUNG_M64N32_K4 = 12,  // 32x32x16 MFMA: 64x32, 2 waves of 32x32, K split over four groups
-    RUNG_COUNT = 13
+    RUNG_M128N64_K2 = 13, // 32x32x16 MFMA: 128x64, 4 waves of 32x64, K split over two groups
+    RUNG_M96N32_K4 = 14,  // 32x32x16 MFMA: 96x32, 3 waves of 32x32, K split over four groups
+    RUNG_COUNT = 15
 };
 
 enum I8Rung {

@@ -288,6 +288,9 @@ def test_i8_ladder():
 # ----------------------------------------------------------------------------
 
 SHAPES = [(4096, 12288), (4096, 4096), (4096, 1024), (12288, 4096), (4096, 32), (1024, 512), (256, 16)]
+# streaming tiles of the round model (one workgroup per CU) and their K groups
+ROUND_TILES = {"mfma32-64x64-k4": 4, "mfma32-64x32-k4": 4, "mfma32-96x32-k4": 4, "mfma32-128x64-k2": 2,
+               "mfma32-192x64-k2": 2}
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16"])
@@ -312,8 +315,9 @@ def test_ladder_sweep(fmt, dtype):
             elif M <= 64:
                 assert info["name"].startswith("direct-") or (
                     info["name"] in ("mfma32-64x64-k4", "mfma32-64x64-sk") and M > 32)
-            if info["name"] == "mfma32-64x32-k4":
-                assert 64 < M <= 128 and 2048 < N <= 4096
+            if M > 64 and info["name"] in ROUND_TILES:
+                # the round model's K-split tiles run with every K group they were measured with
+                assert info["k_split"] == ROUND_TILES[info["name"]], (M, N, K, info)
             if info["name"] == "mfma32-64x64-sk":
                 # slices across workgroups: whole chunks for every K group of every slice
                 assert (K // info["k_step"]) % info["k_split"] == 0 and info["k_split"] % info["waves"] == 0
@@ -323,27 +327,48 @@ def test_ladder_sweep(fmt, dtype):
 
 
 def test_ladder_mid_m_round_model():
-    """Below 128 tiles of 128x128 and above 64 rows the ladder picks among
-    the one-panel direct kernel, the four-panel 48-row direct kernel (Q4_K
-    only), 64x64 K-split tiles and, on fragment-major activations, 192x64
-    tiles split over two groups, by whole rounds of one workgroup per CU;
-    the expected names are the measured winners on MI355X."""
-    for fmt, M, N, K, want in [("q4k", 128, 1024, 4096, "direct-small-m"), ("q4k", 200, 1024, 4096, "direct-small-m"),
-                               ("q4k", 300, 1024, 4096, "direct-wide"), ("q4k", 200, 4096, 4096, "mfma32-64x64-k4"),
-                               ("q4k", 80, 6144, 4096, "direct-wide"),
-                               ("q4k", 128, 6144, 4096, "mfma32-64x64-k4"),                                ("q6k", 200, 4096, 12288, "mfma32-64x64-k4"),
-                               ("q4k", 658, 1024, 4096, "direct-wide")]:
-        for sel in (qg.select_rung, qg.select_rung_xf):
-            assert sel(fmt, M, N, K)["name"] == want, (fmt, M, N, K, sel.__name__)
-    # one round of 192x64 tiles (27 us) against two of 48-row direct or 64x64 tiles (Q6_K at
-    # M = 300, N = 4096: 72 against 91 us); row-major activations keep the three direct/64x64 rungs
-    for fmt, M, K, xf, row in [("q4k", 300, 4096, "mfma32-192x64-k2", "direct-wide"),
-                               ("q6k", 300, 12288, "mfma32-192x64-k2", "mfma32-64x64-k4"),
-                               ("q6k", 384, 12288, "mfma32-192x64-k2", "mfma32-64x64-k4")]:
-        assert qg.select_rung_xf(fmt, M, 4096, K)["name"] == xf, (fmt, M)
-        assert qg.select_rung(fmt, M, 4096, K)["name"] == row, (fmt, M)
-    # the 64x64 K-split tile stays where one round of it beats one of 192x64
-    assert qg.select_rung_xf("q6k", 256, 4096, 12288)["name"] == "mfma32-64x64-k4"
+    """Above 64 rows the ladder first asks the round model: each candidate
+    rung's workgroups run in rounds of one per CU (two for the 128-row
+    tiles), each round costing what it measured on MI355X for that format
+    and activation layout.  The expected names are the measured winners
+    (every rung forced, weights rotating); the numbers are Q4_K at K = 4096
+    unless stated."""
+    xf, row = qg.select_rung_xf, qg.select_rung
+    for dt in (qg.F16, qg.BF16):
+        for fmt in ("q4k", "q6k", "w4a16"):
+            # 64x32 tiles, K split four ways: few panels, 129..512 rows (N = 1024, M = 320: 10.5
+            # against 17.1 us for direct-wide; N = 2048, M = 129..256: 10.2-11.2 against 16.3-17.9)
+            for M, N in ((320, 1024), (512, 1024), (129, 2048), (256, 2048), (65, 4096), (128, 3072)):
+                assert xf(fmt, M, N, 4096, dt)["name"] == "mfma32-64x32-k4", (fmt, dt, M, N)
+            # 96x32 tiles: one round of them (N = 4096, M = 129..192: 13.8-14.9 against 17.2-18.8 us;
+            # N = 2048, M = 320..384: 14.6-14.8 against 18.3-19.1)
+            for M, N in ((129, 4096), (192, 4096), (320, 2048), (384, 2048), (65, 8192), (96, 6144)):
+                assert xf(fmt, M, N, 4096, dt)["name"] == "mfma32-96x32-k4", (fmt, dt, M, N)
+            # 128x64 tiles, K split two ways: N = 4096, M = 320..512 (22.7-26.0 against 28.0-32.5 us
+            # for 192x64); N = 6144..8192, M = 129..256 (21.9-25.8 against 26.8-32.6); N = 12288,
+            # M = 65..128 on both layouts (0.58-0.86 of the 192x64 / 64x64 times)
+            for M, N in ((320, 4096), (512, 4096), (129, 6144), (256, 8192), (65, 12288), (128, 12288)):
+                assert xf(fmt, M, N, 4096, dt)["name"] == "mfma32-128x64-k2", (fmt, dt, M, N)
+            assert xf(fmt, 384, 4096, 12288, dt)["name"] == "mfma32-128x64-k2", (fmt, dt)
+            for M in (65, 96):
+                assert row(fmt, M, 12288, 4096, dt)["name"] == "mfma32-128x64-k2", (fmt, dt, M)
+            # one panel and all rows per wave while its workgroups fit one round (N = 1024,
+            # M = 129..256: 8.4-9.1 against 10.0-10.5 us for 64x32 tiles)
+            for M, N in ((129, 1024), (256, 1024), (96, 2048)):
+                assert xf(fmt, M, N, 4096, dt)["name"] == "direct-small-m", (fmt, dt, M, N)
+            # 64x64 tiles, K split four ways: one round of them where the narrower tiles need two
+            # (N = 4096, M = 256: 19.1 against 20.6 us for 64x32 and 21.8 for 128x64)
+            assert xf(fmt, 256, 4096, 4096, dt)["name"] == "mfma32-64x64-k4", (fmt, dt)
+            assert xf(fmt, 128, 8192, 4096, dt)["name"] == "mfma32-64x64-k4", (fmt, dt)
+            # the large tiles keep their rules (merged QKV and beyond)
+            assert xf(fmt, 658, 4096, 4096, dt)["name"] == "mfma32-192x64-k2", (fmt, dt)
+            assert row(fmt, 658, 4096, 4096, dt)["name"] == "mfma32-128x128", (fmt, dt)
+    # the four-panel direct kernel only for Q4_K (its 48-row variant spills for the other formats):
+    # row-major fp16 Q4_K at N = 4096, M = 129..192 (19.5-19.8 against 29.2-29.4 us for 96x32 tiles)
+    for M in (129, 192):
+        assert row("q4k", M, 4096, 4096)["name"] == "direct-wide", M
+        assert row("w4a16", M, 4096, 4096)["name"] != "direct-wide", M
+        assert row("q6k", M, 4096, 4096)["name"] != "direct-wide", M
     # Q6_K over few panels, 33..64 rows: row-major keeps one panel and all rows per wave,
     # fragment-major splits 64x64 tiles four ways across workgroups (M = 64: 24.2 against 28.1 us);
     # from 65 rows both take 64x32 tiles with K split four ways (M = 96: 36 against 45 us, 56
@@ -355,7 +380,13 @@ def test_ladder_mid_m_round_model():
     for M in (65, 80, 128):
         for sel in (qg.select_rung, qg.select_rung_xf):
             assert sel("q6k", M, 4096, 12288)["name"] == "mfma32-64x32-k4", (M, sel.__name__)
-    assert qg.select_rung_xf("q6k", 150, 4096, 12288)["name"] == "mfma32-64x64-k4"
+    # the split rung never leaves the decode-adjacent range: above 64 rows the round model's
+    # tiles beat it on fragment-major activations, and row-major callers get no workspace
+    for fmt in ("q4k", "q6k", "w4a16"):
+        for M in (65, 96, 128, 200):
+            for N, K in ((4096, 12288), (4096, 4096), (2048, 4096), (1024, 4096)):
+                for sel in (qg.select_rung, qg.select_rung_xf):
+                    assert sel(fmt, M, N, K)["name"] != "mfma32-64x64-sk", (fmt, M, N, K, sel.__name__)
     # up to 16 rows: one panel per wave, except over >= 1536 panels (merged gate/up), where four
     # panels per wave win (M = 8, N = 24576: Q4_K 20.7 against 23.8 us); both layouts
     # (row-major X keeps four panels per wave at 9..16 rows over >= 512 panels: 12.2 against 15.7 us)
@@ -367,8 +398,8 @@ def test_ladder_mid_m_round_model():
             assert qg.select_rung_xf(fmt, M, 12288, 4096)["name"] == "direct-small-m", (fmt, M)
         assert qg.select_rung(fmt, 8, 12288, 4096)["name"] == "direct-small-m", fmt
         assert qg.select_rung(fmt, 16, 12288, 4096)["name"] == "direct-skinny-n", fmt
-    # the split rung at the down projection's shape (fragment-major X): fp16 Q6_K and W4A16 33..128
-    # rows, Q4_K 49..64 (from 96 rows direct-wide); bf16 every format from 33 rows
+    # the split rung at the down projection's shape (fragment-major X): fp16 Q6_K and W4A16 33..64
+    # rows, Q4_K 49..64; bf16 every format from 33 rows; above 64 rows the 64x32 tiles
     for fmt, M, want in [("q6k", 40, "mfma32-64x64-sk"), ("w4a16", 40, "mfma32-64x64-sk"),
                          ("w4a16", 64, "mfma32-64x64-sk"), ("w4a16", 128, "mfma32-64x32-k4"),
                          ("q4k", 64, "mfma32-64x64-sk"), ("q4k", 96, "mfma32-64x32-k4"), ("q4k", 32, "direct-small-m")]:
@@ -376,21 +407,9 @@ def test_ladder_mid_m_round_model():
     for fmt, M, want in [("q4k", 96, "mfma32-64x32-k4"), ("q4k", 48, "mfma32-64x64-sk"),
                          ("w4a16", 40, "mfma32-64x64-sk"), ("q4k", 32, "direct-small-m")]:
         assert qg.select_rung_xf(fmt, M, 4096, 12288, qg.BF16)["name"] == want, (fmt, M)
-    # K = 4096 over 4096 columns: 64x32 tiles with K split four ways at 65..128 rows in both
-    # dtypes (Q4_K M = 96: 11.1 against 15.0 us for two slices of 64x64 tiles); not over 2048,
-    # 1024 or 6144 columns, nor above 128 rows; fp16 Q4_K on row-major X keeps direct-wide
     for dt in (qg.F16, qg.BF16):
         for fmt in ("q4k", "q6k", "w4a16"):
-            for M in (65, 96, 128):
-                assert qg.select_rung_xf(fmt, M, 4096, 4096, dt)["name"] == "mfma32-64x32-k4", (fmt, dt, M)
-                assert qg.select_rung_xf(fmt, M, 3072, 4096, dt)["name"] == "mfma32-64x32-k4", (fmt, dt, M)
-                row = qg.select_rung(fmt, M, 4096, 4096, dt)["name"]
-                assert (row == "mfma32-64x32-k4") == (fmt != "q4k" or dt == qg.BF16), (fmt, dt, M, row)
             assert qg.select_rung_xf(fmt, 64, 4096, 4096, dt)["name"] == "direct-small-m", (fmt, dt)
-            for M, N in ((160, 4096), (96, 2048), (128, 1024), (96, 6144)):
-                assert qg.select_rung_xf(fmt, M, N, 4096, dt)["name"] != "mfma32-64x32-k4", (fmt, dt, M, N)
-            assert qg.select_rung_xf(fmt, 128, 1024, 4096, dt)["name"] != "mfma32-64x64-sk", (fmt, dt)
-            assert qg.select_rung_xf(fmt, 96, 6144, 4096, dt)["name"] != "mfma32-64x64-sk", (fmt, dt)
     # Q6_K over many panels, 33..64 rows: 64x64 tiles unpack each weight once for all rows
     # (M = 64, N = K = 12288: 52 against 93 us for direct-skinny-n)
     for M in (33, 48, 64):
@@ -415,7 +434,8 @@ def test_ladder_fragment_major():
     assert qg.select_rung_xf("q4k", 200, 12288, 4096)["name"] == "mfma32-128x128-k2"
     assert qg.select_rung_xf("q4k", 1000, 4096, 4096)["name"] == "mfma32-128x128-k2"
     assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"        # row-major: K < 8192
-    assert qg.select_rung_xf("q4k", 512, 4096, 4096)["name"] == "mfma32-192x64-k2"    # one round, despite 64 padding rows
+    # one round of 128x64 tiles against one of 192x64 with 64 padding rows (26.0 against 32.5 us)
+    assert qg.select_rung_xf("q4k", 512, 4096, 4096)["name"] == "mfma32-128x64-k2"
     assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
     assert qg.select_rung_xf("q4k", 512, 12288, 4096)["name"] == "mfma16-256x128"
     # 512 tiles of 352x96 in two rounds against 576 of 256x128 in three
@@ -429,7 +449,7 @@ def test_ladder_fragment_major():
     assert qg.select_rung_xf("q6k", 1024, 12288, 12288)["name"] == "mfma16-256x128"   # Q6_K from one round of 256-row tiles
     assert qg.select_rung_xf("q6k", 1024, 4096, 12288)["name"] == "mfma32-128x128-k2"  # half a round: not
     # (at 9..16 rows over 512..1535 panels the layouts differ on purpose: see the small-M test)
-    for fmt, M, K, N in [("q4k", 658, 4096, 1024), ("q4k", 8, 4096, 12288),
+    for fmt, M, K, N in [("q4k", 8, 4096, 12288),
                          ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
                          ("q6k", 1024, 12288, 4096)]:
         assert qg.select_rung_xf(fmt, M, N, K)["name"] == qg.select_rung(fmt, M, N, K)["name"], (fmt, M, K, N)
