@@ -134,13 +134,13 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    and the kernel is a weight stream; up to 16 rows one panel and all rows
 //    per wave (the most waves streaming, each weight unpacked once), except
 //    over 1536 panels and more and, on row-major activations, at 9..16 rows
-//    over 512 panels and more: four panels and 16 rows per wave; with fewer
-//    than 512 panels up to 64 rows one panel per wave, or on fragment-major
-//    activations over 129..256 panels 64x64 tiles with K split across
-//    workgroups too (split_pays); with many panels: 17..32 rows (17..48 for
-//    Q4_K) four panels and all rows per wave (each activation fragment feeds
-//    four panels), 49..64 rows of Q4_K and 33..64 of W4A16 and Q6_K 64x64
-//    streaming tiles with K split four ways;
+//    over 512 panels and more: four panels and 16 rows per wave; 17..64 rows
+//    over at most 256 panels one panel and all rows per wave (on row-major
+//    activations above 32 rows 16 rows and four panels per wave), or on
+//    fragment-major activations 64x64 tiles with K split across workgroups
+//    too (split_pays); over more panels the direct kernels up to 32 rows
+//    (four panels and all rows per wave from 512 panels, for fp16 Q4_K up to
+//    48 rows), above that the round model's streaming tiles;
 //  * above 64 rows, the round model of round_model_rung over the direct
 //    kernels and the streaming tiles that run one workgroup per CU (64x32,
 //    96x32 and 64x64 with K split four ways, 128x64 and 192x64 with K split
@@ -193,52 +193,62 @@ bool split_pays(int fmt, int dtype, long long M, long long np, long long K, int 
 
 // Cost of one full round of a rung's workgroups (256 CUs, `per_cu`
 // workgroups on each at once), in microseconds at K = 4096, by activation
-// layout (row-major, fragment-major) and format (Q4_K, Q6_K, W4A16).
-// Measured on MI355X with every rung forced, weights rotating through 320 MB:
-// medians of time / rounds over M = 65..512 and N = 1024..12288, both dtypes
-// (the four-panel direct kernel runs about 15% faster in fp16 on Q4_K and
-// has a row per dtype; its 48-row variant spills for Q6_K and W4A16, and
-// the zero entries leave it out for them: 64x64 tiles beat it there by
-// 6-10% where the medians tie).  Every rung's time grows with K alike, so
-// the comparison holds at other K.  `large` marks the tiles whose rules
-// follow in select_rung: when one of them is cheapest, the model defers to
-// those.
+// layout (row-major, fragment-major) and format (Q4_K, Q6_K, W4A16); the
+// direct kernels have a row per number of 16-row blocks each wave carries
+// (`rb`, as make_plan sets it; 0 for the streaming tiles).  Measured on
+// MI355X with every rung forced, weights rotating through 320 MB: medians of
+// time / rounds, scaled to K = 4096, over M = 17..512, N = 1024..27648 and K
+// = 4096..14336, both dtypes (the four-panel direct kernel runs 10-20%
+// faster in fp16 on Q4_K and has rows per dtype; its 48-row variant spills
+// for Q6_K and W4A16, and the zero entries leave it out for them, as they
+// leave out the 192x64 tile on row-major activations, where it never wins).
+// `large` marks the tiles whose rules follow in select_rung: above 64 rows,
+// when one of them is cheapest, the model defers to those.
 struct RoundCost {
-    int rung, per_cu, dtype, large;  // dtype -1: both
+    int rung, rb, per_cu, dtype, large;  // dtype -1: both
     float us[2][3];
 };
 constexpr RoundCost kRoundCost[] = {
-    {RUNG_M64N32_K4, 1, -1, 0, {{18.8f, 20.5f, 18.5f}, {9.9f, 11.3f, 8.7f}}},
-    {RUNG_M96N32_K4, 1, -1, 0, {{27.8f, 29.6f, 27.3f}, {13.6f, 15.6f, 12.9f}}},
-    {RUNG_M64_K4, 1, -1, 0, {{22.4f, 25.1f, 21.7f}, {16.9f, 19.4f, 15.7f}}},
-    {RUNG_M128N64_K2, 1, -1, 0, {{35.2f, 37.2f, 34.8f}, {20.4f, 22.1f, 19.1f}}},
-    {RUNG_M192N64_K2, 1, -1, 0, {{45.5f, 48.0f, 44.9f}, {26.2f, 29.1f, 25.0f}}},
-    {RUNG_SMALL_M, 1, -1, 0, {{15.8f, 16.2f, 15.6f}, {7.3f, 7.9f, 6.8f}}},
-    {RUNG_WIDE, 1, DT_F16, 0, {{18.3f, 0.0f, 0.0f}, {14.3f, 0.0f, 0.0f}}},
-    {RUNG_WIDE, 1, DT_BF16, 0, {{20.8f, 0.0f, 0.0f}, {16.9f, 0.0f, 0.0f}}},
-    {RUNG_M128, 2, -1, 1, {{38.9f, 43.0f, 36.9f}, {39.2f, 42.3f, 35.7f}}},
-    {RUNG_M128_K2, 1, -1, 1, {{38.9f, 43.8f, 37.8f}, {33.6f, 37.8f, 32.0f}}},
-    {RUNG_M128N160, 2, -1, 1, {{52.0f, 92.2f, 47.0f}, {53.2f, 92.2f, 48.1f}}},
-    {RUNG_M16_256, 1, -1, 1, {{52.5f, 56.7f, 50.2f}, {49.1f, 52.5f, 48.4f}}},
-    {RUNG_M192N96_K2, 1, -1, 1, {{49.9f, 51.0f, 46.1f}, {32.4f, 34.5f, 30.5f}}},
+    {RUNG_M64_K4, 0, 1, -1, 0, {{21.4f, 23.8f, 20.7f}, {16.4f, 18.7f, 15.2f}}},
+    {RUNG_M64N32_K4, 0, 1, -1, 0, {{18.2f, 19.7f, 17.7f}, {9.7f, 11.0f, 8.6f}}},
+    {RUNG_M96N32_K4, 0, 1, -1, 0, {{25.1f, 26.9f, 24.6f}, {13.0f, 14.9f, 12.4f}}},
+    {RUNG_M128N64_K2, 0, 1, -1, 0, {{31.5f, 33.3f, 30.7f}, {19.5f, 21.1f, 18.4f}}},
+    {RUNG_M192N64_K2, 0, 1, -1, 0, {{0.0f, 0.0f, 0.0f}, {25.2f, 27.6f, 24.2f}}},
+    {RUNG_SMALL_M, 2, 1, -1, 0, {{8.0f, 8.4f, 7.8f}, {5.5f, 5.8f, 5.0f}}},
+    {RUNG_SMALL_M, 3, 1, -1, 0, {{12.1f, 12.8f, 12.0f}, {7.0f, 7.9f, 6.7f}}},
+    {RUNG_SMALL_M, 4, 1, -1, 0, {{15.5f, 15.9f, 15.4f}, {7.4f, 7.7f, 6.8f}}},
+    {RUNG_SKINNY_N, 1, 1, -1, 0, {{11.0f, 12.5f, 9.7f}, {10.6f, 12.0f, 9.2f}}},
+    {RUNG_WIDE, 2, 1, DT_F16, 0, {{13.8f, 16.3f, 13.3f}, {11.9f, 14.9f, 11.5f}}},
+    {RUNG_WIDE, 3, 1, DT_F16, 0, {{17.8f, 0.0f, 0.0f}, {14.1f, 0.0f, 0.0f}}},
+    {RUNG_WIDE, 2, 1, DT_BF16, 0, {{14.4f, 15.7f, 12.8f}, {13.3f, 13.9f, 10.5f}}},
+    {RUNG_WIDE, 3, 1, DT_BF16, 0, {{20.4f, 0.0f, 0.0f}, {16.6f, 0.0f, 0.0f}}},
+    {RUNG_M128_K2, 0, 1, -1, 1, {{36.3f, 40.2f, 34.8f}, {33.1f, 37.2f, 31.5f}}},
+    {RUNG_M128, 0, 2, -1, 1, {{38.1f, 41.9f, 36.3f}, {38.2f, 41.4f, 35.0f}}},
+    {RUNG_M128N160, 0, 2, -1, 1, {{49.7f, 90.7f, 46.5f}, {52.0f, 91.7f, 47.6f}}},
+    {RUNG_M16_256, 0, 1, -1, 1, {{54.2f, 58.4f, 52.6f}, {48.9f, 51.9f, 48.0f}}},
+    {RUNG_M192N96_K2, 0, 1, -1, 1, {{50.2f, 52.2f, 48.4f}, {32.1f, 34.2f, 30.4f}}},
 };
 
-// The rung the round model finishes first, or -1 when that is one of the
-// large tiles; on a tie the earlier entry of the table, a streaming tile
-// before a direct kernel (Q4_K at M = 100, N = 5120, K = 13824, bf16: 64x64
-// tiles 46.0 against 54.5 us for direct-wide, whose costs tie).  A K-split
-// rung takes part only with an even chunk count: with an odd one it runs a
-// single K group.  With two chunks over (K = 11008: 86 chunks) the four-way
-// tiles run two K groups and measured no slower per round than with four
-// (64x32 tiles at M = 100, N = 4096: 44-50 us, the K = 12288 times scaled
-// to that K).  Measured against the fastest forced rung over the sweep
-// above: 1.002-1.005 of it on average, where the earlier rules (fixed
-// thresholds and a Q4_K-only round model) came to 1.06-1.13; e.g. M = 320,
-// N = 1024 on fragment-major Q4_K: 64x32 tiles 10.5 against 17.1 us for
-// direct-wide; M = 129..192, N = 4096: 96x32 tiles 13.8-14.9 against
-// 17.2-18.8; M = 320..512, N = 4096: 128x64 tiles 22.7-26.0 against
-// 28.0-32.5 for 192x64; M = 65..128, N = 12288: 128x64 tiles 0.58-0.86 of
-// the former time.
+// The rung the round model finishes first; above 64 rows -1 when that is
+// one of the large tiles.  On a tie the earlier entry of the table, a
+// streaming tile before a direct kernel (Q4_K at M = 100, N = 5120, K =
+// 13824, bf16: 64x64 tiles 46.0 against 54.5 us for direct-wide, whose
+// costs tie).  A K-split tile takes part only with an even chunk count:
+// with an odd one it runs a single K group.  With two chunks over (K =
+// 11008: 86 chunks) the four-way tiles run two K groups and measured no
+// slower per round than with four (64x32 tiles at M = 100, N = 4096: 44-50
+// us, the K = 12288 times scaled to that K).  Measured against the fastest
+// forced rung over the sweeps the table comes from: 1.002-1.007 of it on
+// average, and 1.010-1.014 on shapes outside them (hidden sizes 5120,
+// 11008, 13824, 14336, 27648); the earlier fixed thresholds came to
+// 1.06-1.13 there.  E.g. M = 320, N = 1024 on fragment-major Q4_K: 64x32
+// tiles 10.5 against 17.1 us for direct-wide; M = 129..192, N = 4096: 96x32
+// tiles 13.8-14.9 against 17.2-18.8; M = 320..512, N = 4096: 128x64 tiles
+// 22.7-26.0 against 28.0-32.5 for 192x64; M = 65..128, N = 12288: 128x64
+// tiles 0.58-0.86 of the former time; M = 40..64, N = 6144: 64x32 tiles
+// 0.6-0.7 of the time of one panel per wave; row-major M = 48..64, N =
+// 1024..4096: 16 rows and four panels per wave 0.57-0.72 of the time of
+// one panel and all rows per wave.
 int round_model_rung(int fmt, long long M, long long N, long long K, int xl, int dtype)
 {
     double best = 1e30;
@@ -247,9 +257,8 @@ int round_model_rung(int fmt, long long M, long long N, long long K, int xl, int
         const float us = rc.us[xl == X_FRAG][fmt];
         if ((rc.dtype >= 0 && rc.dtype != dtype) || us <= 0.0f) continue;
         Plan pl;
-        if (make_plan(rc.rung, M, N, K, pl) != QGEMM_OK) continue;
-        if (pl.kw == 1 && rc.rung != RUNG_SMALL_M && rc.rung != RUNG_WIDE && rc.rung != RUNG_M128 &&
-            rc.rung != RUNG_M128N160 && rc.rung != RUNG_M16_256)
+        if (make_plan(rc.rung, M, N, K, pl) != QGEMM_OK || pl.rb != rc.rb) continue;
+        if (pl.kw == 1 && rc.rb == 0 && rc.rung != RUNG_M128 && rc.rung != RUNG_M128N160 && rc.rung != RUNG_M16_256)
             continue;  // a K-split tile left with one K group
         const long long wgs = (long long)pl.grid.x * pl.grid.y * pl.grid.z;
         const long long per_round = (long long)kCUs * rc.per_cu;
@@ -260,7 +269,7 @@ int round_model_rung(int fmt, long long M, long long N, long long K, int xl, int
             large = rc.large;
         }
     }
-    return large ? -1 : pick;
+    return large && M > 64 ? -1 : pick;
 }
 
 int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtype = DT_F16)
@@ -285,21 +294,13 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
             if (np >= 1536 || (xl == X_ROW && M > 8 && np >= 512)) return RUNG_SKINNY_N;
             return RUNG_SMALL_M;
         }
-        // (three row blocks per wave only pay off for Q4_K: the other
-        // formats' larger raw runs spill at that size)
-        if (np >= 512 && M > 16 && (M <= 32 || (M <= 48 && fmt == FMT_Q4K))) return RUNG_WIDE;
-        // 49..64 rows of Q4_K (33..64 of W4A16 and Q6_K) over many panels:
-        // unpack each weight once for all rows into LDS (64x64 tiles, K split
-        // four ways) instead of once per 16-row group (Q6_K 12288->12288 at
-        // M = 64: 50.5 against 90.1 us for direct-skinny-n)
-        if (np >= 512 && ((fmt == FMT_Q4K && M > 48) || (fmt != FMT_Q4K && M > 32))) return RUNG_M64_K4;
-        // Q6_K over few panels (N = 4096): 64x64 tiles with K also split
-        // across workgroups, so that each CU reads a quarter of the
-        // activations
+        // 17..64 rows: the split rung where split_pays, else the round model
+        // over the direct kernels and the streaming tiles (on row-major
+        // activations above 32 rows over few panels 16 rows and four panels
+        // per wave, over 384 panels 64x32 tiles in one round, over 768 64x64
+        // tiles in one round, over 1536 the K-split 128x128 tile ...)
         if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
-        // fewer panels: one panel and all rows per wave (each weight
-        // unpacked once) beats four panels of 16 rows up to 64 rows
-        return RUNG_SMALL_M;
+        return round_model_rung(fmt, M, N, K, xl, dtype);
     }
     if (const int r = round_model_rung(fmt, M, N, K, xl, dtype); r >= 0) return r;
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);

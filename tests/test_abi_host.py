@@ -312,10 +312,14 @@ def test_ladder_sweep(fmt, dtype):
             assert (K // info["k_step"]) >= info["k_split"] >= 1
             if N <= 64:
                 assert info["name"] == "direct-skinny-n"
+            elif M <= 16:
+                assert info["name"].startswith("direct-")
             elif M <= 64:
+                # the direct kernels up to 24 rows; above, also the split rung and the streaming
+                # tiles of the round model
                 assert info["name"].startswith("direct-") or (
-                    info["name"] in ("mfma32-64x64-k4", "mfma32-64x64-sk") and M > 32)
-            if M > 64 and info["name"] in ROUND_TILES:
+                    info["name"] in set(ROUND_TILES) | {"mfma32-64x64-sk", "mfma32-128x128-k2"} and M > 24)
+            if M > 16 and info["name"] in ROUND_TILES:
                 # the round model's K-split tiles run with every K group they were measured with
                 assert info["k_split"] == ROUND_TILES[info["name"]], (M, N, K, info)
             if info["name"] == "mfma32-64x64-sk":
@@ -369,12 +373,13 @@ def test_ladder_mid_m_round_model():
         assert row("q4k", M, 4096, 4096)["name"] == "direct-wide", M
         assert row("w4a16", M, 4096, 4096)["name"] != "direct-wide", M
         assert row("q6k", M, 4096, 4096)["name"] != "direct-wide", M
-    # Q6_K over few panels, 33..64 rows: row-major keeps one panel and all rows per wave,
-    # fragment-major splits 64x64 tiles four ways across workgroups (M = 64: 24.2 against 28.1 us);
+    # Q6_K over few panels, 33..64 rows: row-major takes 16 rows and four panels per wave
+    # (M = 40..64: 0.50-0.68 of the time of one panel and all rows per wave), fragment-major
+    # splits 64x64 tiles four ways across workgroups (M = 64: 24.2 against 28.1 us);
     # from 65 rows both take 64x32 tiles with K split four ways (M = 96: 36 against 45 us, 56
     # against 81 us on row-major X)
     for M in (33, 64):
-        assert qg.select_rung("q6k", M, 4096, 12288)["name"] == "direct-small-m", M
+        assert qg.select_rung("q6k", M, 4096, 12288)["name"] == "direct-skinny-n", M
         sk = qg.select_rung_xf("q6k", M, 4096, 12288)
         assert sk["name"] == "mfma32-64x64-sk" and sk["k_split"] == 16, (M, sk)
     for M in (65, 80, 128):
@@ -416,6 +421,45 @@ def test_ladder_mid_m_round_model():
         for sel in (qg.select_rung, qg.select_rung_xf):
             assert sel("q6k", M, 12288, 12288)["name"] == "mfma32-64x64-k4", (M, sel.__name__)
             assert sel("q6k", M, 12288, 4096)["name"] == "mfma32-64x64-k4", (M, sel.__name__)
+
+
+def test_ladder_decode_adjacent_tiles():
+    """17..64 rows: the split rung where it pays, else the round model over
+    the direct kernels and the streaming tiles.  Pinned here are decisions
+    the measurements on MI355X make by at least 8% over every other rung, in
+    both dtypes and all three formats (every rung forced, weights rotating,
+    K = 4096)."""
+    xf, row = qg.select_rung_xf, qg.select_rung
+    for dt in (qg.F16, qg.BF16):
+        for fmt in ("q4k", "q6k", "w4a16"):
+            # few panels: one panel and all rows per wave on fragment-major X; on row-major X
+            # 16 rows and four panels per wave from about 50 rows (M = 56..64: 0.57-0.68 of the
+            # one-panel time), one panel per wave at 17 rows
+            for N in (1024, 2048, 4096):
+                for M in (17, 32, 48):
+                    assert xf(fmt, M, N, 4096, dt)["name"] == "direct-small-m", (fmt, dt, N, M)
+                for M in (56, 64):
+                    assert row(fmt, M, N, 4096, dt)["name"] == "direct-skinny-n", (fmt, dt, N, M)
+                assert row(fmt, 17, N, 4096, dt)["name"] == "direct-small-m", (fmt, dt, N)
+            assert xf(fmt, 36, 3072, 4096, dt)["name"] == "direct-small-m", (fmt, dt)
+            assert row(fmt, 60, 3072, 4096, dt)["name"] == "direct-skinny-n", (fmt, dt)
+            # 384..512 panels on fragment-major X: 64x32 tiles in one round (N = 6144, M = 40..64:
+            # 0.6-0.7 of the time of one panel per wave; N = 8192, M = 36..60)
+            for M in (40, 48, 56, 64):
+                assert xf(fmt, M, 6144, 4096, dt)["name"] == "mfma32-64x32-k4", (fmt, dt, M)
+            for M in (36, 44, 52, 60):
+                assert xf(fmt, M, 8192, 4096, dt)["name"] == "mfma32-64x32-k4", (fmt, dt, M)
+            # 768 panels up to 32 rows: four panels and all rows per wave (both layouts); row-major
+            # X at N = 6144, 32 rows: 16 rows and four panels per wave
+            for M in (17, 24, 32):
+                assert row(fmt, M, 12288, 4096, dt)["name"] == "direct-wide", (fmt, dt, M)
+            assert row(fmt, 32, 6144, 4096, dt)["name"] == "direct-skinny-n", (fmt, dt)
+            # 896 panels (N = 14336): four panels per wave at 20..28 rows, one round of 64x64 tiles
+            # at 60 rows on fragment-major X
+            for M in (20, 28):
+                for sel in (xf, row):
+                    assert sel(fmt, M, 14336, 4096, dt)["name"] == "direct-wide", (fmt, dt, M)
+            assert xf(fmt, 60, 14336, 4096, dt)["name"] == "mfma32-64x64-k4", (fmt, dt)
 
 
 def test_ladder_fragment_major():
