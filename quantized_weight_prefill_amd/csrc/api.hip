@@ -272,6 +272,21 @@ int round_model_rung(int fmt, long long M, long long N, long long K, int xl, int
     return large && M > 64 ? -1 : pick;
 }
 
+// The round model's cost of one streaming rung (its whole rounds times its
+// round cost), 1e30 when the table has no entry for it.
+double round_cost(int rung, int fmt, long long M, long long N, long long K, int xl)
+{
+    for (const RoundCost &rc : kRoundCost) {
+        if (rc.rung != rung || rc.rb != 0) continue;
+        const float us = rc.us[xl == X_FRAG][fmt];
+        Plan pl;
+        if (us <= 0.0f || make_plan(rung, M, N, K, pl) != QGEMM_OK) return 1e30;
+        const long long wgs = (long long)pl.grid.x * pl.grid.y * pl.grid.z, per_round = (long long)kCUs * rc.per_cu;
+        return us * (double)((wgs + per_round - 1) / per_round);
+    }
+    return 1e30;
+}
+
 int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtype = DT_F16)
 {
     const long long np = (N + 15) / 16, tn = (np + 7) / 8;
@@ -330,8 +345,10 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
     // 256-row tiles need three (merged gate_up at M = 658: 147 against 173 us;
     // M = 700, N = 12288: 76 against 95 us for 128x160; Q6_K, whose larger raw
     // runs spill four registers in it, at M = 658, N = 12288: 218 against
-    // 333 us for 128x128).
-    if (xl == X_FRAG) {
+    // 333 us for 128x128); on row-major activations for Q6_K too, which has
+    // no 160-wide tile (M = 700, N = 11008..24576: 101-204 against 130-222 us
+    // for 128x128; the other formats' 128x160 tile beats it there)
+    if (xl == X_FRAG || fmt == FMT_Q6K) {
         const long long t352 = ((np + 5) / 6) * ((M + 351) / 352);
         const double c352 = 2.44 * (double)((t352 + kCUs - 1) / kCUs);
         if (c352 < c256 && c352 < c128) return RUNG_M352N96;
@@ -348,7 +365,19 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
     if (c256 <= c128 && xl == X_ROW && fmt == FMT_Q6K && (K / kChunk) % 2 == 0 &&
         r192 * 192 <= (M + 127) / 128 * 128 && t192 <= kCUs)
         return RUNG_M192N96_K2;
-    if (c256 <= c128 || (xl == X_FRAG && (t256 >= 512 || (fmt == FMT_Q6K && t256 >= kCUs)))) return RUNG_M16_256;
+    // (and Q6_K on row-major activations from 512 of them: M = 1500..4096,
+    // N = 11008..24576: 0.88-0.98 of the 128x128 time; at 1.5 rounds, 384
+    // tiles, it loses by 6-9%)
+    if (c256 <= c128 || (xl == X_FRAG && (t256 >= 512 || (fmt == FMT_Q6K && t256 >= kCUs))) ||
+        (fmt == FMT_Q6K && t256 >= 512)) {
+        // (on fragment-major activations 192x96 K-split tiles instead where
+        // the round model has their whole rounds at least 5% cheaper: M =
+        // 1500, N = 11008..12288 and M = 3072, N = 6144: 0.91-0.97 of the
+        // 256-row tile's time; at a modelled tie they measured 0.98-1.05)
+        if (k2_192 && round_cost(RUNG_M192N96_K2, fmt, M, N, K, xl) < 0.95 * round_cost(RUNG_M16_256, fmt, M, N, K, xl))
+            return RUNG_M192N96_K2;
+        return RUNG_M16_256;
+    }
     // few tiles: split K inside the workgroup (on row-major activations only
     // over a long K, where the halves' activation reloads stay affordable)
     if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) return RUNG_M128_K2;

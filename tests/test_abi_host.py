@@ -492,6 +492,22 @@ def test_ladder_fragment_major():
     assert qg.select_rung_xf("q4k", 2048, 12288, 4096)["name"] == "mfma16-256x128"    # 768 tiles: three rounds either way
     assert qg.select_rung_xf("q6k", 1024, 12288, 12288)["name"] == "mfma16-256x128"   # Q6_K from one round of 256-row tiles
     assert qg.select_rung_xf("q6k", 1024, 4096, 12288)["name"] == "mfma32-128x128-k2"  # half a round: not
+    # on fragment-major X, 192x96 K-split tiles instead of the 256-row tile where their whole rounds
+    # cost at least 5% less by the round costs (M = 1500, N = 11008..12288: 0.91-0.95 of its time)
+    for fmt in ("q4k", "q6k", "w4a16"):
+        assert qg.select_rung_xf(fmt, 1500, 12288, 4096)["name"] == "mfma32-192x96-k2", fmt
+        assert qg.select_rung_xf(fmt, 1500, 11008, 4096)["name"] == "mfma32-192x96-k2", fmt
+        assert qg.select_rung_xf(fmt, 2048, 12288, 4096)["name"] == "mfma16-256x128", fmt  # 1.24-1.29 there
+    # row-major Q6_K (no 160-wide tile): the 352x96 tile at M = 700 over N = 11008..24576 (0.78-0.92
+    # of the 128x128 time) and the 256-row tile from 512 of its tiles (M = 3072, N = 11008..12288:
+    # 0.90 of it); not at 1.5 rounds (M = 1024, N = 12288) nor for the other formats
+    for N in (11008, 12288, 24576):
+        assert qg.select_rung("q6k", 700, N, 4096)["name"] == "mfma32-352x96", N
+    for N in (11008, 12288):
+        assert qg.select_rung("q6k", 3072, N, 4096)["name"] == "mfma16-256x128", N
+    assert qg.select_rung("q6k", 1024, 12288, 4096)["name"] == "mfma32-128x128"
+    for fmt in ("q4k", "w4a16"):
+        assert qg.select_rung(fmt, 700, 12288, 4096)["name"] == "mfma32-128x160", fmt
     # (at 9..16 rows over 512..1535 panels the layouts differ on purpose: see the small-M test)
     for fmt, M, K, N in [("q4k", 8, 4096, 12288),
                          ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
