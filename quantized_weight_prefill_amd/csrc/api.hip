@@ -683,13 +683,18 @@ int i8_select(int fmt, long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8), r192 = (M + 191) / 192;
     const long long nch = K / kChunk;
-    // few tiles of 192x64 (at most half the CUs): 64x64 tiles with K split
-    // across workgroups as well, up to 64 rows (Q6_K, whose unpack weighs
-    // most, up to 256): Q6_K 12288->4096 at M = 16..256 28.6-56.1 against
-    // 59.4-64.3 us, Q4_K 4096->4096 at M = 16..64 15.2-17.0 against
-    // 23.5-24.1 us (row quantizer included); over more tiles, or Q4_K from
-    // 96 rows, the 192x64 tile wins (4096->12288: 23.7-25.7 against 24.2-26.3)
-    if (nch % 8 == 0 && nch >= 16 && r192 * ((np + 3) / 4) <= kCUs / 2 && (M <= 64 || (fmt == FMT_Q6K && M <= 256)))
+    // few 64x64 tiles: those tiles with K split across workgroups as well,
+    // every format and M, up to 96 tiles (128 for Q6_K, whose unpack weighs
+    // most: M = 128, N = 4096 23.7 against 26.4 us), and up to 256 over K >=
+    // 8192
+    // (every rung forced, weights rotating: up to 64 tiles 0.44-0.66 of the
+    // time of the 192x64 K-split tile, e.g. Q4_K 4096->1024 at M = 128..256
+    // 11.7-13.1 against 20.2-20.8 us, Q6_K 12288->4096 at M = 16..128
+    // 24.9-35.8 against 56.1-59.5; 96 tiles 0.82-0.97; at K = 12288 256
+    // tiles 0.85-0.91; at K = 4096 from 128 tiles a tie, from 256 a loss of
+    // 7-15%)
+    const long long t64 = ((np + 3) / 4) * ((M + 63) / 64);
+    if (nch % 8 == 0 && nch >= 16 && (t64 <= (fmt == FMT_Q6K ? 128 : 96) || (nch >= 64 && t64 <= 256)))
         return I8_M64_SK;
     if ((K / kChunk) % 2 == 0 && r192 * ((np + 3) / 4) <= kCUs) return I8_M192N64_K2;
     if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs) return I8_M192N96_K2;

@@ -270,9 +270,15 @@ def test_i8_ladder():
                     assert info["tiles_m"] * info["rows"] >= M and info["tiles_n"] * info["cols"] >= N
                     assert info["tiles_m"] * info["tiles_n"] < 2 ** 31
                     assert K // info["k_step"] >= info["k_split"] >= 1, info
-    # few 192x64 tiles: 64x64 tiles with K also split across workgroups, up to 64 rows (Q6_K up
-    # to 256); measured winners on MI355X, the row quantizer included
-    for fmt, M, N, K, want in [("q6k", 16, 4096, 12288, "i8-64x64-sk"), ("q6k", 256, 4096, 12288, "i8-64x64-sk"),
+    # few 64x64 tiles (up to 96, 128 for Q6_K, and 256 over K >= 8192): those tiles with K also
+    # split across workgroups, at any M; measured winners on MI355X (every rung forced, weights
+    # rotating): Q4_K/W4A16 4096->1024 at M = 128..256 0.55-0.62 of the 192x64 time, 12288->4096
+    # at M = 128 0.60, at M = 256 0.85-0.91
+    for fmt, M, N, K, want in [("q4k", 256, 1024, 4096, "i8-64x64-sk"), ("w4a16", 128, 1024, 4096, "i8-64x64-sk"),
+                               ("q4k", 128, 4096, 12288, "i8-64x64-sk"), ("w4a16", 256, 4096, 12288, "i8-64x64-sk"),
+                               ("q6k", 128, 4096, 4096, "i8-64x64-sk"), ("q6k", 256, 4096, 4096, "i8-192x64-k2"),
+                               ("q4k", 256, 4096, 4096, "i8-192x64-k2"), ("q4k", 512, 4096, 12288, "i8-192x64-k2"),
+                               ("q6k", 16, 4096, 12288, "i8-64x64-sk"), ("q6k", 256, 4096, 12288, "i8-64x64-sk"),
                                ("q6k", 300, 4096, 12288, "i8-192x64-k2"), ("q4k", 64, 4096, 4096, "i8-64x64-sk"),
                                ("q4k", 96, 4096, 4096, "i8-192x64-k2"), ("q4k", 64, 6144, 4096, "i8-64x64-sk"),
                                ("q4k", 64, 12288, 4096, "i8-192x64-k2"), ("q6k", 658, 4096, 12288, "i8-192x64-k2")]:
