@@ -33,11 +33,21 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 // per wave, at most eight waves.  For decode-adjacent M (a pure weight
 // stream) a wave keeps at least eight chunks once the grid holds 512 waves:
 // with one chunk in flight ahead, shorter K ranges leave the stream idle
-// while each wave starts and drains (measured at M = 1..16).
-int pick_kw(long long groups, int nch, bool stream)
+// while each wave starts and drains (measured at M = 1..16); with one panel
+// per wave, four chunks per wave do pay while the grid stays within 2048
+// waves (K = 4096, every K split forced, weights rotating: N = 4096 6.2-6.9
+// against 7.7-8.3 us for four waves per workgroup, N = 2048 5.6-6.0 against
+// 6.2-6.5; at N = 6144, 3072 waves, they lose by 4-10%, and with four
+// panels per wave by up to 9%).
+int pick_kw(long long groups, int nch, bool stream, int pn)
 {
     int kw = 1;
-    while (kw < 8 && groups * kw < 2048 && nch / (2 * kw) >= ((stream && groups * kw >= 512) ? 8 : 2)) kw *= 2;
+    while (kw < 8 && groups * kw < 2048) {
+        const int per = nch / (2 * kw);  // chunks per wave after doubling
+        if (per < ((stream && groups * kw >= 512) ? 8 : 2) && !(stream && pn == 1 && per >= 4 && groups * 2 * kw <= 2048))
+            break;
+        kw *= 2;
+    }
     return kw;
 }
 
@@ -120,7 +130,7 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     pl.split = 1;
     pl.tiles_n = (int)pl.grid.x;
     pl.tiles_m = (int)pl.grid.y;
-    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch, M <= 16);
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, nch, M <= 16, pl.pn);
     pl.waves = pl.kw;
     pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
     return launch_fits(pl.grid.x, 64 * pl.kw) ? QGEMM_OK : QGEMM_ERR_SHAPE;
@@ -534,7 +544,7 @@ Plan grouped_plan(int fmt, long long T, long long E, long long N, long long K)
     pl.pn = 4;
     pl.rb = avg <= 16 ? 1 : (avg <= 32 || fmt != FMT_Q4K) ? 2 : 3;
     pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)(ceil_div(T, 16 * pl.rb) + E), 1);
-    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, (int)(K / kChunk), false);
+    pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, (int)(K / kChunk), false, pl.pn);
     pl.waves = pl.kw;
     pl.rows = 16 * pl.rb;
     pl.cols = 64;
