@@ -166,8 +166,12 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 // On fragment-major activations the three-waves-per-SIMD tiles come first
 // where they fit (192x64 and 192x96 with K split over two 6-wave groups,
 // 352x96; the rules are in select_rung), the K-split 128x128 tile serves the
-// other shapes with at most 256 of its tiles, and the 256-row tile also wins
-// whenever it has 512 tiles.
+// other shapes with at most 256 of its tiles, the 256-row tile also wins
+// whenever it has 512 tiles, and 192x96 replaces it where the round costs
+// put its whole rounds 5% lower.  Row-major Q6_K, which has no 160-wide
+// tile, takes the 352x96 tile by the same occupancy rule, one round of
+// 192x96 tiles where the 256-row tile would serve, and the 256-row tile from
+// 512 of its tiles.
 // Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
 // of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
 // the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that
