@@ -24,7 +24,9 @@ Profiling helpers (same JSON line, restricted work):
                         totalling >= MB (default 640), so the 256 MB Infinity
                         Cache cannot serve them (0: one copy)
     --rung R            force rung R instead of the M-ladder's choice
-    --x-layout xf|row   activation layout the GEMMs read (default xf)
+    --x-layout xf|row   activation layout the GEMMs read (default xf; row for
+                        the mixture-of-experts FFN, where the two steps tie:
+                        the grouped GEMMs gain about what the copies cost)
     --no-merge          seven separate GEMMs instead of qkv, o, gate_up, down
     --copy-calibration BYTES
                         run a plain device-to-device copy of BYTES bytes three
@@ -156,8 +158,9 @@ def main() -> int:
     ap.add_argument("--rung", type=int, default=-1, help="force a rung (-1: M-ladder)")
     ap.add_argument("--no-merge", action="store_true",
                     help="run the projections that share an input (q/k/v, gate/up) as separate GEMMs")
-    ap.add_argument("--x-layout", choices=["xf", "row"], default="xf",
-                    help="xf: fragment-major copies made inside the step (default); row: row-major X")
+    ap.add_argument("--x-layout", choices=["xf", "row"], default=None,
+                    help="xf: fragment-major copies made inside the step (default of the dense layers); row: row-major "
+                         "X (default of the mixture-of-experts FFN, whose routed rows arrive row-major)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--no-staged", action="store_true", help="skip the staged-arm comparison")
@@ -176,6 +179,9 @@ def main() -> int:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path would shard by N or K across GPUs, which is not built here)", file=sys.stderr)
         return 2
+
+    if args.x_layout is None:
+        args.x_layout = "row" if args.workload in synth.MOE_WORKLOADS else "xf"
 
     import torch
 
@@ -546,10 +552,14 @@ def mfma_ceiling(dt) -> dict:
 
 def run_grouped(args) -> int:
     """A mixture-of-experts FFN at prompt size: each GEMM is one grouped launch
-    over the routed rows (already grouped by expert), against the same work
-    issued as one launch per expert.  Weight-bound, so the experts' weights
-    rotate through copies totalling >= --pool-mb, and the streaming-read probe
-    of the same bytes sits beside each GEMM."""
+    over the routed rows (already grouped by expert), by default on those
+    row-major rows; --x-layout xf runs them on the rows' fragment-major copy
+    made inside the step (one copy for gate and up, which read the same rows,
+    one for down).  Beside it: the two layouts' steps and GEMMs interleaved,
+    and the same work issued as one launch per expert.  Weight-bound, so the
+    experts' weights rotate through copies totalling >= --pool-mb, and the
+    streaming-read probe of the same bytes sits beside each GEMM.  Launches
+    are pre-marshalled C calls on one stream, timed as the layer step is."""
     import torch
 
     name = args.workload
@@ -558,9 +568,18 @@ def run_grouped(args) -> int:
     counts = synth.moe_counts(name)
     offs_h = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     T = int(offs_h[-1])
+    lib = qg.lib()
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    timer = HipTimer()
+
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr())
+
     offs = torch.from_numpy(offs_h).cuda()
-    stream = torch.cuda.current_stream()
-    gemms = []
+    xf_layout = args.x_layout == "xf"
+    gemms, inputs = [], {}
     for j, (label, fmt, K, N) in enumerate(w["gemms"]):
         if args.only is not None and label != args.only:
             continue
@@ -571,78 +590,129 @@ def run_grouped(args) -> int:
         del per, fields, enc
         ncopy = max(1, int(np.ceil(args.pool_mb * 1e6 / wp.numel()))) if args.pool_mb > 0 else 1
         pool = [wp] + [wp.clone() for _ in range(ncopy - 1)]
-        x = torch.from_numpy(X.view(np.int16)).view(torch.float16).cuda()
+        src = w["input_of"][j]
+        if src not in inputs:
+            x = torch.from_numpy(X.view(np.int16)).view(torch.float16).cuda()
+            xf = torch.empty(qg.xf_bytes(T, K) // 2, dtype=torch.float16, device="cuda")
+            inputs[src] = dict(label=f"x_to_xf({w['gemms'][src][0]})", x=x, xf=xf, K=K,
+                               call=functools.partial(lib.qgemm_x_to_xf, ptr(x), ptr(xf), T, K, sp))
+        inp = inputs[src]
         y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+        F = qg.FORMATS[fmt]
+        calls = {"xf": [functools.partial(lib.qgemm_grouped_xf, F, ptr(inp["xf"]), ptr(wq), ptr(y), ptr(offs), E, T, N,
+                                          K, 0, 0, qg.F16, sp) for wq in pool],
+                 "row": [functools.partial(lib.qgemm_grouped, F, ptr(inp["x"]), ptr(wq), ptr(y), ptr(offs), E, T, N, K,
+                                           0, 0, qg.F16, sp) for wq in pool]}
         used = int((counts > 0).sum())
-        gemms.append(dict(label=label, fmt=fmt, K=K, N=N, x=x, y=y, pool=pool, turn=0, stride=stride,
+        gemms.append(dict(label=label, fmt=fmt, K=K, N=N, inp=inp, y=y, pool=pool, turn=0, stride=stride, calls=calls,
                           flops=2.0 * T * N * K, wbytes=float(used * stride)))
-        print(f"[bench] {label}: grouped {fmt} T={T} K={K} N={N} E={E} ({used} with rows)", file=sys.stderr, flush=True)
+        print(f"[bench] {label}: grouped {fmt} T={T} K={K} N={N} E={E} ({used} with rows), rows of "
+              f"{w['gemms'][src][0]}, x={args.x_layout}", file=sys.stderr, flush=True)
+    if not gemms:
+        print(f"bench.py: no GEMM labelled {args.only!r} in {name}", file=sys.stderr)
+        return 2
 
-    def call(g):
-        wp = g["pool"][g["turn"] % len(g["pool"])]
+    def call(g, layout):
+        st = g["calls"][layout][g["turn"] % len(g["pool"])]()
         g["turn"] += 1
-        qg.grouped(g["fmt"], g["x"], wp, g["N"], offs, E, out=g["y"])
+        if st != 0:
+            raise qg.QGemmError(f"{g['label']} grouped GEMM", st)
 
-    def timed(fn, reps):
-        fn()
-        samples = []
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            samples.append(e0.elapsed_time(e1) / reps)
-        return float(np.median(samples))
+    def copy(inp):
+        st = inp["call"]()
+        if st != 0:
+            raise qg.QGemmError(inp["label"], st)
 
-    for _ in range(args.warmup):
+    def step(layout):
+        if layout == "xf":
+            for inp in inputs.values():
+                copy(inp)
         for g in gemms:
-            call(g)
+            call(g, layout)
+
+    lay = "xf" if xf_layout else "row"
+    for _ in range(args.warmup):
+        step(lay)
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in gemms]
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for s_ in range(args.steps):
+
+    # per-launch times: an untimed pass with events around every launch
+    nprof = max(3, min(args.steps, PROFILE_STEPS))
+    inps = list(inputs.values()) if xf_layout else []
+    evc = [[timer.pair() for _ in inps] for _ in range(nprof)]
+    ev = [[timer.pair() for _ in gemms] for _ in range(nprof)]
+    for s_ in range(nprof):
+        for i, inp in enumerate(inps):
+            timer.record(evc[s_][i][0], sp)
+            copy(inp)
+            timer.record(evc[s_][i][1], sp)
         for j, g in enumerate(gemms):
-            ev[s_][j][0].record(stream)
-            call(g)
-            ev[s_][j][1].record(stream)
+            timer.record(ev[s_][j][0], sp)
+            call(g, lay)
+            timer.record(ev[s_][j][1], sp)
+    torch.cuda.synchronize()
+
+    # timed region: K steps in (up to) ten samples of consecutive steps,
+    # events only at the samples' ends
+    nsamp = min(10, args.steps)
+    bounds = [round(i * args.steps / nsamp) for i in range(nsamp + 1)]
+    evs = [timer.pair() for _ in range(nsamp)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(nsamp):
+        timer.record(evs[i][0], sp)
+        for s_ in range(bounds[i], bounds[i + 1]):
+            step(lay)
+        timer.record(evs[i][1], sp)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    sample_ms = [timer.ms(*evs[i]) / (bounds[i + 1] - bounds[i]) for i in range(nsamp)]
+
+    steps_cmp = interleaved({"fragment_major_with_copies": lambda: step("xf"), "row_major": lambda: step("row")},
+                            reps=10)
     out_k = []
+    for i, inp in enumerate(inps):
+        ms = float(np.mean([timer.ms(*evc[s_][i]) for s_ in range(nprof)]))
+        out_k.append(dict(label=inp["label"], T=T, K=inp["K"], ms=round(ms, 5),
+                          gbps=round(4.0 * T * inp["K"] / ms / 1e6, 1)))
     for j, g in enumerate(gemms):
-        ms = float(np.mean([ev[s_][j][0].elapsed_time(ev[s_][j][1]) for s_ in range(args.steps)]))
-        b2b = timed(lambda: call(g), 50)
+        ms = float(np.mean([timer.ms(*ev[s_][j]) for s_ in range(nprof)]))
+        b2b = interleaved({"xf": lambda: call(g, "xf"), "row": lambda: call(g, "row")})
 
         def per_expert():
             wp = g["pool"][0]
             for e in range(E):
                 if counts[e]:
                     a, b = int(offs_h[e]), int(offs_h[e + 1])
-                    qg.gemm_rung(g["fmt"], -1, g["x"][a:b], wp[e * g["stride"]:(e + 1) * g["stride"]], g["N"],
+                    qg.gemm_rung(g["fmt"], -1, g["inp"]["x"][a:b], wp[e * g["stride"]:(e + 1) * g["stride"]], g["N"],
                                  out=g["y"][a:b])
-        loop = timed(per_expert, 3)
+        loop = interleaved({"loop": per_expert}, reps=3, rounds=3)["loop"]
         rd = read_ceiling(g["pool"])
         out_k.append(dict(label=g["label"], fmt=g["fmt"], T=T, K=g["K"], N=g["N"], experts=E, ms=round(ms, 5),
-                          tflops=round(g["flops"] / ms / 1e9, 2), ms_back_to_back=round(b2b, 5),
-                          weight_gbps_back_to_back=round(g["wbytes"] / b2b / 1e6, 1), read_probe_gbps=rd,
-                          weight_frac_of_read_probe=round(g["wbytes"] / b2b / 1e6 / rd, 4),
+                          tflops=round(g["flops"] / ms / 1e9, 2), weight_gbps=round(g["wbytes"] / ms / 1e6, 1),
+                          read_probe_gbps=rd, weight_frac_of_read_probe=round(g["wbytes"] / ms / 1e6 / rd, 4),
+                          back_to_back_ms_by_layout={k: round(v, 5) for k, v in b2b.items()},
                           per_expert_launches_ms=round(loop, 5), weight_copies=len(g["pool"])))
+    timer.close()
     flops_step = sum(g["flops"] for g in gemms)
-    jd = int(np.argmax([p["ms"] for p in out_k]))
-    gd, pd = gemms[jd], out_k[jd]
+    gk = [p for p in out_k if "fmt" in p]
+    jd = int(np.argmax([p["ms"] for p in gk]))
+    gd, pd = gemms[jd], gk[jd]
     gbps = (gd["wbytes"] + 2.0 * T * gd["K"] + 2.0 * T * gd["N"]) / (pd["ms"] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_HBM_GBPS, 4), "kernel": f"{gd['label']} (grouped {gd['fmt']} T={T} K={gd['K']} N={gd['N']} E={E})",
             "traffic": None, "frac_of_sustained": pd["weight_frac_of_read_probe"]}
     print(json.dumps({
         "metric": METRIC, "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(float(np.median(sample_ms)), 5),
+        "ms_per_step_samples": [round(v, 5) for v in sample_ms],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded; routed row counts drawn from a Zipf-like expert popularity, random weights)",
         "config": {"workload": name, "tokens": w["tokens"], "top_k": w["top_k"], "experts": E, "rows": T,
-                   "rows_per_expert_min_mean_max": [int(counts.min()), round(float(counts.mean()), 1), int(counts.max())]},
+                   "rows_per_expert_min_mean_max": [int(counts.min()), round(float(counts.mean()), 1), int(counts.max())],
+                   "x_layout": "fragment-major (copies of the routed rows made inside the step: one for gate and up, one "
+                               "for down)" if xf_layout else "row-major"},
+        "steps_interleaved_ms": {k: round(v, 5) for k, v in steps_cmp.items()},
         "per_kernel": out_k, "roofline": roof}), flush=True)
     return 0
 

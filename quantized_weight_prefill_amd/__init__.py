@@ -84,6 +84,7 @@ SIGNATURES = {
     "qgemm_workspace_bytes": (_SZ, [_INT, _INT, _INT, _I64, _I64, _I64, _INT]),
     "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_grouped": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_grouped_xf": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_staged_scratch_bytes": (_SZ, [_I64, _I64]),
     "qgemm_staged": (_INT, [_INT, _VP, _VP, _VP, _SZ, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_xf_bytes": (_SZ, [_I64, _I64]),
@@ -629,6 +630,27 @@ def grouped(fmt, x, wp, N: int, offsets, E: int, group: int = 0, has_zp: bool = 
                              group, int(bool(has_zp)), _dtype_code(x), _stream(stream))
     _check("qgemm_grouped", st)
     return y
+
+
+def grouped_xf(fmt, xf, wp, T: int, N: int, K: int, offsets, E: int, group: int = 0, has_zp: bool = False, out=None,
+               stream=None):
+    """:func:`grouped` with the routed rows given as their fragment-major copy
+    `xf` (from :func:`x_to_xf` of the [T, K] rows); returns Y [T, N]."""
+    torch = _torch()
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    if xf.numel() < xf_bytes(T, K) // 2:
+        raise ValueError("xf is smaller than the fragment-major copy of a T x K matrix")
+    _check_wp(f, wp, N, K, group, has_zp, experts=E)
+    if out is None:
+        out = torch.empty((T, N), dtype=xf.dtype, device=xf.device)
+    elif tuple(out.shape) != (T, N) or out.dtype != xf.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, N] tensor of xf's dtype")
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.numel() != E + 1:
+        raise ValueError("offsets must be an int32 device tensor of E+1 entries")
+    st = lib().qgemm_grouped_xf(f, _dev(xf, "xf"), _dev(wp, "wp"), _dev(out, "out"), _dev(offsets, "offsets"), E, T, N,
+                                K, group, int(bool(has_zp)), _dtype_code(xf), _stream(stream))
+    _check("qgemm_grouped_xf", st)
+    return out
 
 
 def staged_scratch_bytes(N: int, K: int) -> int:

@@ -536,17 +536,17 @@ long long packed_bytes(int fmt, long long N, long long K, long long group, int h
     return (long long)qgemm_w4a16_packed_bytes(N, K, group, has_zp);
 }
 
-// Grouped plan: four panels per wave, row blocks sized by the mean rows per
-// expert (three 16-row blocks only for Q4_K, whose runs fit that variant),
+// Grouped plan: four panels per wave, one or two 16-row blocks by the mean
+// rows per expert (the three-block variant spills with the expert search),
 // grid.y an upper bound on every expert's row blocks, K split as the direct
 // rungs do.
-Plan grouped_plan(int fmt, long long T, long long E, long long N, long long K)
+Plan grouped_plan(long long T, long long E, long long N, long long K)
 {
     Plan pl{};
     const long long np = (N + 15) / 16, avg = (T + E - 1) / E;
     pl.rung = -1;
     pl.pn = 4;
-    pl.rb = avg <= 16 ? 1 : (avg <= 32 || fmt != FMT_Q4K) ? 2 : 3;
+    pl.rb = avg <= 16 ? 1 : 2;
     pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)(ceil_div(T, 16 * pl.rb) + E), 1);
     pl.kw = pick_kw((long long)pl.grid.x * pl.grid.y, (int)(K / kChunk), false, pl.pn);
     pl.waves = pl.kw;
@@ -556,8 +556,22 @@ Plan grouped_plan(int fmt, long long T, long long E, long long N, long long K)
     return pl;
 }
 
+// The 64x64 streaming tiles or the direct kernel: measured with both forced
+// (E = 32 and 128 experts, 24-82 rows per expert on average, Zipf-like
+// counts, Q4_K 2048 -> 768 and Q6_K 768 -> 2048, weights rotating), the
+// tiles win from about 64 rows per expert on fragment-major X at any K
+// (128 experts, 64 rows: Q4_K 82 against 86 us, Q6_K 97 against 104; at 41
+// rows the direct kernel, 62 against 67 and 72 against 83); on row-major X,
+// whose activation loads touch a cache line per row, from more rows and
+// only over 16 or more chunks.
+bool grouped_tiles(int xl, long long T, long long E, long long K)
+{
+    const long long avg = (T + E - 1) / E;
+    return xl == X_FRAG ? avg > 56 : avg > 64 && K / kChunk >= 16;
+}
+
 int grouped(int fmt, const void *X, const void *W, void *Y, const int32_t *offs, long long E, long long T, long long N,
-            long long K, long long group, int has_zp, int dtype, void *stream)
+            long long K, long long group, int has_zp, int dtype, void *stream, int xl)
 {
     if (fmt == FMT_W4 && group == 0) return QGEMM_ERR_FORMAT;
     int st = check_shape(fmt, T, N, K, group);
@@ -574,17 +588,13 @@ int grouped(int fmt, const void *X, const void *W, void *Y, const int32_t *offs,
     a.offs = offs;
     a.E = (int)E;
     a.wstride = wstride;
-    // more than 32 rows per expert on average and at least 16 chunks: 64x64
-    // streaming tiles, which read an expert's activation rows once per 64
-    // columns (the direct kernel reads them once per 16): 128 experts, 41
-    // rows each on average, Q4_K 2048 -> 768: 80-81 against 101 us; over 6
-    // chunks (Q6_K 768 -> 2048) the direct kernel stays ahead, 91 against 94
-    const bool tiles = (T + E - 1) / E > 32 && K / kChunk >= 16;
-    const Plan pl = grouped_plan(fmt, T, E, N, K);
-    if (tiles ? !launch_fits(((N + 63) / 64) * ((T + 63) / 64 + E), 128) : !launch_fits(pl.grid.x, 64 * pl.kw))
+    const bool tiles = grouped_tiles(xl, T, E, K);
+    const Plan pl = grouped_plan(T, E, N, K);
+    if (tiles ? !launch_fits(((N + 63) / 64) * (((T + 63) / 64 + E + 7) / 8 * 8), 128)
+              : !launch_fits(pl.grid.x, 64 * pl.kw))
         return QGEMM_ERR_SHAPE;
     a.kw = pl.kw;
-    return launch_status(launch_grouped(fmt, dtype, tiles, pl, a, T, E, (hipStream_t)stream), "grouped");
+    return launch_status(launch_grouped(fmt, dtype, xl, tiles, pl, a, T, E, (hipStream_t)stream), "grouped");
 }
 
 size_t staged_scratch_bytes(long long N, long long K)
@@ -974,7 +984,15 @@ int qgemm_staged(int format, const void *X, const void *Wpacked, void *scratch, 
 int qgemm_grouped(int format, const void *X, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E, int64_t T,
                   int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream)
 {
-    return grouped(format, X, Wpacked, Y, offsets, E, T, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream);
+    return grouped(format, X, Wpacked, Y, offsets, E, T, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream,
+                   X_ROW);
+}
+
+int qgemm_grouped_xf(int format, const void *Xf, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E,
+                     int64_t T, int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream)
+{
+    return grouped(format, Xf, Wpacked, Y, offsets, E, T, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream,
+                   X_FRAG);
 }
 
 size_t qgemm_i8_xq_bytes(int64_t M, int64_t K)

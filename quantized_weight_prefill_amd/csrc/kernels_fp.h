@@ -113,32 +113,6 @@ __global__ void __launch_bounds__(512) k_direct(Args a)
     direct_body<FMT, DT, RB, PN, XL>(a, blockIdx.x * PN, blockIdx.y * (16 * RB));
 }
 
-// Grouped per-expert GEMM: rows offs[e] .. offs[e+1]-1 of X and Y use expert
-// e's weights (expert e's packed bytes start at W + e*wstride).  grid.y is an
-// upper bound on the row blocks of all experts (ceil(T/R) + E, T = a.M);
-// workgroup y walks the experts' block counts to find its own, and the ones
-// past the last block exit.  Offsets are clamped into [0, T] and made
-// non-decreasing, so no access leaves X, Y or W whatever they hold.
-template <int FMT, int DT, int RB, int PN>
-__global__ void __launch_bounds__(512) k_direct_grouped(Args a)
-{
-    constexpr int R = 16 * RB;
-    const int j = blockIdx.y;
-    int base = 0, lo = 0, hi = 0, e = 0;
-    for (; e < a.E; e++) {
-        lo = min(max(a.offs[e], hi), a.M);
-        hi = min(max(a.offs[e + 1], lo), a.M);
-        const int nb = (hi - lo + R - 1) / R;
-        if (j < base + nb) break;
-        base += nb;
-    }
-    if (e >= a.E) return;  // the whole workgroup leaves together, before any barrier
-    Args b = a;
-    b.W = a.W + (long long)e * a.wstride;
-    b.M = hi;
-    direct_body<FMT, DT, RB, PN, X_ROW>(b, blockIdx.x * PN, lo + (j - base) * R);
-}
-
 // ---------------------------------------------------------------------------
 // Streaming tile kernel: mid and long prefill.
 //
@@ -512,15 +486,21 @@ k_stream32(Args a)
 }
 
 // ---------------------------------------------------------------------------
-// Grouped streaming tiles (per-expert GEMM, rows pre-grouped by expert):
-// each workgroup owns one 64x64 tile of one expert (two 32-row waves per K
-// group, KS K groups reduced through LDS as in k_stream32), so an expert's
-// activation rows are read once per 64 columns instead of once per 16 as in
-// k_direct_grouped.  Grid: (ceil(T/64) + E) row-tile slots (an upper bound of
-// the experts' row tiles) times the column tiles; a workgroup finds its
-// expert by scanning the device offsets (clamped to be non-decreasing and at
-// most T, as k_direct_grouped does) and leaves at once, before any barrier,
-// when its slot is past the last tile.  Activations row-major.
+// Grouped per-expert GEMM: rows offs[e] .. offs[e+1]-1 of X and Y use expert
+// e's weights (expert e's packed bytes start at W + e*wstride).  Offsets are
+// clamped into [0, T] and made non-decreasing, so no access leaves X, Y or W
+// whatever they hold.  Each workgroup owns one row tile of one expert: the
+// grid carries an upper bound on the experts' row tiles (ceil(T/R) + E
+// slots for R-row tiles), a workgroup finds its expert and tile with
+// find_group_tile, and the ones past the last tile leave at once, before any
+// barrier.  Two kernels:
+//   * k_direct_grouped: the direct kernel's body on 16*RB rows x 4 panels
+//     (few rows per expert: each weight unpacked once per row tile);
+//   * k_stream32_grouped: 64x64 streaming tiles (two 32-row waves), which
+//     read an expert's activation rows once per 64 columns.
+// Both take row-major or fragment-major X (the fragment-major copy of the T
+// routed rows; a tile's rows may start anywhere inside a 32-row block, each
+// lane addresses its own row).
 // ---------------------------------------------------------------------------
 // Row tile j of the grouped problem: expert e, rows [lo, hi) of the expert
 // (offsets clamped as k_direct_grouped clamps them), tile t of it; false
@@ -568,19 +548,40 @@ __device__ __forceinline__ bool find_group_tile(const Args &a, int j, int BMt, i
     return false;
 }
 
-template <int FMT, int DT, int KS>
+// Grid: x = panel groups of PN panels, y = row-tile slots of 16*RB rows.
+template <int FMT, int DT, int RB, int PN, int XL>
+__global__ void __launch_bounds__(512) k_direct_grouped(Args a)
+{
+    constexpr int R = 16 * RB;
+    int e, lo, hi, t;
+    // the same answer in every wave: the whole workgroup leaves together
+    if (!find_group_tile(a, blockIdx.y, R, threadIdx.x & 63, e, lo, hi, t)) return;
+    Args b = a;
+    b.W = a.W + (long long)e * a.wstride;
+    b.M = hi;
+    direct_body<FMT, DT, RB, PN, XL>(b, blockIdx.x * PN, lo + t * R);
+}
+
+// Grid: 8 * ceil(slots/8) * tn workgroups (slots = ceil(T/64) + E row-tile
+// slots, tn column tiles).  Row slot j and all its column tiles run on XCD
+// j % 8 (workgroup b runs on XCD b % 8), so an expert's activation rows are
+// fetched into one XCD's L2, and the slots past the last tile, which leave
+// at once, are spread over all XCDs.
+template <int FMT, int DT, int KS, int XL>
 __global__ void __launch_bounds__(128 * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_stream32_grouped(Args a)
 {
-    using St = Stream32<FMT, DT, 32, 4, 2, 1, X_ROW>;
+    using St = Stream32<FMT, DT, 32, 4, 2, 1, XL>;
     constexpr int CBW = St::CBW, RBW = St::RBW, PB = St::PB, BM = St::BM;
     constexpr int NACC = 2 * CBW * RBW * 64;
     static_assert(KS == 1 || (KS - 1) * NACC * sizeof(f32x16) <= KS * sizeof(typename St::Lds),
                   "K-split reduction must fit in LDS");
     __shared__ typename St::Lds sWall[KS];
 
-    const int tn = (a.np + PB - 1) / PB;
-    const int nt = blockIdx.x % tn, j = blockIdx.x / tn;
+    const int tn = (a.np + PB - 1) / PB, slots = (a.M + BM - 1) / BM + a.E;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nt = q % tn, j = xcd + 8 * (q / tn);
+    if (j >= slots) return;
     const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
     int e, lo, hi, t;
     // every wave computes the same answer: the whole workgroup leaves

@@ -69,8 +69,9 @@ hipError_t launch_dequant(int fmt, int dtype, const Args &a, uint16_t *out, hipS
 hipError_t launch_x_to_xf(const uint16_t *X, uint16_t *Xf, int M, int K, hipStream_t s);
 hipError_t launch_staged(int fmt, int dtype, const Args &a, uint8_t *scratch, const Plan &pl, hipStream_t s);
 // misc_grouped.hip: the direct grouped kernel with the Plan's row blocks, or
-// (stream_tiles) the 64x64 streaming tiles over T rows and E experts
-hipError_t launch_grouped(int fmt, int dtype, bool stream_tiles, const Plan &pl, const Args &a, long long T,
+// (stream_tiles) the 64x64 streaming tiles over T rows and E experts, on
+// activations of layout xl (X_ROW or X_FRAG)
+hipError_t launch_grouped(int fmt, int dtype, int xl, bool stream_tiles, const Plan &pl, const Args &a, long long T,
                           long long E, hipStream_t s);
 
 // api.hip: the checked fp16/bf16 GEMM of qgemm_gemm_rung (layout X_ROW) and

@@ -326,6 +326,7 @@ MOE_WORKLOADS = {
     "moe_e128_top8_m658": {  # 128 experts, 8 per token, hidden 2048, expert width 768, 658 prompt tokens
         "index": 6, "tokens": 658, "experts": 128, "top_k": 8, "zipf": 0.8,
         "gemms": [("gate", "q4k", 2048, 768), ("up", "q4k", 2048, 768), ("down", "q6k", 768, 2048)],
+        "input_of": [0, 0, 2],  # GEMM j reads the routed rows of GEMM input_of[j]: gate and up share theirs
     },
 }
 
@@ -346,11 +347,12 @@ def moe_counts(name: str) -> np.ndarray:
 
 def moe_inputs(name: str, j: int, dtype: int = F16):
     """(X bits [T][K], weight fields of all experts as one N*E-column matrix,
-    encoded blocks) of GEMM j; expert e owns columns e*N .. (e+1)*N-1."""
+    encoded blocks) of GEMM j; expert e owns columns e*N .. (e+1)*N-1.  GEMMs
+    that read the same routed rows (gate and up) get the same X."""
     w = MOE_WORKLOADS[name]
     label, fmt, K, N = w["gemms"][j]
     T = int(moe_counts(name).sum())
     rs = streams(2000 + w["index"], 2 * len(w["gemms"]))
-    X = activations(rs[2 * j], T, K, dtype)
+    X = activations(rs[2 * w["input_of"][j]], T, K, dtype)
     fields = weight_fields(fmt, rs[2 * j + 1], N * w["experts"], K)
     return X, fields, encode(fmt, fields)

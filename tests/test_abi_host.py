@@ -190,6 +190,13 @@ def test_device_entry_argument_errors():
     assert lib.qgemm_grouped(2, A, A, A, A, 2, 8, 16, 128, 128, 1, 0, s) == -4     # 1064-byte experts
     assert lib.qgemm_grouped(0, None, None, None, None, 3, 0, 16, 256, 0, 0, 0, s) == 0  # T = 0
     assert lib.qgemm_grouped(1, A, A, A, A, 2, 8, 16, 300, 0, 0, 0, s) == -2
+    # the same checks on fragment-major routed rows
+    assert lib.qgemm_grouped_xf(0, A, A, A, A, 0, 8, 16, 256, 0, 0, 0, s) == -2
+    assert lib.qgemm_grouped_xf(0, A, A, A, None, 2, 8, 16, 256, 0, 0, 0, s) == -1
+    assert lib.qgemm_grouped_xf(0, mis, A, A, ctypes.c_void_p((1 << 20) + 2), 2, 8, 16, 256, 0, 0, 0, s) == -4
+    assert lib.qgemm_grouped_xf(0, None, None, None, None, 3, 0, 16, 256, 0, 0, 0, s) == 0
+    assert lib.qgemm_grouped_xf(0, A, A, A, A, 2, 8, 16, 256, 0, 0, 5, s) == -3
+    assert lib.qgemm_grouped_xf(0, A, A, A, A, 2, 1 << 20, 16, 256, 0, 0, 0, s) == -2  # grid.y beyond 65535
     # staged arm: scratch checks come before any launch
     need = lib.qgemm_staged_scratch_bytes(20, 512)
     assert need == 32 * 512 * 2 and lib.qgemm_staged_scratch_bytes(20, 200) == 0
@@ -720,11 +727,15 @@ def test_binding_checks_buffers_before_any_call():
     short = torch.zeros(full - 16, dtype=torch.uint8)
     ok = torch.zeros(full, dtype=torch.uint8)
     offs = torch.zeros(3, dtype=torch.int32)
+    xf = torch.zeros(qg.xf_bytes(M, K) // 2, dtype=torch.float16)
     for call in (lambda: qg.q4k(x, short, N), lambda: qg.gemm_rung("q4k", -1, x, short, N),
                  lambda: qg.staged("q4k", x, short, N), lambda: qg.grouped("q4k", x, ok, N, offs, 2),
+                 lambda: qg.grouped_xf("q4k", xf, ok, M, N, K, offs, 2),
                  lambda: qg.dequant("q4k", short, N, K, qg.F16)):
         with pytest.raises(ValueError, match="packed weight"):
             call()
+    with pytest.raises(ValueError, match="fragment-major"):
+        qg.grouped_xf("q4k", xf[:-8], torch.zeros(2 * full, dtype=torch.uint8), M, N, K, offs, 2)
     w4_sym = qg.packed_bytes("w4a16", N, K, 128, False)
     assert w4_sym < qg.packed_bytes("w4a16", N, K, 128, True)
     with pytest.raises(ValueError, match="packed weight"):  # an asymmetric call on a symmetric packing
@@ -734,11 +745,12 @@ def test_binding_checks_buffers_before_any_call():
     two = torch.zeros(2 * full, dtype=torch.uint8)
     for out in (bad_out, bad_dt):
         for call in (lambda: qg.grouped("q4k", x, two, N, offs, 2, out=out), lambda: qg.staged("q4k", x, ok, N, out=out),
+                     lambda: qg.grouped_xf("q4k", xf, two, M, N, K, offs, 2, out=out),
                      lambda: qg.gemm_rung("q4k", -1, x, ok, N, out=out), lambda: qg.q6k(x, torch.zeros(
                          qg.packed_bytes("q6k", N, K), dtype=torch.uint8), N, out=out)):
             with pytest.raises(ValueError, match="out"):
                 call()
-    for fn in (qg.grouped, qg.staged, qg.gemm_rung, qg.gemm_xf, qg.gemm_i8, qg.dequant, qg.i8_colscale):
+    for fn in (qg.grouped, qg.grouped_xf, qg.staged, qg.gemm_rung, qg.gemm_xf, qg.gemm_i8, qg.dequant, qg.i8_colscale):
         assert inspect.signature(fn).parameters["has_zp"].default is False, fn.__name__
 
 

@@ -138,11 +138,12 @@ def test_exact_path_dequant_and_staged(dtype):
     assert_gemm_close(from_device(ys), Yref, B, dtype, what="staged wide-gap")
 
 
+@pytest.mark.parametrize("layout", ["row", "xf"])
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
 @pytest.mark.parametrize("K", [256, 2048])  # the direct grouped kernel, then the 64x64 streaming tiles
-def test_exact_path_grouped(dtype, K):
+def test_exact_path_grouped(dtype, K, layout):
     """Two experts, each fed an identity block, so each expert's rows of Y
-    are its weights bit for bit."""
+    are its weights bit for bit (row-major X and its fragment-major copy)."""
     import torch
 
     N, E = 48, 2
@@ -152,8 +153,12 @@ def test_exact_path_grouped(dtype, K):
     X = np.concatenate([_eye(K, dtype)] * E, axis=0)
     wp = bytes_to_device(np.concatenate([c.packed for c in cases]))
     offs = torch.tensor([0, K, 2 * K], dtype=torch.int32, device="cuda")
-    print(f"exact grouped dtype={dtype} K={K}", flush=True)
-    y = from_device(qg.grouped("q4k", to_device(X, dtype), wp, N, offs, E))
+    print(f"exact grouped dtype={dtype} K={K} layout={layout}", flush=True)
+    x = to_device(X, dtype)
+    if layout == "row":
+        y = from_device(qg.grouped("q4k", x, wp, N, offs, E))
+    else:
+        y = from_device(qg.grouped_xf("q4k", qg.x_to_xf(x), wp, E * K, N, K, offs, E))
     for e, c in enumerate(cases):
         assert same_bits(y[e * K:(e + 1) * K], c.W), f"expert {e}"
 

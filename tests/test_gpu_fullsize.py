@@ -52,11 +52,13 @@ def test_workload_sampled(name, j, layout):
 MOE_CASES = [("moe_e128_top8_m658", 0), ("moe_e128_top8_m658", 2)]  # gate (Q4_K), down (Q6_K)
 
 
+@pytest.mark.parametrize("layout", ["row", "xf"])
 @pytest.mark.parametrize("name,j", MOE_CASES, ids=[f"{n}-{synth.MOE_WORKLOADS[n]['gemms'][j][0]}" for n, j in MOE_CASES])
-def test_moe_grouped_sampled(name, j):
-    """The grouped per-expert GEMM at the MoE workload's full size, as the
-    benchmark launches it, on a seeded sample of outputs (first and last rows
-    included): each sampled row is checked against its own expert's weights."""
+def test_moe_grouped_sampled(name, j, layout):
+    """The grouped per-expert GEMM at the MoE workload's full size, on row-major
+    routed rows and on their fragment-major copy (as the benchmark launches
+    it), on a seeded sample of outputs (first and last rows included): each
+    sampled row is checked against its own expert's weights."""
     import torch
 
     w = synth.MOE_WORKLOADS[name]
@@ -65,10 +67,14 @@ def test_moe_grouped_sampled(name, j):
     counts = synth.moe_counts(name)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     T = int(offs[-1])
-    print(f"moe {name}/{label} fmt={fmt} T={T} K={K} N={N} E={E}", flush=True)
+    print(f"moe {name}/{label} fmt={fmt} T={T} K={K} N={N} E={E} layout={layout}", flush=True)
     X, fields, enc = synth.moe_inputs(name, j)
     packed = np.concatenate([qg.pack(fmt, enc[e * N:(e + 1) * N], N, K) for e in range(E)])
-    y = qg.grouped(fmt, to_device(X, qg.F16), bytes_to_device(packed), N, torch.from_numpy(offs).cuda(), E)
+    x, wp, offs_d = to_device(X, qg.F16), bytes_to_device(packed), torch.from_numpy(offs).cuda()
+    if layout == "row":
+        y = qg.grouped(fmt, x, wp, N, offs_d, E)
+    else:
+        y = qg.grouped_xf(fmt, qg.x_to_xf(x), wp, T, N, K, offs_d, E)
     Y = from_device(y)
     W = oracle.dequant(fmt, enc, E * N, K, qg.F16)
     rng = np.random.default_rng(4343 + j)

@@ -330,6 +330,17 @@ def _grouped_case(fmt, sym, counts, N, K, dtype, seed):
     return cases, X, torch.from_numpy(W_all).cuda(), torch.from_numpy(offs).cuda(), offs
 
 
+def _grouped_call(layout, fmt, X, W, N, offs_d, E, dtype, out=None, sym=True):
+    """One grouped launch on row-major X (qgemm_grouped) or on its
+    fragment-major copy (qgemm_grouped_xf)."""
+    x = to_device(X, dtype)
+    kw = dict(group=128 if fmt == "w4a16" else 0, has_zp=not sym, out=out)
+    if layout == "row":
+        return qg.grouped(fmt, x, W, N, offs_d, E, **kw)
+    T, K = X.shape
+    return qg.grouped_xf(fmt, qg.x_to_xf(x), W, T, N, K, offs_d, E, **kw)
+
+
 def _clamped_ranges(offs, T):
     """The row range each expert gets from arbitrary offsets, by the header's
     rule: every offset clamped into [0, T] and to at least the previous
@@ -342,24 +353,25 @@ def _clamped_ranges(offs, T):
     return out
 
 
+@pytest.mark.parametrize("layout", ["row", "xf"])
 @pytest.mark.parametrize("K", [512, 2048], ids=["direct", "stream"])
-def test_grouped_malformed_offsets(K):
+def test_grouped_malformed_offsets(K, layout):
     """Offsets that are negative, decreasing or past T: both grouped kernels
     (K = 512 takes the direct kernel, K = 2048 the 64x64 streaming tiles at
-    these 50 rows per expert) compute exactly the clamped ranges, and write
-    nothing outside Y."""
+    these 75 rows per expert) compute exactly the clamped ranges, and write
+    nothing outside Y, on both activation layouts."""
     import torch
 
-    T, N, fmt = 200, 80, "q4k"
-    offs = np.array([-5, 90, 40, 170, 500], np.int32)
+    T, N, fmt = 300, 80, "q4k"
+    offs = np.array([-5, 90, 40, 250, 700], np.int32)
     cases = [Case(fmt, T, N, K, qg.F16, seed=450 + e) for e in range(len(offs) - 1)]
     X = cases[0].X
     W = torch.from_numpy(np.concatenate([c.packed for c in cases])).cuda()
     pad = 4096
     buf = torch.full((T * N + 2 * pad,), 7.0, dtype=torch.float16, device="cuda")
     out = buf[pad:pad + T * N].view(T, N)
-    print(f"grouped malformed offsets K={K} offs={offs.tolist()}", flush=True)
-    qg.grouped(fmt, to_device(X, qg.F16), W, N, torch.from_numpy(offs).cuda(), len(cases), out=out)
+    print(f"grouped malformed offsets K={K} layout={layout} offs={offs.tolist()}", flush=True)
+    _grouped_call(layout, fmt, X, W, N, torch.from_numpy(offs).cuda(), len(cases), qg.F16, out=out)
     host = buf.cpu()
     assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
     Y = from_device(out)
@@ -376,31 +388,34 @@ def test_grouped_malformed_offsets(K):
 @pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
 def test_grouped_stream_parity(fmt, sym, dtype):
-    """The grouped 64x64 streaming tiles (more than 32 rows per expert on
-    average, at least 16 chunks): experts spanning several 64-row tiles,
-    empty and one-row experts, a ragged last column tile; rows outside every
-    expert's range are left untouched."""
+    """The grouped 64x64 streaming tiles (more than 64 rows per expert on
+    average, at least 16 chunks, on either activation layout): experts
+    spanning several 64-row tiles and starting inside a 32-row block, empty
+    and one-row experts, a ragged last column tile; rows outside every
+    expert's range are left untouched, and both layouts give the same bits."""
     import torch
 
     N, K = 144, 2048
-    counts = [0, 70, 130, 1, 65]
+    counts = [0, 70, 130, 1, 140]
     cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=410)
     T = int(offs[-1])
-    print(f"grouped stream {fmt} sym={sym} dtype={dtype} counts={counts}", flush=True)
-    pad = 4096
-    tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
-    buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
-    out = buf[pad:pad + T * N].view(T, N)
-    qg.grouped(fmt, to_device(X, dtype), W, N, offs_d, len(counts), group=128 if fmt == "w4a16" else 0,
-               has_zp=not sym, out=out)
-    host = buf.cpu()
-    assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
-    Y = from_device(out)
-    for e, (c, m) in enumerate(zip(cases, counts)):
-        if m == 0:
-            continue
-        Yref, B = oracle.gemm(c.X[:m], c.W, dtype)
-        assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"grouped stream expert {e} rows {m}")
+    outs = {}
+    for layout in ("row", "xf"):
+        print(f"grouped stream {fmt} sym={sym} dtype={dtype} layout={layout} counts={counts}", flush=True)
+        pad = 4096
+        tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
+        buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
+        out = buf[pad:pad + T * N].view(T, N)
+        _grouped_call(layout, fmt, X, W, N, offs_d, len(counts), dtype, out=out, sym=sym)
+        host = buf.cpu()
+        assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
+        outs[layout] = Y = from_device(out)
+        for e, (c, m) in enumerate(zip(cases, counts)):
+            if m == 0:
+                continue
+            Yref, B = oracle.gemm(c.X[:m], c.W, dtype)
+            assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"grouped stream {layout} expert {e} rows {m}")
+    assert np.array_equal(outs["row"], outs["xf"])
 
 
 @pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
@@ -408,26 +423,29 @@ def test_grouped_stream_parity(fmt, sym, dtype):
 def test_grouped_parity(fmt, sym, dtype):
     """Each expert's rows match the oracle on that expert's weights, with empty
     experts, one-row experts and ragged counts; mean rows per expert of 10, 27
-    and 44 select one, two and (Q4_K) three 16-row blocks per wave (K = 512 is
-    too short for the grouped streaming tiles)."""
+    and 44 select one and two 16-row blocks per wave (K = 512 and these
+    counts keep both layouts on the direct grouped kernel, so both give the
+    same bits)."""
     import torch
 
     N, K = 96, 512
     for counts in ([0, 1, 17, 40, 100, 3], [5, 0, 12, 3, 30, 10], [44, 60, 28]):
         cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=400)
         T = int(offs[-1])
-        print(f"grouped {fmt} sym={sym} dtype={dtype} counts={counts}", flush=True)
-        pad = 4096
-        tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
-        buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
-        out = buf[pad:pad + T * N].view(T, N)
-        qg.grouped(fmt, to_device(X, dtype), W, N, offs_d, len(counts), group=128 if fmt == "w4a16" else 0,
-                   has_zp=not sym, out=out)
-        host = buf.cpu()
-        assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
-        Y = from_device(out)
-        for e, (c, m) in enumerate(zip(cases, counts)):
-            if m == 0:
-                continue
-            Yref, B = oracle.gemm(c.X[:m], c.W, dtype)
-            assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"grouped expert {e} rows {m}")
+        outs = {}
+        for layout in ("row", "xf"):
+            print(f"grouped {fmt} sym={sym} dtype={dtype} layout={layout} counts={counts}", flush=True)
+            pad = 4096
+            tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
+            buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
+            out = buf[pad:pad + T * N].view(T, N)
+            _grouped_call(layout, fmt, X, W, N, offs_d, len(counts), dtype, out=out, sym=sym)
+            host = buf.cpu()
+            assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
+            outs[layout] = Y = from_device(out)
+            for e, (c, m) in enumerate(zip(cases, counts)):
+                if m == 0:
+                    continue
+                Yref, B = oracle.gemm(c.X[:m], c.W, dtype)
+                assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"grouped {layout} expert {e} rows {m}")
+        assert np.array_equal(outs["row"], outs["xf"])
