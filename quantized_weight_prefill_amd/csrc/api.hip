@@ -20,7 +20,8 @@ const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-
                                             "mfma16-256x128",    "mfma32-128x128",    "mfma32-128x128-k2",
                                             "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
                                             "mfma32-192x96-k2",  "mfma32-192x64-k2",  "mfma32-64x64-sk",
-                                            "mfma32-64x32-k4",   "mfma32-128x64-k2",  "mfma32-96x32-k4"};
+                                            "mfma32-64x32-k4",   "mfma32-128x64-k2",  "mfma32-96x32-k4",
+                                            "mfma32-768x96",     "mfma32-512x128",    "mfma32-512x96"};
 
 // A one-dimensional launch of gx workgroups of `threads` threads fits when
 // gx is at most 2^31-1 and the work-items along x at most 2^32-1.
@@ -90,18 +91,22 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M96N32_K4:
     case RUNG_M352N96:
     case RUNG_M192N96_K2:
-    case RUNG_M192N64_K2: {
-        const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2;
+    case RUNG_M192N64_K2:
+    case RUNG_M768N96:
+    case RUNG_M512N128:
+    case RUNG_M512N96: {
+        const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2 || rung == RUNG_M768N96 || rung == RUNG_M512N96;
+        const bool big = rung == RUNG_M768N96 || rung == RUNG_M512N128 || rung == RUNG_M512N96;  // 8 waves, K whole
         const bool r192 = rung == RUNG_M192N96_K2 || rung == RUNG_M192N64_K2;
         const bool r64 = rung == RUNG_M64_K4 || rung == RUNG_M64_SK || rung == RUNG_M64N32_K4;
         const bool k4 = r64 || rung == RUNG_M96N32_K4;  // K split over up to four groups
         pl.rows = rung == RUNG_M16_256 ? 256 : r64 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192
-                  : rung == RUNG_M96N32_K4 ? 96 : 128;
+                  : rung == RUNG_M96N32_K4 ? 96 : rung == RUNG_M768N96 ? 768 : big ? 512 : 128;
         pl.cols = rung == RUNG_M128N160 ? 160 : (rung == RUNG_M64N32_K4 || rung == RUNG_M96N32_K4) ? 32
                   : (r64 || rung == RUNG_M192N64_K2 || rung == RUNG_M128N64_K2) ? 64 : n96 ? 96 : 128;
         pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M128N64_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
         if (k4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
-        pl.waves = rung == RUNG_M16_256 ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M96N32_K4 ? 3 * pl.kw
+        pl.waves = (rung == RUNG_M16_256 || big) ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M96N32_K4 ? 3 * pl.kw
                    : rung == RUNG_M352N96 ? 11 : r192 ? 6 * pl.kw : 4 * pl.kw;
         // one-dimensional grid: the kernel renumbers tiles per XCD
         const long long tn = (np + pl.cols / 16 - 1) / (pl.cols / 16), tm = (M + pl.rows - 1) / pl.rows;
@@ -286,19 +291,50 @@ int round_model_rung(int fmt, long long M, long long N, long long K, int xl, int
     return large && M > 64 ? -1 : pick;
 }
 
-// The round model's cost of one streaming rung (its whole rounds times its
-// round cost), 1e30 when the table has no entry for it.
-double round_cost(int rung, int fmt, long long M, long long N, long long K, int xl)
+// Full-round cost of the large tiles on fragment-major activations, in
+// microseconds at K = 4096 per format (Q4_K, Q6_K, W4A16): medians of time /
+// rounds over the shapes whose last round is at least 75% full, every large
+// tile forced on M = 384..4096, N = 4096..24576, K = 4096 and 12288 (fp16,
+// weights rotating).  A round is 256 workgroups (512 for the 4-wave 128x128
+// and 128x160 tiles, two per CU).  The 8-wave tiles of 64- and 96-row waves
+// cost the most per round but unpack each weight once for 512 or 768 rows
+// and read a third to a half of the LDS bytes per MFMA.
+struct LargeCost {
+    int rung, per_cu;
+    float us[3];
+};
+constexpr LargeCost kLargeCostXf[] = {
+    {RUNG_M192N64_K2, 1, {31.8f, 34.5f, 31.0f}}, {RUNG_M128_K2, 1, {41.2f, 46.0f, 40.0f}},
+    {RUNG_M192N96_K2, 1, {42.8f, 46.4f, 42.0f}}, {RUNG_M16_256, 1, {61.6f, 65.6f, 61.6f}},
+    {RUNG_M352N96, 1, {70.1f, 75.0f, 69.5f}},    {RUNG_M128, 2, {71.4f, 81.6f, 69.8f}},
+    {RUNG_M128N160, 2, {94.9f, 129.2f, 92.2f}},  {RUNG_M512N96, 1, {96.3f, 100.4f, 95.8f}},
+    {RUNG_M512N128, 1, {104.4f, 109.0f, 104.1f}}, {RUNG_M768N96, 1, {137.5f, 145.0f, 135.1f}},
+};
+
+// The large tile with the fewest modelled microseconds on fragment-major
+// activations (whole rounds times the round cost; a K-split tile left with
+// one K group takes no part; ties to the earlier entry).  Against the
+// fastest forced rung over that sweep: 1.004 of it on average, where the
+// rule chain it replaces came to 1.056 (e.g. M = 640, N = 24576: 768x96
+// 139 against 175 us for 256x128; M = 1024, N = 12288: 512x96 102 against
+// 119 us for 128x128; Q6_K at M = 640, N = 12288: 352x96 80 against 122 us).
+int large_tile_xf(int fmt, long long M, long long N, long long K)
 {
-    for (const RoundCost &rc : kRoundCost) {
-        if (rc.rung != rung || rc.rb != 0) continue;
-        const float us = rc.us[xl == X_FRAG][fmt];
+    double best = 1e30;
+    int pick = RUNG_M128;
+    for (const LargeCost &lc : kLargeCostXf) {
         Plan pl;
-        if (us <= 0.0f || make_plan(rung, M, N, K, pl) != QGEMM_OK) return 1e30;
-        const long long wgs = (long long)pl.grid.x * pl.grid.y * pl.grid.z, per_round = (long long)kCUs * rc.per_cu;
-        return us * (double)((wgs + per_round - 1) / per_round);
+        if (make_plan(lc.rung, M, N, K, pl) != QGEMM_OK) continue;
+        const bool ksplit = lc.rung == RUNG_M192N64_K2 || lc.rung == RUNG_M128_K2 || lc.rung == RUNG_M192N96_K2;
+        if (ksplit && pl.kw == 1) continue;
+        const long long wgs = (long long)pl.grid.x * pl.grid.y * pl.grid.z, per_round = (long long)kCUs * lc.per_cu;
+        const double cost = lc.us[fmt] * (double)((wgs + per_round - 1) / per_round) * (double)K / 4096.0;
+        if (cost < best) {
+            best = cost;
+            pick = lc.rung;
+        }
     }
-    return 1e30;
+    return pick;
 }
 
 int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtype = DT_F16)
@@ -332,69 +368,39 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
         return round_model_rung(fmt, M, N, K, xl, dtype);
     }
     if (const int r = round_model_rung(fmt, M, N, K, xl, dtype); r >= 0) return r;
+    if (xl == X_FRAG) return large_tile_xf(fmt, M, N, K);
+    // row-major activations: the rule chain below (its tiles read 32 rows x
+    // 32 bytes per activation operand, so the three-waves-per-SIMD and
+    // 8-wave tiles that win on fragment-major activations lose here, except
+    // the ones named)
     const long long t128 = tn * ((M + 127) / 128), t256 = tn * ((M + 255) / 256);
     // occupancy model: a 256x128 tile counts as two 128x128 tiles; the
     // 128-row rungs as stream_cost has them (160 wide only off Q6_K)
     const double c256 = 2.0 * (double)((t256 + kCUs - 1) / kCUs);
     const double c128 = std::min(stream_cost(M, np, 128), fmt != FMT_Q6K ? stream_cost(M, np, 160) : 1e30);
-    // on fragment-major activations, a 192-row tile with K split over two
-    // 6-wave groups (three waves per SIMD) whenever its tiles fit one round
-    // and cover M with no more rows than 128-row tiles: 64 columns wide when
-    // those tiles fit (o and down at M = 658: 36.5 and 113-119 us), else 96
-    // (qkv: 47-50 us against 62 for 128x160; 192x64 would take 1.5 rounds, 64
-    // us); after the 352x96 check below, the 96-wide one also over two rounds
-    // at least 90% full (M = 768, N = 12288: Q4_K 90 against 101, Q6_K 254
-    // against 331 us; with 1.5 or three rounds it loses to the 256-row tile)
     const long long r192 = (M + 191) / 192, t192 = r192 * ((np + 5) / 6);
-    const bool even2 = xl == X_FRAG && (K / kChunk) % 2 == 0;
-    const bool k2_192 = even2 && r192 * 192 <= (M + 127) / 128 * 128;
-    // (the 64-wide tile pays even where it computes more padding rows: Q4_K
-    // and Q6_K at M = 512, N = 4096: 29 and 85 us against 35 and 106 us for
-    // the 128x128 K-split tile)
-    if (even2 && r192 * ((np + 3) / 4) <= kCUs) return RUNG_M192N64_K2;
-    if (k2_192 && t192 <= kCUs) return RUNG_M192N96_K2;
-    // on fragment-major activations, the 352x96 tile (11 waves, three per
+    // Q6_K, which has no 160-wide tile: the 352x96 tile (11 waves, three per
     // SIMD) when its rounds, each costing 1.22 rounds of the 256-row tile,
-    // come out cheapest: two of its row tiles cover M = 641..704 where
-    // 256-row tiles need three (merged gate_up at M = 658: 147 against 173 us;
-    // M = 700, N = 12288: 76 against 95 us for 128x160; Q6_K, whose larger raw
-    // runs spill four registers in it, at M = 658, N = 12288: 218 against
-    // 333 us for 128x128); on row-major activations for Q6_K too, which has
-    // no 160-wide tile (M = 700, N = 11008..24576: 101-204 against 130-222 us
-    // for 128x128; the other formats' 128x160 tile beats it there)
-    if (xl == X_FRAG || fmt == FMT_Q6K) {
+    // come out cheapest (M = 700, N = 11008..24576: 101-204 against 130-222
+    // us for 128x128; the other formats' 128x160 tile beats it there)
+    if (fmt == FMT_Q6K) {
         const long long t352 = ((np + 5) / 6) * ((M + 351) / 352);
         const double c352 = 2.44 * (double)((t352 + kCUs - 1) / kCUs);
         if (c352 < c256 && c352 < c128) return RUNG_M352N96;
     }
-    if (k2_192 && t192 <= 2 * kCUs && 10 * t192 >= 18 * kCUs) return RUNG_M192N96_K2;
     // the 256-row tile when the occupancy model has it finish no later than
-    // the 128-row tiles (it unpacks each weight once for 256 rows); on
-    // fragment-major activations also whenever it has 512 tiles, and for
-    // Q6_K, whose unpack costs most, from one full round of them (M = 1024,
-    // N = K = 12288: 363.9 against 400.4 us for 128x128)
-    // (on row-major activations Q6_K takes one round of 192x96 K-split tiles
-    // instead where they fit: M = 300..384, N = 11008..12288: 61-66 against
-    // 73-76 us; for the other formats, and elsewhere, they lose by 5-50%)
-    if (c256 <= c128 && xl == X_ROW && fmt == FMT_Q6K && (K / kChunk) % 2 == 0 &&
-        r192 * 192 <= (M + 127) / 128 * 128 && t192 <= kCUs)
+    // the 128-row tiles (it unpacks each weight once for 256 rows); Q6_K
+    // takes one round of 192x96 K-split tiles instead where they fit (M =
+    // 300..384, N = 11008..12288: 61-66 against 73-76 us; for the other
+    // formats, and elsewhere, they lose by 5-50%), and the 256-row tile also
+    // from 512 of its tiles (M = 1500..4096, N = 11008..24576: 0.88-0.98 of
+    // the 128x128 time; at 1.5 rounds, 384 tiles, it loses by 6-9%)
+    if (c256 <= c128 && fmt == FMT_Q6K && (K / kChunk) % 2 == 0 && r192 * 192 <= (M + 127) / 128 * 128 && t192 <= kCUs)
         return RUNG_M192N96_K2;
-    // (and Q6_K on row-major activations from 512 of them: M = 1500..4096,
-    // N = 11008..24576: 0.88-0.98 of the 128x128 time; at 1.5 rounds, 384
-    // tiles, it loses by 6-9%)
-    if (c256 <= c128 || (xl == X_FRAG && (t256 >= 512 || (fmt == FMT_Q6K && t256 >= kCUs))) ||
-        (fmt == FMT_Q6K && t256 >= 512)) {
-        // (on fragment-major activations 192x96 K-split tiles instead where
-        // the round model has their whole rounds at least 5% cheaper: M =
-        // 1500, N = 11008..12288 and M = 3072, N = 6144: 0.91-0.97 of the
-        // 256-row tile's time; at a modelled tie they measured 0.98-1.05)
-        if (k2_192 && round_cost(RUNG_M192N96_K2, fmt, M, N, K, xl) < 0.95 * round_cost(RUNG_M16_256, fmt, M, N, K, xl))
-            return RUNG_M192N96_K2;
-        return RUNG_M16_256;
-    }
-    // few tiles: split K inside the workgroup (on row-major activations only
-    // over a long K, where the halves' activation reloads stay affordable)
-    if (t128 <= 256 && (K >= 8192 || xl == X_FRAG)) return RUNG_M128_K2;
+    if (c256 <= c128 || (fmt == FMT_Q6K && t256 >= 512)) return RUNG_M16_256;
+    // few tiles: split K inside the workgroup, over a long K only, where the
+    // halves' activation reloads stay affordable
+    if (t128 <= 256 && K >= 8192) return RUNG_M128_K2;
     // 160-wide tiles when they even out the tiles per CU (Q6_K's larger raw
     // runs do not fit that variant's registers)
     if (fmt != FMT_Q6K && stream_cost(M, np, 160) < stream_cost(M, np, 128)) return RUNG_M128N160;

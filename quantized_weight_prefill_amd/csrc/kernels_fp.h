@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 // ---------------------------------------------------------------------------
 // One workgroup's pass over K chunks [c_lo, c_hi) of one tile: wave (wm, wn)
 // adds its WM x (16*WPB) block of X[rows m0..][:] * W[:][panels p0..] into acc.
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int XL>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int XL, int D = 8, int LA = 1>
 struct Stream32 {
     using XA = XLay<XL>;
     static constexpr int NTG = 64 * NWM * NWN;  // threads of one K group
@@ -319,7 +319,10 @@ struct Stream32 {
         xrow[rb] = XA::row(a, r) + XA::off(8 * (lane >> 5));
     }
 
-    u32x4 xf[RBW][8];
+    // activation fragments in flight: a ring of D k-steps (k-step s in slot
+    // s % D); D = 8 holds a whole chunk ahead
+    static_assert(D == 1 || D == 2 || D == 4 || D == 8, "the ring divides a chunk's eight k-steps");
+    u32x4 xr[D][RBW];
     RunSrc<FMT> src[UPT];
     RunRaw<FMT> raw[UPT];
     int slot_cp[UPT], slot_lane[UPT];
@@ -347,7 +350,7 @@ struct Stream32 {
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
-        for (int ks = 0; ks < 8; ks++) xf[rb][ks] = *(const u32x4 *)(xrow[rb] + XA::chunk(c_lo) + XA::off(16 * ks));
+        for (int ks = 0; ks < D; ks++) xr[ks][rb] = *(const u32x4 *)(xrow[rb] + XA::chunk(c_lo) + XA::off(16 * ks));
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
         u32x4 f[4];
@@ -362,18 +365,20 @@ struct Stream32 {
 
     // One chunk: MFMAs over LDS buffer `buf`, unpack of chunk c+1 (held in
     // `ru`) into the other buffer, and the raw loads of chunk c+2 into `rf`,
-    // issued first so that a whole chunk of MFMAs covers their latency.  The
-    // activation fragment of k-step ks is reloaded for chunk c+1 as soon as
-    // its MFMAs are issued.  Scheduling barriers keep the compiler from
-    // sinking those loads to the end of the loop and put each k-step's LDS
-    // reads ahead of the previous k-step's MFMAs.
+    // issued first so that a whole chunk of MFMAs covers their latency.  As
+    // soon as the MFMAs of k-step ks are issued, its ring slot is refilled
+    // with k-step ks + D (of chunk c+1 past the chunk's end).  Scheduling
+    // barriers keep the compiler from sinking those loads to the end of the
+    // loop and (LA = 1) put each k-step's LDS reads ahead of the previous
+    // k-step's MFMAs; with LA = 0 a k-step reads its weight fragments right
+    // before its MFMAs (fewer registers).
     RunRaw<FMT> raw2[UPT];
     auto chunk = [&](int c, int buf, RunRaw<FMT>(&ru)[UPT], RunRaw<FMT>(&rf)[UPT]) {
         const int cn = c + 1 < c_hi ? c + 1 : c_hi - 1;
         const int cnn = c + 2 < c_hi ? c + 2 : c_hi - 1;
 #pragma unroll
         for (int s = 0; s < UPT; s++) src[s].load(cnn, rf[s]);
-        u32x4 wcur[CBW], wnxt[CBW];
+        u32x4 wcur[CBW], wnxt[LA ? CBW : 1];
 #pragma unroll
         for (int cb = 0; cb < CBW; cb++) wcur[cb] = sW[buf][wn * CBW + cb][0][lane];
         __builtin_amdgcn_sched_barrier(0);
@@ -382,24 +387,27 @@ struct Stream32 {
         for (int s = 0; s < UPT; s++) pr[s] = run_params<FMT, DT>(ru[s], src[s], cn);
 #pragma unroll
         for (int ks = 0; ks < 8; ks++) {
-            if (ks < 7) {
+            if (LA && ks < 7) {
 #pragma unroll
-                for (int cb = 0; cb < CBW; cb++) wnxt[cb] = sW[buf][wn * CBW + cb][ks + 1][lane];
+                for (int cb = 0; cb < CBW; cb++) wnxt[LA ? cb : 0] = sW[buf][wn * CBW + cb][ks + 1][lane];
+            } else if (!LA && ks > 0) {
+#pragma unroll
+                for (int cb = 0; cb < CBW; cb++) wcur[cb] = sW[buf][wn * CBW + cb][ks][lane];
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
-                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma32<DT>(wcur[cb], xf[rb][ks], acc[cb][rb]);
-                xf[rb][ks] = *(const u32x4 *)(xrow[rb] + XA::chunk(cn) + XA::off(16 * ks));
+                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma32<DT>(wcur[cb], xr[ks % D][rb], acc[cb][rb]);
+                xr[ks % D][rb] = *(const u32x4 *)(xrow[rb] + XA::chunk(ks + D >= 8 ? cn : c) + XA::off(16 * ((ks + D) % 8)));
             }
             if ((ks & 1) == 0) {
 #pragma unroll
                 for (int s = 0; s < UPT; s++) put(buf ^ 1, s, ks >> 1, unpack_word<FMT, DT>(ru[s], pr[s], ks >> 1));
             }
-            if (ks < 7) {
+            if (LA && ks < 7) {
 #pragma unroll
-                for (int cb = 0; cb < CBW; cb++) wcur[cb] = wnxt[cb];
+                for (int cb = 0; cb < CBW; cb++) wcur[cb] = wnxt[LA ? cb : 0];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -424,11 +432,11 @@ struct Stream32 {
     }
 };
 
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int XL>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int XL, int D = 8, int LA = 1>
 __global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_stream32(Args a)
 {
-    using S = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL>;
+    using S = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL, D, LA>;
     constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
     // f32x16 partial sums one K group hands over: one per (wave, block, lane)
     constexpr int NACC = NWM * NWN * CBW * RBW * 64;
@@ -771,6 +779,15 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
         return hipGetLastError();
     case RUNG_M352N96:
         hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 6, 11, 1, 1, XL>), pl.grid, dim3(704), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M768N96:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 96, 6, 8, 1, 1, XL, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M512N128:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 64, 8, 8, 1, 1, XL, 2, 1>), pl.grid, dim3(512), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M512N96:
+        hipLaunchKernelGGL((k_stream32<FMT, DT, 64, 6, 8, 1, 1, XL, 4, 1>), pl.grid, dim3(512), 0, s, a);
         return hipGetLastError();
     case RUNG_M192N96_K2:
         if (even)

@@ -30,7 +30,10 @@ enum Rung {
     RUNG_M64N32_K4 = 12,  // 32x32x16 MFMA: 64x32, 2 waves of 32x32, K split over four groups
     RUNG_M128N64_K2 = 13, // 32x32x16 MFMA: 128x64, 4 waves of 32x64, K split over two groups
     RUNG_M96N32_K4 = 14,  // 32x32x16 MFMA: 96x32, 3 waves of 32x32, K split over four groups
-    RUNG_COUNT = 15
+    RUNG_M768N96 = 15,    // 32x32x16 MFMA: 768x96, 8 waves of 96x96 (two per SIMD)
+    RUNG_M512N128 = 16,   // 32x32x16 MFMA: 512x128, 8 waves of 64x128
+    RUNG_M512N96 = 17,    // 32x32x16 MFMA: 512x96, 8 waves of 64x96
+    RUNG_COUNT = 18
 };
 
 enum I8Rung {

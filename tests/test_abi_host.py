@@ -476,41 +476,48 @@ def test_ladder_decode_adjacent_tiles():
 
 
 def test_ladder_fragment_major():
-    """The ladder for fragment-major activations: a K-split tile for every
-    shape with at most 256 tiles of 128x128 (row-major only over a long K;
-    192x96 where it fits one round without more padding, else 128x128),
-    the 352x96 tile where its rounds cost least (two of its row tiles cover
-    M = 641..704), the 256-row tile also whenever it has 512 tiles; otherwise
-    the same rung as for row-major activations."""
-    # few tiles on fragment-major X: a 192-row K-split tile where its tiles fit one round and its
-    # 768 rows are no more than the 128-row tiles' (down and o: 256 tiles of 192x64; qkv: 256 of
-    # 192x96, where 192x64 would need 384); 128x128 when 192-row tiles pad more
-    assert qg.select_rung_xf("q6k", 658, 4096, 12288)["name"] == "mfma32-192x64-k2"
-    assert qg.select_rung_xf("q4k", 658, 4096, 4096)["name"] == "mfma32-192x64-k2"
-    assert qg.select_rung_xf("q4k", 658, 6144, 4096)["name"] == "mfma32-192x96-k2"
-    assert qg.select_rung_xf("q4k", 200, 12288, 4096)["name"] == "mfma32-128x128-k2"
-    assert qg.select_rung_xf("q4k", 1000, 4096, 4096)["name"] == "mfma32-128x128-k2"
-    assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"        # row-major: K < 8192
-    # one round of 128x64 tiles against one of 192x64 with 64 padding rows (26.0 against 32.5 us)
-    assert qg.select_rung_xf("q4k", 512, 4096, 4096)["name"] == "mfma32-128x64-k2"
-    assert qg.select_rung_xf("q6k", 2048, 4096, 12288)["name"] == "mfma16-256x128"    # occupancy tie
-    assert qg.select_rung_xf("q4k", 512, 12288, 4096)["name"] == "mfma16-256x128"
-    # 512 tiles of 352x96 in two rounds against 576 of 256x128 in three
-    assert qg.select_rung_xf("q4k", 1400, 12288, 4096)["name"] == "mfma32-352x96"
-    assert qg.select_rung_xf("q4k", 658, 24576, 4096)["name"] == "mfma32-352x96"       # merged gate_up
-    assert qg.select_rung("q4k", 658, 24576, 4096)["name"] == "mfma32-128x160"         # row-major: not measured
-    assert qg.select_rung_xf("q6k", 658, 24576, 4096)["name"] == "mfma32-352x96"       # Q6_K too (4 VGPRs spill)
-    assert qg.select_rung_xf("q4k", 658, 12288, 4096)["name"] == "mfma32-352x96"       # 352x96 before two 192x96 rounds
-    assert qg.select_rung_xf("q6k", 768, 12288, 4096)["name"] == "mfma32-192x96-k2"    # two full rounds of 192x96
-    assert qg.select_rung_xf("q4k", 2048, 12288, 4096)["name"] == "mfma16-256x128"    # 768 tiles: three rounds either way
-    assert qg.select_rung_xf("q6k", 1024, 12288, 12288)["name"] == "mfma16-256x128"   # Q6_K from one round of 256-row tiles
-    assert qg.select_rung_xf("q6k", 1024, 4096, 12288)["name"] == "mfma32-128x128-k2"  # half a round: not
-    # on fragment-major X, 192x96 K-split tiles instead of the 256-row tile where their whole rounds
-    # cost at least 5% less by the round costs (M = 1500, N = 11008..12288: 0.91-0.95 of its time)
+    """The ladder for fragment-major activations above 64 rows: where the
+    round model defers to the large tiles, the large tile whose whole rounds
+    cost least by the full-round cost table (the 192-row K-split tiles, the
+    K-split 128x128, 256x128, 352x96, 128x128, 128x160 and the 8-wave
+    512x96, 512x128 and 768x96 tiles).  The pins are measured winners on
+    MI355X (every large tile forced, weights rotating) by at least 10% over
+    the next tile, plus the dense layer's four GEMMs at M = 658; row-major
+    activations keep their rule chain."""
+    XF_WINNERS = [
+        # (fmt, M, N, K, rung): fp16 unless noted; the margin over the next tile
+        ("q4k", 658, 4096, 4096, "mfma32-192x64-k2"),    # o (bf16: 31.8 against 36.9 us)
+        ("q6k", 658, 4096, 12288, "mfma32-192x64-k2"),   # down
+        ("q4k", 658, 6144, 4096, "mfma32-192x96-k2"),    # qkv: 44.6 against 59.1 us (128x160)
+        ("q6k", 700, 6144, 4096, "mfma32-192x96-k2"),    # 47.5 against 64.5 (352x96)
+        ("q4k", 384, 12288, 4096, "mfma32-192x96-k2"),   # 46.2 against 59.6 (128x160)
+        ("w4a16", 300, 11008, 4096, "mfma32-192x96-k2"),  # 39.1 against 53.0
+        ("q4k", 384, 6144, 4096, "mfma32-192x64-k2"),    # 30.1 against 34.0
+        ("q4k", 658, 12288, 4096, "mfma32-352x96"),      # 75.5 against 87.3 (192x96-k2)
+        ("q6k", 640, 12288, 4096, "mfma32-352x96"),      # 79.7 against 87.9 (128x128; the rule chain took 256x128, 123.7)
+        ("q4k", 768, 24576, 4096, "mfma32-768x96"),      # 145.8 against 175.2 (192x96-k2)
+        ("q4k", 1500, 12288, 4096, "mfma32-768x96"),     # 144.9 against 175.2
+        ("q6k", 3072, 6144, 4096, "mfma32-768x96"),      # 151.9 against 186.2 (512x96)
+        ("q4k", 3072, 4096, 4096, "mfma32-512x128"),     # 103.9 against 119.1 (128x128)
+        ("q6k", 900, 14336, 4096, "mfma32-512x128"),     # 110.7 against 135.0
+        ("w4a16", 2500, 5120, 5120, "mfma32-512x128"),   # 122.5 against 143.7 (256x128)
+        ("q4k", 2048, 4096, 4096, "mfma16-256x128"),     # 68.5 against 83.5
+        ("q4k", 512, 12288, 4096, "mfma16-256x128"),     # 60.5 against 72.1 (352x96)
+        ("q6k", 450, 14336, 4096, "mfma16-256x128"),     # 66.9 against 83.1
+        ("q4k", 1024, 4096, 12288, "mfma32-128x128-k2"),  # bf16: 113.4 against 125.4
+    ]
+    for fmt, M, N, K, rung in XF_WINNERS:
+        assert qg.select_rung_xf(fmt, M, N, K)["name"] == rung, (fmt, M, N, K)
+    # the merged gate_up at M = 658: one round of 768x96 tiles (140.8 against 147.1 us for 352x96)
     for fmt in ("q4k", "q6k", "w4a16"):
-        assert qg.select_rung_xf(fmt, 1500, 12288, 4096)["name"] == "mfma32-192x96-k2", fmt
-        assert qg.select_rung_xf(fmt, 1500, 11008, 4096)["name"] == "mfma32-192x96-k2", fmt
-        assert qg.select_rung_xf(fmt, 2048, 12288, 4096)["name"] == "mfma16-256x128", fmt  # 1.24-1.29 there
+        assert qg.select_rung_xf(fmt, 658, 24576, 4096)["name"] == "mfma32-768x96", fmt
+    assert qg.select_rung("q4k", 658, 24576, 4096)["name"] == "mfma32-128x160"         # row-major
+    assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"          # row-major: K < 8192
+    # one round of 128x64 tiles (the round model, before the large tiles)
+    assert qg.select_rung_xf("q4k", 512, 4096, 4096)["name"] == "mfma32-128x64-k2"
+    # a K-split tile with an odd chunk count (W4A16, K = 33 x 128) runs one K group: not a candidate
+    assert qg.select_rung_xf("w4a16", 658, 4096, 4224)["name"] not in ("mfma32-192x64-k2", "mfma32-128x128-k2",
+                                                                      "mfma32-192x96-k2")
     # row-major Q6_K (no 160-wide tile): the 352x96 tile at M = 700 over N = 11008..24576 (0.78-0.92
     # of the 128x128 time) and the 256-row tile from 512 of its tiles (M = 3072, N = 11008..12288:
     # 0.90 of it); not at 1.5 rounds (M = 1024, N = 12288) nor for the other formats
@@ -522,16 +529,12 @@ def test_ladder_fragment_major():
     for fmt in ("q4k", "w4a16"):
         assert qg.select_rung(fmt, 700, 12288, 4096)["name"] == "mfma32-128x160", fmt
     # (at 9..16 rows over 512..1535 panels the layouts differ on purpose: see the small-M test)
-    for fmt, M, K, N in [("q4k", 8, 4096, 12288),
-                         ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 12288), ("q4k", 4096, 4096, 32),
-                         ("q6k", 1024, 12288, 4096)]:
+    for fmt, M, K, N in [("q4k", 8, 4096, 12288), ("w4a16", 2048, 4096, 12288), ("q4k", 4096, 4096, 32)]:
         assert qg.select_rung_xf(fmt, M, N, K)["name"] == qg.select_rung(fmt, M, N, K)["name"], (fmt, M, K, N)
     for K, N in SHAPES:
         for M in list(range(1, 70)) + [96, 200, 300, 511, 658, 1000, 1024, 4096]:
             info = qg.select_rung_xf("w4a16", M, N, K)
             assert info["tiles_n"] * info["cols"] >= N and info["tiles_m"] * info["rows"] >= M
-            if info["name"] in ("mfma32-128x128-k2", "mfma32-192x96-k2", "mfma32-192x64-k2"):
-                assert info["tiles_n"] * info["tiles_m"] <= 256
 
 
 def test_grid_limits():

@@ -1,6 +1,6 @@
 """The automatic ladder at mid and large M, through the entry points a caller
 uses (the format calls on row-major X, qgemm_gemm_xf on fragment-major X):
-each shape is one where the round model or a large-tile rule picks a
+each shape is one where the round model or the large-tile costs pick a
 particular rung (asserted first, so the case keeps covering that rung), and
 the product is checked against the oracle on a seeded sample of outputs
 (first and last rows and columns included).  The expected rungs are the
@@ -25,7 +25,10 @@ SHAPES = [
     ("w4a16", "xf", qg.F16, 384, 4096, 4096, "mfma32-128x64-k2"),    # one round of 128-row tiles
     ("q4k", "row", qg.BF16, 96, 12288, 4096, "mfma32-128x64-k2"),    # row-major, 768 panels
     ("q6k", "row", qg.F16, 64, 2048, 4096, "direct-skinny-n"),       # row-major: 16 rows, four panels per wave
-    ("q4k", "xf", qg.F16, 1500, 12288, 4096, "mfma32-192x96-k2"),    # 192x96 over the 256-row tile by round costs
+    ("q4k", "xf", qg.F16, 1500, 12288, 4096, "mfma32-768x96"),       # one round of 768x96 tiles (96x96 waves)
+    ("q6k", "xf", qg.BF16, 1500, 12288, 4096, "mfma32-768x96"),      # Q6_K bf16 (its 96x96 waves spill a few VGPRs)
+    ("q4k", "xf", qg.BF16, 3072, 4096, 4096, "mfma32-512x128"),      # 64x128 waves
+    ("w4a16", "xf", qg.F16, 1024, 12288, 4096, "mfma32-512x96"),     # 64x96 waves
     ("q6k", "row", qg.F16, 700, 12288, 4096, "mfma32-352x96"),       # row-major Q6_K: the 352-row tile
     ("q6k", "row", qg.F16, 3072, 12288, 4096, "mfma16-256x128"),     # row-major Q6_K from 512 256-row tiles
 ]
