@@ -632,7 +632,8 @@ int staged(int fmt, const void *X, const void *W, void *scratch, size_t scratch_
 
 const char *const kI8RungNames[I8_RUNG_COUNT] = {"i8-128x128",   "i8-256x128",   "i8-128x128-k2",
                                                    "i8-256x96",    "i8-512x96",    "i8-352x96",
-                                                   "i8-192x96-k2", "i8-192x64-k2", "i8-64x64-sk"};
+                                                   "i8-192x96-k2", "i8-192x64-k2", "i8-64x64-sk",
+                                                   "i8-768x96"};
 // int32 sums stay exact while K * 127 * 127 < 2^31
 constexpr long long kI8MaxK = 131072;
 
@@ -655,6 +656,7 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case I8_M256N96: pl.rows = 256; pl.cols = 96; pl.waves = 8; break;
     case I8_M512N96: pl.rows = 512; pl.cols = 96; pl.waves = 8; break;
     case I8_M352N96: pl.rows = 352; pl.cols = 96; pl.waves = 11; break;
+    case I8_M768N96: pl.rows = 768; pl.cols = 96; pl.waves = 8; break;
     case I8_M192N96_K2:
     case I8_M192N64_K2:
         pl.rows = 192;
@@ -730,14 +732,18 @@ int i8_select(int fmt, long long M, long long N, long long K)
     if ((K / kChunk) % 2 == 0 && r192 * ((np + 5) / 6) <= kCUs) return I8_M192N96_K2;
     if (t128 <= 256 && (K / kChunk) % 2 == 0) return I8_M128_K2;
     if (M <= 128) return I8_M128;
-    const long long tm256 = (M + 255) / 256, tm352 = (M + 351) / 352, tm512 = (M + 511) / 512;
+    const long long tm256 = (M + 255) / 256, tm352 = (M + 351) / 352, tm512 = (M + 511) / 512, tm768 = (M + 767) / 768;
     const long long tn128 = (np + 7) / 8, tn96 = (np + 5) / 6;
     const auto rounds = [](long long tiles) { return (double)((tiles + kCUs - 1) / kCUs); };
-    const double c[4] = {rounds(tm256 * tn128), 0.85 * rounds(tm256 * tn96), 1.17 * rounds(tm352 * tn96),
-                         1.35 * rounds(tm512 * tn96)};
-    const int rung[4] = {I8_M256, I8_M256N96, I8_M352N96, I8_M512N96};
+    // (the 768-row tile of 96-row waves, a round costing 2.1: one round of it
+    // for the merged gate_up at M = 658, 93.7 against 95.0 us for two of
+    // 352x96, Q6_K 104.2 against 117.8; M = 1500, N = 12288: 100.1 against
+    // 116.8 us for three rounds of 256x96)
+    const double c[5] = {rounds(tm256 * tn128), 0.85 * rounds(tm256 * tn96), 1.17 * rounds(tm352 * tn96),
+                         1.35 * rounds(tm512 * tn96), 2.1 * rounds(tm768 * tn96)};
+    const int rung[5] = {I8_M256, I8_M256N96, I8_M352N96, I8_M512N96, I8_M768N96};
     int best = 0;
-    for (int i = 1; i < 4; i++)
+    for (int i = 1; i < 5; i++)
         if (c[i] < c[best]) best = i;
     return rung[best];
 }

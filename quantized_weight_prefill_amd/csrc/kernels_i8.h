@@ -269,7 +269,7 @@ __device__ __forceinline__ void store_block_i8(const Args &a, const i32x16 &v, i
 // k-steps of MFMAs, so with CPB = 2 the barrier and the LDS round trip after
 // it are paid half as often.  Each thread then unpacks one run of each chunk
 // of the stage (same column and lane group).
-template <int FMT, int WM, int WPB, int NWM, int NWN, int CPB>
+template <int FMT, int WM, int WPB, int NWM, int NWN, int CPB, int D = 4 * CPB>
 struct StreamI8 {
     static constexpr int NTG = 64 * NWM * NWN;
     static constexpr int PB = WPB * NWN;
@@ -301,7 +301,10 @@ struct StreamI8 {
         xrow[rb] = Xq + (long long)blk * 32 * a.K + (lane & 31) * 16 + (lane >> 5) * 512;
     }
 
-    u32x4 xf[RBW][KSTEPS];
+    // activation fragments in flight: a ring of D k-steps (k-step s in slot
+    // s % D); D = KSTEPS holds a whole stage ahead
+    static_assert(KSTEPS % D == 0, "the ring divides a stage's k-steps");
+    u32x4 xr[D][RBW];
     RunSrc<FMT> src[UPT];
     RunRaw<FMT> raw[UPT][CPB];
     int slot_cp[UPT], slot_lane[UPT];
@@ -338,7 +341,7 @@ struct StreamI8 {
 #pragma unroll
     for (int rb = 0; rb < RBW; rb++)
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ks++) xf[rb][ks] = xload(rb, c_lo, ks);
+        for (int ks = 0; ks < D; ks++) xr[ks][rb] = xload(rb, c_lo, ks);
 #pragma unroll
     for (int s = 0; s < UPT; s++) {
 #pragma unroll
@@ -383,8 +386,8 @@ struct StreamI8 {
 #pragma unroll
             for (int rb = 0; rb < RBW; rb++) {
 #pragma unroll
-                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma_i8(wcur[cb], xf[rb][ks], acc[cb][rb]);
-                xf[rb][ks] = xload(rb, tn, ks);
+                for (int cb = 0; cb < CBW; cb++) acc[cb][rb] = mma_i8(wcur[cb], xr[ks % D][rb], acc[cb][rb]);
+                xr[ks % D][rb] = xload(rb, ks + D >= KSTEPS ? tn : t, (ks + D) % KSTEPS);
             }
             // word ks%4 of the runs of chunk ks/4
             const int j = ks >> 2, i = ks & 3;
@@ -411,11 +414,11 @@ struct StreamI8 {
     }
 };
 
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int CPB = 1>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int CPB = 1, int D = 4 * CPB>
 __global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_i8_stream(Args a)
 {
-    using S = StreamI8<FMT, WM, WPB, NWM, NWN, CPB>;
+    using S = StreamI8<FMT, WM, WPB, NWM, NWN, CPB, D>;
     constexpr int CBW = S::CBW, RBW = S::RBW, PB = S::PB, BM = S::BM;
     constexpr int NACC = NWM * NWN * CBW * RBW * 64;
     // the partial sums of groups 1.. overlay the LDS of every group (free
@@ -602,6 +605,9 @@ hipError_t launch_i8_cpb(int base, const Plan &pl, const Args &a, hipStream_t s)
     case I8_M352N96:
         hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 11, 1, 1, CPB>), pl.grid, dim3(704), 0, s, a);
         break;
+    case I8_M768N96:  // 96-row waves: one chunk per stage, activations one k-step ahead
+        hipLaunchKernelGGL((k_i8_stream<FMT, DT, 96, 6, 8, 1, 1, 1, 1>), pl.grid, dim3(512), 0, s, a);
+        break;
     case I8_M192N96_K2:
         if (pl.kw == 2)
             hipLaunchKernelGGL((k_i8_stream<FMT, DT, 32, 6, 6, 1, 2, CPB>), pl.grid, dim3(768), 0, s, a);
@@ -643,7 +649,7 @@ template <int FMT, int DT>
 hipError_t launch_i8_fd(const Plan &pl, const Args &a, hipStream_t s)
 {
     if (pl.rung == I8_M64_SK) return launch_i8_sk<FMT, DT>(pl, a, s);
-    const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) || pl.rung == I8_M192N96_K2 ||
+    const bool slower2 = (FMT == FMT_W4 && pl.rung == I8_M256N96) || pl.rung == I8_M192N96_K2 || pl.rung == I8_M768N96 ||
                          (FMT == FMT_Q6K && (pl.rung == I8_M512N96 || pl.rung == I8_M352N96));
     if (!slower2 && (a.K / kChunk) % (2 * pl.kw) == 0) return launch_i8_cpb<FMT, DT, 2>(pl.rung, pl, a, s);
     return launch_i8_cpb<FMT, DT, 1>(pl.rung, pl, a, s);

@@ -46,7 +46,8 @@ enum I8Rung {
     I8_M192N96_K2 = 6,  // 192x96, K split over two 6-wave groups (three waves per SIMD)
     I8_M192N64_K2 = 7,  // 192x64, K split over two 6-wave groups
     I8_M64_SK = 8,      // 64x64, K split over four groups and across workgroups
-    I8_RUNG_COUNT = 9
+    I8_M768N96 = 9,     // 768x96, 8 waves of 96x96: each weight unpacked once for 768 rows
+    I8_RUNG_COUNT = 10
 };
 
 struct Plan {

@@ -288,7 +288,13 @@ def test_i8_ladder():
                                ("q6k", 16, 4096, 12288, "i8-64x64-sk"), ("q6k", 256, 4096, 12288, "i8-64x64-sk"),
                                ("q6k", 300, 4096, 12288, "i8-192x64-k2"), ("q4k", 64, 4096, 4096, "i8-64x64-sk"),
                                ("q4k", 96, 4096, 4096, "i8-192x64-k2"), ("q4k", 64, 6144, 4096, "i8-64x64-sk"),
-                               ("q4k", 64, 12288, 4096, "i8-192x64-k2"), ("q6k", 658, 4096, 12288, "i8-192x64-k2")]:
+                               ("q4k", 64, 12288, 4096, "i8-192x64-k2"), ("q6k", 658, 4096, 12288, "i8-192x64-k2"),
+                               # one round of 768x96 tiles (96-row waves): the merged gate_up at M = 658 (Q4_K
+                               # 93.7 against 95.0 us for two rounds of 352x96, Q6_K 104.2 against 117.8) and
+                               # M = 1500, N = 12288 (100.1 against 116.8 for 256x96); 512x96 keeps M = 1024-4096
+                               ("q4k", 658, 24576, 4096, "i8-768x96"), ("q6k", 658, 24576, 4096, "i8-768x96"),
+                               ("q4k", 1500, 12288, 4096, "i8-768x96"), ("q4k", 1024, 12288, 4096, "i8-512x96"),
+                               ("q4k", 2048, 12288, 4096, "i8-512x96"), ("q4k", 4096, 12288, 4096, "i8-512x96")]:
         sel = qg.i8_select_rung(fmt, M, N, K)
         assert sel["name"] == want, (fmt, M, N, K, sel)
         if want == "i8-64x64-sk":
