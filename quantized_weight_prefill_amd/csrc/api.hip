@@ -168,15 +168,14 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //    32x32x16 MFMAs with K split between two wave groups;
 //  * otherwise the 128-row tile on 32x32x16 MFMAs, 128 or 160 columns wide,
 //    whichever the occupancy model below finishes first.
-// On fragment-major activations the three-waves-per-SIMD tiles come first
-// where they fit (192x64 and 192x96 with K split over two 6-wave groups,
-// 352x96; the rules are in select_rung), the K-split 128x128 tile serves the
-// other shapes with at most 256 of its tiles, the 256-row tile also wins
-// whenever it has 512 tiles, and 192x96 replaces it where the round costs
-// put its whole rounds 5% lower.  Row-major Q6_K, which has no 160-wide
-// tile, takes the 352x96 tile by the same occupancy rule, one round of
-// 192x96 tiles where the 256-row tile would serve, and the 256-row tile from
-// 512 of its tiles.
+// On fragment-major activations the large tiles instead go by their
+// full-round costs (large_tile_xf): the three-waves-per-SIMD tiles (192x64
+// and 192x96 with K split over two 6-wave groups, 352x96), the K-split
+// 128x128, 256x128, 128x128 and 128x160 tiles and the 8-wave tiles of 64-
+// and 96-row waves (512x96, 512x128, 768x96), whichever finishes its whole
+// rounds first.  Row-major Q6_K, which has no 160-wide tile, takes the
+// 352x96 tile by the occupancy rule, one round of 192x96 tiles where the
+// 256-row tile would serve, and the 256-row tile from 512 of its tiles.
 // Modeled time of a 128-row streaming rung with tiles `cols` wide, in units
 // of one 128x128 tile at full CU rate: two tiles share a CU at a time, so
 // the busiest of the 256 CUs carries ceil(T/256) tiles, and a tile that

@@ -289,6 +289,9 @@ __global__ void __launch_bounds__(64 * NWM * NWN) k_stream(Args a)
 // 16 K; lane (r, h) of k-step s carries k = 128c + 16s + 8h + 0..7 in both
 // operands, so word i of the run g of a column lands in k-step 2g + i/2,
 // lane half i%2, and an activation fragment is 16 contiguous bytes of a row.
+// A wave's activation fragments sit in a ring of D k-steps (D = 8: the whole
+// next chunk, for 32-row waves; fewer for the 64- and 96-row waves, whose
+// accumulators leave no room for a chunk of them).
 // ---------------------------------------------------------------------------
 // One workgroup's pass over K chunks [c_lo, c_hi) of one tile: wave (wm, wn)
 // adds its WM x (16*WPB) block of X[rows m0..][:] * W[:][panels p0..] into acc.
