@@ -702,14 +702,16 @@ int i8_plan(int rung, long long M, long long N, long long K, Plan &pl)
 //  * at most 256 tiles of 128x128 (and an even chunk count): the 128x128
 //    tile with K split over two wave groups (o and down at M = 658);
 //  * up to 128 rows: the 128x128 tile;
-//  * otherwise the 256x128, 256x96, 352x96 or 512x96 tile, whichever
-//    finishes in the fewest rounds of one workgroup per CU, a round costing
-//    1, 0.85, 1.17 and 1.35 (fitted to the measured times: the merged
-//    gate_up at M = 658 91 us on 352x96 against 107 on 256x96 and 117 on
-//    256x128; M = 2048 121 us on 512x96 against 133 on 256x128 and 138 on
-//    352x96; M = 4096 238 against 260 and 268).  The 352-row tile runs three
-//    waves per SIMD and unpacks each weight for 352 rows: two of its row
-//    tiles cover M = 658 where 256-row tiles need three.
+//  * otherwise the 256x128, 256x96, 352x96, 512x96 or 768x96 tile,
+//    whichever finishes in the fewest rounds of one workgroup per CU, a
+//    round costing 1, 0.85, 1.17, 1.35 and 2.1 (fitted to the measured
+//    times: the merged gate_up at M = 658 91 us on 352x96 against 107 on
+//    256x96 and 117 on 256x128, and 93.7 on one round of 768x96 against
+//    95.0 on two of 352x96; M = 2048 121 us on 512x96 against 133 on
+//    256x128 and 138 on 352x96; M = 4096 238 against 260 and 268).  The
+//    352-row tile runs three waves per SIMD and unpacks each weight for 352
+//    rows: two of its row tiles cover M = 658 where 256-row tiles need
+//    three; the 768-row tile unpacks each weight once for 768 rows.
 int i8_select(int fmt, long long M, long long N, long long K)
 {
     const long long np = (N + 15) / 16, t128 = ((M + 127) / 128) * ((np + 7) / 8), r192 = (M + 191) / 192;
