@@ -700,7 +700,8 @@ def run_grouped(args) -> int:
     gbps = (gd["wbytes"] + 2.0 * T * gd["K"] + 2.0 * T * gd["N"]) / (pd["ms"] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_HBM_GBPS, 4), "kernel": f"{gd['label']} (grouped {gd['fmt']} T={T} K={gd['K']} N={gd['N']} E={E})",
-            "traffic": None, "frac_of_sustained": pd["weight_frac_of_read_probe"]}
+            "traffic": measured_traffic(f"{name}/{gd['label']}") if not xf_layout else None,
+            "frac_of_sustained": pd["weight_frac_of_read_probe"]}
     print(json.dumps({
         "metric": METRIC, "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
