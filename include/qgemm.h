@@ -356,27 +356,43 @@ int qgemm_dequant(int format, const void *Wpacked, void *Wout, int64_t N, int64_
  * T.  The kernel clamps every offset into [0, T] and to at least the
  * previous one, so any contents stay inside X, Y and W (bad offsets only
  * give wrong rows).  Rows outside [offsets[0], offsets[E]) are not written.
- * One launch on `stream`: with more than 64 rows per expert on average
- * (ceil(T/E)) and K of at least 16 chunks of 128, 64x64 streaming tiles of
- * one expert per workgroup, else the direct kernel with 16- or 32-row
- * groups; results as qgemm_gemm_rung for each expert.  Errors as
- * qgemm_w4a16 (group_size ignored for the k-quants), plus QGEMM_ERR_SHAPE
- * for E < 1 or a grid beyond ceil(T/16) + E = 65535, QGEMM_ERR_ALIGN when
- * one expert's packed size is not a multiple of 16 bytes; T = 0 is a no-op.
+ * One launch on `stream`, planned from T, E, N and K alone (the counts
+ * stay on the device): qgemm_grouped_plan below names the kernel.  Results
+ * as qgemm_gemm_rung for each expert.  Errors as qgemm_w4a16 (group_size
+ * ignored for the k-quants), plus QGEMM_ERR_SHAPE for E < 1 or a grid
+ * beyond ceil(T/16) + E = 65535, QGEMM_ERR_ALIGN when one expert's packed
+ * size is not a multiple of 16 bytes; T = 0 is a no-op.
  *
  * qgemm_grouped_xf: the same product with X given as the fragment-major copy
  * of the T routed rows (qgemm_x_to_xf of X [T][K]; Xf holds
  * qgemm_xf_bytes(T, K) bytes, device, 16-byte aligned, caller-owned), the
  * layout of qgemm_gemm_xf (the delta-net page, "Gap #2: State Layout": one
  * cache line per activation read instead of one per row).  An expert's rows
- * may start anywhere inside a 32-row block.  The streaming tiles serve more
- * than 56 rows per expert on average at any K, the direct kernel the rest;
- * for the same kernel Y is bit-identical to qgemm_grouped's.  Arguments,
- * ownership and errors as qgemm_grouped. */
+ * may start anywhere inside a 32-row block.  The plan is qgemm_grouped's and
+ * Y is bit-identical to qgemm_grouped's.  Arguments, ownership and errors as
+ * qgemm_grouped.
+ *
+ * qgemm_grouped_plan: the launch both grouped calls make for T routed rows,
+ * E experts and an N x K weight matrix per expert, in 8 integers (host
+ * memory, caller-owned):
+ *   [0] kernel: 0 the direct kernel (16 or 32 rows by 64 columns per
+ *       workgroup, K split over [4] waves when the grid is small), 1 the
+ *       shared-activation kernel (four waves over 128 columns that read each
+ *       chunk of their rows' activations once, through LDS)
+ *   [1] rows per tile  [2] columns per tile  [3] waves per workgroup
+ *   [4] K-split ways inside a workgroup  [5] grid x  [6] grid y (row-tile
+ *       slots: an upper bound on the tiles of all experts)  [7] 0
+ * The shared kernel serves more than 16 rows per expert on average
+ * (ceil(T/E)) once the grid fills the chip without a K split, with 32-row
+ * tiles up to 48 rows per expert and 80-row tiles above.  Returns
+ * QGEMM_ERR_NULL for a NULL info8, QGEMM_ERR_SHAPE for T < 0, E < 1, N < 1,
+ * K not a positive multiple of 128 or a grid beyond ceil(T/16) + E = 65535,
+ * else QGEMM_OK. */
 int qgemm_grouped(int format, const void *X, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E, int64_t T,
                   int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
 int qgemm_grouped_xf(int format, const void *Xf, const void *Wpacked, void *Y, const int32_t *offsets, int64_t E,
                      int64_t T, int64_t N, int64_t K, int64_t group_size, int has_zp, int dtype, void *stream);
+int qgemm_grouped_plan(int64_t T, int64_t E, int64_t N, int64_t K, int32_t *info8);
 
 /* The staged arm (the dequant-scratch post, "The two passes hiding inside
  * one matmul": unpack to a 16-bit scratch, then a GEMM that reads it), kept

@@ -85,6 +85,7 @@ SIGNATURES = {
     "qgemm_dequant": (_INT, [_INT, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_grouped": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_grouped_xf": (_INT, [_INT, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
+    "qgemm_grouped_plan": (_INT, [_I64, _I64, _I64, _I64, _VP]),
     "qgemm_staged_scratch_bytes": (_SZ, [_I64, _I64]),
     "qgemm_staged": (_INT, [_INT, _VP, _VP, _VP, _SZ, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _VP]),
     "qgemm_xf_bytes": (_SZ, [_I64, _I64]),
@@ -710,6 +711,21 @@ def select_rung_xf(fmt, M: int, N: int, K: int, dtype: int = F16) -> dict:
     _check("qgemm_select_rung_xf", lib().qgemm_select_rung_xf(f, M, N, K, dtype, _np_ptr(info)))
     d = dict(zip(_INFO_KEYS, (int(v) for v in info)))
     d["name"] = rung_name(d["rung"])
+    return d
+
+
+GROUPED_KERNELS = ("direct", "shared")
+_GROUPED_KEYS = ("kernel", "rows", "cols", "waves", "kw", "grid_x", "grid_y")
+
+
+def grouped_plan(T: int, E: int, N: int, K: int) -> dict:
+    """The launch :func:`grouped` and :func:`grouped_xf` make for T routed
+    rows over E experts of N x K weights (qgemm_grouped_plan); "name" is
+    "direct" or "shared"."""
+    info = np.zeros(8, np.int32)
+    _check("qgemm_grouped_plan", lib().qgemm_grouped_plan(T, E, N, K, _np_ptr(info)))
+    d = dict(zip(_GROUPED_KEYS, (int(v) for v in info)))
+    d["name"] = GROUPED_KERNELS[d["kernel"]]
     return d
 
 

@@ -541,15 +541,27 @@ long long packed_bytes(int fmt, long long N, long long K, long long group, int h
     return (long long)qgemm_w4a16_packed_bytes(N, K, group, has_zp);
 }
 
-// Grouped plan: four panels per wave, one or two 16-row blocks by the mean
-// rows per expert (the three-block variant spills with the expert search),
-// grid.y an upper bound on every expert's row blocks, K split as the direct
-// rungs do.
+// Grouped plan.  Up to 16 rows per expert on average (ceil(T/E)), or when
+// the grid is too small to fill the chip without splitting K (the direct
+// plan's kw above 1), the direct grouped kernel: four panels per wave, one
+// or two 16-row blocks, K split as the direct rungs split it.  Otherwise the
+// shared-activation kernel, 32-row tiles up to 48 rows per expert and
+// 80-row tiles above.  Measured on the 128-expert, 8-per-token routing of a
+// 658-token prompt (Zipf-like counts) with the counts scaled to 10-288 rows
+// per expert, Q4_K 2048 -> 768 and Q6_K 768 -> 2048, weights rotating: at
+// 10 rows the two kernels tie (38 against 38 us, 47 against 48); at 41 rows
+// the shared kernel takes 58-60 against the direct kernel's 63-67 us and
+// 70-72 against 71-77; from 66 rows its 80-row tiles beat 64x64 streaming
+// tiles (two 32-row waves, weights unpacked once into LDS) by 12-25% (288
+// rows: 200-204 against 250-258 us, 235 against 305-320).  32-row tiles lead up to 49 rows
+// (Q4_K), 48- to 96-row tiles differ by a few percent from 49 to 99 rows,
+// and 80-row tiles lead or tie from 99 rows on; a wider wave (four panels)
+// or eight waves measured slower throughout.
 Plan grouped_plan(long long T, long long E, long long N, long long K)
 {
     Plan pl{};
     const long long np = (N + 15) / 16, avg = (T + E - 1) / E;
-    pl.rung = -1;
+    pl.rung = GROUPED_DIRECT;
     pl.pn = 4;
     pl.rb = avg <= 16 ? 1 : 2;
     pl.grid = dim3((unsigned)ceil_div(np, 4), (unsigned)(ceil_div(T, 16 * pl.rb) + E), 1);
@@ -558,21 +570,17 @@ Plan grouped_plan(long long T, long long E, long long N, long long K)
     pl.rows = 16 * pl.rb;
     pl.cols = 64;
     pl.lds = pl.kw > 1 ? (size_t)pl.kw * pl.pn * pl.rb * 64 * sizeof(float) * 4 : 0;
+    if (avg > 16 && pl.kw == 1) {
+        pl.rung = GROUPED_SHARED;
+        pl.pn = 2;
+        pl.rb = avg <= 48 ? 2 : 5;
+        pl.waves = 4;
+        pl.grid = dim3((unsigned)ceil_div(np, 8), (unsigned)(ceil_div(T, 16 * pl.rb) + E), 1);
+        pl.rows = 16 * pl.rb;
+        pl.cols = 128;
+        pl.lds = 0;
+    }
     return pl;
-}
-
-// The 64x64 streaming tiles or the direct kernel: measured with both forced
-// (E = 32 and 128 experts, 24-82 rows per expert on average, Zipf-like
-// counts, Q4_K 2048 -> 768 and Q6_K 768 -> 2048, weights rotating), the
-// tiles win from about 64 rows per expert on fragment-major X at any K
-// (128 experts, 64 rows: Q4_K 82 against 86 us, Q6_K 97 against 104; at 41
-// rows the direct kernel, 62 against 67 and 72 against 83); on row-major X,
-// whose activation loads touch a cache line per row, from more rows and
-// only over 16 or more chunks.
-bool grouped_tiles(int xl, long long T, long long E, long long K)
-{
-    const long long avg = (T + E - 1) / E;
-    return xl == X_FRAG ? avg > 56 : avg > 64 && K / kChunk >= 16;
 }
 
 int grouped(int fmt, const void *X, const void *W, void *Y, const int32_t *offs, long long E, long long T, long long N,
@@ -593,13 +601,10 @@ int grouped(int fmt, const void *X, const void *W, void *Y, const int32_t *offs,
     a.offs = offs;
     a.E = (int)E;
     a.wstride = wstride;
-    const bool tiles = grouped_tiles(xl, T, E, K);
     const Plan pl = grouped_plan(T, E, N, K);
-    if (tiles ? !launch_fits(((N + 63) / 64) * (((T + 63) / 64 + E + 7) / 8 * 8), 128)
-              : !launch_fits(pl.grid.x, 64 * pl.kw))
-        return QGEMM_ERR_SHAPE;
+    if (!launch_fits(pl.grid.x, 64 * pl.waves)) return QGEMM_ERR_SHAPE;
     a.kw = pl.kw;
-    return launch_status(launch_grouped(fmt, dtype, xl, tiles, pl, a, T, E, (hipStream_t)stream), "grouped");
+    return launch_status(launch_grouped(fmt, dtype, xl, pl, a, (hipStream_t)stream), "grouped");
 }
 
 size_t staged_scratch_bytes(long long N, long long K)
@@ -1006,6 +1011,18 @@ int qgemm_grouped_xf(int format, const void *Xf, const void *Wpacked, void *Y, c
 {
     return grouped(format, Xf, Wpacked, Y, offsets, E, T, N, K, format == FMT_W4 ? group_size : 0, has_zp, dtype, stream,
                    X_FRAG);
+}
+
+int qgemm_grouped_plan(int64_t T, int64_t E, int64_t N, int64_t K, int32_t *info8)
+{
+    if (!info8) return QGEMM_ERR_NULL;
+    if (T < 0 || E < 1 || E > INT32_MAX / 2 || N < 1 || N > INT32_MAX || K < kChunk || K % kChunk != 0 ||
+        K > INT32_MAX || T > INT32_MAX || (long long)ceil_div(T, 16) + E > 65535)
+        return QGEMM_ERR_SHAPE;
+    const Plan pl = grouped_plan(T, E, N, K);
+    const int32_t v[8] = {pl.rung, pl.rows, pl.cols, pl.waves, pl.kw, (int32_t)pl.grid.x, (int32_t)pl.grid.y, 0};
+    for (int i = 0; i < 8; i++) info8[i] = v[i];
+    return QGEMM_OK;
 }
 
 size_t qgemm_i8_xq_bytes(int64_t M, int64_t K)

@@ -505,10 +505,11 @@ k_stream32(Args a)
 // slots for R-row tiles), a workgroup finds its expert and tile with
 // find_group_tile, and the ones past the last tile leave at once, before any
 // barrier.  Two kernels:
-//   * k_direct_grouped: the direct kernel's body on 16*RB rows x 4 panels
-//     (few rows per expert: each weight unpacked once per row tile);
-//   * k_stream32_grouped: 64x64 streaming tiles (two 32-row waves), which
-//     read an expert's activation rows once per 64 columns.
+//   * k_direct_grouped: the direct kernel's body on 16*RB rows x 4 panels,
+//     K split across the waves of a workgroup when the grid is small;
+//   * k_grouped_shared: 16*RB rows x 8 panels, four waves sharing each
+//     chunk of activation fragments through LDS (each weight unpacked once
+//     per row tile, each activation fragment fetched once per 128 columns).
 // Both take row-major or fragment-major X (the fragment-major copy of the T
 // routed rows; a tile's rows may start anywhere inside a 32-row block, each
 // lane addresses its own row).
@@ -573,71 +574,107 @@ __global__ void __launch_bounds__(512) k_direct_grouped(Args a)
     direct_body<FMT, DT, RB, PN, XL>(b, blockIdx.x * PN, lo + t * R);
 }
 
-// Grid: 8 * ceil(slots/8) * tn workgroups (slots = ceil(T/64) + E row-tile
-// slots, tn column tiles).  Row slot j and all its column tiles run on XCD
-// j % 8 (workgroup b runs on XCD b % 8), so an expert's activation rows are
-// fetched into one XCD's L2, and the slots past the last tile, which leave
-// at once, are spread over all XCDs.
-template <int FMT, int DT, int KS, int XL>
-__global__ void __launch_bounds__(128 * KS) __attribute__((amdgpu_waves_per_eu(2)))
-k_stream32_grouped(Args a)
+// Grid: x = panel groups of PN*NW panels, y = row-tile slots of 16*RB rows.
+// The NW waves of a workgroup own PN panels each, side by side, over the same
+// 16*RB rows of one expert.  Per chunk the workgroup copies the activation
+// fragments of its rows into LDS once (each thread one or a few 16-byte
+// pieces, stored in the order the lanes read them) and every wave multiplies
+// them with its own weight runs, unpacked into VGPRs as in the direct kernel;
+// chunk c+1's pieces wait in VGPRs while chunk c is multiplied, and one
+// barrier per chunk separates the two LDS buffers.  An activation fragment
+// is thus fetched once per PN*NW panels instead of once per PN, which is what
+// holds the direct kernel back from tens of rows per expert on.  Each
+// output's MFMAs run in the direct kernel's order, so the two give the same
+// bits.
+template <int FMT, int DT, int RB, int PN, int NW, int XL>
+__global__ void __launch_bounds__(64 * NW) k_grouped_shared(Args a)
 {
-    using St = Stream32<FMT, DT, 32, 4, 2, 1, XL>;
-    constexpr int CBW = St::CBW, RBW = St::RBW, PB = St::PB, BM = St::BM;
-    constexpr int NACC = 2 * CBW * RBW * 64;
-    static_assert(KS == 1 || (KS - 1) * NACC * sizeof(f32x16) <= KS * sizeof(typename St::Lds),
-                  "K-split reduction must fit in LDS");
-    __shared__ typename St::Lds sWall[KS];
-
-    const int tn = (a.np + PB - 1) / PB, slots = (a.M + BM - 1) / BM + a.E;
-    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-    const int nt = q % tn, j = xcd + 8 * (q / tn);
-    if (j >= slots) return;
-    const int lane = threadIdx.x & 63, wall = threadIdx.x >> 6;
+    using XA = XLay<XL>;
+    constexpr int R = 16 * RB;
+    constexpr int PIECES = RB * 4 * 64;                       // 16-byte pieces per chunk
+    constexpr int PT = (PIECES + 64 * NW - 1) / (64 * NW);    // pieces per thread
+    __shared__ u32x4 xs[2][RB][4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int e, lo, hi, t;
-    // every wave computes the same answer: the whole workgroup leaves
-    // together, before any barrier
-    if (!find_group_tile(a, j, BM, lane, e, lo, hi, t)) return;
+    // the same answer in every wave: the whole workgroup leaves together,
+    // before any barrier
+    if (!find_group_tile(a, blockIdx.y, R, lane, e, lo, hi, t)) return;
     Args b = a;
     b.W = a.W + (long long)e * a.wstride;
     b.M = hi;
+    const int m0 = lo + t * R;
+    const int p0 = (blockIdx.x * NW + w) * PN;
+    const int col = lane & 15, g = lane >> 4;
+    const int nch = a.K / kChunk;
 
-    const int kg = wall / 2, w = wall % 2, tid = threadIdx.x % St::NTG;
-    const int m0 = lo + t * BM + w * 32, p0 = nt * PB;
-    const int nchk = a.K / kChunk / KS, c_lo = kg * nchk, c_hi = c_lo + nchk;
+    // piece q: row block q/256, fragment (q/64)%4 of lane q%64, i.e. row
+    // m0 + 16*(q/256) + q%16 (clamped: computed and discarded), columns
+    // 32*((q%64)/16) + 8*((q/64)%4) .. +7 of the chunk
+    const uint16_t *psrc[PT];
+    int pdst[PT];
+#pragma unroll
+    for (int s = 0; s < PT; s++) {
+        const int q = threadIdx.x + 64 * NW * s;
+        const int qq = q < PIECES ? q : 0;
+        pdst[s] = q < PIECES ? q : -1;
+        int r = m0 + 16 * (qq >> 8) + (qq & 15);
+        r = r < hi ? r : hi - 1;
+        psrc[s] = XA::row(b, r) + XA::off(32 * ((qq & 63) >> 4)) + XA::off(8 * ((qq >> 6) & 3));
+    }
+    u32x4 *xflat = &xs[0][0][0][0];
 
-    f32x16 acc[CBW][RBW];
+    f32x4 acc[PN][RB];
 #pragma unroll
-    for (int cb = 0; cb < CBW; cb++)
+    for (int pn = 0; pn < PN; pn++)
 #pragma unroll
-        for (int rb = 0; rb < RBW; rb++)
+        for (int rb = 0; rb < RB; rb++) acc[pn][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    RunSrc<FMT> src[PN];
 #pragma unroll
-            for (int q = 0; q < 16; q++) acc[cb][rb][q] = 0.f;
-    St::run(b, sWall[kg], tid, lane, 0, m0, p0, c_lo, c_hi, acc);
-    if constexpr (KS > 1) {
-        f32x16 *red = reinterpret_cast<f32x16 *>(&sWall[0]);
-        if (kg > 0) {
+    for (int pn = 0; pn < PN; pn++) {
+        const int p = p0 + pn;
+        src[pn].init(b, p < b.np ? p : b.np - 1, g, col);
+    }
+
+    RunRaw<FMT> raw[PN];
+    u32x4 xp[PT];
 #pragma unroll
-            for (int cb = 0; cb < CBW; cb++)
+    for (int s = 0; s < PT; s++) xp[s] = *(const u32x4 *)(psrc[s] + XA::chunk(0));
 #pragma unroll
-                for (int rb = 0; rb < RBW; rb++)
-                    red[(kg - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane] = acc[cb][rb];
+    for (int pn = 0; pn < PN; pn++) src[pn].load(0, raw[pn]);
+#pragma unroll
+    for (int s = 0; s < PT; s++)
+        if (pdst[s] >= 0) xflat[pdst[s]] = xp[s];
+    __syncthreads();
+    for (int c = 0; c < nch; c++) {
+        const int buf = c & 1;
+        u32x4 wf[PN][4];
+#pragma unroll
+        for (int pn = 0; pn < PN; pn++) unpack_run<FMT, DT>(raw[pn], src[pn], c, wf[pn]);
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int pn = 0; pn < PN; pn++) src[pn].load(c + 1, raw[pn]);
+#pragma unroll
+            for (int s = 0; s < PT; s++) xp[s] = *(const u32x4 *)(psrc[s] + XA::chunk(c + 1));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const u32x4 xc = xs[buf][rb][i][lane];
+#pragma unroll
+                for (int pn = 0; pn < PN; pn++) acc[pn][rb] = mma<DT>(wf[pn][i], xc, acc[pn][rb]);
+            }
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int s = 0; s < PT; s++)
+                if (pdst[s] >= 0) xflat[(buf ^ 1) * PIECES + pdst[s]] = xp[s];
         }
         __syncthreads();
-        if (kg > 0) return;
-#pragma unroll
-        for (int g = 1; g < KS; g++)
-#pragma unroll
-            for (int cb = 0; cb < CBW; cb++)
-#pragma unroll
-                for (int rb = 0; rb < RBW; rb++)
-                    acc[cb][rb] += red[(g - 1) * NACC + ((w * CBW + cb) * RBW + rb) * 64 + lane];
     }
 #pragma unroll
-    for (int cb = 0; cb < CBW; cb++)
+    for (int pn = 0; pn < PN; pn++)
 #pragma unroll
-        for (int rb = 0; rb < RBW; rb++)
-            store_block32<DT>(b, acc[cb][rb], m0 + 32 * rb, 16 * p0 + 32 * cb, lane);
+        for (int rb = 0; rb < RB; rb++) store_block<DT>(b, acc[pn][rb], m0 + 16 * rb, 16 * (p0 + pn), lane);
 }
 
 // ---------------------------------------------------------------------------

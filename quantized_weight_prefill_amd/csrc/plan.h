@@ -72,11 +72,14 @@ hipError_t launch_splitk_reduce(int dtype, const float *part, uint16_t *Y, long 
 hipError_t launch_dequant(int fmt, int dtype, const Args &a, uint16_t *out, hipStream_t s);
 hipError_t launch_x_to_xf(const uint16_t *X, uint16_t *Xf, int M, int K, hipStream_t s);
 hipError_t launch_staged(int fmt, int dtype, const Args &a, uint8_t *scratch, const Plan &pl, hipStream_t s);
-// misc_grouped.hip: the direct grouped kernel with the Plan's row blocks, or
-// (stream_tiles) the 64x64 streaming tiles over T rows and E experts, on
-// activations of layout xl (X_ROW or X_FRAG)
-hipError_t launch_grouped(int fmt, int dtype, int xl, bool stream_tiles, const Plan &pl, const Args &a, long long T,
-                          long long E, hipStream_t s);
+// Grouped plans: Plan.rung names the kernel, Plan.rb its 16-row blocks.
+enum GroupedKernel {
+    GROUPED_DIRECT = 0,  // k_direct_grouped: 4 panels per wave, rb 1 or 2, K split over kw waves
+    GROUPED_SHARED = 1   // k_grouped_shared: 4 waves of 2 panels sharing X through LDS, rb 2 or 5
+};
+// misc_grouped.hip: the Plan's grouped kernel on activations of layout xl
+// (X_ROW or X_FRAG)
+hipError_t launch_grouped(int fmt, int dtype, int xl, const Plan &pl, const Args &a, hipStream_t s);
 
 // api.hip: the checked fp16/bf16 GEMM of qgemm_gemm_rung (layout X_ROW) and
 // qgemm_gemm_xf (X_FRAG) with an explicit workspace, and the workspace it

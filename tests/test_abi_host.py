@@ -599,8 +599,48 @@ def test_step_gemms_merge():
     assert flops(sg) == flops(synth.step_gemms("qwen3_8b_layer_m658", merge=False))
 
 
+def test_grouped_plan():
+    """The grouped plan: the direct kernel up to 16 rows per expert on average
+    and where the grid needs a K split, else the shared-activation kernel with
+    32-row tiles up to 48 rows per expert and 80-row tiles above (the measured
+    winners on MI355X on the 128-expert routing of a 658-token prompt, its
+    counts scaled); row-tile slots bound every expert's tiles."""
+    E = 128
+    for T, N, K, name, rows in [
+        (1316, 768, 2048, "direct", 16),    # 10 rows per expert
+        (3688, 768, 2048, "shared", 32),    # 29
+        (5264, 768, 2048, "shared", 32),    # 41: the MoE gate and up GEMMs
+        (5264, 2048, 768, "shared", 32),    # 41: the MoE down GEMM
+        (6144, 768, 2048, "shared", 32),    # 48
+        (6145, 768, 2048, "shared", 80),    # 49
+        (36848, 2048, 768, "shared", 80),   # 288
+    ]:
+        p = qg.grouped_plan(T, E, N, K)
+        assert (p["name"], p["rows"]) == (name, rows), (T, N, K, p)
+        assert p["grid_y"] == -(-T // rows) + E
+        if name == "shared":
+            assert (p["cols"], p["waves"], p["kw"], p["grid_x"]) == (128, 4, 1, -(-N // 128))
+        else:
+            assert (p["cols"], p["grid_x"]) == (64, -(-N // 64)) and p["waves"] == p["kw"]
+    # a small grid splits K in the direct kernel; at two or three chunks no
+    # split is possible and the shared kernel serves it
+    p = qg.grouped_plan(341, 5, 144, 2048)
+    assert p["name"] == "direct" and p["kw"] == 8 and p["rows"] == 32
+    for K in (256, 384):
+        p = qg.grouped_plan(341, 5, 144, K)
+        assert (p["name"], p["rows"], p["grid_x"], p["grid_y"]) == ("shared", 80, 2, 5 + 5)
+    assert qg.grouped_plan(0, 4, 64, 256)["name"] == "direct"
+    lib = qg.lib()
+    info = np.zeros(8, np.int32)
+    ptr = info.ctypes.data_as(ctypes.c_void_p)
+    assert lib.qgemm_grouped_plan(64, 4, 64, 256, None) == -1
+    for bad in [(-1, 4, 64, 256), (64, 0, 64, 256), (64, 4, 0, 256), (64, 4, 64, 100), (64, 4, 64, 0),
+                (1 << 20, 4, 64, 256)]:
+        assert lib.qgemm_grouped_plan(*bad, ptr) == -2, bad
+
+
 def test_grouped_offset_clamping_prefix_max_form():
-    """The grouped streaming tiles find an expert's rows from prefix maxima,
+    """The grouped kernels find an expert's rows from prefix maxima,
     lo_e = min(T, max(0, offs[0..e])) and hi_e = min(T, max(0, offs[0..e+1])),
     instead of clamping the offsets one after another (each into [0, T] and to
     at least the previous end).  The two forms agree on arbitrary offsets,

@@ -22,7 +22,7 @@ import pytest
 from quantized_weight_prefill_amd import build as B
 
 # kernels that unpack weights: FMT is their first template argument, DT the second
-UNPACKING = ("k_direct", "k_stream", "k_stream32", "k_stream32_sk", "k_stream32_grouped", "k_direct_grouped",
+UNPACKING = ("k_direct", "k_stream", "k_stream32", "k_stream32_sk", "k_grouped_shared", "k_direct_grouped",
              "k_dequant", "k_stage")
 
 

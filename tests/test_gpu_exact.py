@@ -140,13 +140,16 @@ def test_exact_path_dequant_and_staged(dtype):
 
 @pytest.mark.parametrize("layout", ["row", "xf"])
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
-@pytest.mark.parametrize("K", [256, 2048])  # the direct grouped kernel, then the 64x64 streaming tiles
-def test_exact_path_grouped(dtype, K, layout):
+@pytest.mark.parametrize("K,kernel", [(256, "shared"), (2048, "direct")])
+def test_exact_path_grouped(dtype, K, kernel, layout):
     """Two experts, each fed an identity block, so each expert's rows of Y
-    are its weights bit for bit (row-major X and its fragment-major copy)."""
+    are its weights bit for bit (row-major X and its fragment-major copy;
+    K = 256 takes the shared-activation kernel, K = 2048 the direct kernel
+    with K split over its waves)."""
     import torch
 
     N, E = 48, 2
+    assert qg.grouped_plan(E * K, E, N, K)["name"] == kernel
     cases = [_wide_case(K, N, K, dtype, seed=930 + e + 4 * dtype) for e in range(E)]
     for c in cases:
         _assert_sensitive(c)

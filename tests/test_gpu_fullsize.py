@@ -49,26 +49,35 @@ def test_workload_sampled(name, j, layout):
     assert rel.max() <= GEMM_TOL
 
 
-MOE_CASES = [("moe_e128_top8_m658", 0), ("moe_e128_top8_m658", 2)]  # gate (Q4_K), down (Q6_K)
+# gate (Q4_K 2048 -> 768) and down (Q6_K 768 -> 2048), with the routed counts
+# as drawn (41 rows per expert: 32-row tiles of the shared-activation kernel)
+# and scaled by 2.4 (99 rows: its 80-row tiles)
+MOE_CASES = [("moe_e128_top8_m658", j, scale) for scale in (1.0, 2.4) for j in (0, 2)]
 
 
 @pytest.mark.parametrize("layout", ["row", "xf"])
-@pytest.mark.parametrize("name,j", MOE_CASES, ids=[f"{n}-{synth.MOE_WORKLOADS[n]['gemms'][j][0]}" for n, j in MOE_CASES])
-def test_moe_grouped_sampled(name, j, layout):
+@pytest.mark.parametrize("name,j,scale", MOE_CASES,
+                         ids=[f"{n}-{synth.MOE_WORKLOADS[n]['gemms'][j][0]}-x{s}" for n, j, s in MOE_CASES])
+def test_moe_grouped_sampled(name, j, scale, layout):
     """The grouped per-expert GEMM at the MoE workload's full size, on row-major
     routed rows and on their fragment-major copy (as the benchmark launches
     it), on a seeded sample of outputs (first and last rows included): each
-    sampled row is checked against its own expert's weights."""
+    sampled row is checked against its own expert's weights.  Scaled counts
+    reuse the drawn rows in turn."""
     import torch
 
     w = synth.MOE_WORKLOADS[name]
     label, fmt, K, N = w["gemms"][j]
     E = w["experts"]
-    counts = synth.moe_counts(name)
+    counts0 = synth.moe_counts(name)
+    counts = np.round(counts0 * scale).astype(np.int64)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     T = int(offs[-1])
-    print(f"moe {name}/{label} fmt={fmt} T={T} K={K} N={N} E={E} layout={layout}", flush=True)
+    plan = qg.grouped_plan(T, E, N, K)
+    assert (plan["name"], plan["rows"]) == ("shared", 32 if scale == 1.0 else 80), plan
+    print(f"moe {name}/{label} fmt={fmt} T={T} K={K} N={N} E={E} layout={layout} plan={plan}", flush=True)
     X, fields, enc = synth.moe_inputs(name, j)
+    X = np.ascontiguousarray(X[np.arange(T) % X.shape[0]])
     packed = np.concatenate([qg.pack(fmt, enc[e * N:(e + 1) * N], N, K) for e in range(E)])
     x, wp, offs_d = to_device(X, qg.F16), bytes_to_device(packed), torch.from_numpy(offs).cuda()
     if layout == "row":

@@ -354,16 +354,18 @@ def _clamped_ranges(offs, T):
 
 
 @pytest.mark.parametrize("layout", ["row", "xf"])
-@pytest.mark.parametrize("K", [512, 2048], ids=["direct", "stream"])
-def test_grouped_malformed_offsets(K, layout):
+@pytest.mark.parametrize("K,kernel", [(2048, "direct"), (256, "shared")], ids=["direct", "shared"])
+def test_grouped_malformed_offsets(K, kernel, layout):
     """Offsets that are negative, decreasing or past T: both grouped kernels
-    (K = 512 takes the direct kernel, K = 2048 the 64x64 streaming tiles at
-    these 75 rows per expert) compute exactly the clamped ranges, and write
-    nothing outside Y, on both activation layouts."""
+    (at these 75 rows per expert, K = 2048 takes the direct kernel with K
+    split over its waves, K = 256 the shared-activation kernel's 80-row
+    tiles) compute exactly the clamped ranges, and write nothing outside Y,
+    on both activation layouts."""
     import torch
 
     T, N, fmt = 300, 80, "q4k"
     offs = np.array([-5, 90, 40, 250, 700], np.int32)
+    assert qg.grouped_plan(T, len(offs) - 1, N, K)["name"] == kernel
     cases = [Case(fmt, T, N, K, qg.F16, seed=450 + e) for e in range(len(offs) - 1)]
     X = cases[0].X
     W = torch.from_numpy(np.concatenate([c.packed for c in cases])).cuda()
@@ -385,23 +387,17 @@ def test_grouped_malformed_offsets(K, layout):
     assert covered.all()  # [0, T) is covered by the clamped ranges here
 
 
-@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
-def test_grouped_stream_parity(fmt, sym, dtype):
-    """The grouped 64x64 streaming tiles (more than 64 rows per expert on
-    average, at least 16 chunks, on either activation layout): experts
-    spanning several 64-row tiles and starting inside a 32-row block, empty
-    and one-row experts, a ragged last column tile; rows outside every
-    expert's range are left untouched, and both layouts give the same bits."""
+def _grouped_check(fmt, sym, dtype, counts, N, K, seed, what):
+    """One grouped case on both activation layouts: each expert's rows against
+    the oracle on that expert's weights, nothing written outside Y, and the
+    same bits from both layouts."""
     import torch
 
-    N, K = 144, 2048
-    counts = [0, 70, 130, 1, 140]
-    cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=410)
+    cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=seed)
     T = int(offs[-1])
     outs = {}
     for layout in ("row", "xf"):
-        print(f"grouped stream {fmt} sym={sym} dtype={dtype} layout={layout} counts={counts}", flush=True)
+        print(f"{what} {fmt} sym={sym} dtype={dtype} layout={layout} counts={counts} K={K}", flush=True)
         pad = 4096
         tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
         buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
@@ -414,38 +410,36 @@ def test_grouped_stream_parity(fmt, sym, dtype):
             if m == 0:
                 continue
             Yref, B = oracle.gemm(c.X[:m], c.W, dtype)
-            assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"grouped stream {layout} expert {e} rows {m}")
+            assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"{what} {layout} expert {e} rows {m}")
     assert np.array_equal(outs["row"], outs["xf"])
 
 
 @pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
-def test_grouped_parity(fmt, sym, dtype):
-    """Each expert's rows match the oracle on that expert's weights, with empty
-    experts, one-row experts and ragged counts; mean rows per expert of 10, 27
-    and 44 select one and two 16-row blocks per wave (K = 512 and these
-    counts keep both layouts on the direct grouped kernel, so both give the
-    same bits)."""
-    import torch
+def test_grouped_shared_parity(fmt, sym, dtype):
+    """The shared-activation grouped kernel (K of two chunks, where the plan
+    never splits K) with both tile heights: 80-row tiles at 69 rows per
+    expert on average, 32-row tiles at 27 and 44.  Experts span several tiles
+    and start inside a 32-row block; empty and one-row experts; N = 144 leaves
+    the second column group with one live panel of eight."""
+    N, K = 144, 256
+    for counts, rows in (([0, 70, 130, 1, 140], 80), ([0, 1, 17, 40, 100, 3], 32), ([44, 60, 28], 32)):
+        plan = qg.grouped_plan(sum(counts), len(counts), N, K)
+        assert (plan["name"], plan["rows"]) == ("shared", rows), plan
+        _grouped_check(fmt, sym, dtype, counts, N, K, seed=410, what="grouped shared")
 
-    N, K = 96, 512
-    for counts in ([0, 1, 17, 40, 100, 3], [5, 0, 12, 3, 30, 10], [44, 60, 28]):
-        cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=400)
-        T = int(offs[-1])
-        outs = {}
-        for layout in ("row", "xf"):
-            print(f"grouped {fmt} sym={sym} dtype={dtype} layout={layout} counts={counts}", flush=True)
-            pad = 4096
-            tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
-            buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
-            out = buf[pad:pad + T * N].view(T, N)
-            _grouped_call(layout, fmt, X, W, N, offs_d, len(counts), dtype, out=out, sym=sym)
-            host = buf.cpu()
-            assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
-            outs[layout] = Y = from_device(out)
-            for e, (c, m) in enumerate(zip(cases, counts)):
-                if m == 0:
-                    continue
-                Yref, B = oracle.gemm(c.X[:m], c.W, dtype)
-                assert_gemm_close(Y[offs[e]:offs[e + 1]], Yref, B, dtype, what=f"grouped {layout} expert {e} rows {m}")
-        assert np.array_equal(outs["row"], outs["xf"])
+
+@pytest.mark.parametrize("fmt,sym", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f16", "bf16"])
+def test_grouped_parity(fmt, sym, dtype):
+    """The direct grouped kernel: each expert's rows match the oracle on that
+    expert's weights, with empty experts, one-row experts and ragged counts;
+    mean rows per expert of 10, 27, 44 and 69 select one and two 16-row
+    blocks per wave, and these small grids split K over the waves (two ways
+    at K = 512, eight at 2048)."""
+    N = 96
+    for counts, K in (([0, 1, 17, 40, 100, 3], 512), ([5, 0, 12, 3, 30, 10], 512), ([44, 60, 28], 512),
+                      ([0, 70, 130, 1, 140], 2048)):
+        plan = qg.grouped_plan(sum(counts), len(counts), N, K)
+        assert plan["name"] == "direct" and plan["kw"] > 1, plan
+        _grouped_check(fmt, sym, dtype, counts, N, K, seed=400, what="grouped direct")
