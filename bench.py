@@ -28,6 +28,8 @@ Profiling helpers (same JSON line, restricted work):
                         the mixture-of-experts FFN, where the two steps tie:
                         the grouped GEMMs gain about what the copies cost)
     --no-merge          seven separate GEMMs instead of qkv, o, gate_up, down
+                        (for the mixture-of-experts FFN: gate and up as two
+                        grouped launches instead of one over both)
     --copy-calibration BYTES
                         run a plain device-to-device copy of BYTES bytes three
                         times and exit (reference for HBM byte counters)
@@ -555,7 +557,8 @@ def run_grouped(args) -> int:
     over the routed rows (already grouped by expert), by default on those
     row-major rows; --x-layout xf runs them on the rows' fragment-major copy
     made inside the step (one copy for gate and up, which read the same rows,
-    one for down).  Beside it: the two layouts' steps and GEMMs interleaved,
+    one for down).  Gate and up run as one grouped GEMM over each expert's
+    gate and up columns side by side (--no-merge: two launches).  Beside it: the two layouts' steps and GEMMs interleaved,
     and the same work issued as one launch per expert.  Weight-bound, so the
     experts' weights rotate through copies totalling >= --pool-mb, and the
     streaming-read probe of the same bytes sits beside each GEMM.  Launches
@@ -580,17 +583,18 @@ def run_grouped(args) -> int:
     offs = torch.from_numpy(offs_h).cuda()
     xf_layout = args.x_layout == "xf"
     gemms, inputs = [], {}
-    for j, (label, fmt, K, N) in enumerate(w["gemms"]):
+    for sg in synth.moe_step_gemms(name, merge=not args.no_merge):
+        label, fmt, K, N = sg["label"], sg["fmt"], sg["K"], sg["N"]
         if args.only is not None and label != args.only:
             continue
-        X, fields, enc = synth.moe_inputs(name, j)
+        X, enc = synth.moe_step_inputs(name, sg["members"])
         per = [qg.pack(fmt, enc[e * N:(e + 1) * N], N, K) for e in range(E)]
         stride = per[0].nbytes
         wp = torch.from_numpy(np.concatenate(per)).cuda()
-        del per, fields, enc
+        del per, enc
         ncopy = max(1, int(np.ceil(args.pool_mb * 1e6 / wp.numel()))) if args.pool_mb > 0 else 1
         pool = [wp] + [wp.clone() for _ in range(ncopy - 1)]
-        src = w["input_of"][j]
+        src = sg["input"]
         if src not in inputs:
             x = torch.from_numpy(X.view(np.int16)).view(torch.float16).cuda()
             xf = torch.empty(qg.xf_bytes(T, K) // 2, dtype=torch.float16, device="cuda")

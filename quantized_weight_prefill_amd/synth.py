@@ -327,6 +327,7 @@ MOE_WORKLOADS = {
         "index": 6, "tokens": 658, "experts": 128, "top_k": 8, "zipf": 0.8,
         "gemms": [("gate", "q4k", 2048, 768), ("up", "q4k", 2048, 768), ("down", "q6k", 768, 2048)],
         "input_of": [0, 0, 2],  # GEMM j reads the routed rows of GEMM input_of[j]: gate and up share theirs
+        "merged": [("gate_up", ("gate", "up"))],  # one grouped GEMM over each expert's gate and up columns
     },
 }
 
@@ -356,3 +357,63 @@ def moe_inputs(name: str, j: int, dtype: int = F16):
     X = activations(rs[2 * w["input_of"][j]], T, K, dtype)
     fields = weight_fields(fmt, rs[2 * j + 1], N * w["experts"], K)
     return X, fields, encode(fmt, fields)
+
+
+def moe_step_gemms(name: str, merge: bool = True) -> list[dict]:
+    """The grouped GEMMs of one MoE step: with merge, each merged group is one
+    grouped GEMM whose expert e holds its members' expert-e columns side by
+    side (placed where its first member is).  Each entry: label, members
+    (GEMM indices), fmt, K, N, input (the GEMM whose routed rows it reads)."""
+    w = MOE_WORKLOADS[name]
+    labels = [g[0] for g in w["gemms"]]
+    groups = {}
+    if merge:
+        for lab, members in w.get("merged", []):
+            idx = [labels.index(m) for m in members]
+            first = w["gemms"][idx[0]]
+            for j in idx:
+                g = w["gemms"][j]
+                assert g[1:3] == first[1:3] and w["input_of"][j] == w["input_of"][idx[0]]
+            groups[idx[0]] = (lab, idx)
+    member_of = {j for _, idx in groups.values() for j in idx}
+    out = []
+    for j, (label, fmt, K, N) in enumerate(w["gemms"]):
+        if j in groups:
+            lab, idx = groups[j]
+            out.append(dict(label=lab, members=idx, fmt=fmt, K=K, N=sum(w["gemms"][i][3] for i in idx),
+                            input=w["input_of"][j]))
+        elif j not in member_of:
+            out.append(dict(label=label, members=[j], fmt=fmt, K=K, N=N, input=w["input_of"][j]))
+    return out
+
+
+def moe_step_inputs(name: str, members):
+    """(X bits [T][K], encoded weights of all experts as one E*N-column
+    matrix) of a step GEMM: expert e owns columns e*N .. (e+1)*N-1, its
+    members' expert-e columns side by side in member order."""
+    w = MOE_WORKLOADS[name]
+    E = w["experts"]
+    fmt = w["gemms"][members[0]][1]
+    X, parts = None, []
+    for j in members:
+        Xj, _, enc = moe_inputs(name, j)
+        X = Xj if X is None else X
+        parts.append((enc, w["gemms"][j][3]))
+    if len(parts) == 1:
+        return X, parts[0][0]
+    cols = []
+    for e in range(E):
+        cols += [enc[e * n:(e + 1) * n] if fmt in ("q4k", "q6k") else _enc_cols(enc, e * n, (e + 1) * n)
+                 for enc, n in parts]
+    return X, concat_encoded(fmt, cols)
+
+
+def _enc_cols(enc, c0: int, c1: int):
+    """Columns c0 .. c1-1 of a W4A16 encoding (codes [N][...], scales and
+    zeros [groups][N])."""
+    out = dict(enc)
+    out["codes"] = enc["codes"][c0:c1]
+    out["scales"] = enc["scales"][:, c0:c1]
+    if enc.get("zeros") is not None:
+        out["zeros"] = enc["zeros"][:, c0:c1]
+    return out

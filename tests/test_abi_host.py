@@ -830,3 +830,21 @@ def test_noalloc_entry_rejects_oversized_calls_before_launch():
     assert lib.qgemm_gemm_xf_noalloc(1, 99, A, A, A, 64, N, K, 0, 0, 0, None) == -5
     assert lib.qgemm_gemm_xf_noalloc(1, -1, None, A, A, 64, N, K, 0, 0, 0, None) == -1
     assert lib.qgemm_gemm_xf_noalloc(1, -1, None, None, None, 0, N, K, 0, 0, 0, None) == 0
+
+
+def test_moe_step_gemms_merge():
+    """The MoE step runs gate and up as one grouped GEMM: expert e of the
+    merged weights is expert e's gate columns, then its up columns, and the
+    merged GEMM reads the routed rows both members read."""
+    name = "moe_e128_top8_m658"
+    merged = synth.moe_step_gemms(name)
+    assert [(g["label"], g["N"], g["members"]) for g in merged] == [("gate_up", 1536, [0, 1]), ("down", 2048, [2])]
+    assert [g["label"] for g in synth.moe_step_gemms(name, merge=False)] == ["gate", "up", "down"]
+    X, enc = synth.moe_step_inputs(name, [0, 1])
+    Xg, _, eg = synth.moe_inputs(name, 0)
+    _, _, eu = synth.moe_inputs(name, 1)
+    assert np.array_equal(X, Xg)
+    N = 768
+    for e in (0, 63, 127):
+        assert np.array_equal(enc[2 * N * e:2 * N * e + N], eg[N * e:N * (e + 1)])
+        assert np.array_equal(enc[2 * N * e + N:2 * N * (e + 1)], eu[N * e:N * (e + 1)])

@@ -49,34 +49,38 @@ def test_workload_sampled(name, j, layout):
     assert rel.max() <= GEMM_TOL
 
 
-# gate (Q4_K 2048 -> 768) and down (Q6_K 768 -> 2048), with the routed counts
-# as drawn (41 rows per expert: 32-row tiles of the shared-activation kernel)
-# and scaled by 2.4 (99 rows: its 80-row tiles)
-MOE_CASES = [("moe_e128_top8_m658", j, scale) for scale in (1.0, 2.4) for j in (0, 2)]
+# gate and up merged (Q4_K 2048 -> 2 x 768 per expert, as the benchmark runs
+# them), down (Q6_K 768 -> 2048) and gate alone, with the routed counts as
+# drawn (41 rows per expert: 32-row tiles of the shared-activation kernel) and
+# scaled by 2.4 (99 rows: its 80-row tiles)
+MOE = "moe_e128_top8_m658"
+MOE_CASES = [("gate_up", 1.0), ("down", 1.0), ("gate", 1.0), ("gate_up", 2.4), ("down", 2.4)]
 
 
 @pytest.mark.parametrize("layout", ["row", "xf"])
-@pytest.mark.parametrize("name,j,scale", MOE_CASES,
-                         ids=[f"{n}-{synth.MOE_WORKLOADS[n]['gemms'][j][0]}-x{s}" for n, j, s in MOE_CASES])
-def test_moe_grouped_sampled(name, j, scale, layout):
+@pytest.mark.parametrize("label,scale", MOE_CASES, ids=[f"{MOE}-{lab}-x{sc}" for lab, sc in MOE_CASES])
+def test_moe_grouped_sampled(label, scale, layout):
     """The grouped per-expert GEMM at the MoE workload's full size, on row-major
     routed rows and on their fragment-major copy (as the benchmark launches
     it), on a seeded sample of outputs (first and last rows included): each
-    sampled row is checked against its own expert's weights.  Scaled counts
-    reuse the drawn rows in turn."""
+    sampled row is checked against its own expert's weights (for gate_up, the
+    expert's gate and up columns side by side).  Scaled counts reuse the drawn
+    rows in turn."""
     import torch
 
-    w = synth.MOE_WORKLOADS[name]
-    label, fmt, K, N = w["gemms"][j]
+    w = synth.MOE_WORKLOADS[MOE]
+    sg = [g for g in synth.moe_step_gemms(MOE, merge=True) + synth.moe_step_gemms(MOE, merge=False)
+          if g["label"] == label][0]
+    fmt, K, N = sg["fmt"], sg["K"], sg["N"]
     E = w["experts"]
-    counts0 = synth.moe_counts(name)
+    counts0 = synth.moe_counts(MOE)
     counts = np.round(counts0 * scale).astype(np.int64)
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     T = int(offs[-1])
     plan = qg.grouped_plan(T, E, N, K)
     assert (plan["name"], plan["rows"]) == ("shared", 32 if scale == 1.0 else 80), plan
-    print(f"moe {name}/{label} fmt={fmt} T={T} K={K} N={N} E={E} layout={layout} plan={plan}", flush=True)
-    X, fields, enc = synth.moe_inputs(name, j)
+    print(f"moe {MOE}/{label} fmt={fmt} T={T} K={K} N={N} E={E} layout={layout} plan={plan}", flush=True)
+    X, enc = synth.moe_step_inputs(MOE, sg["members"])
     X = np.ascontiguousarray(X[np.arange(T) % X.shape[0]])
     packed = np.concatenate([qg.pack(fmt, enc[e * N:(e + 1) * N], N, K) for e in range(E)])
     x, wp, offs_d = to_device(X, qg.F16), bytes_to_device(packed), torch.from_numpy(offs).cuda()
@@ -86,7 +90,7 @@ def test_moe_grouped_sampled(name, j, scale, layout):
         y = qg.grouped_xf(fmt, qg.x_to_xf(x), wp, T, N, K, offs_d, E)
     Y = from_device(y)
     W = oracle.dequant(fmt, enc, E * N, K, qg.F16)
-    rng = np.random.default_rng(4343 + j)
+    rng = np.random.default_rng(4343 + K + N)
     count = 2000
     rows = np.concatenate([rng.integers(0, T, count), [0, T - 1]])
     cols = np.concatenate([rng.integers(0, N, count), [N - 1, 0]])
