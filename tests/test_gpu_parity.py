@@ -319,22 +319,22 @@ def test_staged_arm_m_zero_fills_scratch():
 # grouped per-expert GEMM
 # ----------------------------------------------------------------------------
 
-def _grouped_case(fmt, sym, counts, N, K, dtype, seed):
+def _grouped_case(fmt, sym, counts, N, K, dtype, seed, group=128):
     """Per-expert inputs: X rows grouped by expert, each expert's own weights."""
     import torch
 
-    cases = [Case(fmt, max(m, 1), N, K, dtype, seed + e, symmetric=sym) for e, m in enumerate(counts)]
+    cases = [Case(fmt, max(m, 1), N, K, dtype, seed + e, group=group, symmetric=sym) for e, m in enumerate(counts)]
     X = np.concatenate([c.X[:m] for c, m in zip(cases, counts)], axis=0)
     W_all = np.concatenate([c.packed for c in cases])
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     return cases, X, torch.from_numpy(W_all).cuda(), torch.from_numpy(offs).cuda(), offs
 
 
-def _grouped_call(layout, fmt, X, W, N, offs_d, E, dtype, out=None, sym=True):
+def _grouped_call(layout, fmt, X, W, N, offs_d, E, dtype, out=None, sym=True, group=128):
     """One grouped launch on row-major X (qgemm_grouped) or on its
     fragment-major copy (qgemm_grouped_xf)."""
     x = to_device(X, dtype)
-    kw = dict(group=128 if fmt == "w4a16" else 0, has_zp=not sym, out=out)
+    kw = dict(group=group if fmt == "w4a16" else 0, has_zp=not sym, out=out)
     if layout == "row":
         return qg.grouped(fmt, x, W, N, offs_d, E, **kw)
     T, K = X.shape
@@ -387,13 +387,13 @@ def test_grouped_malformed_offsets(K, kernel, layout):
     assert covered.all()  # [0, T) is covered by the clamped ranges here
 
 
-def _grouped_check(fmt, sym, dtype, counts, N, K, seed, what):
+def _grouped_check(fmt, sym, dtype, counts, N, K, seed, what, group=128):
     """One grouped case on both activation layouts: each expert's rows against
     the oracle on that expert's weights, nothing written outside Y, and the
     same bits from both layouts."""
     import torch
 
-    cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=seed)
+    cases, X, W, offs_d, offs = _grouped_case(fmt, sym, counts, N, K, dtype, seed=seed, group=group)
     T = int(offs[-1])
     outs = {}
     for layout in ("row", "xf"):
@@ -402,7 +402,7 @@ def _grouped_check(fmt, sym, dtype, counts, N, K, seed, what):
         tdt = torch.float16 if dtype == qg.F16 else torch.bfloat16
         buf = torch.full((T * N + 2 * pad,), 7.0, dtype=tdt, device="cuda")
         out = buf[pad:pad + T * N].view(T, N)
-        _grouped_call(layout, fmt, X, W, N, offs_d, len(counts), dtype, out=out, sym=sym)
+        _grouped_call(layout, fmt, X, W, N, offs_d, len(counts), dtype, out=out, sym=sym, group=group)
         host = buf.cpu()
         assert torch.all(host[:pad] == 7.0) and torch.all(host[pad + T * N:] == 7.0)
         outs[layout] = Y = from_device(out)
@@ -443,3 +443,18 @@ def test_grouped_parity(fmt, sym, dtype):
         plan = qg.grouped_plan(sum(counts), len(counts), N, K)
         assert plan["name"] == "direct" and plan["kw"] > 1, plan
         _grouped_check(fmt, sym, dtype, counts, N, K, seed=400, what="grouped direct")
+
+
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("sym", [False, True], ids=["asym", "sym"])
+def test_grouped_w4a16_group_sizes(group, sym):
+    """W4A16 experts quantized in groups of 32 and 64 (each expert's packed
+    size, and so its offset in the weights, depends on the group size): the
+    shared-activation kernel (K = 256) and the direct kernel (K = 2048, K
+    split over its waves), both layouts, against the oracle."""
+    N = 144
+    counts = [0, 70, 130, 1, 140]
+    for K, kernel in ((256, "shared"), (2048, "direct")):
+        assert qg.grouped_plan(sum(counts), len(counts), N, K)["name"] == kernel
+        _grouped_check("w4a16", sym, qg.F16, counts, N, K, seed=470 + group, what=f"grouped w4a16 g{group} {kernel}",
+                       group=group)
