@@ -21,7 +21,8 @@ const char *const kRungNames[RUNG_COUNT] = {"direct-small-m",    "direct-skinny-
                                             "mfma32-128x160",    "mfma32-64x64-k4",   "mfma32-352x96",
                                             "mfma32-192x96-k2",  "mfma32-192x64-k2",  "mfma32-64x64-sk",
                                             "mfma32-64x32-k4",   "mfma32-128x64-k2",  "mfma32-96x32-k4",
-                                            "mfma32-768x96",     "mfma32-512x128",    "mfma32-512x96"};
+                                            "mfma32-768x96",     "mfma32-512x128",    "mfma32-512x96",
+                                            "mfma32-768x64-sk"};
 
 // A one-dimensional launch of gx workgroups of `threads` threads fits when
 // gx is at most 2^31-1 and the work-items along x at most 2^32-1.
@@ -94,16 +95,20 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
     case RUNG_M192N64_K2:
     case RUNG_M768N96:
     case RUNG_M512N128:
-    case RUNG_M512N96: {
+    case RUNG_M512N96:
+    case RUNG_M768N64_SK: {
         const bool n96 = rung == RUNG_M352N96 || rung == RUNG_M192N96_K2 || rung == RUNG_M768N96 || rung == RUNG_M512N96;
-        const bool big = rung == RUNG_M768N96 || rung == RUNG_M512N128 || rung == RUNG_M512N96;  // 8 waves, K whole
+        const bool big = rung == RUNG_M768N96 || rung == RUNG_M512N128 || rung == RUNG_M512N96 ||
+                         rung == RUNG_M768N64_SK;  // 8 waves, no K groups inside the workgroup
         const bool r192 = rung == RUNG_M192N96_K2 || rung == RUNG_M192N64_K2;
         const bool r64 = rung == RUNG_M64_K4 || rung == RUNG_M64_SK || rung == RUNG_M64N32_K4;
         const bool k4 = r64 || rung == RUNG_M96N32_K4;  // K split over up to four groups
         pl.rows = rung == RUNG_M16_256 ? 256 : r64 ? 64 : rung == RUNG_M352N96 ? 352 : r192 ? 192
-                  : rung == RUNG_M96N32_K4 ? 96 : rung == RUNG_M768N96 ? 768 : big ? 512 : 128;
+                  : rung == RUNG_M96N32_K4 ? 96 : (rung == RUNG_M768N96 || rung == RUNG_M768N64_SK) ? 768
+                  : big ? 512 : 128;
         pl.cols = rung == RUNG_M128N160 ? 160 : (rung == RUNG_M64N32_K4 || rung == RUNG_M96N32_K4) ? 32
-                  : (r64 || rung == RUNG_M192N64_K2 || rung == RUNG_M128N64_K2) ? 64 : n96 ? 96 : 128;
+                  : (r64 || rung == RUNG_M192N64_K2 || rung == RUNG_M128N64_K2 || rung == RUNG_M768N64_SK) ? 64
+                  : n96 ? 96 : 128;
         pl.kw = ((rung == RUNG_M128_K2 || rung == RUNG_M128N64_K2 || r192) && (K / kChunk) % 2 == 0) ? 2 : 1;
         if (k4) pl.kw = (K / kChunk) % 4 == 0 ? 4 : (K / kChunk) % 2 == 0 ? 2 : 1;
         pl.waves = (rung == RUNG_M16_256 || big) ? 8 : r64 ? 2 * pl.kw : rung == RUNG_M96N32_K4 ? 3 * pl.kw
@@ -121,6 +126,10 @@ int make_plan(int rung, long long M, long long N, long long K, Plan &pl)
             while (pl.split < 8 && tn * tm * 2 * pl.split <= 2 * kCUs && nch % (2 * pl.split * pl.kw) == 0 &&
                    nch / (2 * pl.split * pl.kw) >= 4)
                 pl.split *= 2;
+        } else if (rung == RUNG_M768N64_SK) {
+            // slices across workgroups: the most (up to eight) that keep the
+            // grid within one round and every slice at least two chunks
+            while (pl.split < 8 && tn * tm * 2 * pl.split <= kCUs && nch / (2 * pl.split) >= 2) pl.split *= 2;
         }
         if (!launch_fits(tn * tm * pl.split, 64 * pl.waves)) return QGEMM_ERR_SHAPE;
         pl.grid = dim3((unsigned)(tn * tm * pl.split), 1, 1);
@@ -336,6 +345,28 @@ int large_tile_xf(int fmt, long long M, long long N, long long K)
     return pick;
 }
 
+// The 768x64 tiles with K split across workgroups, on fragment-major
+// activations (the caller passes the partial sums' workspace): for 513..768
+// rows of Q4_K or Q6_K over at least 96 chunks (K >= 12288), when 64-column
+// tiles times a power-of-two slice count of 2..8 make exactly one round.
+// Each weight is then unpacked once for all the rows and the CUs stay busy
+// although the tiles alone would fill a quarter or half of them.  Measured
+// against the ladder's choice (fp16, weights rotating, interleaved): Q6_K
+// 658x12288 -> 4096 92.0 against 101.4 us (four slices), 520 rows 86.7 against
+// 93.2, 768 rows 95.6 against 103.5, K = 16384 115.2 against 132.9, N = 8192
+// at 600 rows 159.1 against 183.7 (two slices); Q4_K 658x12288 -> 4096 89.2
+// against 95.2, -> 2048 53.4 against 57.7 (eight slices).  It loses at K =
+// 8192 (Q4_K, 700 rows: 68.0 against 64.2 us) and at 400 rows (80.8 against
+// 71.9), where the 768-row tile is half empty.
+bool split768_pays(int fmt, long long M, long long np, long long K)
+{
+    if (fmt == FMT_W4 || M <= 512 || M > 768 || K / kChunk < 96 || np % 4 != 0) return false;
+    const long long tn = np / 4;
+    for (long long S = 2; S <= 8; S *= 2)
+        if (tn * S == kCUs) return true;
+    return false;
+}
+
 int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtype = DT_F16)
 {
     const long long np = (N + 15) / 16, tn = (np + 7) / 8;
@@ -366,6 +397,7 @@ int select_rung(int fmt, long long M, long long N, long long K, int xl, int dtyp
         if (split_pays(fmt, dtype, M, np, K, xl)) return RUNG_M64_SK;
         return round_model_rung(fmt, M, N, K, xl, dtype);
     }
+    if (xl == X_FRAG && split768_pays(fmt, M, np, K)) return RUNG_M768N64_SK;
     if (const int r = round_model_rung(fmt, M, N, K, xl, dtype); r >= 0) return r;
     if (xl == X_FRAG) return large_tile_xf(fmt, M, N, K);
     // row-major activations: the rule chain below (its tiles read 32 rows x
@@ -472,7 +504,7 @@ hipError_t launch(int fmt, int dtype, int xl, const Plan &pl, const Args &a, hip
 // so that every slice starts 16-byte aligned.  0 for the other rungs.
 size_t split_ws_bytes(const Plan &pl, long long M, long long N)
 {
-    if (pl.split <= 1 && pl.rung != RUNG_M64_SK) return 0;
+    if (pl.split <= 1 && pl.rung != RUNG_M64_SK && pl.rung != RUNG_M768N64_SK) return 0;
     const long long stride = (M * N + 3) & ~3LL;
     return (size_t)(stride * pl.split) * 4;
 }

@@ -688,14 +688,17 @@ __global__ void __launch_bounds__(64 * NW) k_grouped_shared(Args a)
 // [M][N], rows below M).  k_splitk_reduce then adds the S slices in slice
 // order and rounds once, so the result does not depend on timing.  Grid: S
 // times the tiles; consecutive logical indices share a slice, so the tiles
-// running together on one XCD read the same activation slice.
+// running together on one XCD read the same activation slice.  The same
+// kernel with 96-row waves (768x64 tiles, a two-deep activation ring) serves
+// a few hundred rows over a long K, where 64 column tiles times S slices fill
+// the CUs in one round and each weight is unpacked once for all the rows.
 // ---------------------------------------------------------------------------
-template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int XL>
+template <int FMT, int DT, int WM, int WPB, int NWM, int NWN, int KS, int XL, int D = 8, int LA = 1>
 __global__ void __launch_bounds__(64 * NWM * NWN * KS) __attribute__((amdgpu_waves_per_eu(2)))
 k_stream32_sk(Args a)
 {
     const int S = a.split;
-    using St = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL>;
+    using St = Stream32<FMT, DT, WM, WPB, NWM, NWN, XL, D, LA>;
     constexpr int CBW = St::CBW, RBW = St::RBW, PB = St::PB, BM = St::BM;
     constexpr int NACC = NWM * NWN * CBW * RBW * 64;
     static_assert(KS == 1 || (KS - 1) * NACC * sizeof(f32x16) <= KS * sizeof(typename St::Lds),
@@ -840,6 +843,9 @@ hipError_t launch_fd(const Plan &pl, const Args &a, hipStream_t s)
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 6, 1, 2, XL>), pl.grid, dim3(768), 0, s, a);
         else
             hipLaunchKernelGGL((k_stream32<FMT, DT, 32, 4, 6, 1, 1, XL>), pl.grid, dim3(384), 0, s, a);
+        return hipGetLastError();
+    case RUNG_M768N64_SK:
+        hipLaunchKernelGGL((k_stream32_sk<FMT, DT, 96, 4, 8, 1, 1, XL, 2, 1>), pl.grid, dim3(512), 0, s, a);
         return hipGetLastError();
     case RUNG_M64_SK:
         if (pl.kw == 4)

@@ -33,7 +33,8 @@ enum Rung {
     RUNG_M768N96 = 15,    // 32x32x16 MFMA: 768x96, 8 waves of 96x96 (two per SIMD)
     RUNG_M512N128 = 16,   // 32x32x16 MFMA: 512x128, 8 waves of 64x128
     RUNG_M512N96 = 17,    // 32x32x16 MFMA: 512x96, 8 waves of 64x96
-    RUNG_COUNT = 18
+    RUNG_M768N64_SK = 18, // 32x32x16 MFMA: 768x64, 8 waves of 96x64, K split across workgroups
+    RUNG_COUNT = 19
 };
 
 enum I8Rung {

@@ -493,7 +493,7 @@ def test_ladder_fragment_major():
     XF_WINNERS = [
         # (fmt, M, N, K, rung): fp16 unless noted; the margin over the next tile
         ("q4k", 658, 4096, 4096, "mfma32-192x64-k2"),    # o (bf16: 31.8 against 36.9 us)
-        ("q6k", 658, 4096, 12288, "mfma32-192x64-k2"),   # down
+        ("q6k", 658, 4096, 12288, "mfma32-768x64-sk"),   # down: four slices, 92.0 against 101.4 (192x64-k2)
         ("q4k", 658, 6144, 4096, "mfma32-192x96-k2"),    # qkv: 44.6 against 59.1 us (128x160)
         ("q6k", 700, 6144, 4096, "mfma32-192x96-k2"),    # 47.5 against 64.5 (352x96)
         ("q4k", 384, 12288, 4096, "mfma32-192x96-k2"),   # 46.2 against 59.6 (128x160)
@@ -519,6 +519,21 @@ def test_ladder_fragment_major():
         assert qg.select_rung_xf(fmt, 658, 24576, 4096)["name"] == "mfma32-768x96", fmt
     assert qg.select_rung("q4k", 658, 24576, 4096)["name"] == "mfma32-128x160"         # row-major
     assert qg.select_rung("q4k", 658, 4096, 4096)["name"] == "mfma32-128x128"          # row-major: K < 8192
+    # the 768x64 tiles split across workgroups: 513..768 rows of Q4_K or Q6_K over K >= 12288 when the
+    # 64-column tiles times 2, 4 or 8 slices make one round (measured winners: Q6_K 520, 658 and 768 rows
+    # over N = 4096, 600 rows over N = 8192, K = 16384; Q4_K over N = 2048 and 4096), with the slices
+    # in the plan and the partial sums in the workspace query
+    for fmt, M, N, K, S in [("q6k", 520, 4096, 12288, 4), ("q6k", 768, 4096, 12288, 4), ("q6k", 600, 8192, 12288, 2),
+                            ("q6k", 658, 4096, 16384, 4), ("q4k", 658, 4096, 12288, 4), ("q4k", 658, 2048, 12288, 8)]:
+        info = qg.select_rung_xf(fmt, M, N, K)
+        assert (info["name"], info["k_split"], info["rows"], info["cols"]) == ("mfma32-768x64-sk", S, 768, 64), (fmt, M, N, K)
+        assert qg.workspace_bytes(fmt, -1, M, N, K, qg.F16, qg.X_FRAG) == S * ((M * N + 3) // 4 * 4) * 4
+    # not at K = 8192 (Q4_K, 700 rows: 68.0 against 64.2 us), at 400 rows (80.8 against 71.9), for W4A16,
+    # over N = 6144 (no whole round), on row-major activations or past 768 rows
+    for fmt, M, N, K in [("q4k", 700, 4096, 8192), ("q6k", 400, 4096, 12288), ("w4a16", 658, 4096, 12288),
+                         ("q6k", 658, 6144, 12288), ("q6k", 800, 4096, 12288)]:
+        assert qg.select_rung_xf(fmt, M, N, K)["name"] != "mfma32-768x64-sk", (fmt, M, N, K)
+    assert qg.select_rung("q6k", 658, 4096, 12288)["name"] != "mfma32-768x64-sk"
     # one round of 128x64 tiles (the round model, before the large tiles)
     assert qg.select_rung_xf("q4k", 512, 4096, 4096)["name"] == "mfma32-128x64-k2"
     # a K-split tile with an odd chunk count (W4A16, K = 33 x 128) runs one K group: not a candidate

@@ -57,6 +57,29 @@ def test_split_rung_auto_down_projection(M):
     assert np.array_equal(y, from_device(c.run_xf(-1)))
 
 
+SK768 = [r for r in range(qg.num_rungs()) if qg.rung_name(r) == "mfma32-768x64-sk"][0]
+
+
+@pytest.mark.parametrize("fmt,M,N,K,dtype,slices", [
+    ("q6k", 600, 200, 4096, qg.F16, 8),       # 13 panels (the last ragged) in 4 column tiles, 4 chunks a slice
+    ("q4k", 530, 128, 2048, qg.BF16, 8),      # 2 chunks a slice
+    ("w4a16", 100, 320, 1536, qg.F16, 4),     # 100 rows of a 768-row tile, 3 chunks a slice
+    ("q4k", 800, 64, 2048, qg.F16, 8),        # two row tiles, the second 32 rows
+])
+def test_split768_rung_forced(fmt, M, N, K, dtype, slices):
+    """The 768x64 tiles (8 waves of 96x64) with K split across workgroups:
+    ragged rows and columns, slices of two to four chunks, both layouts."""
+    c = Case(fmt, M, N, K, dtype, seed=760 + M, group=128)
+    info = qg.rung_info(SK768, fmt, M, N, K, dtype)
+    print(f"split768 forced {fmt} M={M} N={N} K={K} dtype={dtype} info={info}", flush=True)
+    assert (info["k_split"], info["rows"], info["cols"]) == (slices, 768, 64), info
+    Yref, B = oracle.gemm(c.X, c.W, dtype)
+    y = from_device(c.run_xf(SK768))
+    assert_gemm_close(y, Yref, B, dtype, what=f"split768 {fmt} M={M} N={N} K={K}")
+    assert np.array_equal(y, from_device(c.run(SK768))), "row-major and fragment-major activations differ"
+    assert np.array_equal(y, from_device(c.run_xf(SK768))), "not reproducible from call to call"
+
+
 def _ws(nbytes: int, guard: int = 0):
     import torch
 
