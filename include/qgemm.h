@@ -253,9 +253,10 @@ const char *qgemm_rung_name(int rung);
 int qgemm_select_rung(int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
 int qgemm_rung_info(int rung, int format, int64_t M, int64_t N, int64_t K, int dtype, int32_t *info8);
 
-/* Workspace of the rung that splits K across workgroups (mfma32-64x64-sk:
- * the batched-prefill post's K-parallel row reduction, "The fix: K-parallel
- * batched DMMV", carried across workgroups with one reduction at the end):
+/* Workspace of the rungs that split K across workgroups (mfma32-64x64-sk and
+ * mfma32-768x64-sk: the batched-prefill post's K-parallel row reduction, "The
+ * fix: K-parallel batched DMMV", carried across workgroups with one
+ * reduction at the end):
  * the bytes a qgemm_gemm_rung (layout QGEMM_X_ROW) or qgemm_gemm_xf
  * (QGEMM_X_FRAG) call with these arguments needs, S*M*N*4 rounded so that
  * each of the S <= 8 slices of fp32 partial sums starts 16-byte aligned; 0
@@ -273,9 +274,12 @@ size_t qgemm_workspace_bytes(int format, int rung, int layout, int64_t M, int64_
  * partial sums of its 64x64 tiles to `workspace` (device, 16-byte aligned,
  * caller-owned, at least qgemm_workspace_bytes); a second launch adds the S
  * slices in slice order and rounds once into Y, so Y is deterministic, but
- * its fp32 summation order differs from the other rungs'.  Such a call with
- * workspace_bytes below that size (NULL included) returns QGEMM_ERR_SIZE
- * before any launch; the other rungs ignore both workspace arguments. */
+ * its fp32 summation order differs from the other rungs'.  mfma32-768x64-sk
+ * does the same with 768x64 tiles (S = 1..8, as many as keep the grid within
+ * one round of the 256 CUs and each slice at least two chunks).  Such a call
+ * with workspace_bytes below that size (NULL included) returns
+ * QGEMM_ERR_SIZE before any launch; the other rungs ignore both workspace
+ * arguments. */
 int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, void *Y, int64_t M, int64_t N,
                     int64_t K, int64_t group_size, int has_zp, int dtype, void *workspace, size_t workspace_bytes,
                     void *stream);
@@ -306,8 +310,10 @@ int qgemm_gemm_rung(int format, int rung, const void *X, const void *Wpacked, vo
  *   Y is bit-identical to qgemm_gemm_rung's on the row-major X: the kernels
  *   and their accumulation order are the same, only the activation addresses
  *   differ.  rung = -1 selects from the ladder tuned for this layout
- *   (qgemm_select_rung_xf), which may pick mfma32-64x64-sk: size the
- *   workspace with qgemm_workspace_bytes(..., QGEMM_X_FRAG, ...). */
+ *   (qgemm_select_rung_xf), which may pick mfma32-64x64-sk (33..64 rows over
+ *   a long K) or mfma32-768x64-sk (513..768 rows of Q4_K or Q6_K over K >=
+ *   12288, e.g. 658 x 12288 -> 4096 needs 43 MB): size the workspace with
+ *   qgemm_workspace_bytes(..., QGEMM_X_FRAG, ...). */
 size_t qgemm_xf_bytes(int64_t M, int64_t K);
 int qgemm_x_to_xf(const void *X, void *Xf, int64_t M, int64_t K, void *stream);
 int qgemm_gemm_xf(int format, int rung, const void *Xf, const void *Wpacked, void *Y, int64_t M, int64_t N,
