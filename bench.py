@@ -178,8 +178,8 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path would shard by N or K across GPUs, which is not built here)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by N or K across GPUs, which is not implemented)", file=sys.stderr)
         return 2
 
     if args.x_layout is None:
